@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Throughput of the CSR SpMM / SDDMM hot path on one MI355X.
+
+A step is one pass of the whole hot path over the Transformer-FFN workload
+(A 2048x512 at 90 % sparsity, row lengths N(51.2, 5.12); B 512x256; companion
+SDDMM with dY 2048x256 and X 512x256): CSR row offsets from the row lengths,
+row swizzle, SpMM C = A B and SDDMM dA = (dY X^T) at A's entries -- four
+kernels, captured once in a HIP graph and replayed.  Inputs are resident in
+HBM before timing starts.
+
+Prints one JSON line:
+  value        useful GFLOP/s of the step, (2 nnz n + 2 nnz d) / step time
+  roofline     the SpMM kernel: algorithmic (compulsory) bytes per launch over
+               its average launch duration, against 8 TB/s HBM peak
+  cpu_baseline the C oracle timed on this host's cores on the same inputs
+  kernels      per-kernel average durations, GFLOP/s and GB/s
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SpMM/SDDMM GFLOP/s (2·nnz·N) + HBM GB/s vs roofline at 90% sparsity"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X FP32 vector, published (counts packed FP32)
+FP32_FMA_PEAK_TFLOPS = 78.6      # 256 CU x 64 FMA/clk x 2 x 2.4 GHz: unpacked FMA (the build's)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spmm_transformer_ffn_traffic.json")
+SPMM_SOURCE = os.path.join(ROOT, "unstructured_sparse_linear_csr_amd", "csrc", "spmm.hip")
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--kernel-reps", type=int, default=200,
+                    help="back-to-back launches per kernel for per-kernel timing")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time spent timing the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-launches", type=int, default=0,
+                    help="only run this many eager launches of each kernel "
+                         "(for rocprofv3 counter passes) and exit")
+    return ap.parse_args()
+
+
+def host_info() -> dict:
+    model = platform.processor()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0))}
+
+
+def spmm_bytes(m, k, n, nnz) -> int:
+    """Compulsory bytes of one SpMM: CSR values and columns, row offsets and
+    row order, B read once, C written once."""
+    return 8 * nnz + 4 * (m + 1) + 4 * m + 4 * k * n + 4 * m * n
+
+
+def sddmm_bytes(m, k, d, nnz) -> int:
+    """Compulsory bytes of one SDDMM: X and Y read once, columns read, outputs
+    written, row offsets and row order."""
+    return 4 * m * d + 4 * k * d + 4 * nnz + 4 * nnz + 4 * (m + 1) + 4 * m
+
+
+def traffic_record():
+    """Measured HBM bytes per SpMM launch from the committed counter passes,
+    if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(SPMM_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards with no exchange; see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+    from unstructured_sparse_linear_csr_amd import binding as sp
+    from unstructured_sparse_linear_csr_amd import inputs
+
+    assert torch.cuda.is_available(), "needs an MI355X"
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    sp.lib()
+
+    w = inputs.transformer_ffn()
+    a = w["a"]
+    m, k, n, d, nnz = w["m"], w["k"], w["n"], w["d"], a.nnz
+    stats = inputs.row_stats(a.lengths, k)
+    log(f"workload {w['name']}: nnz={nnz} stats={stats}")
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    lengths, cols, vals = up(a.lengths), up(a.cols), up(a.values)
+    b, x, y = up(w["b"]), up(w["x"]), up(w["y"])
+    ro = torch.empty(m + 1, dtype=torch.int32, device=dev)
+    ri = torch.empty(m, dtype=torch.int32, device=dev)
+    c = torch.empty(m, n, dtype=torch.float32, device=dev)
+    out = torch.empty(nnz, dtype=torch.float32, device=dev)
+
+    def k_offsets():
+        sp.sp_csr_offsets_from_lengths(m, lengths, ro)
+
+    def k_swizzle():
+        sp.sp_row_swizzle(m, ro, ri)
+
+    def k_spmm():
+        sp.sp_spmm(m, k, n, nnz, ri, vals, ro, cols, b, c)
+
+    def k_sddmm():
+        sp.sp_sddmm(m, k, d, nnz, ri, ro, cols, x, y, 1.0, out)
+
+    def step():
+        k_offsets()
+        k_swizzle()
+        k_spmm()
+        k_sddmm()
+
+    if args.profile_launches:
+        step()
+        torch.cuda.synchronize()
+        for fn in (k_offsets, k_swizzle, k_spmm, k_sddmm):
+            for _ in range(args.profile_launches):
+                fn()
+        # a plain copy of known size, to calibrate the byte counters
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(args.profile_launches):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("profile launches done")
+        return 0
+
+    def capture(fn, reps):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        return g
+
+    # ---- the timed steps: W warmup steps, then exactly K steps
+    g_warm = capture(step, max(args.warmup, 1))
+    g_steps = capture(step, args.steps)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g_steps.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+    flops_step = 2.0 * nnz * n + 2.0 * nnz * d
+    gflops = flops_step / (ms_per_step * 1e-3) / 1e9
+    log(f"step: {ms_per_step * 1e3:.2f} us  {gflops:.1f} GFLOP/s")
+
+    # ---- per-kernel average launch duration: R back-to-back launches in a
+    # graph on the stream the kernels run on, bracketed by events
+    kernel_us = {}
+    for name, fn in (("csr_offsets_from_lengths", k_offsets), ("row_swizzle", k_swizzle),
+                     ("spmm", k_spmm), ("sddmm", k_sddmm)):
+        g = capture(fn, args.kernel_reps)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        kernel_us[name] = e0.elapsed_time(e1) * 1e3 / args.kernel_reps
+        log(f"kernel {name}: {kernel_us[name]:.2f} us")
+
+    sb = spmm_bytes(m, k, n, nnz)
+    db = sddmm_bytes(m, k, d, nnz)
+    spmm_s = kernel_us["spmm"] * 1e-6
+    sddmm_s = kernel_us["sddmm"] * 1e-6
+    kernels = {
+        "spmm": {"avg_us": kernel_us["spmm"],
+                 "gflops": 2.0 * nnz * n / spmm_s / 1e9,
+                 "compulsory_gbs": sb / spmm_s / 1e9,
+                 "gather_gbs": 4.0 * nnz * n / spmm_s / 1e9},
+        "sddmm": {"avg_us": kernel_us["sddmm"],
+                  "gflops": 2.0 * nnz * d / sddmm_s / 1e9,
+                  "compulsory_gbs": db / sddmm_s / 1e9,
+                  "gather_gbs": 4.0 * nnz * d / sddmm_s / 1e9},
+        "row_swizzle": {"avg_us": kernel_us["row_swizzle"]},
+        "csr_offsets_from_lengths": {"avg_us": kernel_us["csr_offsets_from_lengths"]},
+    }
+    for kk in ("spmm", "sddmm"):
+        kernels[kk]["frac_fp32_fma_peak"] = kernels[kk]["gflops"] / (FP32_FMA_PEAK_TFLOPS * 1e3)
+    achieved = kernels["spmm"]["compulsory_gbs"]
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_record(),
+                "kernel": "spmm", "algorithmic_bytes_per_launch": sb,
+                "avg_launch_us": kernel_us["spmm"]}
+
+    result = {
+        "metric": METRIC, "value": gflops, "unit": "GFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded numpy PCG64, seed 0)",
+        "config": {"workload": w["name"], "m": m, "k": k, "n": n, "d": d, "nnz": nnz,
+                   "sparsity": stats["sparsity"], "mean_row_length": stats["mean_row_length"],
+                   "row_length_cov": stats["row_length_cov"],
+                   "step": "csr_offsets_from_lengths + row_swizzle + spmm + sddmm",
+                   "launch": "HIP graph of the K steps", "flops_per_step": flops_step},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+
+    # ---- CPU baseline: the oracle on this host, same inputs, one thread
+    if not args.no_cpu_baseline:
+        import oracle
+        torch.cuda.synchronize()
+        c_gpu = c.cpu().numpy()
+        out_gpu = out.cpu().numpy()
+        ro_gpu = ro.cpu().numpy()
+        ri_gpu = ri.cpu().numpy()
+        reps = 0
+        t0 = time.perf_counter()
+        cpu0 = time.process_time()
+        while True:
+            ro_o = oracle.csr_offsets_from_lengths(a.lengths)
+            ri_o = oracle.row_swizzle(ro_o)
+            c_o, c_abs = oracle.spmm(m, k, n, ro_o, a.cols, a.values, w["b"])
+            s_o, s_abs = oracle.sddmm(m, k, d, ro_o, a.cols, w["x"], w["y"])
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        wall = time.perf_counter() - t0
+        cpu_used = time.process_time() - cpu0
+        per_step = wall / reps
+        result["cpu_baseline"] = {
+            "value": flops_step / per_step / 1e9, "unit": "GFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"the full step (offsets, swizzle, SpMM, SDDMM) on the same "
+                       f"workload, repeated {reps} times in {wall:.1f} s "
+                       f"({cpu_used:.1f} s CPU); single-threaded C, double accumulation"),
+            "ms_per_step": per_step * 1e3, **host_info()}
+        with np.errstate(divide="ignore", invalid="ignore"):
+            spmm_ratio = float(np.max(np.abs(c_gpu - c_o) / (1e-5 * c_abs)))
+            sddmm_ratio = float(np.max(np.abs(out_gpu - s_o) / (1e-5 * s_abs)))
+        result["parity"] = {
+            "row_offsets_bit_exact": bool(np.array_equal(ro_gpu, ro_o)),
+            "row_swizzle_bit_exact": bool(np.array_equal(ri_gpu, ri_o)),
+            "spmm_max_err_over_bound": spmm_ratio,
+            "sddmm_max_err_over_bound": sddmm_ratio}
+        log(f"cpu baseline: {result['cpu_baseline']['value']:.3f} GFLOP/s; "
+            f"parity {result['parity']}")
+
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

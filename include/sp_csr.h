@@ -1,0 +1,182 @@
+/*
+ * sp_csr.h -- unstructured-sparse CSR kernels for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels: CSR build, row swizzle, SpMM and
+ * SDDMM.  What the operations compute follows the summary card of "Sparse GPU
+ * Kernels for Deep Learning" (Gale, Zaharia, Young, Elsen; SC 2020); each entry
+ * point names the passage it implements.  The card prints no formula; the
+ * operations are the textbook definitions of the named kernels.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array argument is a DEVICE pointer (memory the caller got
+ * from hipMalloc or an allocator on top of it, e.g. a torch tensor).  The
+ * library never allocates, frees or retains caller memory, keeps no mutable
+ * global state, and is safe to call from several host threads at once.
+ * Outputs must not overlap inputs.
+ *
+ * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Every call
+ * only enqueues work on `stream` and returns without synchronising.  The
+ * library records no hipMemsetAsync, so calls may be captured in HIP graphs.
+ *
+ * CSR.  Standard CSR with int32 indices and fp32 values: an m x k matrix with
+ * nnz entries has row_offsets[m+1] (row_offsets[0] = 0, non-decreasing,
+ * row_offsets[m] = nnz), col_indices[nnz] (in [0, k), strictly increasing
+ * within a row) and values[nnz].  These are preconditions, documented and not
+ * checked on the device: a structure that violates them gives unspecified
+ * results and may make the kernels read or write out of bounds.  Dense matrices are
+ * row-major and contiguous.
+ *
+ * Row order.  `row_indices` (int32[m], a permutation of 0..m-1, or NULL for
+ * the identity) gives the order in which rows are handed to the GPU's workers:
+ * the r-th work slot handles row row_indices[r].  It changes scheduling only,
+ * never results; sp_row_swizzle computes the balanced order.
+ *
+ * Errors.  Return codes only; nothing is thrown and nothing aborts.  Argument
+ * checks happen on the host before any HIP call: a negative size, a NULL
+ * pointer for a non-empty buffer, or a size beyond int32 indexing returns
+ * SP_ERROR_INVALID_VALUE and enqueues nothing.  A failed launch returns
+ * SP_ERROR_LAUNCH_FAILED.  Alignment is never required: unaligned pointers or
+ * widths that are not multiples of 4 take a scalar-load variant of the same
+ * kernel.
+ */
+#ifndef SP_CSR_H
+#define SP_CSR_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sp_status {
+    SP_SUCCESS = 0,
+    SP_ERROR_INVALID_VALUE = 1,
+    SP_ERROR_NOT_SUPPORTED = 2,
+    SP_ERROR_LAUNCH_FAILED = 3
+} sp_status_t;
+
+/* A hipStream_t, passed as an opaque pointer so this header needs no HIP
+ * header. */
+typedef void *sp_stream_t;
+
+/* Static English description of a status code (never NULL). */
+const char *sp_status_string(sp_status_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int sp_version(void);
+
+/* ------------------------------------------------------------------------
+ * CSR build ("Summary" and "Interesting ideas" I5 of the card: the kernels
+ * work on plain, standard CSR with no structural constraint).
+ * ---------------------------------------------------------------------- */
+
+/* row_offsets[0] = 0 and row_offsets[i+1] = lengths[0] + ... + lengths[i]
+ * (the exclusive prefix sum of the row lengths).
+ *   m            rows, >= 0
+ *   lengths      int32[m], each >= 0, sum <= INT32_MAX (precondition)
+ *   row_offsets  int32[m+1], output; must not overlap lengths
+ * m == 0 writes row_offsets[0] = 0. */
+sp_status_t sp_csr_offsets_from_lengths(int m, const int *lengths,
+                                        int *row_offsets, sp_stream_t stream);
+
+/* First half of building CSR from a dense m x k byte mask (row-major; a
+ * nonzero byte marks a structural entry): writes row_offsets[m+1] for the
+ * mask's rows.  The caller reads row_offsets[m] (= nnz) to size col_indices
+ * and values, then calls sp_csr_fill_dense.
+ *   mask         uint8[m*k]
+ *   row_offsets  int32[m+1], output */
+sp_status_t sp_csr_count_dense(int m, int k, const unsigned char *mask,
+                               int *row_offsets, sp_stream_t stream);
+
+/* Second half: col_indices/values of the mask's entries, rows ascending and
+ * columns ascending within a row.  values[p] takes dense_values at the entry's
+ * position; an explicit zero value at a set mask position stays an entry.
+ *   row_offsets   int32[m+1] as written by sp_csr_count_dense for this mask
+ *   dense_values  fp32[m*k] or NULL (then values is not written and may be NULL)
+ *   col_indices   int32[nnz], output;  values fp32[nnz], output
+ * Both outputs are written only at set mask positions; they must be non-NULL
+ * whenever the mask has an entry (not checked: the host does not know nnz). */
+sp_status_t sp_csr_fill_dense(int m, int k, const unsigned char *mask,
+                              const float *dense_values, const int *row_offsets,
+                              int *col_indices, float *values,
+                              sp_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Row swizzle ("Interesting ideas" I4 of the card: load balancing by
+ * reordering rows, kept separate from how the kernels split their work).
+ * ---------------------------------------------------------------------- */
+
+/* row_indices[r] = the r-th row when rows are ordered by nonzero count,
+ * longest first, rows of equal count by ascending row index (a unique,
+ * deterministic order).
+ *   row_offsets  int32[m+1] (CSR row offsets)
+ *   row_indices  int32[m], output */
+sp_status_t sp_row_swizzle(int m, const int *row_offsets, int *row_indices,
+                           sp_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * SpMM ("Summary" of the card): C = A * B, A sparse in CSR, B dense.
+ * ---------------------------------------------------------------------- */
+
+/* C[i][j] = sum over entries p of row i of values[p] * B[col_indices[p]][j].
+ * C is overwritten (an empty row gives a zero row).
+ *   m, k, n      A is m x k, B is k x n, C is m x n;  nnz = row_offsets[m]
+ *   row_indices  int32[m] row order, or NULL (identity)
+ *   values, row_offsets, col_indices   the CSR of A
+ *   b            fp32[k*n];  c  fp32[m*n], output
+ * Sizes: m, k, n, nnz >= 0 and m*n, k*n < 2^62.  m == 0 or n == 0 enqueues
+ * nothing.  Summation per output element is sequential in entry order, so
+ * results are deterministic run to run. */
+sp_status_t sp_spmm(int m, int k, int n, int nnz, const int *row_indices,
+                    const float *values, const int *row_offsets,
+                    const int *col_indices, const float *b, float *c,
+                    sp_stream_t stream);
+
+/* `batch` independent SpMMs sharing one sparsity structure (row_offsets,
+ * col_indices, row_indices): for z < batch,
+ *   C_z = A_z * B_z, values_z = values + z*stride_values,
+ *   b_z = b + z*stride_b, c_z = c + z*stride_c   (strides in elements).
+ * stride_values or stride_b may be 0 (shared operand); stride_c must be
+ * >= m*n when batch > 1 (outputs may not overlap). */
+sp_status_t sp_spmm_batched(int m, int k, int n, int nnz,
+                            const int *row_indices, const float *values,
+                            const int *row_offsets, const int *col_indices,
+                            const float *b, float *c, int batch,
+                            long long stride_values, long long stride_b,
+                            long long stride_c, sp_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * SDDMM ("Summary" and "Interesting ideas" I3 of the card): the dense product
+ * X * Y^T evaluated only at the entries of a CSR mask, in the specialised form
+ * gradients and sparse attention need -- no element-wise scaling by the
+ * mask's values (the mask has no values here) and the second operand given
+ * transposed, so both operands are read by contiguous rows.
+ * ---------------------------------------------------------------------- */
+
+/* out[p] = alpha * sum over l < d of X[i][l] * Y[col_indices[p]][l], for each
+ * entry p of row i.  out is overwritten.  alpha = 1 is the plain product;
+ * sparse attention passes its 1/sqrt(d) score scale here.
+ *   m, k, d      mask is m x k, X is m x d, Y is k x d;  nnz = row_offsets[m]
+ *   row_indices  int32[m] row order, or NULL (identity)
+ *   row_offsets, col_indices   the mask's CSR structure
+ *   x  fp32[m*d];  y  fp32[k*d];  out  fp32[nnz], output
+ * d == 0 writes zeros.  Deterministic run to run. */
+sp_status_t sp_sddmm(int m, int k, int d, int nnz, const int *row_indices,
+                     const int *row_offsets, const int *col_indices,
+                     const float *x, const float *y, float alpha, float *out,
+                     sp_stream_t stream);
+
+/* `batch` SDDMMs sharing one mask: x_z = x + z*stride_x, y_z = y + z*stride_y,
+ * out_z = out + z*stride_out (elements).  stride_out must be >= nnz when
+ * batch > 1. */
+sp_status_t sp_sddmm_batched(int m, int k, int d, int nnz,
+                             const int *row_indices, const int *row_offsets,
+                             const int *col_indices, const float *x,
+                             const float *y, float alpha, float *out,
+                             int batch, long long stride_x, long long stride_y,
+                             long long stride_out, sp_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SP_CSR_H */

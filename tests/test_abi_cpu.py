@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/sp_csr.h declares, and rejects bad arguments on the host before any
+HIP call.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import torch  # noqa: F401  (load torch's HIP runtime first, as the binding does)
+from unstructured_sparse_linear_csr_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sp_csr.h")
+
+INVALID = binding.SP_ERROR_INVALID_VALUE
+OK = binding.SP_SUCCESS
+NULL = ctypes.c_void_p(None)
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails
+                                 # validation or returns before touching memory
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sp_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from unstructured_sparse_linear_csr_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    declared = _declared_functions()
+    assert len(declared) == 10, declared
+    assert sorted(binding.SIGNATURES) == declared
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings_and_version(lib):
+    for code in range(4):
+        assert binding.status_string(code)
+    assert binding.status_string(99) == "unknown status"
+    assert binding.version() == 10000
+
+
+def test_spmm_validation(lib):
+    f = lib.sp_spmm_batched
+    s = NULL
+    # negative sizes
+    assert f(-1, 4, 4, 0, NULL, NULL, FAKE, NULL, NULL, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, -1, 4, 0, NULL, NULL, FAKE, NULL, NULL, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, -1, 0, NULL, NULL, FAKE, NULL, NULL, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, -1, NULL, NULL, FAKE, NULL, NULL, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, 0, NULL, NULL, FAKE, NULL, NULL, FAKE, -1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, 0, NULL, NULL, FAKE, NULL, NULL, FAKE, 1, -4, 0, 0, s) == INVALID
+    # NULL for a non-empty buffer
+    assert f(4, 4, 4, 8, NULL, FAKE, NULL, FAKE, FAKE, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, 8, NULL, FAKE, FAKE, NULL, FAKE, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, 8, NULL, NULL, FAKE, FAKE, FAKE, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, NULL, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, FAKE, NULL, 1, 0, 0, 0, s) == INVALID
+    # overlapping batched outputs
+    assert f(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 16, 15, s) == INVALID
+    # empty problems succeed without launching anything
+    assert f(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, 1, 0, 0, 0, s) == OK
+    assert f(4, 4, 0, 0, NULL, NULL, NULL, NULL, NULL, NULL, 1, 0, 0, 0, s) == OK
+    assert f(4, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, 0, 0, 0, 0, s) == OK
+    assert lib.sp_spmm(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, s) == OK
+    assert lib.sp_spmm(-2, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, s) == INVALID
+
+
+def test_sddmm_validation(lib):
+    f = lib.sp_sddmm_batched
+    s = NULL
+    assert f(-1, 4, 4, 0, NULL, FAKE, NULL, FAKE, FAKE, 1.0, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, -1, 0, NULL, FAKE, NULL, FAKE, FAKE, 1.0, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, 8, NULL, NULL, FAKE, FAKE, FAKE, 1.0, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, 8, NULL, FAKE, NULL, FAKE, FAKE, 1.0, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, 8, NULL, FAKE, FAKE, NULL, FAKE, 1.0, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, NULL, 1.0, FAKE, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, FAKE, 1.0, NULL, 1, 0, 0, 0, s) == INVALID
+    assert f(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE, 2, 0, 0, 7, s) == INVALID
+    assert f(4, 4, 4, 0, NULL, FAKE, NULL, FAKE, FAKE, 1.0, NULL, 1, 0, 0, 0, s) == OK
+    assert f(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, 1.0, NULL, 1, 0, 0, 0, s) == OK
+    assert lib.sp_sddmm(4, 4, 4, 8, NULL, NULL, FAKE, FAKE, FAKE, 1.0, FAKE, s) == INVALID
+
+
+def test_build_and_swizzle_validation(lib):
+    s = NULL
+    assert lib.sp_csr_offsets_from_lengths(-1, FAKE, FAKE, s) == INVALID
+    assert lib.sp_csr_offsets_from_lengths(3, NULL, FAKE, s) == INVALID
+    assert lib.sp_csr_offsets_from_lengths(3, FAKE, NULL, s) == INVALID
+    assert lib.sp_csr_count_dense(3, -1, FAKE, FAKE, s) == INVALID
+    assert lib.sp_csr_count_dense(3, 3, NULL, FAKE, s) == INVALID
+    assert lib.sp_csr_count_dense(3, 3, FAKE, NULL, s) == INVALID
+    assert lib.sp_csr_fill_dense(3, 3, NULL, NULL, FAKE, FAKE, NULL, s) == INVALID
+    assert lib.sp_csr_fill_dense(3, 3, FAKE, NULL, NULL, FAKE, NULL, s) == INVALID
+    assert lib.sp_csr_fill_dense(-3, 3, FAKE, FAKE, FAKE, FAKE, FAKE, s) == INVALID
+    assert lib.sp_row_swizzle(-1, FAKE, FAKE, s) == INVALID
+    assert lib.sp_row_swizzle(3, NULL, FAKE, s) == INVALID
+    assert lib.sp_row_swizzle(3, FAKE, NULL, s) == INVALID
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libsp_csr.so")
+    with pytest.raises(ImportError):
+        binding.lib()
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "unstructured_sparse_linear_csr_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), fn
+                assert "liboracle" not in text, fn

@@ -1,0 +1,164 @@
+// The C ABI of include/sp_csr.h: argument checks on the host, then kernel
+// launches on the caller's stream.  No allocation, no synchronisation, no
+// global mutable state.
+#include <climits>
+
+#include "../../include/sp_csr.h"
+#include "sp_launch.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+sp_status_t from_hip(hipError_t e)
+{
+    if (e == hipSuccess) return SP_SUCCESS;
+    if (e == hipErrorInvalidConfiguration) return SP_ERROR_NOT_SUPPORTED;
+    return SP_ERROR_LAUNCH_FAILED;
+}
+
+hipStream_t as_stream(sp_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+// A pointer must be non-NULL when the buffer it describes is non-empty.
+bool need(const void *ptr, long long elements) { return elements <= 0 || ptr != nullptr; }
+
+}  // namespace
+
+extern "C" {
+
+const char *sp_status_string(sp_status_t status)
+{
+    switch (status) {
+    case SP_SUCCESS: return "success";
+    case SP_ERROR_INVALID_VALUE: return "invalid argument";
+    case SP_ERROR_NOT_SUPPORTED: return "problem size not supported by this build";
+    case SP_ERROR_LAUNCH_FAILED: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int sp_version(void) { return kVersion; }
+
+sp_status_t sp_csr_offsets_from_lengths(int m, const int *lengths, int *row_offsets,
+                                        sp_stream_t stream)
+{
+    if (m < 0 || !need(lengths, m) || row_offsets == nullptr)
+        return SP_ERROR_INVALID_VALUE;
+    return from_hip(spk::launch_offsets_from_lengths(m, lengths, row_offsets,
+                                                     as_stream(stream)));
+}
+
+sp_status_t sp_csr_count_dense(int m, int k, const unsigned char *mask,
+                               int *row_offsets, sp_stream_t stream)
+{
+    if (m < 0 || k < 0 || !need(mask, (long long)m * k) || row_offsets == nullptr)
+        return SP_ERROR_INVALID_VALUE;
+    return from_hip(spk::launch_count_dense(m, k, mask, row_offsets, as_stream(stream)));
+}
+
+sp_status_t sp_csr_fill_dense(int m, int k, const unsigned char *mask,
+                              const float *dense_values, const int *row_offsets,
+                              int *col_indices, float *values, sp_stream_t stream)
+{
+    // col_indices (and values, when dense_values is given) are written only at
+    // the mask's set positions, so they may be NULL for a mask with none; the
+    // host cannot know nnz without reading the device, so that is left to the
+    // caller (documented precondition).
+    if (m < 0 || k < 0 || !need(mask, (long long)m * k) || !need(row_offsets, m))
+        return SP_ERROR_INVALID_VALUE;
+    return from_hip(spk::launch_fill_dense(m, k, mask, dense_values, row_offsets,
+                                           col_indices, values, as_stream(stream)));
+}
+
+sp_status_t sp_row_swizzle(int m, const int *row_offsets, int *row_indices,
+                           sp_stream_t stream)
+{
+    if (m < 0 || !need(row_offsets, m) || !need(row_indices, m))
+        return SP_ERROR_INVALID_VALUE;
+    return from_hip(spk::launch_row_swizzle(m, row_offsets, row_indices,
+                                            as_stream(stream)));
+}
+
+sp_status_t sp_spmm_batched(int m, int k, int n, int nnz, const int *row_indices,
+                            const float *values, const int *row_offsets,
+                            const int *col_indices, const float *b, float *c,
+                            int batch, long long stride_values, long long stride_b,
+                            long long stride_c, sp_stream_t stream)
+{
+    if (m < 0 || k < 0 || n < 0 || nnz < 0 || batch < 0 || stride_values < 0 ||
+        stride_b < 0 || stride_c < 0)
+        return SP_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0 || batch == 0) return SP_SUCCESS;
+    if (!need(row_offsets, m) || !need(col_indices, nnz) || !need(values, nnz) ||
+        !need(b, nnz > 0 ? (long long)k * n : 0) || c == nullptr)
+        return SP_ERROR_INVALID_VALUE;
+    if (batch > 1 && stride_c < (long long)m * n) return SP_ERROR_INVALID_VALUE;
+    spk::SpmmArgs a;
+    a.m = m;
+    a.k = k;
+    a.n = n;
+    a.nnz = nnz;
+    a.row_indices = row_indices;
+    a.row_offsets = row_offsets;
+    a.col_indices = col_indices;
+    a.values = values;
+    a.b = b;
+    a.c = c;
+    a.batch = batch;
+    a.stride_values = stride_values;
+    a.stride_b = stride_b;
+    a.stride_c = stride_c;
+    return from_hip(spk::launch_spmm(a, as_stream(stream)));
+}
+
+sp_status_t sp_spmm(int m, int k, int n, int nnz, const int *row_indices,
+                    const float *values, const int *row_offsets,
+                    const int *col_indices, const float *b, float *c,
+                    sp_stream_t stream)
+{
+    return sp_spmm_batched(m, k, n, nnz, row_indices, values, row_offsets,
+                           col_indices, b, c, 1, 0, 0, 0, stream);
+}
+
+sp_status_t sp_sddmm_batched(int m, int k, int d, int nnz, const int *row_indices,
+                             const int *row_offsets, const int *col_indices,
+                             const float *x, const float *y, float alpha, float *out,
+                             int batch, long long stride_x, long long stride_y,
+                             long long stride_out, sp_stream_t stream)
+{
+    if (m < 0 || k < 0 || d < 0 || nnz < 0 || batch < 0 || stride_x < 0 ||
+        stride_y < 0 || stride_out < 0)
+        return SP_ERROR_INVALID_VALUE;
+    if (m == 0 || nnz == 0 || batch == 0) return SP_SUCCESS;
+    if (!need(row_offsets, m) || !need(col_indices, nnz) || out == nullptr ||
+        !need(x, (long long)m * d) || !need(y, (long long)k * d))
+        return SP_ERROR_INVALID_VALUE;
+    if (batch > 1 && stride_out < nnz) return SP_ERROR_INVALID_VALUE;
+    spk::SddmmArgs a;
+    a.m = m;
+    a.k = k;
+    a.d = d;
+    a.nnz = nnz;
+    a.row_indices = row_indices;
+    a.row_offsets = row_offsets;
+    a.col_indices = col_indices;
+    a.x = x;
+    a.y = y;
+    a.alpha = alpha;
+    a.out = out;
+    a.batch = batch;
+    a.stride_x = stride_x;
+    a.stride_y = stride_y;
+    a.stride_out = stride_out;
+    return from_hip(spk::launch_sddmm(a, as_stream(stream)));
+}
+
+sp_status_t sp_sddmm(int m, int k, int d, int nnz, const int *row_indices,
+                     const int *row_offsets, const int *col_indices, const float *x,
+                     const float *y, float alpha, float *out, sp_stream_t stream)
+{
+    return sp_sddmm_batched(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y,
+                            alpha, out, 1, 0, 0, 0, stream);
+}
+
+}  // extern "C"

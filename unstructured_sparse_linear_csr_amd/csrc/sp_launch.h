@@ -1,0 +1,47 @@
+// Host-side launchers of the device kernels, called by the C ABI layer after
+// it has validated the arguments.  Each returns the launch's hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace spk {
+
+struct SpmmArgs {
+    int m, k, n, nnz;
+    const int *row_indices;  // NULL = identity order
+    const int *row_offsets;
+    const int *col_indices;
+    const float *values;
+    const float *b;
+    float *c;
+    int batch;
+    long long stride_values, stride_b, stride_c;  // elements
+};
+
+struct SddmmArgs {
+    int m, k, d, nnz;
+    const int *row_indices;  // NULL = identity order
+    const int *row_offsets;
+    const int *col_indices;
+    const float *x;
+    const float *y;
+    float alpha;
+    float *out;
+    int batch;
+    long long stride_x, stride_y, stride_out;  // elements
+};
+
+hipError_t launch_offsets_from_lengths(int m, const int *lengths,
+                                       int *row_offsets, hipStream_t stream);
+hipError_t launch_count_dense(int m, int k, const unsigned char *mask,
+                              int *row_offsets, hipStream_t stream);
+hipError_t launch_fill_dense(int m, int k, const unsigned char *mask,
+                             const float *dense_values, const int *row_offsets,
+                             int *col_indices, float *values, hipStream_t stream);
+hipError_t launch_row_swizzle(int m, const int *row_offsets, int *row_indices,
+                              hipStream_t stream);
+hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream);
+hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream);
+hipError_t launch_fill_zero(float *dst, long long count, hipStream_t stream);
+
+}  // namespace spk
