@@ -56,6 +56,11 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent timing the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakeven", action="store_true",
+                    help="skip the LSTM-sized sparsity sweep against dense GEMM")
+    ap.add_argument("--suite", metavar="JSONL", default=None,
+                    help="also time every workload (warm and cold caches) and "
+                         "write one JSON record per kernel run to this file")
     ap.add_argument("--profile-launches", type=int, default=0,
                     help="only run this many eager launches of each kernel "
                          "(for rocprofv3 counter passes) and exit")
@@ -101,6 +106,209 @@ def traffic_record():
     if rec.get("kernel_source_sha256") != sha:
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def graph_time_us(torch, fn, reps: int) -> float:
+    """Average launch duration of `fn` over `reps` back-to-back launches
+    captured in one HIP graph, timed with events on the launch stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def cold_time_us(torch, fn, flush, reps: int = 10) -> float:
+    """Median duration of single launches of `fn`, each after writing a
+    buffer larger than the chip's caches (so operands come from HBM)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        flush.add_(1.0)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(times))
+
+
+def spmm_record(name, m, k, n, nnz, us, extra=None) -> dict:
+    s = us * 1e-6
+    rec = {"record": "spmm", "workload": name, "m": m, "k": k, "n": n, "nnz": nnz,
+           "us": us, "gflops": 2.0 * nnz * n / s / 1e9,
+           "compulsory_gbs": spmm_bytes(m, k, n, nnz) / s / 1e9,
+           "gather_gbs": 4.0 * nnz * n / s / 1e9}
+    rec["hbm_frac"] = rec["compulsory_gbs"] / HBM_PEAK_GBS
+    rec["fp32_fma_frac"] = rec["gflops"] / (FP32_FMA_PEAK_TFLOPS * 1e3)
+    if extra:
+        rec.update(extra)
+    return rec
+
+
+def upload_csr(torch, sp, dev, rl):
+    """Device CSR of row lists: lengths, columns and values uploaded, offsets
+    and the swizzled row order computed on the device."""
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    lengths, cols, vals = up(rl.lengths), up(rl.cols), up(rl.values)
+    ro = torch.empty(rl.m + 1, dtype=torch.int32, device=dev)
+    sp.sp_csr_offsets_from_lengths(rl.m, lengths, ro)
+    ri = torch.empty(rl.m, dtype=torch.int32, device=dev)
+    sp.sp_row_swizzle(rl.m, ro, ri)
+    return ro, ri, cols, vals
+
+
+def lstm_breakeven(torch, sp, inputs, dev, reps=50, records=None, flush=None):
+    """SpMM time at each LSTM-sized sparsity next to a dense fp32 GEMM of the
+    same shape; the break-even sparsity is where t_sparse / t_dense crosses 1,
+    interpolated linearly between sweep points."""
+    torch.backends.cuda.matmul.allow_tf32 = False
+    torch.set_float32_matmul_precision("highest")
+    times = {}
+    dense_us = None
+    for s in inputs.LSTM_SPARSITIES:
+        w = inputs.lstm(s)
+        a = w["a"]
+        m, k, n = w["m"], w["k"], w["n"]
+        ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+        b = torch.from_numpy(w["b"]).to(dev)
+        c = torch.empty(m, n, device=dev)
+        fn = lambda: sp.sp_spmm(m, k, n, a.nnz, ri, vals, ro, cols, b, c)
+        times[s] = graph_time_us(torch, fn, reps)
+        if records is not None:
+            cold = cold_time_us(torch, fn, flush) if flush is not None else None
+            records.append(spmm_record(w["name"], m, k, n, a.nnz, times[s],
+                                       {"sparsity": s, "cold_us": cold}))
+        if dense_us is None:
+            # The dense operand of the comparison: A with every entry present.
+            dense_a = torch.from_numpy(inputs.random_dense(5, m, k, std=0.02)).to(dev)
+            dfn = lambda: torch.mm(dense_a, b, out=c)
+            dense_us = graph_time_us(torch, dfn, reps)
+            if records is not None:
+                records.append({"record": "dense_gemm", "workload": "lstm_8192x2048x128_dense",
+                                "m": m, "k": k, "n": n, "us": dense_us,
+                                "gflops": 2.0 * m * k * n / (dense_us * 1e-6) / 1e9,
+                                "precision": "fp32 (TF32 off, matmul precision 'highest')"})
+        log(f"lstm s={s}: spmm {times[s]:.2f} us (dense {dense_us:.2f} us)")
+    ratio = {s: t / dense_us for s, t in times.items()}
+    sps = sorted(ratio)
+    breakeven = None
+    for lo, hi in zip(sps, sps[1:]):
+        if (ratio[lo] - 1.0) * (ratio[hi] - 1.0) <= 0 and ratio[lo] != ratio[hi]:
+            breakeven = lo + (1.0 - ratio[lo]) * (hi - lo) / (ratio[hi] - ratio[lo])
+            break
+    return {"dense_fp32_gemm_us": dense_us, "spmm_us": {str(s): t for s, t in times.items()},
+            "sparse_over_dense": {str(s): r for s, r in ratio.items()},
+            "breakeven_sparsity": breakeven,
+            "note": ("sparsity where SpMM time equals dense fp32 GEMM time, "
+                     "linearly interpolated; null if the sweep has no crossing")}
+
+
+def run_suite(torch, sp, inputs, dev, path: str) -> None:
+    """Every workload, warm (graph back-to-back) and cold (after flushing the
+    caches), one JSON record per kernel run."""
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB > caches
+    flush.zero_()
+    recs = []
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    # Transformer FFN SpMM + SDDMM, and the lognormal imbalance variant with
+    # and without the swizzled row order.
+    for w in (inputs.transformer_ffn(), inputs.imbalance()):
+        a = w["a"]
+        m, k, n, d = w["m"], w["k"], w["n"], w["d"]
+        ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+        b, x, y = up(w["b"]), up(w["x"]), up(w["y"])
+        c = torch.empty(m, n, device=dev)
+        out = torch.empty(a.nnz, device=dev)
+        for swz in (True, False):
+            order = ri if swz else None
+            fn = lambda: sp.sp_spmm(m, k, n, a.nnz, order, vals, ro, cols, b, c)
+            recs.append(spmm_record(w["name"], m, k, n, a.nnz, graph_time_us(torch, fn, 200),
+                                    {"swizzle": swz, "cold_us": cold_time_us(torch, fn, flush)}))
+            sfn = lambda: sp.sp_sddmm(m, k, d, a.nnz, order, ro, cols, x, y, 1.0, out)
+            us = graph_time_us(torch, sfn, 200)
+            recs.append({"record": "sddmm", "workload": w["name"], "m": m, "k": k, "d": d,
+                         "nnz": a.nnz, "swizzle": swz, "us": us,
+                         "cold_us": cold_time_us(torch, sfn, flush),
+                         "gflops": 2.0 * a.nnz * d / (us * 1e-6) / 1e9,
+                         "compulsory_gbs": sddmm_bytes(m, k, d, a.nnz) / (us * 1e-6) / 1e9})
+        recs.append({"record": "row_swizzle", "workload": w["name"], "m": m,
+                     "us": graph_time_us(torch, lambda: sp.sp_row_swizzle(m, ro, ri), 200)})
+    # ResNet-50 1x1 conv
+    w = inputs.resnet_1x1()
+    a = w["a"]
+    ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+    b = up(w["b"])
+    c = torch.empty(w["m"], w["n"], device=dev)
+    fn = lambda: sp.sp_spmm(w["m"], w["k"], w["n"], a.nnz, ri, vals, ro, cols, b, c)
+    recs.append(spmm_record(w["name"], w["m"], w["k"], w["n"], a.nnz, graph_time_us(torch, fn, 50),
+                            {"cold_us": cold_time_us(torch, fn, flush)}))
+    # LSTM sweep with the dense comparison
+    be = lstm_breakeven(torch, sp, inputs, dev, records=recs, flush=flush)
+    recs.append({"record": "breakeven", **be})
+    # Sparse attention: batched SDDMM (scores, scale 1/8) and batched SpMM
+    # (P V) over one shared mask; the host softmax between them is not timed.
+    w = inputs.sparse_attention()
+    bh, seq, hd = w["batch"], w["seq"], w["head_dim"]
+    mk = up(w["mask"])
+    ro = torch.empty(seq + 1, dtype=torch.int32, device=dev)
+    sp.sp_csr_count_dense(seq, seq, mk, ro)
+    nnz = int(ro[seq].item())
+    cols = torch.empty(nnz, dtype=torch.int32, device=dev)
+    sp.sp_csr_fill_dense(seq, seq, mk, None, ro, cols, None)
+    ri = torch.empty(seq, dtype=torch.int32, device=dev)
+    sp.sp_row_swizzle(seq, ro, ri)
+    q, kk, v = up(w["q"]), up(w["k"]), up(w["v"])
+    s_out = torch.empty(bh, nnz, device=dev)
+    p_vals = torch.full((bh, nnz), 1.0 / 80.0, device=dev)
+    o = torch.empty(bh, seq, hd, device=dev)
+    sfn = lambda: sp.sp_sddmm_batched(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125, s_out,
+                                      bh, seq * hd, seq * hd, nnz)
+    pfn = lambda: sp.sp_spmm_batched(seq, seq, hd, nnz, ri, p_vals, ro, cols, v, o, bh,
+                                     nnz, seq * hd, seq * hd)
+    for kind, fn in (("sddmm_batched", sfn), ("spmm_batched", pfn)):
+        us = graph_time_us(torch, fn, 20)
+        flops = 2.0 * bh * nnz * hd
+        byts = bh * (sddmm_bytes(seq, seq, hd, nnz) if kind.startswith("sddmm")
+                     else spmm_bytes(seq, seq, hd, nnz))
+        recs.append({"record": kind, "workload": w["name"], "batch": bh, "seq": seq,
+                     "head_dim": hd, "nnz_per_head": nnz, "us": us,
+                     "cold_us": cold_time_us(torch, fn, flush),
+                     "gflops": flops / (us * 1e-6) / 1e9,
+                     "compulsory_gbs": byts / (us * 1e-6) / 1e9})
+    # The streaming regime: CSR far larger than every cache, n = 8
+    w = inputs.hbm_stream()
+    a = w["a"]
+    ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+    b = up(w["b"])
+    c = torch.empty(w["m"], w["n"], device=dev)
+    fn = lambda: sp.sp_spmm(w["m"], w["k"], w["n"], a.nnz, ri, vals, ro, cols, b, c)
+    recs.append(spmm_record(w["name"], w["m"], w["k"], w["n"], a.nnz,
+                            graph_time_us(torch, fn, 20),
+                            {"cold_us": cold_time_us(torch, fn, flush),
+                             "csr_bytes": 8 * a.nnz}))
+    with open(path, "w") as f:
+        for r in recs:
+            f.write(json.dumps(r) + "\n")
+    for r in recs:
+        log(json.dumps({kk: (round(vv, 3) if isinstance(vv, float) else vv)
+                        for kk, vv in r.items() if not isinstance(vv, dict)}))
 
 
 def main() -> int:
@@ -252,6 +460,12 @@ def main() -> int:
         "roofline": roofline,
         "kernels": kernels,
     }
+
+    if not args.no_breakeven:
+        result["breakeven"] = lstm_breakeven(torch, sp, inputs, dev)
+
+    if args.suite:
+        run_suite(torch, sp, inputs, dev, args.suite)
 
     # ---- CPU baseline: the oracle on this host, same inputs, one thread
     if not args.no_cpu_baseline:

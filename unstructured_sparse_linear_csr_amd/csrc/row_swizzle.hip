@@ -3,14 +3,15 @@
 // ideas" I4: load balancing by reordering rows, independent of how the
 // kernels split their work).
 //
-// Order: longest row first; rows of equal length by ascending row index.  The
-// kernel is a stable rank sort: row i goes to slot
-//   rank(i) = #{j : len_j > len_i} + #{j < i : len_j == len_i},
-// which is a bijection onto 0..m-1 and needs no workspace and no atomics, so
-// the order is deterministic and identical to any stable descending sort.
-// Cost is m^2 comparisons, served from LDS as broadcast reads four lengths at
-// a time; it runs once per sparsity structure and is reused by every SpMM and
-// SDDMM on that structure.
+// Order: longest row first; rows of equal length by ascending row index.  Each
+// row gets the unique 64-bit key (length << 32) | (2^32 - 1 - row), so the
+// wanted order is descending key order and a row's slot is its rank
+//   rank(i) = #{j : key_j > key_i},
+// a bijection onto 0..m-1 that needs no workspace and no atomics: the order is
+// deterministic and identical to any stable descending sort by length.  Cost
+// is m^2 64-bit comparisons, served from LDS as broadcast reads; the pass runs
+// once per sparsity structure and its order is reused by every SpMM and SDDMM
+// on that structure.
 #include "sp_device.h"
 #include "sp_launch.h"
 
@@ -19,40 +20,66 @@ namespace spk {
 namespace {
 
 constexpr int kSwizzleThreads = 256;
-constexpr int kSwizzleTile = 4096;  // lengths staged in LDS per pass (16 KB)
+constexpr int kLanesPerRow = 16;  // lanes sharing one row's comparisons
+constexpr int kRowsPerBlock = kSwizzleThreads / kLanesPerRow;
+constexpr int kSwizzleTile = 2048;  // keys staged in LDS per pass (16 KB)
 
+__device__ __forceinline__ unsigned long long row_key(int length, int row)
+{
+    return ((unsigned long long)(unsigned)length << 32) | (unsigned)(0xFFFFFFFFu - (unsigned)row);
+}
+
+// Each row's rank is counted by kLanesPerRow lanes, each taking every
+// kLanesPerRow-th pair of staged keys; the partial counts are summed across
+// the lanes (integer sums, so the order does not matter).  Lanes of a wave
+// that read the same pair read the same LDS address (a broadcast), and the
+// 16 pairs a wave reads at once are contiguous.  Padding slots hold key 0,
+// which is below every real key.
 __global__ __launch_bounds__(kSwizzleThreads) void row_swizzle_kernel(
     int m, const int *__restrict__ row_offsets, int *__restrict__ row_indices)
 {
-    __shared__ int4 s_len4[kSwizzleTile / 4];
-    const int i = blockIdx.x * kSwizzleThreads + threadIdx.x;
+    __shared__ __align__(16) unsigned long long s_key[kSwizzleTile];
+    const int t = threadIdx.x;
+    const int sub = t % kLanesPerRow;
+    const int i = blockIdx.x * kRowsPerBlock + t / kLanesPerRow;
     const bool mine = i < m;
-    const int len_i = mine ? row_offsets[i + 1] - row_offsets[i] : 0;
+    const unsigned long long key_i =
+        mine ? row_key(row_offsets[i + 1] - row_offsets[i], i) : ~0ull;
     int rank = 0;
     for (int t0 = 0; t0 < m; t0 += kSwizzleTile) {
         const int cnt = min(kSwizzleTile, m - t0);
-        for (int j = threadIdx.x; j < kSwizzleTile; j += kSwizzleThreads) {
-            // Padding slots get length -1: never greater than, never equal to,
-            // any real length, so they never count.
-            const int r = t0 + j;
-            reinterpret_cast<int *>(s_len4)[j] =
-                (j < cnt) ? row_offsets[r + 1] - row_offsets[r] : -1;
+        // All of a thread's offset loads are issued before any is used.
+        constexpr int kPer = kSwizzleTile / kSwizzleThreads;
+        int lo[kPer], hi[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int j = t + q * kSwizzleThreads;
+            lo[q] = j < cnt ? row_offsets[t0 + j] : 0;
+            hi[q] = j < cnt ? row_offsets[t0 + j + 1] : 0;
+        }
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int j = t + q * kSwizzleThreads;
+            s_key[j] = j < cnt ? row_key(hi[q] - lo[q], t0 + j) : 0ull;
         }
         __syncthreads();
-        if (mine) {
-            const int groups = (cnt + 3) / 4;
-            for (int g = 0; g < groups; ++g) {
-                const int4 l4 = s_len4[g];
-                const int j = t0 + 4 * g;
-                rank += (l4.x > len_i) | ((l4.x == len_i) & (j + 0 < i));
-                rank += (l4.y > len_i) | ((l4.y == len_i) & (j + 1 < i));
-                rank += (l4.z > len_i) | ((l4.z == len_i) & (j + 2 < i));
-                rank += (l4.w > len_i) | ((l4.w == len_i) & (j + 3 < i));
-            }
+        // Eight independent LDS reads in flight per lane.  The tile's padding
+        // keys are 0, so reading whole groups of eight past cnt is harmless.
+        constexpr int kStep = kLanesPerRow * 8;
+        const int pairs = min(kSwizzleTile / 2, ((cnt + 1) / 2 + kStep - 1) / kStep * kStep);
+        const ulonglong2 *keys2 = reinterpret_cast<const ulonglong2 *>(s_key);
+        for (int g0 = sub; g0 < pairs; g0 += kStep) {
+            ulonglong2 k2[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) k2[u] = keys2[g0 + u * kLanesPerRow];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) rank += (k2[u].x > key_i) + (k2[u].y > key_i);
         }
         __syncthreads();
     }
-    if (mine) row_indices[rank] = i;
+#pragma unroll
+    for (int off = 1; off < kLanesPerRow; off <<= 1) rank += __shfl_xor(rank, off);
+    if (mine && sub == 0) row_indices[rank] = i;
 }
 
 }  // namespace
@@ -61,7 +88,7 @@ hipError_t launch_row_swizzle(int m, const int *row_offsets, int *row_indices,
                               hipStream_t stream)
 {
     if (m == 0) return hipSuccess;
-    const int blocks = (m + kSwizzleThreads - 1) / kSwizzleThreads;
+    const int blocks = (m + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL(row_swizzle_kernel, dim3(blocks), dim3(kSwizzleThreads),
                        0, stream, m, row_offsets, row_indices);
     return hipGetLastError();

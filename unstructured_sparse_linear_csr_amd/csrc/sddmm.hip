@@ -32,13 +32,14 @@ namespace spk {
 namespace {
 
 struct SddmmParams {
-    int m, d, nnz;
+    int m, d, nnz, batch;
     const int *row_indices;
     const int *row_offsets;
     const int *col_indices;
     const float *x;
     const float *y;
     float alpha;
+    unsigned y_bytes;  // bytes of one Y operand (buffer path)
     float *out;
     long long stride_x, stride_y, stride_out;
 };
@@ -64,23 +65,51 @@ template <> struct DVec<1> {
     }
 };
 
-// kNv > 0: the lane's kNv vectors of the X row live in registers.
-// kNv == 0: any d; X and Y are both read from memory in a loop over d.
-template <int kG, int kNv, int kVec, bool kOff32>
+#ifndef SP_SDDMM_LOADS_PER_BATCH
+#define SP_SDDMM_LOADS_PER_BATCH 8
+#endif
+constexpr unsigned kOutOfRange = 0x80000000u;  // buffer offset that reads as zero
+
+template <int kVec> __device__ __forceinline__ typename DVec<kVec>::T
+buf_load(__amdgpu_buffer_rsrc_t r, unsigned off);
+template <> __device__ __forceinline__ float4 buf_load<4>(__amdgpu_buffer_rsrc_t r, unsigned off)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                       __uint_as_float(v[3]));
+}
+template <> __device__ __forceinline__ float buf_load<1>(__amdgpu_buffer_rsrc_t r, unsigned off)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+// kNv > 0 (Y < 2 GiB): the lane's kNv vectors of the X row live in registers;
+// Y rows are gathered through a buffer resource, and window slots past the
+// row's end carry an out-of-range offset that reads as zeros, so steps are
+// issued in unconditional double-buffered batches of kU.
+// kNv == 0: any d and any Y size; X and Y are read with 64-bit addresses in a
+// loop over d, one step at a time.
+template <int kG, int kNv, int kVec>
 __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
 {
     using V = DVec<kVec>;
     using VecT = typename V::T;
-    constexpr int kNg = kWave / kG;                          // entries per step
-    constexpr int kU = kNv == 0 ? 1 : (kNv >= 8 ? 1 : 8 / kNv);  // steps in flight
+    constexpr int kNg = kWave / kG;  // entries per step
+    constexpr int kU = kNv == 0 ? 1
+                                : (SP_SDDMM_LOADS_PER_BATCH / kNv > 0 ? SP_SDDMM_LOADS_PER_BATCH / kNv : 1);
     constexpr int kXv = kNv == 0 ? 1 : kNv;
-    __shared__ int s_off[kWave];
+    // The window's 64 entries, then padding for the prefetch of up to two
+    // batches past the last step.
+    constexpr int kSlots = kWave + 2 * kU * kNg;
+    __shared__ unsigned s_off[kSlots];
 
+    const long long w = xcd_work_index(p.batch, p.m);
+    if (w < 0) return;
+    const long long z = w / p.m;
+    const int slot = (int)(w - z * p.m);
     const int lane = threadIdx.x;
     const int g = lane / kG;
     const int gl = lane - g * kG;
-    const int slot = blockIdx.x;
-    const long long z = blockIdx.y;
     const int row = p.row_indices ? p.row_indices[slot] : slot;
     const int p0 = p.row_offsets[row];
     const int p1 = p.row_offsets[row + 1];
@@ -90,78 +119,90 @@ __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
     const float *__restrict__ yz = p.y + z * p.stride_y;
     float *__restrict__ oz = p.out + z * p.stride_out;
 
-    auto offset_of = [&](int col) -> int {
-        if constexpr (kOff32)
-            return (int)((unsigned)col * (unsigned)p.d * 4u);
-        else
-            return col;
-    };
-    auto load_y = [&](int off, int e) -> VecT {
-        if constexpr (kOff32)
-            return *reinterpret_cast<const VecT *>(
-                reinterpret_cast<const char *>(yz) + ((unsigned)off + (unsigned)e * 4u));
-        else
-            return *reinterpret_cast<const VecT *>(yz + (size_t)off * (size_t)p.d + e);
-    };
-
-    VecT xr[kXv];
-    if constexpr (kNv > 0) {
+    if constexpr (kNv == 0) {
+        __shared__ int s_col[kWave];
+        for (int base = p0; base < p1; base += kWave) {
+            const int cnt = min(kWave, p1 - base);
+            s_col[lane] = lane < cnt ? p.col_indices[base + lane] : 0;
+            __syncthreads();
+            const int steps = (cnt + kNg - 1) / kNg;
+            float res = 0.f;
+            for (int s = 0; s < steps; ++s) {
+                const int j = s * kNg + g;
+                float acc = 0.f;
+                if (j < cnt) {
+                    const float *yr = yz + (size_t)s_col[j] * (size_t)p.d;
+                    for (int e = gl * kVec; e < p.d; e += kG * kVec)
+                        acc = V::dot(*reinterpret_cast<const VecT *>(xr_ptr + e),
+                                     *reinterpret_cast<const VecT *>(yr + e), acc);
+                }
+                const float sum = group_sum<kG>(acc);
+                if (gl == s) res = sum;
+            }
+            const int jo = gl * kNg + g;
+            if (jo < cnt) oz[base + jo] = p.alpha * res;
+            __syncthreads();
+        }
+    } else {
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(yz), 0, (int)p.y_bytes, 0x00020000);
+        VecT xr[kXv];
+        unsigned lane_off[kXv];
 #pragma unroll
         for (int v = 0; v < kNv; ++v) {
             const int e = (v * kG + gl) * kVec;
             xr[v] = e < p.d ? *reinterpret_cast<const VecT *>(xr_ptr + e) : V::zero();
+            lane_off[v] = e < p.d ? (unsigned)e * 4u : kOutOfRange;
         }
-    }
+        for (int t = kWave + lane; t < kSlots; t += kWave) s_off[t] = kOutOfRange;
 
-    for (int base = p0; base < p1; base += kWave) {
-        const int cnt = min(kWave, p1 - base);
-        s_off[lane] = lane < cnt ? offset_of(p.col_indices[base + lane]) : 0;
-        __syncthreads();
-        const int steps = (cnt + kNg - 1) / kNg;
-        float res = 0.f;
-        for (int s0 = 0; s0 < steps; s0 += kU) {
-            float part[kU];
-            if constexpr (kNv > 0) {
-                VecT yv[kU][kNv];
-#pragma unroll
-                for (int u = 0; u < kU; ++u) {
-                    const int j = (s0 + u) * kNg + g;
-                    const bool valid = (s0 + u < steps) && (j < cnt);
-                    const int off = s_off[valid ? j : 0];
-#pragma unroll
-                    for (int v = 0; v < kNv; ++v) {
-                        const int e = (v * kG + gl) * kVec;
-                        yv[u][v] = (valid && e < p.d) ? load_y(off, e) : V::zero();
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < kU; ++u) {
-                    float acc = 0.f;
-#pragma unroll
-                    for (int v = 0; v < kNv; ++v) acc = V::dot(xr[v], yv[u][v], acc);
-                    part[u] = acc;
-                }
-            } else {
-                const int j = s0 * kNg + g;
-                const bool valid = j < cnt;
-                const int off = s_off[valid ? j : 0];
-                float acc = 0.f;
-                if (valid) {
-                    for (int e = gl * kVec; e < p.d; e += kG * kVec)
-                        acc = V::dot(*reinterpret_cast<const VecT *>(xr_ptr + e),
-                                     load_y(off, e), acc);
-                }
-                part[0] = acc;
-            }
+        auto load_batch = [&](int s0, VecT (&yv)[kU][kXv]) {
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
-                const float sum = group_sum<kG>(part[u]);
+                const unsigned off = s_off[(s0 + u) * kNg + g];
+#pragma unroll
+                for (int v = 0; v < kNv; ++v) yv[u][v] = buf_load<kVec>(rsrc, off + lane_off[v]);
+            }
+        };
+        auto reduce_batch = [&](int s0, const VecT (&yv)[kU][kXv], float &res) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                float acc = 0.f;
+#pragma unroll
+                for (int v = 0; v < kNv; ++v) acc = V::dot(xr[v], yv[u][v], acc);
+                const float sum = group_sum<kG>(acc);
                 if (gl == s0 + u) res = sum;
             }
+        };
+
+        for (int base = p0; base < p1; base += kWave) {
+            const int cnt = min(kWave, p1 - base);
+            s_off[lane] = lane < cnt
+                              ? (unsigned)p.col_indices[base + lane] * (unsigned)p.d * 4u
+                              : kOutOfRange;
+            __syncthreads();
+            const int steps = (cnt + kNg - 1) / kNg;
+            float res = 0.f;
+            // A window has at most kG steps, so its batches are unrolled into
+            // straight-line code (exact wait counts: no loop back edge).
+            constexpr int kBatches = (kG + kU - 1) / kU;
+            VecT ya[kU][kXv], yb[kU][kXv];
+            load_batch(0, ya);
+#pragma unroll
+            for (int bt = 0; bt < kBatches; bt += 2) {
+                if (bt * kU >= steps) break;
+                load_batch((bt + 1) * kU, yb);
+                keep_issued_above();
+                reduce_batch(bt * kU, ya, res);
+                if ((bt + 1) * kU >= steps) break;
+                load_batch((bt + 2) * kU, ya);
+                keep_issued_above();
+                reduce_batch((bt + 1) * kU, yb, res);
+            }
+            const int jo = gl * kNg + g;  // the entry whose sum this lane kept
+            if (jo < cnt) oz[base + jo] = p.alpha * res;
+            __syncthreads();
         }
-        const int jo = gl * kNg + g;  // the entry whose sum this lane kept
-        if (jo < cnt) oz[base + jo] = p.alpha * res;
-        __syncthreads();
     }
 }
 
@@ -175,36 +216,33 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *dst, long long co
 }
 
 template <int kG, int kNv, int kVec>
-hipError_t launch_t(const SddmmParams &p, int batch, bool off32, hipStream_t s)
+hipError_t launch_t(const SddmmParams &p, int batch, hipStream_t s)
 {
-    dim3 grid((unsigned)p.m, (unsigned)batch);
-    if (off32)
-        hipLaunchKernelGGL((sddmm_kernel<kG, kNv, kVec, true>), grid, dim3(kWave), 0, s, p);
-    else
-        hipLaunchKernelGGL((sddmm_kernel<kG, kNv, kVec, false>), grid, dim3(kWave), 0, s, p);
+    (void)batch;
+    dim3 grid((unsigned)xcd_grid(p.batch, p.m));
+    hipLaunchKernelGGL((sddmm_kernel<kG, kNv, kVec>), grid, dim3(kWave), 0, s, p);
     return hipGetLastError();
 }
 
 template <int kG, int kVec>
-hipError_t launch_nv(int nv, const SddmmParams &p, int batch, bool off32, hipStream_t s)
+hipError_t launch_nv(int nv, const SddmmParams &p, int batch, hipStream_t s)
 {
     switch (nv) {
-    case 1: return launch_t<kG, 1, kVec>(p, batch, off32, s);
-    case 2: return launch_t<kG, 2, kVec>(p, batch, off32, s);
-    case 4: return launch_t<kG, 4, kVec>(p, batch, off32, s);
-    case 8: return launch_t<kG, 8, kVec>(p, batch, off32, s);
-    default: return launch_t<kG, 0, kVec>(p, batch, off32, s);
+    case 1: return launch_t<kG, 1, kVec>(p, batch, s);
+    case 2: return launch_t<kG, 2, kVec>(p, batch, s);
+    case 4: return launch_t<kG, 4, kVec>(p, batch, s);
+    case 8: return launch_t<kG, 8, kVec>(p, batch, s);
+    default: return launch_t<kG, 0, kVec>(p, batch, s);
     }
 }
 
 template <int kVec>
-hipError_t launch_g(int g, int nv, const SddmmParams &p, int batch, bool off32,
-                    hipStream_t s)
+hipError_t launch_g(int g, int nv, const SddmmParams &p, int batch, hipStream_t s)
 {
     switch (g) {
-    case 4: return launch_nv<4, kVec>(nv, p, batch, off32, s);
-    case 8: return launch_nv<8, kVec>(nv, p, batch, off32, s);
-    default: return launch_nv<16, kVec>(nv, p, batch, off32, s);
+    case 4: return launch_nv<4, kVec>(nv, p, batch, s);
+    case 8: return launch_nv<8, kVec>(nv, p, batch, s);
+    default: return launch_nv<16, kVec>(nv, p, batch, s);
     }
 }
 
@@ -230,7 +268,7 @@ hipError_t launch_fill_zero(float *dst, long long count, hipStream_t stream)
 hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream)
 {
     if (a.m == 0 || a.nnz == 0) return hipSuccess;
-    if (a.batch > 65535) return hipErrorInvalidConfiguration;
+    if (xcd_grid(a.batch, a.m) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (a.d == 0) {
         const long long blocks = std::min<long long>((a.nnz + 255) / 256, 65536);
         hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks, (unsigned)a.batch),
@@ -239,15 +277,19 @@ hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream)
     }
     const bool vec = (a.d % 4 == 0) && aligned16(a.x) && aligned16(a.y) &&
                      (a.stride_x % 4 == 0) && (a.stride_y % 4 == 0);
-    const bool off32 = (long long)a.k * (long long)a.d < (1LL << 30);
+    // Register-resident X and buffer gathers need valid offsets below Y's size
+    // and padding offsets (>= 2^31) beyond it.
+    const bool buf = (long long)a.k * (long long)a.d <= (1LL << 29);
     const int kvec = vec ? 4 : 1;
     const int dv = (a.d + kvec - 1) / kvec;
     const int g = dv <= 4 ? 4 : dv <= 8 ? 8 : 16;
     const int need = (dv + g - 1) / g;
-    const int nv = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
+    int nv = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
+    if (!buf) nv = 0;
 
     SddmmParams p;
     p.m = a.m;
+    p.batch = a.batch;
     p.d = a.d;
     p.nnz = a.nnz;
     p.row_indices = a.row_indices;
@@ -256,12 +298,13 @@ hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream)
     p.x = a.x;
     p.y = a.y;
     p.alpha = a.alpha;
+    p.y_bytes = buf ? (unsigned)((long long)a.k * a.d * 4) : 0u;
     p.out = a.out;
     p.stride_x = a.stride_x;
     p.stride_y = a.stride_y;
     p.stride_out = a.stride_out;
-    return vec ? launch_g<4>(g, nv, p, a.batch, off32, stream)
-               : launch_g<1>(g, nv, p, a.batch, off32, stream);
+    return vec ? launch_g<4>(g, nv, p, a.batch, stream)
+               : launch_g<1>(g, nv, p, a.batch, stream);
 }
 
 }  // namespace spk

@@ -3,7 +3,7 @@
 // global mutable state.
 #include <climits>
 
-#include "../../include/sp_csr.h"
+#include "sp_csr.h"
 #include "sp_launch.h"
 
 namespace {

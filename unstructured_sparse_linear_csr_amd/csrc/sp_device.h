@@ -41,6 +41,18 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+// Keeps the compiler from moving any instruction across this point (memory
+// operations at the IR level, everything in the machine scheduler).  Used
+// after a batch of prefetch gathers so that they stay issued ahead of the
+// arithmetic on the previous batch: otherwise the scheduler interleaves the
+// two to shorten register lifetimes, the two buffers share registers, and
+// every batch waits for all outstanding gathers.
+__device__ __forceinline__ void keep_issued_above()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Wave-wide inclusive prefix sum of an int (Hillis-Steele over 64 lanes).
 __device__ __forceinline__ int wave_inclusive_sum(int v, int lane)
 {
@@ -50,6 +62,34 @@ __device__ __forceinline__ int wave_inclusive_sum(int v, int lane)
         if (lane >= off) v += up;
     }
     return v;
+}
+
+// Workgroups of a launch are dealt to the chip's 8 XCDs round-robin, and
+// each XCD has its own L2.  A launch whose work splits into `outer` independent
+// units (batch entries times column tiles), each of `inner` row blocks, can
+// keep each unit's operands (a tile's B slice, a batch entry's dense
+// matrices) in one L2 instead of all eight: with outer >= 8, launch slot i is
+// mapped so that each XCD takes one contiguous range of the outer-major work
+// order.  With fewer outer units the identity order is kept: consecutive
+// slots (rows in swizzled order, longest first) then spread over all XCDs,
+// which is what load balance needs.  The mapping only affects locality and
+// balance, never results.
+constexpr int kXcds = 8;
+__host__ __device__ inline bool xcd_remap(long long outer) { return outer >= kXcds; }
+__host__ __device__ inline long long xcd_grid(long long outer, long long inner)
+{
+    const long long units = outer * inner;
+    return xcd_remap(outer) ? (units + kXcds - 1) / kXcds * kXcds : units;
+}
+// The work index of this workgroup, or -1 for a padding slot.
+__device__ __forceinline__ long long xcd_work_index(long long outer, long long inner)
+{
+    const long long units = outer * inner;
+    const long long i = blockIdx.x;
+    if (!xcd_remap(outer)) return i;
+    const long long per = (units + kXcds - 1) / kXcds;
+    const long long w = (i % kXcds) * per + i / kXcds;
+    return w < units ? w : -1;
 }
 
 // Bit mask of the lanes below `lane` (for ballot-based compaction).

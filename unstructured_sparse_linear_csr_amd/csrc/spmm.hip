@@ -9,22 +9,25 @@
 // owns kVec adjacent output columns and keeps their sums in registers, so C is
 // written exactly once, with no atomics and no split over k.
 //
-// Staging.  A group copies its row's (column, value) pairs into LDS one window
-// of 4 * kLpr entries at a time.  On the vector path each lane reads 4 entries
-// with one dwordx4 load of col_indices and one of values, starting from the
-// row's first entry rounded down to a multiple of 4; entries before the row's
-// start (the misaligned prefix) and after its end are staged but skipped.  The
-// first window thus costs at most one extra 16-byte segment per row, and every
-// CSR load is a full aligned vector.
+// Staging.  A group copies its row's (B-row offset, value) pairs into LDS one
+// window of kEpl * kLpr entries at a time.  On the vector path each lane reads
+// 16-byte segments of col_indices and values with dwordx4 loads, starting from
+// the row's first entry rounded down to a multiple of 4; slots before the
+// row's start (the misaligned prefix) or after its end become padding.  A
+// segment that holds no entry of the row is not loaded.
 //
-// Hot loop.  Per staged entry each lane issues one dwordx4 load of its kVec
-// columns of the B row the entry selects, then kVec FMAs.  kUnroll entries are
-// loaded before any is used so that many gathers are in flight per wave.  The
-// staged B-row offset is kept in bytes as a 32-bit value when k*n < 2^30, so
-// the gather is a scalar-base plus 32-bit vector-offset load.
+// Gathers.  B is read through a buffer resource: a padding slot carries an
+// offset beyond the resource's range, for which the hardware returns zeros
+// without touching memory, and its value is 0.  Every gather is therefore
+// unconditional, batches of kU gathers are issued back to back, and the next
+// batch is in flight while the current one is summed (two register buffers).
+// Loop bounds are wave-uniform: a group whose row is done reads padding, so
+// multi-row waves never diverge.  B larger than 2 GiB takes the same kernel
+// with 64-bit addresses and per-slot predicates instead.
 //
 // Order of summation: entries of a row in CSR order, sequentially, with fused
-// multiply-add -- deterministic, and identical whatever row order is used.
+// multiply-add (a padding slot adds 0 * 0) -- deterministic, and identical
+// whatever row order is used.
 #include "sp_device.h"
 #include "sp_launch.h"
 
@@ -32,10 +35,20 @@ namespace spk {
 
 namespace {
 
-constexpr int kSpmmUnroll = 8;
+#ifndef SP_SPMM_UNROLL
+#define SP_SPMM_UNROLL 4
+#endif
+#ifndef SP_SPMM_ENTRIES_PER_LANE
+#define SP_SPMM_ENTRIES_PER_LANE 8
+#endif
+constexpr int kU = SP_SPMM_UNROLL;                // gathers per batch
+constexpr int kEpl = SP_SPMM_ENTRIES_PER_LANE;    // staged entries per lane per window
+constexpr unsigned kOutOfRange = 0x80000000u;     // buffer offset that reads as zero
+static_assert(kEpl % 4 == 0, "segments of 4 entries");
 
 struct SpmmParams {
-    int m, n, nnz, row_blocks;
+    int m, n, nnz, row_blocks, tiles, batch;
+    unsigned b_bytes;  // bytes of one B operand (buffer path)
     const int *row_indices;
     const int *row_offsets;
     const int *col_indices;
@@ -49,6 +62,12 @@ template <int kVec> struct Vec;
 template <> struct Vec<4> {
     using T = float4;
     static __device__ __forceinline__ T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+    static __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, unsigned off)
+    {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+        return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]),
+                           __uint_as_float(v[2]), __uint_as_float(v[3]));
+    }
     static __device__ __forceinline__ void fma(float a, const T &b, float *acc)
     {
         acc[0] = fmaf(a, b.x, acc[0]);
@@ -64,6 +83,10 @@ template <> struct Vec<4> {
 template <> struct Vec<1> {
     using T = float;
     static __device__ __forceinline__ T zero() { return 0.f; }
+    static __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, unsigned off)
+    {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    }
     static __device__ __forceinline__ void fma(float a, const T &b, float *acc)
     {
         acc[0] = fmaf(a, b, acc[0]);
@@ -74,23 +97,38 @@ template <> struct Vec<1> {
     }
 };
 
-template <int kLpr, int kVec, bool kVecCsr, bool kOff32>
+// kBuf: B < 2 GiB, gathers through a buffer resource with byte offsets.
+// Otherwise: 64-bit addressing, staged offsets are columns, padding has value
+// 0 and column -1 and is skipped by a predicate.
+template <int kLpr, int kVec, bool kVecCsr, bool kBuf>
 __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
 {
     using V = Vec<kVec>;
     using VecT = typename V::T;
-    constexpr int kRpw = kWave / kLpr;   // rows per wave
-    constexpr int kChunk = 4 * kLpr;     // staged entries per row per window
-    constexpr int kPitch = kChunk + 1;   // +1 int2 spreads the groups over banks
-    // Staged entry: .x = B-row offset (bytes if kOff32, else the column), .y = value bits.
-    __shared__ int2 s_ent[kRpw * kPitch];
+    constexpr int kRpw = kWave / kLpr;       // rows per wave
+    constexpr int kChunk = kEpl * kLpr;      // entries per row per window
+    // A group's slots: the window, kU padding slots read by the prefetch, and
+    // 4 more so that the groups' regions start 12 words apart modulo the 64
+    // LDS banks (their broadcast reads then never share a bank).
+    constexpr int kPitch = kChunk + kU + 4;
+    constexpr int kPad = kBuf ? (int)kOutOfRange : -1;
+    static_assert(kPitch % 4 == 0 && kU % 4 == 0, "16-byte aligned batches");
+    static_assert(kChunk % kU == 0, "batches never straddle the window end");
+    // Staged entries, one array per field so that each lane's staging writes
+    // are 16 contiguous bytes: B-row byte offset (kBuf) or column, and value.
+    __shared__ __align__(16) int s_off[kRpw * kPitch];
+    __shared__ __align__(16) float s_val[kRpw * kPitch];
+
+    const long long w = xcd_work_index((long long)p.batch * p.tiles, p.row_blocks);
+    if (w < 0) return;
+    const long long per_z = (long long)p.tiles * p.row_blocks;
+    const long long z = w / per_z;
+    const int tile = (int)((w - z * per_z) / p.row_blocks);
+    const int rb = (int)(w - z * per_z - (long long)tile * p.row_blocks);
 
     const int lane = threadIdx.x;
-    const int grp = lane / kLpr;
-    const int gl = lane - grp * kLpr;
-    const int tile = blockIdx.x / p.row_blocks;
-    const int rb = blockIdx.x - tile * p.row_blocks;
-    const long long z = blockIdx.y;
+    const int grp = kRpw == 1 ? 0 : lane / kLpr;
+    const int gl = kRpw == 1 ? lane : lane - grp * kLpr;
     const float *__restrict__ vals = p.values + z * p.stride_values;
     const float *__restrict__ bz = p.b + z * p.stride_b;
     float *__restrict__ cz = p.c + z * p.stride_c;
@@ -102,21 +140,48 @@ __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
     const int p1 = has_row ? p.row_offsets[row + 1] : 0;
     const int col0 = (tile * kLpr + gl) * kVec;
     const bool col_ok = col0 < p.n;  // vector path: n % 4 == 0, so the whole vector is in range
-    const unsigned lane_bytes = (unsigned)col0 * 4u;
-    int2 *ent = s_ent + grp * kPitch;
+    // Lanes past the last column read only out-of-range (zero) data.
+    const unsigned lane_bytes = col_ok ? (unsigned)col0 * 4u : kOutOfRange;
+    int *g_off = s_off + grp * kPitch;
+    float *g_val = s_val + grp * kPitch;
+    for (int j = gl; j < kU; j += kLpr) {
+        g_off[kChunk + j] = kPad;
+        g_val[kChunk + j] = 0.f;
+    }
 
-    auto offset_of = [&](int col) -> int {
-        if constexpr (kOff32)
-            return (int)((unsigned)col * (unsigned)p.n * 4u);
+    __amdgpu_buffer_rsrc_t rsrc;
+    if constexpr (kBuf)
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(bz), 0, p.b_bytes,
+                                                 0x00020000);
+
+    auto offset_of = [&](int idx, int col) -> int {
+        const bool in = idx >= p0 && idx < p1;
+        if constexpr (kBuf)
+            return in ? (int)((unsigned)col * (unsigned)p.n * 4u) : kPad;
         else
-            return col;
+            return in ? col : kPad;
     };
-    auto load_b = [&](int off) -> VecT {
-        if constexpr (kOff32)
-            return *reinterpret_cast<const VecT *>(
-                reinterpret_cast<const char *>(bz) + ((unsigned)off + lane_bytes));
-        else
+    auto value_of = [&](int idx, float v) -> float {
+        return (idx >= p0 && idx < p1) ? v : 0.f;
+    };
+    auto gather = [&](int off) -> VecT {
+        if constexpr (kBuf) {
+            return V::buf_load(rsrc, (unsigned)off + lane_bytes);
+        } else {
+            if (off < 0 || !col_ok) return V::zero();
             return *reinterpret_cast<const VecT *>(bz + (size_t)off * (size_t)p.n + col0);
+        }
+    };
+    // kU staged entries starting at slot j (a multiple of 4): 16-byte
+    // broadcast reads of both arrays.
+    auto read_batch = [&](int j, int (&off)[kU], float (&val)[kU]) {
+#pragma unroll
+        for (int u = 0; u < kU; u += 4) {
+            const int4 o4 = *reinterpret_cast<const int4 *>(g_off + j + u);
+            const float4 v4 = *reinterpret_cast<const float4 *>(g_val + j + u);
+            off[u] = o4.x; off[u + 1] = o4.y; off[u + 2] = o4.z; off[u + 3] = o4.w;
+            val[u] = v4.x; val[u + 1] = v4.y; val[u + 2] = v4.z; val[u + 3] = v4.w;
+        }
     };
 
     float acc[kVec];
@@ -127,93 +192,118 @@ __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
     for (;;) {
         const bool more = win < p1;
         if (!__any(more)) break;  // wave-uniform: every lane reaches the barriers
-        if (more) {
-            if constexpr (kVecCsr) {
-                const int e = win + gl * 4;
-                int cc[4];
-                float vv[4];
-                if (e + 4 <= p.nnz) {
-                    const int4 c4 = *reinterpret_cast<const int4 *>(p.col_indices + e);
-                    const float4 v4 = *reinterpret_cast<const float4 *>(vals + e);
-                    cc[0] = c4.x; cc[1] = c4.y; cc[2] = c4.z; cc[3] = c4.w;
-                    vv[0] = v4.x; vv[1] = v4.y; vv[2] = v4.z; vv[3] = v4.w;
-                } else {
+        // ---- stage one window (padding outside [p0, p1))
+        if constexpr (kVecCsr) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const bool in = e + t < p.nnz;
-                        cc[t] = in ? p.col_indices[e + t] : 0;
-                        vv[t] = in ? vals[e + t] : 0.f;
+            for (int sg = 0; sg < kEpl / 4; ++sg) {
+                const int slot0 = (sg * kLpr + gl) * 4;
+                const int e = win + slot0;
+                int cc[4] = {0, 0, 0, 0};
+                float vv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (e < p1 && e + 4 > p0) {
+                    if (e + 4 <= p.nnz) {
+                        const int4 c4 = *reinterpret_cast<const int4 *>(p.col_indices + e);
+                        const float4 v4 = *reinterpret_cast<const float4 *>(vals + e);
+                        cc[0] = c4.x; cc[1] = c4.y; cc[2] = c4.z; cc[3] = c4.w;
+                        vv[0] = v4.x; vv[1] = v4.y; vv[2] = v4.z; vv[3] = v4.w;
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            if (e + t < p.nnz) {
+                                cc[t] = p.col_indices[e + t];
+                                vv[t] = vals[e + t];
+                            }
+                        }
                     }
                 }
+                *reinterpret_cast<int4 *>(g_off + slot0) =
+                    make_int4(offset_of(e, cc[0]), offset_of(e + 1, cc[1]),
+                              offset_of(e + 2, cc[2]), offset_of(e + 3, cc[3]));
+                *reinterpret_cast<float4 *>(g_val + slot0) =
+                    make_float4(value_of(e, vv[0]), value_of(e + 1, vv[1]),
+                                value_of(e + 2, vv[2]), value_of(e + 3, vv[3]));
+            }
+        } else {
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    ent[gl * 4 + t] = make_int2(offset_of(cc[t]), __float_as_int(vv[t]));
-            } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int idx = win + t * kLpr + gl;
-                    const bool in = idx < p1;
-                    const int cc = in ? p.col_indices[idx] : 0;
-                    const float vv = in ? vals[idx] : 0.f;
-                    ent[t * kLpr + gl] = make_int2(offset_of(cc), __float_as_int(vv));
-                }
+            for (int t = 0; t < kEpl; ++t) {
+                const int idx = win + t * kLpr + gl;
+                const bool in = idx < p1;
+                g_off[t * kLpr + gl] = offset_of(idx, in ? p.col_indices[idx] : 0);
+                g_val[t * kLpr + gl] = value_of(idx, in ? vals[idx] : 0.f);
             }
         }
         __syncthreads();
-        if (more && col_ok) {
-            const int jb = max(p0 - win, 0);  // > 0 only for a misaligned first window
-            const int je = min(p1 - win, kChunk);
-            int j = jb;
-            for (; j + kSpmmUnroll <= je; j += kSpmmUnroll) {
-                int2 en[kSpmmUnroll];
-                VecT bv[kSpmmUnroll];
+        // ---- gather and accumulate: double-buffered batches of kU slots.
+        // Slots [0, wend) of the window cover every group's live entries.
+        const int my_end = min(p1 - win, kChunk);
+        int wend = my_end;
 #pragma unroll
-                for (int u = 0; u < kSpmmUnroll; ++u) en[u] = ent[j + u];
+        for (int o = kLpr; o < kWave; o <<= 1) wend = max(wend, __shfl_xor(wend, o));
+        VecT bufa[kU], bufb[kU];
+        int offa[kU], offb[kU];
+        float vala[kU], valb[kU];
+        // Each batch's staged entries are read right after the arithmetic
+        // that frees their registers, and the loop body is one basic block
+        // (two batches per trip, the second possibly all padding): the
+        // compiler's wait counts are then exact and the next batch's gathers
+        // are issued before the current batch is waited for.  Batches past
+        // the window are the kU padding slots (min(., kChunk)).
+        read_batch(0, offa, vala);
 #pragma unroll
-                for (int u = 0; u < kSpmmUnroll; ++u) bv[u] = load_b(en[u].x);
+        for (int u = 0; u < kU; ++u) bufa[u] = gather(offa[u]);
+        read_batch(min(kU, kChunk), offb, valb);
+        int j = 0;
+        do {
 #pragma unroll
-                for (int u = 0; u < kSpmmUnroll; ++u) V::fma(__int_as_float(en[u].y), bv[u], acc);
-            }
-            for (; j < je; ++j) {
-                const int2 en = ent[j];
-                V::fma(__int_as_float(en.y), load_b(en.x), acc);
-            }
-        }
+            for (int u = 0; u < kU; ++u) bufb[u] = gather(offb[u]);
+            keep_issued_above();
+#pragma unroll
+            for (int u = 0; u < kU; ++u) V::fma(vala[u], bufa[u], acc);
+            read_batch(min(j + 2 * kU, kChunk), offa, vala);
+#pragma unroll
+            for (int u = 0; u < kU; ++u) bufa[u] = gather(offa[u]);
+            keep_issued_above();
+#pragma unroll
+            for (int u = 0; u < kU; ++u) V::fma(valb[u], bufb[u], acc);
+            read_batch(min(j + 3 * kU, kChunk), offb, valb);
+            j += 2 * kU;
+        } while (j < wend);
         __syncthreads();
         win += kChunk;
     }
     if (has_row && col_ok) V::store(cz + (size_t)row * (size_t)p.n + col0, acc);
 }
 
-template <int kLpr, int kVec, bool kVecCsr, bool kOff32>
+template <int kLpr, int kVec, bool kVecCsr, bool kBuf>
 hipError_t launch_t(const SpmmParams &p, int tiles, int batch, hipStream_t s)
 {
-    dim3 grid((unsigned)(tiles * p.row_blocks), (unsigned)batch);
-    hipLaunchKernelGGL((spmm_kernel<kLpr, kVec, kVecCsr, kOff32>), grid,
-                       dim3(kWave), 0, s, p);
+    (void)tiles;
+    (void)batch;
+    dim3 grid((unsigned)xcd_grid((long long)p.batch * p.tiles, p.row_blocks));
+    hipLaunchKernelGGL((spmm_kernel<kLpr, kVec, kVecCsr, kBuf>), grid, dim3(kWave), 0, s, p);
     return hipGetLastError();
 }
 
 template <int kLpr, int kVec>
-hipError_t launch_csr(const SpmmParams &p, int tiles, int batch, bool vec_csr,
-                      bool off32, hipStream_t s)
+hipError_t launch_csr(const SpmmParams &p, int tiles, int batch, bool vec_csr, bool buf,
+                      hipStream_t s)
 {
     if (vec_csr)
-        return off32 ? launch_t<kLpr, kVec, true, true>(p, tiles, batch, s)
-                     : launch_t<kLpr, kVec, true, false>(p, tiles, batch, s);
-    return off32 ? launch_t<kLpr, kVec, false, true>(p, tiles, batch, s)
-                 : launch_t<kLpr, kVec, false, false>(p, tiles, batch, s);
+        return buf ? launch_t<kLpr, kVec, true, true>(p, tiles, batch, s)
+                   : launch_t<kLpr, kVec, true, false>(p, tiles, batch, s);
+    return buf ? launch_t<kLpr, kVec, false, true>(p, tiles, batch, s)
+               : launch_t<kLpr, kVec, false, false>(p, tiles, batch, s);
 }
 
 template <int kVec>
-hipError_t launch_lpr(int lpr, const SpmmParams &p, int tiles, int batch,
-                      bool vec_csr, bool off32, hipStream_t s)
+hipError_t launch_lpr(int lpr, const SpmmParams &p, int tiles, int batch, bool vec_csr,
+                      bool buf, hipStream_t s)
 {
     switch (lpr) {
-    case 8: return launch_csr<8, kVec>(p, tiles, batch, vec_csr, off32, s);
-    case 16: return launch_csr<16, kVec>(p, tiles, batch, vec_csr, off32, s);
-    case 32: return launch_csr<32, kVec>(p, tiles, batch, vec_csr, off32, s);
-    default: return launch_csr<64, kVec>(p, tiles, batch, vec_csr, off32, s);
+    case 8: return launch_csr<8, kVec>(p, tiles, batch, vec_csr, buf, s);
+    case 16: return launch_csr<16, kVec>(p, tiles, batch, vec_csr, buf, s);
+    case 32: return launch_csr<32, kVec>(p, tiles, batch, vec_csr, buf, s);
+    default: return launch_csr<64, kVec>(p, tiles, batch, vec_csr, buf, s);
     }
 }
 
@@ -233,14 +323,15 @@ hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream)
                      (a.stride_b % 4 == 0) && (a.stride_c % 4 == 0);
     const bool vec_csr = aligned16(a.col_indices) && aligned16(a.values) &&
                          (a.stride_values % 4 == 0);
-    const bool off32 = (long long)a.k * (long long)a.n < (1LL << 30);
+    // Valid offsets stay below B's size and padding offsets (>= 2^31) beyond it.
+    const bool buf = (long long)a.k * (long long)a.n <= (1LL << 29);
     const int kvec = vec ? 4 : 1;
     const int nv = (a.n + kvec - 1) / kvec;
     const int lpr = nv <= 8 ? 8 : nv <= 16 ? 16 : nv <= 32 ? 32 : 64;
     const int rpw = kWave / lpr;
     const int tiles = (nv + lpr - 1) / lpr;
     const long long row_blocks = ((long long)a.m + rpw - 1) / rpw;
-    if ((long long)tiles * row_blocks > 0x7fffffffLL || a.batch > 65535)
+    if (xcd_grid((long long)a.batch * tiles, row_blocks) > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
 
     SpmmParams p;
@@ -248,6 +339,9 @@ hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream)
     p.n = a.n;
     p.nnz = a.nnz;
     p.row_blocks = (int)row_blocks;
+    p.tiles = tiles;
+    p.batch = a.batch;
+    p.b_bytes = buf ? (unsigned)((long long)a.k * a.n * 4) : 0u;
     p.row_indices = a.row_indices;
     p.row_offsets = a.row_offsets;
     p.col_indices = a.col_indices;
@@ -257,8 +351,8 @@ hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream)
     p.stride_values = a.stride_values;
     p.stride_b = a.stride_b;
     p.stride_c = a.stride_c;
-    return vec ? launch_lpr<4>(lpr, p, tiles, a.batch, vec_csr, off32, stream)
-               : launch_lpr<1>(lpr, p, tiles, a.batch, vec_csr, off32, stream);
+    return vec ? launch_lpr<4>(lpr, p, tiles, a.batch, vec_csr, buf, stream)
+               : launch_lpr<1>(lpr, p, tiles, a.batch, vec_csr, buf, stream);
 }
 
 }  // namespace spk
