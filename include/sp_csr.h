@@ -113,6 +113,16 @@ sp_status_t sp_csr_fill_dense(int m, int k, const unsigned char *mask,
 sp_status_t sp_row_swizzle(int m, const int *row_offsets, int *row_indices,
                            sp_stream_t stream);
 
+/* CSR row offsets and the swizzled row order from row lengths in one launch
+ * (the order depends on the lengths only): row_offsets as
+ * sp_csr_offsets_from_lengths writes them and row_indices as sp_row_swizzle
+ * writes them for those offsets.  For a structure given as per-row lists this
+ * is the whole preparation before SpMM/SDDMM.
+ *   lengths      int32[m], each >= 0, sum <= INT32_MAX (precondition)
+ *   row_offsets  int32[m+1], output;  row_indices  int32[m], output */
+sp_status_t sp_csr_build_from_lengths(int m, const int *lengths, int *row_offsets,
+                                      int *row_indices, sp_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * SpMM ("Summary" of the card): C = A * B, A sparse in CSR, B dense.
  * ---------------------------------------------------------------------- */

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 10, declared
+    assert len(declared) == 11, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -102,6 +102,10 @@ def test_build_and_swizzle_validation(lib):
     assert lib.sp_csr_fill_dense(3, 3, NULL, NULL, FAKE, FAKE, NULL, s) == INVALID
     assert lib.sp_csr_fill_dense(3, 3, FAKE, NULL, NULL, FAKE, NULL, s) == INVALID
     assert lib.sp_csr_fill_dense(-3, 3, FAKE, FAKE, FAKE, FAKE, FAKE, s) == INVALID
+    assert lib.sp_csr_build_from_lengths(-1, FAKE, FAKE, FAKE, s) == INVALID
+    assert lib.sp_csr_build_from_lengths(3, NULL, FAKE, FAKE, s) == INVALID
+    assert lib.sp_csr_build_from_lengths(3, FAKE, NULL, FAKE, s) == INVALID
+    assert lib.sp_csr_build_from_lengths(3, FAKE, FAKE, NULL, s) == INVALID
     assert lib.sp_row_swizzle(-1, FAKE, FAKE, s) == INVALID
     assert lib.sp_row_swizzle(3, NULL, FAKE, s) == INVALID
     assert lib.sp_row_swizzle(3, FAKE, NULL, s) == INVALID

@@ -137,6 +137,19 @@ def test_row_swizzle_bit_exact(name):
     assert np.array_equal(got, oracle.row_swizzle(ro)), name
 
 
+@pytest.mark.parametrize("name", list(_swizzle_cases()))
+def test_build_from_lengths_bit_exact(name):
+    lengths = _swizzle_cases()[name]
+    m = lengths.shape[0]
+    note(f"build_from_lengths {name} m={m}")
+    ro = torch.full((m + 1,), -7, dtype=torch.int32, device="cuda")
+    ri = torch.full((m,), -7, dtype=torch.int32, device="cuda")
+    sp.sp_csr_build_from_lengths(m, dev(lengths), ro, ri)
+    ro_o = oracle.csr_offsets_from_lengths(lengths)
+    assert np.array_equal(host(ro), ro_o), name
+    assert np.array_equal(host(ri), oracle.row_swizzle(ro_o)), name
+
+
 # ------------------------------------------------------------------ SpMM, workloads
 
 def test_spmm_tiny():
@@ -230,6 +243,37 @@ def test_spmm_one_entry_rows_bit_exact():
     c = run_spmm(a, b)
     ref, _ = oracle.spmm(m, k, n, a.ro, a.ci, a.vals, b)
     assert np.array_equal(c.view(np.int32), ref.astype(np.float32).view(np.int32))
+
+
+def test_spmm_narrow_exact_cases():
+    # n = 8 and n = 4 take the lanes-over-entries kernel: identity and
+    # one-entry rows stay exact through its shuffle tree (it adds zeros).
+    for n in (4, 8, 16):
+        k = 300
+        b = inputs.random_dense(50 + n, k, n)
+        ident = DevCsr(k, k, np.arange(k + 1), np.arange(k), np.ones(k, np.float32))
+        note(f"spmm narrow identity n={n}")
+        assert np.array_equal(run_spmm(ident, b).view(np.int32), b.view(np.int32))
+        rl = inputs.random_row_lists(60 + n, 500, k, np.ones(500, np.int32))
+        a = csr_of_row_lists(rl)
+        note(f"spmm narrow one-entry rows n={n}")
+        c = run_spmm(a, b)
+        ref, _ = oracle.spmm(500, k, n, a.ro, a.ci, a.vals, b)
+        assert np.array_equal(c.view(np.int32), ref.astype(np.float32).view(np.int32))
+
+
+def test_spmm_hbm_stream_sampled_rows():
+    # The streaming workload (CSR ~430 MB, n = 8) in the bench's launch
+    # configuration, checked on sampled rows.
+    w = inputs.hbm_stream()
+    a = csr_of_row_lists(w["a"])
+    note("spmm hbm_stream 65536x8192x8 swizzled")
+    c = run_spmm(a, w["b"], row_indices=swizzle(a))
+    rows = np.random.default_rng(70).choice(a.m, 2000, replace=False).astype(np.int32)
+    rows[:2] = [0, a.m - 1]
+    ref, s = oracle.spmm_rows(rows, w["n"], a.ro, a.ci, a.vals, w["b"])
+    check_close(c[rows], ref, s, "spmm hbm_stream")
+    assert np.all(np.isfinite(c))
 
 
 # ------------------------------------------------------------------ SpMM, edges

@@ -34,6 +34,7 @@ SIGNATURES = {
     "sp_csr_count_dense": ([_c_int, _c_int, _vp, _vp, _vp], _c_int),
     "sp_csr_fill_dense": ([_c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp], _c_int),
     "sp_row_swizzle": ([_c_int, _vp, _vp, _vp], _c_int),
+    "sp_csr_build_from_lengths": ([_c_int, _vp, _vp, _vp, _vp], _c_int),
     "sp_spmm": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
                 _c_int),
     "sp_spmm_batched": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -137,6 +138,13 @@ def sp_row_swizzle(m, row_offsets, row_indices, stream=None):
     _check(lib().sp_row_swizzle(
         m, _ptr(row_offsets, _I32, "row_offsets"), _ptr(row_indices, _I32, "row_indices", True),
         _stream(stream)), "sp_row_swizzle")
+
+
+def sp_csr_build_from_lengths(m, lengths, row_offsets, row_indices, stream=None):
+    _check(lib().sp_csr_build_from_lengths(
+        m, _ptr(lengths, _I32, "lengths", True), _ptr(row_offsets, _I32, "row_offsets"),
+        _ptr(row_indices, _I32, "row_indices", True), _stream(stream)),
+        "sp_csr_build_from_lengths")
 
 
 # ---------------------------------------------------------------- SpMM / SDDMM

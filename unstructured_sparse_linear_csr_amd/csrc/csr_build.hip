@@ -8,54 +8,18 @@
 // is bit-identical to any correct CSR construction.
 #include "sp_device.h"
 #include "sp_launch.h"
+#include "sp_scan.h"
 
 namespace spk {
 
 namespace {
 
 constexpr int kScanThreads = 1024;
-constexpr int kScanPerThread = 4;
-constexpr int kScanTile = kScanThreads * kScanPerThread;
 
-// out[0] = 0 and out[i+1] = in[0] + ... + in[i] for i < m.  One workgroup walks
-// the array tile by tile, carrying the running total.  Each thread reads its
-// own elements before the barrier and writes the same positions after it, so
-// `in` may alias `out + 1` (the in-place form used after counting).
 __global__ __launch_bounds__(kScanThreads) void exclusive_scan_kernel(
     int m, const int *in, int *out)
 {
-    __shared__ int wave_total[kScanThreads / kWave];
-    const int tid = threadIdx.x;
-    const int lane = tid % kWave;
-    const int wave = tid / kWave;
-    if (tid == 0) out[0] = 0;
-    int carry = 0;
-    for (int base = 0; base < m; base += kScanTile) {
-        const int i0 = base + tid * kScanPerThread;
-        int v[kScanPerThread];
-#pragma unroll
-        for (int t = 0; t < kScanPerThread; ++t)
-            v[t] = (i0 + t < m) ? in[i0 + t] : 0;
-#pragma unroll
-        for (int t = 1; t < kScanPerThread; ++t) v[t] += v[t - 1];
-        const int mine = v[kScanPerThread - 1];
-        const int incl = wave_inclusive_sum(mine, lane);
-        if (lane == kWave - 1) wave_total[wave] = incl;
-        __syncthreads();
-        int before = 0, tile_total = 0;
-#pragma unroll
-        for (int w = 0; w < kScanThreads / kWave; ++w) {
-            const int t = wave_total[w];
-            before += (w < wave) ? t : 0;
-            tile_total += t;
-        }
-        const int excl = carry + before + incl - mine;
-#pragma unroll
-        for (int t = 0; t < kScanPerThread; ++t)
-            if (i0 + t < m) out[i0 + t + 1] = excl + v[t];
-        carry += tile_total;
-        __syncthreads();
-    }
+    exclusive_scan_block<kScanThreads>(m, in, out);
 }
 
 // counts[row] = number of nonzero bytes in mask row `row` (one wave per row).

@@ -14,6 +14,7 @@
 // on that structure.
 #include "sp_device.h"
 #include "sp_launch.h"
+#include "sp_scan.h"
 
 namespace spk {
 
@@ -29,38 +30,46 @@ __device__ __forceinline__ unsigned long long row_key(int length, int row)
     return ((unsigned long long)(unsigned)length << 32) | (unsigned)(0xFFFFFFFFu - (unsigned)row);
 }
 
+// Row lengths from CSR row offsets, or given directly.
+struct FromOffsets {
+    const int *row_offsets;
+    __device__ int operator()(int r) const { return row_offsets[r + 1] - row_offsets[r]; }
+};
+struct FromLengths {
+    const int *lengths;
+    __device__ int operator()(int r) const { return lengths[r]; }
+};
+
 // Each row's rank is counted by kLanesPerRow lanes, each taking every
 // kLanesPerRow-th pair of staged keys; the partial counts are summed across
 // the lanes (integer sums, so the order does not matter).  Lanes of a wave
 // that read the same pair read the same LDS address (a broadcast), and the
 // 16 pairs a wave reads at once are contiguous.  Padding slots hold key 0,
 // which is below every real key.
-__global__ __launch_bounds__(kSwizzleThreads) void row_swizzle_kernel(
-    int m, const int *__restrict__ row_offsets, int *__restrict__ row_indices)
+template <class Len>
+__device__ void rank_rows(int m, Len len, int *__restrict__ row_indices, int block)
 {
     __shared__ __align__(16) unsigned long long s_key[kSwizzleTile];
     const int t = threadIdx.x;
     const int sub = t % kLanesPerRow;
-    const int i = blockIdx.x * kRowsPerBlock + t / kLanesPerRow;
+    const int i = block * kRowsPerBlock + t / kLanesPerRow;
     const bool mine = i < m;
-    const unsigned long long key_i =
-        mine ? row_key(row_offsets[i + 1] - row_offsets[i], i) : ~0ull;
+    const unsigned long long key_i = mine ? row_key(len(i), i) : ~0ull;
     int rank = 0;
     for (int t0 = 0; t0 < m; t0 += kSwizzleTile) {
         const int cnt = min(kSwizzleTile, m - t0);
-        // All of a thread's offset loads are issued before any is used.
+        // All of a thread's length loads are issued before any is used.
         constexpr int kPer = kSwizzleTile / kSwizzleThreads;
-        int lo[kPer], hi[kPer];
+        int l[kPer];
 #pragma unroll
         for (int q = 0; q < kPer; ++q) {
             const int j = t + q * kSwizzleThreads;
-            lo[q] = j < cnt ? row_offsets[t0 + j] : 0;
-            hi[q] = j < cnt ? row_offsets[t0 + j + 1] : 0;
+            l[q] = j < cnt ? len(t0 + j) : 0;
         }
 #pragma unroll
         for (int q = 0; q < kPer; ++q) {
             const int j = t + q * kSwizzleThreads;
-            s_key[j] = j < cnt ? row_key(hi[q] - lo[q], t0 + j) : 0ull;
+            s_key[j] = j < cnt ? row_key(l[q], t0 + j) : 0ull;
         }
         __syncthreads();
         // Eight independent LDS reads in flight per lane.  The tile's padding
@@ -82,7 +91,36 @@ __global__ __launch_bounds__(kSwizzleThreads) void row_swizzle_kernel(
     if (mine && sub == 0) row_indices[rank] = i;
 }
 
+__global__ __launch_bounds__(kSwizzleThreads) void row_swizzle_kernel(
+    int m, const int *__restrict__ row_offsets, int *__restrict__ row_indices)
+{
+    rank_rows(m, FromOffsets{row_offsets}, row_indices, blockIdx.x);
+}
+
+// CSR offsets and the swizzled order from row lengths in one launch: the
+// order needs only the lengths, so the last workgroup scans them into the
+// offsets while the others rank the rows.
+__global__ __launch_bounds__(kSwizzleThreads) void build_and_swizzle_kernel(
+    int m, const int *__restrict__ lengths, int *__restrict__ row_offsets,
+    int *__restrict__ row_indices)
+{
+    if (blockIdx.x == gridDim.x - 1) {
+        exclusive_scan_block<kSwizzleThreads>(m, lengths, row_offsets);
+        return;
+    }
+    rank_rows(m, FromLengths{lengths}, row_indices, blockIdx.x);
+}
+
 }  // namespace
+
+hipError_t launch_build_and_swizzle(int m, const int *lengths, int *row_offsets,
+                                   int *row_indices, hipStream_t stream)
+{
+    const int blocks = (m + kRowsPerBlock - 1) / kRowsPerBlock + 1;
+    hipLaunchKernelGGL(build_and_swizzle_kernel, dim3(blocks), dim3(kSwizzleThreads), 0,
+                       stream, m, lengths, row_offsets, row_indices);
+    return hipGetLastError();
+}
 
 hipError_t launch_row_swizzle(int m, const int *row_offsets, int *row_indices,
                               hipStream_t stream)

@@ -79,6 +79,15 @@ sp_status_t sp_row_swizzle(int m, const int *row_offsets, int *row_indices,
                                             as_stream(stream)));
 }
 
+sp_status_t sp_csr_build_from_lengths(int m, const int *lengths, int *row_offsets,
+                                      int *row_indices, sp_stream_t stream)
+{
+    if (m < 0 || !need(lengths, m) || row_offsets == nullptr || !need(row_indices, m))
+        return SP_ERROR_INVALID_VALUE;
+    return from_hip(spk::launch_build_and_swizzle(m, lengths, row_offsets, row_indices,
+                                                  as_stream(stream)));
+}
+
 sp_status_t sp_spmm_batched(int m, int k, int n, int nnz, const int *row_indices,
                             const float *values, const int *row_offsets,
                             const int *col_indices, const float *b, float *c,

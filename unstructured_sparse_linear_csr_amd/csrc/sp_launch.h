@@ -38,6 +38,8 @@ hipError_t launch_count_dense(int m, int k, const unsigned char *mask,
 hipError_t launch_fill_dense(int m, int k, const unsigned char *mask,
                              const float *dense_values, const int *row_offsets,
                              int *col_indices, float *values, hipStream_t stream);
+hipError_t launch_build_and_swizzle(int m, const int *lengths, int *row_offsets,
+                                   int *row_indices, hipStream_t stream);
 hipError_t launch_row_swizzle(int m, const int *row_offsets, int *row_indices,
                               hipStream_t stream);
 hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream);

@@ -48,7 +48,8 @@ static_assert(kEpl % 4 == 0, "segments of 4 entries");
 
 struct SpmmParams {
     int m, n, nnz, row_blocks, tiles, batch;
-    unsigned b_bytes;  // bytes of one B operand (buffer path)
+    unsigned b_bytes;    // bytes of one B operand (buffer path)
+    unsigned csr_bytes;  // bytes of col_indices (= of one values array), narrow kernel
     const int *row_indices;
     const int *row_offsets;
     const int *col_indices;
@@ -274,6 +275,99 @@ __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
     if (has_row && col_ok) V::store(cz + (size_t)row * (size_t)p.n + col0, acc);
 }
 
+// Narrow B (n of at most 16 columns): the lane-over-columns mapping above
+// would leave most of a row group idle, so here the lanes of one wave split
+// a row's entries instead.  Lane (s, v) handles entries s, s + kS, s + 2kS, ...
+// of the row (kS = 64 / kE entry slots) and the v-th vector of kVec columns
+// of B (kE vectors cover the row of B).  Column indices and values are read
+// through buffer resources (out-of-range past the row's end: zeros, no
+// traffic); each lane sums its entries in order, then the kS partial sums of
+// each column vector are added by a shuffle tree over the lane bits above kE.
+// Deterministic; a different (tree) order from the wide kernel.
+template <int kE, int kVec>
+__global__ __launch_bounds__(kWave) void spmm_narrow_kernel(SpmmParams p)
+{
+    using V = Vec<kVec>;
+    using VecT = typename V::T;
+    constexpr int kS = kWave / kE;  // entries per step
+    constexpr int kSteps = 8;       // steps per batch (CSR loads, then gathers)
+    const long long w = xcd_work_index(p.batch, p.m);
+    if (w < 0) return;
+    const long long z = w / p.m;
+    const int slot = (int)(w - z * p.m);
+    const int lane = threadIdx.x;
+    const int s = lane / kE;
+    const int v = lane - s * kE;
+    const int row = p.row_indices ? p.row_indices[slot] : slot;
+    const int p0 = p.row_offsets[row];
+    const int p1 = p.row_offsets[row + 1];
+    const float *vals = p.values + z * p.stride_values;
+    const float *bz = p.b + z * p.stride_b;
+    float *cz = p.c + z * p.stride_c;
+    const int col0 = v * kVec;
+    const bool col_ok = col0 < p.n;
+    const unsigned lane_bytes = col_ok ? (unsigned)col0 * 4u : kOutOfRange;
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(bz), 0, (int)p.b_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int *>(p.col_indices), 0, (int)p.csr_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(vals), 0, (int)p.csr_bytes, 0x00020000);
+
+    float acc[kVec];
+#pragma unroll
+    for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
+    for (int base = p0; base < p1; base += kS * kSteps) {  // wave-uniform bound
+        unsigned coff[kSteps];
+        int cc[kSteps];
+        float vv[kSteps];
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            const int idx = base + u * kS + s;
+            coff[u] = idx < p1 ? (unsigned)idx * 4u : kOutOfRange;
+        }
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            cc[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (int)coff[u], 0, 0);
+            vv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, (int)coff[u], 0, 0));
+        }
+        VecT bv[kSteps];
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            const unsigned off = coff[u] == kOutOfRange
+                                     ? kOutOfRange
+                                     : (unsigned)cc[u] * (unsigned)p.n * 4u + lane_bytes;
+            bv[u] = V::buf_load(rb, off);
+        }
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) V::fma(vv[u], bv[u], acc);
+    }
+#pragma unroll
+    for (int o = kE; o < kWave; o <<= 1) {
+#pragma unroll
+        for (int t = 0; t < kVec; ++t) acc[t] += __shfl_xor(acc[t], o);
+    }
+    if (s == 0 && col_ok) V::store(cz + (size_t)row * (size_t)p.n + col0, acc);
+}
+
+template <int kE, int kVec>
+hipError_t launch_narrow_t(const SpmmParams &p, hipStream_t s)
+{
+    dim3 grid((unsigned)xcd_grid(p.batch, p.m));
+    hipLaunchKernelGGL((spmm_narrow_kernel<kE, kVec>), grid, dim3(kWave), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int kVec>
+hipError_t launch_narrow(int e, const SpmmParams &p, hipStream_t s)
+{
+    switch (e) {
+    case 1: return launch_narrow_t<1, kVec>(p, s);
+    case 2: return launch_narrow_t<2, kVec>(p, s);
+    default: return launch_narrow_t<4, kVec>(p, s);
+    }
+}
+
 template <int kLpr, int kVec, bool kVecCsr, bool kBuf>
 hipError_t launch_t(const SpmmParams &p, int tiles, int batch, hipStream_t s)
 {
@@ -334,6 +428,10 @@ hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream)
     if (xcd_grid((long long)a.batch * tiles, row_blocks) > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
 
+    // Narrow B: lanes over entries (needs the buffer paths for B and the CSR).
+    const bool narrow = buf && nv <= 4 && (long long)a.nnz * 4 <= (1LL << 31);
+    if (narrow && xcd_grid(a.batch, a.m) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+
     SpmmParams p;
     p.m = a.m;
     p.n = a.n;
@@ -342,6 +440,7 @@ hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream)
     p.tiles = tiles;
     p.batch = a.batch;
     p.b_bytes = buf ? (unsigned)((long long)a.k * a.n * 4) : 0u;
+    p.csr_bytes = narrow ? (unsigned)((long long)a.nnz * 4) : 0u;
     p.row_indices = a.row_indices;
     p.row_offsets = a.row_offsets;
     p.col_indices = a.col_indices;
@@ -351,6 +450,10 @@ hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream)
     p.stride_values = a.stride_values;
     p.stride_b = a.stride_b;
     p.stride_c = a.stride_c;
+    if (narrow) {
+        const int e = nv <= 1 ? 1 : nv <= 2 ? 2 : 4;
+        return vec ? launch_narrow<4>(e, p, stream) : launch_narrow<1>(e, p, stream);
+    }
     return vec ? launch_lpr<4>(lpr, p, tiles, a.batch, vec_csr, buf, stream)
                : launch_lpr<1>(lpr, p, tiles, a.batch, vec_csr, buf, stream);
 }
