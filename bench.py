@@ -292,17 +292,21 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
                      "cold_us": cold_time_us(torch, fn, flush),
                      "gflops": flops / (us * 1e-6) / 1e9,
                      "compulsory_gbs": byts / (us * 1e-6) / 1e9})
-    # The streaming regime: CSR far larger than every cache, n = 8
-    w = inputs.hbm_stream()
-    a = w["a"]
-    ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
-    b = up(w["b"])
-    c = torch.empty(w["m"], w["n"], device=dev)
-    fn = lambda: sp.sp_spmm(w["m"], w["k"], w["n"], a.nnz, ri, vals, ro, cols, b, c)
-    recs.append(spmm_record(w["name"], w["m"], w["k"], w["n"], a.nnz,
-                            graph_time_us(torch, fn, 20),
-                            {"cold_us": cold_time_us(torch, fn, flush),
-                             "csr_bytes": 8 * a.nnz}))
+    # The streaming regime: CSR far larger than every cache, n = 8 and n = 4
+    # (B in LDS), natural and swizzled row order.
+    for n_cols in (8, 4):
+        w = inputs.hbm_stream(n=n_cols)
+        a = w["a"]
+        ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+        b = up(w["b"])
+        c = torch.empty(w["m"], w["n"], device=dev)
+        for order in (None, ri):
+            fn = lambda: sp.sp_spmm(w["m"], w["k"], w["n"], a.nnz, order, vals, ro, cols, b, c)
+            recs.append(spmm_record(w["name"], w["m"], w["k"], w["n"], a.nnz,
+                                    graph_time_us(torch, fn, 20),
+                                    {"cold_us": cold_time_us(torch, fn, flush),
+                                     "csr_bytes": 8 * a.nnz, "swizzle": order is not None}))
+        del a, ro, ri, cols, vals
     with open(path, "w") as f:
         for r in recs:
             f.write(json.dumps(r) + "\n")

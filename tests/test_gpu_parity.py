@@ -276,6 +276,43 @@ def test_spmm_hbm_stream_sampled_rows():
     assert np.all(np.isfinite(c))
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
+def test_spmm_lds_resident_b(n):
+    # Narrow B that fits in LDS with >= (CUs * k * n) entries: the streaming
+    # kernel with B copied into LDS once per workgroup.
+    m, k = 8192, 256
+    lengths = np.random.default_rng(80 + n).integers(100, 220, m).astype(np.int32)
+    lengths[::97] = 0                                   # some empty rows
+    # nnz = 3 (mod 4) with a non-empty last row: the final 16-byte segment of
+    # the CSR arrays extends past nnz
+    lengths[-1] += (3 - int(lengths.sum()) % 4) % 4
+    assert int(lengths.sum()) % 4 == 3 and lengths[-1] > 0
+    a = csr_of_row_lists(inputs.random_row_lists(81 + n, m, k, lengths))
+    b = inputs.random_dense(82 + n, k, n)
+    note(f"spmm lds-resident B n={n} nnz={a.nnz}")
+    c = run_spmm(a, b, row_indices=swizzle(a))
+    ref, s = oracle.spmm(m, k, n, a.ro, a.ci, a.vals, b)
+    check_close(c, ref, s, f"spmm lds n={n}")
+    # one-entry rows through the same kernel are exact
+    rl = inputs.random_row_lists(83 + n, 1100000, k, np.ones(1100000, np.int32))
+    a1 = csr_of_row_lists(rl)
+    note(f"spmm lds-resident B one-entry rows n={n}")
+    c1 = run_spmm(a1, b)
+    ref1, _ = oracle.spmm(1100000, k, n, a1.ro, a1.ci, a1.vals, b)
+    assert np.array_equal(c1.view(np.int32), ref1.astype(np.float32).view(np.int32))
+
+
+def test_spmm_hbm_stream_n4_sampled_rows():
+    w = inputs.hbm_stream(n=4)
+    a = csr_of_row_lists(w["a"])
+    note("spmm hbm_stream 65536x8192x4 (B in LDS)")
+    c = run_spmm(a, w["b"])
+    rows = np.random.default_rng(71).choice(a.m, 2000, replace=False).astype(np.int32)
+    rows[:2] = [0, a.m - 1]
+    ref, s = oracle.spmm_rows(rows, w["n"], a.ro, a.ci, a.vals, w["b"])
+    check_close(c[rows], ref, s, "spmm hbm_stream n=4")
+
+
 # ------------------------------------------------------------------ SpMM, edges
 
 WIDTHS = [1, 2, 3, 4, 5, 8, 12, 16, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256,

@@ -350,6 +350,201 @@ __global__ __launch_bounds__(kWave) void spmm_narrow_kernel(SpmmParams p)
     if (s == 0 && col_ok) V::store(cz + (size_t)row * (size_t)p.n + col0, acc);
 }
 
+// Narrow B that fits in LDS, with many entries per B element: the streaming
+// regime, where the CSR arrays (8 bytes per entry) are the traffic that must
+// reach HBM speed.  One 1024-thread workgroup per CU copies B into LDS once;
+// its 16 waves then take rows (in row_indices order, round-robin over all
+// waves of the launch).  Lanes split a row's entries in 16-byte segments of 4
+// (lane (s, v): segments s, s + kS, ...; the kE lanes of a segment cover the
+// kE column vectors of B), and each segment's column indices and values are
+// read with one dwordx4 buffer load each, starting from the row's first entry
+// rounded down to a multiple of 4 (entries outside the row are skipped).  With
+// the LDS holding B, only 16 waves fit on a CU, so the 16-byte reads are what
+// keeps enough bytes in flight to stream from HBM.  Batches are issued
+// unconditionally and double-buffered across row boundaries: the wave walks
+// its (row, batch) pairs as one sequence, and the metadata of its next 64 rows
+// sits one row per lane in registers (read with readlane), so a row change
+// costs no memory operation.  The array's last segment, if it extends past
+// nnz, is read from the last 4 entries instead and shifted into place, so no
+// load is ever partly out of range.
+constexpr int kLdsThreads = 1024;
+constexpr int kLdsWaves = kLdsThreads / kWave;
+constexpr unsigned kLdsMaxB = 128u * 1024u;
+
+template <int kE, int kVec>
+__global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
+{
+    using V = Vec<kVec>;
+    using VecT = typename V::T;
+    constexpr int kS = kWave / kE;  // segment slots per step
+    constexpr int kSteps = 4;       // steps per batch
+    constexpr int kBatch = kSteps * kS * 4;  // entries per batch
+    extern __shared__ __align__(16) float s_b[];
+
+    // ---- B into LDS
+    const int tid = threadIdx.x;
+    const int nb = (int)(p.b_bytes / 4u);
+    if constexpr (kVec == 4) {
+        const float4 *b4 = reinterpret_cast<const float4 *>(p.b);
+        for (int i = tid; i < nb / 4; i += kLdsThreads)
+            reinterpret_cast<float4 *>(s_b)[i] = b4[i];
+    } else {
+        for (int i = tid; i < nb; i += kLdsThreads) s_b[i] = p.b[i];
+    }
+    __syncthreads();
+
+    const int lane = tid % kWave;
+    const int s = lane / kE;
+    const int v = lane - s * kE;
+    const int col0 = v * kVec;
+    const bool col_ok = col0 < p.n;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int *>(p.col_indices), 0, (int)p.csr_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(p.values), 0, (int)p.csr_bytes, 0x00020000);
+    const int last4 = p.nnz - 4;  // first entry of the array's last full segment (nnz >= 4)
+
+    const int *__restrict__ order = p.row_indices;
+    const int *__restrict__ offsets = p.row_offsets;
+    float *__restrict__ c_out = p.c;
+    const int stride = gridDim.x * kLdsWaves;
+    const int first = blockIdx.x * kLdsWaves + tid / kWave;
+    if (first >= p.m) return;  // no LDS barrier follows
+    const int rows_of_wave = (p.m - first + stride - 1) / stride;
+
+    int meta_row = 0, meta_p0 = 0, meta_p1 = 0, meta_base = 0;
+    auto load_meta = [&](int t0) {
+        const int t = t0 + lane;
+        const int sl = first + t * stride;
+        const bool ok = t < rows_of_wave;
+        meta_row = ok ? (order ? order[sl] : sl) : 0;
+        meta_p0 = ok ? offsets[meta_row] : 0;
+        meta_p1 = ok ? offsets[meta_row + 1] : 0;
+        meta_base = t0;
+    };
+    struct Batch {
+        int t, row, p0, p1, base;  // base: first entry of the batch (a multiple of 4)
+    };
+    auto row_batch = [&](int t) -> Batch {
+        if (t - meta_base >= kWave) load_meta(t);
+        const int j = t - meta_base;
+        const int p0 = __builtin_amdgcn_readlane(meta_p0, j);
+        return {t, __builtin_amdgcn_readlane(meta_row, j), p0,
+                __builtin_amdgcn_readlane(meta_p1, j), p0 & ~3};
+    };
+    auto next_of = [&](const Batch &cur) -> Batch {
+        if (cur.base + kBatch < cur.p1)
+            return {cur.t, cur.row, cur.p0, cur.p1, cur.base + kBatch};
+        if (cur.t + 1 >= rows_of_wave) return {rows_of_wave, -1, 0, 0, 0};  // empty
+        return row_batch(cur.t + 1);
+    };
+
+    struct Seg {
+        int4 c;
+        float4 v;
+    };
+    auto load = [&](const Batch &b, Seg (&sg)[kSteps]) {
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            const int e = b.base + (u * kS + s) * 4;
+            const bool any = e < b.p1;
+            const unsigned off = !any ? kOutOfRange
+                                      : (unsigned)(e + 4 <= p.nnz ? e : last4) * 4u;
+            const auto c4 = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)off, 0, 0);
+            const auto v4 = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off, 0, 0);
+            sg[u].c = make_int4((int)c4[0], (int)c4[1], (int)c4[2], (int)c4[3]);
+            sg[u].v = make_float4(__uint_as_float(v4[0]), __uint_as_float(v4[1]),
+                                  __uint_as_float(v4[2]), __uint_as_float(v4[3]));
+        }
+    };
+    auto consume = [&](const Batch &b, const Seg (&sg)[kSteps], float *acc) {
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            const int e = b.base + (u * kS + s) * 4;
+            // entry e + t sits at position t + sh of the loaded segment
+            const int sh = e + 4 <= p.nnz ? 0 : e - last4;
+            const int cs[4] = {sg[u].c.x, sg[u].c.y, sg[u].c.z, sg[u].c.w};
+            const float vs[4] = {sg[u].v.x, sg[u].v.y, sg[u].v.z, sg[u].v.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int idx = e + t;
+                if (idx >= b.p0 && idx < b.p1 && col_ok) {
+                    int col = cs[t];
+                    float val = vs[t];
+                    if (sh != 0) {  // only the array's final, shifted segment
+                        const int q = t + sh;
+                        col = q == 1 ? cs[1] : q == 2 ? cs[2] : cs[3];
+                        val = q == 1 ? vs[1] : q == 2 ? vs[2] : vs[3];
+                    }
+                    // Row col of B, this lane's vector: indexed in units of
+                    // the vector so the compiler knows it is 16-byte aligned
+                    // (one ds_read_b128, not two 8-byte reads).
+                    const VecT bv = reinterpret_cast<const VecT *>(s_b)[col * (p.n / kVec) + v];
+                    V::fma(val, bv, acc);
+                }
+            }
+        }
+    };
+    float acc[kVec];
+#pragma unroll
+    for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
+    auto finish_row = [&](int r) {
+#pragma unroll
+        for (int o = kE; o < kWave; o <<= 1) {
+#pragma unroll
+            for (int t = 0; t < kVec; ++t) acc[t] += __shfl_xor(acc[t], o);
+        }
+        if (s == 0 && col_ok) V::store(c_out + (size_t)r * (size_t)p.n + col0, acc);
+#pragma unroll
+        for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
+    };
+
+    load_meta(0);
+    Batch cur = row_batch(0);
+    Seg sa[kSteps], sb[kSteps];
+    load(cur, sa);
+    for (;;) {
+        // Issued unconditionally (an empty next batch is all out of range),
+        // which keeps the compiler's wait counts exact.
+        const Batch nb = next_of(cur);
+        load(nb, sb);
+        keep_issued_above();
+        consume(cur, sa, acc);
+        if (nb.t != cur.t) finish_row(cur.row);
+        if (nb.row < 0) break;
+        cur = nb;
+        const Batch na = next_of(cur);
+        load(na, sa);
+        keep_issued_above();
+        consume(cur, sb, acc);
+        if (na.t != cur.t) finish_row(cur.row);
+        if (na.row < 0) break;
+        cur = na;
+    }
+}
+
+template <int kE, int kVec>
+hipError_t launch_lds_t(const SpmmParams &p, int blocks, hipStream_t s)
+{
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&spmm_lds_kernel<kE, kVec>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMaxB);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((spmm_lds_kernel<kE, kVec>), dim3(blocks), dim3(kLdsThreads),
+                       p.b_bytes, s, p);
+    return hipGetLastError();
+}
+
+template <int kVec>
+hipError_t launch_lds(int e, const SpmmParams &p, int blocks, hipStream_t s)
+{
+    switch (e) {
+    case 1: return launch_lds_t<1, kVec>(p, blocks, s);
+    case 2: return launch_lds_t<2, kVec>(p, blocks, s);
+    default: return launch_lds_t<4, kVec>(p, blocks, s);
+    }
+}
+
 template <int kE, int kVec>
 hipError_t launch_narrow_t(const SpmmParams &p, hipStream_t s)
 {
@@ -452,6 +647,24 @@ hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream)
     p.stride_c = a.stride_c;
     if (narrow) {
         const int e = nv <= 1 ? 1 : nv <= 2 ? 2 : 4;
+        // B in LDS when it fits and every CU has at least as many entries to
+        // stream as it copies B elements (nnz >= CUs * k * n).
+        int cus = 0, lds_max = 0, device = 0;
+        if (hipGetDevice(&device) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock,
+                                  device) != hipSuccess)
+            cus = 0;
+        const long long b_elems = (long long)a.k * a.n;
+        if (a.batch == 1 && cus > 0 && vec_csr && a.nnz >= 4 &&
+            b_elems * 4 <= (long long)kLdsMaxB &&
+            b_elems * 4 <= (long long)lds_max &&
+            (long long)a.nnz >= (long long)cus * b_elems) {
+            const long long want = ((long long)a.m + kLdsWaves - 1) / kLdsWaves;
+            const int blocks = (int)(want < cus ? want : cus);
+            return vec ? launch_lds<4>(e, p, blocks, stream) : launch_lds<1>(e, p, blocks, stream);
+        }
         return vec ? launch_narrow<4>(e, p, stream) : launch_narrow<1>(e, p, stream);
     }
     return vec ? launch_lpr<4>(lpr, p, tiles, a.batch, vec_csr, buf, stream)

@@ -233,13 +233,16 @@ def imbalance(seed: int = DEFAULT_SEED) -> dict:
 def hbm_stream(seed: int = DEFAULT_SEED, m: int = 65536, k: int = 8192,
                n: int = 8, sparsity: float = 0.9) -> dict:
     """A streaming-regime SpMM at 90 % sparsity whose CSR (about 430 MB) is far
-    larger than every on-chip cache, with a narrow dense operand (n = 8): row
-    lengths round(N(819.2, 81.92)), values N(0, 0.02), B 8192x8 N(0,1)."""
+    larger than every on-chip cache, with a narrow dense operand (n = 8, or
+    n = 4 so that B fits in a CU's LDS): row lengths round(N(819.2, 81.92)),
+    values N(0, 0.02), B 8192xn N(0,1)."""
     r = _streams(seed, ["lengths", "cols", "values", "b"])
     lengths = normal_lengths(r["lengths"], m, k, (1.0 - sparsity) * k, 0.1)
     a = row_lists(r["cols"], r["values"], m, k, lengths, 0.02)
+    # B is drawn at its widest (8 columns) and narrowed, so every n shares A.
+    b = normal(r["b"], (k, 8))[:, :n] if n <= 8 else normal(r["b"], (k, n))
     return {"name": f"hbm_stream_{m}x{k}x{n}_s{sparsity:g}", "m": m, "k": k,
-            "n": n, "a": a, "b": normal(r["b"], (k, n))}
+            "n": n, "a": a, "b": np.ascontiguousarray(b)}
 
 
 def random_row_lists(seed: int, m: int, k: int, lengths) -> RowLists:
