@@ -185,6 +185,27 @@ sp_status_t sp_sddmm_batched(int m, int k, int d, int nnz,
                              int batch, long long stride_x, long long stride_y,
                              long long stride_out, sp_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Row softmax over CSR entries ("Interesting ideas" I3 of the card: the SDDMM
+ * form sparse attention needs; softmax over each row's entries is the step
+ * between the attention scores (SDDMM) and their weighted sum (SpMM)).
+ * ---------------------------------------------------------------------- */
+
+/* For each batch entry z < batch and each row i with entries p:
+ *   out_z[p] = exp(in_z[p] - mx) / sum over the row's entries q of
+ *              exp(in_z[q] - mx),   mx = the row's maximum of in_z,
+ * computed in fp32 (expf); rows without entries are left untouched.
+ * in_z = in + z*stride_in, out_z = out + z*stride_out (elements); the CSR
+ * structure (row_offsets, row_indices) is shared by all batch entries.
+ *   row_indices  int32[m] row order, or NULL (identity)
+ *   in, out      fp32, nnz per batch entry; out may equal in (in place),
+ *                otherwise they must not overlap.  stride_out >= nnz when
+ *                batch > 1. */
+sp_status_t sp_csr_row_softmax(int m, int nnz, const int *row_indices,
+                               const int *row_offsets, const float *in, float *out,
+                               int batch, long long stride_in, long long stride_out,
+                               sp_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 11, declared
+    assert len(declared) == 12, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -109,6 +109,20 @@ def test_build_and_swizzle_validation(lib):
     assert lib.sp_row_swizzle(-1, FAKE, FAKE, s) == INVALID
     assert lib.sp_row_swizzle(3, NULL, FAKE, s) == INVALID
     assert lib.sp_row_swizzle(3, FAKE, NULL, s) == INVALID
+
+
+def test_softmax_validation(lib):
+    f = lib.sp_csr_row_softmax
+    s = NULL
+    assert f(-1, 4, NULL, FAKE, FAKE, FAKE, 1, 0, 0, s) == INVALID
+    assert f(3, -4, NULL, FAKE, FAKE, FAKE, 1, 0, 0, s) == INVALID
+    assert f(3, 4, NULL, FAKE, FAKE, FAKE, -1, 0, 0, s) == INVALID
+    assert f(3, 4, NULL, NULL, FAKE, FAKE, 1, 0, 0, s) == INVALID
+    assert f(3, 4, NULL, FAKE, NULL, FAKE, 1, 0, 0, s) == INVALID
+    assert f(3, 4, NULL, FAKE, FAKE, NULL, 1, 0, 0, s) == INVALID
+    assert f(3, 4, NULL, FAKE, FAKE, FAKE, 2, 4, 3, s) == INVALID
+    assert f(0, 4, NULL, NULL, NULL, NULL, 1, 0, 0, s) == OK
+    assert f(3, 0, NULL, FAKE, NULL, NULL, 1, 0, 0, s) == OK
 
 
 def test_missing_library_fails_loudly(monkeypatch):

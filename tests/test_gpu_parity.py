@@ -614,3 +614,110 @@ def test_graph_replays_match_eager(ffn):
         got = [host(t) for t in (ro, ri, c, out)]
         for want, have, name in zip(ref, got, ("row_offsets", "row_indices", "c", "out")):
             assert np.array_equal(want.view(np.int32), have.view(np.int32)), (r, name)
+
+
+# ------------------------------------------------------------------ row softmax
+
+def _softmax_bound(ro, s, p_ref):
+    """Per-element bound of the fp32 softmax: relative (|s - max| + 8) * 2^-23
+    (rounding of s - max amplified by exp, expf itself, the row sum and the
+    division), in units of the exact result."""
+    b = np.zeros_like(p_ref)
+    for i in range(ro.shape[0] - 1):
+        seg = slice(ro[i], ro[i + 1])
+        if ro[i + 1] > ro[i]:
+            x = s[seg].astype(np.float64) - float(s[seg].max())
+            b[seg] = p_ref[seg] * (np.abs(x) + 8.0) * 2.0 ** -23
+    return b
+
+
+def _check_softmax(got, ro, s, what):
+    ref = oracle.softmax_rows(ro, s)
+    bound = _softmax_bound(ro, s, ref)
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.all(np.isfinite(got)), what
+    assert np.all(err <= bound), f"{what}: worst {np.max(err / np.maximum(bound, 1e-300)):.3g}"
+
+
+@pytest.mark.parametrize("case", ["short", "long", "mixed_empty"])
+def test_row_softmax(case):
+    rng = np.random.default_rng({"short": 90, "long": 91, "mixed_empty": 92}[case])
+    if case == "short":
+        lengths = rng.integers(1, 80, 700)
+    elif case == "long":
+        lengths = rng.integers(250, 900, 60)          # beyond the register-held path
+    else:
+        lengths = rng.integers(0, 400, 500)
+        lengths[::7] = 0
+    lengths = lengths.astype(np.int32)
+    m = lengths.shape[0]
+    ro = oracle.csr_offsets_from_lengths(lengths)
+    nnz = int(ro[-1])
+    s = (inputs.random_dense(93, nnz) * np.float32(4.0)).astype(np.float32)
+    d_ro = dev(ro)
+    ri = torch.empty(m, dtype=torch.int32, device="cuda")
+    sp.sp_row_swizzle(m, d_ro, ri)
+    out = torch.full((nnz,), float("nan"), device="cuda")
+    note(f"row softmax {case} m={m} nnz={nnz}")
+    sp.sp_csr_row_softmax(m, nnz, ri, d_ro, dev(s), out)
+    _check_softmax(host(out), ro, s, f"softmax {case}")
+    note(f"row softmax {case} in place")
+    buf = dev(s)
+    sp.sp_csr_row_softmax(m, nnz, None, d_ro, buf, buf)
+    _check_softmax(host(buf), ro, s, f"softmax {case} in place")
+
+
+def test_row_softmax_batched_attention_mask():
+    mask = inputs.attention_mask(4096)
+    ro, ci, _ = oracle.csr_from_dense(mask)
+    nnz = int(ro[-1])
+    batch = 4
+    s = (inputs.random_dense(94, batch, nnz) * np.float32(3.0)).astype(np.float32)
+    out = torch.empty(batch, nnz, device="cuda")
+    note("row softmax batched attention mask")
+    sp.sp_csr_row_softmax(4096, nnz, None, dev(ro), dev(s), out, batch, nnz, nnz)
+    got = host(out)
+    for z in range(batch):
+        _check_softmax(got[z], ro, s[z], f"softmax attention z={z}")
+
+
+def test_sparse_attention_all_device():
+    # SDDMM (scale 1/8) -> row softmax -> SpMM, every step on the device,
+    # against the oracle pipeline in double with the propagated bound: S within
+    # e_S = 1e-5 sum|q k| / 8; softmax maps that to a relative P error of at most
+    # 2 max_row(e_S) plus its own rounding; O inherits sum_j P_j |V_j| times those
+    # relative errors, plus the SpMM's 1e-5.
+    w = inputs.sparse_attention()
+    heads = [0, 7, 31]
+    seq, hd, bh = w["seq"], w["head_dim"], w["batch"]
+    ro, ci, _ = oracle.csr_from_dense(w["mask"])
+    a = DevCsr(seq, seq, ro, ci)
+    nnz = a.nnz
+    ri = swizzle(a)
+    q, kk, v = dev(w["q"]), dev(w["k"]), dev(w["v"])
+    s_dev = torch.empty(bh, nnz, device="cuda")
+    o_dev = torch.empty(bh, seq, hd, device="cuda")
+    note("attention all-device: sddmm, softmax, spmm")
+    sp.sp_sddmm_batched(seq, seq, hd, nnz, ri, a.d_ro, a.d_ci, q, kk, 0.125, s_dev, bh,
+                        seq * hd, seq * hd, nnz)
+    sp.sp_csr_row_softmax(seq, nnz, ri, a.d_ro, s_dev, s_dev, bh, nnz, nnz)
+    sp.sp_spmm_batched(seq, seq, hd, nnz, ri, s_dev, a.d_ro, a.d_ci, v, o_dev, bh, nnz,
+                       seq * hd, seq * hd)
+    o_gpu = host(o_dev)
+    rows = np.repeat(np.arange(seq), np.diff(ro))
+    for z in heads:
+        s_ref, s_abs = oracle.sddmm(seq, seq, hd, ro, ci, w["q"][z], w["k"][z])
+        s_ref, e_s = 0.125 * s_ref, 0.125 * 1e-5 * s_abs
+        p_ref = oracle.softmax_rows(ro, s_ref.astype(np.float32))
+        # row maxima of e_S and of the softmax rounding term
+        e_row = np.zeros(seq)
+        np.maximum.at(e_row, rows, e_s)
+        smax = np.full(seq, -np.inf)
+        np.maximum.at(smax, rows, s_ref)
+        x_row = np.zeros(seq)
+        np.maximum.at(x_row, rows, np.abs(s_ref - smax[rows]))
+        rel = 2.0 * e_row + (x_row + 8.0) * 2.0 ** -23 + 1e-5
+        o_ref, _ = oracle.spmm(seq, seq, hd, ro, ci, p_ref, w["v"][z])
+        pv, _ = oracle.spmm(seq, seq, hd, ro, ci, p_ref, np.abs(w["v"][z]))
+        err = np.abs(o_gpu[z].astype(np.float64) - o_ref)
+        assert np.all(err <= rel[:, None] * pv * 1.01), f"attention head {z}"

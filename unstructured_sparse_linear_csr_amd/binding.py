@@ -43,6 +43,8 @@ SIGNATURES = {
                   _vp, _vp], _c_int),
     "sp_sddmm_batched": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                           _c_float, _vp, _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
+    "sp_csr_row_softmax": ([_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_ll, _c_ll, _vp],
+                           _c_int),
 }
 
 
@@ -185,6 +187,15 @@ def sp_sddmm_batched(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, 
         _ptr(x, _F32, "x", True), _ptr(y, _F32, "y", True), float(alpha),
         _ptr(out, _F32, "out", True), batch, stride_x, stride_y, stride_out,
         _stream(stream)), "sp_sddmm_batched")
+
+
+def sp_csr_row_softmax(m, nnz, row_indices, row_offsets, inp, out, batch=1, stride_in=0,
+                       stride_out=0, stream=None):
+    _check(lib().sp_csr_row_softmax(
+        m, nnz, _ptr(row_indices, _I32, "row_indices", True),
+        _ptr(row_offsets, _I32, "row_offsets"), _ptr(inp, _F32, "in", True),
+        _ptr(out, _F32, "out", True), batch, stride_in, stride_out, _stream(stream)),
+        "sp_csr_row_softmax")
 
 
 # ---------------------------------------------------------------- conveniences

@@ -170,4 +170,19 @@ sp_status_t sp_sddmm(int m, int k, int d, int nnz, const int *row_indices,
                             alpha, out, 1, 0, 0, 0, stream);
 }
 
+sp_status_t sp_csr_row_softmax(int m, int nnz, const int *row_indices,
+                               const int *row_offsets, const float *in, float *out,
+                               int batch, long long stride_in, long long stride_out,
+                               sp_stream_t stream)
+{
+    if (m < 0 || nnz < 0 || batch < 0 || stride_in < 0 || stride_out < 0)
+        return SP_ERROR_INVALID_VALUE;
+    if (m == 0 || nnz == 0 || batch == 0) return SP_SUCCESS;
+    if (!need(row_offsets, m) || in == nullptr || out == nullptr)
+        return SP_ERROR_INVALID_VALUE;
+    if (batch > 1 && stride_out < nnz) return SP_ERROR_INVALID_VALUE;
+    return from_hip(spk::launch_row_softmax(m, row_indices, row_offsets, in, out, batch,
+                                            stride_in, stride_out, as_stream(stream)));
+}
+
 }  // extern "C"
