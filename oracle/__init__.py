@@ -76,6 +76,10 @@ def _load():
     lib.orc_sddmm.argtypes = [c_int, c_int, c_int, _I32P, _I32P, _F32P, _F32P,
                               _F64P, _F64P]
     lib.orc_sddmm.restype = None
+    lib.orc_sddmm_general.argtypes = [c_int, c_int, c_int, _I32P, _I32P, vp, _F32P, _F32P,
+                                      c_int, ctypes.c_double, ctypes.c_double, vp, _F64P,
+                                      _F64P]
+    lib.orc_sddmm_general.restype = None
     lib.orc_softmax_rows.argtypes = [c_int, _I32P, _F32P, _F64P]
     lib.orc_softmax_rows.restype = None
     _lib = lib
@@ -180,6 +184,26 @@ def sddmm(m: int, k: int, d: int, row_offsets, col_indices, x, y):
     a = np.zeros(nnz, np.float64)
     _load().orc_sddmm(m, k, d, ro, _nz(ci), _nz(xx.reshape(-1)),
                       _nz(yy.reshape(-1)), _nz(out), _nz(a))
+    return out, a
+
+
+def sddmm_general(m: int, k: int, d: int, row_offsets, col_indices, x, y, y_layout=0,
+                  mask_values=None, alpha=1.0, beta=0.0, out_in=None):
+    """alpha * v_p * (X Yop)[i, col] + beta * out_in[p] in double, and the
+    tolerance scale -> (out f64[nnz], abs f64[nnz]).  y_layout 0: Y is k x d;
+    1: Y is d x k."""
+    ro, ci, xx, yy = _i32(row_offsets), _i32(col_indices), _f32(x), _f32(y)
+    assert ro.shape == (m + 1,) and xx.shape == (m, d)
+    assert yy.shape == ((k, d) if y_layout == 0 else (d, k))
+    nnz = int(ro[m])
+    mv = None if mask_values is None else _f32(mask_values)
+    oi = None if out_in is None else _f32(out_in)
+    out = np.zeros(nnz, np.float64)
+    a = np.zeros(nnz, np.float64)
+    _load().orc_sddmm_general(m, k, d, ro, _nz(ci), None if mv is None else mv.ctypes.data,
+                              _nz(xx.reshape(-1)), _nz(yy.reshape(-1)), int(y_layout),
+                              float(alpha), float(beta),
+                              None if oi is None else oi.ctypes.data, _nz(out), _nz(a))
     return out, a
 
 

@@ -230,6 +230,39 @@ void orc_sddmm(int m, int k, int d, const int32_t *row_offsets,
     }
 }
 
+/* General SDDMM: the form I3 says is easy to add back -- scaling by the
+ * mask's values, either layout of the second operand, and accumulation:
+ *   out[p] = alpha * v_p * sum over l < d of X[i][l] * Yop(col_indices[p], l)
+ *            + beta * out_in[p]
+ * for each entry p of row i, where v_p = mask_values[p] (1 when mask_values is
+ * NULL) and Yop(c, l) = Y[c][l] with Y stored k x d (y_layout 0) or Y[l][c]
+ * with Y stored d x k (y_layout 1).  With beta == 0, out_in is not read.
+ * abs_sum[p] = |alpha * v_p| * sum |X[i][l] * Yop(c, l)| + |beta * out_in[p]|,
+ * the scale of the fp32 tolerance.  Double arithmetic throughout. */
+void orc_sddmm_general(int m, int k, int d, const int32_t *row_offsets,
+                       const int32_t *col_indices, const float *mask_values,
+                       const float *x, const float *y, int y_layout, double alpha,
+                       double beta, const float *out_in, double *out, double *abs_sum)
+{
+    for (int i = 0; i < m; ++i) {
+        for (int32_t p = row_offsets[i]; p < row_offsets[i + 1]; ++p) {
+            const int c = col_indices[p];
+            double acc = 0.0, mag = 0.0;
+            for (int l = 0; l < d; ++l) {
+                double yv = y_layout == 0 ? (double)y[(long long)c * d + l]
+                                          : (double)y[(long long)l * k + c];
+                double term = (double)x[(long long)i * d + l] * yv;
+                acc += term;
+                mag += fabs(term);
+            }
+            double scale = alpha * (mask_values != NULL ? (double)mask_values[p] : 1.0);
+            double prior = beta != 0.0 ? beta * (double)out_in[p] : 0.0;
+            out[p] = scale * acc + prior;
+            abs_sum[p] = fabs(scale) * mag + fabs(prior);
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Row softmax over CSR entries (the step between SDDMM and SpMM in sparse   */
 /* attention, I3)                                                            */

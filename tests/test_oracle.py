@@ -362,3 +362,56 @@ def test_softmax_shift_invariance_and_uniform_rows():
     p_shift = oracle.softmax_rows(ro, s + np.float32(64.0))
     assert np.allclose(p, p_shift, rtol=1e-14, atol=0)
     assert np.allclose(p[4:], 1.0 / 3.0, rtol=0, atol=1e-16)
+
+
+# ---------------------------------------------------------------- general SDDMM
+
+def test_sddmm_general_hand_example():
+    g = _golden("sddmm_general_hand.json")
+    for case in g["cases"]:
+        y = np.array(case["y"], np.float32)
+        out, a = oracle.sddmm_general(
+            g["m"], g["k"], g["d"], g["row_offsets"], g["col_indices"],
+            np.array(g["x"], np.float32), y, case["y_layout"],
+            None if case["mask_values"] is None else np.array(case["mask_values"], np.float32),
+            case["alpha"], case["beta"],
+            None if case["out_in"] is None else np.array(case["out_in"], np.float32))
+        assert out.tolist() == case["out"], case["name"]
+        assert a.tolist() == case["abs_sum"], case["name"]
+
+
+@pytest.mark.parametrize("seed,m,k,d", [(111, 5, 7, 3), (112, 9, 4, 6), (113, 3, 8, 1)])
+def test_sddmm_general_brute_force(seed, m, k, d):
+    rng = np.random.default_rng(seed)
+    mask = (rng.random((m, k)) < 0.6).astype(np.uint8)
+    ro, ci, mv = oracle.csr_from_dense(mask, rng.standard_normal((m, k)).astype(np.float32))
+    x = rng.standard_normal((m, d)).astype(np.float32)
+    y_kd = rng.standard_normal((k, d)).astype(np.float32)
+    prior = rng.standard_normal(int(ro[-1])).astype(np.float32)
+    alpha, beta = -1.5, 0.25
+    want = []
+    for i in range(m):
+        for q in range(ro[i], ro[i + 1]):
+            dot = 0.0
+            for l in range(d):
+                dot += float(x[i, l]) * float(y_kd[ci[q], l])
+            want.append(alpha * float(mv[q]) * dot + beta * float(prior[q]))
+    out0, _ = oracle.sddmm_general(m, k, d, ro, ci, x, y_kd, 0, mv, alpha, beta, prior)
+    # the d x k layout of the same operand gives the same sums in the same order
+    out1, _ = oracle.sddmm_general(m, k, d, ro, ci, x, np.ascontiguousarray(y_kd.T), 1, mv,
+                                   alpha, beta, prior)
+    assert out0.tolist() == want
+    assert out1.tolist() == want
+
+
+def test_sddmm_general_reduces_to_specialised_form():
+    w = inputs.tiny()
+    ro, ci, _ = oracle.csr_from_dense(w["mask"])
+    spec, spec_abs = oracle.sddmm(256, 256, 32, ro, ci, w["x"], w["y"])
+    gen, gen_abs = oracle.sddmm_general(256, 256, 32, ro, ci, w["x"], w["y"])
+    assert np.array_equal(spec, gen) and np.array_equal(spec_abs, gen_abs)
+    # alpha = 0: only the accumulated prior remains, scaled exactly
+    prior = inputs.random_dense(5, int(ro[-1]))
+    only, _ = oracle.sddmm_general(256, 256, 32, ro, ci, w["x"], w["y"], 0, None, 0.0, 2.0,
+                                   prior)
+    assert np.array_equal(only, 2.0 * prior.astype(np.float64))
