@@ -250,6 +250,23 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
                          "compulsory_gbs": sddmm_bytes(m, k, d, a.nnz) / (us * 1e-6) / 1e9})
         recs.append({"record": "row_swizzle", "workload": w["name"], "m": m,
                      "us": graph_time_us(torch, lambda: sp.sp_row_swizzle(m, ro, ri), 200)})
+        if w["name"] != inputs.transformer_ffn()["name"]:
+            continue
+        # General SDDMM on the same shapes: the mask's values as the element-wise
+        # scale and accumulation into the previous output, with Y stored k x d
+        # and d x k.
+        y_dk = y.t().contiguous()
+        for layout, yy in ((sp.SP_Y_KD, y), (sp.SP_Y_DK, y_dk)):
+            gfn = lambda: sp.sp_sddmm_general(m, k, d, a.nnz, ri, ro, cols, vals, x, yy,
+                                              layout, 0.5, 1.0, out)
+            us = graph_time_us(torch, gfn, 200)
+            recs.append({"record": "sddmm_general", "workload": w["name"], "m": m, "k": k,
+                         "d": d, "nnz": a.nnz, "y_layout": "kd" if layout == sp.SP_Y_KD
+                         else "dk", "mask_values": True, "beta": 1.0, "us": us,
+                         "cold_us": cold_time_us(torch, gfn, flush),
+                         "gflops": 2.0 * a.nnz * d / (us * 1e-6) / 1e9,
+                         "compulsory_gbs": (sddmm_bytes(m, k, d, a.nnz) + 8 * a.nnz)
+                         / (us * 1e-6) / 1e9})
     # ResNet-50 1x1 conv
     w = inputs.resnet_1x1()
     a = w["a"]
@@ -262,8 +279,9 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
     # LSTM sweep with the dense comparison
     be = lstm_breakeven(torch, sp, inputs, dev, records=recs, flush=flush)
     recs.append({"record": "breakeven", **be})
-    # Sparse attention: batched SDDMM (scores, scale 1/8) and batched SpMM
-    # (P V) over one shared mask; the host softmax between them is not timed.
+    # Sparse attention over one shared mask: batched SDDMM (scores, scale
+    # 1/8), the row softmax in place, batched SpMM (P V), each alone and the
+    # three as one graph; and the scores with K given d x k.
     w = inputs.sparse_attention()
     bh, seq, hd = w["batch"], w["seq"], w["head_dim"]
     mk = up(w["mask"])
@@ -282,11 +300,33 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
                                       bh, seq * hd, seq * hd, nnz)
     pfn = lambda: sp.sp_spmm_batched(seq, seq, hd, nnz, ri, p_vals, ro, cols, v, o, bh,
                                      nnz, seq * hd, seq * hd)
-    for kind, fn in (("sddmm_batched", sfn), ("spmm_batched", pfn)):
+    kt = kk.transpose(1, 2).contiguous()
+    tfn = lambda: sp.sp_sddmm_general(seq, seq, hd, nnz, ri, ro, cols, None, q, kt,
+                                      sp.SP_Y_DK, 0.125, 0.0, s_out, bh, 0, seq * hd,
+                                      seq * hd, nnz)
+    smfn = lambda: sp.sp_csr_row_softmax(seq, nnz, ri, ro, s_out, s_out, bh, nnz, nnz)
+
+    def attention():
+        sfn()
+        smfn()
+        sp.sp_spmm_batched(seq, seq, hd, nnz, ri, s_out, ro, cols, v, o, bh, nnz, seq * hd,
+                           seq * hd)
+
+    for kind, fn in (("sddmm_batched", sfn), ("sddmm_general_dk_batched", tfn),
+                     ("row_softmax_batched", smfn), ("spmm_batched", pfn),
+                     ("attention_all_device", attention)):
         us = graph_time_us(torch, fn, 20)
         flops = 2.0 * bh * nnz * hd
-        byts = bh * (sddmm_bytes(seq, seq, hd, nnz) if kind.startswith("sddmm")
-                     else spmm_bytes(seq, seq, hd, nnz))
+        if kind == "row_softmax_batched":
+            flops = 0.0
+            byts = bh * 8 * nnz + 8 * seq
+        elif kind == "attention_all_device":
+            flops = 4.0 * bh * nnz * hd
+            byts = bh * (sddmm_bytes(seq, seq, hd, nnz) + 8 * nnz
+                         + spmm_bytes(seq, seq, hd, nnz))
+        else:
+            byts = bh * (sddmm_bytes(seq, seq, hd, nnz) if kind.startswith("sddmm")
+                         else spmm_bytes(seq, seq, hd, nnz))
         recs.append({"record": kind, "workload": w["name"], "batch": bh, "seq": seq,
                      "head_dim": hd, "nnz_per_head": nnz, "us": us,
                      "cold_us": cold_time_us(torch, fn, flush),

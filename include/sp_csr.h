@@ -185,6 +185,37 @@ sp_status_t sp_sddmm_batched(int m, int k, int d, int nnz,
                              int batch, long long stride_x, long long stride_y,
                              long long stride_out, sp_stream_t stream);
 
+/* Layout of SDDMM's second operand Y. */
+typedef enum sp_y_layout {
+    SP_Y_KD = 0, /* Y stored k x d: Yop(c, l) = y[c*d + l] (the transposed form) */
+    SP_Y_DK = 1  /* Y stored d x k: Yop(c, l) = y[l*k + c] */
+} sp_y_layout_t;
+
+/* General SDDMM ("Interesting ideas" I3 of the card: the specialised form
+ * above leaves out the element-wise scaling by the mask's values and assumes a
+ * transposed operand; the card notes the general case is easy to add back).
+ * For each batch entry z < batch and each entry p of row i:
+ *   out_z[p] = alpha * v_z[p] * sum over l < d of X_z[i][l] * Yop_z(col_indices[p], l)
+ *              + beta * out_z[p]
+ * with v_z = mask_values + z*stride_values (v = 1 when mask_values is NULL),
+ * x_z = x + z*stride_x, y_z = y + z*stride_y, out_z = out + z*stride_out.
+ *   y_layout     SP_Y_KD or SP_Y_DK (anything else: SP_ERROR_INVALID_VALUE).
+ *                SP_Y_DK gathers single elements along rows of Y and is
+ *                several times slower than SP_Y_KD for the same product.
+ *   mask_values  fp32[nnz] per batch entry, or NULL
+ *   beta         0: out is overwritten and never read (it may hold NaN);
+ *                otherwise out holds the prior values and is updated in place.
+ * Everything else as sp_sddmm_batched, which is this call with mask_values =
+ * NULL, y_layout = SP_Y_KD and beta = 0.  Each output's dot product is summed
+ * in l order per entry; deterministic run to run. */
+sp_status_t sp_sddmm_general(int m, int k, int d, int nnz, const int *row_indices,
+                             const int *row_offsets, const int *col_indices,
+                             const float *mask_values, const float *x, const float *y,
+                             int y_layout, float alpha, float beta, float *out, int batch,
+                             long long stride_values, long long stride_x,
+                             long long stride_y, long long stride_out,
+                             sp_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Row softmax over CSR entries ("Interesting ideas" I3 of the card: the SDDMM
  * form sparse attention needs; softmax over each row's entries is the step

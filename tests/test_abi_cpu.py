@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 12, declared
+    assert len(declared) == 13, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -73,6 +73,35 @@ def test_spmm_validation(lib):
     assert f(4, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, 0, 0, 0, 0, s) == OK
     assert lib.sp_spmm(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, s) == OK
     assert lib.sp_spmm(-2, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, s) == INVALID
+
+
+def test_sddmm_general_validation(lib):
+    f = lib.sp_sddmm_general
+    s = NULL
+    fl = ctypes.c_float
+
+    def call(m=4, k=4, d=4, nnz=8, ro=FAKE, ci=FAKE, mv=NULL, x=FAKE, y=FAKE, layout=0,
+             out=FAKE, batch=1, sv=0, sx=0, sy=0, so=0):
+        return f(m, k, d, nnz, NULL, ro, ci, mv, x, y, layout, fl(1.0), fl(0.5), out, batch,
+                 sv, sx, sy, so, s)
+
+    assert call(layout=2) == INVALID
+    assert call(layout=-1) == INVALID
+    assert call(m=-1) == INVALID
+    assert call(d=-1) == INVALID
+    assert call(sv=-1) == INVALID
+    assert call(ro=NULL) == INVALID
+    assert call(ci=NULL) == INVALID
+    assert call(x=NULL) == INVALID
+    assert call(y=NULL, layout=1) == INVALID
+    assert call(out=NULL) == INVALID
+    assert call(batch=2, so=7) == INVALID
+    # a bad layout is rejected even for an empty problem
+    assert call(m=0, layout=3) == INVALID
+    # empty problems succeed without launching anything
+    assert call(m=0, ro=NULL, ci=NULL, x=NULL, y=NULL, out=NULL) == OK
+    assert call(nnz=0, ci=NULL, out=NULL, layout=1) == OK
+    assert call(batch=0) == OK
 
 
 def test_sddmm_validation(lib):

@@ -24,6 +24,8 @@ SP_SUCCESS = 0
 SP_ERROR_INVALID_VALUE = 1
 SP_ERROR_NOT_SUPPORTED = 2
 SP_ERROR_LAUNCH_FAILED = 3
+SP_Y_KD = 0  # SDDMM operand Y stored k x d
+SP_Y_DK = 1  # SDDMM operand Y stored d x k
 
 # Every symbol include/sp_csr.h declares, with its ctypes signature.
 _c_int, _c_ll, _c_float, _vp = ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_void_p
@@ -43,6 +45,9 @@ SIGNATURES = {
                   _vp, _vp], _c_int),
     "sp_sddmm_batched": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                           _c_float, _vp, _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
+    "sp_sddmm_general": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+                          _c_int, _c_float, _c_float, _vp, _c_int, _c_ll, _c_ll, _c_ll,
+                          _c_ll, _vp], _c_int),
     "sp_csr_row_softmax": ([_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_ll, _c_ll, _vp],
                            _c_int),
 }
@@ -187,6 +192,18 @@ def sp_sddmm_batched(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, 
         _ptr(x, _F32, "x", True), _ptr(y, _F32, "y", True), float(alpha),
         _ptr(out, _F32, "out", True), batch, stride_x, stride_y, stride_out,
         _stream(stream)), "sp_sddmm_batched")
+
+
+def sp_sddmm_general(m, k, d, nnz, row_indices, row_offsets, col_indices, mask_values, x, y,
+                     y_layout, alpha, beta, out, batch=1, stride_values=0, stride_x=0,
+                     stride_y=0, stride_out=0, stream=None):
+    _check(lib().sp_sddmm_general(
+        m, k, d, nnz, _ptr(row_indices, _I32, "row_indices", True),
+        _ptr(row_offsets, _I32, "row_offsets"), _ptr(col_indices, _I32, "col_indices", True),
+        _ptr(mask_values, _F32, "mask_values", True), _ptr(x, _F32, "x", True),
+        _ptr(y, _F32, "y", True), int(y_layout), float(alpha), float(beta),
+        _ptr(out, _F32, "out", True), batch, stride_values, stride_x, stride_y, stride_out,
+        _stream(stream)), "sp_sddmm_general")
 
 
 def sp_csr_row_softmax(m, nnz, row_indices, row_offsets, inp, out, batch=1, stride_in=0,

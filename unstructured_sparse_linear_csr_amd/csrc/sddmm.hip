@@ -2,7 +2,9 @@
 // entry p of row i ("Sparse GPU Kernels for Deep Learning", summary card,
 // "Summary" and "Interesting ideas" I3: the specialised form with no scaling
 // by mask values and the second operand transposed, so that X and Y are both
-// read by contiguous rows).
+// read by contiguous rows).  The general form I3 leaves out is an epilogue of
+// the same kernels (scaling by the mask's values, out = ... + beta * out) and,
+// for Y stored d x k, a second kernel that deals lanes to entries.
 //
 // Mapping.  One wavefront (= one workgroup) per mask row.  The wave is split
 // into 64/kG groups of kG lanes; a group computes one entry's dot product at a
@@ -36,13 +38,27 @@ struct SddmmParams {
     const int *row_indices;
     const int *row_offsets;
     const int *col_indices;
+    const float *mask_values;  // NULL: scale by alpha only
     const float *x;
     const float *y;
-    float alpha;
+    int k;
+    float alpha, beta;
     unsigned y_bytes;  // bytes of one Y operand (buffer path)
     float *out;
-    long long stride_x, stride_y, stride_out;
+    long long stride_values, stride_x, stride_y, stride_out;
 };
+
+// out[q] = alpha * v_q * dot + beta * out[q] for the entry q a lane finished.
+// beta == 0 leaves out unread (it may hold anything, NaN included).
+__device__ __forceinline__ void store_entry(const SddmmParams &p, long long z, int q, float dot)
+{
+    float scale = p.alpha;
+    if (p.mask_values) scale *= p.mask_values[z * p.stride_values + q];
+    float *o = p.out + z * p.stride_out + q;
+    float r = scale * dot;
+    if (p.beta != 0.f) r = fmaf(p.beta, *o, r);
+    *o = r;
+}
 
 template <int kVec> struct DVec;
 template <> struct DVec<4> {
@@ -117,7 +133,6 @@ __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
 
     const float *__restrict__ xr_ptr = p.x + z * p.stride_x + (size_t)row * (size_t)p.d;
     const float *__restrict__ yz = p.y + z * p.stride_y;
-    float *__restrict__ oz = p.out + z * p.stride_out;
 
     if constexpr (kNv == 0) {
         __shared__ int s_col[kWave];
@@ -140,7 +155,7 @@ __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
                 if (gl == s) res = sum;
             }
             const int jo = gl * kNg + g;
-            if (jo < cnt) oz[base + jo] = p.alpha * res;
+            if (jo < cnt) store_entry(p, z, base + jo, res);
             __syncthreads();
         }
     } else {
@@ -200,9 +215,58 @@ __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
                 reduce_batch((bt + 1) * kU, yb, res);
             }
             const int jo = gl * kNg + g;  // the entry whose sum this lane kept
-            if (jo < cnt) oz[base + jo] = p.alpha * res;
+            if (jo < cnt) store_entry(p, z, base + jo, res);
             __syncthreads();
         }
+    }
+}
+
+// Y stored d x k (the operand not transposed): Yop(c, l) = Y[l][c].  One wave
+// per row slot as above, but lanes are dealt to entries, 64 at a time: for each
+// l the wave gathers Y[l][c] of its 64 columns -- all within row l of Y, whose
+// columns ascend with the lanes -- and multiplies by X[i][l], which every lane
+// shares (a wave-uniform, scalar load).  Each lane sums its entry's d products
+// in order with FMA; kU gathers are issued before their FMAs.  Idle lanes of a
+// row's last pass gather column 0 (in bounds) and store nothing.
+template <bool kBuf>
+__global__ __launch_bounds__(kWave) void sddmm_cols_kernel(SddmmParams p)
+{
+    constexpr int kU = 16;
+    const long long w = xcd_work_index(p.batch, p.m);
+    if (w < 0) return;
+    const long long z = w / p.m;
+    const int slot = (int)(w - z * p.m);
+    const int lane = threadIdx.x;
+    const int row = p.row_indices ? p.row_indices[slot] : slot;
+    const int p0 = p.row_offsets[row];
+    const int p1 = p.row_offsets[row + 1];
+    const float *__restrict__ xr = p.x + z * p.stride_x + (size_t)row * (size_t)p.d;
+    const float *__restrict__ yz = p.y + z * p.stride_y;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(yz), 0, (int)p.y_bytes, 0x00020000);
+    const unsigned row_bytes = (unsigned)p.k * 4u;
+
+    for (int base = p0; base < p1; base += kWave) {
+        const int q = base + lane;
+        const bool live = q < p1;
+        const int c = live ? p.col_indices[q] : 0;
+        float acc = 0.f;
+        int l = 0;
+        for (; l + kU <= p.d; l += kU) {
+            float yv[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if constexpr (kBuf)
+                    yv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        rsrc, (int)((unsigned)(l + u) * row_bytes + (unsigned)c * 4u), 0, 0));
+                else
+                    yv[u] = yz[(size_t)(l + u) * (size_t)p.k + (size_t)c];
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) acc = fmaf(xr[l + u], yv[u], acc);
+        }
+        for (; l < p.d; ++l) acc = fmaf(xr[l], yz[(size_t)l * (size_t)p.k + (size_t)c], acc);
+        if (live) store_entry(p, z, q, acc);
     }
 }
 
@@ -264,12 +328,43 @@ hipError_t launch_fill_zero(float *dst, long long count, hipStream_t stream)
 
 // Lanes per entry kG: the smallest of 4/8/16 covering the row's vectors (16
 // beyond).  Vectors per lane kNv rounded up to 1/2/4/8; wider rows take the
-// kNv == 0 loop.  d == 0 zero-fills every batch's outputs.
+// kNv == 0 loop.  d == 0 with no mask values and beta == 0 zero-fills every
+// batch's outputs; otherwise the kernels run with empty dot products.
 hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream)
 {
     if (a.m == 0 || a.nnz == 0) return hipSuccess;
     if (xcd_grid(a.batch, a.m) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (a.d == 0) {
+    SddmmParams p;
+    p.m = a.m;
+    p.batch = a.batch;
+    p.d = a.d;
+    p.k = a.k;
+    p.nnz = a.nnz;
+    p.row_indices = a.row_indices;
+    p.row_offsets = a.row_offsets;
+    p.col_indices = a.col_indices;
+    p.mask_values = a.mask_values;
+    p.x = a.x;
+    p.y = a.y;
+    p.alpha = a.alpha;
+    p.beta = a.beta;
+    p.out = a.out;
+    p.stride_values = a.stride_values;
+    p.stride_x = a.stride_x;
+    p.stride_y = a.stride_y;
+    p.stride_out = a.stride_out;
+    if (a.y_layout == 1) {
+        // Buffer offsets (l*k + c)*4 must stay below 2^31.
+        const bool buf = (long long)a.k * (long long)a.d <= (1LL << 29);
+        p.y_bytes = buf ? (unsigned)((long long)a.k * a.d * 4) : 0u;
+        const dim3 grid((unsigned)xcd_grid(a.batch, a.m));
+        if (buf)
+            hipLaunchKernelGGL(sddmm_cols_kernel<true>, grid, dim3(kWave), 0, stream, p);
+        else
+            hipLaunchKernelGGL(sddmm_cols_kernel<false>, grid, dim3(kWave), 0, stream, p);
+        return hipGetLastError();
+    }
+    if (a.d == 0 && a.mask_values == nullptr && a.beta == 0.f) {
         const long long blocks = std::min<long long>((a.nnz + 255) / 256, 65536);
         hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks, (unsigned)a.batch),
                            dim3(256), 0, stream, a.out, (long long)a.nnz, a.stride_out);
@@ -286,23 +381,7 @@ hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream)
     const int need = (dv + g - 1) / g;
     int nv = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
     if (!buf) nv = 0;
-
-    SddmmParams p;
-    p.m = a.m;
-    p.batch = a.batch;
-    p.d = a.d;
-    p.nnz = a.nnz;
-    p.row_indices = a.row_indices;
-    p.row_offsets = a.row_offsets;
-    p.col_indices = a.col_indices;
-    p.x = a.x;
-    p.y = a.y;
-    p.alpha = a.alpha;
     p.y_bytes = buf ? (unsigned)((long long)a.k * a.d * 4) : 0u;
-    p.out = a.out;
-    p.stride_x = a.stride_x;
-    p.stride_y = a.stride_y;
-    p.stride_out = a.stride_out;
     return vec ? launch_g<4>(g, nv, p, a.batch, stream)
                : launch_g<1>(g, nv, p, a.batch, stream);
 }

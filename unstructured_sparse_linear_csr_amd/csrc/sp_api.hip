@@ -129,15 +129,17 @@ sp_status_t sp_spmm(int m, int k, int n, int nnz, const int *row_indices,
                            col_indices, b, c, 1, 0, 0, 0, stream);
 }
 
-sp_status_t sp_sddmm_batched(int m, int k, int d, int nnz, const int *row_indices,
+sp_status_t sp_sddmm_general(int m, int k, int d, int nnz, const int *row_indices,
                              const int *row_offsets, const int *col_indices,
-                             const float *x, const float *y, float alpha, float *out,
-                             int batch, long long stride_x, long long stride_y,
-                             long long stride_out, sp_stream_t stream)
+                             const float *mask_values, const float *x, const float *y,
+                             int y_layout, float alpha, float beta, float *out, int batch,
+                             long long stride_values, long long stride_x,
+                             long long stride_y, long long stride_out, sp_stream_t stream)
 {
-    if (m < 0 || k < 0 || d < 0 || nnz < 0 || batch < 0 || stride_x < 0 ||
-        stride_y < 0 || stride_out < 0)
+    if (m < 0 || k < 0 || d < 0 || nnz < 0 || batch < 0 || stride_values < 0 ||
+        stride_x < 0 || stride_y < 0 || stride_out < 0)
         return SP_ERROR_INVALID_VALUE;
+    if (y_layout != SP_Y_KD && y_layout != SP_Y_DK) return SP_ERROR_INVALID_VALUE;
     if (m == 0 || nnz == 0 || batch == 0) return SP_SUCCESS;
     if (!need(row_offsets, m) || !need(col_indices, nnz) || out == nullptr ||
         !need(x, (long long)m * d) || !need(y, (long long)k * d))
@@ -151,15 +153,30 @@ sp_status_t sp_sddmm_batched(int m, int k, int d, int nnz, const int *row_indice
     a.row_indices = row_indices;
     a.row_offsets = row_offsets;
     a.col_indices = col_indices;
+    a.mask_values = mask_values;
     a.x = x;
     a.y = y;
+    a.y_layout = y_layout;
     a.alpha = alpha;
+    a.beta = beta;
     a.out = out;
     a.batch = batch;
+    a.stride_values = stride_values;
     a.stride_x = stride_x;
     a.stride_y = stride_y;
     a.stride_out = stride_out;
     return from_hip(spk::launch_sddmm(a, as_stream(stream)));
+}
+
+sp_status_t sp_sddmm_batched(int m, int k, int d, int nnz, const int *row_indices,
+                             const int *row_offsets, const int *col_indices,
+                             const float *x, const float *y, float alpha, float *out,
+                             int batch, long long stride_x, long long stride_y,
+                             long long stride_out, sp_stream_t stream)
+{
+    return sp_sddmm_general(m, k, d, nnz, row_indices, row_offsets, col_indices, nullptr, x,
+                            y, SP_Y_KD, alpha, 0.f, out, batch, 0, stride_x, stride_y,
+                            stride_out, stream);
 }
 
 sp_status_t sp_sddmm(int m, int k, int d, int nnz, const int *row_indices,

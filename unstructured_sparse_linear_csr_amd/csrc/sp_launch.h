@@ -23,12 +23,14 @@ struct SddmmArgs {
     const int *row_indices;  // NULL = identity order
     const int *row_offsets;
     const int *col_indices;
+    const float *mask_values;  // NULL = no scaling by the mask's values
     const float *x;
     const float *y;
-    float alpha;
+    int y_layout;  // 0: Y is k x d; 1: Y is d x k
+    float alpha, beta;  // beta == 0: out is not read
     float *out;
     int batch;
-    long long stride_x, stride_y, stride_out;  // elements
+    long long stride_values, stride_x, stride_y, stride_out;  // elements
 };
 
 hipError_t launch_offsets_from_lengths(int m, const int *lengths,
