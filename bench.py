@@ -38,6 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X FP32 vector, published (counts packed FP32)
 FP32_FMA_PEAK_TFLOPS = 78.6      # 256 CU x 64 FMA/clk x 2 x 2.4 GHz: unpacked FMA (the build's)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spmm_transformer_ffn_traffic.json")
+STREAM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spmm_lds_hbm_stream_traffic.json")
 SPMM_SOURCE = os.path.join(ROOT, "unstructured_sparse_linear_csr_amd", "csrc", "spmm.hip")
 
 
@@ -61,6 +62,10 @@ def parse_args():
     ap.add_argument("--suite", metavar="JSONL", default=None,
                     help="also time every workload (warm and cold caches) and "
                          "write one JSON record per kernel run to this file")
+    ap.add_argument("--no-stream", action="store_true",
+                    help="skip the streaming-regime SpMM (CSR far beyond the caches)")
+    ap.add_argument("--profile-stream", action="store_true",
+                    help="with --profile-launches: also launch the streaming-regime SpMM")
     ap.add_argument("--profile-launches", type=int, default=0,
                     help="only run this many eager launches of each kernel "
                          "(for rocprofv3 counter passes) and exit")
@@ -93,11 +98,11 @@ def sddmm_bytes(m, k, d, nnz) -> int:
     return 4 * m * d + 4 * k * d + 4 * nnz + 4 * nnz + 4 * (m + 1) + 4 * m
 
 
-def traffic_record():
+def traffic_record(path=TRAFFIC_FILE):
     """Measured HBM bytes per SpMM launch from the committed counter passes,
     if they were taken on the current kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
         with open(SPMM_SOURCE, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
@@ -218,6 +223,35 @@ def lstm_breakeven(torch, sp, inputs, dev, reps=50, records=None, flush=None):
             "breakeven_sparsity": breakeven,
             "note": ("sparsity where SpMM time equals dense fp32 GEMM time, "
                      "linearly interpolated; null if the sweep has no crossing")}
+
+
+def stream_setup(torch, sp, inputs, dev):
+    """The streaming regime: A 65536 x 8192 at 90 % sparsity (53.7 M entries,
+    430 MB of CSR, far beyond L2 and MALL), B 8192 x 4 held in LDS, natural
+    row order.  Returns (launch, workload description)."""
+    w = inputs.hbm_stream(n=4)
+    a = w["a"]
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    ro = up(np.concatenate([[0], np.cumsum(a.lengths)]).astype(np.int32))
+    cols, vals, b = up(a.cols), up(a.values), up(w["b"])
+    c = torch.empty(w["m"], w["n"], device=dev)
+    m, k, n, nnz = w["m"], w["k"], w["n"], a.nnz
+    fn = lambda: sp.sp_spmm(m, k, n, nnz, None, vals, ro, cols, b, c)
+    return fn, {"workload": w["name"], "m": m, "k": k, "n": n, "nnz": nnz}
+
+
+def stream_record(torch, sp, inputs, dev) -> dict:
+    """Average launch time of the streaming-regime SpMM (graph of 20
+    launches, events on the launch stream) against the HBM roofline."""
+    fn, desc = stream_setup(torch, sp, inputs, dev)
+    us = graph_time_us(torch, fn, 20)
+    alg = spmm_bytes(desc["m"], desc["k"], desc["n"], desc["nnz"])
+    gbs = alg / (us * 1e-6) / 1e9
+    return {**desc, "kernel": "spmm (B in LDS)", "avg_us": us,
+            "gflops": 2.0 * desc["nnz"] * desc["n"] / (us * 1e-6) / 1e9,
+            "algorithmic_bytes_per_launch": alg, "achieved_gbs": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+            "traffic": traffic_record(STREAM_TRAFFIC_FILE)}
 
 
 def run_suite(torch, sp, inputs, dev, path: str) -> None:
@@ -413,6 +447,10 @@ def main() -> int:
         for fn in (k_build, k_offsets, k_swizzle, k_spmm, k_sddmm):
             for _ in range(args.profile_launches):
                 fn()
+        if args.profile_stream:
+            fn, _ = stream_setup(torch, sp, inputs, dev)
+            for _ in range(args.profile_launches):
+                fn()
         # a plain copy of known size, to calibrate the byte counters
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
         dst = torch.empty_like(src)
@@ -513,6 +551,12 @@ def main() -> int:
 
     if not args.no_breakeven:
         result["breakeven"] = lstm_breakeven(torch, sp, inputs, dev)
+
+    if not args.no_stream:
+        result["streaming"] = stream_record(torch, sp, inputs, dev)
+        log(f"streaming spmm: {result['streaming']['avg_us']:.1f} us "
+            f"{result['streaming']['achieved_gbs']:.0f} GB/s "
+            f"({100 * result['streaming']['frac_hbm_peak']:.1f} % of HBM peak)")
 
     if args.suite:
         run_suite(torch, sp, inputs, dev, args.suite)
