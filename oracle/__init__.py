@@ -80,6 +80,11 @@ def _load():
                                       c_int, ctypes.c_double, ctypes.c_double, vp, _F64P,
                                       _F64P]
     lib.orc_sddmm_general.restype = None
+    lib.orc_csr_transpose.argtypes = [c_int, c_int, _I32P, _I32P, vp, _I32P, _I32P, vp, vp]
+    lib.orc_csr_transpose.restype = None
+    lib.orc_spmm_transposed.argtypes = [c_int, c_int, c_int, _I32P, _I32P, _F32P, _F32P,
+                                        _F64P, _F64P]
+    lib.orc_spmm_transposed.restype = None
     lib.orc_softmax_rows.argtypes = [c_int, _I32P, _F32P, _F64P]
     lib.orc_softmax_rows.restype = None
     _lib = lib
@@ -205,6 +210,33 @@ def sddmm_general(m: int, k: int, d: int, row_offsets, col_indices, x, y, y_layo
                               float(alpha), float(beta),
                               None if oi is None else oi.ctypes.data, _nz(out), _nz(a))
     return out, a
+
+
+def csr_transpose(m: int, k: int, row_offsets, col_indices, values=None):
+    """CSR of A^T -> (t_row_offsets[k+1], t_col_indices, t_values|None, t_perm)."""
+    ro, ci = _i32(row_offsets), _i32(col_indices)
+    assert ro.shape == (m + 1,)
+    nnz = int(ro[m])
+    t_ro = np.zeros(k + 1, np.int32)
+    t_ci = np.zeros(max(nnz, 1), np.int32)
+    t_perm = np.zeros(max(nnz, 1), np.int32)
+    v = None if values is None else _f32(values)
+    t_v = None if values is None else np.zeros(max(nnz, 1), np.float32)
+    _load().orc_csr_transpose(m, k, ro, _nz(ci), None if v is None else _nz(v).ctypes.data,
+                              t_ro, t_ci, None if t_v is None else t_v.ctypes.data,
+                              t_perm.ctypes.data)
+    return t_ro, t_ci[:nnz], (None if t_v is None else t_v[:nnz]), t_perm[:nnz]
+
+
+def spmm_transposed(m: int, k: int, n: int, row_offsets, col_indices, values, dy):
+    """dX = A^T dY in double -> (dx f64[k,n], abs f64[k,n])."""
+    ro, ci, v, d = _i32(row_offsets), _i32(col_indices), _f32(values), _f32(dy)
+    assert ro.shape == (m + 1,) and d.shape == (m, n)
+    dx = np.zeros((k, n), np.float64)
+    a = np.zeros((k, n), np.float64)
+    _load().orc_spmm_transposed(m, k, n, ro, _nz(ci), _nz(v), _nz(d.reshape(-1)),
+                                _nz(dx.reshape(-1)), _nz(a.reshape(-1)))
+    return dx, a
 
 
 def softmax_rows(row_offsets, s):

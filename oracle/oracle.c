@@ -200,6 +200,74 @@ void orc_spmm_rows(int nrows, const int32_t *rows, int n,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Transpose and the transposed product (the backward pass of a sparse      */
+/* layer: the card's "Summary" speaks of training, and the input gradient   */
+/* of C = A B is dB = A^T dC)                                               */
+/* ------------------------------------------------------------------------ */
+
+/* CSR of A^T (k x m) from the CSR of A (m x k): row j of A^T lists the rows i
+ * of A that hold an entry in column j, ascending, each with that entry's
+ * value -- so the result is again standard CSR.  A counting sort by column:
+ * count the entries of each column, take the exclusive prefix sum as the row
+ * offsets of A^T, then visit A's entries in order (rows ascending) and append
+ * each to its column's list.  t_perm[q] (if non-NULL) is the index in A's
+ * arrays of the entry that became entry q of A^T; t_values may be NULL. */
+void orc_csr_transpose(int m, int k, const int32_t *row_offsets,
+                       const int32_t *col_indices, const float *values,
+                       int32_t *t_row_offsets, int32_t *t_col_indices,
+                       float *t_values, int32_t *t_perm)
+{
+    int32_t *next = (int32_t *)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
+    for (int j = 0; j <= k; ++j)
+        t_row_offsets[j] = 0;
+    for (int32_t p = 0; p < row_offsets[m]; ++p)
+        t_row_offsets[col_indices[p] + 1] += 1;
+    for (int j = 0; j < k; ++j)
+        t_row_offsets[j + 1] += t_row_offsets[j];
+    for (int j = 0; j < k; ++j)
+        next[j] = t_row_offsets[j];
+    for (int i = 0; i < m; ++i) {
+        for (int32_t p = row_offsets[i]; p < row_offsets[i + 1]; ++p) {
+            int32_t q = next[col_indices[p]]++;
+            t_col_indices[q] = i;
+            if (t_values != NULL)
+                t_values[q] = values[p];
+            if (t_perm != NULL)
+                t_perm[q] = p;
+        }
+    }
+    free(next);
+}
+
+/* dX = A^T dY for A (m x k) in CSR and dY (m x n) dense: dX is k x n with
+ *   dX[j][l] = sum over entries p = (i, j) of A, rows i ascending, of
+ *              values[p] * dY[i][l],
+ * written from A's own structure without forming A^T (each entry adds its
+ * product to the row of dX named by its column).  abs_sum is the matching sum
+ * of |values[p] * dY[i][l]|.  dX is overwritten. */
+void orc_spmm_transposed(int m, int k, int n, const int32_t *row_offsets,
+                         const int32_t *col_indices, const float *values,
+                         const float *dy, double *dx, double *abs_sum)
+{
+    for (long long e = 0; e < (long long)k * n; ++e) {
+        dx[e] = 0.0;
+        abs_sum[e] = 0.0;
+    }
+    for (int i = 0; i < m; ++i) {
+        for (int32_t p = row_offsets[i]; p < row_offsets[i + 1]; ++p) {
+            double a = (double)values[p];
+            double *dx_row = dx + (long long)col_indices[p] * n;
+            double *abs_row = abs_sum + (long long)col_indices[p] * n;
+            for (int l = 0; l < n; ++l) {
+                double term = a * (double)dy[(long long)i * n + l];
+                dx_row[l] += term;
+                abs_row[l] += fabs(term);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* SDDMM                                                                    */
 /* ------------------------------------------------------------------------ */
 

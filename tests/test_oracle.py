@@ -415,3 +415,61 @@ def test_sddmm_general_reduces_to_specialised_form():
     only, _ = oracle.sddmm_general(256, 256, 32, ro, ci, w["x"], w["y"], 0, None, 0.0, 2.0,
                                    prior)
     assert np.array_equal(only, 2.0 * prior.astype(np.float64))
+
+
+# ---------------------------------------------------------------- transpose
+
+def test_csr_transpose_hand_example():
+    g = _golden("transpose_hand.json")
+    t_ro, t_ci, t_v, t_perm = oracle.csr_transpose(g["m"], g["k"], g["row_offsets"],
+                                                   g["col_indices"], g["values"])
+    assert t_ro.tolist() == g["t_row_offsets"]
+    assert t_ci.tolist() == g["t_col_indices"]
+    assert t_v.tolist() == g["t_values"]
+    assert t_perm.tolist() == g["t_perm"]
+
+
+@pytest.mark.parametrize("seed,m,k,p", [(201, 7, 5, 0.4), (202, 5, 9, 0.7), (203, 1, 1, 1.0),
+                                        (204, 6, 3, 0.0), (205, 33, 17, 0.2), (206, 4, 40, 0.5)])
+def test_csr_transpose_is_dense_transpose(seed, m, k, p):
+    mask, dv = _tiny_case(seed, m, k, p)
+    ro, ci, v = oracle.csr_from_dense(mask, dv)
+    t_ro, t_ci, t_v, t_perm = oracle.csr_transpose(m, k, ro, ci, v)
+    # the CSR of the transposed dense matrix, built independently
+    ro_ref, ci_ref, v_ref = oracle.csr_from_dense(mask.T.copy(), dv.T.copy())
+    assert np.array_equal(t_ro, ro_ref)
+    assert np.array_equal(t_ci, ci_ref)
+    assert np.array_equal(t_v, v_ref)
+    assert oracle.csr_check(k, m, t_ro, t_ci) == 0
+    # the permutation names the source entry of every transposed entry
+    assert sorted(t_perm.tolist()) == list(range(int(ro[-1])))
+    assert np.array_equal(v[t_perm], t_v)
+    assert np.array_equal(ci[t_perm], np.repeat(np.arange(k), np.diff(t_ro)))
+    # transposing twice gives A back
+    r2, c2, v2, _ = oracle.csr_transpose(k, m, t_ro, t_ci, t_v)
+    assert np.array_equal(r2, ro) and np.array_equal(c2, ci) and np.array_equal(v2, v)
+
+
+@pytest.mark.parametrize("seed,m,k,n,p", [(211, 6, 9, 5, 0.3), (212, 9, 4, 7, 0.8),
+                                          (213, 3, 3, 1, 1.0), (214, 5, 8, 3, 0.0),
+                                          (215, 17, 13, 11, 0.25)])
+def test_spmm_transposed_brute_force(seed, m, k, n, p):
+    mask, dv = _tiny_case(seed, m, k, p)
+    ro, ci, v = oracle.csr_from_dense(mask, dv)
+    dy = np.random.default_rng(seed + 1000).standard_normal((m, n)).astype(np.float32)
+    dense_a, _ = _densify(m, k, ro, ci, v)
+    # pure-Python dense A^T dY, rows of A ascending
+    want = [[0.0] * n for _ in range(k)]
+    for j in range(k):
+        for l in range(n):
+            acc = 0.0
+            for i in range(m):
+                acc += float(dense_a[i, j]) * float(dy[i, l])
+            want[j][l] = acc
+    dx, a = oracle.spmm_transposed(m, k, n, ro, ci, v, dy)
+    assert dx.tolist() == want
+    assert np.allclose(a, np.abs(dense_a).T @ np.abs(dy.astype(np.float64)), rtol=1e-12)
+    # and it is the plain SpMM of the transposed CSR, term for term
+    t_ro, t_ci, t_v, _ = oracle.csr_transpose(m, k, ro, ci, v)
+    c2, a2 = oracle.spmm(k, m, n, t_ro, t_ci, t_v, dy)
+    assert np.array_equal(c2, dx) and np.array_equal(a2, a)
