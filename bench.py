@@ -254,6 +254,35 @@ def stream_record(torch, sp, inputs, dev) -> dict:
             "traffic": traffic_record(STREAM_TRAFFIC_FILE)}
 
 
+def backward_records(torch, sp, inputs, dev, w, flush) -> list:
+    """Transpose of A (structure and values), the values-only update, and the
+    backward product dX = A^T dY, for one workload."""
+    a = w["a"]
+    m, k, n, nnz = w["m"], w["k"], w["n"], a.nnz
+    ro, _, cols, vals = upload_csr(torch, sp, dev, a)
+    ws = torch.empty(sp.sp_csr_transpose_workspace(m, k, nnz), dtype=torch.uint8, device=dev)
+    t_ro = torch.empty(k + 1, dtype=torch.int32, device=dev)
+    t_ci = torch.empty(nnz, dtype=torch.int32, device=dev)
+    t_v = torch.empty(nnz, device=dev)
+    t_p = torch.empty(nnz, dtype=torch.int32, device=dev)
+    t_ri = torch.empty(k, dtype=torch.int32, device=dev)
+    tfn = lambda: sp.sp_csr_transpose(m, k, nnz, ro, cols, vals, t_ro, t_ci, t_v, t_p, ws)
+    us_t = graph_time_us(torch, tfn, 20)
+    tfn()
+    sp.sp_row_swizzle(k, t_ro, t_ri)
+    vfn = lambda: sp.sp_csr_transpose_values(nnz, t_p, vals, t_v)
+    dy = torch.from_numpy(inputs.random_dense(7, m, n)).to(dev)
+    dx = torch.empty(k, n, device=dev)
+    bfn = lambda: sp.sp_spmm(k, m, n, nnz, t_ri, t_v, t_ro, t_ci, dy, dx)
+    us_b = graph_time_us(torch, bfn, 50)
+    return [{"record": "csr_transpose", "workload": w["name"], "m": m, "k": k, "nnz": nnz,
+             "us": us_t, "entries_per_s": nnz / (us_t * 1e-6)},
+            {"record": "csr_transpose_values", "workload": w["name"], "nnz": nnz,
+             "us": graph_time_us(torch, vfn, 50)},
+            spmm_record(w["name"] + "_backward_AT_dY", k, m, n, nnz, us_b,
+                        {"cold_us": cold_time_us(torch, bfn, flush), "swizzle": True})]
+
+
 def run_suite(torch, sp, inputs, dev, path: str) -> None:
     """Every workload, warm (graph back-to-back) and cold (after flushing the
     caches), one JSON record per kernel run."""
@@ -301,6 +330,11 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
                          "gflops": 2.0 * a.nnz * d / (us * 1e-6) / 1e9,
                          "compulsory_gbs": (sddmm_bytes(m, k, d, a.nnz) + 8 * a.nnz)
                          / (us * 1e-6) / 1e9})
+    # Backward pass of a sparse layer: A^T in CSR (once per structure; the
+    # values of a new A follow through the permutation), then dX = A^T dY on
+    # the swizzled rows of A^T.
+    for w in (inputs.transformer_ffn(), inputs.lstm(0.9)):
+        recs.extend(backward_records(torch, sp, inputs, dev, w, flush))
     # ResNet-50 1x1 conv
     w = inputs.resnet_1x1()
     a = w["a"]

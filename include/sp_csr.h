@@ -43,6 +43,8 @@
 #ifndef SP_CSR_H
 #define SP_CSR_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -122,6 +124,46 @@ sp_status_t sp_row_swizzle(int m, const int *row_offsets, int *row_indices,
  *   row_offsets  int32[m+1], output;  row_indices  int32[m], output */
 sp_status_t sp_csr_build_from_lengths(int m, const int *lengths, int *row_offsets,
                                       int *row_indices, sp_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Transpose ("Summary" of the card: the kernels serve training; the input
+ * gradient of C = A * B is dB = A^T * dC, an SpMM with the transposed sparse
+ * operand).  sp_csr_transpose gives A^T in standard CSR; sp_row_swizzle and
+ * sp_spmm on it then compute the product, entries of each output row summed in
+ * ascending row order of A.
+ * ---------------------------------------------------------------------- */
+
+/* *bytes = the device workspace sp_csr_transpose needs for nnz entries
+ * (about 20 bytes per entry plus 1 KiB per 4096 entries).  Pure host
+ * arithmetic; enqueues nothing. */
+sp_status_t sp_csr_transpose_workspace(int m, int k, int nnz, size_t *bytes);
+
+/* The CSR of A^T (k x m) from the CSR of A (m x k): row j of A^T lists, in
+ * ascending order, the rows i of A with an entry in column j, each with that
+ * entry's value.  Identical on every run (no atomic operation decides an
+ * order).
+ *   row_offsets, col_indices, values   the CSR of A (values may be NULL when
+ *                 t_values is NULL)
+ *   t_row_offsets int32[k+1], output;  t_col_indices int32[nnz], output
+ *   t_values      fp32[nnz], output, or NULL
+ *   t_perm        int32[nnz], output, or NULL: t_perm[q] is the index in A's
+ *                 arrays of A^T's entry q (for sp_csr_transpose_values)
+ *   workspace     device memory of at least sp_csr_transpose_workspace bytes,
+ *                 256-byte aligned, not overlapping any argument; its contents
+ *                 on entry do not matter and on return are unspecified.
+ * Errors: k == INT32_MAX, k == 0 with nnz > 0, a missing or short workspace,
+ * or a NULL array that must exist returns SP_ERROR_INVALID_VALUE. */
+sp_status_t sp_csr_transpose(int m, int k, int nnz, const int *row_offsets,
+                             const int *col_indices, const float *values,
+                             int *t_row_offsets, int *t_col_indices, float *t_values,
+                             int *t_perm, void *workspace, size_t workspace_bytes,
+                             sp_stream_t stream);
+
+/* t_values[q] = values[t_perm[q]] for q < nnz: new values of A (same
+ * structure) carried into the order of A^T without transposing again.
+ * t_values must not overlap values. */
+sp_status_t sp_csr_transpose_values(int nnz, const int *t_perm, const float *values,
+                                    float *t_values, sp_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * SpMM ("Summary" of the card): C = A * B, A sparse in CSR, B dense.

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 13, declared
+    assert len(declared) == 16, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -73,6 +73,45 @@ def test_spmm_validation(lib):
     assert f(4, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, 0, 0, 0, 0, s) == OK
     assert lib.sp_spmm(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, s) == OK
     assert lib.sp_spmm(-2, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, s) == INVALID
+
+
+def test_transpose_validation(lib):
+    size = ctypes.c_size_t(0)
+    assert lib.sp_csr_transpose_workspace(4, 5, 10000, ctypes.byref(size)) == OK
+    # five int32 arrays of nnz entries (256-byte aligned) and 256 counters per
+    # 4096-entry tile plus one
+    arr = (10000 * 4 + 255) // 256 * 256
+    assert size.value == 5 * arr + (256 * 4 * 4 + 255) // 256 * 256
+    assert lib.sp_csr_transpose_workspace(-1, 5, 10, ctypes.byref(size)) == INVALID
+    assert lib.sp_csr_transpose_workspace(1, 5, 10, None) == INVALID
+    f = lib.sp_csr_transpose
+    s = NULL
+    ws = ctypes.c_void_p(0x100000)  # 256-byte aligned, never dereferenced
+    need = binding.sp_csr_transpose_workspace(4, 5, 8)
+
+    def call(m=4, k=5, nnz=8, ro=FAKE, ci=FAKE, v=FAKE, tro=FAKE, tci=FAKE, tv=FAKE,
+             tp=NULL, w=ws, wb=None):
+        return f(m, k, nnz, ro, ci, v, tro, tci, tv, tp, w, need if wb is None else wb, s)
+
+    assert call(m=-1) == INVALID
+    assert call(k=-1) == INVALID
+    assert call(nnz=-1) == INVALID
+    assert call(k=2**31 - 1) == INVALID
+    assert call(k=0) == INVALID
+    assert call(ro=NULL) == INVALID
+    assert call(ci=NULL) == INVALID
+    assert call(tro=NULL) == INVALID
+    assert call(tci=NULL) == INVALID
+    assert call(v=NULL) == INVALID           # t_values asked for without values
+    assert call(w=NULL) == INVALID
+    assert call(wb=need - 1) == INVALID
+    assert call(w=ctypes.c_void_p(0x100010)) == INVALID   # misaligned workspace
+    g = lib.sp_csr_transpose_values
+    assert g(-1, FAKE, FAKE, FAKE, s) == INVALID
+    assert g(4, NULL, FAKE, FAKE, s) == INVALID
+    assert g(4, FAKE, NULL, FAKE, s) == INVALID
+    assert g(4, FAKE, FAKE, NULL, s) == INVALID
+    assert g(0, NULL, NULL, NULL, s) == OK
 
 
 def test_sddmm_general_validation(lib):

@@ -50,6 +50,11 @@ SIGNATURES = {
                           _c_ll, _vp], _c_int),
     "sp_csr_row_softmax": ([_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_ll, _c_ll, _vp],
                            _c_int),
+    "sp_csr_transpose_workspace": ([_c_int, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)],
+                                   _c_int),
+    "sp_csr_transpose": ([_c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                          ctypes.c_size_t, _vp], _c_int),
+    "sp_csr_transpose_values": ([_c_int, _vp, _vp, _vp, _vp], _c_int),
 }
 
 
@@ -204,6 +209,33 @@ def sp_sddmm_general(m, k, d, nnz, row_indices, row_offsets, col_indices, mask_v
         _ptr(y, _F32, "y", True), int(y_layout), float(alpha), float(beta),
         _ptr(out, _F32, "out", True), batch, stride_values, stride_x, stride_y, stride_out,
         _stream(stream)), "sp_sddmm_general")
+
+
+def sp_csr_transpose_workspace(m, k, nnz) -> int:
+    size = ctypes.c_size_t(0)
+    _check(lib().sp_csr_transpose_workspace(m, k, nnz, ctypes.byref(size)),
+           "sp_csr_transpose_workspace")
+    return size.value
+
+
+def sp_csr_transpose(m, k, nnz, row_offsets, col_indices, values, t_row_offsets,
+                     t_col_indices, t_values, t_perm, workspace, stream=None):
+    """workspace: a uint8 device tensor of at least sp_csr_transpose_workspace bytes."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sp_csr_transpose(
+        m, k, nnz, _ptr(row_offsets, _I32, "row_offsets"),
+        _ptr(col_indices, _I32, "col_indices", True), _ptr(values, _F32, "values", True),
+        _ptr(t_row_offsets, _I32, "t_row_offsets"),
+        _ptr(t_col_indices, _I32, "t_col_indices", True),
+        _ptr(t_values, _F32, "t_values", True), _ptr(t_perm, _I32, "t_perm", True),
+        _ptr(workspace, _U8, "workspace", True), ws_bytes, _stream(stream)),
+        "sp_csr_transpose")
+
+
+def sp_csr_transpose_values(nnz, t_perm, values, t_values, stream=None):
+    _check(lib().sp_csr_transpose_values(
+        nnz, _ptr(t_perm, _I32, "t_perm", True), _ptr(values, _F32, "values", True),
+        _ptr(t_values, _F32, "t_values", True), _stream(stream)), "sp_csr_transpose_values")
 
 
 def sp_csr_row_softmax(m, nnz, row_indices, row_offsets, inp, out, batch=1, stride_in=0,

@@ -187,6 +187,42 @@ sp_status_t sp_sddmm(int m, int k, int d, int nnz, const int *row_indices,
                             alpha, out, 1, 0, 0, 0, stream);
 }
 
+sp_status_t sp_csr_transpose_workspace(int m, int k, int nnz, size_t *bytes)
+{
+    if (m < 0 || k < 0 || nnz < 0 || bytes == nullptr) return SP_ERROR_INVALID_VALUE;
+    *bytes = spk::transpose_workspace_bytes(nnz);
+    return SP_SUCCESS;
+}
+
+sp_status_t sp_csr_transpose(int m, int k, int nnz, const int *row_offsets,
+                             const int *col_indices, const float *values, int *t_row_offsets,
+                             int *t_col_indices, float *t_values, int *t_perm, void *workspace,
+                             size_t workspace_bytes, sp_stream_t stream)
+{
+    if (m < 0 || k < 0 || nnz < 0) return SP_ERROR_INVALID_VALUE;
+    if (k == INT_MAX) return SP_ERROR_INVALID_VALUE;  // k + 1 offsets must be indexable
+    if (!need(row_offsets, m) || t_row_offsets == nullptr || !need(col_indices, nnz) ||
+        !need(t_col_indices, nnz) || (t_values != nullptr && !need(values, nnz)))
+        return SP_ERROR_INVALID_VALUE;
+    if (nnz > 0 && k == 0) return SP_ERROR_INVALID_VALUE;  // an entry needs a column
+    if (nnz > 0 && (workspace == nullptr ||
+                    workspace_bytes < spk::transpose_workspace_bytes(nnz)))
+        return SP_ERROR_INVALID_VALUE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SP_ERROR_INVALID_VALUE;
+    return from_hip(spk::launch_csr_transpose(m, k, nnz, row_offsets, col_indices, values,
+                                              t_row_offsets, t_col_indices, t_values, t_perm,
+                                              workspace, as_stream(stream)));
+}
+
+sp_status_t sp_csr_transpose_values(int nnz, const int *t_perm, const float *values,
+                                    float *t_values, sp_stream_t stream)
+{
+    if (nnz < 0) return SP_ERROR_INVALID_VALUE;
+    if (!need(t_perm, nnz) || !need(values, nnz) || !need(t_values, nnz))
+        return SP_ERROR_INVALID_VALUE;
+    return from_hip(spk::launch_gather_values(nnz, t_perm, values, t_values, as_stream(stream)));
+}
+
 sp_status_t sp_csr_row_softmax(int m, int nnz, const int *row_indices,
                                const int *row_offsets, const float *in, float *out,
                                int batch, long long stride_in, long long stride_out,

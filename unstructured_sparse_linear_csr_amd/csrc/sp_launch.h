@@ -50,5 +50,12 @@ hipError_t launch_row_softmax(int m, const int *row_indices, const int *row_offs
                               const float *in, float *out, int batch, long long stride_in,
                               long long stride_out, hipStream_t stream);
 hipError_t launch_fill_zero(float *dst, long long count, hipStream_t stream);
+size_t transpose_workspace_bytes(int nnz);
+hipError_t launch_csr_transpose(int m, int k, int nnz, const int *row_offsets,
+                                const int *col_indices, const float *values,
+                                int *t_row_offsets, int *t_col_indices, float *t_values,
+                                int *t_perm, void *workspace, hipStream_t stream);
+hipError_t launch_gather_values(int nnz, const int *perm, const float *in, float *out,
+                                hipStream_t stream);
 
 }  // namespace spk

@@ -1,0 +1,279 @@
+// CSR transpose on the device: the CSR of A^T (k x m) from the CSR of A
+// (m x k), which the backward pass of a sparse layer needs for the input
+// gradient dB = A^T dC ("Sparse GPU Kernels for Deep Learning", summary card,
+// "Summary": the kernels serve training, and its gradients take the
+// transposed operand).
+//
+// Method.  A^T in CSR is A's entries ordered by (column, row).  A's arrays
+// already list them by (row, column), so a stable sort of the entry indices
+// by column gives the order: a least-significant-digit radix sort of the
+// column indices, 8 bits per pass, ceil(log2(k) / 8) passes, carrying each
+// entry's index.  Every pass has three launches:
+//   upsweep   -- each 4096-entry tile counts its digits (LDS counters);
+//   scan      -- one workgroup per digit turns its per-tile counts into
+//                exclusive offsets within the digit and the digit's total;
+//   downsweep -- each tile ranks its entries within the tile, stably, with
+//                wave ballots (the lanes that share a digit, and how many of
+//                them come before), and scatters them to
+//                digit base + tile offset + rank.
+// No atomic operation decides any position, so the result is the same on
+// every run.  Then the row offsets of A^T come from the sorted columns (the
+// first position of each column), and a last pass writes each transposed
+// entry's row (the source entry's row, from an expanded row-id array), value
+// and source index.
+#include <algorithm>
+
+#include "sp_device.h"
+#include "sp_launch.h"
+#include "sp_scan.h"
+
+namespace spk {
+
+namespace {
+
+constexpr int kSortThreads = 256;
+constexpr int kSortWaves = kSortThreads / kWave;
+constexpr int kItems = 16;                              // entries per thread
+constexpr int kTile = kSortThreads * kItems;            // entries per tile
+constexpr int kDigits = 256;                            // 8-bit digits
+constexpr int kDigitScanThreads = 1024;
+static_assert(kSortThreads == kDigits, "one thread per digit in the bases");
+
+// Entry `j` of thread (wave w, lane l) in tile b is entry
+// b * kTile + w * (kItems * kWave) + j * kWave + l: a wave's entries in
+// (j, lane) order, waves in order, tiles in order -- the original order.
+__device__ __forceinline__ long long item_index(int tile, int wave, int j, int lane)
+{
+    return (long long)tile * kTile + wave * (kItems * kWave) + j * kWave + lane;
+}
+
+// rowid[p] = the row of entry p (one wave per row).
+__global__ __launch_bounds__(kWave) void expand_rows_kernel(const int *__restrict__ row_offsets,
+                                                            int *__restrict__ rowid)
+{
+    const int row = blockIdx.x;
+    const int p1 = row_offsets[row + 1];
+    for (int p = row_offsets[row] + (int)threadIdx.x; p < p1; p += kWave) rowid[p] = row;
+}
+
+// hist[d * (tiles + 1) + b + 1] = number of entries of tile b whose digit is d.
+__global__ __launch_bounds__(kSortThreads) void radix_upsweep_kernel(
+    int nnz, int shift, const int *__restrict__ keys, int *__restrict__ hist, int tiles)
+{
+    __shared__ int s_count[kDigits];
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    const int b = blockIdx.x;
+    s_count[tid] = 0;
+    __syncthreads();
+    int key[kItems];
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        const long long idx = item_index(b, wave, j, lane);
+        key[j] = idx < nnz ? keys[idx] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kItems; ++j)
+        if (key[j] >= 0) atomicAdd(&s_count[(key[j] >> shift) & (kDigits - 1)], 1);
+    __syncthreads();
+    hist[(size_t)tid * (tiles + 1) + b + 1] = s_count[tid];
+}
+
+// Per digit d: hist[d][b] = sum of tile counts of digit d before tile b, and
+// hist[d][tiles] = the digit's total (in place; counts sit at b + 1).
+__global__ __launch_bounds__(kDigitScanThreads) void digit_scan_kernel(int tiles, int *hist)
+{
+    int *row = hist + (size_t)blockIdx.x * (tiles + 1);
+    exclusive_scan_block<kDigitScanThreads>(tiles, row + 1, row);
+}
+
+// Scatter tile b's entries to their sorted positions.  vals_in == NULL means
+// the identity (entry index) as the carried value.
+__global__ __launch_bounds__(kSortThreads) void radix_downsweep_kernel(
+    int nnz, int shift, const int *__restrict__ keys_in, const int *__restrict__ vals_in,
+    int *__restrict__ keys_out, int *__restrict__ vals_out, const int *__restrict__ hist,
+    int tiles)
+{
+    __shared__ int s_wave_count[kSortWaves][kDigits];
+    __shared__ int s_base[kDigits];
+    __shared__ int s_wave_sum[kSortWaves];
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    const int b = blockIdx.x;
+
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) s_wave_count[w][tid] = 0;
+    // Digit bases: exclusive scan of the digit totals (thread d holds digit
+    // d), plus this tile's offset within the digit.
+    const int total = hist[(size_t)tid * (tiles + 1) + tiles];
+    const int incl = wave_inclusive_sum(total, lane);
+    if (lane == kWave - 1) s_wave_sum[wave] = incl;
+
+    int key[kItems], val[kItems], rank[kItems];
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        const long long idx = item_index(b, wave, j, lane);
+        const bool ok = idx < nnz;
+        key[j] = ok ? keys_in[idx] : -1;
+        val[j] = vals_in ? (ok ? vals_in[idx] : 0) : (int)idx;
+    }
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) before += w < wave ? s_wave_sum[w] : 0;
+    s_base[tid] = before + incl - total + hist[(size_t)tid * (tiles + 1) + b];
+
+    // Rank within the wave, round by round in (j, lane) order.  In a round,
+    // the lanes sharing a digit read the wave's running count for it, take
+    // their place among themselves, and the lowest of them advances the
+    // count.  A wave's LDS operations complete in program order, so every
+    // read of a round precedes that round's update.
+    const uint64_t below = lanes_below(lane);
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        const bool ok = key[j] >= 0;
+        const int d = ok ? (key[j] >> shift) & (kDigits - 1) : 0;
+        uint64_t peers = __ballot(ok);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const uint64_t ones = __ballot((d >> bit) & 1);
+            peers &= ((d >> bit) & 1) ? ones : ~ones;
+        }
+        const int ahead = __popcll(peers & below);
+        const int old = s_wave_count[wave][d];
+        if (ok && ahead == 0) s_wave_count[wave][d] = old + __popcll(peers);
+        rank[j] = old + ahead;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        if (key[j] < 0) continue;
+        const int d = (key[j] >> shift) & (kDigits - 1);
+        int pos = s_base[d] + rank[j];
+#pragma unroll
+        for (int w = 0; w < kSortWaves; ++w) pos += w < wave ? s_wave_count[w][d] : 0;
+        keys_out[pos] = key[j];
+        vals_out[pos] = val[j];
+    }
+}
+
+// t_row_offsets[c] = first position of column c in the sorted columns (nnz
+// past the last): position q writes every column in (keys[q-1], keys[q]].
+__global__ __launch_bounds__(256) void offsets_from_sorted_kernel(int nnz, int k,
+                                                                  const int *__restrict__ keys,
+                                                                  int *__restrict__ t_row_offsets)
+{
+    const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (q > nnz) return;
+    const long long prev = q > 0 ? keys[q - 1] : -1;
+    const long long cur = q < nnz ? keys[q] : k;
+    for (long long c = prev + 1; c <= cur; ++c) t_row_offsets[c] = (int)q;
+}
+
+// Entry q of A^T: source entry p = perm[q] (q itself when perm == NULL).
+__global__ __launch_bounds__(256) void transpose_finish_kernel(
+    int nnz, const int *__restrict__ perm, const int *__restrict__ rowid,
+    const float *__restrict__ values, int *__restrict__ t_col_indices,
+    float *__restrict__ t_values, int *__restrict__ t_perm)
+{
+    const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (q >= nnz) return;
+    const int p = perm ? perm[q] : (int)q;
+    t_col_indices[q] = rowid[p];
+    if (t_values) t_values[q] = values[p];
+    if (t_perm) t_perm[q] = p;
+}
+
+__global__ __launch_bounds__(256) void gather_values_kernel(int nnz, const int *__restrict__ perm,
+                                                            const float *__restrict__ in,
+                                                            float *__restrict__ out)
+{
+    const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (q < nnz) out[q] = in[perm[q]];
+}
+
+struct Workspace {
+    int *keys[2], *vals[2], *rowid, *hist;
+    size_t bytes;
+};
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+Workspace carve(int nnz, void *base)
+{
+    const size_t arr = align256((size_t)std::max(nnz, 1) * sizeof(int));
+    const int tiles = (nnz + kTile - 1) / kTile;
+    const size_t hist = align256((size_t)kDigits * (size_t)(tiles + 1) * sizeof(int));
+    Workspace w;
+    char *p = static_cast<char *>(base);
+    w.keys[0] = reinterpret_cast<int *>(p);
+    w.keys[1] = reinterpret_cast<int *>(p + arr);
+    w.vals[0] = reinterpret_cast<int *>(p + 2 * arr);
+    w.vals[1] = reinterpret_cast<int *>(p + 3 * arr);
+    w.rowid = reinterpret_cast<int *>(p + 4 * arr);
+    w.hist = reinterpret_cast<int *>(p + 5 * arr);
+    w.bytes = 5 * arr + hist;
+    return w;
+}
+
+unsigned blocks_for(long long count) { return (unsigned)((count + 255) / 256); }
+
+}  // namespace
+
+size_t transpose_workspace_bytes(int nnz) { return carve(nnz, nullptr).bytes; }
+
+hipError_t launch_csr_transpose(int m, int k, int nnz, const int *row_offsets,
+                                const int *col_indices, const float *values,
+                                int *t_row_offsets, int *t_col_indices, float *t_values,
+                                int *t_perm, void *workspace, hipStream_t stream)
+{
+    hipError_t e;
+    if (nnz == 0) return launch_fill_zero(reinterpret_cast<float *>(t_row_offsets), k + 1, stream);
+    const Workspace w = carve(nnz, workspace);
+    const int tiles = (nnz + kTile - 1) / kTile;
+    int bits = 0;
+    while (bits < 31 && (1LL << bits) < (long long)k) ++bits;  // columns lie in [0, 2^bits)
+    const int passes = (bits + 7) / 8;
+
+    hipLaunchKernelGGL(expand_rows_kernel, dim3((unsigned)m), dim3(kWave), 0, stream,
+                       row_offsets, w.rowid);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int *keys = col_indices;
+    const int *vals = nullptr;
+    for (int pass = 0; pass < passes; ++pass) {
+        const int shift = 8 * pass;
+        int *keys_out = w.keys[pass & 1];
+        int *vals_out = w.vals[pass & 1];
+        hipLaunchKernelGGL(radix_upsweep_kernel, dim3((unsigned)tiles), dim3(kSortThreads), 0,
+                           stream, nnz, shift, keys, w.hist, tiles);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(digit_scan_kernel, dim3(kDigits), dim3(kDigitScanThreads), 0, stream,
+                           tiles, w.hist);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(radix_downsweep_kernel, dim3((unsigned)tiles), dim3(kSortThreads), 0,
+                           stream, nnz, shift, keys, vals, keys_out, vals_out, w.hist, tiles);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        keys = keys_out;
+        vals = vals_out;
+    }
+    // With no pass (k == 1) every column is 0: the entries are already in order.
+    hipLaunchKernelGGL(offsets_from_sorted_kernel, dim3(blocks_for((long long)nnz + 1)),
+                       dim3(256), 0, stream, nnz, k, keys, t_row_offsets);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(transpose_finish_kernel, dim3(blocks_for(nnz)), dim3(256), 0, stream, nnz,
+                       vals, w.rowid, values, t_col_indices, t_values, t_perm);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_values(int nnz, const int *perm, const float *in, float *out,
+                                hipStream_t stream)
+{
+    if (nnz == 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_values_kernel, dim3(blocks_for(nnz)), dim3(256), 0, stream, nnz,
+                       perm, in, out);
+    return hipGetLastError();
+}
+
+}  // namespace spk
