@@ -46,6 +46,7 @@ _I32P = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 _F32P = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 _F64P = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 _U8P = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
+_U16P = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
 
 
 def _load():
@@ -85,6 +86,8 @@ def _load():
     lib.orc_spmm_transposed.argtypes = [c_int, c_int, c_int, _I32P, _I32P, _F32P, _F32P,
                                         _F64P, _F64P]
     lib.orc_spmm_transposed.restype = None
+    lib.orc_decode16.argtypes = [c_int, c_ll, _U16P, _F64P]
+    lib.orc_decode16.restype = None
     lib.orc_softmax_rows.argtypes = [c_int, _I32P, _F32P, _F64P]
     lib.orc_softmax_rows.restype = None
     _lib = lib
@@ -237,6 +240,18 @@ def spmm_transposed(m: int, k: int, n: int, row_offsets, col_indices, values, dy
     _load().orc_spmm_transposed(m, k, n, ro, _nz(ci), _nz(v), _nz(d.reshape(-1)),
                                 _nz(dx.reshape(-1)), _nz(a.reshape(-1)))
     return dx, a
+
+
+F16, BF16 = 1, 2
+
+
+def decode16(kind: int, bits) -> np.ndarray:
+    """Values (float64, same shape) of binary16 (kind 1) or bfloat16 (kind 2)
+    bit patterns given as uint16."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.zeros(b.shape, np.float64)
+    _load().orc_decode16(int(kind), b.size, _nz(b.reshape(-1)), _nz(out.reshape(-1)))
+    return out
 
 
 def softmax_rows(row_offsets, s):

@@ -110,6 +110,56 @@ int orc_csr_check(int m, int k, long long nnz, const int32_t *row_offsets,
 }
 
 /* ------------------------------------------------------------------------ */
+/* 16-bit operand formats (mixed precision: 16-bit storage, products and     */
+/* sums in wider arithmetic)                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Value of an IEEE 754 binary16 bit pattern: sign bit 15, exponent bits 14-10
+ * (bias 15), fraction bits 9-0.  Exponent 0 encodes zero and the subnormals
+ * f * 2^-24; exponent 31 encodes infinity (f = 0) or NaN; otherwise the value
+ * is (1024 + f) * 2^(e - 25). */
+double orc_f16_value(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int e = (bits >> 10) & 0x1f;
+    int f = bits & 0x3ff;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -24);
+    else if (e == 31)
+        mag = f == 0 ? INFINITY : NAN;
+    else
+        mag = ldexp((double)(1024 + f), e - 25);
+    return sign ? -mag : mag;
+}
+
+/* Value of a bfloat16 bit pattern (the upper half of a binary32): sign bit
+ * 15, exponent bits 14-7 (bias 127), fraction bits 6-0.  Exponent 0: f *
+ * 2^-133 (zero and subnormals); 255: infinity or NaN; otherwise
+ * (128 + f) * 2^(e - 134). */
+double orc_bf16_value(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int e = (bits >> 7) & 0xff;
+    int f = bits & 0x7f;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -133);
+    else if (e == 255)
+        mag = f == 0 ? INFINITY : NAN;
+    else
+        mag = ldexp((double)(128 + f), e - 134);
+    return sign ? -mag : mag;
+}
+
+/* out[i] = value of bits[i]; kind 1 = binary16, 2 = bfloat16. */
+void orc_decode16(int kind, long long count, const uint16_t *bits, double *out)
+{
+    for (long long i = 0; i < count; ++i)
+        out[i] = kind == 1 ? orc_f16_value(bits[i]) : orc_bf16_value(bits[i]);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Row swizzle                                                              */
 /* ------------------------------------------------------------------------ */
 

@@ -473,3 +473,37 @@ def test_spmm_transposed_brute_force(seed, m, k, n, p):
     t_ro, t_ci, t_v, _ = oracle.csr_transpose(m, k, ro, ci, v)
     c2, a2 = oracle.spmm(k, m, n, t_ro, t_ci, t_v, dy)
     assert np.array_equal(c2, dx) and np.array_equal(a2, a)
+
+
+# ---------------------------------------------------------------- 16-bit formats
+
+def test_decode16_hand_values():
+    g = _golden("float16_hand.json")
+    for kind, key in ((oracle.F16, "binary16"), (oracle.BF16, "bfloat16")):
+        for hexbits, value in g[key]:
+            got = oracle.decode16(kind, np.array([int(hexbits, 16)], np.uint16))[0]
+            if value == "nan":
+                assert math.isnan(got), (key, hexbits)
+            else:
+                assert got == float(value), (key, hexbits, got)
+
+
+def test_decode16_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    # binary16 against numpy's own conversion
+    f16 = oracle.decode16(oracle.F16, bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(f16), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(f16[ok], ref[ok])
+    # bfloat16 against the binary32 whose upper half it is
+    b16 = oracle.decode16(oracle.BF16, bits)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns
+        ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(np.isnan(b16), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(b16[ok], ref[ok])
+    # every finite value is exactly an fp32 value (widening loses nothing)
+    for v in (f16, b16):
+        fin = np.isfinite(v)
+        assert np.array_equal(v[fin].astype(np.float32).astype(np.float64), v[fin])
