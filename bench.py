@@ -283,6 +283,63 @@ def backward_records(torch, sp, inputs, dev, w, flush) -> list:
                         {"cold_us": cold_time_us(torch, bfn, flush), "swizzle": True})]
 
 
+def lowp_records(torch, sp, inputs, dev, flush) -> list:
+    """SpMM and SDDMM with 16-bit operands on the FFN, LSTM 90 % and ResNet
+    shapes and the attention pair; bytes counted at 2 per operand element."""
+    recs = []
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    for tdt, tag in ((torch.bfloat16, "bf16"), (torch.float16, "f16")):
+        for w in (inputs.transformer_ffn(), inputs.lstm(0.9), inputs.resnet_1x1()):
+            a = w["a"]
+            m, k, n, nnz = w["m"], w["k"], w["n"], a.nnz
+            ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+            v16, b16 = vals.to(tdt), up(w["b"]).to(tdt)
+            c = torch.empty(m, n, device=dev)
+            fn = lambda: sp.sp_spmm_ex(m, k, n, nnz, ri, v16, ro, cols, b16, c)
+            us = graph_time_us(torch, fn, 50)
+            byts = 6 * nnz + 8 * m + 4 + 2 * k * n + 4 * m * n
+            recs.append({"record": "spmm_" + tag, "workload": w["name"], "m": m, "k": k,
+                         "n": n, "nnz": nnz, "us": us,
+                         "gflops": 2.0 * nnz * n / (us * 1e-6) / 1e9,
+                         "compulsory_gbs": byts / (us * 1e-6) / 1e9,
+                         "cold_us": cold_time_us(torch, fn, flush)})
+            if "x" in w:
+                d = w["d"]
+                x16, y16 = up(w["x"]).to(tdt), up(w["y"]).to(tdt)
+                out = torch.empty(nnz, device=dev)
+                sfn = lambda: sp.sp_sddmm_ex(m, k, d, nnz, ri, ro, cols, x16, y16, 1.0, out)
+                us = graph_time_us(torch, sfn, 50)
+                recs.append({"record": "sddmm_" + tag, "workload": w["name"], "m": m, "k": k,
+                             "d": d, "nnz": nnz, "us": us,
+                             "gflops": 2.0 * nnz * d / (us * 1e-6) / 1e9,
+                             "cold_us": cold_time_us(torch, sfn, flush)})
+        w = inputs.sparse_attention()
+        bh, seq, hd = w["batch"], w["seq"], w["head_dim"]
+        mk = up(w["mask"])
+        ro = torch.empty(seq + 1, dtype=torch.int32, device=dev)
+        sp.sp_csr_count_dense(seq, seq, mk, ro)
+        nnz = int(ro[seq].item())
+        cols = torch.empty(nnz, dtype=torch.int32, device=dev)
+        sp.sp_csr_fill_dense(seq, seq, mk, None, ro, cols, None)
+        ri = torch.empty(seq, dtype=torch.int32, device=dev)
+        sp.sp_row_swizzle(seq, ro, ri)
+        q, kk, vv = up(w["q"]).to(tdt), up(w["k"]).to(tdt), up(w["v"]).to(tdt)
+        s_out = torch.empty(bh, nnz, device=dev)
+        p16 = torch.full((bh, nnz), 1.0 / 80.0, device=dev).to(tdt)
+        o = torch.empty(bh, seq, hd, device=dev)
+        sfn = lambda: sp.sp_sddmm_ex(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125, s_out, bh,
+                                     seq * hd, seq * hd, nnz)
+        pfn = lambda: sp.sp_spmm_ex(seq, seq, hd, nnz, ri, p16, ro, cols, vv, o, bh, nnz,
+                                    seq * hd, seq * hd)
+        for kind, fn in (("sddmm_batched_" + tag, sfn), ("spmm_batched_" + tag, pfn)):
+            us = graph_time_us(torch, fn, 20)
+            recs.append({"record": kind, "workload": w["name"], "batch": bh, "seq": seq,
+                         "head_dim": hd, "nnz_per_head": nnz, "us": us,
+                         "gflops": 2.0 * bh * nnz * hd / (us * 1e-6) / 1e9,
+                         "cold_us": cold_time_us(torch, fn, flush)})
+    return recs
+
+
 def run_suite(torch, sp, inputs, dev, path: str) -> None:
     """Every workload, warm (graph back-to-back) and cold (after flushing the
     caches), one JSON record per kernel run."""
@@ -335,6 +392,8 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
     # the swizzled rows of A^T.
     for w in (inputs.transformer_ffn(), inputs.lstm(0.9)):
         recs.extend(backward_records(torch, sp, inputs, dev, w, flush))
+    # Mixed precision: values and B (X and Y) in 16-bit, fp32 arithmetic.
+    recs.extend(lowp_records(torch, sp, inputs, dev, flush))
     # ResNet-50 1x1 conv
     w = inputs.resnet_1x1()
     a = w["a"]

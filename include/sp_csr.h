@@ -259,6 +259,40 @@ sp_status_t sp_sddmm_general(int m, int k, int d, int nnz, const int *row_indice
                              sp_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Mixed precision (fp16/bf16 operands, fp32 arithmetic).  The card's kernels
+ * are fp32; 16-bit storage halves the bytes of the gathered operand, which
+ * is what bounds these kernels.  Every 16-bit element is widened to fp32
+ * exactly on load, products and sums are fp32 as in the fp32 entry points,
+ * and outputs are fp32.
+ * ---------------------------------------------------------------------- */
+
+/* Element type of the 16-bit-capable operands. */
+typedef enum sp_dtype {
+    SP_DTYPE_F32 = 0,  /* IEEE binary32 */
+    SP_DTYPE_F16 = 1,  /* IEEE binary16 */
+    SP_DTYPE_BF16 = 2  /* bfloat16: the upper 16 bits of a binary32 */
+} sp_dtype_t;
+
+/* sp_spmm_batched with values and B of element type `dtype` (strides in
+ * elements of that type); C is fp32.  SP_DTYPE_F32 is exactly
+ * sp_spmm_batched.  16-bit B rows are read in 16-byte vectors of 8 elements
+ * when n % 8 == 0 and B, C are 16-byte aligned, else element by element.
+ * An unknown dtype returns SP_ERROR_INVALID_VALUE. */
+sp_status_t sp_spmm_ex(int m, int k, int n, int nnz, const int *row_indices, int dtype,
+                       const void *values, const int *row_offsets, const int *col_indices,
+                       const void *b, float *c, int batch, long long stride_values,
+                       long long stride_b, long long stride_c, sp_stream_t stream);
+
+/* sp_sddmm_batched with X and Y of element type `dtype` (strides in elements
+ * of that type); out is fp32.  SP_DTYPE_F32 is exactly sp_sddmm_batched.  An
+ * unknown dtype returns SP_ERROR_INVALID_VALUE. */
+sp_status_t sp_sddmm_ex(int m, int k, int d, int nnz, const int *row_indices,
+                        const int *row_offsets, const int *col_indices, int dtype,
+                        const void *x, const void *y, float alpha, float *out, int batch,
+                        long long stride_x, long long stride_y, long long stride_out,
+                        sp_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Row softmax over CSR entries ("Interesting ideas" I3 of the card: the SDDMM
  * form sparse attention needs; softmax over each row's entries is the step
  * between the attention scores (SDDMM) and their weighted sum (SpMM)).

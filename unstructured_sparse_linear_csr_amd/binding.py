@@ -26,6 +26,9 @@ SP_ERROR_NOT_SUPPORTED = 2
 SP_ERROR_LAUNCH_FAILED = 3
 SP_Y_KD = 0  # SDDMM operand Y stored k x d
 SP_Y_DK = 1  # SDDMM operand Y stored d x k
+SP_DTYPE_F32 = 0
+SP_DTYPE_F16 = 1
+SP_DTYPE_BF16 = 2
 
 # Every symbol include/sp_csr.h declares, with its ctypes signature.
 _c_int, _c_ll, _c_float, _vp = ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_void_p
@@ -55,6 +58,10 @@ SIGNATURES = {
     "sp_csr_transpose": ([_c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           ctypes.c_size_t, _vp], _c_int),
     "sp_csr_transpose_values": ([_c_int, _vp, _vp, _vp, _vp], _c_int),
+    "sp_spmm_ex": ([_c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp,
+                    _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
+    "sp_sddmm_ex": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
+                     _c_float, _vp, _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
 }
 
 
@@ -236,6 +243,44 @@ def sp_csr_transpose_values(nnz, t_perm, values, t_values, stream=None):
     _check(lib().sp_csr_transpose_values(
         nnz, _ptr(t_perm, _I32, "t_perm", True), _ptr(values, _F32, "values", True),
         _ptr(t_values, _F32, "t_values", True), _stream(stream)), "sp_csr_transpose_values")
+
+
+_DTYPE_CODES = {torch.float32: SP_DTYPE_F32, torch.float16: SP_DTYPE_F16,
+                torch.bfloat16: SP_DTYPE_BF16}
+
+
+def _dtype_of(*tensors) -> int:
+    """The one element type shared by the non-None tensors."""
+    kinds = {t.dtype for t in tensors if t is not None}
+    if len(kinds) != 1 or next(iter(kinds)) not in _DTYPE_CODES:
+        raise ValueError(f"operands must share one of float32/float16/bfloat16, got {kinds}")
+    return _DTYPE_CODES[next(iter(kinds))]
+
+
+def sp_spmm_ex(m, k, n, nnz, row_indices, values, row_offsets, col_indices, b, c, batch=1,
+               stride_values=0, stride_b=0, stride_c=0, stream=None):
+    """SpMM with values and B in float32, float16 or bfloat16 (one type); C float32."""
+    code = _dtype_of(values, b)
+    dt = [k_ for k_, v in _DTYPE_CODES.items() if v == code][0]
+    _check(lib().sp_spmm_ex(
+        m, k, n, nnz, _ptr(row_indices, _I32, "row_indices", True), code,
+        _ptr(values, dt, "values", True), _ptr(row_offsets, _I32, "row_offsets"),
+        _ptr(col_indices, _I32, "col_indices", True), _ptr(b, dt, "b", True),
+        _ptr(c, _F32, "c"), batch, stride_values, stride_b, stride_c, _stream(stream)),
+        "sp_spmm_ex")
+
+
+def sp_sddmm_ex(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, alpha, out,
+                batch=1, stride_x=0, stride_y=0, stride_out=0, stream=None):
+    """SDDMM with X and Y in float32, float16 or bfloat16 (one type); out float32."""
+    code = _dtype_of(x, y)
+    dt = [k_ for k_, v in _DTYPE_CODES.items() if v == code][0]
+    _check(lib().sp_sddmm_ex(
+        m, k, d, nnz, _ptr(row_indices, _I32, "row_indices", True),
+        _ptr(row_offsets, _I32, "row_offsets"), _ptr(col_indices, _I32, "col_indices", True),
+        code, _ptr(x, dt, "x", True), _ptr(y, dt, "y", True), float(alpha),
+        _ptr(out, _F32, "out", True), batch, stride_x, stride_y, stride_out, _stream(stream)),
+        "sp_sddmm_ex")
 
 
 def sp_csr_row_softmax(m, nnz, row_indices, row_offsets, inp, out, batch=1, stride_in=0,

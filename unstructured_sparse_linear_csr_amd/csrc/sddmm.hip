@@ -28,6 +28,7 @@
 
 #include "sp_device.h"
 #include "sp_launch.h"
+#include "sp_types.h"
 
 namespace spk {
 
@@ -39,8 +40,8 @@ struct SddmmParams {
     const int *row_offsets;
     const int *col_indices;
     const float *mask_values;  // NULL: scale by alpha only
-    const float *x;
-    const float *y;
+    const void *x;             // element type of the kernel instance
+    const void *y;
     int k;
     float alpha, beta;
     unsigned y_bytes;  // bytes of one Y operand (buffer path)
@@ -60,56 +61,35 @@ __device__ __forceinline__ void store_entry(const SddmmParams &p, long long z, i
     *o = r;
 }
 
-template <int kVec> struct DVec;
-template <> struct DVec<4> {
-    using T = float4;
-    static __device__ __forceinline__ T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
-    static __device__ __forceinline__ float dot(const T &a, const T &b, float acc)
-    {
-        acc = fmaf(a.x, b.x, acc);
-        acc = fmaf(a.y, b.y, acc);
-        acc = fmaf(a.z, b.z, acc);
-        return fmaf(a.w, b.w, acc);
-    }
-};
-template <> struct DVec<1> {
-    using T = float;
-    static __device__ __forceinline__ T zero() { return 0.f; }
-    static __device__ __forceinline__ float dot(const T &a, const T &b, float acc)
-    {
-        return fmaf(a, b, acc);
-    }
-};
-
 #ifndef SP_SDDMM_LOADS_PER_BATCH
 #define SP_SDDMM_LOADS_PER_BATCH 8
 #endif
 constexpr unsigned kOutOfRange = 0x80000000u;  // buffer offset that reads as zero
 
-template <int kVec> __device__ __forceinline__ typename DVec<kVec>::T
-buf_load(__amdgpu_buffer_rsrc_t r, unsigned off);
-template <> __device__ __forceinline__ float4 buf_load<4>(__amdgpu_buffer_rsrc_t r, unsigned off)
+// sum over i < kVec of x[i] * y[i], in order, added to acc with FMA.
+template <typename V, int kVec>
+__device__ __forceinline__ float dot_f32(const float *x, const typename V::T &y, float acc)
 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
-                       __uint_as_float(v[3]));
-}
-template <> __device__ __forceinline__ float buf_load<1>(__amdgpu_buffer_rsrc_t r, unsigned off)
-{
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    float yf[kVec];
+    V::to_f32(y, yf);
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) acc = fmaf(x[i], yf[i], acc);
+    return acc;
 }
 
-// kNv > 0 (Y < 2 GiB): the lane's kNv vectors of the X row live in registers;
-// Y rows are gathered through a buffer resource, and window slots past the
-// row's end carry an out-of-range offset that reads as zeros, so steps are
-// issued in unconditional double-buffered batches of kU.
+// kNv > 0 (Y < 2 GiB): the lane's kNv vectors of the X row live in registers
+// (widened to fp32); Y rows are gathered through a buffer resource, and window
+// slots past the row's end carry an out-of-range offset that reads as zeros,
+// so steps are issued in unconditional double-buffered batches of kU.
 // kNv == 0: any d and any Y size; X and Y are read with 64-bit addresses in a
-// loop over d, one step at a time.
-template <int kG, int kNv, int kVec>
+// loop over d, one step at a time.  E is the element type of X and Y (fp32,
+// fp16 or bf16); arithmetic is fp32 throughout.
+template <typename E, int kG, int kNv, int kVec>
 __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
 {
-    using V = DVec<kVec>;
+    using V = GVec<E, kVec>;
     using VecT = typename V::T;
+    constexpr unsigned kEb = Elem<E>::kBytes;
     constexpr int kNg = kWave / kG;  // entries per step
     constexpr int kU = kNv == 0 ? 1
                                 : (SP_SDDMM_LOADS_PER_BATCH / kNv > 0 ? SP_SDDMM_LOADS_PER_BATCH / kNv : 1);
@@ -131,8 +111,9 @@ __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
     const int p1 = p.row_offsets[row + 1];
     if (p0 >= p1) return;  // one row per wave: uniform, before any barrier
 
-    const float *__restrict__ xr_ptr = p.x + z * p.stride_x + (size_t)row * (size_t)p.d;
-    const float *__restrict__ yz = p.y + z * p.stride_y;
+    const E *__restrict__ xr_ptr =
+        static_cast<const E *>(p.x) + z * p.stride_x + (size_t)row * (size_t)p.d;
+    const E *__restrict__ yz = static_cast<const E *>(p.y) + z * p.stride_y;
 
     if constexpr (kNv == 0) {
         __shared__ int s_col[kWave];
@@ -146,10 +127,12 @@ __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
                 const int j = s * kNg + g;
                 float acc = 0.f;
                 if (j < cnt) {
-                    const float *yr = yz + (size_t)s_col[j] * (size_t)p.d;
-                    for (int e = gl * kVec; e < p.d; e += kG * kVec)
-                        acc = V::dot(*reinterpret_cast<const VecT *>(xr_ptr + e),
-                                     *reinterpret_cast<const VecT *>(yr + e), acc);
+                    const E *yr = yz + (size_t)s_col[j] * (size_t)p.d;
+                    for (int e = gl * kVec; e < p.d; e += kG * kVec) {
+                        float xf[kVec];
+                        V::to_f32(V::load(xr_ptr + e), xf);
+                        acc = dot_f32<V, kVec>(xf, V::load(yr + e), acc);
+                    }
                 }
                 const float sum = group_sum<kG>(acc);
                 if (gl == s) res = sum;
@@ -160,14 +143,14 @@ __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
         }
     } else {
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float *>(yz), 0, (int)p.y_bytes, 0x00020000);
-        VecT xr[kXv];
+            const_cast<E *>(yz), 0, (int)p.y_bytes, 0x00020000);
+        float xr[kXv][kVec];
         unsigned lane_off[kXv];
 #pragma unroll
         for (int v = 0; v < kNv; ++v) {
             const int e = (v * kG + gl) * kVec;
-            xr[v] = e < p.d ? *reinterpret_cast<const VecT *>(xr_ptr + e) : V::zero();
-            lane_off[v] = e < p.d ? (unsigned)e * 4u : kOutOfRange;
+            V::to_f32(e < p.d ? V::load(xr_ptr + e) : V::zero(), xr[v]);
+            lane_off[v] = e < p.d ? (unsigned)e * kEb : kOutOfRange;
         }
         for (int t = kWave + lane; t < kSlots; t += kWave) s_off[t] = kOutOfRange;
 
@@ -176,7 +159,7 @@ __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
             for (int u = 0; u < kU; ++u) {
                 const unsigned off = s_off[(s0 + u) * kNg + g];
 #pragma unroll
-                for (int v = 0; v < kNv; ++v) yv[u][v] = buf_load<kVec>(rsrc, off + lane_off[v]);
+                for (int v = 0; v < kNv; ++v) yv[u][v] = V::buf_load(rsrc, off + lane_off[v]);
             }
         };
         auto reduce_batch = [&](int s0, const VecT (&yv)[kU][kXv], float &res) {
@@ -184,7 +167,7 @@ __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
             for (int u = 0; u < kU; ++u) {
                 float acc = 0.f;
 #pragma unroll
-                for (int v = 0; v < kNv; ++v) acc = V::dot(xr[v], yv[u][v], acc);
+                for (int v = 0; v < kNv; ++v) acc = dot_f32<V, kVec>(xr[v], yv[u][v], acc);
                 const float sum = group_sum<kG>(acc);
                 if (gl == s0 + u) res = sum;
             }
@@ -193,7 +176,7 @@ __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
         for (int base = p0; base < p1; base += kWave) {
             const int cnt = min(kWave, p1 - base);
             s_off[lane] = lane < cnt
-                              ? (unsigned)p.col_indices[base + lane] * (unsigned)p.d * 4u
+                              ? (unsigned)p.col_indices[base + lane] * (unsigned)p.d * kEb
                               : kOutOfRange;
             __syncthreads();
             const int steps = (cnt + kNg - 1) / kNg;
@@ -228,9 +211,11 @@ __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
 // shares (a wave-uniform, scalar load).  Each lane sums its entry's d products
 // in order with FMA; kU gathers are issued before their FMAs.  Idle lanes of a
 // row's last pass gather column 0 (in bounds) and store nothing.
-template <bool kBuf>
+template <typename E, bool kBuf>
 __global__ __launch_bounds__(kWave) void sddmm_cols_kernel(SddmmParams p)
 {
+    using V1 = GVec<E, 1>;
+    constexpr unsigned kEb = Elem<E>::kBytes;
     constexpr int kU = 16;
     const long long w = xcd_work_index(p.batch, p.m);
     if (w < 0) return;
@@ -240,11 +225,12 @@ __global__ __launch_bounds__(kWave) void sddmm_cols_kernel(SddmmParams p)
     const int row = p.row_indices ? p.row_indices[slot] : slot;
     const int p0 = p.row_offsets[row];
     const int p1 = p.row_offsets[row + 1];
-    const float *__restrict__ xr = p.x + z * p.stride_x + (size_t)row * (size_t)p.d;
-    const float *__restrict__ yz = p.y + z * p.stride_y;
+    const E *__restrict__ xr =
+        static_cast<const E *>(p.x) + z * p.stride_x + (size_t)row * (size_t)p.d;
+    const E *__restrict__ yz = static_cast<const E *>(p.y) + z * p.stride_y;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(yz), 0, (int)p.y_bytes, 0x00020000);
-    const unsigned row_bytes = (unsigned)p.k * 4u;
+        const_cast<E *>(yz), 0, (int)p.y_bytes, 0x00020000);
+    const unsigned row_bytes = (unsigned)p.k * kEb;
 
     for (int base = p0; base < p1; base += kWave) {
         const int q = base + lane;
@@ -257,15 +243,18 @@ __global__ __launch_bounds__(kWave) void sddmm_cols_kernel(SddmmParams p)
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 if constexpr (kBuf)
-                    yv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                        rsrc, (int)((unsigned)(l + u) * row_bytes + (unsigned)c * 4u), 0, 0));
+                    V1::to_f32(V1::buf_load(rsrc, (unsigned)(l + u) * row_bytes +
+                                                      (unsigned)c * kEb),
+                               &yv[u]);
                 else
-                    yv[u] = yz[(size_t)(l + u) * (size_t)p.k + (size_t)c];
+                    yv[u] = Elem<E>::f32(yz[(size_t)(l + u) * (size_t)p.k + (size_t)c]);
             }
 #pragma unroll
-            for (int u = 0; u < kU; ++u) acc = fmaf(xr[l + u], yv[u], acc);
+            for (int u = 0; u < kU; ++u) acc = fmaf(Elem<E>::f32(xr[l + u]), yv[u], acc);
         }
-        for (; l < p.d; ++l) acc = fmaf(xr[l], yz[(size_t)l * (size_t)p.k + (size_t)c], acc);
+        for (; l < p.d; ++l)
+            acc = fmaf(Elem<E>::f32(xr[l]),
+                       Elem<E>::f32(yz[(size_t)l * (size_t)p.k + (size_t)c]), acc);
         if (live) store_entry(p, z, q, acc);
     }
 }
@@ -279,35 +268,52 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *dst, long long co
         dz[i] = 0.f;
 }
 
-template <int kG, int kNv, int kVec>
-hipError_t launch_t(const SddmmParams &p, int batch, hipStream_t s)
+template <typename E, int kG, int kNv, int kVec>
+hipError_t launch_t(const SddmmParams &p, hipStream_t s)
 {
-    (void)batch;
     dim3 grid((unsigned)xcd_grid(p.batch, p.m));
-    hipLaunchKernelGGL((sddmm_kernel<kG, kNv, kVec>), grid, dim3(kWave), 0, s, p);
+    hipLaunchKernelGGL((sddmm_kernel<E, kG, kNv, kVec>), grid, dim3(kWave), 0, s, p);
     return hipGetLastError();
 }
 
-template <int kG, int kVec>
-hipError_t launch_nv(int nv, const SddmmParams &p, int batch, hipStream_t s)
+template <typename E, int kG, int kVec>
+hipError_t launch_nv(int nv, const SddmmParams &p, hipStream_t s)
 {
     switch (nv) {
-    case 1: return launch_t<kG, 1, kVec>(p, batch, s);
-    case 2: return launch_t<kG, 2, kVec>(p, batch, s);
-    case 4: return launch_t<kG, 4, kVec>(p, batch, s);
-    case 8: return launch_t<kG, 8, kVec>(p, batch, s);
-    default: return launch_t<kG, 0, kVec>(p, batch, s);
+    case 1: return launch_t<E, kG, 1, kVec>(p, s);
+    case 2: return launch_t<E, kG, 2, kVec>(p, s);
+    case 4: return launch_t<E, kG, 4, kVec>(p, s);
+    case 8: return launch_t<E, kG, 8, kVec>(p, s);
+    default: return launch_t<E, kG, 0, kVec>(p, s);
     }
 }
 
-template <int kVec>
-hipError_t launch_g(int g, int nv, const SddmmParams &p, int batch, hipStream_t s)
+template <typename E, int kVec>
+hipError_t launch_g(int g, int nv, const SddmmParams &p, hipStream_t s)
 {
     switch (g) {
-    case 4: return launch_nv<4, kVec>(nv, p, batch, s);
-    case 8: return launch_nv<8, kVec>(nv, p, batch, s);
-    default: return launch_nv<16, kVec>(nv, p, batch, s);
+    case 4: return launch_nv<E, 4, kVec>(nv, p, s);
+    case 8: return launch_nv<E, 8, kVec>(nv, p, s);
+    default: return launch_nv<E, 16, kVec>(nv, p, s);
     }
+}
+
+// Element type E: 16-byte vectors of kVec16 elements, or single elements.
+template <typename E, int kVec16>
+hipError_t launch_typed(bool vec, int g, int nv, const SddmmParams &p, hipStream_t s)
+{
+    return vec ? launch_g<E, kVec16>(g, nv, p, s) : launch_g<E, 1>(g, nv, p, s);
+}
+
+template <typename E>
+hipError_t launch_cols(bool buf, const SddmmParams &p, hipStream_t s)
+{
+    const dim3 grid((unsigned)xcd_grid(p.batch, p.m));
+    if (buf)
+        hipLaunchKernelGGL((sddmm_cols_kernel<E, true>), grid, dim3(kWave), 0, s, p);
+    else
+        hipLaunchKernelGGL((sddmm_cols_kernel<E, false>), grid, dim3(kWave), 0, s, p);
+    return hipGetLastError();
 }
 
 inline bool aligned16(const void *ptr)
@@ -353,16 +359,17 @@ hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream)
     p.stride_x = a.stride_x;
     p.stride_y = a.stride_y;
     p.stride_out = a.stride_out;
+    const int eb = a.dtype == Dtype::f32 ? 4 : 2;  // bytes per element of X and Y
+    const int vlen = 16 / eb;                        // elements per 16-byte vector
+    // Buffer offsets into Y must stay below 2^31 (padding offsets lie beyond).
+    const bool buf = (long long)a.k * (long long)a.d * eb <= (1LL << 31);
+    p.y_bytes = buf ? (unsigned)((long long)a.k * a.d * eb) : 0u;
     if (a.y_layout == 1) {
-        // Buffer offsets (l*k + c)*4 must stay below 2^31.
-        const bool buf = (long long)a.k * (long long)a.d <= (1LL << 29);
-        p.y_bytes = buf ? (unsigned)((long long)a.k * a.d * 4) : 0u;
-        const dim3 grid((unsigned)xcd_grid(a.batch, a.m));
-        if (buf)
-            hipLaunchKernelGGL(sddmm_cols_kernel<true>, grid, dim3(kWave), 0, stream, p);
-        else
-            hipLaunchKernelGGL(sddmm_cols_kernel<false>, grid, dim3(kWave), 0, stream, p);
-        return hipGetLastError();
+        switch (a.dtype) {
+        case Dtype::f16: return launch_cols<_Float16>(buf, p, stream);
+        case Dtype::bf16: return launch_cols<bf16>(buf, p, stream);
+        default: return launch_cols<float>(buf, p, stream);
+        }
     }
     if (a.d == 0 && a.mask_values == nullptr && a.beta == 0.f) {
         const long long blocks = std::min<long long>((a.nnz + 255) / 256, 65536);
@@ -370,20 +377,21 @@ hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream)
                            dim3(256), 0, stream, a.out, (long long)a.nnz, a.stride_out);
         return hipGetLastError();
     }
-    const bool vec = (a.d % 4 == 0) && aligned16(a.x) && aligned16(a.y) &&
-                     (a.stride_x % 4 == 0) && (a.stride_y % 4 == 0);
+    const bool vec = (a.d % vlen == 0) && aligned16(a.x) && aligned16(a.y) &&
+                     (a.stride_x % vlen == 0) && (a.stride_y % vlen == 0);
     // Register-resident X and buffer gathers need valid offsets below Y's size
     // and padding offsets (>= 2^31) beyond it.
-    const bool buf = (long long)a.k * (long long)a.d <= (1LL << 29);
-    const int kvec = vec ? 4 : 1;
+    const int kvec = vec ? vlen : 1;
     const int dv = (a.d + kvec - 1) / kvec;
     const int g = dv <= 4 ? 4 : dv <= 8 ? 8 : 16;
     const int need = (dv + g - 1) / g;
     int nv = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
     if (!buf) nv = 0;
-    p.y_bytes = buf ? (unsigned)((long long)a.k * a.d * 4) : 0u;
-    return vec ? launch_g<4>(g, nv, p, a.batch, stream)
-               : launch_g<1>(g, nv, p, a.batch, stream);
+    switch (a.dtype) {
+    case Dtype::f16: return launch_typed<_Float16, 8>(vec, g, nv, p, stream);
+    case Dtype::bf16: return launch_typed<bf16, 8>(vec, g, nv, p, stream);
+    default: return launch_typed<float, 4>(vec, g, nv, p, stream);
+    }
 }
 
 }  // namespace spk

@@ -22,6 +22,56 @@ hipStream_t as_stream(sp_stream_t s) { return reinterpret_cast<hipStream_t>(s); 
 // A pointer must be non-NULL when the buffer it describes is non-empty.
 bool need(const void *ptr, long long elements) { return elements <= 0 || ptr != nullptr; }
 
+bool dtype_of(int code, spk::Dtype *out)
+{
+    switch (code) {
+    case SP_DTYPE_F32: *out = spk::Dtype::f32; return true;
+    case SP_DTYPE_F16: *out = spk::Dtype::f16; return true;
+    case SP_DTYPE_BF16: *out = spk::Dtype::bf16; return true;
+    default: return false;
+    }
+}
+
+sp_status_t sddmm_any(int m, int k, int d, int nnz, const int *row_indices,
+                      const int *row_offsets, const int *col_indices,
+                      const float *mask_values, spk::Dtype dtype, const void *x, const void *y,
+                      int y_layout, float alpha, float beta, float *out, int batch,
+                      long long stride_values, long long stride_x, long long stride_y,
+                      long long stride_out, sp_stream_t stream)
+{
+    if (m < 0 || k < 0 || d < 0 || nnz < 0 || batch < 0 || stride_values < 0 ||
+        stride_x < 0 || stride_y < 0 || stride_out < 0)
+        return SP_ERROR_INVALID_VALUE;
+    if (y_layout != SP_Y_KD && y_layout != SP_Y_DK) return SP_ERROR_INVALID_VALUE;
+    if (m == 0 || nnz == 0 || batch == 0) return SP_SUCCESS;
+    if (!need(row_offsets, m) || !need(col_indices, nnz) || out == nullptr ||
+        !need(x, (long long)m * d) || !need(y, (long long)k * d))
+        return SP_ERROR_INVALID_VALUE;
+    if (batch > 1 && stride_out < nnz) return SP_ERROR_INVALID_VALUE;
+    spk::SddmmArgs a;
+    a.m = m;
+    a.k = k;
+    a.d = d;
+    a.nnz = nnz;
+    a.row_indices = row_indices;
+    a.row_offsets = row_offsets;
+    a.col_indices = col_indices;
+    a.mask_values = mask_values;
+    a.x = x;
+    a.y = y;
+    a.y_layout = y_layout;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.out = out;
+    a.batch = batch;
+    a.stride_values = stride_values;
+    a.stride_x = stride_x;
+    a.stride_y = stride_y;
+    a.stride_out = stride_out;
+    a.dtype = dtype;
+    return from_hip(spk::launch_sddmm(a, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -88,12 +138,13 @@ sp_status_t sp_csr_build_from_lengths(int m, const int *lengths, int *row_offset
                                                   as_stream(stream)));
 }
 
-sp_status_t sp_spmm_batched(int m, int k, int n, int nnz, const int *row_indices,
-                            const float *values, const int *row_offsets,
-                            const int *col_indices, const float *b, float *c,
-                            int batch, long long stride_values, long long stride_b,
-                            long long stride_c, sp_stream_t stream)
+sp_status_t sp_spmm_ex(int m, int k, int n, int nnz, const int *row_indices, int dtype,
+                       const void *values, const int *row_offsets, const int *col_indices,
+                       const void *b, float *c, int batch, long long stride_values,
+                       long long stride_b, long long stride_c, sp_stream_t stream)
 {
+    spk::Dtype dt;
+    if (!dtype_of(dtype, &dt)) return SP_ERROR_INVALID_VALUE;
     if (m < 0 || k < 0 || n < 0 || nnz < 0 || batch < 0 || stride_values < 0 ||
         stride_b < 0 || stride_c < 0)
         return SP_ERROR_INVALID_VALUE;
@@ -117,7 +168,18 @@ sp_status_t sp_spmm_batched(int m, int k, int n, int nnz, const int *row_indices
     a.stride_values = stride_values;
     a.stride_b = stride_b;
     a.stride_c = stride_c;
+    a.dtype = dt;
     return from_hip(spk::launch_spmm(a, as_stream(stream)));
+}
+
+sp_status_t sp_spmm_batched(int m, int k, int n, int nnz, const int *row_indices,
+                            const float *values, const int *row_offsets,
+                            const int *col_indices, const float *b, float *c,
+                            int batch, long long stride_values, long long stride_b,
+                            long long stride_c, sp_stream_t stream)
+{
+    return sp_spmm_ex(m, k, n, nnz, row_indices, SP_DTYPE_F32, values, row_offsets,
+                      col_indices, b, c, batch, stride_values, stride_b, stride_c, stream);
 }
 
 sp_status_t sp_spmm(int m, int k, int n, int nnz, const int *row_indices,
@@ -136,36 +198,22 @@ sp_status_t sp_sddmm_general(int m, int k, int d, int nnz, const int *row_indice
                              long long stride_values, long long stride_x,
                              long long stride_y, long long stride_out, sp_stream_t stream)
 {
-    if (m < 0 || k < 0 || d < 0 || nnz < 0 || batch < 0 || stride_values < 0 ||
-        stride_x < 0 || stride_y < 0 || stride_out < 0)
-        return SP_ERROR_INVALID_VALUE;
-    if (y_layout != SP_Y_KD && y_layout != SP_Y_DK) return SP_ERROR_INVALID_VALUE;
-    if (m == 0 || nnz == 0 || batch == 0) return SP_SUCCESS;
-    if (!need(row_offsets, m) || !need(col_indices, nnz) || out == nullptr ||
-        !need(x, (long long)m * d) || !need(y, (long long)k * d))
-        return SP_ERROR_INVALID_VALUE;
-    if (batch > 1 && stride_out < nnz) return SP_ERROR_INVALID_VALUE;
-    spk::SddmmArgs a;
-    a.m = m;
-    a.k = k;
-    a.d = d;
-    a.nnz = nnz;
-    a.row_indices = row_indices;
-    a.row_offsets = row_offsets;
-    a.col_indices = col_indices;
-    a.mask_values = mask_values;
-    a.x = x;
-    a.y = y;
-    a.y_layout = y_layout;
-    a.alpha = alpha;
-    a.beta = beta;
-    a.out = out;
-    a.batch = batch;
-    a.stride_values = stride_values;
-    a.stride_x = stride_x;
-    a.stride_y = stride_y;
-    a.stride_out = stride_out;
-    return from_hip(spk::launch_sddmm(a, as_stream(stream)));
+    return sddmm_any(m, k, d, nnz, row_indices, row_offsets, col_indices, mask_values,
+                     spk::Dtype::f32, x, y, y_layout, alpha, beta, out, batch, stride_values,
+                     stride_x, stride_y, stride_out, stream);
+}
+
+sp_status_t sp_sddmm_ex(int m, int k, int d, int nnz, const int *row_indices,
+                        const int *row_offsets, const int *col_indices, int dtype,
+                        const void *x, const void *y, float alpha, float *out, int batch,
+                        long long stride_x, long long stride_y, long long stride_out,
+                        sp_stream_t stream)
+{
+    spk::Dtype dt;
+    if (!dtype_of(dtype, &dt)) return SP_ERROR_INVALID_VALUE;
+    return sddmm_any(m, k, d, nnz, row_indices, row_offsets, col_indices, nullptr, dt, x, y,
+                     SP_Y_KD, alpha, 0.f, out, batch, 0, stride_x, stride_y, stride_out,
+                     stream);
 }
 
 sp_status_t sp_sddmm_batched(int m, int k, int d, int nnz, const int *row_indices,

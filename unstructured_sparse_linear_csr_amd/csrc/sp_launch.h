@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "sp_types.h"
+
 namespace spk {
 
 struct SpmmArgs {
@@ -11,11 +13,12 @@ struct SpmmArgs {
     const int *row_indices;  // NULL = identity order
     const int *row_offsets;
     const int *col_indices;
-    const float *values;
-    const float *b;
+    const void *values;  // element type `dtype`
+    const void *b;       // element type `dtype`
     float *c;
     int batch;
     long long stride_values, stride_b, stride_c;  // elements
+    Dtype dtype = Dtype::f32;
 };
 
 struct SddmmArgs {
@@ -24,13 +27,14 @@ struct SddmmArgs {
     const int *row_offsets;
     const int *col_indices;
     const float *mask_values;  // NULL = no scaling by the mask's values
-    const float *x;
-    const float *y;
+    const void *x;             // element type `dtype`
+    const void *y;             // element type `dtype`
     int y_layout;  // 0: Y is k x d; 1: Y is d x k
     float alpha, beta;  // beta == 0: out is not read
     float *out;
     int batch;
     long long stride_values, stride_x, stride_y, stride_out;  // elements
+    Dtype dtype = Dtype::f32;
 };
 
 hipError_t launch_offsets_from_lengths(int m, const int *lengths,

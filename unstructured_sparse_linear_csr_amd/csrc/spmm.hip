@@ -30,6 +30,7 @@
 // whatever row order is used.
 #include "sp_device.h"
 #include "sp_launch.h"
+#include "sp_types.h"
 
 namespace spk {
 
@@ -53,59 +54,25 @@ struct SpmmParams {
     const int *row_indices;
     const int *row_offsets;
     const int *col_indices;
-    const float *values;
-    const float *b;
+    const void *values;  // element type of the kernel instance (fp32 elsewhere)
+    const void *b;
     float *c;
     long long stride_values, stride_b, stride_c;
 };
 
-template <int kVec> struct Vec;
-template <> struct Vec<4> {
-    using T = float4;
-    static __device__ __forceinline__ T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
-    static __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, unsigned off)
-    {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-        return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]),
-                           __uint_as_float(v[2]), __uint_as_float(v[3]));
-    }
-    static __device__ __forceinline__ void fma(float a, const T &b, float *acc)
-    {
-        acc[0] = fmaf(a, b.x, acc[0]);
-        acc[1] = fmaf(a, b.y, acc[1]);
-        acc[2] = fmaf(a, b.z, acc[2]);
-        acc[3] = fmaf(a, b.w, acc[3]);
-    }
-    static __device__ __forceinline__ void store(float *dst, const float *acc)
-    {
-        *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    }
-};
-template <> struct Vec<1> {
-    using T = float;
-    static __device__ __forceinline__ T zero() { return 0.f; }
-    static __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, unsigned off)
-    {
-        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
-    }
-    static __device__ __forceinline__ void fma(float a, const T &b, float *acc)
-    {
-        acc[0] = fmaf(a, b, acc[0]);
-    }
-    static __device__ __forceinline__ void store(float *dst, const float *acc)
-    {
-        *dst = acc[0];
-    }
-};
+template <int kVec> using Vec = GVec<float, kVec>;
 
 // kBuf: B < 2 GiB, gathers through a buffer resource with byte offsets.
 // Otherwise: 64-bit addressing, staged offsets are columns, padding has value
-// 0 and column -1 and is skipped by a predicate.
-template <int kLpr, int kVec, bool kVecCsr, bool kBuf>
+// 0 and column -1 and is skipped by a predicate.  E is the element type of
+// the values and of B (fp32, fp16 or bf16); values are widened to fp32 when
+// staged and B elements when gathered, so all arithmetic is fp32.
+template <typename E, int kLpr, int kVec, bool kVecCsr, bool kBuf>
 __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
 {
-    using V = Vec<kVec>;
+    using V = GVec<E, kVec>;
     using VecT = typename V::T;
+    constexpr unsigned kEb = Elem<E>::kBytes;
     constexpr int kRpw = kWave / kLpr;       // rows per wave
     constexpr int kChunk = kEpl * kLpr;      // entries per row per window
     // A group's slots: the window, kU padding slots read by the prefetch, and
@@ -130,8 +97,8 @@ __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
     const int lane = threadIdx.x;
     const int grp = kRpw == 1 ? 0 : lane / kLpr;
     const int gl = kRpw == 1 ? lane : lane - grp * kLpr;
-    const float *__restrict__ vals = p.values + z * p.stride_values;
-    const float *__restrict__ bz = p.b + z * p.stride_b;
+    const E *__restrict__ vals = static_cast<const E *>(p.values) + z * p.stride_values;
+    const E *__restrict__ bz = static_cast<const E *>(p.b) + z * p.stride_b;
     float *__restrict__ cz = p.c + z * p.stride_c;
 
     const int slot = rb * kRpw + grp;
@@ -140,9 +107,9 @@ __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
     const int p0 = has_row ? p.row_offsets[row] : 0;
     const int p1 = has_row ? p.row_offsets[row + 1] : 0;
     const int col0 = (tile * kLpr + gl) * kVec;
-    const bool col_ok = col0 < p.n;  // vector path: n % 4 == 0, so the whole vector is in range
+    const bool col_ok = col0 < p.n;  // vector path: n % kVec == 0, so the whole vector is in range
     // Lanes past the last column read only out-of-range (zero) data.
-    const unsigned lane_bytes = col_ok ? (unsigned)col0 * 4u : kOutOfRange;
+    const unsigned lane_bytes = col_ok ? (unsigned)col0 * kEb : kOutOfRange;
     int *g_off = s_off + grp * kPitch;
     float *g_val = s_val + grp * kPitch;
     for (int j = gl; j < kU; j += kLpr) {
@@ -152,13 +119,13 @@ __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
 
     __amdgpu_buffer_rsrc_t rsrc;
     if constexpr (kBuf)
-        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(bz), 0, p.b_bytes,
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<E *>(bz), 0, p.b_bytes,
                                                  0x00020000);
 
     auto offset_of = [&](int idx, int col) -> int {
         const bool in = idx >= p0 && idx < p1;
         if constexpr (kBuf)
-            return in ? (int)((unsigned)col * (unsigned)p.n * 4u) : kPad;
+            return in ? (int)((unsigned)col * (unsigned)p.n * kEb) : kPad;
         else
             return in ? col : kPad;
     };
@@ -170,7 +137,7 @@ __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
             return V::buf_load(rsrc, (unsigned)off + lane_bytes);
         } else {
             if (off < 0 || !col_ok) return V::zero();
-            return *reinterpret_cast<const VecT *>(bz + (size_t)off * (size_t)p.n + col0);
+            return V::load(bz + (size_t)off * (size_t)p.n + col0);
         }
     };
     // kU staged entries starting at slot j (a multiple of 4): 16-byte
@@ -204,15 +171,14 @@ __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
                 if (e < p1 && e + 4 > p0) {
                     if (e + 4 <= p.nnz) {
                         const int4 c4 = *reinterpret_cast<const int4 *>(p.col_indices + e);
-                        const float4 v4 = *reinterpret_cast<const float4 *>(vals + e);
                         cc[0] = c4.x; cc[1] = c4.y; cc[2] = c4.z; cc[3] = c4.w;
-                        vv[0] = v4.x; vv[1] = v4.y; vv[2] = v4.z; vv[3] = v4.w;
+                        load4_f32<E>(vals + e, vv);
                     } else {
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
                             if (e + t < p.nnz) {
                                 cc[t] = p.col_indices[e + t];
-                                vv[t] = vals[e + t];
+                                vv[t] = Elem<E>::f32(vals[e + t]);
                             }
                         }
                     }
@@ -230,7 +196,7 @@ __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
                 const int idx = win + t * kLpr + gl;
                 const bool in = idx < p1;
                 g_off[t * kLpr + gl] = offset_of(idx, in ? p.col_indices[idx] : 0);
-                g_val[t * kLpr + gl] = value_of(idx, in ? vals[idx] : 0.f);
+                g_val[t * kLpr + gl] = value_of(idx, in ? Elem<E>::f32(vals[idx]) : 0.f);
             }
         }
         __syncthreads();
@@ -301,8 +267,8 @@ __global__ __launch_bounds__(kWave) void spmm_narrow_kernel(SpmmParams p)
     const int row = p.row_indices ? p.row_indices[slot] : slot;
     const int p0 = p.row_offsets[row];
     const int p1 = p.row_offsets[row + 1];
-    const float *vals = p.values + z * p.stride_values;
-    const float *bz = p.b + z * p.stride_b;
+    const float *vals = static_cast<const float *>(p.values) + z * p.stride_values;
+    const float *bz = static_cast<const float *>(p.b) + z * p.stride_b;
     float *cz = p.c + z * p.stride_c;
     const int col0 = v * kVec;
     const bool col_ok = col0 < p.n;
@@ -389,7 +355,7 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
         for (int i = tid; i < nb / 4; i += kLdsThreads)
             reinterpret_cast<float4 *>(s_b)[i] = b4[i];
     } else {
-        for (int i = tid; i < nb; i += kLdsThreads) s_b[i] = p.b[i];
+        for (int i = tid; i < nb; i += kLdsThreads) s_b[i] = static_cast<const float *>(p.b)[i];
     }
     __syncthreads();
 
@@ -401,7 +367,7 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int *>(p.col_indices), 0, (int)p.csr_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(p.values), 0, (int)p.csr_bytes, 0x00020000);
+        const_cast<void *>(p.values), 0, (int)p.csr_bytes, 0x00020000);
     const int last4 = p.nnz - 4;  // first entry of the array's last full segment (nnz >= 4)
 
     const int *__restrict__ order = p.row_indices;
@@ -563,58 +529,70 @@ hipError_t launch_narrow(int e, const SpmmParams &p, hipStream_t s)
     }
 }
 
-template <int kLpr, int kVec, bool kVecCsr, bool kBuf>
-hipError_t launch_t(const SpmmParams &p, int tiles, int batch, hipStream_t s)
+template <typename E, int kLpr, int kVec, bool kVecCsr, bool kBuf>
+hipError_t launch_t(const SpmmParams &p, hipStream_t s)
 {
-    (void)tiles;
-    (void)batch;
     dim3 grid((unsigned)xcd_grid((long long)p.batch * p.tiles, p.row_blocks));
-    hipLaunchKernelGGL((spmm_kernel<kLpr, kVec, kVecCsr, kBuf>), grid, dim3(kWave), 0, s, p);
+    hipLaunchKernelGGL((spmm_kernel<E, kLpr, kVec, kVecCsr, kBuf>), grid, dim3(kWave), 0, s, p);
     return hipGetLastError();
 }
 
-template <int kLpr, int kVec>
-hipError_t launch_csr(const SpmmParams &p, int tiles, int batch, bool vec_csr, bool buf,
-                      hipStream_t s)
+template <typename E, int kLpr, int kVec>
+hipError_t launch_csr(const SpmmParams &p, bool vec_csr, bool buf, hipStream_t s)
 {
     if (vec_csr)
-        return buf ? launch_t<kLpr, kVec, true, true>(p, tiles, batch, s)
-                   : launch_t<kLpr, kVec, true, false>(p, tiles, batch, s);
-    return buf ? launch_t<kLpr, kVec, false, true>(p, tiles, batch, s)
-               : launch_t<kLpr, kVec, false, false>(p, tiles, batch, s);
+        return buf ? launch_t<E, kLpr, kVec, true, true>(p, s)
+                   : launch_t<E, kLpr, kVec, true, false>(p, s);
+    return buf ? launch_t<E, kLpr, kVec, false, true>(p, s)
+               : launch_t<E, kLpr, kVec, false, false>(p, s);
 }
 
-template <int kVec>
-hipError_t launch_lpr(int lpr, const SpmmParams &p, int tiles, int batch, bool vec_csr,
-                      bool buf, hipStream_t s)
+template <typename E, int kVec>
+hipError_t launch_lpr(int lpr, const SpmmParams &p, bool vec_csr, bool buf, hipStream_t s)
 {
     switch (lpr) {
-    case 8: return launch_csr<8, kVec>(p, tiles, batch, vec_csr, buf, s);
-    case 16: return launch_csr<16, kVec>(p, tiles, batch, vec_csr, buf, s);
-    case 32: return launch_csr<32, kVec>(p, tiles, batch, vec_csr, buf, s);
-    default: return launch_csr<64, kVec>(p, tiles, batch, vec_csr, buf, s);
+    case 8: return launch_csr<E, 8, kVec>(p, vec_csr, buf, s);
+    case 16: return launch_csr<E, 16, kVec>(p, vec_csr, buf, s);
+    case 32: return launch_csr<E, 32, kVec>(p, vec_csr, buf, s);
+    default: return launch_csr<E, 64, kVec>(p, vec_csr, buf, s);
     }
 }
 
-inline bool aligned16(const void *ptr)
+// The wide kernel for element type E: 16-byte vectors (kVec16 elements) or
+// single elements.
+template <typename E, int kVec16>
+hipError_t launch_wide(bool vec, int lpr, const SpmmParams &p, bool vec_csr, bool buf,
+                       hipStream_t s)
 {
-    return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0;
+    return vec ? launch_lpr<E, kVec16>(lpr, p, vec_csr, buf, s)
+               : launch_lpr<E, 1>(lpr, p, vec_csr, buf, s);
 }
+
+inline bool aligned(const void *ptr, unsigned bytes)
+{
+    return (reinterpret_cast<uintptr_t>(ptr) & (bytes - 1u)) == 0;
+}
+inline bool aligned16(const void *ptr) { return aligned(ptr, 16); }
 
 }  // namespace
 
 // Lanes per row: the smallest of 8/16/32/64 that covers the row's vectors,
 // else 64 with several column tiles.  A grid that would not fit the launch
-// limits returns hipErrorInvalidConfiguration without launching.
+// limits returns hipErrorInvalidConfiguration without launching.  fp16 and
+// bf16 operands take the wide kernel with 8-element vectors (or single
+// elements) for every width.
 hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream)
 {
-    const bool vec = (a.n % 4 == 0) && aligned16(a.b) && aligned16(a.c) &&
-                     (a.stride_b % 4 == 0) && (a.stride_c % 4 == 0);
-    const bool vec_csr = aligned16(a.col_indices) && aligned16(a.values) &&
+    const bool f32 = a.dtype == Dtype::f32;
+    const int eb = f32 ? 4 : 2;   // bytes per element of values and B
+    const int vlen = 16 / eb;     // elements per 16-byte vector
+    const bool vec = (a.n % vlen == 0) && aligned16(a.b) && aligned16(a.c) &&
+                     (a.stride_b % vlen == 0) && (a.stride_c % 4 == 0);
+    const bool vec_csr = aligned16(a.col_indices) && aligned(a.values, 4u * eb) &&
                          (a.stride_values % 4 == 0);
     // Valid offsets stay below B's size and padding offsets (>= 2^31) beyond it.
-    const bool buf = (long long)a.k * (long long)a.n <= (1LL << 29);
-    const int kvec = vec ? 4 : 1;
+    const bool buf = (long long)a.k * (long long)a.n * eb <= (1LL << 31);
+    const int kvec = vec ? vlen : 1;
     const int nv = (a.n + kvec - 1) / kvec;
     const int lpr = nv <= 8 ? 8 : nv <= 16 ? 16 : nv <= 32 ? 32 : 64;
     const int rpw = kWave / lpr;
@@ -624,7 +602,7 @@ hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream)
         return hipErrorInvalidConfiguration;
 
     // Narrow B: lanes over entries (needs the buffer paths for B and the CSR).
-    const bool narrow = buf && nv <= 4 && (long long)a.nnz * 4 <= (1LL << 31);
+    const bool narrow = f32 && buf && nv <= 4 && (long long)a.nnz * 4 <= (1LL << 31);
     if (narrow && xcd_grid(a.batch, a.m) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 
     SpmmParams p;
@@ -634,7 +612,7 @@ hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream)
     p.row_blocks = (int)row_blocks;
     p.tiles = tiles;
     p.batch = a.batch;
-    p.b_bytes = buf ? (unsigned)((long long)a.k * a.n * 4) : 0u;
+    p.b_bytes = buf ? (unsigned)((long long)a.k * a.n * eb) : 0u;
     p.csr_bytes = narrow ? (unsigned)((long long)a.nnz * 4) : 0u;
     p.row_indices = a.row_indices;
     p.row_offsets = a.row_offsets;
@@ -667,8 +645,11 @@ hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream)
         }
         return vec ? launch_narrow<4>(e, p, stream) : launch_narrow<1>(e, p, stream);
     }
-    return vec ? launch_lpr<4>(lpr, p, tiles, a.batch, vec_csr, buf, stream)
-               : launch_lpr<1>(lpr, p, tiles, a.batch, vec_csr, buf, stream);
+    switch (a.dtype) {
+    case Dtype::f16: return launch_wide<_Float16, 8>(vec, lpr, p, vec_csr, buf, stream);
+    case Dtype::bf16: return launch_wide<bf16, 8>(vec, lpr, p, vec_csr, buf, stream);
+    default: return launch_wide<float, 4>(vec, lpr, p, vec_csr, buf, stream);
+    }
 }
 
 }  // namespace spk
