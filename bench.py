@@ -529,15 +529,18 @@ def main() -> int:
     def k_sddmm():
         sp.sp_sddmm(m, k, d, nnz, ri, ro, cols, x, y, 1.0, out)
 
+    def k_fused():
+        sp.sp_spmm_sddmm(m, k, n, nnz, ri, vals, ro, cols, b, c, m, k, d, nnz, ri, ro, cols, x,
+                         y, 1.0, out)
+
     def step():
         k_build()
-        k_spmm()
-        k_sddmm()
+        k_fused()
 
     if args.profile_launches:
         step()
         torch.cuda.synchronize()
-        for fn in (k_build, k_offsets, k_swizzle, k_spmm, k_sddmm):
+        for fn in (k_build, k_offsets, k_swizzle, k_spmm, k_sddmm, k_fused):
             for _ in range(args.profile_launches):
                 fn()
         if args.profile_stream:
@@ -590,7 +593,7 @@ def main() -> int:
     kernel_us = {}
     for name, fn in (("csr_build_from_lengths", k_build),
                      ("csr_offsets_from_lengths", k_offsets), ("row_swizzle", k_swizzle),
-                     ("spmm", k_spmm), ("sddmm", k_sddmm)):
+                     ("spmm", k_spmm), ("sddmm", k_sddmm), ("spmm_sddmm", k_fused)):
         g = capture(fn, args.kernel_reps)
         g.replay()
         torch.cuda.synchronize()
@@ -614,6 +617,9 @@ def main() -> int:
                   "gflops": 2.0 * nnz * d / sddmm_s / 1e9,
                   "compulsory_gbs": db / sddmm_s / 1e9,
                   "gather_gbs": 4.0 * nnz * d / sddmm_s / 1e9},
+        "spmm_sddmm": {"avg_us": kernel_us["spmm_sddmm"],
+                       "gflops": flops_step / (kernel_us["spmm_sddmm"] * 1e-6) / 1e9,
+                       "note": "the SpMM and the SDDMM in one launch (in the step)"},
         "csr_build_from_lengths": {"avg_us": kernel_us["csr_build_from_lengths"],
                                    "note": "offsets and swizzled order in one launch (in the step)"},
         "row_swizzle": {"avg_us": kernel_us["row_swizzle"], "note": "standalone, not in the step"},
@@ -636,7 +642,8 @@ def main() -> int:
         "config": {"workload": w["name"], "m": m, "k": k, "n": n, "d": d, "nnz": nnz,
                    "sparsity": stats["sparsity"], "mean_row_length": stats["mean_row_length"],
                    "row_length_cov": stats["row_length_cov"],
-                   "step": "csr_build_from_lengths (offsets + row swizzle) + spmm + sddmm",
+                   "step": ("csr_build_from_lengths (offsets + row swizzle), then spmm and "
+                            "sddmm in one launch (sp_spmm_sddmm)"),
                    "launch": "HIP graph of the K steps", "flops_per_step": flops_step},
         "roofline": roofline,
         "kernels": kernels,

@@ -126,6 +126,29 @@ sp_status_t sp_csr_build_from_lengths(int m, const int *lengths, int *row_offset
                                       int *row_indices, sp_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * SpMM and SDDMM together ("Summary" of the card: the two kernels of the
+ * method).  Problems of DL sizes leave the GPU mostly idle in either kernel
+ * alone; one launch that carries both keeps it busier and pays one launch.
+ * ---------------------------------------------------------------------- */
+
+/* The SpMM sp_spmm(m, k, n, nnz, row_indices, values, row_offsets,
+ * col_indices, b, c) and the SDDMM sp_sddmm(s_m, s_k, d, s_nnz,
+ * s_row_indices, s_row_offsets, s_col_indices, x, y, alpha, out) -- two
+ * independent problems, whose sparsity structures may be the same arrays or
+ * different ones -- enqueued as one launch when both take their fp32 vector
+ * paths (16-byte aligned operands, B and Y under 2 GiB, n % 4 == 0,
+ * d % 4 == 0, d <= 256), otherwise as the two separate launches.  Results
+ * are bit-identical to calling the two entry points.  Arguments are checked
+ * as those entry points check them; c and out must not overlap each other or
+ * any input. */
+sp_status_t sp_spmm_sddmm(int m, int k, int n, int nnz, const int *row_indices,
+                          const float *values, const int *row_offsets, const int *col_indices,
+                          const float *b, float *c, int s_m, int s_k, int d, int s_nnz,
+                          const int *s_row_indices, const int *s_row_offsets,
+                          const int *s_col_indices, const float *x, const float *y,
+                          float alpha, float *out, sp_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Transpose ("Summary" of the card: the kernels serve training; the input
  * gradient of C = A * B is dB = A^T * dC, an SpMM with the transposed sparse
  * operand).  sp_csr_transpose gives A^T in standard CSR; sp_row_swizzle and

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 18, declared
+    assert len(declared) == 19, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -73,6 +73,31 @@ def test_spmm_validation(lib):
     assert f(4, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, 0, 0, 0, 0, s) == OK
     assert lib.sp_spmm(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, s) == OK
     assert lib.sp_spmm(-2, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, s) == INVALID
+
+
+def test_spmm_sddmm_validation(lib):
+    f = lib.sp_spmm_sddmm
+    s = NULL
+    fl = ctypes.c_float(1.0)
+
+    def call(spmm=(4, 4, 4, 8), sddmm=(4, 4, 4, 8), v=FAKE, x=FAKE, c=FAKE, out=FAKE):
+        m, k, n, nnz = spmm
+        sm, sk, d, snnz = sddmm
+        return f(m, k, n, nnz, NULL, v, FAKE, FAKE, FAKE, c, sm, sk, d, snnz, NULL, FAKE, FAKE,
+                 x, FAKE, fl, out, s)
+
+    assert call(spmm=(-1, 4, 4, 8)) == INVALID
+    assert call(sddmm=(4, 4, -1, 8)) == INVALID
+    assert call(v=NULL) == INVALID
+    assert call(x=NULL) == INVALID
+    assert call(c=NULL) == INVALID
+    assert call(out=NULL) == INVALID
+    # an invalid half is reported even when the other half is empty
+    assert call(spmm=(0, 4, 4, 0), x=NULL) == INVALID
+    assert call(sddmm=(0, 4, 4, 0), v=NULL) == INVALID
+    # both halves empty: nothing to do
+    assert f(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, 0, 4, 4, 0, NULL, NULL, NULL,
+             NULL, NULL, fl, NULL, s) == OK
 
 
 def test_mixed_precision_validation(lib):

@@ -58,6 +58,9 @@ SIGNATURES = {
     "sp_csr_transpose": ([_c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           ctypes.c_size_t, _vp], _c_int),
     "sp_csr_transpose_values": ([_c_int, _vp, _vp, _vp, _vp], _c_int),
+    "sp_spmm_sddmm": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+                       _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_float, _vp,
+                       _vp], _c_int),
     "sp_spmm_ex": ([_c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp,
                     _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
     "sp_sddmm_ex": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
@@ -243,6 +246,22 @@ def sp_csr_transpose_values(nnz, t_perm, values, t_values, stream=None):
     _check(lib().sp_csr_transpose_values(
         nnz, _ptr(t_perm, _I32, "t_perm", True), _ptr(values, _F32, "values", True),
         _ptr(t_values, _F32, "t_values", True), _stream(stream)), "sp_csr_transpose_values")
+
+
+def sp_spmm_sddmm(m, k, n, nnz, row_indices, values, row_offsets, col_indices, b, c,
+                  s_m, s_k, d, s_nnz, s_row_indices, s_row_offsets, s_col_indices, x, y, alpha,
+                  out, stream=None):
+    """sp_spmm(...) and sp_sddmm(...) as one launch where possible."""
+    _check(lib().sp_spmm_sddmm(
+        m, k, n, nnz, _ptr(row_indices, _I32, "row_indices", True),
+        _ptr(values, _F32, "values", True), _ptr(row_offsets, _I32, "row_offsets", True),
+        _ptr(col_indices, _I32, "col_indices", True), _ptr(b, _F32, "b", True),
+        _ptr(c, _F32, "c", True), s_m, s_k, d, s_nnz,
+        _ptr(s_row_indices, _I32, "s_row_indices", True),
+        _ptr(s_row_offsets, _I32, "s_row_offsets", True),
+        _ptr(s_col_indices, _I32, "s_col_indices", True), _ptr(x, _F32, "x", True),
+        _ptr(y, _F32, "y", True), float(alpha), _ptr(out, _F32, "out", True),
+        _stream(stream)), "sp_spmm_sddmm")
 
 
 _DTYPE_CODES = {torch.float32: SP_DTYPE_F32, torch.float16: SP_DTYPE_F16,

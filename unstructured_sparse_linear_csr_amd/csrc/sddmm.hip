@@ -1,207 +1,25 @@
-// CSR SDDMM for gfx950: out[p] = alpha * dot(X[i], Y[col_indices[p]]) for each
-// entry p of row i ("Sparse GPU Kernels for Deep Learning", summary card,
-// "Summary" and "Interesting ideas" I3: the specialised form with no scaling
-// by mask values and the second operand transposed, so that X and Y are both
-// read by contiguous rows).  The general form I3 leaves out is an epilogue of
-// the same kernels (scaling by the mask's values, out = ... + beta * out) and,
-// for Y stored d x k, a second kernel that deals lanes to entries.
-//
-// Mapping.  One wavefront (= one workgroup) per mask row.  The wave is split
-// into 64/kG groups of kG lanes; a group computes one entry's dot product at a
-// time, each lane covering kNv vectors of kVec elements of the d-long rows
-// (interleaved so that the group's loads of one Y row are contiguous).  The X
-// row is loaded once into registers and reused for every entry of the row.
-//
-// Reduction.  The kG lane partials of an entry are summed with DPP moves inside
-// a 16-lane row (quad swaps, half-row mirror, row mirror), fused into
-// v_add_f32_dpp; no LDS round trip.  Entries are dealt to groups round-robin
-// in windows of 64: at step s group g takes entry s*(64/kG) + g, and lane
-// (g, s) keeps that entry's sum, so after a window every lane holds one result
-// and the wave writes 64 consecutive outputs with one store.
-//
-// Staging.  The window's 64 column indices are read with one coalesced load and
-// kept in LDS as Y-row offsets (bytes when k*d < 2^30).
-//
-// Summation order: each lane sums its elements in order with FMA, then the
-// DPP tree adds the kG lane partials; deterministic run to run.
+// CSR SDDMM for gfx950 ("Sparse GPU Kernels for Deep Learning", summary card,
+// "Summary" and "Interesting ideas" I3).  The body for Y stored k x d, and the
+// design notes for it, are in sddmm_rows.h; this file holds the kernel for Y
+// stored d x k (the general form I3 leaves out) and the variant selection.
 #include <algorithm>
 
 #include "sp_device.h"
 #include "sp_launch.h"
 #include "sp_types.h"
+#include "sddmm_rows.h"
+#include "sp_plan.h"
 
 namespace spk {
 
 namespace {
 
-struct SddmmParams {
-    int m, d, nnz, batch;
-    const int *row_indices;
-    const int *row_offsets;
-    const int *col_indices;
-    const float *mask_values;  // NULL: scale by alpha only
-    const void *x;             // element type of the kernel instance
-    const void *y;
-    int k;
-    float alpha, beta;
-    unsigned y_bytes;  // bytes of one Y operand (buffer path)
-    float *out;
-    long long stride_values, stride_x, stride_y, stride_out;
-};
+using namespace sddmm_detail;
 
-// out[q] = alpha * v_q * dot + beta * out[q] for the entry q a lane finished.
-// beta == 0 leaves out unread (it may hold anything, NaN included).
-__device__ __forceinline__ void store_entry(const SddmmParams &p, long long z, int q, float dot)
-{
-    float scale = p.alpha;
-    if (p.mask_values) scale *= p.mask_values[z * p.stride_values + q];
-    float *o = p.out + z * p.stride_out + q;
-    float r = scale * dot;
-    if (p.beta != 0.f) r = fmaf(p.beta, *o, r);
-    *o = r;
-}
-
-#ifndef SP_SDDMM_LOADS_PER_BATCH
-#define SP_SDDMM_LOADS_PER_BATCH 8
-#endif
-constexpr unsigned kOutOfRange = 0x80000000u;  // buffer offset that reads as zero
-
-// sum over i < kVec of x[i] * y[i], in order, added to acc with FMA.
-template <typename V, int kVec>
-__device__ __forceinline__ float dot_f32(const float *x, const typename V::T &y, float acc)
-{
-    float yf[kVec];
-    V::to_f32(y, yf);
-#pragma unroll
-    for (int i = 0; i < kVec; ++i) acc = fmaf(x[i], yf[i], acc);
-    return acc;
-}
-
-// kNv > 0 (Y < 2 GiB): the lane's kNv vectors of the X row live in registers
-// (widened to fp32); Y rows are gathered through a buffer resource, and window
-// slots past the row's end carry an out-of-range offset that reads as zeros,
-// so steps are issued in unconditional double-buffered batches of kU.
-// kNv == 0: any d and any Y size; X and Y are read with 64-bit addresses in a
-// loop over d, one step at a time.  E is the element type of X and Y (fp32,
-// fp16 or bf16); arithmetic is fp32 throughout.
 template <typename E, int kG, int kNv, int kVec>
 __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
 {
-    using V = GVec<E, kVec>;
-    using VecT = typename V::T;
-    constexpr unsigned kEb = Elem<E>::kBytes;
-    constexpr int kNg = kWave / kG;  // entries per step
-    constexpr int kU = kNv == 0 ? 1
-                                : (SP_SDDMM_LOADS_PER_BATCH / kNv > 0 ? SP_SDDMM_LOADS_PER_BATCH / kNv : 1);
-    constexpr int kXv = kNv == 0 ? 1 : kNv;
-    // The window's 64 entries, then padding for the prefetch of up to two
-    // batches past the last step.
-    constexpr int kSlots = kWave + 2 * kU * kNg;
-    __shared__ unsigned s_off[kSlots];
-
-    const long long w = xcd_work_index(p.batch, p.m);
-    if (w < 0) return;
-    const long long z = w / p.m;
-    const int slot = (int)(w - z * p.m);
-    const int lane = threadIdx.x;
-    const int g = lane / kG;
-    const int gl = lane - g * kG;
-    const int row = p.row_indices ? p.row_indices[slot] : slot;
-    const int p0 = p.row_offsets[row];
-    const int p1 = p.row_offsets[row + 1];
-    if (p0 >= p1) return;  // one row per wave: uniform, before any barrier
-
-    const E *__restrict__ xr_ptr =
-        static_cast<const E *>(p.x) + z * p.stride_x + (size_t)row * (size_t)p.d;
-    const E *__restrict__ yz = static_cast<const E *>(p.y) + z * p.stride_y;
-
-    if constexpr (kNv == 0) {
-        __shared__ int s_col[kWave];
-        for (int base = p0; base < p1; base += kWave) {
-            const int cnt = min(kWave, p1 - base);
-            s_col[lane] = lane < cnt ? p.col_indices[base + lane] : 0;
-            __syncthreads();
-            const int steps = (cnt + kNg - 1) / kNg;
-            float res = 0.f;
-            for (int s = 0; s < steps; ++s) {
-                const int j = s * kNg + g;
-                float acc = 0.f;
-                if (j < cnt) {
-                    const E *yr = yz + (size_t)s_col[j] * (size_t)p.d;
-                    for (int e = gl * kVec; e < p.d; e += kG * kVec) {
-                        float xf[kVec];
-                        V::to_f32(V::load(xr_ptr + e), xf);
-                        acc = dot_f32<V, kVec>(xf, V::load(yr + e), acc);
-                    }
-                }
-                const float sum = group_sum<kG>(acc);
-                if (gl == s) res = sum;
-            }
-            const int jo = gl * kNg + g;
-            if (jo < cnt) store_entry(p, z, base + jo, res);
-            __syncthreads();
-        }
-    } else {
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<E *>(yz), 0, (int)p.y_bytes, 0x00020000);
-        float xr[kXv][kVec];
-        unsigned lane_off[kXv];
-#pragma unroll
-        for (int v = 0; v < kNv; ++v) {
-            const int e = (v * kG + gl) * kVec;
-            V::to_f32(e < p.d ? V::load(xr_ptr + e) : V::zero(), xr[v]);
-            lane_off[v] = e < p.d ? (unsigned)e * kEb : kOutOfRange;
-        }
-        for (int t = kWave + lane; t < kSlots; t += kWave) s_off[t] = kOutOfRange;
-
-        auto load_batch = [&](int s0, VecT (&yv)[kU][kXv]) {
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                const unsigned off = s_off[(s0 + u) * kNg + g];
-#pragma unroll
-                for (int v = 0; v < kNv; ++v) yv[u][v] = V::buf_load(rsrc, off + lane_off[v]);
-            }
-        };
-        auto reduce_batch = [&](int s0, const VecT (&yv)[kU][kXv], float &res) {
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                float acc = 0.f;
-#pragma unroll
-                for (int v = 0; v < kNv; ++v) acc = dot_f32<V, kVec>(xr[v], yv[u][v], acc);
-                const float sum = group_sum<kG>(acc);
-                if (gl == s0 + u) res = sum;
-            }
-        };
-
-        for (int base = p0; base < p1; base += kWave) {
-            const int cnt = min(kWave, p1 - base);
-            s_off[lane] = lane < cnt
-                              ? (unsigned)p.col_indices[base + lane] * (unsigned)p.d * kEb
-                              : kOutOfRange;
-            __syncthreads();
-            const int steps = (cnt + kNg - 1) / kNg;
-            float res = 0.f;
-            // A window has at most kG steps, so its batches are unrolled into
-            // straight-line code (exact wait counts: no loop back edge).
-            constexpr int kBatches = (kG + kU - 1) / kU;
-            VecT ya[kU][kXv], yb[kU][kXv];
-            load_batch(0, ya);
-#pragma unroll
-            for (int bt = 0; bt < kBatches; bt += 2) {
-                if (bt * kU >= steps) break;
-                load_batch((bt + 1) * kU, yb);
-                keep_issued_above();
-                reduce_batch(bt * kU, ya, res);
-                if ((bt + 1) * kU >= steps) break;
-                load_batch((bt + 2) * kU, ya);
-                keep_issued_above();
-                reduce_batch((bt + 1) * kU, yb, res);
-            }
-            const int jo = gl * kNg + g;  // the entry whose sum this lane kept
-            if (jo < cnt) store_entry(p, z, base + jo, res);
-            __syncthreads();
-        }
-    }
+    sddmm_rows_body<E, kG, kNv, kVec>(p, rows_work(p, blockIdx.x));
 }
 
 // Y stored d x k (the operand not transposed): Yop(c, l) = Y[l][c].  One wave
@@ -271,7 +89,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *dst, long long co
 template <typename E, int kG, int kNv, int kVec>
 hipError_t launch_t(const SddmmParams &p, hipStream_t s)
 {
-    dim3 grid((unsigned)xcd_grid(p.batch, p.m));
+    dim3 grid((unsigned)rows_grid(p));
     hipLaunchKernelGGL((sddmm_kernel<E, kG, kNv, kVec>), grid, dim3(kWave), 0, s, p);
     return hipGetLastError();
 }
@@ -336,11 +154,13 @@ hipError_t launch_fill_zero(float *dst, long long count, hipStream_t stream)
 // beyond).  Vectors per lane kNv rounded up to 1/2/4/8; wider rows take the
 // kNv == 0 loop.  d == 0 with no mask values and beta == 0 zero-fills every
 // batch's outputs; otherwise the kernels run with empty dot products.
-hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream)
+hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
 {
+    plan->kind = SddmmPlan::kNothing;
+    plan->dtype = a.dtype;
     if (a.m == 0 || a.nnz == 0) return hipSuccess;
     if (xcd_grid(a.batch, a.m) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    SddmmParams p;
+    SddmmParams &p = plan->p;
     p.m = a.m;
     p.batch = a.batch;
     p.d = a.d;
@@ -364,18 +184,14 @@ hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream)
     // Buffer offsets into Y must stay below 2^31 (padding offsets lie beyond).
     const bool buf = (long long)a.k * (long long)a.d * eb <= (1LL << 31);
     p.y_bytes = buf ? (unsigned)((long long)a.k * a.d * eb) : 0u;
+    plan->buf = buf;
     if (a.y_layout == 1) {
-        switch (a.dtype) {
-        case Dtype::f16: return launch_cols<_Float16>(buf, p, stream);
-        case Dtype::bf16: return launch_cols<bf16>(buf, p, stream);
-        default: return launch_cols<float>(buf, p, stream);
-        }
+        plan->kind = SddmmPlan::kCols;
+        return hipSuccess;
     }
     if (a.d == 0 && a.mask_values == nullptr && a.beta == 0.f) {
-        const long long blocks = std::min<long long>((a.nnz + 255) / 256, 65536);
-        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks, (unsigned)a.batch),
-                           dim3(256), 0, stream, a.out, (long long)a.nnz, a.stride_out);
-        return hipGetLastError();
+        plan->kind = SddmmPlan::kFill;
+        return hipSuccess;
     }
     const bool vec = (a.d % vlen == 0) && aligned16(a.x) && aligned16(a.y) &&
                      (a.stride_x % vlen == 0) && (a.stride_y % vlen == 0);
@@ -387,11 +203,46 @@ hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream)
     const int need = (dv + g - 1) / g;
     int nv = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
     if (!buf) nv = 0;
-    switch (a.dtype) {
-    case Dtype::f16: return launch_typed<_Float16, 8>(vec, g, nv, p, stream);
-    case Dtype::bf16: return launch_typed<bf16, 8>(vec, g, nv, p, stream);
-    default: return launch_typed<float, 4>(vec, g, nv, p, stream);
+    plan->kind = SddmmPlan::kRows;
+    plan->vec = vec;
+    plan->g = g;
+    plan->nv = nv;
+    return hipSuccess;
+}
+
+hipError_t run_sddmm(const SddmmPlan &plan, hipStream_t stream)
+{
+    const SddmmParams &p = plan.p;
+    switch (plan.kind) {
+    case SddmmPlan::kNothing:
+        return hipSuccess;
+    case SddmmPlan::kFill: {
+        const long long blocks = std::min<long long>((p.nnz + 255) / 256, 65536);
+        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks, (unsigned)p.batch),
+                           dim3(256), 0, stream, p.out, (long long)p.nnz, p.stride_out);
+        return hipGetLastError();
     }
+    case SddmmPlan::kCols:
+        switch (plan.dtype) {
+        case Dtype::f16: return launch_cols<_Float16>(plan.buf, p, stream);
+        case Dtype::bf16: return launch_cols<bf16>(plan.buf, p, stream);
+        default: return launch_cols<float>(plan.buf, p, stream);
+        }
+    default:
+        break;
+    }
+    switch (plan.dtype) {
+    case Dtype::f16: return launch_typed<_Float16, 8>(plan.vec, plan.g, plan.nv, p, stream);
+    case Dtype::bf16: return launch_typed<bf16, 8>(plan.vec, plan.g, plan.nv, p, stream);
+    default: return launch_typed<float, 4>(plan.vec, plan.g, plan.nv, p, stream);
+    }
+}
+
+hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream)
+{
+    SddmmPlan plan;
+    const hipError_t e = plan_sddmm(a, &plan);
+    return e != hipSuccess ? e : run_sddmm(plan, stream);
 }
 
 }  // namespace spk

@@ -32,13 +32,17 @@ bool dtype_of(int code, spk::Dtype *out)
     }
 }
 
-sp_status_t sddmm_any(int m, int k, int d, int nnz, const int *row_indices,
-                      const int *row_offsets, const int *col_indices,
-                      const float *mask_values, spk::Dtype dtype, const void *x, const void *y,
-                      int y_layout, float alpha, float beta, float *out, int batch,
-                      long long stride_values, long long stride_x, long long stride_y,
-                      long long stride_out, sp_stream_t stream)
+// Checks an SDDMM's arguments and fills `a`; *work is false when there is
+// nothing to launch.
+sp_status_t sddmm_prepare(int m, int k, int d, int nnz, const int *row_indices,
+                          const int *row_offsets, const int *col_indices,
+                          const float *mask_values, spk::Dtype dtype, const void *x,
+                          const void *y, int y_layout, float alpha, float beta, float *out,
+                          int batch, long long stride_values, long long stride_x,
+                          long long stride_y, long long stride_out, spk::SddmmArgs *args,
+                          bool *work)
 {
+    *work = false;
     if (m < 0 || k < 0 || d < 0 || nnz < 0 || batch < 0 || stride_values < 0 ||
         stride_x < 0 || stride_y < 0 || stride_out < 0)
         return SP_ERROR_INVALID_VALUE;
@@ -48,7 +52,7 @@ sp_status_t sddmm_any(int m, int k, int d, int nnz, const int *row_indices,
         !need(x, (long long)m * d) || !need(y, (long long)k * d))
         return SP_ERROR_INVALID_VALUE;
     if (batch > 1 && stride_out < nnz) return SP_ERROR_INVALID_VALUE;
-    spk::SddmmArgs a;
+    spk::SddmmArgs &a = *args;
     a.m = m;
     a.k = k;
     a.d = d;
@@ -69,7 +73,62 @@ sp_status_t sddmm_any(int m, int k, int d, int nnz, const int *row_indices,
     a.stride_y = stride_y;
     a.stride_out = stride_out;
     a.dtype = dtype;
+    *work = true;
+    return SP_SUCCESS;
+}
+
+sp_status_t sddmm_any(int m, int k, int d, int nnz, const int *row_indices,
+                      const int *row_offsets, const int *col_indices,
+                      const float *mask_values, spk::Dtype dtype, const void *x, const void *y,
+                      int y_layout, float alpha, float beta, float *out, int batch,
+                      long long stride_values, long long stride_x, long long stride_y,
+                      long long stride_out, sp_stream_t stream)
+{
+    spk::SddmmArgs a;
+    bool work = false;
+    const sp_status_t st = sddmm_prepare(m, k, d, nnz, row_indices, row_offsets, col_indices,
+                                         mask_values, dtype, x, y, y_layout, alpha, beta, out,
+                                         batch, stride_values, stride_x, stride_y, stride_out,
+                                         &a, &work);
+    if (st != SP_SUCCESS || !work) return st;
     return from_hip(spk::launch_sddmm(a, as_stream(stream)));
+}
+
+// Checks an SpMM's arguments and fills `a`; *work is false when there is
+// nothing to launch.
+sp_status_t spmm_prepare(int m, int k, int n, int nnz, const int *row_indices,
+                         spk::Dtype dt, const void *values, const int *row_offsets,
+                         const int *col_indices, const void *b, float *c, int batch,
+                         long long stride_values, long long stride_b, long long stride_c,
+                         spk::SpmmArgs *args, bool *work)
+{
+    *work = false;
+    if (m < 0 || k < 0 || n < 0 || nnz < 0 || batch < 0 || stride_values < 0 ||
+        stride_b < 0 || stride_c < 0)
+        return SP_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0 || batch == 0) return SP_SUCCESS;
+    if (!need(row_offsets, m) || !need(col_indices, nnz) || !need(values, nnz) ||
+        !need(b, nnz > 0 ? (long long)k * n : 0) || c == nullptr)
+        return SP_ERROR_INVALID_VALUE;
+    if (batch > 1 && stride_c < (long long)m * n) return SP_ERROR_INVALID_VALUE;
+    spk::SpmmArgs &a = *args;
+    a.m = m;
+    a.k = k;
+    a.n = n;
+    a.nnz = nnz;
+    a.row_indices = row_indices;
+    a.row_offsets = row_offsets;
+    a.col_indices = col_indices;
+    a.values = values;
+    a.b = b;
+    a.c = c;
+    a.batch = batch;
+    a.stride_values = stride_values;
+    a.stride_b = stride_b;
+    a.stride_c = stride_c;
+    a.dtype = dt;
+    *work = true;
+    return SP_SUCCESS;
 }
 
 }  // namespace
@@ -145,31 +204,37 @@ sp_status_t sp_spmm_ex(int m, int k, int n, int nnz, const int *row_indices, int
 {
     spk::Dtype dt;
     if (!dtype_of(dtype, &dt)) return SP_ERROR_INVALID_VALUE;
-    if (m < 0 || k < 0 || n < 0 || nnz < 0 || batch < 0 || stride_values < 0 ||
-        stride_b < 0 || stride_c < 0)
-        return SP_ERROR_INVALID_VALUE;
-    if (m == 0 || n == 0 || batch == 0) return SP_SUCCESS;
-    if (!need(row_offsets, m) || !need(col_indices, nnz) || !need(values, nnz) ||
-        !need(b, nnz > 0 ? (long long)k * n : 0) || c == nullptr)
-        return SP_ERROR_INVALID_VALUE;
-    if (batch > 1 && stride_c < (long long)m * n) return SP_ERROR_INVALID_VALUE;
     spk::SpmmArgs a;
-    a.m = m;
-    a.k = k;
-    a.n = n;
-    a.nnz = nnz;
-    a.row_indices = row_indices;
-    a.row_offsets = row_offsets;
-    a.col_indices = col_indices;
-    a.values = values;
-    a.b = b;
-    a.c = c;
-    a.batch = batch;
-    a.stride_values = stride_values;
-    a.stride_b = stride_b;
-    a.stride_c = stride_c;
-    a.dtype = dt;
+    bool work = false;
+    const sp_status_t st = spmm_prepare(m, k, n, nnz, row_indices, dt, values, row_offsets,
+                                        col_indices, b, c, batch, stride_values, stride_b,
+                                        stride_c, &a, &work);
+    if (st != SP_SUCCESS || !work) return st;
     return from_hip(spk::launch_spmm(a, as_stream(stream)));
+}
+
+sp_status_t sp_spmm_sddmm(int m, int k, int n, int nnz, const int *row_indices,
+                          const float *values, const int *row_offsets, const int *col_indices,
+                          const float *b, float *c, int s_m, int s_k, int d, int s_nnz,
+                          const int *s_row_indices, const int *s_row_offsets,
+                          const int *s_col_indices, const float *x, const float *y,
+                          float alpha, float *out, sp_stream_t stream)
+{
+    spk::SpmmArgs a;
+    spk::SddmmArgs q;
+    bool work_a = false, work_q = false;
+    sp_status_t st = spmm_prepare(m, k, n, nnz, row_indices, spk::Dtype::f32, values,
+                                  row_offsets, col_indices, b, c, 1, 0, 0, 0, &a, &work_a);
+    if (st != SP_SUCCESS) return st;
+    st = sddmm_prepare(s_m, s_k, d, s_nnz, s_row_indices, s_row_offsets, s_col_indices, nullptr,
+                       spk::Dtype::f32, x, y, SP_Y_KD, alpha, 0.f, out, 1, 0, 0, 0, 0, &q,
+                       &work_q);
+    if (st != SP_SUCCESS) return st;
+    const hipStream_t s = as_stream(stream);
+    if (work_a && work_q) return from_hip(spk::launch_spmm_sddmm(a, q, s));
+    if (work_a) return from_hip(spk::launch_spmm(a, s));
+    if (work_q) return from_hip(spk::launch_sddmm(q, s));
+    return SP_SUCCESS;
 }
 
 sp_status_t sp_spmm_batched(int m, int k, int n, int nnz, const int *row_indices,

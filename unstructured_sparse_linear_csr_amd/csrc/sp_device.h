@@ -81,15 +81,21 @@ __host__ __device__ inline long long xcd_grid(long long outer, long long inner)
     const long long units = outer * inner;
     return xcd_remap(outer) ? (units + kXcds - 1) / kXcds * kXcds : units;
 }
+// The work index of workgroup `block` of a launch of xcd_grid(outer, inner)
+// workgroups, or -1 for a padding slot.
+__device__ __forceinline__ long long xcd_work_index_of(long long block, long long outer,
+                                                       long long inner)
+{
+    const long long units = outer * inner;
+    if (!xcd_remap(outer)) return block;
+    const long long per = (units + kXcds - 1) / kXcds;
+    const long long w = (block % kXcds) * per + block / kXcds;
+    return w < units ? w : -1;
+}
 // The work index of this workgroup, or -1 for a padding slot.
 __device__ __forceinline__ long long xcd_work_index(long long outer, long long inner)
 {
-    const long long units = outer * inner;
-    const long long i = blockIdx.x;
-    if (!xcd_remap(outer)) return i;
-    const long long per = (units + kXcds - 1) / kXcds;
-    const long long w = (i % kXcds) * per + i / kXcds;
-    return w < units ? w : -1;
+    return xcd_work_index_of(blockIdx.x, outer, inner);
 }
 
 // Bit mask of the lanes below `lane` (for ballot-based compaction).

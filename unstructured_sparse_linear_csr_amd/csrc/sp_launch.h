@@ -50,6 +50,7 @@ hipError_t launch_row_swizzle(int m, const int *row_offsets, int *row_indices,
                               hipStream_t stream);
 hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream);
 hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream);
+hipError_t launch_spmm_sddmm(const SpmmArgs &x, const SddmmArgs &y, hipStream_t stream);
 hipError_t launch_row_softmax(int m, const int *row_indices, const int *row_offsets,
                               const float *in, float *out, int batch, long long stride_in,
                               long long stride_out, hipStream_t stream);

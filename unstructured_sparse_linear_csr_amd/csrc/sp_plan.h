@@ -1,0 +1,35 @@
+// Variant selection, separated from the launch, for the operations whose
+// bodies can share a launch (SpMM on wide B, SDDMM with Y stored k x d).
+#pragma once
+
+#include "sp_launch.h"
+#include "sddmm_rows.h"
+#include "spmm_wide.h"
+
+namespace spk {
+
+struct SpmmPlan {
+    enum Kind { kWide, kNarrow, kLds } kind;
+    spmm_detail::SpmmParams p;
+    Dtype dtype;
+    bool vec, vec_csr, buf;
+    int lpr;     // wide: lanes per row
+    int e;       // narrow and LDS kernels: lanes per entry slot
+    int blocks;  // LDS kernel: workgroups
+};
+
+struct SddmmPlan {
+    enum Kind { kNothing, kFill, kCols, kRows } kind;
+    sddmm_detail::SddmmParams p;
+    Dtype dtype;
+    bool vec, buf;
+    int g, nv;  // rows kernel: lanes per entry, vectors per lane (0: generic loop)
+};
+
+// hipErrorInvalidConfiguration when the grid would exceed the launch limits.
+hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan);
+hipError_t run_spmm(const SpmmPlan &plan, hipStream_t stream);
+hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan);
+hipError_t run_sddmm(const SddmmPlan &plan, hipStream_t stream);
+
+}  // namespace spk
