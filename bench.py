@@ -449,15 +449,24 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
         sp.sp_spmm_batched(seq, seq, hd, nnz, ri, s_out, ro, cols, v, o, bh, nnz, seq * hd,
                            seq * hd)
 
+    fsfn = lambda: sp.sp_sddmm_softmax(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125, s_out,
+                                       bh, seq * hd, seq * hd, nnz)
+
+    def attention_fused():
+        fsfn()
+        sp.sp_spmm_batched(seq, seq, hd, nnz, ri, s_out, ro, cols, v, o, bh, nnz, seq * hd,
+                           seq * hd)
+
     for kind, fn in (("sddmm_batched", sfn), ("sddmm_general_dk_batched", tfn),
-                     ("row_softmax_batched", smfn), ("spmm_batched", pfn),
-                     ("attention_all_device", attention)):
+                     ("row_softmax_batched", smfn), ("sddmm_softmax_batched", fsfn),
+                     ("spmm_batched", pfn), ("attention_all_device", attention),
+                     ("attention_all_device_fused_scores", attention_fused)):
         us = graph_time_us(torch, fn, 20)
         flops = 2.0 * bh * nnz * hd
         if kind == "row_softmax_batched":
             flops = 0.0
             byts = bh * 8 * nnz + 8 * seq
-        elif kind == "attention_all_device":
+        elif kind.startswith("attention_all_device"):
             flops = 4.0 * bh * nnz * hd
             byts = bh * (sddmm_bytes(seq, seq, hd, nnz) + 8 * nnz
                          + spmm_bytes(seq, seq, hd, nnz))

@@ -336,6 +336,22 @@ sp_status_t sp_csr_row_softmax(int m, int nnz, const int *row_indices,
                                int batch, long long stride_in, long long stride_out,
                                sp_stream_t stream);
 
+/* Scores and their row softmax in one pass (sparse attention's first two
+ * steps, "Interesting ideas" I3 of the card): for each batch entry z and each
+ * row i with entries p,
+ *   out_z[p] = exp(s_p - mx) / sum over the row's entries q of exp(s_q - mx),
+ *   s_p = alpha * sum over l < d of X_z[i][l] * Y_z[col_indices[p]][l],
+ *   mx = the row's maximum of s,
+ * with X and Y of element type `dtype` (Y stored k x d), fp32 arithmetic and
+ * expf; rows without entries are left untouched.  Equal, up to rounding, to
+ * sp_sddmm_ex followed by sp_csr_row_softmax, without writing and re-reading
+ * the scores in between.  Arguments as sp_sddmm_ex. */
+sp_status_t sp_sddmm_softmax(int m, int k, int d, int nnz, const int *row_indices,
+                             const int *row_offsets, const int *col_indices, int dtype,
+                             const void *x, const void *y, float alpha, float *out, int batch,
+                             long long stride_x, long long stride_y, long long stride_out,
+                             sp_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 19, declared
+    assert len(declared) == 20, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -111,6 +111,15 @@ def test_mixed_precision_validation(lib):
         assert f(0, 4, 4, 0, NULL, dt, NULL, NULL, NULL, NULL, NULL, 1, 0, 0, 0, s) == OK
         assert f(4, 4, 4, 8, NULL, dt, NULL, FAKE, FAKE, FAKE, FAKE, 1, 0, 0, 0, s) == INVALID
         assert f(4, 4, 4, 8, NULL, dt, FAKE, FAKE, FAKE, NULL, FAKE, 1, 0, 0, 0, s) == INVALID
+    for g in (lib.sp_sddmm_ex, lib.sp_sddmm_softmax):
+        fl = ctypes.c_float(1.0)
+        assert g(4, 4, 4, 8, NULL, FAKE, FAKE, 5, FAKE, FAKE, fl, FAKE, 1, 0, 0, 0, s) == INVALID
+        for dt in (0, 1, 2):
+            assert g(0, 4, 4, 0, NULL, NULL, NULL, dt, NULL, NULL, fl, NULL, 1, 0, 0, 0, s) == OK
+            assert g(4, 4, 4, 8, NULL, FAKE, FAKE, dt, NULL, FAKE, fl, FAKE, 1, 0, 0, 0,
+                     s) == INVALID
+            assert g(4, 4, 4, 8, NULL, NULL, FAKE, dt, FAKE, FAKE, fl, FAKE, 1, 0, 0, 0,
+                     s) == INVALID
     g = lib.sp_sddmm_ex
     fl = ctypes.c_float(1.0)
     assert g(4, 4, 4, 8, NULL, FAKE, FAKE, 5, FAKE, FAKE, fl, FAKE, 1, 0, 0, 0, s) == INVALID

@@ -621,13 +621,14 @@ def test_graph_replays_match_eager(ffn):
 def _softmax_bound(ro, s, p_ref):
     """Per-element bound of the fp32 softmax: relative (|s - max| + 8) * 2^-23
     (rounding of s - max amplified by exp, expf itself, the row sum and the
-    division), in units of the exact result."""
+    division), in units of the exact result, plus an absolute 2^-126 (below
+    fp32's smallest normal a value has no relative precision)."""
     b = np.zeros_like(p_ref)
     for i in range(ro.shape[0] - 1):
         seg = slice(ro[i], ro[i + 1])
         if ro[i + 1] > ro[i]:
             x = s[seg].astype(np.float64) - float(s[seg].max())
-            b[seg] = p_ref[seg] * (np.abs(x) + 8.0) * 2.0 ** -23
+            b[seg] = p_ref[seg] * (np.abs(x) + 8.0) * 2.0 ** -23 + 2.0 ** -126
     return b
 
 

@@ -61,6 +61,8 @@ SIGNATURES = {
     "sp_spmm_sddmm": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                        _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_float, _vp,
                        _vp], _c_int),
+    "sp_sddmm_softmax": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
+                          _c_float, _vp, _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
     "sp_spmm_ex": ([_c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp,
                     _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
     "sp_sddmm_ex": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
@@ -300,6 +302,19 @@ def sp_sddmm_ex(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, alpha
         code, _ptr(x, dt, "x", True), _ptr(y, dt, "y", True), float(alpha),
         _ptr(out, _F32, "out", True), batch, stride_x, stride_y, stride_out, _stream(stream)),
         "sp_sddmm_ex")
+
+
+def sp_sddmm_softmax(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, alpha, out,
+                     batch=1, stride_x=0, stride_y=0, stride_out=0, stream=None):
+    """Row softmax of alpha * (X Y^T) at the mask, X and Y float32/float16/bfloat16."""
+    code = _dtype_of(x, y)
+    dt = [k_ for k_, v in _DTYPE_CODES.items() if v == code][0]
+    _check(lib().sp_sddmm_softmax(
+        m, k, d, nnz, _ptr(row_indices, _I32, "row_indices", True),
+        _ptr(row_offsets, _I32, "row_offsets"), _ptr(col_indices, _I32, "col_indices", True),
+        code, _ptr(x, dt, "x", True), _ptr(y, dt, "y", True), float(alpha),
+        _ptr(out, _F32, "out", True), batch, stride_x, stride_y, stride_out, _stream(stream)),
+        "sp_sddmm_softmax")
 
 
 def sp_csr_row_softmax(m, nnz, row_indices, row_offsets, inp, out, batch=1, stride_in=0,

@@ -67,7 +67,7 @@ hipError_t launch_fused_g(int g, int nv, const SpmmParams &a, const SddmmParams 
 bool fusable(const SpmmPlan &x, const SddmmPlan &y)
 {
     return x.kind == SpmmPlan::kWide && x.dtype == Dtype::f32 && x.vec && x.vec_csr && x.buf &&
-           y.kind == SddmmPlan::kRows && y.dtype == Dtype::f32 && y.vec && y.buf &&
+           y.kind == SddmmPlan::kRows && y.dtype == Dtype::f32 && y.vec && y.buf && !y.softmax &&
            (y.nv == 1 || y.nv == 2 || y.nv == 4) &&
            spmm_detail::wide_grid(x.p) + sddmm_detail::rows_grid(y.p) <= 0x7fffffffLL;
 }

@@ -16,10 +16,10 @@ namespace {
 
 using namespace sddmm_detail;
 
-template <typename E, int kG, int kNv, int kVec>
+template <typename E, int kG, int kNv, int kVec, bool kSoftmax>
 __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
 {
-    sddmm_rows_body<E, kG, kNv, kVec>(p, rows_work(p, blockIdx.x));
+    sddmm_rows_body<E, kG, kNv, kVec, kSoftmax>(p, rows_work(p, blockIdx.x));
 }
 
 // Y stored d x k (the operand not transposed): Yop(c, l) = Y[l][c].  One wave
@@ -86,41 +86,45 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *dst, long long co
         dz[i] = 0.f;
 }
 
-template <typename E, int kG, int kNv, int kVec>
+template <typename E, int kG, int kNv, int kVec, bool kSm>
 hipError_t launch_t(const SddmmParams &p, hipStream_t s)
 {
     dim3 grid((unsigned)rows_grid(p));
-    hipLaunchKernelGGL((sddmm_kernel<E, kG, kNv, kVec>), grid, dim3(kWave), 0, s, p);
+    hipLaunchKernelGGL((sddmm_kernel<E, kG, kNv, kVec, kSm>), grid, dim3(kWave), 0, s, p);
     return hipGetLastError();
 }
 
-template <typename E, int kG, int kVec>
+template <typename E, int kG, int kVec, bool kSm>
 hipError_t launch_nv(int nv, const SddmmParams &p, hipStream_t s)
 {
     switch (nv) {
-    case 1: return launch_t<E, kG, 1, kVec>(p, s);
-    case 2: return launch_t<E, kG, 2, kVec>(p, s);
-    case 4: return launch_t<E, kG, 4, kVec>(p, s);
-    case 8: return launch_t<E, kG, 8, kVec>(p, s);
-    default: return launch_t<E, kG, 0, kVec>(p, s);
+    case 1: return launch_t<E, kG, 1, kVec, kSm>(p, s);
+    case 2: return launch_t<E, kG, 2, kVec, kSm>(p, s);
+    case 4: return launch_t<E, kG, 4, kVec, kSm>(p, s);
+    case 8: return launch_t<E, kG, 8, kVec, kSm>(p, s);
+    default: return launch_t<E, kG, 0, kVec, kSm>(p, s);
     }
 }
 
-template <typename E, int kVec>
+template <typename E, int kVec, bool kSm>
 hipError_t launch_g(int g, int nv, const SddmmParams &p, hipStream_t s)
 {
     switch (g) {
-    case 4: return launch_nv<E, 4, kVec>(nv, p, s);
-    case 8: return launch_nv<E, 8, kVec>(nv, p, s);
-    default: return launch_nv<E, 16, kVec>(nv, p, s);
+    case 4: return launch_nv<E, 4, kVec, kSm>(nv, p, s);
+    case 8: return launch_nv<E, 8, kVec, kSm>(nv, p, s);
+    default: return launch_nv<E, 16, kVec, kSm>(nv, p, s);
     }
 }
 
-// Element type E: 16-byte vectors of kVec16 elements, or single elements.
+// Element type E: 16-byte vectors of kVec16 elements, or single elements;
+// scores written as they are, or row-softmaxed.
 template <typename E, int kVec16>
-hipError_t launch_typed(bool vec, int g, int nv, const SddmmParams &p, hipStream_t s)
+hipError_t launch_typed(bool vec, bool softmax, int g, int nv, const SddmmParams &p,
+                        hipStream_t s)
 {
-    return vec ? launch_g<E, kVec16>(g, nv, p, s) : launch_g<E, 1>(g, nv, p, s);
+    if (softmax)
+        return vec ? launch_g<E, kVec16, true>(g, nv, p, s) : launch_g<E, 1, true>(g, nv, p, s);
+    return vec ? launch_g<E, kVec16, false>(g, nv, p, s) : launch_g<E, 1, false>(g, nv, p, s);
 }
 
 template <typename E>
@@ -158,6 +162,7 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
 {
     plan->kind = SddmmPlan::kNothing;
     plan->dtype = a.dtype;
+    plan->softmax = false;
     if (a.m == 0 || a.nnz == 0) return hipSuccess;
     if (xcd_grid(a.batch, a.m) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     SddmmParams &p = plan->p;
@@ -189,7 +194,8 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
         plan->kind = SddmmPlan::kCols;
         return hipSuccess;
     }
-    if (a.d == 0 && a.mask_values == nullptr && a.beta == 0.f) {
+    plan->softmax = a.softmax;
+    if (a.d == 0 && a.mask_values == nullptr && a.beta == 0.f && !a.softmax) {
         plan->kind = SddmmPlan::kFill;
         return hipSuccess;
     }
@@ -231,10 +237,11 @@ hipError_t run_sddmm(const SddmmPlan &plan, hipStream_t stream)
     default:
         break;
     }
+    const bool sm = plan.softmax;
     switch (plan.dtype) {
-    case Dtype::f16: return launch_typed<_Float16, 8>(plan.vec, plan.g, plan.nv, p, stream);
-    case Dtype::bf16: return launch_typed<bf16, 8>(plan.vec, plan.g, plan.nv, p, stream);
-    default: return launch_typed<float, 4>(plan.vec, plan.g, plan.nv, p, stream);
+    case Dtype::f16: return launch_typed<_Float16, 8>(plan.vec, sm, plan.g, plan.nv, p, stream);
+    case Dtype::bf16: return launch_typed<bf16, 8>(plan.vec, sm, plan.g, plan.nv, p, stream);
+    default: return launch_typed<float, 4>(plan.vec, sm, plan.g, plan.nv, p, stream);
     }
 }
 

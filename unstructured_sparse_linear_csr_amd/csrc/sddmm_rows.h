@@ -85,7 +85,15 @@ __device__ __forceinline__ float dot_f32(const float *x, const typename V::T &y,
 // kNv == 0: any d and any Y size; X and Y are read with 64-bit addresses in a
 // loop over d, one step at a time.  E is the element type of X and Y (fp32,
 // fp16 or bf16); arithmetic is fp32 throughout.
-template <typename E, int kG, int kNv, int kVec>
+//
+// kSoftmax: the row softmax of the scaled scores is applied before they are
+// written (out = softmax over the row's entries of alpha * X Y^T), the step
+// between the scores and their weighted sum in sparse attention.  The wave
+// holds its row's scores (one per lane per window of 64) in registers for up
+// to kHeldWindows windows and parks later windows' scores in `out`; after the
+// last window it reduces the row maximum and the sum of exp(s - max) across
+// the wave (butterflies, fixed order) and writes exp(s - max) / sum.
+template <typename E, int kG, int kNv, int kVec, bool kSoftmax = false>
 __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long w)
 {
     using V = GVec<E, kVec>;
@@ -99,6 +107,11 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
     // batches past the last step.
     constexpr int kSlots = kWave + 2 * kU * kNg;
     __shared__ unsigned s_off[kSlots];
+
+    constexpr int kHeldWindows = 4;
+    float held[kHeldWindows];
+    float row_max = -INFINITY;
+    int window = 0;
 
     if (w < 0) return;
     const long long z = w / p.m;
@@ -114,6 +127,21 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
     const E *__restrict__ xr_ptr =
         static_cast<const E *>(p.x) + z * p.stride_x + (size_t)row * (size_t)p.d;
     const E *__restrict__ yz = static_cast<const E *>(p.y) + z * p.stride_y;
+    float *__restrict__ oz = p.out + z * p.stride_out;
+
+    // The score of entry q, kept by this lane, in window `window` of the row.
+    auto emit = [&](int q, float res) {
+        if constexpr (kSoftmax) {
+            const float s = p.alpha * res;
+            row_max = fmaxf(row_max, s);
+#pragma unroll
+            for (int t = 0; t < kHeldWindows; ++t)
+                if (t == window) held[t] = s;
+            if (window >= kHeldWindows) oz[q] = s;
+        } else {
+            store_entry(p, z, q, res);
+        }
+    };
 
     if constexpr (kNv == 0) {
         __shared__ int s_col[kWave];
@@ -138,8 +166,9 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
                 if (gl == s) res = sum;
             }
             const int jo = gl * kNg + g;
-            if (jo < cnt) store_entry(p, z, base + jo, res);
+            if (jo < cnt) emit(base + jo, res);
             __syncthreads();
+            ++window;
         }
     } else {
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -198,9 +227,34 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
                 reduce_batch((bt + 1) * kU, yb, res);
             }
             const int jo = gl * kNg + g;  // the entry whose sum this lane kept
-            if (jo < cnt) store_entry(p, z, base + jo, res);
+            if (jo < cnt) emit(base + jo, res);
             __syncthreads();
+            ++window;
         }
+    }
+    if constexpr (kSoftmax) {
+        // window t of the row holds entries p0 + 64 t ...; this lane's is jo
+        const int jo = gl * kNg + g;
+        auto live = [&](int t) { return jo < min(kWave, p1 - p0 - t * kWave); };
+        const float mx = wave_max(row_max);
+        float sum = 0.f;
+#pragma unroll
+        for (int t = 0; t < kHeldWindows; ++t) {
+            const float e = (t < window && live(t)) ? expf(held[t] - mx) : 0.f;
+            held[t] = e;
+            sum += e;
+        }
+        for (int t = kHeldWindows; t < window; ++t)
+            if (live(t)) sum += expf(oz[p0 + t * kWave + jo] - mx);
+        const float inv = 1.f / wave_sum(sum);
+#pragma unroll
+        for (int t = 0; t < kHeldWindows; ++t)
+            if (t < window && live(t)) oz[p0 + t * kWave + jo] = held[t] * inv;
+        for (int t = kHeldWindows; t < window; ++t)
+            if (live(t)) {
+                const int q = p0 + t * kWave + jo;
+                oz[q] = expf(oz[q] - mx) * inv;
+            }
     }
 }
 

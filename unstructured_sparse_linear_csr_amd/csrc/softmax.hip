@@ -22,20 +22,6 @@ namespace {
 constexpr int kHeldPerLane = 4;
 constexpr int kHeld = kHeldPerLane * kWave;
 
-__device__ __forceinline__ float wave_max(float v)
-{
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v)
-{
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
 struct SoftmaxParams {
     int m, batch;
     const int *row_indices;

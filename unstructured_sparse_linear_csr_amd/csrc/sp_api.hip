@@ -268,6 +268,24 @@ sp_status_t sp_sddmm_general(int m, int k, int d, int nnz, const int *row_indice
                      stride_x, stride_y, stride_out, stream);
 }
 
+sp_status_t sp_sddmm_softmax(int m, int k, int d, int nnz, const int *row_indices,
+                             const int *row_offsets, const int *col_indices, int dtype,
+                             const void *x, const void *y, float alpha, float *out, int batch,
+                             long long stride_x, long long stride_y, long long stride_out,
+                             sp_stream_t stream)
+{
+    spk::Dtype dt;
+    if (!dtype_of(dtype, &dt)) return SP_ERROR_INVALID_VALUE;
+    spk::SddmmArgs a;
+    bool work = false;
+    const sp_status_t st = sddmm_prepare(m, k, d, nnz, row_indices, row_offsets, col_indices,
+                                         nullptr, dt, x, y, SP_Y_KD, alpha, 0.f, out, batch, 0,
+                                         stride_x, stride_y, stride_out, &a, &work);
+    if (st != SP_SUCCESS || !work) return st;
+    a.softmax = true;
+    return from_hip(spk::launch_sddmm(a, as_stream(stream)));
+}
+
 sp_status_t sp_sddmm_ex(int m, int k, int d, int nnz, const int *row_indices,
                         const int *row_offsets, const int *col_indices, int dtype,
                         const void *x, const void *y, float alpha, float *out, int batch,

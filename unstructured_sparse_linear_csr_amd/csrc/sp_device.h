@@ -53,6 +53,22 @@ __device__ __forceinline__ void keep_issued_above()
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Wave-wide maximum and sum of a float, the same value in every lane (a
+// butterfly over the 64 lanes: a fixed order, so results are deterministic).
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
 // Wave-wide inclusive prefix sum of an int (Hillis-Steele over 64 lanes).
 __device__ __forceinline__ int wave_inclusive_sum(int v, int lane)
 {

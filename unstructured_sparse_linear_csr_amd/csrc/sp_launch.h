@@ -35,6 +35,7 @@ struct SddmmArgs {
     int batch;
     long long stride_values, stride_x, stride_y, stride_out;  // elements
     Dtype dtype = Dtype::f32;
+    bool softmax = false;  // row softmax of alpha * scores (k x d layout, no v, beta 0)
 };
 
 hipError_t launch_offsets_from_lengths(int m, const int *lengths,

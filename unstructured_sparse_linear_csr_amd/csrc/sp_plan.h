@@ -23,7 +23,8 @@ struct SddmmPlan {
     sddmm_detail::SddmmParams p;
     Dtype dtype;
     bool vec, buf;
-    int g, nv;  // rows kernel: lanes per entry, vectors per lane (0: generic loop)
+    bool softmax;  // rows kernel: row softmax of the scores before they are written
+    int g, nv;     // rows kernel: lanes per entry, vectors per lane (0: generic loop)
 };
 
 // hipErrorInvalidConfiguration when the grid would exceed the launch limits.
