@@ -341,11 +341,15 @@ def lowp_records(torch, sp, inputs, dev, flush) -> list:
                                      seq * hd, seq * hd, nnz)
         pfn = lambda: sp.sp_spmm_ex(seq, seq, hd, nnz, ri, p16, ro, cols, vv, o, bh, nnz,
                                     seq * hd, seq * hd)
-        for kind, fn in (("sddmm_batched_" + tag, sfn), ("spmm_batched_" + tag, pfn)):
+        afn = lambda: sp.sp_sparse_attention(seq, seq, hd, nnz, ri, ro, cols, q, kk, vv, 0.125, o,
+                                             bh, seq * hd, seq * hd, seq * hd, seq * hd)
+        for kind, fn in (("sddmm_batched_" + tag, sfn), ("spmm_batched_" + tag, pfn),
+                         ("attention_one_pass_" + tag, afn)):
             us = graph_time_us(torch, fn, 20)
+            flops = (4.0 if kind.startswith("attention") else 2.0) * bh * nnz * hd
             recs.append({"record": kind, "workload": w["name"], "batch": bh, "seq": seq,
                          "head_dim": hd, "nnz_per_head": nnz, "us": us,
-                         "gflops": 2.0 * bh * nnz * hd / (us * 1e-6) / 1e9,
+                         "gflops": flops / (us * 1e-6) / 1e9,
                          "cold_us": cold_time_us(torch, fn, flush)})
     return recs
 
@@ -457,16 +461,19 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
         sp.sp_spmm_batched(seq, seq, hd, nnz, ri, s_out, ro, cols, v, o, bh, nnz, seq * hd,
                            seq * hd)
 
+    vfn = lambda: sp.sp_sparse_attention(seq, seq, hd, nnz, ri, ro, cols, q, kk, v, 0.125, o,
+                                         bh, seq * hd, seq * hd, seq * hd, seq * hd)
     for kind, fn in (("sddmm_batched", sfn), ("sddmm_general_dk_batched", tfn),
                      ("row_softmax_batched", smfn), ("sddmm_softmax_batched", fsfn),
                      ("spmm_batched", pfn), ("attention_all_device", attention),
-                     ("attention_all_device_fused_scores", attention_fused)):
+                     ("attention_all_device_fused_scores", attention_fused),
+                     ("attention_one_pass", vfn)):
         us = graph_time_us(torch, fn, 20)
         flops = 2.0 * bh * nnz * hd
         if kind == "row_softmax_batched":
             flops = 0.0
             byts = bh * 8 * nnz + 8 * seq
-        elif kind.startswith("attention_all_device"):
+        elif kind.startswith("attention_"):
             flops = 4.0 * bh * nnz * hd
             byts = bh * (sddmm_bytes(seq, seq, hd, nnz) + 8 * nnz
                          + spmm_bytes(seq, seq, hd, nnz))

@@ -352,6 +352,31 @@ sp_status_t sp_sddmm_softmax(int m, int k, int d, int nnz, const int *row_indice
                              long long stride_x, long long stride_y, long long stride_out,
                              sp_stream_t stream);
 
+/* Sparse attention in one pass ("Interesting ideas" I3 of the card: the
+ * SDDMM -> row softmax -> SpMM composition), without writing the scores or
+ * the probabilities: for each batch entry z and each query row i with mask
+ * entries p (columns j_p),
+ *   out_z[i][:] = sum over p of P_p * V_z[j_p][:],
+ *   P = the row softmax of s_p = alpha * sum over l < d of Q_z[i][l] * K_z[j_p][l]
+ * (fp32 arithmetic, expf; the softmax in its running-maximum form, so rows of
+ * any length take one pass).  A row without entries gives a zero row.
+ *   m, k         query rows and key rows; the mask is m x k;  nnz = row_offsets[m]
+ *   d            the head dimension of Q, K and V
+ *   dtype        element type of Q, K and V (SP_DTYPE_*); out is fp32
+ *   q            [m x d],  kmat, v  [k x d] per batch entry;  out  [m x d] fp32
+ *   stride_*     elements between batch entries; stride_out >= m*d when batch > 1
+ * Supported shapes: d = 32, 64, 128 or 256 for fp32 and 64, 128, 256 or 512
+ * for 16-bit types; 16-byte aligned operands with strides that keep them so;
+ * K and V under 2 GiB per batch entry.  Anything else returns
+ * SP_ERROR_NOT_SUPPORTED (the three separate entry points handle it).
+ * Deterministic run to run; equal up to rounding to sp_sddmm_softmax (or
+ * sp_sddmm + sp_csr_row_softmax) followed by sp_spmm. */
+sp_status_t sp_sparse_attention(int m, int k, int d, int nnz, const int *row_indices,
+                                const int *row_offsets, const int *col_indices, int dtype,
+                                const void *q, const void *kmat, const void *v, float alpha,
+                                float *out, int batch, long long stride_q, long long stride_k,
+                                long long stride_v, long long stride_out, sp_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 20, declared
+    assert len(declared) == 21, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -98,6 +98,32 @@ def test_spmm_sddmm_validation(lib):
     # both halves empty: nothing to do
     assert f(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, 0, 4, 4, 0, NULL, NULL, NULL,
              NULL, NULL, fl, NULL, s) == OK
+
+
+def test_sparse_attention_validation(lib):
+    f = lib.sp_sparse_attention
+    s = NULL
+    fl = ctypes.c_float(0.125)
+
+    def call(m=4, k=4, d=64, nnz=8, dtype=0, ro=FAKE, ci=FAKE, q=FAKE, kk=FAKE, v=FAKE,
+             out=FAKE, batch=1, so=0):
+        return f(m, k, d, nnz, NULL, ro, ci, dtype, q, kk, v, fl, out, batch, 0, 0, 0, so, s)
+
+    assert call(dtype=3) == INVALID
+    assert call(m=-1) == INVALID
+    assert call(d=-1) == INVALID
+    assert call(ro=NULL) == INVALID
+    assert call(ci=NULL) == INVALID
+    assert call(q=NULL) == INVALID
+    assert call(kk=NULL) == INVALID
+    assert call(v=NULL) == INVALID
+    assert call(out=NULL) == INVALID
+    assert call(batch=2, so=255) == INVALID
+    assert call(m=0, ro=NULL, ci=NULL, q=NULL, kk=NULL, v=NULL, out=NULL) == OK
+    assert call(batch=0) == OK
+    # unsupported head dimension: reported before any launch
+    assert call(d=48) == binding.SP_ERROR_NOT_SUPPORTED
+    assert call(d=32, dtype=1) == binding.SP_ERROR_NOT_SUPPORTED
 
 
 def test_mixed_precision_validation(lib):

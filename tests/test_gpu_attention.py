@@ -187,3 +187,120 @@ def test_all_device_attention_fused_scores():
     pv, _ = oracle.spmm(seq, seq, hd, ro, ci, p_ref, np.abs(w["v"][z]))
     err = np.abs(o_gpu.astype(np.float64) - o_ref)
     assert np.all(err <= rel[:, None] * pv * 1.01 + 2.0 ** -126)
+
+
+# ---------------------------------------------------------------- one-pass attention
+
+def check_attention(o_gpu, m, k, ro, ci, q, kk, v, alpha, what):
+    """O against the oracle's double pipeline: P's relative error (scores,
+    fp32 softmax, the running-maximum rescalings, a few ulps per window of 64)
+    times sum_j P_j |V_j|, plus the weighted sum's own 1e-5."""
+    s, s_abs = oracle.sddmm(m, k, q.shape[1], ro, ci, q, kk)
+    s, e_s = alpha * s, abs(alpha) * 1e-5 * s_abs
+    p_ref = oracle.softmax_rows(ro, s.astype(np.float32))
+    lengths = np.diff(ro)
+    rows = np.repeat(np.arange(m), lengths)
+    e_row = np.zeros(m)
+    np.maximum.at(e_row, rows, e_s)
+    smax = np.full(m, -np.inf)
+    np.maximum.at(smax, rows, s)
+    x_row = np.zeros(m)
+    np.maximum.at(x_row, rows, np.abs(s - smax[rows]))
+    a_row = np.zeros(m)
+    np.maximum.at(a_row, rows, np.abs(s))
+    windows = (lengths + 63) // 64
+    rel = (2.0 * e_row + 2.0 * a_row * 2.0 ** -24 + (x_row + 8.0) * 2.0 ** -23
+           + 8.0 * windows * 2.0 ** -23 + 1e-5)
+    o_ref, _ = oracle.spmm(m, k, q.shape[1], ro, ci, p_ref, v)
+    pv, _ = oracle.spmm(m, k, q.shape[1], ro, ci, p_ref, np.abs(v))
+    err = np.abs(o_gpu.astype(np.float64) - o_ref)
+    bound = rel[:, None] * pv * 1.01 + 2.0 ** -126
+    assert np.all(np.isfinite(o_gpu)), what
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} out of bound; worst "
+                           f"{np.max(err / np.maximum(bound, 1e-300)):.3g}")
+    assert np.all(o_gpu[lengths == 0] == 0.0), f"{what}: empty rows not zero"
+
+
+def test_sparse_attention_heads():
+    w = inputs.sparse_attention()
+    ro, ci, _ = oracle.csr_from_dense(w["mask"])
+    seq, hd = w["seq"], w["head_dim"]
+    a = DevCsr(seq, seq, ro, ci)
+    heads = [3, 30]
+    q = dev(np.stack([w["q"][z] for z in heads]))
+    kk = dev(np.stack([w["k"][z] for z in heads]))
+    v = dev(np.stack([w["v"][z] for z in heads]))
+    out = torch.full((len(heads), seq, hd), float("nan"), device="cuda")
+    note("sparse_attention 2 heads batched")
+    sp.sp_sparse_attention(seq, seq, hd, a.nnz, swizzle(a), a.d_ro, a.d_ci, q, kk, v, 0.125,
+                           out, len(heads), seq * hd, seq * hd, seq * hd, seq * hd)
+    got = host(out)
+    for i, z in enumerate(heads):
+        check_attention(got[i], seq, seq, ro, ci, w["q"][z], w["k"][z], w["v"][z], 0.125,
+                        f"attention head {z}")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+def test_sparse_attention_dims_and_lengths(d):
+    """Every head dimension; rows of 1 to 700 entries (several windows, the
+    running maximum rising from window to window), empty rows; the result does
+    not depend on the row order."""
+    rng = np.random.default_rng(820 + d)
+    m, k = 240, 900
+    lengths = rng.integers(0, 700, m).astype(np.int32)
+    lengths[::9] = 0
+    lengths[1::9] = 1
+    rl = inputs.random_row_lists(821 + d, m, k, lengths)
+    ro = oracle.csr_offsets_from_lengths(lengths)
+    a = DevCsr(m, k, ro, rl.cols)
+    q = inputs.random_dense(822 + d, m, d)
+    kk = inputs.random_dense(823 + d, k, d)
+    v = inputs.random_dense(824 + d, k, d)
+    alpha = float(np.float32(1.0 / np.sqrt(d)))
+    o1 = torch.full((m, d), float("nan"), device="cuda")
+    o2 = torch.full((m, d), float("nan"), device="cuda")
+    note(f"sparse_attention d={d}")
+    sp.sp_sparse_attention(m, k, d, a.nnz, swizzle(a), a.d_ro, a.d_ci, dev(q), dev(kk), dev(v),
+                           alpha, o1)
+    sp.sp_sparse_attention(m, k, d, a.nnz, None, a.d_ro, a.d_ci, dev(q), dev(kk), dev(v),
+                           alpha, o2)
+    g1 = host(o1)
+    assert np.array_equal(g1.view(np.int32), host(o2).view(np.int32))
+    check_attention(g1, m, k, ro, rl.cols, q, kk, v, alpha, f"d={d}")
+
+
+@pytest.mark.parametrize("kind,d", [("f16", 64), ("f16", 128), ("bf16", 64), ("bf16", 512)])
+def test_sparse_attention_16bit(kind, d):
+    tdt, code = {"f16": (torch.float16, oracle.F16), "bf16": (torch.bfloat16, oracle.BF16)}[kind]
+    m, k = 300, 500
+    lengths = np.random.default_rng(830 + d).integers(0, 300, m).astype(np.int32)
+    rl = inputs.random_row_lists(831 + d, m, k, lengths)
+    ro = oracle.csr_offsets_from_lengths(lengths)
+    a = DevCsr(m, k, ro, rl.cols)
+
+    def to16(a32):
+        t = torch.from_numpy(a32).to(tdt)
+        vals = oracle.decode16(code, t.view(torch.int16).numpy().view(np.uint16))
+        return t.cuda(), vals.astype(np.float32)
+
+    q16, q = to16(inputs.random_dense(832 + d, m, d))
+    k16, kk = to16(inputs.random_dense(833 + d, k, d))
+    v16, v = to16(inputs.random_dense(834 + d, k, d))
+    out = torch.full((m, d), float("nan"), device="cuda")
+    note(f"sparse_attention {kind} d={d}")
+    sp.sp_sparse_attention(m, k, d, a.nnz, swizzle(a), a.d_ro, a.d_ci, q16, k16, v16, 0.0625,
+                           out)
+    check_attention(host(out), m, k, ro, rl.cols, q, kk, v, 0.0625, f"{kind} d={d}")
+
+
+def test_sparse_attention_unsupported_shape():
+    w = inputs.tiny()
+    ro, ci, _ = oracle.csr_from_dense(w["mask"])
+    a = DevCsr(256, 256, ro, ci)
+    x = dev(inputs.random_dense(840, 256, 48))
+    out = torch.empty(256, 48, device="cuda")
+    note("sparse_attention d=48 rejected")
+    with pytest.raises(sp.SpError) as err:
+        sp.sp_sparse_attention(256, 256, 48, a.nnz, None, a.d_ro, a.d_ci, x, x, x, 1.0, out)
+    assert err.value.status == sp.SP_ERROR_NOT_SUPPORTED

@@ -63,6 +63,9 @@ SIGNATURES = {
                        _vp], _c_int),
     "sp_sddmm_softmax": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
                           _c_float, _vp, _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
+    "sp_sparse_attention": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
+                             _vp, _c_float, _vp, _c_int, _c_ll, _c_ll, _c_ll, _c_ll, _vp],
+                            _c_int),
     "sp_spmm_ex": ([_c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp,
                     _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
     "sp_sddmm_ex": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
@@ -315,6 +318,21 @@ def sp_sddmm_softmax(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, 
         code, _ptr(x, dt, "x", True), _ptr(y, dt, "y", True), float(alpha),
         _ptr(out, _F32, "out", True), batch, stride_x, stride_y, stride_out, _stream(stream)),
         "sp_sddmm_softmax")
+
+
+def sp_sparse_attention(m, k, d, nnz, row_indices, row_offsets, col_indices, q, kmat, v,
+                        alpha, out, batch=1, stride_q=0, stride_k=0, stride_v=0, stride_out=0,
+                        stream=None):
+    """softmax(alpha * Q K^T at the mask) V in one pass; Q, K, V one of
+    float32/float16/bfloat16, out float32."""
+    code = _dtype_of(q, kmat, v)
+    dt = [k_ for k_, v_ in _DTYPE_CODES.items() if v_ == code][0]
+    _check(lib().sp_sparse_attention(
+        m, k, d, nnz, _ptr(row_indices, _I32, "row_indices", True),
+        _ptr(row_offsets, _I32, "row_offsets"), _ptr(col_indices, _I32, "col_indices", True),
+        code, _ptr(q, dt, "q", True), _ptr(kmat, dt, "kmat", True), _ptr(v, dt, "v", True),
+        float(alpha), _ptr(out, _F32, "out", True), batch, stride_q, stride_k, stride_v,
+        stride_out, _stream(stream)), "sp_sparse_attention")
 
 
 def sp_csr_row_softmax(m, nnz, row_indices, row_offsets, inp, out, batch=1, stride_in=0,

@@ -286,6 +286,44 @@ sp_status_t sp_sddmm_softmax(int m, int k, int d, int nnz, const int *row_indice
     return from_hip(spk::launch_sddmm(a, as_stream(stream)));
 }
 
+sp_status_t sp_sparse_attention(int m, int k, int d, int nnz, const int *row_indices,
+                                const int *row_offsets, const int *col_indices, int dtype,
+                                const void *q, const void *kmat, const void *v, float alpha,
+                                float *out, int batch, long long stride_q, long long stride_k,
+                                long long stride_v, long long stride_out, sp_stream_t stream)
+{
+    spk::Dtype dt;
+    if (!dtype_of(dtype, &dt)) return SP_ERROR_INVALID_VALUE;
+    if (m < 0 || k < 0 || d < 0 || nnz < 0 || batch < 0 || stride_q < 0 || stride_k < 0 ||
+        stride_v < 0 || stride_out < 0)
+        return SP_ERROR_INVALID_VALUE;
+    if (m == 0 || batch == 0) return SP_SUCCESS;
+    if (!need(row_offsets, m) || !need(col_indices, nnz) || out == nullptr ||
+        !need(q, (long long)m * d) || !need(kmat, nnz > 0 ? (long long)k * d : 0) ||
+        !need(v, nnz > 0 ? (long long)k * d : 0))
+        return SP_ERROR_INVALID_VALUE;
+    if (batch > 1 && stride_out < (long long)m * d) return SP_ERROR_INVALID_VALUE;
+    spk::AttnArgs a;
+    a.m = m;
+    a.k_rows = k;
+    a.d = d;
+    a.batch = batch;
+    a.row_indices = row_indices;
+    a.row_offsets = row_offsets;
+    a.col_indices = col_indices;
+    a.q = q;
+    a.k = kmat;
+    a.v = v;
+    a.alpha = alpha;
+    a.out = out;
+    a.stride_q = stride_q;
+    a.stride_k = stride_k;
+    a.stride_v = stride_v;
+    a.stride_out = stride_out;
+    a.dtype = dt;
+    return from_hip(spk::launch_attention(a, as_stream(stream)));
+}
+
 sp_status_t sp_sddmm_ex(int m, int k, int d, int nnz, const int *row_indices,
                         const int *row_offsets, const int *col_indices, int dtype,
                         const void *x, const void *y, float alpha, float *out, int batch,

@@ -38,6 +38,18 @@ struct SddmmArgs {
     bool softmax = false;  // row softmax of alpha * scores (k x d layout, no v, beta 0)
 };
 
+struct AttnArgs {
+    int m, k_rows, d, batch;
+    const int *row_indices;  // NULL = identity order
+    const int *row_offsets;
+    const int *col_indices;
+    const void *q, *k, *v;   // element type `dtype`
+    float alpha;
+    float *out;
+    long long stride_q, stride_k, stride_v, stride_out;  // elements
+    Dtype dtype = Dtype::f32;
+};
+
 hipError_t launch_offsets_from_lengths(int m, const int *lengths,
                                        int *row_offsets, hipStream_t stream);
 hipError_t launch_count_dense(int m, int k, const unsigned char *mask,
@@ -52,6 +64,7 @@ hipError_t launch_row_swizzle(int m, const int *row_offsets, int *row_indices,
 hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream);
 hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream);
 hipError_t launch_spmm_sddmm(const SpmmArgs &x, const SddmmArgs &y, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_row_softmax(int m, const int *row_indices, const int *row_offsets,
                               const float *in, float *out, int batch, long long stride_in,
                               long long stride_out, hipStream_t stream);
