@@ -375,6 +375,10 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
             fn = lambda: sp.sp_spmm(m, k, n, a.nnz, order, vals, ro, cols, b, c)
             recs.append(spmm_record(w["name"], m, k, n, a.nnz, graph_time_us(torch, fn, 200),
                                     {"swizzle": swz, "cold_us": cold_time_us(torch, fn, flush)}))
+            bfn = lambda: sp.sp_spmm_balanced(m, k, n, a.nnz, order, vals, ro, cols, b, c)
+            recs.append(spmm_record(w["name"], m, k, n, a.nnz, graph_time_us(torch, bfn, 200),
+                                    {"swizzle": swz, "kernel": "balanced",
+                                     "cold_us": cold_time_us(torch, bfn, flush)}))
             sfn = lambda: sp.sp_sddmm(m, k, d, a.nnz, order, ro, cols, x, y, 1.0, out)
             us = graph_time_us(torch, sfn, 200)
             recs.append({"record": "sddmm", "workload": w["name"], "m": m, "k": k, "d": d,

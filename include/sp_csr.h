@@ -206,6 +206,23 @@ sp_status_t sp_spmm(int m, int k, int n, int nnz, const int *row_indices,
                     const int *col_indices, const float *b, float *c,
                     sp_stream_t stream);
 
+/* sp_spmm for row-length distributions with a heavy tail ("Interesting
+ * ideas" I4 of the card: balancing kept separate from the kernels).  With
+ * every wave of a launch resident at once, as on this GPU at these sizes, the
+ * order rows are handed out in cannot balance anything: the longest row's
+ * chain of loads sets the duration.  Here, for B of more than 128 fp32
+ * columns, workgroups of 4 waves take 4 rows in serpentine order over the
+ * work slots (in the swizzled order: long rows with short ones) and split the
+ * group's entries evenly across the waves, adding the pieces' partial sums in
+ * a fixed order.  Results are deterministic for a given row order and within
+ * rounding of sp_spmm (pieces are summed separately).  On rows of uniform
+ * length it is slower than sp_spmm (4-wave groups, an extra LDS pass);
+ * narrower B takes sp_spmm's kernels.  Arguments as sp_spmm. */
+sp_status_t sp_spmm_balanced(int m, int k, int n, int nnz, const int *row_indices,
+                             const float *values, const int *row_offsets,
+                             const int *col_indices, const float *b, float *c,
+                             sp_stream_t stream);
+
 /* `batch` independent SpMMs sharing one sparsity structure (row_offsets,
  * col_indices, row_indices): for z < batch,
  *   C_z = A_z * B_z, values_z = values + z*stride_values,

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 21, declared
+    assert len(declared) == 22, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -72,6 +72,11 @@ def test_spmm_validation(lib):
     assert f(4, 4, 0, 0, NULL, NULL, NULL, NULL, NULL, NULL, 1, 0, 0, 0, s) == OK
     assert f(4, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, 0, 0, 0, 0, s) == OK
     assert lib.sp_spmm(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, s) == OK
+    g = lib.sp_spmm_balanced
+    assert g(-1, 4, 4, 0, NULL, NULL, FAKE, NULL, NULL, FAKE, s) == INVALID
+    assert g(4, 4, 4, 8, NULL, NULL, FAKE, FAKE, FAKE, FAKE, s) == INVALID
+    assert g(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, FAKE, NULL, s) == INVALID
+    assert g(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, s) == OK
     assert lib.sp_spmm(-2, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, s) == INVALID
 
 

@@ -58,6 +58,8 @@ SIGNATURES = {
     "sp_csr_transpose": ([_c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           ctypes.c_size_t, _vp], _c_int),
     "sp_csr_transpose_values": ([_c_int, _vp, _vp, _vp, _vp], _c_int),
+    "sp_spmm_balanced": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+                         _c_int),
     "sp_spmm_sddmm": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                        _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_float, _vp,
                        _vp], _c_int),
@@ -251,6 +253,15 @@ def sp_csr_transpose_values(nnz, t_perm, values, t_values, stream=None):
     _check(lib().sp_csr_transpose_values(
         nnz, _ptr(t_perm, _I32, "t_perm", True), _ptr(values, _F32, "values", True),
         _ptr(t_values, _F32, "t_values", True), _stream(stream)), "sp_csr_transpose_values")
+
+
+def sp_spmm_balanced(m, k, n, nnz, row_indices, values, row_offsets, col_indices, b, c,
+                     stream=None):
+    _check(lib().sp_spmm_balanced(
+        m, k, n, nnz, _ptr(row_indices, _I32, "row_indices", True),
+        _ptr(values, _F32, "values", True), _ptr(row_offsets, _I32, "row_offsets"),
+        _ptr(col_indices, _I32, "col_indices", True), _ptr(b, _F32, "b", True),
+        _ptr(c, _F32, "c"), _stream(stream)), "sp_spmm_balanced")
 
 
 def sp_spmm_sddmm(m, k, n, nnz, row_indices, values, row_offsets, col_indices, b, c,

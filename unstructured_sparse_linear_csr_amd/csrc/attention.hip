@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kWave) void attention_kernel(AttnParams p)
     constexpr int kBatches = (kG + kU - 1) / kU;
     // P.V phase: kDv lanes per entry (one vector each), kSl entries per step
     constexpr int kSl = kWave / kDv;
-    constexpr int kUv = 2;                       // P.V steps per batch
+    constexpr int kUv = kDv <= 16 ? 2 : kDv / 8; // P.V steps per batch (at most 8 batches)
     constexpr int kVB = (kDv + kUv - 1) / kUv;   // P.V batches of a full window
     static_assert(kNv * kG == kDv, "score lanes cover the row");
     // windows plus the padding read by the prefetch of up to two batches

@@ -237,6 +237,20 @@ sp_status_t sp_spmm_sddmm(int m, int k, int n, int nnz, const int *row_indices,
     return SP_SUCCESS;
 }
 
+sp_status_t sp_spmm_balanced(int m, int k, int n, int nnz, const int *row_indices,
+                             const float *values, const int *row_offsets,
+                             const int *col_indices, const float *b, float *c,
+                             sp_stream_t stream)
+{
+    spk::SpmmArgs a;
+    bool work = false;
+    const sp_status_t st = spmm_prepare(m, k, n, nnz, row_indices, spk::Dtype::f32, values,
+                                        row_offsets, col_indices, b, c, 1, 0, 0, 0, &a, &work);
+    if (st != SP_SUCCESS || !work) return st;
+    a.balanced = true;
+    return from_hip(spk::launch_spmm(a, as_stream(stream)));
+}
+
 sp_status_t sp_spmm_batched(int m, int k, int n, int nnz, const int *row_indices,
                             const float *values, const int *row_offsets,
                             const int *col_indices, const float *b, float *c,

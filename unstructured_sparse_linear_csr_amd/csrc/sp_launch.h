@@ -19,6 +19,7 @@ struct SpmmArgs {
     int batch;
     long long stride_values, stride_b, stride_c;  // elements
     Dtype dtype = Dtype::f32;
+    bool balanced = false;  // wide B: waves share each group's entries evenly
 };
 
 struct SddmmArgs {

@@ -21,6 +21,100 @@ __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
     spmm_wide_body<E, kLpr, kVec, kVecCsr, kBuf>(p, wide_work(p, blockIdx.x));
 }
 
+// Wide B with balanced waves (64 lanes per row, one column tile of 64 kVec
+// columns per workgroup).  A workgroup of kBalWaves waves takes kBalWaves
+// rows chosen in serpentine order over the work slots -- g, 2G-1-g, 2G+g,
+// 4G-1-g for group g of G -- so that, in the swizzled order (rows by nonzero
+// count, longest first), each group pairs long rows with short ones.  The
+// group's entries, taken as one sequence (row after row), are cut into
+// kBalWaves equal parts, one per wave; a wave accumulates each row piece of
+// its part (the wide kernel's staging and gathers, with a wave-local barrier
+// since the waves run different numbers of windows) and leaves the partial
+// sums in LDS; then wave j adds row j's partial sums in wave order and writes
+// the row.  Every wave thus streams about the group's mean row length, and
+// the longest row no longer sets the launch's duration.  Summation: in entry
+// order within a piece, pieces in order; deterministic for a given row order.
+constexpr int kBalWaves = 4;
+
+template <typename E, int kVec, bool kVecCsr, bool kBuf>
+__global__ __launch_bounds__(kBalWaves * kWave) void spmm_balanced_kernel(SpmmParams p)
+{
+    using V = GVec<E, kVec>;
+    constexpr int kChunk = kEpl * kWave;
+    constexpr int kPitch = kChunk + kU + 4;
+    __shared__ __align__(16) int s_off[kBalWaves * kPitch];
+    __shared__ __align__(16) float s_val[kBalWaves * kPitch];
+    __shared__ __align__(16) float s_part[kBalWaves][kBalWaves][kWave * kVec];
+    __shared__ int s_row[kBalWaves], s_p0[kBalWaves], s_len[kBalWaves];
+
+    const int groups = p.row_blocks;
+    const long long w = xcd_work_index((long long)p.batch * p.tiles, groups);
+    if (w < 0) return;  // uniform over the workgroup
+    const long long per_z = (long long)p.tiles * groups;
+    const long long z = w / per_z;
+    const int tile = (int)((w - z * per_z) / groups);
+    const int g = (int)(w - z * per_z - (long long)tile * groups);
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x - wave * kWave;
+
+    if (lane == 0) {
+        const int half = wave >> 1;
+        const int slot = (wave & 1) ? half * 2 * groups + 2 * groups - 1 - g
+                                    : half * 2 * groups + g;
+        int row = -1, p0 = 0, len = 0;
+        if (slot < p.m) {
+            row = p.row_indices ? p.row_indices[slot] : slot;
+            p0 = p.row_offsets[row];
+            len = p.row_offsets[row + 1] - p0;
+        }
+        s_row[wave] = row;
+        s_p0[wave] = p0;
+        s_len[wave] = len;
+    }
+    __syncthreads();
+    int cum[kBalWaves + 1];
+    cum[0] = 0;
+#pragma unroll
+    for (int j = 0; j < kBalWaves; ++j) cum[j + 1] = cum[j] + s_len[j];
+    const long long total = cum[kBalWaves];
+    auto part_lo = [&](int v) { return (int)(total * v / kBalWaves); };
+
+    const E *__restrict__ vals = static_cast<const E *>(p.values) + z * p.stride_values;
+    const E *__restrict__ bz = static_cast<const E *>(p.b) + z * p.stride_b;
+    const int col0 = (tile * kWave + lane) * kVec;
+    const bool col_ok = col0 < p.n;
+    const int lo_w = part_lo(wave), hi_w = part_lo(wave + 1);
+#pragma unroll
+    for (int j = 0; j < kBalWaves; ++j) {
+        const int lo = max(lo_w, cum[j]), hi = min(hi_w, cum[j + 1]);
+        if (lo >= hi) continue;  // uniform over the wave
+        float acc[kVec];
+#pragma unroll
+        for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
+        wide_accumulate<E, kWave, kVec, kVecCsr, kBuf, true>(
+            p, vals, bz, s_p0[j] + lo - cum[j], s_p0[j] + hi - cum[j], lane, col0, col_ok,
+            s_off + wave * kPitch, s_val + wave * kPitch, acc);
+#pragma unroll
+        for (int t = 0; t < kVec; ++t) s_part[j][wave][lane * kVec + t] = acc[t];
+    }
+    __syncthreads();
+    const int row = s_row[wave];
+    if (row < 0 || !col_ok) return;
+    float acc[kVec];
+#pragma unroll
+    for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
+#pragma unroll
+    for (int v = 0; v < kBalWaves; ++v) {
+        const int lo = max(part_lo(v), cum[wave]), hi = min(part_lo(v + 1), cum[wave + 1]);
+        if (lo < hi) {
+#pragma unroll
+            for (int t = 0; t < kVec; ++t) acc[t] += s_part[wave][v][lane * kVec + t];
+        }
+    }
+    float *cz = p.c + z * p.stride_c;
+    V::store(cz + (size_t)row * (size_t)p.n + col0, acc);
+}
+
 // Narrow B (n of at most 16 columns): the lane-over-columns mapping above
 // would leave most of a row group idle, so here the lanes of one wave split
 // a row's entries instead.  Lane (s, v) handles entries s, s + kS, s + 2kS, ...
@@ -348,6 +442,25 @@ hipError_t launch_wide(bool vec, int lpr, const SpmmParams &p, bool vec_csr, boo
                : launch_lpr<E, 1>(lpr, p, vec_csr, buf, s);
 }
 
+template <typename E, int kVec>
+hipError_t launch_balanced(const SpmmParams &p, bool vec_csr, bool buf, hipStream_t s)
+{
+    const dim3 grid((unsigned)xcd_grid((long long)p.batch * p.tiles, p.row_blocks));
+    const dim3 block(kBalWaves * kWave);
+    if (vec_csr) {
+        if (buf)
+            hipLaunchKernelGGL((spmm_balanced_kernel<E, kVec, true, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((spmm_balanced_kernel<E, kVec, true, false>), grid, block, 0, s, p);
+    } else {
+        if (buf)
+            hipLaunchKernelGGL((spmm_balanced_kernel<E, kVec, false, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((spmm_balanced_kernel<E, kVec, false, false>), grid, block, 0, s, p);
+    }
+    return hipGetLastError();
+}
+
 inline bool aligned(const void *ptr, unsigned bytes)
 {
     return (reinterpret_cast<uintptr_t>(ptr) & (bytes - 1u)) == 0;
@@ -411,6 +524,11 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
     plan->e = nv <= 1 ? 1 : nv <= 2 ? 2 : 4;
     plan->blocks = 0;
     plan->kind = SpmmPlan::kWide;
+    if (lpr == kWave && a.balanced) {
+        // groups of kBalWaves rows in place of row blocks
+        plan->kind = SpmmPlan::kBalanced;
+        p.row_blocks = (int)(((long long)a.m + kBalWaves - 1) / kBalWaves);
+    }
     if (narrow) {
         plan->kind = SpmmPlan::kNarrow;
         // B in LDS when it fits and every CU has at least as many entries to
@@ -445,6 +563,18 @@ hipError_t run_spmm(const SpmmPlan &plan, hipStream_t stream)
     case SpmmPlan::kNarrow:
         return plan.vec ? launch_narrow<4>(plan.e, p, stream)
                         : launch_narrow<1>(plan.e, p, stream);
+    case SpmmPlan::kBalanced:
+        switch (plan.dtype) {
+        case Dtype::f16:
+            return plan.vec ? launch_balanced<_Float16, 8>(p, plan.vec_csr, plan.buf, stream)
+                            : launch_balanced<_Float16, 1>(p, plan.vec_csr, plan.buf, stream);
+        case Dtype::bf16:
+            return plan.vec ? launch_balanced<bf16, 8>(p, plan.vec_csr, plan.buf, stream)
+                            : launch_balanced<bf16, 1>(p, plan.vec_csr, plan.buf, stream);
+        default:
+            return plan.vec ? launch_balanced<float, 4>(p, plan.vec_csr, plan.buf, stream)
+                            : launch_balanced<float, 1>(p, plan.vec_csr, plan.buf, stream);
+        }
     default:
         break;
     }

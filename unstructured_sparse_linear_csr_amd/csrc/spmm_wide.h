@@ -68,50 +68,39 @@ struct SpmmParams {
 // 0 and column -1 and is skipped by a predicate.  E is the element type of
 // the values and of B (fp32, fp16 or bf16); values are widened to fp32 when
 // staged and B elements when gathered, so all arithmetic is fp32.
-template <typename E, int kLpr, int kVec, bool kVecCsr, bool kBuf>
-__device__ __forceinline__ void spmm_wide_body(const SpmmParams &p, long long w)
+// Staging barrier between windows: the workgroup's when a workgroup is one
+// wave, or only the wave's own (LDS operations of a wave complete in program
+// order, so a compiler barrier suffices) when several waves of a workgroup
+// run different numbers of windows over private staging regions.
+template <bool kWaveSync>
+__device__ __forceinline__ void window_sync()
+{
+    if constexpr (kWaveSync) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+        __syncthreads();
+    }
+}
+
+// acc += sum over entries q in [p0, p1) of value(q) * B[col(q)][col0 ...],
+// for this lane's kVec columns starting at col0 (col_ok: the lane owns
+// columns), in entry order, through the staging region g_off / g_val of the
+// lane's group (kLpr lanes).  p0 and p1 may delimit any part of a row.
+template <typename E, int kLpr, int kVec, bool kVecCsr, bool kBuf, bool kWaveSync>
+__device__ __forceinline__ void wide_accumulate(const SpmmParams &p, const E *__restrict__ vals,
+                                                const E *__restrict__ bz, int p0, int p1,
+                                                int gl, int col0, bool col_ok, int *g_off,
+                                                float *g_val, float *acc)
 {
     using V = GVec<E, kVec>;
     using VecT = typename V::T;
     constexpr unsigned kEb = Elem<E>::kBytes;
-    constexpr int kRpw = kWave / kLpr;       // rows per wave
     constexpr int kChunk = kEpl * kLpr;      // entries per row per window
-    // A group's slots: the window, kU padding slots read by the prefetch, and
-    // 4 more so that the groups' regions start 12 words apart modulo the 64
-    // LDS banks (their broadcast reads then never share a bank).
-    constexpr int kPitch = kChunk + kU + 4;
     constexpr int kPad = kBuf ? (int)kOutOfRange : -1;
-    static_assert(kPitch % 4 == 0 && kU % 4 == 0, "16-byte aligned batches");
-    static_assert(kChunk % kU == 0, "batches never straddle the window end");
-    // Staged entries, one array per field so that each lane's staging writes
-    // are 16 contiguous bytes: B-row byte offset (kBuf) or column, and value.
-    __shared__ __align__(16) int s_off[kRpw * kPitch];
-    __shared__ __align__(16) float s_val[kRpw * kPitch];
-
-    if (w < 0) return;
-    const long long per_z = (long long)p.tiles * p.row_blocks;
-    const long long z = w / per_z;
-    const int tile = (int)((w - z * per_z) / p.row_blocks);
-    const int rb = (int)(w - z * per_z - (long long)tile * p.row_blocks);
-
-    const int lane = threadIdx.x;
-    const int grp = kRpw == 1 ? 0 : lane / kLpr;
-    const int gl = kRpw == 1 ? lane : lane - grp * kLpr;
-    const E *__restrict__ vals = static_cast<const E *>(p.values) + z * p.stride_values;
-    const E *__restrict__ bz = static_cast<const E *>(p.b) + z * p.stride_b;
-    float *__restrict__ cz = p.c + z * p.stride_c;
-
-    const int slot = rb * kRpw + grp;
-    const bool has_row = slot < p.m;
-    const int row = has_row ? (p.row_indices ? p.row_indices[slot] : slot) : 0;
-    const int p0 = has_row ? p.row_offsets[row] : 0;
-    const int p1 = has_row ? p.row_offsets[row + 1] : 0;
-    const int col0 = (tile * kLpr + gl) * kVec;
-    const bool col_ok = col0 < p.n;  // vector path: n % kVec == 0, so the whole vector is in range
     // Lanes past the last column read only out-of-range (zero) data.
     const unsigned lane_bytes = col_ok ? (unsigned)col0 * kEb : kOutOfRange;
-    int *g_off = s_off + grp * kPitch;
-    float *g_val = s_val + grp * kPitch;
     for (int j = gl; j < kU; j += kLpr) {
         g_off[kChunk + j] = kPad;
         g_val[kChunk + j] = 0.f;
@@ -151,10 +140,6 @@ __device__ __forceinline__ void spmm_wide_body(const SpmmParams &p, long long w)
             val[u] = v4.x; val[u + 1] = v4.y; val[u + 2] = v4.z; val[u + 3] = v4.w;
         }
     };
-
-    float acc[kVec];
-#pragma unroll
-    for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
 
     int win = kVecCsr ? (p0 & ~3) : p0;
     for (;;) {
@@ -199,7 +184,7 @@ __device__ __forceinline__ void spmm_wide_body(const SpmmParams &p, long long w)
                 g_val[t * kLpr + gl] = value_of(idx, in ? Elem<E>::f32(vals[idx]) : 0.f);
             }
         }
-        __syncthreads();
+        window_sync<kWaveSync>();
         // ---- gather and accumulate: double-buffered batches of kU slots.
         // Slots [0, wend) of the window cover every group's live entries.
         const int my_end = min(p1 - win, kChunk);
@@ -235,9 +220,56 @@ __device__ __forceinline__ void spmm_wide_body(const SpmmParams &p, long long w)
             read_batch(min(j + 3 * kU, kChunk), offb, valb);
             j += 2 * kU;
         } while (j < wend);
-        __syncthreads();
+        window_sync<kWaveSync>();
         win += kChunk;
     }
+}
+
+template <typename E, int kLpr, int kVec, bool kVecCsr, bool kBuf>
+__device__ __forceinline__ void spmm_wide_body(const SpmmParams &p, long long w)
+{
+    using V = GVec<E, kVec>;
+    constexpr int kRpw = kWave / kLpr;       // rows per wave
+    constexpr int kChunk = kEpl * kLpr;      // entries per row per window
+    // A group's slots: the window, kU padding slots read by the prefetch, and
+    // 4 more so that the groups' regions start 12 words apart modulo the 64
+    // LDS banks (their broadcast reads then never share a bank).
+    constexpr int kPitch = kChunk + kU + 4;
+    static_assert(kPitch % 4 == 0 && kU % 4 == 0, "16-byte aligned batches");
+    static_assert(kChunk % kU == 0, "batches never straddle the window end");
+    // Staged entries, one array per field so that each lane's staging writes
+    // are 16 contiguous bytes: B-row byte offset (kBuf) or column, and value.
+    __shared__ __align__(16) int s_off[kRpw * kPitch];
+    __shared__ __align__(16) float s_val[kRpw * kPitch];
+
+    if (w < 0) return;
+    const long long per_z = (long long)p.tiles * p.row_blocks;
+    const long long z = w / per_z;
+    const int tile = (int)((w - z * per_z) / p.row_blocks);
+    const int rb = (int)(w - z * per_z - (long long)tile * p.row_blocks);
+
+    const int lane = threadIdx.x;
+    const int grp = kRpw == 1 ? 0 : lane / kLpr;
+    const int gl = kRpw == 1 ? lane : lane - grp * kLpr;
+    const E *__restrict__ vals = static_cast<const E *>(p.values) + z * p.stride_values;
+    const E *__restrict__ bz = static_cast<const E *>(p.b) + z * p.stride_b;
+    float *__restrict__ cz = p.c + z * p.stride_c;
+
+    const int slot = rb * kRpw + grp;
+    const bool has_row = slot < p.m;
+    const int row = has_row ? (p.row_indices ? p.row_indices[slot] : slot) : 0;
+    const int p0 = has_row ? p.row_offsets[row] : 0;
+    const int p1 = has_row ? p.row_offsets[row + 1] : 0;
+    const int col0 = (tile * kLpr + gl) * kVec;
+    const bool col_ok = col0 < p.n;  // vector path: n % kVec == 0, so the whole vector is in range
+    int *g_off = s_off + grp * kPitch;
+    float *g_val = s_val + grp * kPitch;
+    float acc[kVec];
+#pragma unroll
+    for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
+
+    wide_accumulate<E, kLpr, kVec, kVecCsr, kBuf, false>(p, vals, bz, p0, p1, gl, col0, col_ok,
+                                                         g_off, g_val, acc);
     if (has_row && col_ok) V::store(cz + (size_t)row * (size_t)p.n + col0, acc);
 }
 
