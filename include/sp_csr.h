@@ -19,7 +19,8 @@
  * only enqueues work on `stream` and returns without synchronising.  The
  * library records no hipMemsetAsync, so calls may be captured in HIP graphs.
  *
- * CSR.  Standard CSR with int32 indices and fp32 values: an m x k matrix with
+ * CSR.  Standard CSR with int32 indices and fp32 values (fp16/bf16 in the
+ * mixed-precision entry points): an m x k matrix with
  * nnz entries has row_offsets[m+1] (row_offsets[0] = 0, non-decreasing,
  * row_offsets[m] = nnz), col_indices[nnz] (in [0, k), strictly increasing
  * within a row) and values[nnz].  These are preconditions, documented and not
@@ -30,15 +31,19 @@
  * Row order.  `row_indices` (int32[m], a permutation of 0..m-1, or NULL for
  * the identity) gives the order in which rows are handed to the GPU's workers:
  * the r-th work slot handles row row_indices[r].  It changes scheduling only,
- * never results; sp_row_swizzle computes the balanced order.
+ * never results (sp_spmm_balanced, which also groups rows by it, is the one
+ * exception: there it can change rounding); sp_row_swizzle computes the
+ * balanced order.
  *
  * Errors.  Return codes only; nothing is thrown and nothing aborts.  Argument
  * checks happen on the host before any HIP call: a negative size, a NULL
  * pointer for a non-empty buffer, or a size beyond int32 indexing returns
- * SP_ERROR_INVALID_VALUE and enqueues nothing.  A failed launch returns
- * SP_ERROR_LAUNCH_FAILED.  Alignment is never required: unaligned pointers or
- * widths that are not multiples of 4 take a scalar-load variant of the same
- * kernel.
+ * SP_ERROR_INVALID_VALUE and enqueues nothing.  A problem outside what a
+ * kernel supports (sizes beyond the launch limits, sp_sparse_attention's head
+ * dimensions) returns SP_ERROR_NOT_SUPPORTED, also before any launch.  A
+ * failed launch returns SP_ERROR_LAUNCH_FAILED.  Alignment is not required
+ * unless an entry point says so: unaligned pointers or widths that are not
+ * multiples of the vector width take a scalar-load variant of the same kernel.
  */
 #ifndef SP_CSR_H
 #define SP_CSR_H
@@ -124,69 +129,6 @@ sp_status_t sp_row_swizzle(int m, const int *row_offsets, int *row_indices,
  *   row_offsets  int32[m+1], output;  row_indices  int32[m], output */
 sp_status_t sp_csr_build_from_lengths(int m, const int *lengths, int *row_offsets,
                                       int *row_indices, sp_stream_t stream);
-
-/* ------------------------------------------------------------------------
- * SpMM and SDDMM together ("Summary" of the card: the two kernels of the
- * method).  Problems of DL sizes leave the GPU mostly idle in either kernel
- * alone; one launch that carries both keeps it busier and pays one launch.
- * ---------------------------------------------------------------------- */
-
-/* The SpMM sp_spmm(m, k, n, nnz, row_indices, values, row_offsets,
- * col_indices, b, c) and the SDDMM sp_sddmm(s_m, s_k, d, s_nnz,
- * s_row_indices, s_row_offsets, s_col_indices, x, y, alpha, out) -- two
- * independent problems, whose sparsity structures may be the same arrays or
- * different ones -- enqueued as one launch when both take their fp32 vector
- * paths (16-byte aligned operands, B and Y under 2 GiB, n % 4 == 0,
- * d % 4 == 0, d <= 256), otherwise as the two separate launches.  Results
- * are bit-identical to calling the two entry points.  Arguments are checked
- * as those entry points check them; c and out must not overlap each other or
- * any input. */
-sp_status_t sp_spmm_sddmm(int m, int k, int n, int nnz, const int *row_indices,
-                          const float *values, const int *row_offsets, const int *col_indices,
-                          const float *b, float *c, int s_m, int s_k, int d, int s_nnz,
-                          const int *s_row_indices, const int *s_row_offsets,
-                          const int *s_col_indices, const float *x, const float *y,
-                          float alpha, float *out, sp_stream_t stream);
-
-/* ------------------------------------------------------------------------
- * Transpose ("Summary" of the card: the kernels serve training; the input
- * gradient of C = A * B is dB = A^T * dC, an SpMM with the transposed sparse
- * operand).  sp_csr_transpose gives A^T in standard CSR; sp_row_swizzle and
- * sp_spmm on it then compute the product, entries of each output row summed in
- * ascending row order of A.
- * ---------------------------------------------------------------------- */
-
-/* *bytes = the device workspace sp_csr_transpose needs for nnz entries
- * (about 20 bytes per entry plus 1 KiB per 4096 entries).  Pure host
- * arithmetic; enqueues nothing. */
-sp_status_t sp_csr_transpose_workspace(int m, int k, int nnz, size_t *bytes);
-
-/* The CSR of A^T (k x m) from the CSR of A (m x k): row j of A^T lists, in
- * ascending order, the rows i of A with an entry in column j, each with that
- * entry's value.  Identical on every run (no atomic operation decides an
- * order).
- *   row_offsets, col_indices, values   the CSR of A (values may be NULL when
- *                 t_values is NULL)
- *   t_row_offsets int32[k+1], output;  t_col_indices int32[nnz], output
- *   t_values      fp32[nnz], output, or NULL
- *   t_perm        int32[nnz], output, or NULL: t_perm[q] is the index in A's
- *                 arrays of A^T's entry q (for sp_csr_transpose_values)
- *   workspace     device memory of at least sp_csr_transpose_workspace bytes,
- *                 256-byte aligned, not overlapping any argument; its contents
- *                 on entry do not matter and on return are unspecified.
- * Errors: k == INT32_MAX, k == 0 with nnz > 0, a missing or short workspace,
- * or a NULL array that must exist returns SP_ERROR_INVALID_VALUE. */
-sp_status_t sp_csr_transpose(int m, int k, int nnz, const int *row_offsets,
-                             const int *col_indices, const float *values,
-                             int *t_row_offsets, int *t_col_indices, float *t_values,
-                             int *t_perm, void *workspace, size_t workspace_bytes,
-                             sp_stream_t stream);
-
-/* t_values[q] = values[t_perm[q]] for q < nnz: new values of A (same
- * structure) carried into the order of A^T without transposing again.
- * t_values must not overlap values. */
-sp_status_t sp_csr_transpose_values(int nnz, const int *t_perm, const float *values,
-                                    float *t_values, sp_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * SpMM ("Summary" of the card): C = A * B, A sparse in CSR, B dense.
@@ -333,9 +275,73 @@ sp_status_t sp_sddmm_ex(int m, int k, int d, int nnz, const int *row_indices,
                         sp_stream_t stream);
 
 /* ------------------------------------------------------------------------
- * Row softmax over CSR entries ("Interesting ideas" I3 of the card: the SDDMM
- * form sparse attention needs; softmax over each row's entries is the step
- * between the attention scores (SDDMM) and their weighted sum (SpMM)).
+ * SpMM and SDDMM together ("Summary" of the card: the two kernels of the
+ * method).  Problems of DL sizes leave the GPU mostly idle in either kernel
+ * alone; one launch that carries both keeps it busier and pays one launch.
+ * ---------------------------------------------------------------------- */
+
+/* The SpMM sp_spmm(m, k, n, nnz, row_indices, values, row_offsets,
+ * col_indices, b, c) and the SDDMM sp_sddmm(s_m, s_k, d, s_nnz,
+ * s_row_indices, s_row_offsets, s_col_indices, x, y, alpha, out) -- two
+ * independent problems, whose sparsity structures may be the same arrays or
+ * different ones -- enqueued as one launch when both take their fp32 vector
+ * paths (16-byte aligned operands, B and Y under 2 GiB, n % 4 == 0,
+ * d % 4 == 0, d <= 256), otherwise as the two separate launches.  Results
+ * are bit-identical to calling the two entry points.  Arguments are checked
+ * as those entry points check them; c and out must not overlap each other or
+ * any input. */
+sp_status_t sp_spmm_sddmm(int m, int k, int n, int nnz, const int *row_indices,
+                          const float *values, const int *row_offsets, const int *col_indices,
+                          const float *b, float *c, int s_m, int s_k, int d, int s_nnz,
+                          const int *s_row_indices, const int *s_row_offsets,
+                          const int *s_col_indices, const float *x, const float *y,
+                          float alpha, float *out, sp_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Transpose ("Summary" of the card: the kernels serve training; the input
+ * gradient of C = A * B is dB = A^T * dC, an SpMM with the transposed sparse
+ * operand).  sp_csr_transpose gives A^T in standard CSR; sp_row_swizzle and
+ * sp_spmm on it then compute the product, entries of each output row summed in
+ * ascending row order of A.
+ * ---------------------------------------------------------------------- */
+
+/* *bytes = the device workspace sp_csr_transpose needs for nnz entries
+ * (about 20 bytes per entry plus 1 KiB per 4096 entries).  Pure host
+ * arithmetic; enqueues nothing. */
+sp_status_t sp_csr_transpose_workspace(int m, int k, int nnz, size_t *bytes);
+
+/* The CSR of A^T (k x m) from the CSR of A (m x k): row j of A^T lists, in
+ * ascending order, the rows i of A with an entry in column j, each with that
+ * entry's value.  Identical on every run (no atomic operation decides an
+ * order).
+ *   row_offsets, col_indices, values   the CSR of A (values may be NULL when
+ *                 t_values is NULL)
+ *   t_row_offsets int32[k+1], output;  t_col_indices int32[nnz], output
+ *   t_values      fp32[nnz], output, or NULL
+ *   t_perm        int32[nnz], output, or NULL: t_perm[q] is the index in A's
+ *                 arrays of A^T's entry q (for sp_csr_transpose_values)
+ *   workspace     device memory of at least sp_csr_transpose_workspace bytes,
+ *                 256-byte aligned, not overlapping any argument; its contents
+ *                 on entry do not matter and on return are unspecified.
+ * Errors: k == INT32_MAX, k == 0 with nnz > 0, a missing or short workspace,
+ * or a NULL array that must exist returns SP_ERROR_INVALID_VALUE. */
+sp_status_t sp_csr_transpose(int m, int k, int nnz, const int *row_offsets,
+                             const int *col_indices, const float *values,
+                             int *t_row_offsets, int *t_col_indices, float *t_values,
+                             int *t_perm, void *workspace, size_t workspace_bytes,
+                             sp_stream_t stream);
+
+/* t_values[q] = values[t_perm[q]] for q < nnz: new values of A (same
+ * structure) carried into the order of A^T without transposing again.
+ * t_values must not overlap values. */
+sp_status_t sp_csr_transpose_values(int nnz, const int *t_perm, const float *values,
+                                    float *t_values, sp_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse attention ("Interesting ideas" I3 of the card: the SDDMM form sparse
+ * attention needs).  Attention is scores (SDDMM), a softmax over each row's
+ * entries, and their weighted sum (SpMM): the softmax alone, the scores with
+ * their softmax in one pass, and the whole attention in one pass.
  * ---------------------------------------------------------------------- */
 
 /* For each batch entry z < batch and each row i with entries p:
