@@ -1,0 +1,100 @@
+"""Every kind of launch the library makes, captured in one HIP graph and
+replayed several times with eager work and synchronisations in between; each
+replay must reproduce the eager results bit for bit (the library records no
+memset nodes and allocates nothing, so capture is plain kernel nodes)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from unstructured_sparse_linear_csr_amd import binding as sp
+from unstructured_sparse_linear_csr_amd import inputs
+
+from gpu_util import dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    sp.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def test_graph_of_every_launch_kind():
+    w = inputs.transformer_ffn()
+    a = w["a"]
+    m, k, n, d, nnz = w["m"], w["k"], w["n"], w["d"], a.nnz
+    lengths, cols, vals = dev(a.lengths), dev(a.cols), dev(a.values)
+    b, x, y = dev(w["b"]), dev(w["x"]), dev(w["y"])
+    prior = dev(inputs.random_dense(950, nnz))
+    ro = torch.empty(m + 1, dtype=torch.int32, device="cuda")
+    ri = torch.empty(m, dtype=torch.int32, device="cuda")
+    ws = torch.empty(sp.sp_csr_transpose_workspace(m, k, nnz), dtype=torch.uint8, device="cuda")
+    t_ro = torch.empty(k + 1, dtype=torch.int32, device="cuda")
+    t_ci = torch.empty(nnz, dtype=torch.int32, device="cuda")
+    t_v = torch.empty(nnz, device="cuda")
+    t_p = torch.empty(nnz, dtype=torch.int32, device="cuda")
+    t_ri = torch.empty(k, dtype=torch.int32, device="cuda")
+    outs = {name: torch.empty(shape, device="cuda") for name, shape in {
+        "c": (m, n), "c_bal": (m, n), "c_bf16": (m, n), "dx": (k, n), "s": (nnz,),
+        "s_gen": (nnz,), "s_dk": (nnz,), "p": (nnz,), "att": (m, d), "c_pair": (m, n),
+        "s_pair": (nnz,)}.items()}
+    b16, v16 = b.to(torch.bfloat16), vals.to(torch.bfloat16)
+    y_dk = y.t().contiguous()
+    dy = dev(inputs.random_dense(951, m, n))
+
+    def work():
+        sp.sp_csr_build_from_lengths(m, lengths, ro, ri)
+        sp.sp_spmm(m, k, n, nnz, ri, vals, ro, cols, b, outs["c"])
+        sp.sp_spmm_balanced(m, k, n, nnz, ri, vals, ro, cols, b, outs["c_bal"])
+        sp.sp_spmm_ex(m, k, n, nnz, ri, v16, ro, cols, b16, outs["c_bf16"])
+        sp.sp_sddmm(m, k, d, nnz, ri, ro, cols, x, y, 1.0, outs["s"])
+        outs["s_gen"].copy_(prior)
+        sp.sp_sddmm_general(m, k, d, nnz, ri, ro, cols, vals, x, y, sp.SP_Y_KD, 0.5, 2.0,
+                            outs["s_gen"])
+        sp.sp_sddmm_general(m, k, d, nnz, ri, ro, cols, None, x, y_dk, sp.SP_Y_DK, 1.0, 0.0,
+                            outs["s_dk"])
+        sp.sp_sddmm_softmax(m, k, d, nnz, ri, ro, cols, x, y, 0.0625, outs["p"])
+        sp.sp_csr_row_softmax(m, nnz, ri, ro, outs["s"], outs["s"])
+        sp.sp_sparse_attention(m, m, d, nnz, ri, ro, cols, x, x, x, 0.0625, outs["att"])
+        sp.sp_spmm_sddmm(m, k, n, nnz, ri, vals, ro, cols, b, outs["c_pair"], m, k, d, nnz, ri,
+                         ro, cols, x, y, 1.0, outs["s_pair"])
+        sp.sp_csr_transpose(m, k, nnz, ro, cols, vals, t_ro, t_ci, t_v, t_p, ws)
+        sp.sp_csr_transpose_values(nnz, t_p, vals, t_v)
+        sp.sp_row_swizzle(k, t_ro, t_ri)
+        sp.sp_spmm(k, m, n, nnz, t_ri, t_v, t_ro, t_ci, dy, outs["dx"])
+
+    note("graph of every launch kind: eager reference")
+    work()
+    torch.cuda.synchronize()
+    want = {name: host(t).copy() for name, t in outs.items()}
+    want["t_ro"], want["t_ci"] = host(t_ro).copy(), host(t_ci).copy()
+    # the structure the graph computes must also be the oracle's
+    assert np.array_equal(want["t_ro"], oracle.csr_transpose(m, k, oracle.csr_offsets_from_lengths(a.lengths), a.cols)[0])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    scratch = torch.empty(1 << 20, device="cuda")
+    for rep in range(3):
+        note(f"graph replay {rep}")
+        for t in outs.values():
+            t.fill_(float("nan"))
+        t_ro.fill_(-1)
+        t_ci.fill_(-1)
+        scratch.normal_()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t in outs.items():
+            assert np.array_equal(host(t).view(np.int32), want[name].view(np.int32)), (rep, name)
+        assert np.array_equal(host(t_ro), want["t_ro"]) and np.array_equal(host(t_ci), want["t_ci"])
