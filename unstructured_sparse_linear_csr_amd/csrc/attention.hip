@@ -55,7 +55,10 @@ __global__ __launch_bounds__(kWave) void attention_kernel(AttnParams p)
     constexpr int kG = kDv <= 8 ? 8 : 16;
     constexpr int kNv = kDv / kG;
     constexpr int kNg = kWave / kG;
-    constexpr int kU = 8 / kNv;                  // steps per batch of gathers
+#ifndef SP_ATTN_SCORE_LOADS
+#define SP_ATTN_SCORE_LOADS 2
+#endif
+    constexpr int kU = SP_ATTN_SCORE_LOADS / kNv > 0 ? SP_ATTN_SCORE_LOADS / kNv : 1;  // steps per batch
     constexpr int kBatches = (kG + kU - 1) / kU;
     // P.V phase: kDv lanes per entry (one vector each), kSl entries per step
     constexpr int kSl = kWave / kDv;

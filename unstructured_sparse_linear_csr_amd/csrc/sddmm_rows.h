@@ -63,7 +63,7 @@ __device__ __forceinline__ void store_entry(const SddmmParams &p, long long z, i
 }
 
 #ifndef SP_SDDMM_LOADS_PER_BATCH
-#define SP_SDDMM_LOADS_PER_BATCH 8
+#define SP_SDDMM_LOADS_PER_BATCH 2
 #endif
 constexpr unsigned kOutOfRange = 0x80000000u;  // buffer offset that reads as zero
 
