@@ -393,14 +393,17 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
         # General SDDMM on the same shapes: the mask's values as the element-wise
         # scale and accumulation into the previous output, with Y stored k x d
         # and d x k.
+        # (d x k once more with a workspace: Y transposed there first).
         y_dk = y.t().contiguous()
-        for layout, yy in ((sp.SP_Y_KD, y), (sp.SP_Y_DK, y_dk)):
+        ws = torch.empty(sp.sp_sddmm_general_workspace(k, d), dtype=torch.uint8, device=dev)
+        for layout, yy, wsp, name in ((sp.SP_Y_KD, y, None, "kd"), (sp.SP_Y_DK, y_dk, None, "dk"),
+                                      (sp.SP_Y_DK, y_dk, ws, "dk_workspace")):
             gfn = lambda: sp.sp_sddmm_general(m, k, d, a.nnz, ri, ro, cols, vals, x, yy,
-                                              layout, 0.5, 1.0, out)
+                                              layout, 0.5, 1.0, out, workspace=wsp)
             us = graph_time_us(torch, gfn, 200)
             recs.append({"record": "sddmm_general", "workload": w["name"], "m": m, "k": k,
-                         "d": d, "nnz": a.nnz, "y_layout": "kd" if layout == sp.SP_Y_KD
-                         else "dk", "mask_values": True, "beta": 1.0, "us": us,
+                         "d": d, "nnz": a.nnz, "y_layout": name, "mask_values": True,
+                         "beta": 1.0, "us": us,
                          "cold_us": cold_time_us(torch, gfn, flush),
                          "gflops": 2.0 * a.nnz * d / (us * 1e-6) / 1e9,
                          "compulsory_gbs": (sddmm_bytes(m, k, d, a.nnz) + 8 * a.nnz)
@@ -449,6 +452,11 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
     tfn = lambda: sp.sp_sddmm_general(seq, seq, hd, nnz, ri, ro, cols, None, q, kt,
                                       sp.SP_Y_DK, 0.125, 0.0, s_out, bh, 0, seq * hd,
                                       seq * hd, nnz)
+    kt_ws = torch.empty(sp.sp_sddmm_general_workspace(seq, hd, bh, seq * hd),
+                        dtype=torch.uint8, device=dev)
+    twfn = lambda: sp.sp_sddmm_general(seq, seq, hd, nnz, ri, ro, cols, None, q, kt,
+                                       sp.SP_Y_DK, 0.125, 0.0, s_out, bh, 0, seq * hd,
+                                       seq * hd, nnz, workspace=kt_ws)
     smfn = lambda: sp.sp_csr_row_softmax(seq, nnz, ri, ro, s_out, s_out, bh, nnz, nnz)
 
     def attention():
@@ -468,6 +476,7 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
     vfn = lambda: sp.sp_sparse_attention(seq, seq, hd, nnz, ri, ro, cols, q, kk, v, 0.125, o,
                                          bh, seq * hd, seq * hd, seq * hd, seq * hd)
     for kind, fn in (("sddmm_batched", sfn), ("sddmm_general_dk_batched", tfn),
+                     ("sddmm_general_dk_workspace_batched", twfn),
                      ("row_softmax_batched", smfn), ("sddmm_softmax_batched", fsfn),
                      ("spmm_batched", pfn), ("attention_all_device", attention),
                      ("attention_all_device_fused_scores", attention_fused),

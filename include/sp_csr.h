@@ -224,21 +224,37 @@ typedef enum sp_y_layout {
  * with v_z = mask_values + z*stride_values (v = 1 when mask_values is NULL),
  * x_z = x + z*stride_x, y_z = y + z*stride_y, out_z = out + z*stride_out.
  *   y_layout     SP_Y_KD or SP_Y_DK (anything else: SP_ERROR_INVALID_VALUE).
- *                SP_Y_DK gathers single elements along rows of Y and is
- *                several times slower than SP_Y_KD for the same product.
  *   mask_values  fp32[nnz] per batch entry, or NULL
  *   beta         0: out is overwritten and never read (it may hold NaN);
  *                otherwise out holds the prior values and is updated in place.
+ *   workspace    device memory, used only with SP_Y_DK, else ignored; NULL or
+ *                workspace_bytes >= sp_sddmm_general_workspace(k, d, batch,
+ *                stride_y) and 256-byte aligned (otherwise
+ *                SP_ERROR_INVALID_VALUE).  With a workspace, Y is first
+ *                transposed into it (one k x d copy per batch entry, or one
+ *                shared copy when stride_y = 0) and the SP_Y_KD kernels run on
+ *                that copy: the same results bit for bit as SP_Y_KD on the
+ *                caller's own transpose.  Without one, SP_Y_DK gathers single
+ *                elements along rows of Y, several times slower.  The
+ *                workspace is the caller's; its contents after the call are
+ *                unspecified, and calls that share one on overlapping streams
+ *                race.
  * Everything else as sp_sddmm_batched, which is this call with mask_values =
- * NULL, y_layout = SP_Y_KD and beta = 0.  Each output's dot product is summed
- * in l order per entry; deterministic run to run. */
+ * NULL, y_layout = SP_Y_KD, beta = 0 and no workspace.  Each output's dot
+ * product is summed in l order per entry; deterministic run to run. */
 sp_status_t sp_sddmm_general(int m, int k, int d, int nnz, const int *row_indices,
                              const int *row_offsets, const int *col_indices,
                              const float *mask_values, const float *x, const float *y,
                              int y_layout, float alpha, float beta, float *out, int batch,
                              long long stride_values, long long stride_x,
-                             long long stride_y, long long stride_out,
-                             sp_stream_t stream);
+                             long long stride_y, long long stride_out, void *workspace,
+                             size_t workspace_bytes, sp_stream_t stream);
+
+/* Workspace bytes sp_sddmm_general needs to transpose a d x k Y:
+ * k * d * 4 per batch entry, or once when stride_y = 0.  Host-only; negative
+ * arguments or a NULL `bytes` return SP_ERROR_INVALID_VALUE. */
+sp_status_t sp_sddmm_general_workspace(int k, int d, int batch, long long stride_y,
+                                       size_t *bytes);
 
 /* ------------------------------------------------------------------------
  * Mixed precision (fp16/bf16 operands, fp32 arithmetic).  The card's kernels

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 22, declared
+    assert len(declared) == 23, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -205,9 +205,9 @@ def test_sddmm_general_validation(lib):
     fl = ctypes.c_float
 
     def call(m=4, k=4, d=4, nnz=8, ro=FAKE, ci=FAKE, mv=NULL, x=FAKE, y=FAKE, layout=0,
-             out=FAKE, batch=1, sv=0, sx=0, sy=0, so=0):
+             out=FAKE, batch=1, sv=0, sx=0, sy=0, so=0, ws=NULL, wb=0):
         return f(m, k, d, nnz, NULL, ro, ci, mv, x, y, layout, fl(1.0), fl(0.5), out, batch,
-                 sv, sx, sy, so, s)
+                 sv, sx, sy, so, ws, wb, s)
 
     assert call(layout=2) == INVALID
     assert call(layout=-1) == INVALID
@@ -226,6 +226,25 @@ def test_sddmm_general_validation(lib):
     assert call(m=0, ro=NULL, ci=NULL, x=NULL, y=NULL, out=NULL) == OK
     assert call(nnz=0, ci=NULL, out=NULL, layout=1) == OK
     assert call(batch=0) == OK
+    # a workspace for the d x k layout: at least k*d*4 bytes per batch entry
+    # (one copy when stride_y is 0), 256-byte aligned
+    ws = ctypes.c_void_p(0x100000)
+    assert call(layout=1, ws=ws, wb=63) == INVALID
+    assert call(layout=1, ws=ctypes.c_void_p(0x100040), wb=1 << 20) == INVALID
+    assert call(layout=1, batch=2, sx=16, sy=16, so=8, ws=ws, wb=64) == INVALID
+    assert call(layout=1, batch=0, ws=ws, wb=0) == OK
+
+
+def test_sddmm_general_workspace_query(lib):
+    q = lib.sp_sddmm_general_workspace
+    size = ctypes.c_size_t(0)
+    assert q(300, 24, 1, 0, ctypes.byref(size)) == OK and size.value == 300 * 24 * 4
+    assert q(300, 24, 5, 0, ctypes.byref(size)) == OK and size.value == 300 * 24 * 4
+    assert q(300, 24, 5, 7200, ctypes.byref(size)) == OK and size.value == 5 * 300 * 24 * 4
+    assert q(0, 24, 5, 7200, ctypes.byref(size)) == OK and size.value == 0
+    assert q(-1, 24, 1, 0, ctypes.byref(size)) == INVALID
+    assert q(3, 24, 1, -2, ctypes.byref(size)) == INVALID
+    assert q(3, 24, 1, 0, None) == INVALID
 
 
 def test_sddmm_validation(lib):

@@ -40,10 +40,11 @@ def test_graph_of_every_launch_kind():
     t_ri = torch.empty(k, dtype=torch.int32, device="cuda")
     outs = {name: torch.empty(shape, device="cuda") for name, shape in {
         "c": (m, n), "c_bal": (m, n), "c_bf16": (m, n), "dx": (k, n), "s": (nnz,),
-        "s_gen": (nnz,), "s_dk": (nnz,), "p": (nnz,), "att": (m, d), "c_pair": (m, n),
+        "s_gen": (nnz,), "s_dk": (nnz,), "s_dkw": (nnz,), "p": (nnz,), "att": (m, d), "c_pair": (m, n),
         "s_pair": (nnz,)}.items()}
     b16, v16 = b.to(torch.bfloat16), vals.to(torch.bfloat16)
     y_dk = y.t().contiguous()
+    y_ws = torch.empty(sp.sp_sddmm_general_workspace(k, d), dtype=torch.uint8, device="cuda")
     dy = dev(inputs.random_dense(951, m, n))
 
     def work():
@@ -57,6 +58,8 @@ def test_graph_of_every_launch_kind():
                             outs["s_gen"])
         sp.sp_sddmm_general(m, k, d, nnz, ri, ro, cols, None, x, y_dk, sp.SP_Y_DK, 1.0, 0.0,
                             outs["s_dk"])
+        sp.sp_sddmm_general(m, k, d, nnz, ri, ro, cols, vals, x, y_dk, sp.SP_Y_DK, 1.0, 0.0,
+                            outs["s_dkw"], workspace=y_ws)
         sp.sp_sddmm_softmax(m, k, d, nnz, ri, ro, cols, x, y, 0.0625, outs["p"])
         sp.sp_csr_row_softmax(m, nnz, ri, ro, outs["s"], outs["s"])
         sp.sp_sparse_attention(m, m, d, nnz, ri, ro, cols, x, x, x, 0.0625, outs["att"])

@@ -50,7 +50,9 @@ SIGNATURES = {
                           _c_float, _vp, _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
     "sp_sddmm_general": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                           _c_int, _c_float, _c_float, _vp, _c_int, _c_ll, _c_ll, _c_ll,
-                          _c_ll, _vp], _c_int),
+                          _c_ll, _vp, ctypes.c_size_t, _vp], _c_int),
+    "sp_sddmm_general_workspace": ([_c_int, _c_int, _c_int, _c_ll,
+                                    ctypes.POINTER(ctypes.c_size_t)], _c_int),
     "sp_csr_row_softmax": ([_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_ll, _c_ll, _vp],
                            _c_int),
     "sp_csr_transpose_workspace": ([_c_int, _c_int, _c_int, ctypes.POINTER(ctypes.c_size_t)],
@@ -218,14 +220,25 @@ def sp_sddmm_batched(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, 
 
 def sp_sddmm_general(m, k, d, nnz, row_indices, row_offsets, col_indices, mask_values, x, y,
                      y_layout, alpha, beta, out, batch=1, stride_values=0, stride_x=0,
-                     stride_y=0, stride_out=0, stream=None):
+                     stride_y=0, stride_out=0, workspace=None, stream=None):
+    """workspace: None, or a uint8 device tensor of at least
+    sp_sddmm_general_workspace bytes (used with SP_Y_DK only)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().sp_sddmm_general(
         m, k, d, nnz, _ptr(row_indices, _I32, "row_indices", True),
         _ptr(row_offsets, _I32, "row_offsets"), _ptr(col_indices, _I32, "col_indices", True),
         _ptr(mask_values, _F32, "mask_values", True), _ptr(x, _F32, "x", True),
         _ptr(y, _F32, "y", True), int(y_layout), float(alpha), float(beta),
         _ptr(out, _F32, "out", True), batch, stride_values, stride_x, stride_y, stride_out,
-        _stream(stream)), "sp_sddmm_general")
+        _ptr(workspace, _U8, "workspace", True), ws_bytes, _stream(stream)),
+        "sp_sddmm_general")
+
+
+def sp_sddmm_general_workspace(k, d, batch=1, stride_y=0) -> int:
+    size = ctypes.c_size_t(0)
+    _check(lib().sp_sddmm_general_workspace(k, d, batch, stride_y, ctypes.byref(size)),
+           "sp_sddmm_general_workspace")
+    return size.value
 
 
 def sp_csr_transpose_workspace(m, k, nnz) -> int:

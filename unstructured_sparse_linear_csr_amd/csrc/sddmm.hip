@@ -77,6 +77,57 @@ __global__ __launch_bounds__(kWave) void sddmm_cols_kernel(SddmmParams p)
     }
 }
 
+// out_z = in_z^T for a rows x cols matrix in_z (row-major, z = blockIdx.z):
+// 32 x 32 tiles through LDS (one padding column, so the transposed reads hit
+// distinct banks), 256 threads reading 4 rows each.  (c_base, r_base) is the
+// first tile's corner, so that grids too large for one launch can be split.
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in, E *__restrict__ out,
+                                                        int rows, int cols, int r_base, int c_base,
+                                                        long long stride_in, long long stride_out)
+{
+    constexpr int kT = 32;
+    __shared__ E tile[kT][kT + 1];
+    const E *iz = in + blockIdx.z * stride_in;
+    E *oz = out + blockIdx.z * stride_out;
+    const int c0 = c_base + (int)blockIdx.x * kT, r0 = r_base + (int)blockIdx.y * kT;
+    const int tx = threadIdx.x % kT, ty = threadIdx.x / kT;  // ty in [0, 8)
+#pragma unroll
+    for (int i = 0; i < kT; i += 8) {
+        const int r = r0 + ty + i, c = c0 + tx;
+        if (r < rows && c < cols) tile[ty + i][tx] = iz[(size_t)r * cols + c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kT; i += 8) {
+        const int c = c0 + ty + i, r = r0 + tx;  // out row c, column r
+        if (c < cols && r < rows) oz[(size_t)c * rows + r] = tile[tx][ty + i];
+    }
+}
+
+template <typename E>
+hipError_t launch_transpose(const void *in, void *out, int rows, int cols, long long stride_in,
+                            long long stride_out, int batch, hipStream_t s)
+{
+    // Tiles per launch in each dimension: x, y and z stay within the grid limits.
+    constexpr long long kMaxX = 1LL << 20, kMaxYZ = 65535;
+    const long long tx = (cols + 31) / 32, ty = (rows + 31) / 32;
+    for (long long z0 = 0; z0 < batch; z0 += kMaxYZ)
+        for (long long y0 = 0; y0 < ty; y0 += kMaxYZ)
+            for (long long x0 = 0; x0 < tx; x0 += kMaxX) {
+                const dim3 grid((unsigned)std::min(kMaxX, tx - x0),
+                                (unsigned)std::min(kMaxYZ, ty - y0),
+                                (unsigned)std::min(kMaxYZ, (long long)batch - z0));
+                hipLaunchKernelGGL((transpose_kernel<E>), grid, dim3(256), 0, s,
+                                   static_cast<const E *>(in) + z0 * stride_in,
+                                   static_cast<E *>(out) + z0 * stride_out, rows, cols,
+                                   (int)(y0 * 32), (int)(x0 * 32), stride_in, stride_out);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
+    return hipSuccess;
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float *dst, long long count,
                                                         long long stride)
 {
@@ -163,6 +214,9 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
     plan->kind = SddmmPlan::kNothing;
     plan->dtype = a.dtype;
     plan->softmax = false;
+    plan->t_src = nullptr;
+    plan->t_src_stride = 0;
+    plan->t_batch = 0;
     if (a.m == 0 || a.nnz == 0) return hipSuccess;
     if (xcd_grid(a.batch, a.m) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     SddmmParams &p = plan->p;
@@ -190,17 +244,26 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
     const bool buf = (long long)a.k * (long long)a.d * eb <= (1LL << 31);
     p.y_bytes = buf ? (unsigned)((long long)a.k * a.d * eb) : 0u;
     plan->buf = buf;
-    if (a.y_layout == 1) {
+    if (a.y_layout == 1 && a.workspace == nullptr) {
         plan->kind = SddmmPlan::kCols;
         return hipSuccess;
+    }
+    if (a.y_layout == 1) {
+        // Y^T (k x d per batch entry, or one shared copy) into the workspace,
+        // then the k x d kernels on it.
+        plan->t_src = a.y;
+        plan->t_src_stride = a.stride_y;
+        plan->t_batch = a.stride_y == 0 ? 1 : a.batch;
+        p.y = a.workspace;
+        p.stride_y = a.stride_y == 0 ? 0 : (long long)a.k * a.d;
     }
     plan->softmax = a.softmax;
     if (a.d == 0 && a.mask_values == nullptr && a.beta == 0.f && !a.softmax) {
         plan->kind = SddmmPlan::kFill;
         return hipSuccess;
     }
-    const bool vec = (a.d % vlen == 0) && aligned16(a.x) && aligned16(a.y) &&
-                     (a.stride_x % vlen == 0) && (a.stride_y % vlen == 0);
+    const bool vec = (a.d % vlen == 0) && aligned16(a.x) && aligned16(p.y) &&
+                     (a.stride_x % vlen == 0) && (p.stride_y % vlen == 0);
     // Register-resident X and buffer gathers need valid offsets below Y's size
     // and padding offsets (>= 2^31) beyond it.
     const int kvec = vec ? vlen : 1;
@@ -219,14 +282,31 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
 hipError_t run_sddmm(const SddmmPlan &plan, hipStream_t stream)
 {
     const SddmmParams &p = plan.p;
+    if (plan.t_src != nullptr && p.d > 0 && p.k > 0) {
+        const long long stride_out = (long long)p.k * p.d;
+        const hipError_t e =
+            plan.dtype == Dtype::f32
+                ? launch_transpose<float>(plan.t_src, const_cast<void *>(p.y), p.d, p.k,
+                                          plan.t_src_stride, stride_out, plan.t_batch, stream)
+                : launch_transpose<unsigned short>(plan.t_src, const_cast<void *>(p.y), p.d,
+                                                   p.k, plan.t_src_stride, stride_out,
+                                                   plan.t_batch, stream);
+        if (e != hipSuccess) return e;
+    }
     switch (plan.kind) {
     case SddmmPlan::kNothing:
         return hipSuccess;
     case SddmmPlan::kFill: {
         const long long blocks = std::min<long long>((p.nnz + 255) / 256, 65536);
-        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks, (unsigned)p.batch),
-                           dim3(256), 0, stream, p.out, (long long)p.nnz, p.stride_out);
-        return hipGetLastError();
+        for (long long z0 = 0; z0 < p.batch; z0 += 65535) {  // batch entries on grid y
+            const long long nz = std::min<long long>(65535, p.batch - z0);
+            hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks, (unsigned)nz), dim3(256),
+                               0, stream, p.out + z0 * p.stride_out, (long long)p.nnz,
+                               p.stride_out);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
     }
     case SddmmPlan::kCols:
         switch (plan.dtype) {

@@ -32,6 +32,14 @@ bool dtype_of(int code, spk::Dtype *out)
     }
 }
 
+// Bytes for the k x d transpose of Y (one per batch entry, or one shared).
+size_t sddmm_workspace_bytes(int k, int d, int batch, long long stride_y, spk::Dtype dtype)
+{
+    const size_t copies = stride_y == 0 ? 1 : (size_t)(batch > 0 ? batch : 0);
+    const size_t eb = dtype == spk::Dtype::f32 ? 4 : 2;
+    return copies * (size_t)(k > 0 ? k : 0) * (size_t)(d > 0 ? d : 0) * eb;
+}
+
 // Checks an SDDMM's arguments and fills `a`; *work is false when there is
 // nothing to launch.
 sp_status_t sddmm_prepare(int m, int k, int d, int nnz, const int *row_indices,
@@ -40,7 +48,7 @@ sp_status_t sddmm_prepare(int m, int k, int d, int nnz, const int *row_indices,
                           const void *y, int y_layout, float alpha, float beta, float *out,
                           int batch, long long stride_values, long long stride_x,
                           long long stride_y, long long stride_out, spk::SddmmArgs *args,
-                          bool *work)
+                          bool *work, void *workspace = nullptr, size_t workspace_bytes = 0)
 {
     *work = false;
     if (m < 0 || k < 0 || d < 0 || nnz < 0 || batch < 0 || stride_values < 0 ||
@@ -73,6 +81,12 @@ sp_status_t sddmm_prepare(int m, int k, int d, int nnz, const int *row_indices,
     a.stride_y = stride_y;
     a.stride_out = stride_out;
     a.dtype = dtype;
+    if (y_layout == SP_Y_DK && workspace != nullptr) {
+        if (workspace_bytes < sddmm_workspace_bytes(k, d, batch, stride_y, dtype) ||
+            reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+            return SP_ERROR_INVALID_VALUE;
+        a.workspace = workspace;
+    }
     *work = true;
     return SP_SUCCESS;
 }
@@ -82,14 +96,15 @@ sp_status_t sddmm_any(int m, int k, int d, int nnz, const int *row_indices,
                       const float *mask_values, spk::Dtype dtype, const void *x, const void *y,
                       int y_layout, float alpha, float beta, float *out, int batch,
                       long long stride_values, long long stride_x, long long stride_y,
-                      long long stride_out, sp_stream_t stream)
+                      long long stride_out, sp_stream_t stream, void *workspace = nullptr,
+                      size_t workspace_bytes = 0)
 {
     spk::SddmmArgs a;
     bool work = false;
     const sp_status_t st = sddmm_prepare(m, k, d, nnz, row_indices, row_offsets, col_indices,
                                          mask_values, dtype, x, y, y_layout, alpha, beta, out,
                                          batch, stride_values, stride_x, stride_y, stride_out,
-                                         &a, &work);
+                                         &a, &work, workspace, workspace_bytes);
     if (st != SP_SUCCESS || !work) return st;
     return from_hip(spk::launch_sddmm(a, as_stream(stream)));
 }
@@ -270,16 +285,26 @@ sp_status_t sp_spmm(int m, int k, int n, int nnz, const int *row_indices,
                            col_indices, b, c, 1, 0, 0, 0, stream);
 }
 
+sp_status_t sp_sddmm_general_workspace(int k, int d, int batch, long long stride_y,
+                                       size_t *bytes)
+{
+    if (k < 0 || d < 0 || batch < 0 || stride_y < 0 || bytes == nullptr)
+        return SP_ERROR_INVALID_VALUE;
+    *bytes = sddmm_workspace_bytes(k, d, batch, stride_y, spk::Dtype::f32);
+    return SP_SUCCESS;
+}
+
 sp_status_t sp_sddmm_general(int m, int k, int d, int nnz, const int *row_indices,
                              const int *row_offsets, const int *col_indices,
                              const float *mask_values, const float *x, const float *y,
                              int y_layout, float alpha, float beta, float *out, int batch,
                              long long stride_values, long long stride_x,
-                             long long stride_y, long long stride_out, sp_stream_t stream)
+                             long long stride_y, long long stride_out, void *workspace,
+                             size_t workspace_bytes, sp_stream_t stream)
 {
     return sddmm_any(m, k, d, nnz, row_indices, row_offsets, col_indices, mask_values,
                      spk::Dtype::f32, x, y, y_layout, alpha, beta, out, batch, stride_values,
-                     stride_x, stride_y, stride_out, stream);
+                     stride_x, stride_y, stride_out, stream, workspace, workspace_bytes);
 }
 
 sp_status_t sp_sddmm_softmax(int m, int k, int d, int nnz, const int *row_indices,
@@ -359,7 +384,7 @@ sp_status_t sp_sddmm_batched(int m, int k, int d, int nnz, const int *row_indice
 {
     return sp_sddmm_general(m, k, d, nnz, row_indices, row_offsets, col_indices, nullptr, x,
                             y, SP_Y_KD, alpha, 0.f, out, batch, 0, stride_x, stride_y,
-                            stride_out, stream);
+                            stride_out, nullptr, 0, stream);
 }
 
 sp_status_t sp_sddmm(int m, int k, int d, int nnz, const int *row_indices,

@@ -25,6 +25,10 @@ struct SddmmPlan {
     bool vec, buf;
     bool softmax;  // rows kernel: row softmax of the scores before they are written
     int g, nv;     // rows kernel: lanes per entry, vectors per lane (0: generic loop)
+    // Y stored d x k with a workspace: transpose it into p.y first
+    const void *t_src;        // NULL: no transpose
+    long long t_src_stride;   // elements between batch entries of the d x k source
+    int t_batch;              // source operands to transpose (1 when shared)
 };
 
 // hipErrorInvalidConfiguration when the grid would exceed the launch limits.
