@@ -302,6 +302,25 @@ def test_spmm_lds_resident_b(n):
     assert np.array_equal(c1.view(np.int32), ref1.astype(np.float32).view(np.int32))
 
 
+@pytest.mark.parametrize("k,n,m", [(8192, 8, 16384), (8192, 12, 10000), (8192, 16, 8000),
+                                   (3000, 12, 12000), (16384, 3, 16384), (5000, 8, 10000)])
+def test_spmm_lds_column_slices(k, n, m):
+    # Narrow B too large for LDS whole, with enough entries per CU: the
+    # streaming kernel over column slices of B (2-4 slices, one uneven: 8 + 4
+    # columns; the scalar path's 2 + 1), every entry checked.
+    lengths = np.random.default_rng(84 + n + k).integers(250, 360, m).astype(np.int32)
+    lengths[::89] = 0
+    lengths[-1] += (3 - int(lengths.sum()) % 4) % 4   # last CSR segment past nnz
+    assert int(lengths.sum()) % 4 == 3 and lengths[-1] > 0
+    a = csr_of_row_lists(inputs.random_row_lists(85 + n + k, m, k, lengths))
+    b = inputs.random_dense(86 + n + k, k, n)
+    note(f"spmm lds column slices k={k} n={n} m={m} nnz={a.nnz}")
+    c = run_spmm(a, b, row_indices=swizzle(a))
+    ref, s = oracle.spmm(m, k, n, a.ro, a.ci, a.vals, b)
+    check_close(c, ref, s, f"spmm lds slices k={k} n={n}")
+    assert np.all(c[lengths == 0] == 0)
+
+
 def test_spmm_hbm_stream_n4_sampled_rows():
     w = inputs.hbm_stream(n=4)
     a = csr_of_row_lists(w["a"])

@@ -194,7 +194,12 @@ __global__ __launch_bounds__(kWave) void spmm_narrow_kernel(SpmmParams p)
 // regime, where the CSR arrays (8 bytes per entry) are the traffic that must
 // reach HBM speed.  One 1024-thread workgroup per CU copies B into LDS once;
 // its 16 waves then take rows (in row_indices order, round-robin over all
-// waves of the launch).  Lanes split a row's entries in 16-byte segments of 4
+// waves of the launch).  When all of B does not fit, B is cut into S column
+// slices that do: the grid is S groups of workgroups, each holding one slice
+// and taking every row for that slice's columns of C, and the S workgroups
+// that take the same rows are launched on the same XCD (block ids 8 apart)
+// at the same time, so the second and later reads of those rows' CSR entries
+// come from that XCD's L2 rather than HBM.  Lanes split a row's entries in 16-byte segments of 4
 // (lane (s, v): segments s, s + kS, ...; the kE lanes of a segment cover the
 // kE column vectors of B), and each segment's column indices and values are
 // read with one dwordx4 buffer load each, starting from the row's first entry
@@ -205,8 +210,12 @@ __global__ __launch_bounds__(kWave) void spmm_narrow_kernel(SpmmParams p)
 // its (row, batch) pairs as one sequence, and the metadata of its next 64 rows
 // sits one row per lane in registers (read with readlane), so a row change
 // costs no memory operation.  The array's last segment, if it extends past
-// nnz, is read from the last 4 entries instead and shifted into place, so no
-// load is ever partly out of range.
+// nnz, is read from the last 4 entries instead (positions before the segment's
+// first entry are skipped), so no load is ever partly out of range.  A zero
+// vector stored after B in LDS
+// stands in for the entries of a segment that lie outside the row (with value
+// 0): every entry slot is one unconditional LDS read and FMA, adding +0
+// exactly, with no branch, so a batch's reads are all issued before its FMAs.
 constexpr int kLdsThreads = 1024;
 constexpr int kLdsWaves = kLdsThreads / kWave;
 constexpr unsigned kLdsMaxB = 128u * 1024u;
@@ -221,15 +230,32 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
     constexpr int kBatch = kSteps * kS * 4;  // entries per batch
     extern __shared__ __align__(16) float s_b[];
 
-    // ---- B into LDS
+    // ---- this workgroup's slice and row group
+    const int n_slices = p.lds_slices;
+    const int groups = (int)gridDim.x / n_slices;
+    int slice = 0, group = (int)blockIdx.x;
+    if (n_slices > 1) {  // gridDim.x is a multiple of 8 * n_slices
+        slice = (int)(blockIdx.x / 8) % n_slices;
+        group = (int)(blockIdx.x / (8 * n_slices)) * 8 + (int)(blockIdx.x % 8);
+    }
+    const int col_base = slice * p.lds_slice_n;
+    const int width = min(p.lds_slice_n, p.n - col_base);  // columns of this slice
+    const int wv = width / kVec;                            // vectors per B row in LDS
+
+    // ---- B's slice into LDS, k x width row-major
     const int tid = threadIdx.x;
-    const int nb = (int)(p.b_bytes / 4u);
-    if constexpr (kVec == 4) {
-        const float4 *b4 = reinterpret_cast<const float4 *>(p.b);
-        for (int i = tid; i < nb / 4; i += kLdsThreads)
-            reinterpret_cast<float4 *>(s_b)[i] = b4[i];
+    const VecT *__restrict__ bsrc = static_cast<const VecT *>(p.b);
+    VecT *s_bv = reinterpret_cast<VecT *>(s_b);
+    const int total = p.k * wv;
+    if (tid == 0) s_bv[total] = VecT{};  // the zero vector
+    if (n_slices == 1) {
+        for (int i = tid; i < total; i += kLdsThreads) s_bv[i] = bsrc[i];
     } else {
-        for (int i = tid; i < nb; i += kLdsThreads) s_b[i] = static_cast<const float *>(p.b)[i];
+        const int nv_all = p.n / kVec, vbase = col_base / kVec;
+        for (int i = tid; i < total; i += kLdsThreads) {
+            const int r = i / wv;
+            s_bv[i] = bsrc[(size_t)r * nv_all + vbase + (i - r * wv)];
+        }
     }
     __syncthreads();
 
@@ -237,7 +263,7 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
     const int s = lane / kE;
     const int v = lane - s * kE;
     const int col0 = v * kVec;
-    const bool col_ok = col0 < p.n;
+    const bool col_ok = col0 < width;
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int *>(p.col_indices), 0, (int)p.csr_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -246,9 +272,9 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
 
     const int *__restrict__ order = p.row_indices;
     const int *__restrict__ offsets = p.row_offsets;
-    float *__restrict__ c_out = p.c;
-    const int stride = gridDim.x * kLdsWaves;
-    const int first = blockIdx.x * kLdsWaves + tid / kWave;
+    float *__restrict__ c_out = p.c + col_base;
+    const int stride = groups * kLdsWaves;
+    const int first = group * kLdsWaves + tid / kWave;
     if (first >= p.m) return;  // no LDS barrier follows
     const int rows_of_wave = (p.m - first + stride - 1) / stride;
 
@@ -297,32 +323,39 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
                                   __uint_as_float(v4[2]), __uint_as_float(v4[3]));
         }
     };
+    const unsigned row_bytes = (unsigned)wv * sizeof(VecT);   // one row of B in LDS
+    const unsigned lane_bytes = (unsigned)v * sizeof(VecT);
+    const unsigned zero_bytes = (unsigned)total * sizeof(VecT);
     auto consume = [&](const Batch &b, const Seg (&sg)[kSteps], float *acc) {
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
             const int e = b.base + (u * kS + s) * 4;
-            // entry e + t sits at position t + sh of the loaded segment
-            const int sh = e + 4 <= p.nnz ? 0 : e - last4;
+            // The segment was loaded from entry e_ld: e, or last4 for the
+            // array's final segment (whose positions before e belong to the
+            // segment before it).  Position t holds entry e_ld + t, which is
+            // this lane's when lo <= e_ld + t < p1 with lo = max(p0, e); an
+            // idle lane (no column vector) takes none.
+            const int e_ld = e + 4 <= p.nnz ? e : last4;
+            const int lo = max(b.p0, e);
+            const unsigned span = (col_ok && b.p1 > lo) ? (unsigned)(b.p1 - lo) : 0u;
+            const int d = e_ld - lo;
+            const char *s_bytes = reinterpret_cast<const char *>(s_bv);
             const int cs[4] = {sg[u].c.x, sg[u].c.y, sg[u].c.z, sg[u].c.w};
             const float vs[4] = {sg[u].v.x, sg[u].v.y, sg[u].v.z, sg[u].v.w};
+            VecT bv[4];
+            float val[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const int idx = e + t;
-                if (idx >= b.p0 && idx < b.p1 && col_ok) {
-                    int col = cs[t];
-                    float val = vs[t];
-                    if (sh != 0) {  // only the array's final, shifted segment
-                        const int q = t + sh;
-                        col = q == 1 ? cs[1] : q == 2 ? cs[2] : cs[3];
-                        val = q == 1 ? vs[1] : q == 2 ? vs[2] : vs[3];
-                    }
-                    // Row col of B, this lane's vector: indexed in units of
-                    // the vector so the compiler knows it is 16-byte aligned
-                    // (one ds_read_b128, not two 8-byte reads).
-                    const VecT bv = reinterpret_cast<const VecT *>(s_b)[col * (p.n / kVec) + v];
-                    V::fma(val, bv, acc);
-                }
+                const bool in_row = (unsigned)(d + t) < span;
+                // Byte offset of row col of B, this lane's vector (or of the
+                // zero vector); 16-byte aligned, so the read is one ds_read_b128.
+                const unsigned off =
+                    in_row ? __umul24((unsigned)cs[t], row_bytes) + lane_bytes : zero_bytes;
+                val[t] = in_row ? vs[t] : 0.f;
+                bv[t] = *reinterpret_cast<const VecT *>(s_bytes + off);
             }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) V::fma(val[t], bv[t], acc);
         }
     };
     float acc[kVec];
@@ -368,10 +401,12 @@ hipError_t launch_lds_t(const SpmmParams &p, int blocks, hipStream_t s)
 {
     hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&spmm_lds_kernel<kE, kVec>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMaxB);
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsMaxB + 16u));
     if (e != hipSuccess) return e;
+    // B's slice and the zero vector
+    const size_t lds_bytes = ((size_t)p.k * (size_t)p.lds_slice_n + kVec) * 4u;
     hipLaunchKernelGGL((spmm_lds_kernel<kE, kVec>), dim3(blocks), dim3(kLdsThreads),
-                       p.b_bytes, s, p);
+                       lds_bytes, s, p);
     return hipGetLastError();
 }
 
@@ -507,6 +542,9 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
     p.batch = a.batch;
     p.b_bytes = buf ? (unsigned)((long long)a.k * a.n * eb) : 0u;
     p.csr_bytes = narrow ? (unsigned)((long long)a.nnz * 4) : 0u;
+    p.k = a.k;
+    p.lds_slices = 1;
+    p.lds_slice_n = a.n;
     p.row_indices = a.row_indices;
     p.row_offsets = a.row_offsets;
     p.col_indices = a.col_indices;
@@ -540,14 +578,27 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
             hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock,
                                   device) != hipSuccess)
             cus = 0;
-        const long long b_elems = (long long)a.k * a.n;
-        if (a.batch == 1 && cus > 0 && vec_csr && a.nnz >= 4 &&
-            b_elems * 4 <= (long long)kLdsMaxB &&
-            b_elems * 4 <= (long long)lds_max &&
-            (long long)a.nnz >= (long long)cus * b_elems) {
+        // B, or when it does not fit, S column slices of B: the widest
+        // slice (in vectors of kvec columns) that fits, then the S slices
+        // evened out.  Every group of S workgroups (one per CU) must stream at
+        // least as many entries as each copies B elements: nnz >= (CUs / S)
+        // * k * slice columns.
+        const long long lds_cap = std::min<long long>(kLdsMaxB, lds_max - 16);
+        const long long row_bytes = (long long)a.k * kvec * 4;  // one vector column of B
+        long long slice_v = row_bytes > 0 ? std::min<long long>(nv, lds_cap / row_bytes) : 0;
+        const int slices = slice_v > 0 ? (int)((nv + slice_v - 1) / slice_v) : 0;
+        if (slices > 0) slice_v = (nv + slices - 1) / slices;
+        const int groups = slices > 1 ? cus / slices / 8 * 8 : cus;
+        if (a.batch == 1 && cus > 0 && vec_csr && a.nnz >= 4 && slices > 0 && groups > 0 &&
+            (long long)a.nnz >= (long long)groups * a.k * slice_v * kvec) {
             const long long want = ((long long)a.m + kLdsWaves - 1) / kLdsWaves;
+            long long g = want < groups ? want : groups;
+            if (slices > 1) g = (g + 7) / 8 * 8;  // whole XCD rounds
             plan->kind = SpmmPlan::kLds;
-            plan->blocks = (int)(want < cus ? want : cus);
+            plan->blocks = (int)(g * slices);
+            plan->e = slice_v <= 1 ? 1 : slice_v <= 2 ? 2 : 4;
+            p.lds_slices = slices;
+            p.lds_slice_n = (int)(slice_v * kvec);
         }
     }
     return hipSuccess;
