@@ -9,7 +9,7 @@
 namespace spk {
 
 struct SpmmPlan {
-    enum Kind { kWide, kNarrow, kLds, kBalanced } kind;
+    enum Kind { kWide, kNarrow, kLds, kBalanced, kSplit } kind;
     spmm_detail::SpmmParams p;
     Dtype dtype;
     bool vec, vec_csr, buf;

@@ -115,6 +115,71 @@ __global__ __launch_bounds__(kBalWaves * kWave) void spmm_balanced_kernel(SpmmPa
     V::store(cz + (size_t)row * (size_t)p.n + col0, acc);
 }
 
+// Few, long rows: the wide launch would leave most SIMDs with one wave or
+// none.  Each row's entries are cut into kSplitWaves equal parts, taken by the
+// kSplitWaves waves of a workgroup (each wave laid out as the wide kernel,
+// kLpr lanes per row, over its part); wave 0 then adds the parts' partial
+// sums in part order from LDS and writes the rows.  Summation: entry order
+// within a part, parts in order; deterministic.
+constexpr int kSplitWaves = 4;
+constexpr int kSplitMinLength = 256;  // mean entries per row for the split kernel
+constexpr int kSimdsPerCu = 4;
+
+template <typename E, int kLpr, int kVec>
+__global__ __launch_bounds__(kSplitWaves * kWave) void spmm_split_kernel(SpmmParams p)
+{
+    using V = GVec<E, kVec>;
+    constexpr int kRpw = kWave / kLpr;
+    constexpr int kChunk = kEpl * kLpr;
+    constexpr int kPitch = kChunk + kU + 4;
+    __shared__ __align__(16) int s_off[kSplitWaves * kRpw * kPitch];
+    __shared__ __align__(16) float s_val[kSplitWaves * kRpw * kPitch];
+    __shared__ __align__(16) float s_part[kSplitWaves][kWave * kVec];
+
+    const long long w = wide_work(p, blockIdx.x);
+    if (w < 0) return;  // uniform over the workgroup
+    const long long per_z = (long long)p.tiles * p.row_blocks;
+    const long long z = w / per_z;
+    const int tile = (int)((w - z * per_z) / p.row_blocks);
+    const int rb = (int)(w - z * per_z - (long long)tile * p.row_blocks);
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x - wave * kWave;
+    const int grp = kRpw == 1 ? 0 : lane / kLpr;
+    const int gl = kRpw == 1 ? lane : lane - grp * kLpr;
+    const E *__restrict__ vals = static_cast<const E *>(p.values) + z * p.stride_values;
+    const E *__restrict__ bz = static_cast<const E *>(p.b) + z * p.stride_b;
+
+    const int slot = rb * kRpw + grp;
+    const bool has_row = slot < p.m;
+    const int row = has_row ? (p.row_indices ? p.row_indices[slot] : slot) : 0;
+    const int p0 = has_row ? p.row_offsets[row] : 0;
+    const int p1 = has_row ? p.row_offsets[row + 1] : 0;
+    const long long len = p1 - p0;
+    const int q0 = p0 + (int)(len * wave / kSplitWaves);
+    const int q1 = p0 + (int)(len * (wave + 1) / kSplitWaves);
+    const int col0 = (tile * kLpr + gl) * kVec;
+    const bool col_ok = col0 < p.n;
+    float acc[kVec];
+#pragma unroll
+    for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
+    wide_accumulate<E, kLpr, kVec, true, true, true>(p, vals, bz, q0, q1, gl, col0, col_ok,
+                                                     s_off + (wave * kRpw + grp) * kPitch,
+                                                     s_val + (wave * kRpw + grp) * kPitch, acc);
+#pragma unroll
+    for (int t = 0; t < kVec; ++t) s_part[wave][lane * kVec + t] = acc[t];
+    __syncthreads();
+    if (wave != 0 || !has_row || !col_ok) return;
+#pragma unroll
+    for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
+#pragma unroll
+    for (int v = 0; v < kSplitWaves; ++v) {
+#pragma unroll
+        for (int t = 0; t < kVec; ++t) acc[t] += s_part[v][lane * kVec + t];
+    }
+    float *cz = p.c + z * p.stride_c;
+    V::store(cz + (size_t)row * (size_t)p.n + col0, acc);
+}
+
 // Narrow B (n of at most 16 columns): the lane-over-columns mapping above
 // would leave most of a row group idle, so here the lanes of one wave split
 // a row's entries instead.  Lane (s, v) handles entries s, s + kS, s + 2kS, ...
@@ -478,6 +543,20 @@ hipError_t launch_wide(bool vec, int lpr, const SpmmParams &p, bool vec_csr, boo
 }
 
 template <typename E, int kVec>
+hipError_t launch_split(int lpr, const SpmmParams &p, hipStream_t s)
+{
+    const dim3 grid((unsigned)wide_grid(p));
+    const dim3 block(kSplitWaves * kWave);
+    switch (lpr) {
+    case 8: hipLaunchKernelGGL((spmm_split_kernel<E, 8, kVec>), grid, block, 0, s, p); break;
+    case 16: hipLaunchKernelGGL((spmm_split_kernel<E, 16, kVec>), grid, block, 0, s, p); break;
+    case 32: hipLaunchKernelGGL((spmm_split_kernel<E, 32, kVec>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((spmm_split_kernel<E, 64, kVec>), grid, block, 0, s, p); break;
+    }
+    return hipGetLastError();
+}
+
+template <typename E, int kVec>
 hipError_t launch_balanced(const SpmmParams &p, bool vec_csr, bool buf, hipStream_t s)
 {
     const dim3 grid((unsigned)xcd_grid((long long)p.batch * p.tiles, p.row_blocks));
@@ -566,6 +645,14 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
         // groups of kBalWaves rows in place of row blocks
         plan->kind = SpmmPlan::kBalanced;
         p.row_blocks = (int)(((long long)a.m + kBalWaves - 1) / kBalWaves);
+    } else if (vec_csr && buf && (long long)a.nnz >= kSplitMinLength * (long long)a.m) {
+        // Few, long rows: fewer than two waves per SIMD in the wide launch.
+        int cus = 0, device = 0;
+        if (hipGetDevice(&device) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) ==
+                hipSuccess &&
+            (long long)a.batch * tiles * row_blocks < 2LL * kSimdsPerCu * cus)
+            plan->kind = SpmmPlan::kSplit;
     }
     if (narrow) {
         plan->kind = SpmmPlan::kNarrow;
@@ -614,6 +701,18 @@ hipError_t run_spmm(const SpmmPlan &plan, hipStream_t stream)
     case SpmmPlan::kNarrow:
         return plan.vec ? launch_narrow<4>(plan.e, p, stream)
                         : launch_narrow<1>(plan.e, p, stream);
+    case SpmmPlan::kSplit:
+        switch (plan.dtype) {
+        case Dtype::f16:
+            return plan.vec ? launch_split<_Float16, 8>(plan.lpr, p, stream)
+                            : launch_split<_Float16, 1>(plan.lpr, p, stream);
+        case Dtype::bf16:
+            return plan.vec ? launch_split<bf16, 8>(plan.lpr, p, stream)
+                            : launch_split<bf16, 1>(plan.lpr, p, stream);
+        default:
+            return plan.vec ? launch_split<float, 4>(plan.lpr, p, stream)
+                            : launch_split<float, 1>(plan.lpr, p, stream);
+        }
     case SpmmPlan::kBalanced:
         switch (plan.dtype) {
         case Dtype::f16:
