@@ -42,11 +42,19 @@ STREAM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spmm_lds_hbm_stream_traffi
 CSRC = os.path.join(ROOT, "unstructured_sparse_linear_csr_amd", "csrc")
 
 
-def kernel_source_sha256() -> str:
-    """Hash of every kernel source file (names and contents, sorted)."""
+# The sources a measured launch is built from: its kernel's file, the files
+# whose variant selection sets its parameters, the entry points, and every
+# header.  A counter record stays valid while these hash the same.
+PAIR_SOURCES = ("fused.hip", "spmm.hip", "sddmm.hip", "sp_api.hip")
+STREAM_SOURCES = ("spmm.hip", "sp_api.hip")
+
+
+def kernel_source_sha256(sources=None) -> str:
+    """Hash of the named kernel source files plus every header (names and
+    contents, sorted); every .hip and .h file when `sources` is None."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
+        if name.endswith(".h") or (name.endswith(".hip") and (sources is None or name in sources)):
             h.update(name.encode())
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(f.read())
@@ -115,7 +123,7 @@ def traffic_record(path=TRAFFIC_FILE):
     try:
         with open(path) as f:
             rec = json.load(f)
-        sha = kernel_source_sha256()
+        sha = kernel_source_sha256(rec.get("kernel_sources"))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256") != sha:
