@@ -10,7 +10,7 @@ import oracle
 from unstructured_sparse_linear_csr_amd import binding as sp
 from unstructured_sparse_linear_csr_amd import inputs
 
-from gpu_util import dev, host, note
+from gpu_util import check_close, dev, host, note
 
 pytestmark = pytest.mark.gpu
 
@@ -21,6 +21,52 @@ def _device():
     sp.lib()
     yield
     torch.cuda.synchronize()
+
+
+def test_graph_of_long_row_and_sliced_launches():
+    """The row-split SpMM (few, long rows) and the streaming SpMM over column
+    slices of B held in LDS, captured and replayed the same way."""
+    m1, k1, n1 = 96, 4096, 128
+    lengths = np.random.default_rng(1300).integers(300, 3000, m1).astype(np.int32)
+    rl1 = inputs.random_row_lists(1301, m1, k1, lengths)
+    m2, k2, n2 = 16384, 8192, 8
+    rl2 = inputs.random_row_lists(1302, m2, k2,
+                                  np.random.default_rng(1303).integers(250, 360, m2).astype(np.int32))
+    args = []
+    for (m, k, n, rl, seed) in ((m1, k1, n1, rl1, 1304), (m2, k2, n2, rl2, 1305)):
+        ro = dev(oracle.csr_offsets_from_lengths(rl.lengths))
+        args.append((m, k, n, rl.nnz, ro, dev(rl.cols), dev(rl.values),
+                     dev(inputs.random_dense(seed, k, n)), torch.empty(m, n, device="cuda")))
+
+    def work():
+        for (m, k, n, nnz, ro, ci, v, b, c) in args:
+            sp.sp_spmm(m, k, n, nnz, None, v, ro, ci, b, c)
+
+    note("graph of split and sliced launches: eager reference")
+    work()
+    torch.cuda.synchronize()
+    want = [host(a[-1]).copy() for a in args]
+    ref, s = oracle.spmm(m1, k1, n1, oracle.csr_offsets_from_lengths(rl1.lengths), rl1.cols,
+                         rl1.values, host(args[0][7]))
+    check_close(want[0], ref, s, "split rows in the graph test")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(3):
+        note(f"split/sliced graph replay {rep}")
+        for a in args:
+            a[-1].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, w in zip(args, want):
+            assert np.array_equal(host(a[-1]).view(np.int32), w.view(np.int32)), rep
 
 
 def test_graph_of_every_launch_kind():

@@ -76,7 +76,10 @@ def test_transpose_hand_example():
 
 
 # Columns across 0 to 4 radix passes, nnz across one tile, several tiles and a
-# ragged last tile, empty rows and columns.
+# ragged last tile, empty rows and columns.  With k <= 16384 (and nnz <= 2^24)
+# the counting method runs instead: rows longer than its 2048-entry LDS piece,
+# k at its LDS limit, ranges of 1024 mostly empty rows, and k one past the
+# limit (the radix method again).
 CASES = [
     ("k1_no_pass", 281, 300, 1, 1),
     ("k2", 282, 500, 2, 2),
@@ -85,6 +88,10 @@ CASES = [
     ("k4096_ragged", 285, 333, 4096, 90),
     ("k70000_three_passes", 286, 3000, 70000, 40),
     ("tall", 287, 20000, 37, 20),
+    ("count_long_rows", 288, 6, 16000, 9000),
+    ("count_k16384", 289, 2500, 16384, 120),
+    ("count_sparse_rows", 290, 100000, 50, 1),
+    ("radix_k16385", 291, 2500, 16385, 120),
 ]
 
 

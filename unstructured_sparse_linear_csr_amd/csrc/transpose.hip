@@ -21,6 +21,24 @@
 // first position of each column), and a last pass writes each transposed
 // entry's row (the source entry's row, from an expanded row-id array), value
 // and source index.
+//
+// Counting method, for k <= kCountMaxK and nnz <= kCountMaxNnz (four
+// launches instead of three per radix pass plus three; FFN-sized problems).  The rows are cut into
+// ranges of S consecutive rows, and:
+//   rank    -- one wave per range walks its rows in order.  A row's entries
+//              have distinct columns, so each lane reads its column's running
+//              count (LDS) as the entry's rank among the range's entries of
+//              that column and advances it; the entry's row is recorded too.
+//              The range's per-column counts go to tbl[c * R + r].
+//   columns -- one wave per column: tbl[c * R + r] becomes the column's count
+//              over the ranges before r, and tot[c] its total.
+//   offsets -- one workgroup: t_row_offsets is the exclusive scan of tot.
+//   scatter -- entry p of column c in range r goes to position
+//              t_row_offsets[c] + tbl[c * R + r] + rank[p].
+// Within a column, ranges come in order and rows in order within a range, so
+// the positions are exactly the stable order of the radix method; no count
+// depends on the order of concurrent updates (LDS counters of one wave,
+// updated by distinct lanes for distinct columns).
 #include <algorithm>
 
 #include "sp_device.h"
@@ -194,6 +212,119 @@ __global__ __launch_bounds__(256) void gather_values_kernel(int nnz, const int *
     if (q < nnz) out[q] = in[perm[q]];
 }
 
+// ---- counting method
+constexpr int kCountMaxK = 16384;     // LDS counters of the rank kernel: 64 KiB
+constexpr int kCountMaxNnz = 1 << 18;
+constexpr long long kCountMaxTable = 1 << 18;  // R * k: the table is written column-major
+                                               // by range-major producers (scattered)
+constexpr int kRangeEntries = 1024;   // aim: entries per range
+constexpr int kRowsCap = 1024;        // rows per range at most (offsets staged in LDS)
+constexpr int kPiece = 2048;          // column indices staged in LDS at a time
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(kWave) void count_rank_kernel(
+    int m, int k, int rows_per_range, int ranges, const int *__restrict__ row_offsets,
+    const int *__restrict__ col_indices, int *__restrict__ rank, int *__restrict__ rowid,
+    int *__restrict__ tbl)
+{
+    extern __shared__ int s_cnt[];  // k counters
+    __shared__ int s_ro[kRowsCap + 1];
+    __shared__ int s_col[kPiece];
+    const int r = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int r0 = r * rows_per_range;
+    const int nrows = min(m - r0, rows_per_range);
+    for (int c = lane; c < k; c += kWave) s_cnt[c] = 0;
+    for (int t = lane; t <= nrows; t += kWave) s_ro[t] = row_offsets[r0 + t];
+    wave_lds_sync();
+    const int e0 = __builtin_amdgcn_readfirstlane(s_ro[0]);
+    const int e1 = __builtin_amdgcn_readfirstlane(s_ro[nrows]);
+    int t = 0;  // the first row not finished
+    for (int e = e0; e < e1; e += kPiece) {
+        const int e_end = min(e1, e + kPiece);
+        for (int i = lane; i < e_end - e; i += kWave) s_col[i] = col_indices[e + i];
+        wave_lds_sync();
+        while (t < nrows) {
+            const int rs = __builtin_amdgcn_readfirstlane(s_ro[t]);
+            const int re = __builtin_amdgcn_readfirstlane(s_ro[t + 1]);
+            if (re <= e) {  // ended before this piece (or empty)
+                ++t;
+                continue;
+            }
+            if (rs >= e_end) break;
+            const int hi = min(re, e_end);
+            for (int base = max(rs, e); base < hi; base += kWave) {
+                const int q = base + lane;
+                if (q < hi) {
+                    const int c = s_col[q - e];
+                    const int old = s_cnt[c];
+                    s_cnt[c] = old + 1;
+                    rank[q] = old;
+                    rowid[q] = r0 + t;
+                }
+                // The next chunk's reads follow these updates (one wave's LDS
+                // operations complete in program order).
+                wave_lds_sync();
+            }
+            if (re > e_end) break;  // the row goes on in the next piece
+            ++t;
+        }
+        wave_lds_sync();  // before the next piece overwrites s_col
+    }
+    for (int c = lane; c < k; c += kWave) tbl[(size_t)c * ranges + r] = s_cnt[c];
+}
+
+// One wave per column: exclusive prefix over the ranges in place, and the total.
+__global__ __launch_bounds__(256) void count_columns_kernel(int k, int ranges,
+                                                           int *__restrict__ tbl,
+                                                           int *__restrict__ tot)
+{
+    const int c = (int)blockIdx.x * 4 + (int)threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (c >= k) return;
+    int *col = tbl + (size_t)c * ranges;
+    int carry = 0;
+    for (int base = 0; base < ranges; base += kWave) {
+        const int i = base + lane;
+        const int v = i < ranges ? col[i] : 0;
+        const int incl = wave_inclusive_sum(v, lane);
+        if (i < ranges) col[i] = carry + incl - v;
+        carry += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) tot[c] = carry;
+}
+
+__global__ __launch_bounds__(kDigitScanThreads) void count_offsets_kernel(int k,
+                                                                         const int *__restrict__ tot,
+                                                                         int *__restrict__ t_row_offsets)
+{
+    exclusive_scan_block<kDigitScanThreads>(k, tot, t_row_offsets);
+}
+
+__global__ __launch_bounds__(256) void count_scatter_kernel(
+    int nnz, int ranges, int rows_per_range, const int *__restrict__ col_indices,
+    const float *__restrict__ values, const int *__restrict__ rank,
+    const int *__restrict__ rowid, const int *__restrict__ tbl,
+    const int *__restrict__ t_row_offsets, int *__restrict__ t_col_indices,
+    float *__restrict__ t_values, int *__restrict__ t_perm)
+{
+    const long long p = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (p >= nnz) return;
+    const int c = col_indices[p];
+    const int row = rowid[p];
+    const int r = row / rows_per_range;
+    const int q = t_row_offsets[c] + tbl[(size_t)c * ranges + r] + rank[p];
+    t_col_indices[q] = row;
+    if (t_values) t_values[q] = values[p];
+    if (t_perm) t_perm[q] = (int)p;
+}
+
 struct Workspace {
     int *keys[2], *vals[2], *rowid, *hist;
     size_t bytes;
@@ -220,6 +351,56 @@ Workspace carve(int nnz, void *base)
 
 unsigned blocks_for(long long count) { return (unsigned)((count + 255) / 256); }
 
+// The counting method's ranges: about kRangeEntries entries each, at most
+// kRowsCap rows, and a table of R * k + k ints within kCountMaxTable and the
+// workspace's three nnz-sized arrays after the rank array.  0: use the radix
+// method (larger problems, where its passes stream better than the rank
+// kernel's row-by-row walk).
+int count_rows_per_range(int m, int k, int nnz)
+{
+    if (k > kCountMaxK || nnz > kCountMaxNnz || m == 0) return 0;
+    const long long cap = std::min<long long>(
+        kCountMaxTable, 3 * (long long)(align256((size_t)nnz * sizeof(int)) / sizeof(int)));
+    long long s = std::max(1LL, std::min<long long>(kRowsCap, (long long)kRangeEntries * m / nnz));
+    for (;;) {
+        const long long ranges = (m + s - 1) / s;
+        if (ranges * k + k <= cap) return (int)s;
+        if (s >= kRowsCap) return 0;
+        s = std::min<long long>(kRowsCap, 2 * s);
+    }
+}
+
+hipError_t launch_count_transpose(int m, int k, int nnz, int rows_per_range,
+                                  const int *row_offsets, const int *col_indices,
+                                  const float *values, int *t_row_offsets, int *t_col_indices,
+                                  float *t_values, int *t_perm, const Workspace &w,
+                                  hipStream_t stream)
+{
+    hipError_t e;
+    const int ranges = (m + rows_per_range - 1) / rows_per_range;
+    int *rank = w.keys[0];
+    int *tbl = w.keys[1];  // keys[1], vals[0], vals[1] are contiguous
+    int *tot = tbl + (size_t)ranges * k;
+    const size_t lds = (size_t)k * sizeof(int);
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(&count_rank_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) !=
+        hipSuccess)
+        return e;
+    hipLaunchKernelGGL(count_rank_kernel, dim3((unsigned)ranges), dim3(kWave), lds, stream, m, k,
+                       rows_per_range, ranges, row_offsets, col_indices, rank, w.rowid, tbl);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(count_columns_kernel, dim3((unsigned)((k + 3) / 4)), dim3(256), 0, stream,
+                       k, ranges, tbl, tot);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(count_offsets_kernel, dim3(1), dim3(kDigitScanThreads), 0, stream, k, tot,
+                       t_row_offsets);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(count_scatter_kernel, dim3(blocks_for(nnz)), dim3(256), 0, stream, nnz,
+                       ranges, rows_per_range, col_indices, values, rank, w.rowid, tbl,
+                       t_row_offsets, t_col_indices, t_values, t_perm);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t transpose_workspace_bytes(int nnz) { return carve(nnz, nullptr).bytes; }
@@ -232,6 +413,9 @@ hipError_t launch_csr_transpose(int m, int k, int nnz, const int *row_offsets,
     hipError_t e;
     if (nnz == 0) return launch_fill_zero(reinterpret_cast<float *>(t_row_offsets), k + 1, stream);
     const Workspace w = carve(nnz, workspace);
+    if (const int s = count_rows_per_range(m, k, nnz))
+        return launch_count_transpose(m, k, nnz, s, row_offsets, col_indices, values,
+                                      t_row_offsets, t_col_indices, t_values, t_perm, w, stream);
     const int tiles = (nnz + kTile - 1) / kTile;
     int bits = 0;
     while (bits < 31 && (1LL << bits) < (long long)k) ++bits;  // columns lie in [0, 2^bits)
