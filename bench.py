@@ -83,6 +83,9 @@ def parse_args():
                          "write one JSON record per kernel run to this file")
     ap.add_argument("--no-stream", action="store_true",
                     help="skip the streaming-regime SpMM (CSR far beyond the caches)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the probe kernels that measure this GPU's stream-read, "
+                         "row-gather and launch ceilings")
     ap.add_argument("--profile-stream", action="store_true",
                     help="with --profile-launches: also launch the streaming-regime SpMM")
     ap.add_argument("--profile-launches", type=int, default=0,
@@ -708,6 +711,16 @@ def main() -> int:
         log(f"streaming spmm: {result['streaming']['avg_us']:.1f} us "
             f"{result['streaming']['achieved_gbs']:.0f} GB/s "
             f"({100 * result['streaming']['frac_hbm_peak']:.1f} % of HBM peak)")
+
+    if not args.no_ceilings:
+        # The same byte count as the streaming SpMM's CSR, and the FFN SpMM's B.
+        from unstructured_sparse_linear_csr_amd import probes
+        result["ceilings"] = probes.measure(torch, stream_bytes=431164900,
+                                            b_bytes=512 * 256 * 4)
+        c = result["ceilings"]
+        log(f"ceilings: stream read {c['stream_read_gbs']:.0f} GB/s; 1 KB row gathers "
+            + ", ".join(f"{k} {v:.1f} TB/s" for k, v in c["row_gather_tbs"].items())
+            + f"; empty launch {c['launch_floor_us']:.2f} us")
 
     if args.suite:
         run_suite(torch, sp, inputs, dev, args.suite)

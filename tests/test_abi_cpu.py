@@ -42,6 +42,20 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
         assert getattr(lib, name) is not None
 
 
+def test_probe_library_exports():
+    """The ceiling probes are a library of their own, outside the declared
+    interface."""
+    from unstructured_sparse_linear_csr_amd import probes
+    l = probes.lib()
+    for name in ("sp_probe_stream_read", "sp_probe_row_gather", "sp_probe_empty"):
+        assert getattr(l, name) is not None
+        assert not hasattr(binding.lib(), name) or name not in binding.SIGNATURES
+    # argument checks return before any launch
+    assert l.sp_probe_empty(0, NULL) != 0
+    assert l.sp_probe_stream_read(NULL, 1 << 20, 4, FAKE, NULL) != 0
+    assert l.sp_probe_row_gather(FAKE, 4, 4, FAKE, 512, FAKE, NULL) != 0
+
+
 def test_status_strings_and_version(lib):
     for code in range(4):
         assert binding.status_string(code)

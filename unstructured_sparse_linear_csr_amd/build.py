@@ -1,8 +1,9 @@
-"""Build ``libsp_csr.so`` in-tree from ``csrc/*.hip`` with hipcc for gfx950.
+"""Build ``libsp_csr.so`` in-tree from ``csrc/*.hip`` with hipcc for gfx950,
+and ``libsp_probes.so`` (the measured-ceiling probes) from ``probes/*.hip``.
 
 Run ``python -m unstructured_sparse_linear_csr_amd.build``.  Every call
 recompiles; sources compile in parallel into ``_build/`` and are linked into
-``unstructured_sparse_linear_csr_amd/libsp_csr.so``.
+the two libraries in ``unstructured_sparse_linear_csr_amd/``.
 """
 from __future__ import annotations
 
@@ -17,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsp_csr.so")
+PROBES = os.path.join(PKG, "probes")
+PROBE_LIB = os.path.join(PKG, "libsp_probes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -41,17 +44,23 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    subprocess.run(cmd, check=True, capture_output=not verbose)
+    os.replace(tmp, lib)
+    if verbose:
+        print(f"built {lib}")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
-        objs = list(ex.map(_compile, sources))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+    probes = sorted(glob.glob(os.path.join(PROBES, "*.hip")))
+    with ThreadPoolExecutor(max_workers=min(8, len(sources) + len(probes))) as ex:
+        objs = list(ex.map(_compile, sources + probes))
+    _link(objs[:len(sources)], LIB, verbose)
+    _link(objs[len(sources):], PROBE_LIB, verbose)
     return LIB
 
 
