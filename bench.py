@@ -536,7 +536,8 @@ def main() -> int:
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(SpMM shards by rows of A or columns of B, attention by head, with no "
+              "exchange; this build runs and measures the one-GPU share)", file=sys.stderr)
         return 2
 
     import torch
