@@ -537,7 +537,7 @@ def main() -> int:
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(SpMM shards by rows of A or columns of B, attention by head, with no "
-              "exchange; this build runs and measures the one-GPU share)", file=sys.stderr)
+              "exchange; only the one-GPU share is implemented)", file=sys.stderr)
         return 2
 
     import torch
