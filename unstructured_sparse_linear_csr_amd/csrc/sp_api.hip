@@ -155,7 +155,7 @@ const char *sp_status_string(sp_status_t status)
     switch (status) {
     case SP_SUCCESS: return "success";
     case SP_ERROR_INVALID_VALUE: return "invalid argument";
-    case SP_ERROR_NOT_SUPPORTED: return "problem size not supported by this build";
+    case SP_ERROR_NOT_SUPPORTED: return "problem shape or size not supported by these kernels";
     case SP_ERROR_LAUNCH_FAILED: return "kernel launch failed";
     }
     return "unknown status";
