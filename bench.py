@@ -718,10 +718,10 @@ def main() -> int:
         from unstructured_sparse_linear_csr_amd import probes
         result["ceilings"] = probes.measure(torch, stream_bytes=431164900,
                                             b_bytes=512 * 256 * 4)
-        c = result["ceilings"]
-        log(f"ceilings: stream read {c['stream_read_gbs']:.0f} GB/s; 1 KB row gathers "
-            + ", ".join(f"{k} {v:.1f} TB/s" for k, v in c["row_gather_tbs"].items())
-            + f"; empty launch {c['launch_floor_us']:.2f} us")
+        ceil = result["ceilings"]
+        log(f"ceilings: stream read {ceil['stream_read_gbs']:.0f} GB/s; 1 KB row gathers "
+            + ", ".join(f"{k} {v:.1f} TB/s" for k, v in ceil["row_gather_tbs"].items())
+            + f"; empty launch {ceil['launch_floor_us']:.2f} us")
 
     if args.suite:
         run_suite(torch, sp, inputs, dev, args.suite)

@@ -21,8 +21,11 @@ namespace spk {
 namespace {
 
 constexpr int kSwizzleThreads = 256;
-constexpr int kLanesPerRow = 16;  // lanes sharing one row's comparisons
-constexpr int kRowsPerBlock = kSwizzleThreads / kLanesPerRow;
+// Lanes sharing one row's comparisons: 32 up to kFewRows rows (twice the
+// workgroups, half the comparisons per lane: the order of a few thousand rows
+// comes sooner), 16 above (fewer workgroups each staging all the keys).
+constexpr int kFewRows = 4096;
+template <int kLanes> constexpr int rows_per_block() { return kSwizzleThreads / kLanes; }
 constexpr int kSwizzleTile = 2048;  // keys staged in LDS per pass (16 KB)
 
 __device__ __forceinline__ unsigned long long row_key(int length, int row)
@@ -44,11 +47,12 @@ struct FromLengths {
 // kLanesPerRow-th pair of staged keys; the partial counts are summed across
 // the lanes (integer sums, so the order does not matter).  Lanes of a wave
 // that read the same pair read the same LDS address (a broadcast), and the
-// 16 pairs a wave reads at once are contiguous.  Padding slots hold key 0,
-// which is below every real key.
-template <class Len>
+// kLanesPerRow pairs a wave reads at once are contiguous.  Padding slots hold
+// key 0, which is below every real key.
+template <int kLanesPerRow, class Len>
 __device__ void rank_rows(int m, Len len, int *__restrict__ row_indices, int block)
 {
+    constexpr int kRowsPerBlock = rows_per_block<kLanesPerRow>();
     __shared__ __align__(16) unsigned long long s_key[kSwizzleTile];
     const int t = threadIdx.x;
     const int sub = t % kLanesPerRow;
@@ -91,15 +95,17 @@ __device__ void rank_rows(int m, Len len, int *__restrict__ row_indices, int blo
     if (mine && sub == 0) row_indices[rank] = i;
 }
 
+template <int kLanes>
 __global__ __launch_bounds__(kSwizzleThreads) void row_swizzle_kernel(
     int m, const int *__restrict__ row_offsets, int *__restrict__ row_indices)
 {
-    rank_rows(m, FromOffsets{row_offsets}, row_indices, blockIdx.x);
+    rank_rows<kLanes>(m, FromOffsets{row_offsets}, row_indices, blockIdx.x);
 }
 
 // CSR offsets and the swizzled order from row lengths in one launch: the
 // order needs only the lengths, so the last workgroup scans them into the
 // offsets while the others rank the rows.
+template <int kLanes>
 __global__ __launch_bounds__(kSwizzleThreads) void build_and_swizzle_kernel(
     int m, const int *__restrict__ lengths, int *__restrict__ row_offsets,
     int *__restrict__ row_indices)
@@ -108,7 +114,26 @@ __global__ __launch_bounds__(kSwizzleThreads) void build_and_swizzle_kernel(
         exclusive_scan_block<kSwizzleThreads>(m, lengths, row_offsets);
         return;
     }
-    rank_rows(m, FromLengths{lengths}, row_indices, blockIdx.x);
+    rank_rows<kLanes>(m, FromLengths{lengths}, row_indices, blockIdx.x);
+}
+
+template <int kLanes>
+hipError_t launch_build_t(int m, const int *lengths, int *row_offsets, int *row_indices,
+                          hipStream_t stream)
+{
+    const int blocks = (m + rows_per_block<kLanes>() - 1) / rows_per_block<kLanes>() + 1;
+    hipLaunchKernelGGL((build_and_swizzle_kernel<kLanes>), dim3(blocks), dim3(kSwizzleThreads),
+                       0, stream, m, lengths, row_offsets, row_indices);
+    return hipGetLastError();
+}
+
+template <int kLanes>
+hipError_t launch_swizzle_t(int m, const int *row_offsets, int *row_indices, hipStream_t stream)
+{
+    const int blocks = (m + rows_per_block<kLanes>() - 1) / rows_per_block<kLanes>();
+    hipLaunchKernelGGL((row_swizzle_kernel<kLanes>), dim3(blocks), dim3(kSwizzleThreads), 0,
+                       stream, m, row_offsets, row_indices);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -116,20 +141,16 @@ __global__ __launch_bounds__(kSwizzleThreads) void build_and_swizzle_kernel(
 hipError_t launch_build_and_swizzle(int m, const int *lengths, int *row_offsets,
                                    int *row_indices, hipStream_t stream)
 {
-    const int blocks = (m + kRowsPerBlock - 1) / kRowsPerBlock + 1;
-    hipLaunchKernelGGL(build_and_swizzle_kernel, dim3(blocks), dim3(kSwizzleThreads), 0,
-                       stream, m, lengths, row_offsets, row_indices);
-    return hipGetLastError();
+    return m <= kFewRows ? launch_build_t<32>(m, lengths, row_offsets, row_indices, stream)
+                         : launch_build_t<16>(m, lengths, row_offsets, row_indices, stream);
 }
 
 hipError_t launch_row_swizzle(int m, const int *row_offsets, int *row_indices,
                               hipStream_t stream)
 {
     if (m == 0) return hipSuccess;
-    const int blocks = (m + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL(row_swizzle_kernel, dim3(blocks), dim3(kSwizzleThreads),
-                       0, stream, m, row_offsets, row_indices);
-    return hipGetLastError();
+    return m <= kFewRows ? launch_swizzle_t<32>(m, row_offsets, row_indices, stream)
+                         : launch_swizzle_t<16>(m, row_offsets, row_indices, stream);
 }
 
 }  // namespace spk
