@@ -84,7 +84,7 @@ def measure(torch, stream_bytes: int, b_bytes: int = 512 * 1024, seed: int = 0) 
     b = torch.ones(b_bytes // 4, device=dev)
     rng = np.random.default_rng(seed)
     gathers = {}
-    for waves, per_wave in ((2048, 51), (16384, 256)):
+    for waves, per_wave in ((2048, 51), (4096, 51), (16384, 256)):
         rows = b_bytes // 1024
         offs = torch.from_numpy((rng.integers(0, rows, waves * per_wave) * 1024)
                                 .astype(np.uint32)).to(dev)
