@@ -141,8 +141,11 @@ sp_status_t sp_csr_build_from_lengths(int m, const int *lengths, int *row_offset
  *   values, row_offsets, col_indices   the CSR of A
  *   b            fp32[k*n];  c  fp32[m*n], output
  * Sizes: m, k, n, nnz >= 0 and m*n, k*n < 2^62.  m == 0 or n == 0 enqueues
- * nothing.  Summation per output element is sequential in entry order, so
- * results are deterministic run to run. */
+ * nothing.  Each output element is summed in an order fixed by the shapes
+ * alone: in entry order (wide B); per-lane partial sums added by a fixed tree
+ * (B of at most 16 columns); four consecutive parts of the row, each in entry
+ * order, added in order (few rows averaging 256 entries or more).  Results are
+ * deterministic run to run and do not depend on row_indices. */
 sp_status_t sp_spmm(int m, int k, int n, int nnz, const int *row_indices,
                     const float *values, const int *row_offsets,
                     const int *col_indices, const float *b, float *c,
