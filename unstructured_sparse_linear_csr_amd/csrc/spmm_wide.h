@@ -43,7 +43,7 @@ namespace spmm_detail {
 #define SP_SPMM_UNROLL 4
 #endif
 #ifndef SP_SPMM_ENTRIES_PER_LANE
-#define SP_SPMM_ENTRIES_PER_LANE 8
+#define SP_SPMM_ENTRIES_PER_LANE 4
 #endif
 constexpr int kU = SP_SPMM_UNROLL;                // gathers per batch
 constexpr int kEpl = SP_SPMM_ENTRIES_PER_LANE;    // staged entries per lane per window
