@@ -575,6 +575,18 @@ hipError_t launch_balanced(const SpmmParams &p, bool vec_csr, bool buf, hipStrea
     return hipGetLastError();
 }
 
+// The current device's compute units and LDS bytes per workgroup (false if
+// they cannot be queried; variant selection then keeps the default kernels).
+bool device_limits(int *cus, int *lds_max)
+{
+    int device = 0;
+    return hipGetDevice(&device) == hipSuccess &&
+           hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, device) ==
+               hipSuccess &&
+           hipDeviceGetAttribute(lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, device) ==
+               hipSuccess;
+}
+
 inline bool aligned(const void *ptr, unsigned bytes)
 {
     return (reinterpret_cast<uintptr_t>(ptr) & (bytes - 1u)) == 0;
@@ -647,10 +659,8 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
         p.row_blocks = (int)(((long long)a.m + kBalWaves - 1) / kBalWaves);
     } else if (vec_csr && buf && (long long)a.nnz >= kSplitMinLength * (long long)a.m) {
         // Few, long rows: fewer than two waves per SIMD in the wide launch.
-        int cus = 0, device = 0;
-        if (hipGetDevice(&device) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) ==
-                hipSuccess &&
+        int cus = 0, lds_max = 0;
+        if (device_limits(&cus, &lds_max) &&
             (long long)a.batch * tiles * row_blocks < 2LL * kSimdsPerCu * cus)
             plan->kind = SpmmPlan::kSplit;
     }
@@ -658,13 +668,8 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
         plan->kind = SpmmPlan::kNarrow;
         // B in LDS when it fits and every CU has at least as many entries to
         // stream as it copies B elements (nnz >= CUs * k * n).
-        int cus = 0, lds_max = 0, device = 0;
-        if (hipGetDevice(&device) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) !=
-                hipSuccess ||
-            hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock,
-                                  device) != hipSuccess)
-            cus = 0;
+        int cus = 0, lds_max = 0;
+        if (!device_limits(&cus, &lds_max)) cus = 0;
         // B, or when it does not fit, S column slices of B: the widest
         // slice (in vectors of kvec columns) that fits, then the S slices
         // evened out.  Every group of S workgroups (one per CU) must stream at
