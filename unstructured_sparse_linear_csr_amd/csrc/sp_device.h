@@ -41,6 +41,39 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+// Sum over the lanes of the wave congruent to this lane modulo kStride (1, 2,
+// 4, 8 or 16); every lane receives its class's sum.  Rotations inside each
+// 16-lane row (DPP row_ror, fused into v_add_f32_dpp) sum a row's lanes of
+// the class; gfx950's v_permlane16_swap then pairs each row with its
+// neighbour, and v_permlane32_swap the two wave halves.  Every lane of a pair
+// adds (lower half) + (upper half), so the order is fixed and the results are
+// deterministic; no LDS traffic.  All 64 lanes must be active.
+constexpr int kDppRowRor1 = 0x121;  // lane i <- lane (i - 1) mod 16 within a row
+constexpr int kDppRowRor2 = 0x122;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+__device__ __forceinline__ float swap_pair_sum(float v, bool halves)
+{
+    const unsigned u = __float_as_uint(v);
+    const auto p = halves ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                          : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+template <int kStride>
+__device__ __forceinline__ float strided_wave_sum(float v)
+{
+    static_assert(kStride == 1 || kStride == 2 || kStride == 4 || kStride == 8 ||
+                      kStride == 16, "stride must divide a DPP row");
+    if constexpr (kStride <= 1) v += dpp_read<kDppRowRor1>(v);
+    if constexpr (kStride <= 2) v += dpp_read<kDppRowRor2>(v);
+    if constexpr (kStride <= 4) v += dpp_read<kDppRowRor4>(v);
+    if constexpr (kStride <= 8) v += dpp_read<kDppRowRor8>(v);
+    v = swap_pair_sum(v, false);
+    return swap_pair_sum(v, true);
+}
+
 // Keeps the compiler from moving any instruction across this point (memory
 // operations at the IR level, everything in the machine scheduler).  Used
 // after a batch of prefetch gathers so that they stay issued ahead of the

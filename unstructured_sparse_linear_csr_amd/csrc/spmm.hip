@@ -187,7 +187,8 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void spmm_split_kernel(SpmmPar
 // of B (kE vectors cover the row of B).  Column indices and values are read
 // through buffer resources (out-of-range past the row's end: zeros, no
 // traffic); each lane sums its entries in order, then the kS partial sums of
-// each column vector are added by a shuffle tree over the lane bits above kE.
+// each column vector are added across lanes (DPP rotations inside 16-lane
+// rows, then lane swaps between rows and between wave halves).
 // Deterministic; a different (tree) order from the wide kernel.
 template <int kE, int kVec>
 __global__ __launch_bounds__(kWave) void spmm_narrow_kernel(SpmmParams p)
@@ -248,10 +249,7 @@ __global__ __launch_bounds__(kWave) void spmm_narrow_kernel(SpmmParams p)
         for (int u = 0; u < kSteps; ++u) V::fma(vv[u], bv[u], acc);
     }
 #pragma unroll
-    for (int o = kE; o < kWave; o <<= 1) {
-#pragma unroll
-        for (int t = 0; t < kVec; ++t) acc[t] += __shfl_xor(acc[t], o);
-    }
+    for (int t = 0; t < kVec; ++t) acc[t] = strided_wave_sum<kE>(acc[t]);
     if (s == 0 && col_ok) V::store(cz + (size_t)row * (size_t)p.n + col0, acc);
 }
 
@@ -428,10 +426,7 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
     for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
     auto finish_row = [&](int r) {
 #pragma unroll
-        for (int o = kE; o < kWave; o <<= 1) {
-#pragma unroll
-            for (int t = 0; t < kVec; ++t) acc[t] += __shfl_xor(acc[t], o);
-        }
+        for (int t = 0; t < kVec; ++t) acc[t] = strided_wave_sum<kE>(acc[t]);
         if (s == 0 && col_ok) V::store(c_out + (size_t)r * (size_t)p.n + col0, acc);
 #pragma unroll
         for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
