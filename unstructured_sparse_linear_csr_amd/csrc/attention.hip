@@ -221,10 +221,7 @@ __global__ __launch_bounds__(kWave) void attention_kernel(AttnParams p)
     }
     // entry slots' partial sums, then the normalisation
 #pragma unroll
-    for (int off = kDv; off < kWave; off <<= 1) {
-#pragma unroll
-        for (int t = 0; t < kVec; ++t) o[t] += __shfl_xor(o[t], off);
-    }
+    for (int t = 0; t < kVec; ++t) o[t] = strided_wave_sum<kDv>(o[t]);
     const float inv = 1.f / l;
 #pragma unroll
     for (int t = 0; t < kVec; ++t) o[t] *= inv;

@@ -90,8 +90,7 @@ __device__ void rank_rows(int m, Len len, int *__restrict__ row_indices, int blo
         }
         __syncthreads();
     }
-#pragma unroll
-    for (int off = 1; off < kLanesPerRow; off <<= 1) rank += __shfl_xor(rank, off);
+    rank = group_reduce<kLanesPerRow>(rank, OpAdd{});
     if (mine && sub == 0) row_indices[rank] = i;
 }
 

@@ -18,60 +18,110 @@ constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i within 8
 constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i within 16
 
-template <int kCtrl>
-__device__ __forceinline__ float dpp_read(float v)
+// 32-bit values travel through the lane-permute builtins as their bits.
+template <class T> __device__ __forceinline__ unsigned to_bits(T v)
 {
-    return __int_as_float(__builtin_amdgcn_update_dpp(
-        0, __float_as_int(v), kCtrl, 0xF, 0xF, true));
+    static_assert(sizeof(T) == 4, "32-bit lane values");
+    return __builtin_bit_cast(unsigned, v);
+}
+template <class T> __device__ __forceinline__ T from_bits(unsigned u)
+{
+    return __builtin_bit_cast(T, u);
 }
 
-// Sum over aligned groups of kLanes consecutive lanes (kLanes in 1, 2, 4, 8,
-// 16); every lane of a group receives the group's sum.  Uses only DPP moves
-// inside a 16-lane row, fused by the compiler into v_add_f32_dpp.  All lanes
-// of each group must be active.
-template <int kLanes>
-__device__ __forceinline__ float group_sum(float v)
+template <int kCtrl, class T>
+__device__ __forceinline__ T dpp_read(T v)
 {
-    static_assert(kLanes == 1 || kLanes == 2 || kLanes == 4 || kLanes == 8 ||
-                      kLanes == 16, "group must fit a DPP row");
-    if constexpr (kLanes >= 2) v += dpp_read<kDppQuadXor1>(v);
-    if constexpr (kLanes >= 4) v += dpp_read<kDppQuadXor2>(v);
-    if constexpr (kLanes >= 8) v += dpp_read<kDppRowHalfMirror>(v);
-    if constexpr (kLanes >= 16) v += dpp_read<kDppRowMirror>(v);
+    return from_bits<T>((unsigned)__builtin_amdgcn_update_dpp(
+        0, (int)to_bits(v), kCtrl, 0xF, 0xF, true));
+}
+
+// gfx950's lane swaps: v_permlane16_swap exchanges the odd 16-lane rows of one
+// copy of v with the even rows of another, v_permlane32_swap the upper wave
+// half of one with the lower half of the other.  Each lane then holds its own
+// value and its partner's as (lower, upper) in the same order in both lanes,
+// so op(lower, upper) is the same in both.
+template <bool kHalves, class T, class Op>
+__device__ __forceinline__ T swap_combine(T v, Op op)
+{
+    const unsigned u = to_bits(v);
+    if constexpr (kHalves) {
+        const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return op(from_bits<T>(p[0]), from_bits<T>(p[1]));
+    } else {
+        const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return op(from_bits<T>(p[0]), from_bits<T>(p[1]));
+    }
+}
+
+struct OpAdd {
+    template <class T> __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct OpMax {
+    __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+    __device__ int operator()(int a, int b) const { return max(a, b); }
+};
+
+// Reduction over aligned groups of kLanes consecutive lanes (1 ... 64); every
+// lane of a group receives the same result.  A butterfly whose every step
+// joins two lanes holding equal values (quad swaps, then the 8- and 16-lane
+// mirrors by DPP, fused by the compiler into v_add_f32_dpp and the like; then
+// the row and half-wave swaps), with a commutative op: every lane computes
+// the same result in a fixed order, so results are deterministic.  No LDS
+// traffic.  All lanes of the wave must be active.
+template <int kLanes, class T, class Op>
+__device__ __forceinline__ T group_reduce(T v, Op op)
+{
+    static_assert(kLanes == 1 || kLanes == 2 || kLanes == 4 || kLanes == 8 || kLanes == 16 ||
+                      kLanes == 32 || kLanes == 64, "group of 1 ... 64 lanes");
+    if constexpr (kLanes >= 2) v = op(v, dpp_read<kDppQuadXor1>(v));
+    if constexpr (kLanes >= 4) v = op(v, dpp_read<kDppQuadXor2>(v));
+    if constexpr (kLanes >= 8) v = op(v, dpp_read<kDppRowHalfMirror>(v));
+    if constexpr (kLanes >= 16) v = op(v, dpp_read<kDppRowMirror>(v));
+    if constexpr (kLanes >= 32) v = swap_combine<false>(v, op);
+    if constexpr (kLanes >= 64) v = swap_combine<true>(v, op);
     return v;
 }
 
-// Sum over the lanes of the wave congruent to this lane modulo kStride (1, 2,
-// 4, 8 or 16); every lane receives its class's sum.  Rotations inside each
-// 16-lane row (DPP row_ror, fused into v_add_f32_dpp) sum a row's lanes of
-// the class; gfx950's v_permlane16_swap then pairs each row with its
-// neighbour, and v_permlane32_swap the two wave halves.  Every lane of a pair
-// adds (lower half) + (upper half), so the order is fixed and the results are
-// deterministic; no LDS traffic.  All 64 lanes must be active.
+// Sum over aligned groups of kLanes consecutive lanes (kLanes in 1, 2, 4, 8,
+// 16: DPP moves inside a 16-lane row only).
+template <int kLanes>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(kLanes <= 16, "group must fit a DPP row");
+    return group_reduce<kLanes>(v, OpAdd{});
+}
+
+// Reduction over the lanes of the wave congruent to this lane modulo kStride
+// (1 ... 64); every lane receives its class's result (for a sum, lanes of a
+// class may differ in rounding: each adds in its own order).  Rotations
+// inside each 16-lane row (DPP row_ror) combine a row's lanes of the class,
+// then the row and half-wave swaps.  Fixed order, deterministic, no LDS
+// traffic.  All 64 lanes must be active.
 constexpr int kDppRowRor1 = 0x121;  // lane i <- lane (i - 1) mod 16 within a row
 constexpr int kDppRowRor2 = 0x122;
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
 
-__device__ __forceinline__ float swap_pair_sum(float v, bool halves)
+template <int kStride, class T, class Op>
+__device__ __forceinline__ T strided_wave_reduce(T v, Op op)
 {
-    const unsigned u = __float_as_uint(v);
-    const auto p = halves ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
-                          : __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    static_assert(kStride == 1 || kStride == 2 || kStride == 4 || kStride == 8 ||
+                      kStride == 16 || kStride == 32 || kStride == 64,
+                  "stride of 1 ... 64 lanes");
+    if constexpr (kStride <= 1) v = op(v, dpp_read<kDppRowRor1>(v));
+    if constexpr (kStride <= 2) v = op(v, dpp_read<kDppRowRor2>(v));
+    if constexpr (kStride <= 4) v = op(v, dpp_read<kDppRowRor4>(v));
+    if constexpr (kStride <= 8) v = op(v, dpp_read<kDppRowRor8>(v));
+    if constexpr (kStride <= 16) v = swap_combine<false>(v, op);
+    if constexpr (kStride <= 32) v = swap_combine<true>(v, op);
+    return v;
 }
 
 template <int kStride>
 __device__ __forceinline__ float strided_wave_sum(float v)
 {
-    static_assert(kStride == 1 || kStride == 2 || kStride == 4 || kStride == 8 ||
-                      kStride == 16, "stride must divide a DPP row");
-    if constexpr (kStride <= 1) v += dpp_read<kDppRowRor1>(v);
-    if constexpr (kStride <= 2) v += dpp_read<kDppRowRor2>(v);
-    if constexpr (kStride <= 4) v += dpp_read<kDppRowRor4>(v);
-    if constexpr (kStride <= 8) v += dpp_read<kDppRowRor8>(v);
-    v = swap_pair_sum(v, false);
-    return swap_pair_sum(v, true);
+    return strided_wave_reduce<kStride>(v, OpAdd{});
 }
 
 // Keeps the compiler from moving any instruction across this point (memory
@@ -86,21 +136,9 @@ __device__ __forceinline__ void keep_issued_above()
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Wave-wide maximum and sum of a float, the same value in every lane (a
-// butterfly over the 64 lanes: a fixed order, so results are deterministic).
-__device__ __forceinline__ float wave_max(float v)
-{
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v)
-{
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o);
-    return v;
-}
+// Wave-wide maximum and sum of a float, the same value in every lane.
+__device__ __forceinline__ float wave_max(float v) { return group_reduce<kWave>(v, OpMax{}); }
+__device__ __forceinline__ float wave_sum(float v) { return group_reduce<kWave>(v, OpAdd{}); }
 
 // Wave-wide inclusive prefix sum of an int (Hillis-Steele over 64 lanes).
 __device__ __forceinline__ int wave_inclusive_sum(int v, int lane)

@@ -191,9 +191,7 @@ __device__ __forceinline__ void wide_accumulate(const SpmmParams &p, const E *__
         // ---- gather and accumulate: double-buffered batches of kU slots.
         // Slots [0, wend) of the window cover every group's live entries.
         const int my_end = min(p1 - win, kChunk);
-        int wend = my_end;
-#pragma unroll
-        for (int o = kLpr; o < kWave; o <<= 1) wend = max(wend, __shfl_xor(wend, o));
+        const int wend = strided_wave_reduce<kLpr>(my_end, OpMax{});
         VecT bufa[kU], bufb[kU];
         int offa[kU], offb[kU];
         float vala[kU], valb[kU];
