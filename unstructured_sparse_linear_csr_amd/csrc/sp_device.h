@@ -140,14 +140,27 @@ __device__ __forceinline__ void keep_issued_above()
 __device__ __forceinline__ float wave_max(float v) { return group_reduce<kWave>(v, OpMax{}); }
 __device__ __forceinline__ float wave_sum(float v) { return group_reduce<kWave>(v, OpAdd{}); }
 
-// Wave-wide inclusive prefix sum of an int (Hillis-Steele over 64 lanes).
-__device__ __forceinline__ int wave_inclusive_sum(int v, int lane)
+// Wave-wide inclusive prefix sum of an int: Hillis-Steele inside each 16-lane
+// row by DPP row shifts (lanes shifted in from outside the row read 0), then
+// each row adds the running total of the rows before it, broadcast from lane
+// 15 (rows 1 and 3) and lane 31 (rows 2 and 3).  No LDS traffic.  All 64
+// lanes must be active.
+constexpr int kDppRowShr1 = 0x111;      // lane i <- lane i-1 within a row (0 at the row start)
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;   // lane 15 of each row to the next row
+constexpr int kDppRowBcast31 = 0x143;   // lane 31 to rows 2 and 3
+
+__device__ __forceinline__ int wave_inclusive_sum(int v)
 {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        int up = __shfl_up(v, off, kWave);
-        if (lane >= off) v += up;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xF, 0xF, true);
+    // rows outside the row mask keep the old value, 0
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
     return v;
 }
 

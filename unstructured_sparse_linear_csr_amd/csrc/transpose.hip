@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_downsweep_kernel(
     // Digit bases: exclusive scan of the digit totals (thread d holds digit
     // d), plus this tile's offset within the digit.
     const int total = hist[(size_t)tid * (tiles + 1) + tiles];
-    const int incl = wave_inclusive_sum(total, lane);
+    const int incl = wave_inclusive_sum(total);
     if (lane == kWave - 1) s_wave_sum[wave] = incl;
 
     int key[kItems], val[kItems], rank[kItems];
@@ -293,9 +293,9 @@ __global__ __launch_bounds__(256) void count_columns_kernel(int k, int ranges,
     for (int base = 0; base < ranges; base += kWave) {
         const int i = base + lane;
         const int v = i < ranges ? col[i] : 0;
-        const int incl = wave_inclusive_sum(v, lane);
+        const int incl = wave_inclusive_sum(v);
         if (i < ranges) col[i] = carry + incl - v;
-        carry += __shfl(incl, kWave - 1);
+        carry += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
     if (lane == 0) tot[c] = carry;
 }
