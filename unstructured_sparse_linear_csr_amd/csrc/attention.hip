@@ -106,12 +106,12 @@ __global__ __launch_bounds__(kWave) void attention_kernel(AttnParams p)
     // score lanes: group g, lane gl within it
     const int g = lane / kG;
     const int gl = lane - g * kG;
-    float qf[kNv][kVec];
+    VecT qv[kNv];
     unsigned lane_koff[kNv];
 #pragma unroll
     for (int u = 0; u < kNv; ++u) {
         const int e = (u * kG + gl) * kVec;
-        V::to_f32(V::load(qz + e), qf[u]);
+        qv[u] = V::load(qz + e);
         lane_koff[u] = (unsigned)e * kEb;
     }
     const unsigned lane_voff = (unsigned)vv * 16u;
@@ -135,12 +135,7 @@ __global__ __launch_bounds__(kWave) void attention_kernel(AttnParams p)
         for (int u = 0; u < kU; ++u) {
             float acc = 0.f;
 #pragma unroll
-            for (int c = 0; c < kNv; ++c) {
-                float kf[kVec];
-                V::to_f32(kb[u][c], kf);
-#pragma unroll
-                for (int t = 0; t < kVec; ++t) acc = fmaf(qf[c][t], kf[t], acc);
-            }
+            for (int c = 0; c < kNv; ++c) acc = V::dot(qv[c], kb[u][c], acc);
             const float sum = group_sum<kG>(acc);
             if (gl == s0 + u) res = sum;
         }

@@ -25,8 +25,9 @@
 // Staging.  The window's 64 column indices are read with one coalesced load and
 // kept in LDS as Y-row offsets (bytes when k*d < 2^30).
 //
-// Summation order: each lane sums its elements in order with FMA, then the
-// DPP tree adds the kG lane partials; deterministic run to run.
+// Summation order: each lane sums its elements in order with FMA (bf16: by
+// pairs, v_dot2c_f32_bf16), then the DPP tree adds the kG lane partials;
+// deterministic run to run.
 #pragma once
 
 #include "sp_device.h"
@@ -67,24 +68,13 @@ __device__ __forceinline__ void store_entry(const SddmmParams &p, long long z, i
 #endif
 constexpr unsigned kOutOfRange = 0x80000000u;  // buffer offset that reads as zero
 
-// sum over i < kVec of x[i] * y[i], in order, added to acc with FMA.
-template <typename V, int kVec>
-__device__ __forceinline__ float dot_f32(const float *x, const typename V::T &y, float acc)
-{
-    float yf[kVec];
-    V::to_f32(y, yf);
-#pragma unroll
-    for (int i = 0; i < kVec; ++i) acc = fmaf(x[i], yf[i], acc);
-    return acc;
-}
-
 // kNv > 0 (Y < 2 GiB): the lane's kNv vectors of the X row live in registers
-// (widened to fp32); Y rows are gathered through a buffer resource, and window
+// (as loaded); Y rows are gathered through a buffer resource, and window
 // slots past the row's end carry an out-of-range offset that reads as zeros,
 // so steps are issued in unconditional double-buffered batches of kU.
 // kNv == 0: any d and any Y size; X and Y are read with 64-bit addresses in a
 // loop over d, one step at a time.  E is the element type of X and Y (fp32,
-// fp16 or bf16); arithmetic is fp32 throughout.
+// fp16 or bf16); products and sums are fp32 (V::dot).
 //
 // kSoftmax: the row softmax of the scaled scores is applied before they are
 // written (out = softmax over the row's entries of alpha * X Y^T), the step
@@ -157,9 +147,7 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
                 if (j < cnt) {
                     const E *yr = yz + (size_t)s_col[j] * (size_t)p.d;
                     for (int e = gl * kVec; e < p.d; e += kG * kVec) {
-                        float xf[kVec];
-                        V::to_f32(V::load(xr_ptr + e), xf);
-                        acc = dot_f32<V, kVec>(xf, V::load(yr + e), acc);
+                        acc = V::dot(V::load(xr_ptr + e), V::load(yr + e), acc);
                     }
                 }
                 const float sum = group_sum<kG>(acc);
@@ -173,12 +161,12 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
     } else {
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<E *>(yz), 0, (int)p.y_bytes, 0x00020000);
-        float xr[kXv][kVec];
+        VecT xr[kXv];
         unsigned lane_off[kXv];
 #pragma unroll
         for (int v = 0; v < kNv; ++v) {
             const int e = (v * kG + gl) * kVec;
-            V::to_f32(e < p.d ? V::load(xr_ptr + e) : V::zero(), xr[v]);
+            xr[v] = e < p.d ? V::load(xr_ptr + e) : V::zero();
             lane_off[v] = e < p.d ? (unsigned)e * kEb : kOutOfRange;
         }
         for (int t = kWave + lane; t < kSlots; t += kWave) s_off[t] = kOutOfRange;
@@ -196,7 +184,7 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
             for (int u = 0; u < kU; ++u) {
                 float acc = 0.f;
 #pragma unroll
-                for (int v = 0; v < kNv; ++v) acc = dot_f32<V, kVec>(xr[v], yv[u][v], acc);
+                for (int v = 0; v < kNv; ++v) acc = V::dot(xr[v], yv[u][v], acc);
                 const float sum = group_sum<kG>(acc);
                 if (gl == s0 + u) res = sum;
             }

@@ -1,7 +1,8 @@
 // Element types of the dense operands and sparse values, and the vectors the
 // kernels gather them in.  fp32 is the card's precision; fp16 and bf16 are
 // the mixed-precision inputs (16-bit storage, fp32 arithmetic and
-// accumulation): every element is widened to fp32 exactly when loaded.
+// accumulation): every element is widened to fp32 exactly when used, and a
+// product of two 16-bit elements is exact in fp32.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -50,7 +51,8 @@ template <> struct Elem<bf16> {
 // A vector of kVec consecutive elements of type E as one load: 16 bytes
 // (4 fp32 or 8 16-bit elements) or a single element.  T is the raw register
 // form; to_f32 widens it, fma multiplies it by a scalar into kVec fp32
-// accumulators (element order 0, 1, ...), store writes kVec fp32 results.
+// accumulators (element order 0, 1, ...), dot adds the dot product of two
+// vectors to an fp32 sum, store writes kVec fp32 results.
 template <typename E, int kVec> struct GVec;
 
 template <> struct GVec<float, 4> {
@@ -80,6 +82,14 @@ template <> struct GVec<float, 4> {
         acc[2] = fmaf(a, b.z, acc[2]);
         acc[3] = fmaf(a, b.w, acc[3]);
     }
+    // element order 0 ... 3, one FMA each
+    static __device__ __forceinline__ float dot(const T &x, const T &y, float acc)
+    {
+        acc = fmaf(x.x, y.x, acc);
+        acc = fmaf(x.y, y.y, acc);
+        acc = fmaf(x.z, y.z, acc);
+        return fmaf(x.w, y.w, acc);
+    }
     static __device__ __forceinline__ void store(float *dst, const float *acc)
     {
         *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -98,6 +108,10 @@ template <> struct GVec<float, 1> {
     static __device__ __forceinline__ void fma(float a, const T &b, float *acc)
     {
         acc[0] = fmaf(a, b, acc[0]);
+    }
+    static __device__ __forceinline__ float dot(const T &x, const T &y, float acc)
+    {
+        return fmaf(x, y, acc);
     }
     static __device__ __forceinline__ void store(float *dst, const float *acc) { *dst = acc[0]; }
 };
@@ -131,6 +145,30 @@ template <typename E> struct GVec16x8 {
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(a, f[i], acc[i]);
     }
+    // fp16: element order 0 ... 7, one FMA each (the conversions fold into
+    // v_fma_mix_f32).  bf16: gfx950's v_dot2c_f32_bf16 adds the two exact
+    // products of elements (0, 1), then (2, 3), ... to the sum, one
+    // instruction per pair instead of a shift or mask plus an FMA per element.
+    static __device__ __forceinline__ float dot(const T &x, const T &y, float acc)
+    {
+        const unsigned xw[4] = {x.x, x.y, x.z, x.w};
+        const unsigned yw[4] = {y.x, y.y, y.z, y.w};
+        if constexpr (__is_same(E, bf16)) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xw[i]),
+                                                      __builtin_bit_cast(bf16x2, yw[i]), acc,
+                                                      false);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc = fmaf(Elem<E>::lo(xw[i]), Elem<E>::lo(yw[i]), acc);
+                acc = fmaf(Elem<E>::hi(xw[i]), Elem<E>::hi(yw[i]), acc);
+            }
+        }
+        return acc;
+    }
     static __device__ __forceinline__ void store(float *dst, const float *acc)
     {
         reinterpret_cast<float4 *>(dst)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -159,6 +197,10 @@ template <typename E> struct GVec16x1 {
     static __device__ __forceinline__ void fma(float a, const T &b, float *acc)
     {
         acc[0] = fmaf(a, Elem<E>::lo((unsigned)b), acc[0]);
+    }
+    static __device__ __forceinline__ float dot(const T &x, const T &y, float acc)
+    {
+        return fmaf(Elem<E>::lo((unsigned)x), Elem<E>::lo((unsigned)y), acc);
     }
     static __device__ __forceinline__ void store(float *dst, const float *acc) { *dst = acc[0]; }
 };
