@@ -263,8 +263,12 @@ sp_status_t sp_sddmm_general_workspace(int k, int d, int batch, long long stride
  * Mixed precision (fp16/bf16 operands, fp32 arithmetic).  The card's kernels
  * are fp32; 16-bit storage halves the bytes of the gathered operand, which
  * is what bounds these kernels.  Every 16-bit element is widened to fp32
- * exactly on load, products and sums are fp32 as in the fp32 entry points,
- * and outputs are fp32.
+ * exactly, a product of two 16-bit elements is exact in fp32, sums are fp32,
+ * and outputs are fp32.  Summation orders are those of the fp32 entry points,
+ * except that bf16 pairs terms: the vector SpMM adds two consecutive entries'
+ * products per column, and the vector SDDMM (and attention scores) two
+ * consecutive elements' products, to the running sum in one step
+ * (v_dot2c_f32_bf16).
  * ---------------------------------------------------------------------- */
 
 /* Element type of the 16-bit-capable operands. */

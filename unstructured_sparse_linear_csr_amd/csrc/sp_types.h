@@ -51,8 +51,9 @@ template <> struct Elem<bf16> {
 // A vector of kVec consecutive elements of type E as one load: 16 bytes
 // (4 fp32 or 8 16-bit elements) or a single element.  T is the raw register
 // form; to_f32 widens it, fma multiplies it by a scalar into kVec fp32
-// accumulators (element order 0, 1, ...), dot adds the dot product of two
-// vectors to an fp32 sum, store writes kVec fp32 results.
+// accumulators (element order 0, 1, ...), fma2 adds the products of two
+// scalars with two vectors (a0 * b0, then a1 * b1), dot adds the dot product
+// of two vectors to an fp32 sum, store writes kVec fp32 results.
 template <typename E, int kVec> struct GVec;
 
 template <> struct GVec<float, 4> {
@@ -82,6 +83,12 @@ template <> struct GVec<float, 4> {
         acc[2] = fmaf(a, b.z, acc[2]);
         acc[3] = fmaf(a, b.w, acc[3]);
     }
+    static __device__ __forceinline__ void fma2(float a0, float a1, const T &b0, const T &b1,
+                                                float *acc)
+    {
+        fma(a0, b0, acc);
+        fma(a1, b1, acc);
+    }
     // element order 0 ... 3, one FMA each
     static __device__ __forceinline__ float dot(const T &x, const T &y, float acc)
     {
@@ -108,6 +115,12 @@ template <> struct GVec<float, 1> {
     static __device__ __forceinline__ void fma(float a, const T &b, float *acc)
     {
         acc[0] = fmaf(a, b, acc[0]);
+    }
+    static __device__ __forceinline__ void fma2(float a0, float a1, const T &b0, const T &b1,
+                                                float *acc)
+    {
+        fma(a0, b0, acc);
+        fma(a1, b1, acc);
     }
     static __device__ __forceinline__ float dot(const T &x, const T &y, float acc)
     {
@@ -144,6 +157,38 @@ template <typename E> struct GVec16x8 {
         to_f32(b, f);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(a, f[i], acc[i]);
+    }
+    // fp16: a0 * b0, then a1 * b1, one FMA per element (v_fma_mix_f32).  bf16
+    // (a0 and a1 are widened bf16 values): for each column, the two products
+    // a0 * b0[j] + a1 * b1[j], both exact in fp32, are added to the sum by one
+    // v_dot2c_f32_bf16 (the two entries' elements paired by a byte permute)
+    // instead of a shift or mask plus an FMA per element.
+    static __device__ __forceinline__ void fma2(float a0, float a1, const T &b0, const T &b1,
+                                                float *acc)
+    {
+        if constexpr (__is_same(E, bf16)) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            // v_perm_b32 selectors over the byte string (second operand:
+            // bytes 0-3, first operand: bytes 4-7): the low halves of both
+            // words, or their high halves, as one (low, high) pair
+            constexpr unsigned kLoHalves = 0x05040100u, kHiHalves = 0x07060302u;
+            const bf16x2 a = __builtin_bit_cast(
+                bf16x2, __builtin_amdgcn_perm(__float_as_uint(a1), __float_as_uint(a0), kHiHalves));
+            const unsigned w0[4] = {b0.x, b0.y, b0.z, b0.w};
+            const unsigned w1[4] = {b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const unsigned lo = __builtin_amdgcn_perm(w1[i], w0[i], kLoHalves);
+                const unsigned hi = __builtin_amdgcn_perm(w1[i], w0[i], kHiHalves);
+                acc[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(
+                    a, __builtin_bit_cast(bf16x2, lo), acc[2 * i], false);
+                acc[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                    a, __builtin_bit_cast(bf16x2, hi), acc[2 * i + 1], false);
+            }
+        } else {
+            fma(a0, b0, acc);
+            fma(a1, b1, acc);
+        }
     }
     // fp16: element order 0 ... 7, one FMA each (the conversions fold into
     // v_fma_mix_f32).  bf16: gfx950's v_dot2c_f32_bf16 adds the two exact
@@ -197,6 +242,12 @@ template <typename E> struct GVec16x1 {
     static __device__ __forceinline__ void fma(float a, const T &b, float *acc)
     {
         acc[0] = fmaf(a, Elem<E>::lo((unsigned)b), acc[0]);
+    }
+    static __device__ __forceinline__ void fma2(float a0, float a1, const T &b0, const T &b1,
+                                                float *acc)
+    {
+        fma(a0, b0, acc);
+        fma(a1, b1, acc);
     }
     static __device__ __forceinline__ float dot(const T &x, const T &y, float acc)
     {

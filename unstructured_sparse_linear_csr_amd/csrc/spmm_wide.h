@@ -211,13 +211,13 @@ __device__ __forceinline__ void wide_accumulate(const SpmmParams &p, const E *__
             for (int u = 0; u < kU; ++u) bufb[u] = gather(offb[u]);
             keep_issued_above();
 #pragma unroll
-            for (int u = 0; u < kU; ++u) V::fma(vala[u], bufa[u], acc);
+            for (int u = 0; u < kU; u += 2) V::fma2(vala[u], vala[u + 1], bufa[u], bufa[u + 1], acc);
             read_batch(min(j + 2 * kU, kChunk), offa, vala);
 #pragma unroll
             for (int u = 0; u < kU; ++u) bufa[u] = gather(offa[u]);
             keep_issued_above();
 #pragma unroll
-            for (int u = 0; u < kU; ++u) V::fma(valb[u], bufb[u], acc);
+            for (int u = 0; u < kU; u += 2) V::fma2(valb[u], valb[u + 1], bufb[u], bufb[u + 1], acc);
             read_batch(min(j + 3 * kU, kChunk), offb, valb);
             j += 2 * kU;
         } while (j < wend);
