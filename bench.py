@@ -175,6 +175,25 @@ def cold_time_us(torch, fn, flush, reps: int = 10) -> float:
     return float(np.median(times))
 
 
+def latency_us(torch, fn, reps: int = 50) -> float:
+    """Median duration of single eager launches of `fn` with its operands warm
+    in the caches, each timed alone with events on the launch stream: what one
+    call costs when it is not batched into a graph."""
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(times))
+
+
 def spmm_record(name, m, k, n, nnz, us, extra=None) -> dict:
     s = us * 1e-6
     rec = {"record": "spmm", "workload": name, "m": m, "k": k, "n": n, "nnz": nnz,
@@ -509,6 +528,43 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
                      "cold_us": cold_time_us(torch, fn, flush),
                      "gflops": flops / (us * 1e-6) / 1e9,
                      "compulsory_gbs": byts / (us * 1e-6) / 1e9})
+    # Single-launch latency where launch overhead exceeds the roofline time:
+    # the tiny problem (256x256 at 80 %), the Transformer FFN and the LSTM
+    # layer at 98 %, one eager call at a time beside the graph-batched average.
+    lat = []
+    wt = inputs.tiny()
+    at = sp.csr_from_dense(up(wt["mask"]), up(wt["dense_values"]))
+    sp.row_swizzle(at)
+    bt, xt, yt = up(wt["b"]), up(wt["x"]), up(wt["y"])
+    ct = torch.empty(wt["m"], wt["n"], device=dev)
+    ot = torch.empty(at.nnz, device=dev)
+    lat.append((wt["name"], "spmm", at.nnz,
+                lambda: sp.sp_spmm(at.m, at.k, wt["n"], at.nnz, at.row_indices, at.values,
+                                   at.row_offsets, at.col_indices, bt, ct)))
+    lat.append((wt["name"], "sddmm", at.nnz,
+                lambda: sp.sp_sddmm(at.m, at.k, wt["d"], at.nnz, at.row_indices,
+                                    at.row_offsets, at.col_indices, xt, yt, 1.0, ot)))
+    wf = inputs.transformer_ffn()
+    rof, rif, colf, valf = upload_csr(torch, sp, dev, wf["a"])
+    bf, xf, yf = up(wf["b"]), up(wf["x"]), up(wf["y"])
+    cf = torch.empty(wf["m"], wf["n"], device=dev)
+    of = torch.empty(wf["a"].nnz, device=dev)
+    nf = wf["a"].nnz
+    lat.append((wf["name"], "spmm", nf,
+                lambda: sp.sp_spmm(wf["m"], wf["k"], wf["n"], nf, rif, valf, rof, colf, bf, cf)))
+    lat.append((wf["name"], "sddmm", nf,
+                lambda: sp.sp_sddmm(wf["m"], wf["k"], wf["d"], nf, rif, rof, colf, xf, yf, 1.0,
+                                    of)))
+    wl = inputs.lstm(0.98)
+    rol, ril, coll, vall = upload_csr(torch, sp, dev, wl["a"])
+    bl = up(wl["b"])
+    cl = torch.empty(wl["m"], wl["n"], device=dev)
+    nl = wl["a"].nnz
+    lat.append((wl["name"], "spmm", nl,
+                lambda: sp.sp_spmm(wl["m"], wl["k"], wl["n"], nl, ril, vall, rol, coll, bl, cl)))
+    for name, kern, nnz, fn in lat:
+        recs.append({"record": "latency", "workload": name, "kernel": kern, "nnz": nnz,
+                     "single_us": latency_us(torch, fn), "graph_us": graph_time_us(torch, fn, 200)})
     # The streaming regime: CSR far larger than every cache, n = 8 and n = 4
     # (B in LDS), natural and swizzled row order.
     for n_cols in (8, 4):
