@@ -13,8 +13,8 @@
 //   3. stages exp(s - mx) and the V-row offsets of the window in LDS and
 //      accumulates sum_j exp(s_j - mx) V[col_j] with lanes over (entry slot,
 //      16-byte vector of the V row) -- the narrow SpMM mapping.
-// After the last window the entry slots' partial sums are added by shuffles
-// and divided by l.  Every reduction has a fixed order: deterministic.  Rows
+// After the last window the entry slots' partial sums are added across lanes
+// (DPP rotations and lane swaps) and divided by l.  Every reduction has a fixed order: deterministic.  Rows
 // without entries produce zero rows (as the three-kernel pipeline does).
 //
 // Head dimensions: Q, K and V rows have the same length d, a multiple of one
@@ -32,6 +32,25 @@ namespace {
 
 constexpr unsigned kOutOfRange = 0x80000000u;  // buffer offset that reads as zero
 
+// Waves per workgroup, each its own query row: kAttnWaves consecutive slots
+// (in the row order) run on one CU, so rows that share most of their keys --
+// a banded mask's neighbouring rows -- find those K and V rows in the CU's
+// L1 cache.  Each wave has its own LDS staging region and syncs only itself.
+#ifndef SP_ATTN_WAVES
+#define SP_ATTN_WAVES 4
+#endif
+constexpr int kAttnWaves = SP_ATTN_WAVES;
+
+// Orders a wave's own LDS writes before its lanes read them (the LDS
+// operations of one wave complete in program order; the fences keep the
+// compiler from moving them across).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 struct AttnParams {
     int m, d, batch;
     const int *row_indices;
@@ -45,7 +64,7 @@ struct AttnParams {
 };
 
 template <typename E, int kDv>
-__global__ __launch_bounds__(kWave) void attention_kernel(AttnParams p)
+__global__ __launch_bounds__(kAttnWaves * kWave) void attention_kernel(AttnParams p)
 {
     constexpr int kVec = 16 / Elem<E>::kBytes;   // elements per 16-byte vector
     using V = GVec<E, kVec>;
@@ -67,15 +86,22 @@ __global__ __launch_bounds__(kWave) void attention_kernel(AttnParams p)
     static_assert(kNv * kG == kDv, "score lanes cover the row");
     // windows plus the padding read by the prefetch of up to two batches
     constexpr int kVPad = 3 * kUv * kSl;
-    __shared__ unsigned s_koff[kWave + 2 * kU * kNg];
-    __shared__ unsigned s_voff[kWave + kVPad];
-    __shared__ float s_e[kWave + kVPad];
+    __shared__ unsigned s_koff_all[kAttnWaves][kWave + 2 * kU * kNg];
+    __shared__ unsigned s_voff_all[kAttnWaves][kWave + kVPad];
+    __shared__ float s_e_all[kAttnWaves][kWave + kVPad];
 
-    const long long w = xcd_work_index(p.batch, p.m);
+    // workgroup: kAttnWaves consecutive slots of one batch entry
+    const int groups = (p.m + kAttnWaves - 1) / kAttnWaves;
+    const long long w = xcd_work_index(p.batch, groups);
     if (w < 0) return;
-    const long long z = w / p.m;
-    const int slot = (int)(w - z * p.m);
-    const int lane = threadIdx.x;
+    const long long z = w / groups;
+    const int wave = threadIdx.x / kWave;
+    const int slot = (int)(w - z * groups) * kAttnWaves + wave;
+    if (slot >= p.m) return;  // no workgroup barrier follows
+    const int lane = threadIdx.x - wave * kWave;
+    unsigned *s_koff = s_koff_all[wave];
+    unsigned *s_voff = s_voff_all[wave];
+    float *s_e = s_e_all[wave];
     const int row = p.row_indices ? p.row_indices[slot] : slot;
     const int p0 = p.row_offsets[row];
     const int p1 = p.row_offsets[row + 1];
@@ -151,7 +177,7 @@ __global__ __launch_bounds__(kWave) void attention_kernel(AttnParams p)
         const int cnt = min(kWave, p1 - base);
         const int col = lane < cnt ? p.col_indices[base + lane] : 0;
         s_koff[lane] = lane < cnt ? (unsigned)col * row_bytes : kOutOfRange;
-        __syncthreads();
+        wave_lds_sync();
         // ---- 1. scores of the window: lane (g, gl) keeps entry gl * kNg + g
         const int steps = (cnt + kNg - 1) / kNg;
         float res = 0.f;
@@ -182,7 +208,7 @@ __global__ __launch_bounds__(kWave) void attention_kernel(AttnParams p)
         // ---- 3. weighted V rows of the window
         s_e[jo] = e;
         s_voff[lane] = lane < cnt ? (unsigned)col * row_bytes : kOutOfRange;
-        __syncthreads();
+        wave_lds_sync();
         // Batches of kUv steps, double-buffered and unrolled like the score
         // phase; slots past the window read zeros with weight 0.
         const int vsteps = (cnt + kSl - 1) / kSl;
@@ -212,7 +238,7 @@ __global__ __launch_bounds__(kWave) void attention_kernel(AttnParams p)
             keep_issued_above();
             add_v(vb2, eb2);
         }
-        __syncthreads();
+        wave_lds_sync();
     }
     // entry slots' partial sums, then the normalisation
 #pragma unroll
@@ -226,8 +252,9 @@ __global__ __launch_bounds__(kWave) void attention_kernel(AttnParams p)
 template <typename E, int kDv>
 hipError_t launch_t(const AttnParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL((attention_kernel<E, kDv>), dim3((unsigned)xcd_grid(p.batch, p.m)),
-                       dim3(kWave), 0, s, p);
+    const long long groups = ((long long)p.m + kAttnWaves - 1) / kAttnWaves;
+    hipLaunchKernelGGL((attention_kernel<E, kDv>), dim3((unsigned)xcd_grid(p.batch, groups)),
+                       dim3(kAttnWaves * kWave), 0, s, p);
     return hipGetLastError();
 }
 
