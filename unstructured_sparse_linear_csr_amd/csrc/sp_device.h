@@ -68,7 +68,8 @@ struct OpMax {
 // mirrors by DPP, fused by the compiler into v_add_f32_dpp and the like; then
 // the row and half-wave swaps), with a commutative op: every lane computes
 // the same result in a fixed order, so results are deterministic.  No LDS
-// traffic.  All lanes of the wave must be active.
+// traffic.  Every lane of each group must be active; lanes of other groups
+// need not be (every source lane lies in the reading lane's own group).
 template <int kLanes, class T, class Op>
 __device__ __forceinline__ T group_reduce(T v, Op op)
 {
