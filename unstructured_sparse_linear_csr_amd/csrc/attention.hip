@@ -91,13 +91,14 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attention_kernel(AttnParam
     __shared__ float s_e_all[kAttnWaves][kWave + kVPad];
 
     // workgroup: kAttnWaves consecutive slots of one batch entry
-    const int groups = (p.m + kAttnWaves - 1) / kAttnWaves;
+    const long long groups = ((long long)p.m + kAttnWaves - 1) / kAttnWaves;
     const long long w = xcd_work_index(p.batch, groups);
     if (w < 0) return;
     const long long z = w / groups;
     const int wave = threadIdx.x / kWave;
-    const int slot = (int)(w - z * groups) * kAttnWaves + wave;
-    if (slot >= p.m) return;  // no workgroup barrier follows
+    const long long slot_ll = (w - z * groups) * kAttnWaves + wave;
+    if (slot_ll >= p.m) return;  // no workgroup barrier follows
+    const int slot = (int)slot_ll;
     const int lane = threadIdx.x - wave * kWave;
     unsigned *s_koff = s_koff_all[wave];
     unsigned *s_voff = s_voff_all[wave];

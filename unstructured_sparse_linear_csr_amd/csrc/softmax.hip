@@ -39,16 +39,17 @@ struct SoftmaxParams {
 
 __global__ __launch_bounds__(kWave) void row_softmax_kernel(SoftmaxParams p)
 {
-    const int groups = (p.m + kSmRows - 1) / kSmRows;
+    const long long groups = ((long long)p.m + kSmRows - 1) / kSmRows;
     const long long w = xcd_work_index(p.batch, groups);
     if (w < 0) return;
     const long long z = w / groups;
     const int lane = threadIdx.x;
     const int gl = lane % kSmLanes;  // lane within the row's group
-    const int slot = (int)(w - z * groups) * kSmRows + lane / kSmLanes;
+    const long long slot_ll = (w - z * groups) * kSmRows + lane / kSmLanes;
     // Groups leave independently: every cross-lane step below stays inside
     // one group's 16-lane DPP row.
-    if (slot >= p.m) return;
+    if (slot_ll >= p.m) return;
+    const int slot = (int)slot_ll;
     const int row = p.row_indices ? p.row_indices[slot] : slot;
     const int p0 = p.row_offsets[row];
     const int p1 = p.row_offsets[row + 1];

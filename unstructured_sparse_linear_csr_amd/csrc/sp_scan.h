@@ -28,17 +28,18 @@ __device__ void exclusive_scan_block(int m, const int *in, int *out)
     const int lane = tid % kWave;
     const int wave = tid / kWave;
     if (tid == 0) out[0] = 0;
-    auto load = [&](int base, int (&v)[kPer]) {
+    // 64-bit positions: m may come within a tile of 2^31 - 1
+    auto load = [&](long long base, int (&v)[kPer]) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int i = base + j * kThreads + tid;
+            const long long i = base + j * kThreads + tid;
             v[j] = i < m ? in[i] : 0;
         }
     };
     int v[kPer];
     load(0, v);
     int carry = 0;
-    for (int base = 0; base < m; base += kTile) {
+    for (long long base = 0; base < m; base += kTile) {
         int nv[kPer];
         load(base + kTile, nv);
         int incl[kPer];
@@ -59,7 +60,7 @@ __device__ void exclusive_scan_block(int m, const int *in, int *out)
                 ahead += (w < wave) ? t : 0;
                 col += t;
             }
-            const int i = base + j * kThreads + tid;
+            const long long i = base + j * kThreads + tid;
             if (i < m) out[i + 1] = run + ahead + incl[j];
             run += col;
         }
