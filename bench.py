@@ -416,6 +416,13 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
                          "cold_us": cold_time_us(torch, sfn, flush),
                          "gflops": 2.0 * a.nnz * d / (us * 1e-6) / 1e9,
                          "compulsory_gbs": sddmm_bytes(m, k, d, a.nnz) / (us * 1e-6) / 1e9})
+            bsfn = lambda: sp.sp_sddmm_balanced(m, k, d, a.nnz, order, ro, cols, x, y, 1.0, out)
+            us = graph_time_us(torch, bsfn, 200)
+            recs.append({"record": "sddmm", "workload": w["name"], "m": m, "k": k, "d": d,
+                         "nnz": a.nnz, "swizzle": swz, "kernel": "balanced", "us": us,
+                         "cold_us": cold_time_us(torch, bsfn, flush),
+                         "gflops": 2.0 * a.nnz * d / (us * 1e-6) / 1e9,
+                         "compulsory_gbs": sddmm_bytes(m, k, d, a.nnz) / (us * 1e-6) / 1e9})
         recs.append({"record": "row_swizzle", "workload": w["name"], "m": m,
                      "us": graph_time_us(torch, lambda: sp.sp_row_swizzle(m, ro, ri), 200)})
         if w["name"] != inputs.transformer_ffn()["name"]:

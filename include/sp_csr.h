@@ -202,6 +202,20 @@ sp_status_t sp_sddmm(int m, int k, int d, int nnz, const int *row_indices,
                      const float *x, const float *y, float alpha, float *out,
                      sp_stream_t stream);
 
+/* sp_sddmm for row-length distributions with a heavy tail ("Interesting
+ * ideas" I4 of the card: balancing kept separate from the kernels).  sp_sddmm
+ * gives each row one wave, which walks the row's windows of 64 entries in
+ * turn, so with every wave resident at once the longest row's chain of
+ * windows sets the duration.  Here each row slot gets a workgroup of 4 waves
+ * and wave j takes windows j, j + 4, j + 8, ... of the row; entries need no
+ * combine step, so outputs are bit-identical to sp_sddmm.  Rows of at most 64
+ * entries leave three of their four waves idle (they exit at once), which
+ * costs about nothing at these sizes.  Arguments, errors and results as
+ * sp_sddmm. */
+sp_status_t sp_sddmm_balanced(int m, int k, int d, int nnz, const int *row_indices,
+                              const int *row_offsets, const int *col_indices, const float *x,
+                              const float *y, float alpha, float *out, sp_stream_t stream);
+
 /* `batch` SDDMMs sharing one mask: x_z = x + z*stride_x, y_z = y + z*stride_y,
  * out_z = out + z*stride_out (elements).  stride_out must be >= nnz when
  * batch > 1. */

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 23, declared
+    assert len(declared) == 24, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -275,6 +275,14 @@ def test_sddmm_validation(lib):
     assert f(4, 4, 4, 0, NULL, FAKE, NULL, FAKE, FAKE, 1.0, NULL, 1, 0, 0, 0, s) == OK
     assert f(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, 1.0, NULL, 1, 0, 0, 0, s) == OK
     assert lib.sp_sddmm(4, 4, 4, 8, NULL, NULL, FAKE, FAKE, FAKE, 1.0, FAKE, s) == INVALID
+    g = lib.sp_sddmm_balanced
+    assert g(-1, 4, 4, 0, NULL, FAKE, NULL, FAKE, FAKE, 1.0, FAKE, s) == INVALID
+    assert g(4, 4, 4, 8, NULL, NULL, FAKE, FAKE, FAKE, 1.0, FAKE, s) == INVALID
+    assert g(4, 4, 4, 8, NULL, FAKE, NULL, FAKE, FAKE, 1.0, FAKE, s) == INVALID
+    assert g(4, 4, 4, 8, NULL, FAKE, FAKE, NULL, FAKE, 1.0, FAKE, s) == INVALID
+    assert g(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, NULL, 1.0, FAKE, s) == INVALID
+    assert g(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, FAKE, 1.0, NULL, s) == INVALID
+    assert g(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, 1.0, NULL, s) == OK
 
 
 def test_build_and_swizzle_validation(lib):

@@ -130,3 +130,58 @@ def test_b_beyond_2gib():
     torch.cuda.empty_cache()
     ref, s = oracle.spmm(m, used.size, n, ro, remap, vals, b_small)
     check_close(c, ref, s, "balanced 2.3 GB B")
+
+
+# ------------------------------------------------------------ sp_sddmm_balanced
+# Each row's windows of 64 entries are dealt to 4 waves; every entry's
+# arithmetic is that of sp_sddmm, so the outputs must be bit-identical to it
+# (and within the fp32 tolerance of the oracle).
+
+def run_sddmm_pair(a, x_np, y_np, alpha=1.0, ri=None):
+    d = x_np.shape[1]
+    x, y = dev(x_np), dev(y_np)
+    o1 = torch.full((a.nnz,), float("nan"), device="cuda")
+    o2 = torch.full((a.nnz,), float("nan"), device="cuda")
+    sp.sp_sddmm(a.m, a.k, d, a.nnz, ri, a.d_ro, a.d_ci, x, y, alpha, o1)
+    sp.sp_sddmm_balanced(a.m, a.k, d, a.nnz, ri, a.d_ro, a.d_ci, x, y, alpha, o2)
+    return host(o1), host(o2)
+
+
+@pytest.mark.parametrize("swz", [True, False])
+def test_sddmm_balanced_imbalance_workload(swz):
+    w = inputs.imbalance()
+    a = csr_of_row_lists(w["a"])
+    ri = swizzle(a) if swz else None
+    note(f"sddmm_balanced lognormal rows swizzle={swz}")
+    plain, bal = run_sddmm_pair(a, w["x"], w["y"], ri=ri)
+    assert np.array_equal(plain.view(np.int32), bal.view(np.int32))
+    ref, s = oracle.sddmm(a.m, a.k, w["d"], a.ro, a.ci, w["x"], w["y"])
+    check_close(bal, ref, s, f"sddmm balanced imbalance swizzle={swz}")
+
+
+def test_sddmm_balanced_transformer_ffn():
+    w = inputs.transformer_ffn()
+    a = csr_of_row_lists(w["a"])
+    note("sddmm_balanced ffn alpha=1/8")
+    plain, bal = run_sddmm_pair(a, w["x"], w["y"], alpha=0.125, ri=swizzle(a))
+    assert np.array_equal(plain.view(np.int32), bal.view(np.int32))
+    ref, s = oracle.sddmm(a.m, a.k, w["d"], a.ro, a.ci, w["x"], w["y"])
+    check_close(bal, 0.125 * ref, 0.125 * s, "sddmm balanced ffn")
+
+
+@pytest.mark.parametrize("d", [1, 3, 8, 64, 256, 600])
+def test_sddmm_balanced_row_lengths(d):
+    # rows around every window boundary up to 5 windows (wave 0 of a row then
+    # takes windows 0 and 4), a 47-window row, and empty rows
+    k = 4000
+    lengths = np.array([0, 1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 320, 0, 3000, 5, 0] * 3,
+                       dtype=np.int32)
+    m = lengths.size
+    a = csr_of_row_lists(inputs.random_row_lists(930 + d, m, k, lengths))
+    x = inputs.random_dense(931 + d, m, d)
+    y = inputs.random_dense(932 + d, k, d)
+    note(f"sddmm_balanced row lengths d={d} nnz={a.nnz}")
+    plain, bal = run_sddmm_pair(a, x, y, ri=swizzle(a))
+    assert np.array_equal(plain.view(np.int32), bal.view(np.int32))
+    ref, s = oracle.sddmm(m, k, d, a.ro, a.ci, x, y)
+    check_close(bal, ref, s, f"sddmm balanced lengths d={d}")

@@ -46,6 +46,8 @@ SIGNATURES = {
                          _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
     "sp_sddmm": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_float,
                   _vp, _vp], _c_int),
+    "sp_sddmm_balanced": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_float,
+                           _vp, _vp], _c_int),
     "sp_sddmm_batched": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                           _c_float, _vp, _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
     "sp_sddmm_general": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -206,6 +208,15 @@ def sp_sddmm(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, alpha, o
         _ptr(row_offsets, _I32, "row_offsets"), _ptr(col_indices, _I32, "col_indices", True),
         _ptr(x, _F32, "x", True), _ptr(y, _F32, "y", True), float(alpha),
         _ptr(out, _F32, "out", True), _stream(stream)), "sp_sddmm")
+
+
+def sp_sddmm_balanced(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, alpha, out,
+                      stream=None):
+    _check(lib().sp_sddmm_balanced(
+        m, k, d, nnz, _ptr(row_indices, _I32, "row_indices", True),
+        _ptr(row_offsets, _I32, "row_offsets"), _ptr(col_indices, _I32, "col_indices", True),
+        _ptr(x, _F32, "x", True), _ptr(y, _F32, "y", True), float(alpha),
+        _ptr(out, _F32, "out", True), _stream(stream)), "sp_sddmm_balanced")
 
 
 def sp_sddmm_batched(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, alpha,

@@ -22,6 +22,14 @@ __global__ __launch_bounds__(kWave) void sddmm_kernel(SddmmParams p)
     sddmm_rows_body<E, kG, kNv, kVec, kSoftmax>(p, rows_work(p, blockIdx.x));
 }
 
+// A workgroup of kSplitParts waves per row slot, sharing the row's windows.
+constexpr int kSplitParts = 4;
+template <typename E, int kG, int kNv, int kVec>
+__global__ __launch_bounds__(kSplitParts * kWave) void sddmm_split_kernel(SddmmParams p)
+{
+    sddmm_rows_body<E, kG, kNv, kVec, false, kSplitParts>(p, rows_work(p, blockIdx.x));
+}
+
 // Y stored d x k (the operand not transposed): Yop(c, l) = Y[l][c].  One wave
 // per row slot as above, but lanes are dealt to entries, 64 at a time: for each
 // l the wave gathers Y[l][c] of its 64 columns -- all within row l of Y, whose
@@ -138,44 +146,53 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *dst, long long co
 }
 
 template <typename E, int kG, int kNv, int kVec, bool kSm>
-hipError_t launch_t(const SddmmParams &p, hipStream_t s)
+hipError_t launch_t(const SddmmParams &p, bool split, hipStream_t s)
 {
     dim3 grid((unsigned)rows_grid(p));
+    if constexpr (!kSm) {
+        if (split) {
+            hipLaunchKernelGGL((sddmm_split_kernel<E, kG, kNv, kVec>), grid,
+                               dim3(kSplitParts * kWave), 0, s, p);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((sddmm_kernel<E, kG, kNv, kVec, kSm>), grid, dim3(kWave), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename E, int kG, int kVec, bool kSm>
-hipError_t launch_nv(int nv, const SddmmParams &p, hipStream_t s)
+hipError_t launch_nv(int nv, const SddmmParams &p, bool split, hipStream_t s)
 {
     switch (nv) {
-    case 1: return launch_t<E, kG, 1, kVec, kSm>(p, s);
-    case 2: return launch_t<E, kG, 2, kVec, kSm>(p, s);
-    case 4: return launch_t<E, kG, 4, kVec, kSm>(p, s);
-    case 8: return launch_t<E, kG, 8, kVec, kSm>(p, s);
-    default: return launch_t<E, kG, 0, kVec, kSm>(p, s);
+    case 1: return launch_t<E, kG, 1, kVec, kSm>(p, split, s);
+    case 2: return launch_t<E, kG, 2, kVec, kSm>(p, split, s);
+    case 4: return launch_t<E, kG, 4, kVec, kSm>(p, split, s);
+    case 8: return launch_t<E, kG, 8, kVec, kSm>(p, split, s);
+    default: return launch_t<E, kG, 0, kVec, kSm>(p, split, s);
     }
 }
 
 template <typename E, int kVec, bool kSm>
-hipError_t launch_g(int g, int nv, const SddmmParams &p, hipStream_t s)
+hipError_t launch_g(int g, int nv, const SddmmParams &p, bool split, hipStream_t s)
 {
     switch (g) {
-    case 4: return launch_nv<E, 4, kVec, kSm>(nv, p, s);
-    case 8: return launch_nv<E, 8, kVec, kSm>(nv, p, s);
-    default: return launch_nv<E, 16, kVec, kSm>(nv, p, s);
+    case 4: return launch_nv<E, 4, kVec, kSm>(nv, p, split, s);
+    case 8: return launch_nv<E, 8, kVec, kSm>(nv, p, split, s);
+    default: return launch_nv<E, 16, kVec, kSm>(nv, p, split, s);
     }
 }
 
 // Element type E: 16-byte vectors of kVec16 elements, or single elements;
 // scores written as they are, or row-softmaxed.
 template <typename E, int kVec16>
-hipError_t launch_typed(bool vec, bool softmax, int g, int nv, const SddmmParams &p,
-                        hipStream_t s)
+hipError_t launch_typed(bool vec, bool softmax, bool split, int g, int nv,
+                        const SddmmParams &p, hipStream_t s)
 {
     if (softmax)
-        return vec ? launch_g<E, kVec16, true>(g, nv, p, s) : launch_g<E, 1, true>(g, nv, p, s);
-    return vec ? launch_g<E, kVec16, false>(g, nv, p, s) : launch_g<E, 1, false>(g, nv, p, s);
+        return vec ? launch_g<E, kVec16, true>(g, nv, p, false, s)
+                   : launch_g<E, 1, true>(g, nv, p, false, s);
+    return vec ? launch_g<E, kVec16, false>(g, nv, p, split, s)
+               : launch_g<E, 1, false>(g, nv, p, split, s);
 }
 
 template <typename E>
@@ -214,11 +231,13 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
     plan->kind = SddmmPlan::kNothing;
     plan->dtype = a.dtype;
     plan->softmax = false;
+    plan->split = false;
     plan->t_src = nullptr;
     plan->t_src_stride = 0;
     plan->t_batch = 0;
     if (a.m == 0 || a.nnz == 0) return hipSuccess;
     if (xcd_grid(a.batch, a.m) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    plan->split = !a.softmax && a.parts > 1;  // the softmax needs whole rows
     SddmmParams &p = plan->p;
     p.m = a.m;
     p.batch = a.batch;
@@ -317,11 +336,12 @@ hipError_t run_sddmm(const SddmmPlan &plan, hipStream_t stream)
     default:
         break;
     }
-    const bool sm = plan.softmax;
+    const bool sm = plan.softmax, sp = plan.split;
     switch (plan.dtype) {
-    case Dtype::f16: return launch_typed<_Float16, 8>(plan.vec, sm, plan.g, plan.nv, p, stream);
-    case Dtype::bf16: return launch_typed<bf16, 8>(plan.vec, sm, plan.g, plan.nv, p, stream);
-    default: return launch_typed<float, 4>(plan.vec, sm, plan.g, plan.nv, p, stream);
+    case Dtype::f16:
+        return launch_typed<_Float16, 8>(plan.vec, sm, sp, plan.g, plan.nv, p, stream);
+    case Dtype::bf16: return launch_typed<bf16, 8>(plan.vec, sm, sp, plan.g, plan.nv, p, stream);
+    default: return launch_typed<float, 4>(plan.vec, sm, sp, plan.g, plan.nv, p, stream);
     }
 }
 

@@ -25,6 +25,14 @@
 // Staging.  The window's 64 column indices are read with one coalesced load and
 // kept in LDS as Y-row offsets (bytes when k*d < 2^30).
 //
+// Long rows.  With kParts > 1, each row slot gets a workgroup of kParts waves
+// and wave j takes the row's windows j, j + kParts, j + 2 kParts, ...: an
+// entry's output never depends on other entries, so windows need no combine
+// step, and a row of many windows no longer runs in one wave.  Each wave loads
+// the X row itself, stages in its own LDS region and syncs only itself; waves
+// without a window leave at once.  The arithmetic of every entry is the same
+// for any kParts (bit-identical outputs).
+//
 // Summation order: each lane sums its elements in order with FMA (bf16: by
 // pairs, v_dot2c_f32_bf16), then the DPP tree adds the kG lane partials;
 // deterministic run to run.
@@ -83,9 +91,25 @@ constexpr unsigned kOutOfRange = 0x80000000u;  // buffer offset that reads as ze
 // to kHeldWindows windows and parks later windows' scores in `out`; after the
 // last window it reduces the row maximum and the sum of exp(s - max) across
 // the wave (butterflies, fixed order) and writes exp(s - max) / sum.
-template <typename E, int kG, int kNv, int kVec, bool kSoftmax = false>
+// The staging barrier between windows: the workgroup's when it is one wave,
+// else only the wave's own (its LDS operations complete in program order; the
+// fences keep the compiler from moving them across).
+template <int kParts>
+__device__ __forceinline__ void rows_sync()
+{
+    if constexpr (kParts == 1) {
+        __syncthreads();
+    } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+template <typename E, int kG, int kNv, int kVec, bool kSoftmax = false, int kParts = 1>
 __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long w)
 {
+    static_assert(!(kSoftmax && kParts > 1), "the row softmax needs the whole row in one wave");
     using V = GVec<E, kVec>;
     using VecT = typename V::T;
     constexpr unsigned kEb = Elem<E>::kBytes;
@@ -96,7 +120,7 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
     // The window's 64 entries, then padding for the prefetch of up to two
     // batches past the last step.
     constexpr int kSlots = kWave + 2 * kU * kNg;
-    __shared__ unsigned s_off[kSlots];
+    __shared__ unsigned s_off_all[kParts][kSlots];
 
     constexpr int kHeldWindows = 4;
     float held[kHeldWindows];
@@ -106,13 +130,17 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
     if (w < 0) return;
     const long long z = w / p.m;
     const int slot = (int)(w - z * p.m);
-    const int lane = threadIdx.x;
+    const int part = kParts == 1 ? 0 : (int)threadIdx.x / kWave;  // this wave's windows
+    const int lane = kParts == 1 ? (int)threadIdx.x : (int)threadIdx.x % kWave;
+    unsigned *s_off = s_off_all[part];
     const int g = lane / kG;
     const int gl = lane - g * kG;
     const int row = p.row_indices ? p.row_indices[slot] : slot;
     const int p0 = p.row_offsets[row];
     const int p1 = p.row_offsets[row + 1];
-    if (p0 >= p1) return;  // one row per wave: uniform, before any barrier
+    // this wave's windows: part, part + kParts, ... of the row's nwin
+    const int nwin = (int)(((long long)p1 - p0 + kWave - 1) / kWave);
+    if (part >= nwin) return;  // one row per wave: uniform, before any barrier
 
     const E *__restrict__ xr_ptr =
         static_cast<const E *>(p.x) + z * p.stride_x + (size_t)row * (size_t)p.d;
@@ -134,11 +162,13 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
     };
 
     if constexpr (kNv == 0) {
-        __shared__ int s_col[kWave];
-        for (int base = p0; base < p1; base += kWave) {
+        __shared__ int s_col_all[kParts][kWave];
+        int *s_col = s_col_all[part];
+        for (int wi = part; wi < nwin; wi += kParts) {
+            const int base = p0 + wi * kWave;
             const int cnt = min(kWave, p1 - base);
             s_col[lane] = lane < cnt ? p.col_indices[base + lane] : 0;
-            __syncthreads();
+            rows_sync<kParts>();
             const int steps = (cnt + kNg - 1) / kNg;
             float res = 0.f;
             for (int s = 0; s < steps; ++s) {
@@ -155,7 +185,7 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
             }
             const int jo = gl * kNg + g;
             if (jo < cnt) emit(base + jo, res);
-            __syncthreads();
+            rows_sync<kParts>();
             ++window;
         }
     } else {
@@ -190,12 +220,13 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
             }
         };
 
-        for (int base = p0; base < p1; base += kWave) {
+        for (int wi = part; wi < nwin; wi += kParts) {
+            const int base = p0 + wi * kWave;
             const int cnt = min(kWave, p1 - base);
             s_off[lane] = lane < cnt
                               ? (unsigned)p.col_indices[base + lane] * (unsigned)p.d * kEb
                               : kOutOfRange;
-            __syncthreads();
+            rows_sync<kParts>();
             const int steps = (cnt + kNg - 1) / kNg;
             float res = 0.f;
             // A window has at most kG steps, so its batches are unrolled into
@@ -216,7 +247,7 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
             }
             const int jo = gl * kNg + g;  // the entry whose sum this lane kept
             if (jo < cnt) emit(base + jo, res);
-            __syncthreads();
+            rows_sync<kParts>();
             ++window;
         }
     }
@@ -247,7 +278,10 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
 }
 
 // Workgroups of the row launch, and the work index of workgroup `block`.
-inline long long rows_grid(const SddmmParams &p) { return xcd_grid(p.batch, p.m); }
+inline long long rows_grid(const SddmmParams &p)
+{
+    return xcd_grid(p.batch, p.m);
+}
 __device__ __forceinline__ long long rows_work(const SddmmParams &p, long long block)
 {
     return xcd_work_index_of(block, p.batch, p.m);

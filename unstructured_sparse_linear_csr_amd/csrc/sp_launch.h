@@ -37,6 +37,7 @@ struct SddmmArgs {
     long long stride_values, stride_x, stride_y, stride_out;  // elements
     Dtype dtype = Dtype::f32;
     bool softmax = false;  // row softmax of alpha * scores (k x d layout, no v, beta 0)
+    int parts = 1;         // > 1: waves sharing each row's 64-entry windows (not with softmax)
     void *workspace = nullptr;  // Y stored d x k: room for its k x d transpose, or NULL
 };
 

@@ -24,6 +24,7 @@ struct SddmmPlan {
     Dtype dtype;
     bool vec, buf;
     bool softmax;  // rows kernel: row softmax of the scores before they are written
+    bool split;    // rows kernel: a workgroup of waves per row, sharing its windows
     int g, nv;     // rows kernel: lanes per entry, vectors per lane (0: generic loop)
     // Y stored d x k with a workspace: transpose it into p.y first
     const void *t_src;        // NULL: no transpose
