@@ -85,7 +85,7 @@ def test_graph_of_every_launch_kind():
     t_p = torch.empty(nnz, dtype=torch.int32, device="cuda")
     t_ri = torch.empty(k, dtype=torch.int32, device="cuda")
     outs = {name: torch.empty(shape, device="cuda") for name, shape in {
-        "c": (m, n), "c_bal": (m, n), "c_bf16": (m, n), "dx": (k, n), "s": (nnz,),
+        "c": (m, n), "c_bal": (m, n), "c_bf16": (m, n), "dx": (k, n), "s": (nnz,), "s_bal": (nnz,),
         "s_gen": (nnz,), "s_dk": (nnz,), "s_dkw": (nnz,), "p": (nnz,), "att": (m, d), "c_pair": (m, n),
         "s_pair": (nnz,)}.items()}
     b16, v16 = b.to(torch.bfloat16), vals.to(torch.bfloat16)
@@ -99,6 +99,7 @@ def test_graph_of_every_launch_kind():
         sp.sp_spmm_balanced(m, k, n, nnz, ri, vals, ro, cols, b, outs["c_bal"])
         sp.sp_spmm_ex(m, k, n, nnz, ri, v16, ro, cols, b16, outs["c_bf16"])
         sp.sp_sddmm(m, k, d, nnz, ri, ro, cols, x, y, 1.0, outs["s"])
+        sp.sp_sddmm_balanced(m, k, d, nnz, ri, ro, cols, x, y, 1.0, outs["s_bal"])
         outs["s_gen"].copy_(prior)
         sp.sp_sddmm_general(m, k, d, nnz, ri, ro, cols, vals, x, y, sp.SP_Y_KD, 0.5, 2.0,
                             outs["s_gen"])
