@@ -60,6 +60,10 @@ def test_offsets_from_lengths_bit_exact():
         "single_row": np.array([7], np.int32),
         "all_empty": np.zeros(5000, np.int32),
         "m0": np.zeros(0, np.int32),
+        # either side of a 2,048-element scan tile
+        "tile_edge_2047": np.random.default_rng(3).integers(0, 600, 2047).astype(np.int32),
+        "tile_edge_2049": np.random.default_rng(4).integers(0, 600, 2049).astype(np.int32),
+        "tiles_6144": np.random.default_rng(5).integers(0, 600, 6144).astype(np.int32),
     }
     for name, lengths in cases.items():
         note(f"offsets_from_lengths {name} m={lengths.shape[0]}")
@@ -124,6 +128,11 @@ def _swizzle_cases():
         "one": np.array([3], np.int32),
         "all_equal": np.full(300, 2, np.int32),
         "zeros": np.zeros(17, np.int32),
+        # the scan tile edge, and either side of the switch from 32 to 16
+        # lanes per row in the rank sort
+        "tile_edge_2049": rng.integers(0, 600, 2049).astype(np.int32),
+        "few_rows_4096": rng.integers(0, 40, 4096).astype(np.int32),
+        "few_rows_4097": rng.integers(0, 40, 4097).astype(np.int32),
     }
 
 
@@ -659,13 +668,18 @@ def _check_softmax(got, ro, s, what):
     assert np.all(err <= bound), f"{what}: worst {np.max(err / np.maximum(bound, 1e-300)):.3g}"
 
 
-@pytest.mark.parametrize("case", ["short", "long", "mixed_empty"])
+@pytest.mark.parametrize("case", ["short", "long", "mixed_empty", "held_edge"])
 def test_row_softmax(case):
-    rng = np.random.default_rng({"short": 90, "long": 91, "mixed_empty": 92}[case])
+    rng = np.random.default_rng({"short": 90, "long": 91, "mixed_empty": 92,
+                                 "held_edge": 94}[case])
     if case == "short":
         lengths = rng.integers(1, 80, 700)
     elif case == "long":
         lengths = rng.integers(250, 900, 60)          # beyond the register-held path
+    elif case == "held_edge":
+        # rows either side of the 128 entries a 16-lane group holds in
+        # registers, one per lane group and mixed within waves; m = 4q + 3
+        lengths = np.tile(np.array([127, 128, 129, 1, 16, 17, 300], np.int32), 41)[:287]
     else:
         lengths = rng.integers(0, 400, 500)
         lengths[::7] = 0
