@@ -782,7 +782,8 @@ def main() -> int:
         result["ceilings"] = probes.measure(torch, stream_bytes=431164900,
                                             b_bytes=512 * 256 * 4)
         ceil = result["ceilings"]
-        log(f"ceilings: stream read {ceil['stream_read_gbs']:.0f} GB/s; 1 KB row gathers "
+        log(f"ceilings: stream read {ceil['stream_read_gbs']:.0f} GB/s (two arrays side by "
+            f"side {ceil['stream_read2_gbs']:.0f} GB/s); 1 KB row gathers "
             + ", ".join(f"{k} {v:.1f} TB/s" for k, v in ceil["row_gather_tbs"].items())
             + f"; empty launch {ceil['launch_floor_us']:.2f} us")
 

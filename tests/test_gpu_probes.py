@@ -24,6 +24,14 @@ def test_probe_arithmetic():
                                   ctypes.c_void_p(out.data_ptr()), cs) == 0
     torch.cuda.synchronize()
     assert out.sum().item() == pytest.approx(0.5 * a.numel(), rel=1e-6)
+    note("probe two-array stream read over 8 + 8 MB")
+    a2 = torch.full((1 << 21,), 0.25, device="cuda")        # 8 MB of 0.25
+    a1 = torch.full((1 << 21,), 0.5, device="cuda")         # 8 MB of 0.5
+    assert l.sp_probe_stream_read2(ctypes.c_void_p(a1.data_ptr()), ctypes.c_void_p(a2.data_ptr()),
+                                   a1.numel() * 4, 64, ctypes.c_void_p(out.data_ptr()), cs) == 0
+    torch.cuda.synchronize()
+    assert out.sum().item() == pytest.approx(0.75 * a1.numel(), rel=1e-6)
+    assert l.sp_probe_stream_read2(None, None, 16, 1, None, cs) != 0  # host-side check
     note("probe row gather of 1 KB rows")
     b = torch.ones(64 * 1024 // 4, device="cuda")           # 64 rows of 1 KB
     waves, per_wave = 96, 37
@@ -42,5 +50,6 @@ def test_probe_measure():
     note("probe measure")
     c = probes.measure(torch, stream_bytes=64 << 20)
     assert math.isfinite(c["stream_read_gbs"]) and c["stream_read_gbs"] > 0
+    assert math.isfinite(c["stream_read2_gbs"]) and c["stream_read2_gbs"] > 0
     assert all(math.isfinite(v) and v > 0 for v in c["row_gather_tbs"].values())
     assert 0 < c["launch_floor_us"] < 1000

@@ -29,9 +29,11 @@ def lib():
         l = ctypes.CDLL(PROBE_LIB)
         vp, ci, cll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
         l.sp_probe_stream_read.argtypes = [vp, cll, ci, vp, vp]
+        l.sp_probe_stream_read2.argtypes = [vp, vp, cll, ci, vp, vp]
         l.sp_probe_row_gather.argtypes = [vp, ci, ci, vp, ctypes.c_uint, vp, vp]
         l.sp_probe_empty.argtypes = [ci, vp]
-        for f in (l.sp_probe_stream_read, l.sp_probe_row_gather, l.sp_probe_empty):
+        for f in (l.sp_probe_stream_read, l.sp_probe_stream_read2, l.sp_probe_row_gather,
+                  l.sp_probe_empty):
             f.restype = ci
         _lib = l
     return _lib
@@ -81,6 +83,19 @@ def measure(torch, stream_bytes: int, b_bytes: int = 512 * 1024, seed: int = 0) 
             cs()), "sp_probe_stream_read"), 10)
         best_read = max(best_read, a.numel() / (us * 1e-6) / 1e9)
     del a
+    # the same bytes as two arrays of half the size, read side by side (a CSR's
+    # column indices and values)
+    half = stream_bytes // 2 // 16 * 16
+    a1 = torch.zeros(half, dtype=torch.uint8, device=dev)
+    a2 = torch.zeros(half, dtype=torch.uint8, device=dev)
+    best_read2 = 0.0
+    for blocks in (2048, 8192, 16384):
+        out = torch.empty(blocks * 256, device=dev)
+        us = _graph_us(torch, lambda: _check(l.sp_probe_stream_read2(
+            ctypes.c_void_p(a1.data_ptr()), ctypes.c_void_p(a2.data_ptr()), half, blocks,
+            ctypes.c_void_p(out.data_ptr()), cs()), "sp_probe_stream_read2"), 10)
+        best_read2 = max(best_read2, 2 * half / (us * 1e-6) / 1e9)
+    del a1, a2
     b = torch.ones(b_bytes // 4, device=dev)
     rng = np.random.default_rng(seed)
     gathers = {}
@@ -94,7 +109,8 @@ def measure(torch, stream_bytes: int, b_bytes: int = 512 * 1024, seed: int = 0) 
             b_bytes, ctypes.c_void_p(out.data_ptr()), cs()), "sp_probe_row_gather"), 20)
         gathers[f"{waves}x{per_wave}"] = waves * per_wave * 1024 / (us * 1e-6) / 1e12
     floor = _graph_us(torch, lambda: _check(l.sp_probe_empty(2048, cs()), "sp_probe_empty"), 200)
-    return {"stream_read_gbs": best_read, "stream_bytes": stream_bytes,
+    return {"stream_read_gbs": best_read, "stream_read2_gbs": best_read2,
+            "stream_bytes": stream_bytes,
             "row_gather_tbs": gathers, "row_gather_b_bytes": b_bytes,
             "launch_floor_us": floor,
             "note": "ceilings measured on this GPU by plain probe kernels (libsp_probes.so); "

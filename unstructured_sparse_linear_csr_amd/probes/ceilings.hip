@@ -32,6 +32,37 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const float4 *__restri
     out[(long long)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// The same over two arrays read side by side: each trip loads kUnroll / 2
+// vectors at the same positions of a and of b -- the access pattern of a CSR
+// whose column-index and value arrays are streamed together.
+template <int kUnroll>
+__global__ __launch_bounds__(256) void stream_read2_kernel(const float4 *__restrict__ a,
+                                                           const float4 *__restrict__ b,
+                                                           long long n4, float *__restrict__ out)
+{
+    constexpr int kHalf = kUnroll / 2;
+    float s = 0.f;
+    const long long stride = (long long)gridDim.x * 256;
+    long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    for (; i + (kHalf - 1) * stride < n4; i += kHalf * stride) {
+        float4 va[kHalf], vb[kHalf];
+#pragma unroll
+        for (int u = 0; u < kHalf; ++u) {
+            va[u] = a[i + u * stride];
+            vb[u] = b[i + u * stride];
+        }
+#pragma unroll
+        for (int u = 0; u < kHalf; ++u)
+            s += ((va[u].x + va[u].y) + (va[u].z + va[u].w)) +
+                 ((vb[u].x + vb[u].y) + (vb[u].z + vb[u].w));
+    }
+    for (; i < n4; i += stride) {
+        const float4 va = a[i], vb = b[i];
+        s += ((va.x + va.y) + (va.z + va.w)) + ((vb.x + vb.y) + (vb.z + vb.w));
+    }
+    out[(long long)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 // One wave per workgroup gathers per_wave rows of 1 KB (64 lanes x 16 bytes)
 // of B at the byte offsets offs[wave * per_wave + j], kUnroll rows in flight,
 // through a buffer resource as the sparse kernels do.
@@ -78,6 +109,19 @@ int sp_probe_stream_read(const void *a, long long bytes, int blocks, float *out,
     hipLaunchKernelGGL(stream_read_kernel<8>, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<const float4 *>(a),
                        bytes / 16, out);
+    return (int)hipGetLastError();
+}
+
+// a and b: bytes_each bytes each (whole 16-byte vectors are read);
+// out: float[blocks * 256].
+int sp_probe_stream_read2(const void *a, const void *b, long long bytes_each, int blocks,
+                          float *out, void *stream)
+{
+    if (a == nullptr || b == nullptr || out == nullptr || bytes_each < 16 || blocks <= 0)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_read2_kernel<8>, dim3((unsigned)blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const float4 *>(a),
+                       static_cast<const float4 *>(b), bytes_each / 16, out);
     return (int)hipGetLastError();
 }
 
