@@ -241,3 +241,60 @@ def test_spmm_b_beyond_2gib(kind):
     torch.cuda.empty_cache()
     ref, s = oracle.spmm(m, used.size, n, ro, remap, v, b_small)
     check_close(got, ref, s, f"spmm {kind} 2.2 GB B")
+
+
+# ------------------------------------------------------ the streaming (LDS) kernel
+# Narrow 16-bit B with many entries per B element takes the streaming kernel:
+# B widened to fp32 in LDS, values read as 2-byte loads and widened.
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_spmm_lds_resident_b(kind, n):
+    m, k = 8192, 256
+    lengths = np.random.default_rng(700 + n).integers(100, 220, m).astype(np.int32)
+    lengths[::97] = 0                                   # some empty rows
+    # nnz = 3 (mod 4) with a non-empty last row: the array's final segment
+    # extends past nnz (read from its last 4 entries), and nnz is odd
+    lengths[-1] += (3 - int(lengths.sum()) % 4) % 4
+    assert int(lengths.sum()) % 4 == 3 and lengths[-1] > 0
+    rl = inputs.random_row_lists(701 + n, m, k, lengths)
+    ro = oracle.csr_offsets_from_lengths(lengths)
+    b32 = inputs.random_dense(702 + n, k, n)
+    note(f"spmm_ex {kind} lds-resident B n={n} nnz={rl.cols.size}")
+    c, v, b = spmm16(kind, m, k, n, ro, rl.cols, rl.values, b32)
+    ref, s = oracle.spmm(m, k, n, ro, rl.cols, v, b)
+    check_close(c, ref, s, f"spmm {kind} lds n={n}")
+    # one-entry rows through the same kernel: one exact product each
+    m1 = 1100000
+    rl1 = inputs.random_row_lists(703 + n, m1, k, np.ones(m1, np.int32))
+    ro1 = oracle.csr_offsets_from_lengths(rl1.lengths)
+    note(f"spmm_ex {kind} lds-resident B one-entry rows n={n}")
+    c1, v1, b1 = spmm16(kind, m1, k, n, ro1, rl1.cols, rl1.values, b32, swz=False)
+    want = (v1.astype(np.float64)[:, None] * b1.astype(np.float64)[rl1.cols]).astype(np.float32)
+    assert np.array_equal(c1, want)
+
+
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+@pytest.mark.parametrize("k,n,m", [(8192, 8, 16384), (8192, 12, 10000)])
+def test_spmm_lds_column_slices(kind, k, n, m):
+    # B of k x n does not fit in LDS as fp32: column slices (8 + 4 columns for n = 12)
+    lengths = np.random.default_rng(710 + n).integers(300, 700, m).astype(np.int32)
+    rl = inputs.random_row_lists(711 + n, m, k, lengths)
+    ro = oracle.csr_offsets_from_lengths(lengths)
+    b32 = inputs.random_dense(712 + n, k, n)
+    note(f"spmm_ex {kind} lds column slices k={k} n={n} m={m} nnz={rl.cols.size}")
+    c, v, b = spmm16(kind, m, k, n, ro, rl.cols, rl.values, b32)
+    ref, s = oracle.spmm(m, k, n, ro, rl.cols, v, b)
+    check_close(c, ref, s, f"spmm {kind} lds slices k={k} n={n}")
+
+
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_spmm_hbm_stream_n4_sampled_rows(kind):
+    w = inputs.hbm_stream(n=4)
+    a = w["a"]
+    ro = oracle.csr_offsets_from_lengths(a.lengths)
+    note(f"spmm_ex {kind} hbm_stream 65536x8192x4 (B in LDS)")
+    c, v, b = spmm16(kind, w["m"], w["k"], w["n"], ro, a.cols, a.values, w["b"], swz=False)
+    rows = np.random.default_rng(720).choice(w["m"], 300, replace=False)
+    ref, s = oracle.spmm_rows(rows, w["n"], ro, a.cols, v, b)
+    check_close(c[rows], ref, s, f"spmm {kind} hbm_stream n=4")

@@ -279,13 +279,22 @@ __global__ __launch_bounds__(kWave) void spmm_narrow_kernel(SpmmParams p)
 // stands in for the entries of a segment that lie outside the row (with value
 // 0): every entry slot is one unconditional LDS read and FMA, adding +0
 // exactly, with no branch, so a batch's reads are all issued before its FMAs.
+// E is the element type of the values and of B: fp16 and bf16 B is widened
+// to fp32 as it is copied into LDS (the LDS layout, reads and FMAs are those of
+// fp32), and a segment's four 16-bit values are read with one 8-byte buffer
+// load and widened when consumed: the CSR then streams 6 bytes per entry
+// instead of 8.  In the 16-bit form every segment, the array's last included,
+// is read from its own first entry: its 4-byte words past the end of the
+// column array (or past the value array rounded up to whole words) are out of
+// the buffer's range and read as zeros.
 constexpr int kLdsThreads = 1024;
 constexpr int kLdsWaves = kLdsThreads / kWave;
 constexpr unsigned kLdsMaxB = 128u * 1024u;
 
-template <int kE, int kVec>
+template <typename E, int kE, int kVec>
 __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
 {
+    constexpr unsigned kEb = Elem<E>::kBytes;
     using V = Vec<kVec>;
     using VecT = typename V::T;
     constexpr int kS = kWave / kE;  // segment slots per step
@@ -307,13 +316,28 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
 
     // ---- B's slice into LDS, k x width row-major
     const int tid = threadIdx.x;
-    const VecT *__restrict__ bsrc = static_cast<const VecT *>(p.b);
     VecT *s_bv = reinterpret_cast<VecT *>(s_b);
     const int total = p.k * wv;
     if (tid == 0) s_bv[total] = VecT{};  // the zero vector
-    if (n_slices == 1) {
+    if constexpr (kEb == 2) {
+        // 16-bit B: vector i of the slice holds B[r][col .. col + kVec) widened
+        const E *__restrict__ b16 = static_cast<const E *>(p.b);
+        for (int i = tid; i < total; i += kLdsThreads) {
+            const int r = i / wv;
+            const E *src = b16 + (size_t)r * p.n + col_base + (i - r * wv) * kVec;
+            if constexpr (kVec == 4) {
+                const uint2 u = *reinterpret_cast<const uint2 *>(src);  // 8-byte aligned
+                s_bv[i] = make_float4(Elem<E>::lo(u.x), Elem<E>::hi(u.x), Elem<E>::lo(u.y),
+                                      Elem<E>::hi(u.y));
+            } else {
+                s_bv[i] = Elem<E>::f32(*src);
+            }
+        }
+    } else if (n_slices == 1) {
+        const VecT *__restrict__ bsrc = static_cast<const VecT *>(p.b);
         for (int i = tid; i < total; i += kLdsThreads) s_bv[i] = bsrc[i];
     } else {
+        const VecT *__restrict__ bsrc = static_cast<const VecT *>(p.b);
         const int nv_all = p.n / kVec, vbase = col_base / kVec;
         for (int i = tid; i < total; i += kLdsThreads) {
             const int r = i / wv;
@@ -329,8 +353,11 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
     const bool col_ok = col0 < width;
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int *>(p.col_indices), 0, (int)p.csr_bytes, 0x00020000);
+    // 16-bit values: the range is rounded up to whole dwords (the array's last
+    // dword may hold one value and 2 bytes beyond it, within the same page)
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void *>(p.values), 0, (int)p.csr_bytes, 0x00020000);
+        const_cast<void *>(p.values), 0,
+        (int)(kEb == 4 ? p.csr_bytes : (p.csr_bytes / 2u + 3u) & ~3u), 0x00020000);
     const int last4 = p.nnz - 4;  // first entry of the array's last full segment (nnz >= 4)
 
     const int *__restrict__ order = p.row_indices;
@@ -377,13 +404,24 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
         for (int u = 0; u < kSteps; ++u) {
             const int e = b.base + (u * kS + s) * 4;
             const bool any = e < b.p1;
+            // fp32: the array's last segment is read from its last 4 entries;
+            // 16-bit: from the segment's own start, its dwords past the end
+            // reading as zeros (range-checked per dword)
             const unsigned off = !any ? kOutOfRange
-                                      : (unsigned)(e + 4 <= p.nnz ? e : last4) * 4u;
+                                      : (unsigned)(kEb == 2 || e + 4 <= p.nnz ? e : last4) * 4u;
             const auto c4 = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)off, 0, 0);
-            const auto v4 = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off, 0, 0);
             sg[u].c = make_int4((int)c4[0], (int)c4[1], (int)c4[2], (int)c4[3]);
-            sg[u].v = make_float4(__uint_as_float(v4[0]), __uint_as_float(v4[1]),
-                                  __uint_as_float(v4[2]), __uint_as_float(v4[3]));
+            if constexpr (kEb == 4) {
+                const auto v4 = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off, 0, 0);
+                sg[u].v = make_float4(__uint_as_float(v4[0]), __uint_as_float(v4[1]),
+                                      __uint_as_float(v4[2]), __uint_as_float(v4[3]));
+            } else {
+                // the four raw 16-bit values in two dwords, widened only when
+                // consumed (so that no instruction here waits for the load)
+                const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(
+                    rv, (int)(off == kOutOfRange ? kOutOfRange : off / 2u), 0, 0);
+                sg[u].v = make_float4(__uint_as_float(v2[0]), __uint_as_float(v2[1]), 0.f, 0.f);
+            }
         }
     };
     const unsigned row_bytes = (unsigned)wv * sizeof(VecT);   // one row of B in LDS
@@ -393,18 +431,25 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
             const int e = b.base + (u * kS + s) * 4;
-            // The segment was loaded from entry e_ld: e, or last4 for the
+            // The segment was loaded from entry e_ld: e, or (fp32) last4 for the
             // array's final segment (whose positions before e belong to the
             // segment before it).  Position t holds entry e_ld + t, which is
             // this lane's when lo <= e_ld + t < p1 with lo = max(p0, e); an
             // idle lane (no column vector) takes none.
-            const int e_ld = e + 4 <= p.nnz ? e : last4;
+            const int e_ld = kEb == 2 || e + 4 <= p.nnz ? e : last4;
             const int lo = max(b.p0, e);
             const unsigned span = (col_ok && b.p1 > lo) ? (unsigned)(b.p1 - lo) : 0u;
             const int d = e_ld - lo;
             const char *s_bytes = reinterpret_cast<const char *>(s_bv);
             const int cs[4] = {sg[u].c.x, sg[u].c.y, sg[u].c.z, sg[u].c.w};
-            const float vs[4] = {sg[u].v.x, sg[u].v.y, sg[u].v.z, sg[u].v.w};
+            float vs[4] = {sg[u].v.x, sg[u].v.y, sg[u].v.z, sg[u].v.w};
+            if constexpr (kEb == 2) {
+                const unsigned w0 = __float_as_uint(sg[u].v.x), w1 = __float_as_uint(sg[u].v.y);
+                vs[0] = Elem<E>::lo(w0);
+                vs[1] = Elem<E>::hi(w0);
+                vs[2] = Elem<E>::lo(w1);
+                vs[3] = Elem<E>::hi(w1);
+            }
             VecT bv[4];
             float val[4];
 #pragma unroll
@@ -456,27 +501,27 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
     }
 }
 
-template <int kE, int kVec>
+template <typename E, int kE, int kVec>
 hipError_t launch_lds_t(const SpmmParams &p, int blocks, hipStream_t s)
 {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&spmm_lds_kernel<kE, kVec>),
+        reinterpret_cast<const void *>(&spmm_lds_kernel<E, kE, kVec>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsMaxB + 16u));
     if (e != hipSuccess) return e;
     // B's slice and the zero vector
     const size_t lds_bytes = ((size_t)p.k * (size_t)p.lds_slice_n + kVec) * 4u;
-    hipLaunchKernelGGL((spmm_lds_kernel<kE, kVec>), dim3(blocks), dim3(kLdsThreads),
+    hipLaunchKernelGGL((spmm_lds_kernel<E, kE, kVec>), dim3(blocks), dim3(kLdsThreads),
                        lds_bytes, s, p);
     return hipGetLastError();
 }
 
-template <int kVec>
+template <typename E, int kVec>
 hipError_t launch_lds(int e, const SpmmParams &p, int blocks, hipStream_t s)
 {
     switch (e) {
-    case 1: return launch_lds_t<1, kVec>(p, blocks, s);
-    case 2: return launch_lds_t<2, kVec>(p, blocks, s);
-    default: return launch_lds_t<4, kVec>(p, blocks, s);
+    case 1: return launch_lds_t<E, 1, kVec>(p, blocks, s);
+    case 2: return launch_lds_t<E, 2, kVec>(p, blocks, s);
+    default: return launch_lds_t<E, 4, kVec>(p, blocks, s);
     }
 }
 
@@ -617,6 +662,16 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
 
     // Narrow B: lanes over entries (needs the buffer paths for B and the CSR).
     const bool narrow = f32 && buf && nv <= 4 && (long long)a.nnz * 4 <= (1LL << 31);
+    // The LDS (streaming) kernel: fp32 as the narrow kernel; 16-bit B is
+    // widened into LDS as fp32 vectors of 4 (n % 4 == 0, B 8-byte aligned) or
+    // single elements, so its vectors are counted in fp32 terms.
+    int lds_kvec = kvec, lds_nv = nv;
+    bool lds_ok = narrow;
+    if (!f32) {
+        lds_kvec = (a.n % 4 == 0 && aligned(a.b, 8) && a.stride_b % 4 == 0) ? 4 : 1;
+        lds_nv = (a.n + lds_kvec - 1) / lds_kvec;
+        lds_ok = buf && lds_nv <= 4 && (long long)a.nnz * 4 <= (1LL << 31);
+    }
     if (narrow && xcd_grid(a.batch, a.m) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 
     SpmmParams &p = plan->p;
@@ -627,7 +682,7 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
     p.tiles = tiles;
     p.batch = a.batch;
     p.b_bytes = buf ? (unsigned)((long long)a.k * a.n * eb) : 0u;
-    p.csr_bytes = narrow ? (unsigned)((long long)a.nnz * 4) : 0u;
+    p.csr_bytes = (narrow || lds_ok) ? (unsigned)((long long)a.nnz * 4) : 0u;
     p.k = a.k;
     p.lds_slices = 1;
     p.lds_slice_n = a.n;
@@ -659,8 +714,8 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
             (long long)a.batch * tiles * row_blocks < 2LL * kSimdsPerCu * cus)
             plan->kind = SpmmPlan::kSplit;
     }
-    if (narrow) {
-        plan->kind = SpmmPlan::kNarrow;
+    if (narrow) plan->kind = SpmmPlan::kNarrow;
+    if (lds_ok) {
         // B in LDS when it fits and every CU has at least as many entries to
         // stream as it copies B elements (nnz >= CUs * k * n).
         int cus = 0, lds_max = 0;
@@ -671,21 +726,22 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
         // least as many entries as each copies B elements: nnz >= (CUs / S)
         // * k * slice columns.
         const long long lds_cap = std::min<long long>(kLdsMaxB, lds_max - 16);
-        const long long row_bytes = (long long)a.k * kvec * 4;  // one vector column of B
-        long long slice_v = row_bytes > 0 ? std::min<long long>(nv, lds_cap / row_bytes) : 0;
-        const int slices = slice_v > 0 ? (int)((nv + slice_v - 1) / slice_v) : 0;
-        if (slices > 0) slice_v = (nv + slices - 1) / slices;
+        const long long row_bytes = (long long)a.k * lds_kvec * 4;  // one vector column of B
+        long long slice_v = row_bytes > 0 ? std::min<long long>(lds_nv, lds_cap / row_bytes) : 0;
+        const int slices = slice_v > 0 ? (int)((lds_nv + slice_v - 1) / slice_v) : 0;
+        if (slices > 0) slice_v = (lds_nv + slices - 1) / slices;
         const int groups = slices > 1 ? cus / slices / 8 * 8 : cus;
         if (a.batch == 1 && cus > 0 && vec_csr && a.nnz >= 4 && slices > 0 && groups > 0 &&
-            (long long)a.nnz >= (long long)groups * a.k * slice_v * kvec) {
+            (long long)a.nnz >= (long long)groups * a.k * slice_v * lds_kvec) {
             const long long want = ((long long)a.m + kLdsWaves - 1) / kLdsWaves;
             long long g = want < groups ? want : groups;
             if (slices > 1) g = (g + 7) / 8 * 8;  // whole XCD rounds
             plan->kind = SpmmPlan::kLds;
+            plan->vec = lds_kvec == 4;
             plan->blocks = (int)(g * slices);
             plan->e = slice_v <= 1 ? 1 : slice_v <= 2 ? 2 : 4;
             p.lds_slices = slices;
-            p.lds_slice_n = (int)(slice_v * kvec);
+            p.lds_slice_n = (int)(slice_v * lds_kvec);
         }
     }
     return hipSuccess;
@@ -696,8 +752,17 @@ hipError_t run_spmm(const SpmmPlan &plan, hipStream_t stream)
     const SpmmParams &p = plan.p;
     switch (plan.kind) {
     case SpmmPlan::kLds:
-        return plan.vec ? launch_lds<4>(plan.e, p, plan.blocks, stream)
-                        : launch_lds<1>(plan.e, p, plan.blocks, stream);
+        switch (plan.dtype) {
+        case Dtype::f16:
+            return plan.vec ? launch_lds<_Float16, 4>(plan.e, p, plan.blocks, stream)
+                            : launch_lds<_Float16, 1>(plan.e, p, plan.blocks, stream);
+        case Dtype::bf16:
+            return plan.vec ? launch_lds<bf16, 4>(plan.e, p, plan.blocks, stream)
+                            : launch_lds<bf16, 1>(plan.e, p, plan.blocks, stream);
+        default:
+            return plan.vec ? launch_lds<float, 4>(plan.e, p, plan.blocks, stream)
+                            : launch_lds<float, 1>(plan.e, p, plan.blocks, stream);
+        }
     case SpmmPlan::kNarrow:
         return plan.vec ? launch_narrow<4>(plan.e, p, stream)
                         : launch_narrow<1>(plan.e, p, stream);
