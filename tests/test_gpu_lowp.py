@@ -298,3 +298,23 @@ def test_spmm_hbm_stream_n4_sampled_rows(kind):
     rows = np.random.default_rng(720).choice(w["m"], 300, replace=False)
     ref, s = oracle.spmm_rows(rows, w["n"], ro, a.cols, v, b)
     check_close(c[rows], ref, s, f"spmm {kind} hbm_stream n=4")
+
+
+@pytest.mark.parametrize("tail", [0, 1, 2, 3])
+@pytest.mark.parametrize("n", [1, 4])
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_spmm_lds_array_end(kind, n, tail):
+    # nnz = tail (mod 4) with the last row non-empty: the array's last segment
+    # holds `tail` entries (4 when 0), its other words outside the buffers'
+    # ranges; with an odd nnz the value range ends 2 bytes past the array
+    m, k = 8192, 256
+    lengths = np.random.default_rng(730 + tail).integers(100, 220, m).astype(np.int32)
+    lengths[-1] += (tail - int(lengths.sum()) % 4) % 4
+    assert int(lengths.sum()) % 4 == tail and lengths[-1] > 0
+    rl = inputs.random_row_lists(731 + tail, m, k, lengths)
+    ro = oracle.csr_offsets_from_lengths(lengths)
+    b32 = inputs.random_dense(732 + n, k, n)
+    note(f"spmm_ex {kind} lds array end n={n} nnz%4={tail}")
+    c, v, b = spmm16(kind, m, k, n, ro, rl.cols, rl.values, b32, swz=False)
+    ref, s = oracle.spmm(m, k, n, ro, rl.cols, v, b)
+    check_close(c, ref, s, f"spmm {kind} lds array end n={n} tail={tail}")
