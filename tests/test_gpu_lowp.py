@@ -249,7 +249,7 @@ def test_spmm_b_beyond_2gib(kind):
 # Narrow 16-bit B with many entries per B element takes the streaming kernel:
 # B widened to fp32 in LDS, values read as 2-byte loads and widened.
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16, 24, 32])
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
 def test_spmm_lds_resident_b(kind, n):
     m, k = 8192, 256
@@ -326,3 +326,19 @@ def test_spmm_lds_array_end(kind, n, tail):
     c, v, b = spmm16(kind, m, k, n, ro, rl.cols, rl.values, b32, swz=False)
     ref, s = oracle.spmm(m, k, n, ro, rl.cols, v, b)
     check_close(c, ref, s, f"spmm {kind} lds array end n={n} tail={tail}")
+
+
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+@pytest.mark.parametrize("k,n,m", [(8192, 16, 16000), (8192, 24, 10000), (8192, 32, 8000)])
+def test_spmm_lds_16bit_b_column_slices(kind, k, n, m):
+    # n % 8 == 0: B kept 16-bit in LDS, 8 columns per vector; B of k x n in 2,
+    # 3 and 4 column slices of 8 (enough entries for the streaming kernel)
+    lengths = np.random.default_rng(740 + n).integers(300, 900, m).astype(np.int32)
+    rl = inputs.random_row_lists(741 + n, m, k, lengths)
+    ro = oracle.csr_offsets_from_lengths(lengths)
+    b32 = inputs.random_dense(742 + n, k, n)
+    note(f"spmm_ex {kind} 16-bit B in LDS, slices k={k} n={n} m={m} nnz={rl.cols.size}")
+    c, v, b = spmm16(kind, m, k, n, ro, rl.cols, rl.values, b32)
+    rows = np.random.default_rng(743).choice(m, 400, replace=False)
+    ref, s = oracle.spmm_rows(rows, n, ro, rl.cols, v, b)
+    check_close(c[rows], ref, s, f"spmm {kind} 16-bit B slices k={k} n={n}")

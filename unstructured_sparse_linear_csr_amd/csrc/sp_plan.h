@@ -16,6 +16,7 @@ struct SpmmPlan {
     int lpr;     // wide: lanes per row
     int e;       // narrow and LDS kernels: lanes per entry slot
     int blocks;  // LDS kernel: workgroups
+    int lds_kvec = 0;  // LDS kernel: B elements per LDS vector (8: 16-bit B kept 16-bit)
 };
 
 struct SddmmPlan {

@@ -2,6 +2,8 @@
 // ("Sparse GPU Kernels for Deep Learning", summary card, "Summary").  The wide
 // kernel's body, and the design notes for it, are in spmm_wide.h; this file
 // holds the narrow-B kernels and the variant selection.
+#include <type_traits>
+
 #include "sp_device.h"
 #include "sp_launch.h"
 #include "sp_types.h"
@@ -295,7 +297,11 @@ template <typename E, int kE, int kVec>
 __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
 {
     constexpr unsigned kEb = Elem<E>::kBytes;
-    using V = Vec<kVec>;
+    // B in LDS: fp32 vectors of kVec (fp32 B, or 16-bit B widened on the copy),
+    // or -- kVec == 8 -- 16-bit B as it is, 8 elements per 16-byte vector,
+    // widened at the FMA
+    constexpr bool kRaw16 = kEb == 2 && kVec == 8;
+    using V = std::conditional_t<kRaw16, GVec<E, 8>, Vec<kVec == 8 ? 4 : kVec>>;
     using VecT = typename V::T;
     constexpr int kS = kWave / kE;  // segment slots per step
     constexpr int kSteps = 4;       // steps per batch
@@ -319,7 +325,7 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
     VecT *s_bv = reinterpret_cast<VecT *>(s_b);
     const int total = p.k * wv;
     if (tid == 0) s_bv[total] = VecT{};  // the zero vector
-    if constexpr (kEb == 2) {
+    if constexpr (kEb == 2 && !kRaw16) {
         // 16-bit B: vector i of the slice holds B[r][col .. col + kVec) widened
         const E *__restrict__ b16 = static_cast<const E *>(p.b);
         for (int i = tid; i < total; i += kLdsThreads) {
@@ -509,7 +515,9 @@ hipError_t launch_lds_t(const SpmmParams &p, int blocks, hipStream_t s)
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsMaxB + 16u));
     if (e != hipSuccess) return e;
     // B's slice and the zero vector
-    const size_t lds_bytes = ((size_t)p.k * (size_t)p.lds_slice_n + kVec) * 4u;
+    // B's slice and the zero vector, fp32 in LDS (or 16-bit B kept 16-bit: kVec 8)
+    constexpr size_t kLdsEb = (Elem<E>::kBytes == 2 && kVec == 8) ? 2u : 4u;
+    const size_t lds_bytes = ((size_t)p.k * (size_t)p.lds_slice_n + kVec) * kLdsEb;
     hipLaunchKernelGGL((spmm_lds_kernel<E, kE, kVec>), dim3(blocks), dim3(kLdsThreads),
                        lds_bytes, s, p);
     return hipGetLastError();
@@ -662,13 +670,20 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
 
     // Narrow B: lanes over entries (needs the buffer paths for B and the CSR).
     const bool narrow = f32 && buf && nv <= 4 && (long long)a.nnz * 4 <= (1LL << 31);
-    // The LDS (streaming) kernel: fp32 as the narrow kernel; 16-bit B is
-    // widened into LDS as fp32 vectors of 4 (n % 4 == 0, B 8-byte aligned) or
-    // single elements, so its vectors are counted in fp32 terms.
-    int lds_kvec = kvec, lds_nv = nv;
+    // The LDS (streaming) kernel: fp32 as the narrow kernel.  16-bit B stays
+    // 16-bit in LDS, 8 elements per 16-byte vector, when n % 8 == 0 and B and C
+    // are 16-byte aligned; otherwise it is widened into LDS as fp32 vectors of
+    // 4 (n % 4 == 0, B 8-byte aligned) or single elements.  lds_eb: bytes per
+    // element of B in LDS.
+    int lds_kvec = kvec, lds_nv = nv, lds_eb = 4;
     bool lds_ok = narrow;
     if (!f32) {
-        lds_kvec = (a.n % 4 == 0 && aligned(a.b, 8) && a.stride_b % 4 == 0) ? 4 : 1;
+        if (a.n % 8 == 0 && aligned16(a.b) && aligned16(a.c) && a.stride_b % 8 == 0) {
+            lds_kvec = 8;
+            lds_eb = 2;
+        } else {
+            lds_kvec = (a.n % 4 == 0 && aligned(a.b, 8) && a.stride_b % 4 == 0) ? 4 : 1;
+        }
         lds_nv = (a.n + lds_kvec - 1) / lds_kvec;
         lds_ok = buf && lds_nv <= 4 && (long long)a.nnz * 4 <= (1LL << 31);
     }
@@ -726,7 +741,7 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
         // least as many entries as each copies B elements: nnz >= (CUs / S)
         // * k * slice columns.
         const long long lds_cap = std::min<long long>(kLdsMaxB, lds_max - 16);
-        const long long row_bytes = (long long)a.k * lds_kvec * 4;  // one vector column of B
+        const long long row_bytes = (long long)a.k * lds_kvec * lds_eb;  // one vector column of B
         long long slice_v = row_bytes > 0 ? std::min<long long>(lds_nv, lds_cap / row_bytes) : 0;
         const int slices = slice_v > 0 ? (int)((lds_nv + slice_v - 1) / slice_v) : 0;
         if (slices > 0) slice_v = (lds_nv + slices - 1) / slices;
@@ -738,6 +753,7 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
             if (slices > 1) g = (g + 7) / 8 * 8;  // whole XCD rounds
             plan->kind = SpmmPlan::kLds;
             plan->vec = lds_kvec == 4;
+            plan->lds_kvec = lds_kvec;
             plan->blocks = (int)(g * slices);
             plan->e = slice_v <= 1 ? 1 : slice_v <= 2 ? 2 : 4;
             p.lds_slices = slices;
@@ -754,11 +770,13 @@ hipError_t run_spmm(const SpmmPlan &plan, hipStream_t stream)
     case SpmmPlan::kLds:
         switch (plan.dtype) {
         case Dtype::f16:
-            return plan.vec ? launch_lds<_Float16, 4>(plan.e, p, plan.blocks, stream)
-                            : launch_lds<_Float16, 1>(plan.e, p, plan.blocks, stream);
+            return plan.lds_kvec == 8 ? launch_lds<_Float16, 8>(plan.e, p, plan.blocks, stream)
+                   : plan.vec         ? launch_lds<_Float16, 4>(plan.e, p, plan.blocks, stream)
+                                      : launch_lds<_Float16, 1>(plan.e, p, plan.blocks, stream);
         case Dtype::bf16:
-            return plan.vec ? launch_lds<bf16, 4>(plan.e, p, plan.blocks, stream)
-                            : launch_lds<bf16, 1>(plan.e, p, plan.blocks, stream);
+            return plan.lds_kvec == 8 ? launch_lds<bf16, 8>(plan.e, p, plan.blocks, stream)
+                   : plan.vec         ? launch_lds<bf16, 4>(plan.e, p, plan.blocks, stream)
+                                      : launch_lds<bf16, 1>(plan.e, p, plan.blocks, stream);
         default:
             return plan.vec ? launch_lds<float, 4>(plan.e, p, plan.blocks, stream)
                             : launch_lds<float, 1>(plan.e, p, plan.blocks, stream);
