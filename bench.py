@@ -586,21 +586,20 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
                                     graph_time_us(torch, fn, 20),
                                     {"cold_us": cold_time_us(torch, fn, flush),
                                      "csr_bytes": 8 * a.nnz, "swizzle": order is not None}))
-        if True:
-            # 16-bit values and B: the CSR streams 6 bytes per entry
-            for tag, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
-                v16, b16 = vals.to(tdt), b.to(tdt)
-                fn = lambda: sp.sp_spmm_ex(w["m"], w["k"], w["n"], a.nnz, None, v16, ro, cols,
-                                           b16, c)
-                us = graph_time_us(torch, fn, 20)
-                byts = 6 * a.nnz + 4 * (w["m"] + 1) + 2 * w["k"] * w["n"] + 4 * w["m"] * w["n"]
-                recs.append({"record": "spmm_" + tag, "workload": w["name"], "m": w["m"],
-                             "k": w["k"], "n": w["n"], "nnz": a.nnz, "us": us,
-                             "cold_us": cold_time_us(torch, fn, flush),
-                             "gflops": 2.0 * a.nnz * w["n"] / (us * 1e-6) / 1e9,
-                             "compulsory_gbs": byts / (us * 1e-6) / 1e9,
-                             "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS})
-                del v16, b16
+        # 16-bit values and B: the CSR streams 6 bytes per entry
+        for tag, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+            v16, b16 = vals.to(tdt), b.to(tdt)
+            fn = lambda: sp.sp_spmm_ex(w["m"], w["k"], w["n"], a.nnz, None, v16, ro, cols,
+                                       b16, c)
+            us = graph_time_us(torch, fn, 20)
+            byts = 6 * a.nnz + 4 * (w["m"] + 1) + 2 * w["k"] * w["n"] + 4 * w["m"] * w["n"]
+            recs.append({"record": "spmm_" + tag, "workload": w["name"], "m": w["m"],
+                         "k": w["k"], "n": w["n"], "nnz": a.nnz, "us": us,
+                         "cold_us": cold_time_us(torch, fn, flush),
+                         "gflops": 2.0 * a.nnz * w["n"] / (us * 1e-6) / 1e9,
+                         "compulsory_gbs": byts / (us * 1e-6) / 1e9,
+                         "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS})
+            del v16, b16
         del a, ro, ri, cols, vals
     with open(path, "w") as f:
         for r in recs:
