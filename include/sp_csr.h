@@ -296,6 +296,10 @@ typedef enum sp_dtype {
  * elements of that type); C is fp32.  SP_DTYPE_F32 is exactly
  * sp_spmm_batched.  16-bit B rows are read in 16-byte vectors of 8 elements
  * when n % 8 == 0 and B, C are 16-byte aligned, else element by element.
+ * Narrow 16-bit B (up to 32 columns) with many entries per B element takes
+ * the streaming kernel (B copied into LDS); it reads the values in whole
+ * 4-byte words, so with an odd nnz it may read the 2 bytes after the value
+ * array (the rest of the word holding the last value; never used).
  * An unknown dtype returns SP_ERROR_INVALID_VALUE. */
 sp_status_t sp_spmm_ex(int m, int k, int n, int nnz, const int *row_indices, int dtype,
                        const void *values, const int *row_offsets, const int *col_indices,
