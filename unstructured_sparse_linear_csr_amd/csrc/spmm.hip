@@ -283,8 +283,10 @@ __global__ __launch_bounds__(kWave) void spmm_narrow_kernel(SpmmParams p)
 // exactly, with no branch, so a batch's reads are all issued before its FMAs.
 // E is the element type of the values and of B: fp16 and bf16 B is widened
 // to fp32 as it is copied into LDS (the LDS layout, reads and FMAs are those of
-// fp32), and a segment's four 16-bit values are read with one 8-byte buffer
-// load and widened when consumed: the CSR then streams 6 bytes per entry
+// fp32), or, with kVec == 8, kept 16-bit there (8 elements per 16-byte vector,
+// widened at the FMA: half the LDS, so fewer column slices); a segment's four
+// 16-bit values are read with one 8-byte buffer load and widened when
+// consumed: the CSR then streams 6 bytes per entry
 // instead of 8.  In the 16-bit form every segment, the array's last included,
 // is read from its own first entry: its 4-byte words past the end of the
 // column array (or past the value array rounded up to whole words) are out of
