@@ -279,10 +279,10 @@ sp_status_t sp_sddmm_general_workspace(int k, int d, int batch, long long stride
  * is what bounds these kernels.  Every 16-bit element is widened to fp32
  * exactly, a product of two 16-bit elements is exact in fp32, sums are fp32,
  * and outputs are fp32.  Summation orders are those of the fp32 entry points,
- * except that bf16 pairs terms: the vector SpMM adds two consecutive entries'
- * products per column, and the vector SDDMM (and attention scores) two
- * consecutive elements' products, to the running sum in one step
- * (v_dot2c_f32_bf16).
+ * except that pairs of terms are added in one step: the bf16 vector SpMM adds
+ * two consecutive entries' products per column, and the 16-bit vector SDDMM
+ * (and attention scores) two consecutive elements' products, to the running
+ * sum (v_dot2c_f32_bf16 / v_dot2c_f32_f16).
  * ---------------------------------------------------------------------- */
 
 /* Element type of the 16-bit-capable operands. */

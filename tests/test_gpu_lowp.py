@@ -342,3 +342,25 @@ def test_spmm_lds_16bit_b_column_slices(kind, k, n, m):
     rows = np.random.default_rng(743).choice(m, 400, replace=False)
     ref, s = oracle.spmm_rows(rows, n, ro, rl.cols, v, b)
     check_close(c[rows], ref, s, f"spmm {kind} 16-bit B slices k={k} n={n}")
+
+
+def test_sddmm_f16_subnormal_operands():
+    # fp16 subnormals (2^-20 and 3 * 2^-24, below fp16's smallest normal 2^-14)
+    # must enter the products unflushed: every output is a sum of exact tiny
+    # products, far above fp32's own subnormal range
+    m, k, d = 64, 96, 64
+    lengths = np.full(m, 40, np.int32)
+    rl = inputs.random_row_lists(750, m, k, lengths)
+    ro = oracle.csr_offsets_from_lengths(lengths)
+    x32 = np.where(np.arange(m * d).reshape(m, d) % 2 == 0, 2.0 ** -20, 3 * 2.0 ** -24)
+    x32 = (x32 * np.sign(inputs.random_dense(751, m, d))).astype(np.float32)
+    y32 = inputs.random_dense(752, k, d)
+    d_x, x = to16(x32, "f16")
+    d_y, y = to16(y32, "f16")
+    assert np.all(np.abs(x) < 2.0 ** -14)               # every X element subnormal in fp16
+    d_ro = devi(ro)
+    out = torch.full((rl.cols.size,), float("nan"), device="cuda")
+    note("sddmm_ex f16 subnormal operands")
+    sp.sp_sddmm_ex(m, k, d, rl.cols.size, None, d_ro, devi(rl.cols), d_x, d_y, 1.0, out)
+    ref, s = oracle.sddmm(m, k, d, ro, rl.cols, x, y)
+    check_close(host(out), ref, s, "sddmm f16 subnormal")

@@ -33,9 +33,9 @@
 // without a window leave at once.  The arithmetic of every entry is the same
 // for any kParts (bit-identical outputs).
 //
-// Summation order: each lane sums its elements in order with FMA (bf16: by
-// pairs, v_dot2c_f32_bf16), then the DPP tree adds the kG lane partials;
-// deterministic run to run.
+// Summation order: each lane sums its elements in order with FMA (16-bit
+// types: by pairs, v_dot2c_f32_bf16 / _f16), then the DPP tree adds the kG
+// lane partials; deterministic run to run.
 #pragma once
 
 #include "sp_device.h"

@@ -190,10 +190,11 @@ template <typename E> struct GVec16x8 {
             fma(a1, b1, acc);
         }
     }
-    // fp16: element order 0 ... 7, one FMA each (the conversions fold into
-    // v_fma_mix_f32).  bf16: gfx950's v_dot2c_f32_bf16 adds the two exact
-    // products of elements (0, 1), then (2, 3), ... to the sum, one
-    // instruction per pair instead of a shift or mask plus an FMA per element.
+    // gfx950's v_dot2c_f32_bf16 / v_dot2c_f32_f16 add the two exact products
+    // of elements (0, 1), then (2, 3), ... to the sum: one instruction per pair
+    // (bf16: instead of a shift or mask plus an FMA per element; fp16: instead
+    // of one v_fma_mix_f32 per element).  fp16 subnormal operands enter the
+    // products unflushed (tested).
     static __device__ __forceinline__ float dot(const T &x, const T &y, float acc)
     {
         const unsigned xw[4] = {x.x, x.y, x.z, x.w};
@@ -206,11 +207,11 @@ template <typename E> struct GVec16x8 {
                                                       __builtin_bit_cast(bf16x2, yw[i]), acc,
                                                       false);
         } else {
+            typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc = fmaf(Elem<E>::lo(xw[i]), Elem<E>::lo(yw[i]), acc);
-                acc = fmaf(Elem<E>::hi(xw[i]), Elem<E>::hi(yw[i]), acc);
-            }
+            for (int i = 0; i < 4; ++i)
+                acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, xw[i]),
+                                             __builtin_bit_cast(f16x2, yw[i]), acc, false);
         }
         return acc;
     }
