@@ -265,10 +265,11 @@ def lstm_breakeven(torch, sp, inputs, dev, reps=50, records=None, flush=None):
                      "linearly interpolated; null if the sweep has no crossing")}
 
 
-def stream_setup(torch, sp, inputs, dev):
+def stream_setup(torch, sp, inputs, dev, dtype=None):
     """The streaming regime: A 65536 x 8192 at 90 % sparsity (53.7 M entries,
     430 MB of CSR, far beyond L2 and MALL), B 8192 x 4 held in LDS, natural
-    row order.  Returns (launch, workload description)."""
+    row order; values and B fp32, or of the 16-bit torch `dtype`.  Returns
+    (launch, workload description)."""
     w = inputs.hbm_stream(n=4)
     a = w["a"]
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
@@ -276,7 +277,11 @@ def stream_setup(torch, sp, inputs, dev):
     cols, vals, b = up(a.cols), up(a.values), up(w["b"])
     c = torch.empty(w["m"], w["n"], device=dev)
     m, k, n, nnz = w["m"], w["k"], w["n"], a.nnz
-    fn = lambda: sp.sp_spmm(m, k, n, nnz, None, vals, ro, cols, b, c)
+    if dtype is None:
+        fn = lambda: sp.sp_spmm(m, k, n, nnz, None, vals, ro, cols, b, c)
+    else:
+        vals, b = vals.to(dtype), b.to(dtype)
+        fn = lambda: sp.sp_spmm_ex(m, k, n, nnz, None, vals, ro, cols, b, c)
     return fn, {"workload": w["name"], "m": m, "k": k, "n": n, "nnz": nnz}
 
 
@@ -287,11 +292,22 @@ def stream_record(torch, sp, inputs, dev) -> dict:
     us = graph_time_us(torch, fn, 20)
     alg = spmm_bytes(desc["m"], desc["k"], desc["n"], desc["nnz"])
     gbs = alg / (us * 1e-6) / 1e9
-    return {**desc, "kernel": "spmm (B in LDS)", "avg_us": us,
-            "gflops": 2.0 * desc["nnz"] * desc["n"] / (us * 1e-6) / 1e9,
-            "algorithmic_bytes_per_launch": alg, "achieved_gbs": gbs,
-            "frac_hbm_peak": gbs / HBM_PEAK_GBS,
-            "traffic": traffic_record(STREAM_TRAFFIC_FILE)}
+    rec = {**desc, "kernel": "spmm (B in LDS)", "avg_us": us,
+           "gflops": 2.0 * desc["nnz"] * desc["n"] / (us * 1e-6) / 1e9,
+           "algorithmic_bytes_per_launch": alg, "achieved_gbs": gbs,
+           "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+           "traffic": traffic_record(STREAM_TRAFFIC_FILE)}
+    del fn
+    # the same matrix with bf16 values and B: 6 bytes per entry
+    fn, desc = stream_setup(torch, sp, inputs, dev, torch.bfloat16)
+    us = graph_time_us(torch, fn, 20)
+    alg = (6 * desc["nnz"] + 4 * (desc["m"] + 1) + 2 * desc["k"] * desc["n"]
+           + 4 * desc["m"] * desc["n"])
+    gbs = alg / (us * 1e-6) / 1e9
+    rec["bf16"] = {"avg_us": us, "algorithmic_bytes_per_launch": alg, "achieved_gbs": gbs,
+                   "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+                   "note": "values and B in bf16, fp32 arithmetic and C; 6 bytes per entry"}
+    return rec
 
 
 def backward_records(torch, sp, inputs, dev, w, flush) -> list:
@@ -788,7 +804,9 @@ def main() -> int:
         result["streaming"] = stream_record(torch, sp, inputs, dev)
         log(f"streaming spmm: {result['streaming']['avg_us']:.1f} us "
             f"{result['streaming']['achieved_gbs']:.0f} GB/s "
-            f"({100 * result['streaming']['frac_hbm_peak']:.1f} % of HBM peak)")
+            f"({100 * result['streaming']['frac_hbm_peak']:.1f} % of HBM peak); bf16 "
+            f"{result['streaming']['bf16']['avg_us']:.1f} us "
+            f"({100 * result['streaming']['bf16']['frac_hbm_peak']:.1f} %)")
 
     if not args.no_ceilings:
         # The same byte count as the streaming SpMM's CSR, and the FFN SpMM's B.
