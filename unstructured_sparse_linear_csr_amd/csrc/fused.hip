@@ -25,12 +25,16 @@ template <int kLpr, int kG, int kNv>
 __global__ __launch_bounds__(kWave) void spmm_sddmm_kernel(SpmmParams a, SddmmParams b,
                                                            long long spmm_blocks)
 {
+    // The SDDMM's workgroups first, then the SpMM's: measured 1-2 % faster on the
+    // Transformer-FFN pair than the other order (interleaving the two, which
+    // puts each problem on half the XCDs, was slower still)
     const long long blk = blockIdx.x;
-    if (blk < spmm_blocks)
-        spmm_detail::spmm_wide_body<float, kLpr, 4, true, true>(a, spmm_detail::wide_work(a, blk));
+    const long long sddmm_blocks = (long long)gridDim.x - spmm_blocks;
+    if (blk < sddmm_blocks)
+        sddmm_detail::sddmm_rows_body<float, kG, kNv, 4>(b, sddmm_detail::rows_work(b, blk));
     else
-        sddmm_detail::sddmm_rows_body<float, kG, kNv, 4>(
-            b, sddmm_detail::rows_work(b, blk - spmm_blocks));
+        spmm_detail::spmm_wide_body<float, kLpr, 4, true, true>(
+            a, spmm_detail::wide_work(a, blk - sddmm_blocks));
 }
 
 template <int kLpr, int kG, int kNv>
