@@ -425,14 +425,14 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
             recs.append(spmm_record(w["name"], m, k, n, a.nnz, graph_time_us(torch, bfn, 200),
                                     {"swizzle": swz, "kernel": "balanced",
                                      "cold_us": cold_time_us(torch, bfn, flush)}))
-            sfn = lambda: sp.sp_sddmm(m, k, d, a.nnz, order, ro, cols, x, y, 1.0, out)
+            sfn = lambda: sp.sp_sddmm(m, k, d, a.nnz, order, ro, cols, x, y, out)
             us = graph_time_us(torch, sfn, 200)
             recs.append({"record": "sddmm", "workload": w["name"], "m": m, "k": k, "d": d,
                          "nnz": a.nnz, "swizzle": swz, "us": us,
                          "cold_us": cold_time_us(torch, sfn, flush),
                          "gflops": 2.0 * a.nnz * d / (us * 1e-6) / 1e9,
                          "compulsory_gbs": sddmm_bytes(m, k, d, a.nnz) / (us * 1e-6) / 1e9})
-            bsfn = lambda: sp.sp_sddmm_balanced(m, k, d, a.nnz, order, ro, cols, x, y, 1.0, out)
+            bsfn = lambda: sp.sp_sddmm_balanced(m, k, d, a.nnz, order, ro, cols, x, y, out)
             us = graph_time_us(torch, bsfn, 200)
             recs.append({"record": "sddmm", "workload": w["name"], "m": m, "k": k, "d": d,
                          "nnz": a.nnz, "swizzle": swz, "kernel": "balanced", "us": us,
@@ -566,7 +566,7 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
                                    at.row_offsets, at.col_indices, bt, ct)))
     lat.append((wt["name"], "sddmm", at.nnz,
                 lambda: sp.sp_sddmm(at.m, at.k, wt["d"], at.nnz, at.row_indices,
-                                    at.row_offsets, at.col_indices, xt, yt, 1.0, ot)))
+                                    at.row_offsets, at.col_indices, xt, yt, ot)))
     wf = inputs.transformer_ffn()
     rof, rif, colf, valf = upload_csr(torch, sp, dev, wf["a"])
     bf, xf, yf = up(wf["b"]), up(wf["x"]), up(wf["y"])
@@ -576,8 +576,7 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
     lat.append((wf["name"], "spmm", nf,
                 lambda: sp.sp_spmm(wf["m"], wf["k"], wf["n"], nf, rif, valf, rof, colf, bf, cf)))
     lat.append((wf["name"], "sddmm", nf,
-                lambda: sp.sp_sddmm(wf["m"], wf["k"], wf["d"], nf, rif, rof, colf, xf, yf, 1.0,
-                                    of)))
+                lambda: sp.sp_sddmm(wf["m"], wf["k"], wf["d"], nf, rif, rof, colf, xf, yf, of)))
     wl = inputs.lstm(0.98)
     rol, ril, coll, vall = upload_csr(torch, sp, dev, wl["a"])
     bl = up(wl["b"])
@@ -671,7 +670,7 @@ def main() -> int:
         sp.sp_spmm(m, k, n, nnz, ri, vals, ro, cols, b, c)
 
     def k_sddmm():
-        sp.sp_sddmm(m, k, d, nnz, ri, ro, cols, x, y, 1.0, out)
+        sp.sp_sddmm(m, k, d, nnz, ri, ro, cols, x, y, out)
 
     def k_fused():
         sp.sp_spmm_sddmm(m, k, n, nnz, ri, vals, ro, cols, b, c, m, k, d, nnz, ri, ro, cols, x,

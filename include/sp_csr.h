@@ -189,9 +189,10 @@ sp_status_t sp_spmm_batched(int m, int k, int n, int nnz,
  * transposed, so both operands are read by contiguous rows.
  * ---------------------------------------------------------------------- */
 
-/* out[p] = alpha * sum over l < d of X[i][l] * Y[col_indices[p]][l], for each
- * entry p of row i.  out is overwritten.  alpha = 1 is the plain product;
- * sparse attention passes its 1/sqrt(d) score scale here.
+/* out[p] = sum over l < d of X[i][l] * Y[col_indices[p]][l], for each entry p
+ * of row i.  out is overwritten.  (A scale factor, such as sparse attention's
+ * 1/sqrt(d), is the `alpha` of sp_sddmm_batched / sp_sddmm_ex; a power-of-two
+ * scale may equally be applied to X first, with identical results.)
  *   m, k, d      mask is m x k, X is m x d, Y is k x d;  nnz = row_offsets[m]
  *   row_indices  int32[m] row order, or NULL (identity)
  *   row_offsets, col_indices   the mask's CSR structure
@@ -199,7 +200,7 @@ sp_status_t sp_spmm_batched(int m, int k, int n, int nnz,
  * d == 0 writes zeros.  Deterministic run to run. */
 sp_status_t sp_sddmm(int m, int k, int d, int nnz, const int *row_indices,
                      const int *row_offsets, const int *col_indices,
-                     const float *x, const float *y, float alpha, float *out,
+                     const float *x, const float *y, float *out,
                      sp_stream_t stream);
 
 /* sp_sddmm for row-length distributions with a heavy tail ("Interesting
@@ -214,7 +215,7 @@ sp_status_t sp_sddmm(int m, int k, int d, int nnz, const int *row_indices,
  * sp_sddmm. */
 sp_status_t sp_sddmm_balanced(int m, int k, int d, int nnz, const int *row_indices,
                               const int *row_offsets, const int *col_indices, const float *x,
-                              const float *y, float alpha, float *out, sp_stream_t stream);
+                              const float *y, float *out, sp_stream_t stream);
 
 /* `batch` SDDMMs sharing one mask: x_z = x + z*stride_x, y_z = y + z*stride_y,
  * out_z = out + z*stride_out (elements).  stride_out must be >= nnz when
@@ -323,9 +324,9 @@ sp_status_t sp_sddmm_ex(int m, int k, int d, int nnz, const int *row_indices,
 
 /* The SpMM sp_spmm(m, k, n, nnz, row_indices, values, row_offsets,
  * col_indices, b, c) and the SDDMM sp_sddmm(s_m, s_k, d, s_nnz,
- * s_row_indices, s_row_offsets, s_col_indices, x, y, alpha, out) -- two
- * independent problems, whose sparsity structures may be the same arrays or
- * different ones -- enqueued as one launch when both take their fp32 vector
+ * s_row_indices, s_row_offsets, s_col_indices, x, y, out) with its products
+ * scaled by alpha (alpha = 1: exactly sp_sddmm) -- two independent problems,
+ * whose sparsity structures may be the same arrays or different ones -- enqueued as one launch when both take their fp32 vector
  * paths (16-byte aligned operands, B and Y under 2 GiB, n % 4 == 0,
  * d % 4 == 0, d <= 256), otherwise as the two separate launches.  Results
  * are bit-identical to calling the two entry points.  Arguments are checked

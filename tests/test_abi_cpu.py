@@ -42,6 +42,47 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
         assert getattr(lib, name) is not None
 
 
+def _declaration(name):
+    """Parameter list of `name` in the header, as (type, name) pairs with
+    whitespace normalised."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    params = []
+    for part in m.group(1).split(","):
+        part = " ".join(part.replace("*", " * ").split())
+        if part == "void":
+            continue
+        typ, _, pname = part.rpartition(" ")
+        params.append((typ.replace(" *", "*"), pname))
+    return params
+
+
+def test_core_boundary_signatures():
+    """The four calls of the core boundary keep the plain argument lists:
+    the swizzle over row offsets, SpMM over CSR values/offsets/columns, SDDMM
+    over the mask structure and two dense operands (no scale factor), each with
+    raw device pointers and a stream, and the status strings."""
+    assert _declaration("sp_row_swizzle") == [
+        ("int", "m"), ("const int*", "row_offsets"), ("int*", "row_indices"),
+        ("sp_stream_t", "stream")]
+    assert _declaration("sp_spmm") == [
+        ("int", "m"), ("int", "k"), ("int", "n"), ("int", "nnz"),
+        ("const int*", "row_indices"), ("const float*", "values"),
+        ("const int*", "row_offsets"), ("const int*", "col_indices"),
+        ("const float*", "b"), ("float*", "c"), ("sp_stream_t", "stream")]
+    assert _declaration("sp_sddmm") == [
+        ("int", "m"), ("int", "k"), ("int", "d"), ("int", "nnz"),
+        ("const int*", "row_indices"), ("const int*", "row_offsets"),
+        ("const int*", "col_indices"), ("const float*", "x"), ("const float*", "y"),
+        ("float*", "out"), ("sp_stream_t", "stream")]
+    assert _declaration("sp_status_string") == [("sp_status_t", "status")]
+    # the ctypes layer passes exactly those arguments
+    for name in ("sp_row_swizzle", "sp_spmm", "sp_sddmm", "sp_status_string"):
+        assert len(binding.SIGNATURES[name][0]) == len(_declaration(name)), name
+    assert ctypes.c_float not in binding.SIGNATURES["sp_sddmm"][0]
+
+
 def test_probe_library_exports():
     """The ceiling probes are a library of their own, outside the declared
     interface."""
@@ -274,15 +315,14 @@ def test_sddmm_validation(lib):
     assert f(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE, 2, 0, 0, 7, s) == INVALID
     assert f(4, 4, 4, 0, NULL, FAKE, NULL, FAKE, FAKE, 1.0, NULL, 1, 0, 0, 0, s) == OK
     assert f(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, 1.0, NULL, 1, 0, 0, 0, s) == OK
-    assert lib.sp_sddmm(4, 4, 4, 8, NULL, NULL, FAKE, FAKE, FAKE, 1.0, FAKE, s) == INVALID
-    g = lib.sp_sddmm_balanced
-    assert g(-1, 4, 4, 0, NULL, FAKE, NULL, FAKE, FAKE, 1.0, FAKE, s) == INVALID
-    assert g(4, 4, 4, 8, NULL, NULL, FAKE, FAKE, FAKE, 1.0, FAKE, s) == INVALID
-    assert g(4, 4, 4, 8, NULL, FAKE, NULL, FAKE, FAKE, 1.0, FAKE, s) == INVALID
-    assert g(4, 4, 4, 8, NULL, FAKE, FAKE, NULL, FAKE, 1.0, FAKE, s) == INVALID
-    assert g(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, NULL, 1.0, FAKE, s) == INVALID
-    assert g(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, FAKE, 1.0, NULL, s) == INVALID
-    assert g(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, 1.0, NULL, s) == OK
+    for g in (lib.sp_sddmm, lib.sp_sddmm_balanced):
+        assert g(-1, 4, 4, 0, NULL, FAKE, NULL, FAKE, FAKE, FAKE, s) == INVALID
+        assert g(4, 4, 4, 8, NULL, NULL, FAKE, FAKE, FAKE, FAKE, s) == INVALID
+        assert g(4, 4, 4, 8, NULL, FAKE, NULL, FAKE, FAKE, FAKE, s) == INVALID
+        assert g(4, 4, 4, 8, NULL, FAKE, FAKE, NULL, FAKE, FAKE, s) == INVALID
+        assert g(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, NULL, FAKE, s) == INVALID
+        assert g(4, 4, 4, 8, NULL, FAKE, FAKE, FAKE, FAKE, NULL, s) == INVALID
+        assert g(0, 4, 4, 0, NULL, NULL, NULL, NULL, NULL, NULL, s) == OK
 
 
 def test_build_and_swizzle_validation(lib):

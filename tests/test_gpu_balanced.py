@@ -137,13 +137,13 @@ def test_b_beyond_2gib():
 # arithmetic is that of sp_sddmm, so the outputs must be bit-identical to it
 # (and within the fp32 tolerance of the oracle).
 
-def run_sddmm_pair(a, x_np, y_np, alpha=1.0, ri=None):
+def run_sddmm_pair(a, x_np, y_np, ri=None):
     d = x_np.shape[1]
     x, y = dev(x_np), dev(y_np)
     o1 = torch.full((a.nnz,), float("nan"), device="cuda")
     o2 = torch.full((a.nnz,), float("nan"), device="cuda")
-    sp.sp_sddmm(a.m, a.k, d, a.nnz, ri, a.d_ro, a.d_ci, x, y, alpha, o1)
-    sp.sp_sddmm_balanced(a.m, a.k, d, a.nnz, ri, a.d_ro, a.d_ci, x, y, alpha, o2)
+    sp.sp_sddmm(a.m, a.k, d, a.nnz, ri, a.d_ro, a.d_ci, x, y, o1)
+    sp.sp_sddmm_balanced(a.m, a.k, d, a.nnz, ri, a.d_ro, a.d_ci, x, y, o2)
     return host(o1), host(o2)
 
 
@@ -162,11 +162,11 @@ def test_sddmm_balanced_imbalance_workload(swz):
 def test_sddmm_balanced_transformer_ffn():
     w = inputs.transformer_ffn()
     a = csr_of_row_lists(w["a"])
-    note("sddmm_balanced ffn alpha=1/8")
-    plain, bal = run_sddmm_pair(a, w["x"], w["y"], alpha=0.125, ri=swizzle(a))
+    note("sddmm_balanced ffn")
+    plain, bal = run_sddmm_pair(a, w["x"], w["y"], ri=swizzle(a))
     assert np.array_equal(plain.view(np.int32), bal.view(np.int32))
     ref, s = oracle.sddmm(a.m, a.k, w["d"], a.ro, a.ci, w["x"], w["y"])
-    check_close(bal, 0.125 * ref, 0.125 * s, "sddmm balanced ffn")
+    check_close(bal, ref, s, "sddmm balanced ffn")
 
 
 @pytest.mark.parametrize("d", [1, 3, 8, 64, 256, 600])

@@ -54,8 +54,8 @@ class Pair:
         out = torch.full((self.s.nnz,), float("nan"), device="cuda")
         sp.sp_spmm(self.a.m, self.a.k, self.n, self.a.nnz, self.ri_a, self.a.d_vals,
                    self.a.d_ro, self.a.d_ci, self.b, c)
-        sp.sp_sddmm(self.s.m, self.s.k, self.d, self.s.nnz, self.ri_s, self.s.d_ro,
-                    self.s.d_ci, self.x, self.y, self.alpha, out)
+        sp.sp_sddmm_batched(self.s.m, self.s.k, self.d, self.s.nnz, self.ri_s, self.s.d_ro,
+                            self.s.d_ci, self.x, self.y, self.alpha, out, 1, 0, 0, 0)
         return host(c), host(out)
 
     def check(self, what):

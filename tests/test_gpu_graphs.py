@@ -98,8 +98,8 @@ def test_graph_of_every_launch_kind():
         sp.sp_spmm(m, k, n, nnz, ri, vals, ro, cols, b, outs["c"])
         sp.sp_spmm_balanced(m, k, n, nnz, ri, vals, ro, cols, b, outs["c_bal"])
         sp.sp_spmm_ex(m, k, n, nnz, ri, v16, ro, cols, b16, outs["c_bf16"])
-        sp.sp_sddmm(m, k, d, nnz, ri, ro, cols, x, y, 1.0, outs["s"])
-        sp.sp_sddmm_balanced(m, k, d, nnz, ri, ro, cols, x, y, 1.0, outs["s_bal"])
+        sp.sp_sddmm(m, k, d, nnz, ri, ro, cols, x, y, outs["s"])
+        sp.sp_sddmm_balanced(m, k, d, nnz, ri, ro, cols, x, y, outs["s_bal"])
         outs["s_gen"].copy_(prior)
         sp.sp_sddmm_general(m, k, d, nnz, ri, ro, cols, vals, x, y, sp.SP_Y_KD, 0.5, 2.0,
                             outs["s_gen"])

@@ -52,11 +52,14 @@ def swizzle(m, d_ro):
     return ri
 
 
-def spmm16(kind, m, k, n, ro, ci, vals32, b32, swz=True):
+def spmm16(kind, m, k, n, ro, ci, vals32, b32, swz=True, c_offset=0):
+    """sp_spmm_ex on 16-bit copies of the values and B; C starts c_offset
+    floats into its allocation (c_offset = 1: only 4-byte aligned)."""
     d_v, v = to16(vals32, kind)
     d_b, b = to16(b32, kind)
     d_ro = devi(ro)
-    c = torch.full((m, n), float("nan"), device="cuda")
+    c_buf = torch.full((m * n + c_offset,), float("nan"), device="cuda")
+    c = c_buf[c_offset:].view(m, n)
     sp.sp_spmm_ex(m, k, n, ci.size, swizzle(m, d_ro) if swz else None, d_v, d_ro,
                   devi(ci), d_b, c)
     return host(c), v, b
@@ -156,15 +159,14 @@ def test_spmm_identity_and_unaligned(kind):
 
 
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
-def test_lstm_sampled_rows(kind):
+def test_lstm_whole(kind):
     w = inputs.lstm(0.9)
     a = w["a"]
     ro = oracle.csr_offsets_from_lengths(a.lengths)
     note(f"spmm_ex {kind} lstm 90%")
     c, v, b = spmm16(kind, a.m, a.k, w["n"], ro, a.cols, a.values, w["b"])
-    rows = np.random.default_rng(630).choice(a.m, 512, replace=False).astype(np.int32)
-    ref, s = oracle.spmm_rows(rows, w["n"], ro, a.cols, v, b)
-    check_close(c[rows], ref, s, f"spmm {kind} lstm sampled")
+    ref, s = oracle.spmm(a.m, a.k, w["n"], ro, a.cols, v, b)
+    check_close(c, ref, s, f"spmm {kind} lstm")
 
 
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
@@ -252,7 +254,10 @@ def test_spmm_b_beyond_2gib(kind):
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16, 24, 32])
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
 def test_spmm_lds_resident_b(kind, n):
-    m, k = 8192, 256
+    # enough rows that every width takes the streaming kernel: it needs at
+    # least (256 CUs) * k * n entries, i.e. 65,536 * n here (rows average 160)
+    k = 256
+    m = max(8192, (65536 * n * 5 // 4) // 160)
     lengths = np.random.default_rng(700 + n).integers(100, 220, m).astype(np.int32)
     lengths[::97] = 0                                   # some empty rows
     # nnz = 3 (mod 4) with a non-empty last row: the array's final segment
@@ -297,19 +302,18 @@ def _hbm_stream_n4():
 
 
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
-def test_spmm_hbm_stream_n4_sampled_rows(kind):
+def test_spmm_hbm_stream_n4_whole(kind):
     w = _hbm_stream_n4()
     a = w["a"]
     ro = oracle.csr_offsets_from_lengths(a.lengths)
     note(f"spmm_ex {kind} hbm_stream 65536x8192x4 (B in LDS)")
     c, v, b = spmm16(kind, w["m"], w["k"], w["n"], ro, a.cols, a.values, w["b"], swz=False)
-    rows = np.random.default_rng(720).choice(w["m"], 300, replace=False)
-    ref, s = oracle.spmm_rows(rows, w["n"], ro, a.cols, v, b)
-    check_close(c[rows], ref, s, f"spmm {kind} hbm_stream n=4")
+    ref, s = oracle.spmm(w["m"], w["k"], w["n"], ro, a.cols, v, b)
+    check_close(c, ref, s, f"spmm {kind} hbm_stream n=4")
 
 
 @pytest.mark.parametrize("tail", [0, 1, 2, 3])
-@pytest.mark.parametrize("n", [1, 4])
+@pytest.mark.parametrize("n", [1, 4, 8, 16])
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
 def test_spmm_lds_array_end(kind, n, tail):
     # nnz = tail (mod 4) with the last row non-empty: the array's last segment
@@ -328,6 +332,22 @@ def test_spmm_lds_array_end(kind, n, tail):
     check_close(c, ref, s, f"spmm {kind} lds array end n={n} tail={tail}")
 
 
+@pytest.mark.parametrize("n", [4, 12])
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_spmm_lds_misaligned_c(kind, n):
+    # 16-bit B widened to fp32 vectors of 4 in LDS stores C in vectors of 4 too:
+    # a C that is only 4-byte aligned must take the element-wise form instead
+    m, k = 8192, 256
+    lengths = np.random.default_rng(760 + n).integers(100, 220, m).astype(np.int32)
+    rl = inputs.random_row_lists(761 + n, m, k, lengths)
+    ro = oracle.csr_offsets_from_lengths(lengths)
+    b32 = inputs.random_dense(762 + n, k, n)
+    note(f"spmm_ex {kind} lds misaligned C n={n} nnz={rl.cols.size}")
+    c, v, b = spmm16(kind, m, k, n, ro, rl.cols, rl.values, b32, c_offset=1)
+    ref, s = oracle.spmm(m, k, n, ro, rl.cols, v, b)
+    check_close(c, ref, s, f"spmm {kind} lds misaligned C n={n}")
+
+
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
 @pytest.mark.parametrize("k,n,m", [(8192, 16, 16000), (8192, 24, 10000), (8192, 32, 8000)])
 def test_spmm_lds_16bit_b_column_slices(kind, k, n, m):
@@ -339,9 +359,8 @@ def test_spmm_lds_16bit_b_column_slices(kind, k, n, m):
     b32 = inputs.random_dense(742 + n, k, n)
     note(f"spmm_ex {kind} 16-bit B in LDS, slices k={k} n={n} m={m} nnz={rl.cols.size}")
     c, v, b = spmm16(kind, m, k, n, ro, rl.cols, rl.values, b32)
-    rows = np.random.default_rng(743).choice(m, 400, replace=False)
-    ref, s = oracle.spmm_rows(rows, n, ro, rl.cols, v, b)
-    check_close(c[rows], ref, s, f"spmm {kind} 16-bit B slices k={k} n={n}")
+    ref, s = oracle.spmm(m, k, n, ro, rl.cols, v, b)
+    check_close(c, ref, s, f"spmm {kind} 16-bit B slices k={k} n={n}")
 
 
 def test_sddmm_f16_subnormal_operands():

@@ -112,8 +112,7 @@ def test_general_reduces_to_specialised(ffn, layout):
     w, a = ffn
     note(f"sddmm_general vs sp_sddmm layout={layout}")
     spec = torch.empty(a.nnz, device="cuda")
-    sp.sp_sddmm(a.m, a.k, w["d"], a.nnz, None, a.d_ro, a.d_ci, dev(w["x"]), dev(w["y"]),
-                1.0, spec)
+    sp.sp_sddmm(a.m, a.k, w["d"], a.nnz, None, a.d_ro, a.d_ci, dev(w["x"]), dev(w["y"]), spec)
     got = run_general(a, w["x"], w["y"], layout)
     if layout == KD:
         assert np.array_equal(got.view(np.int32), host(spec).view(np.int32))

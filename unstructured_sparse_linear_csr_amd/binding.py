@@ -44,10 +44,10 @@ SIGNATURES = {
                 _c_int),
     "sp_spmm_batched": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                          _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
-    "sp_sddmm": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_float,
-                  _vp, _vp], _c_int),
-    "sp_sddmm_balanced": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_float,
-                           _vp, _vp], _c_int),
+    "sp_sddmm": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+                 _c_int),
+    "sp_sddmm_balanced": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+                           _vp], _c_int),
     "sp_sddmm_batched": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                           _c_float, _vp, _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
     "sp_sddmm_general": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -201,21 +201,20 @@ def sp_spmm_batched(m, k, n, nnz, row_indices, values, row_offsets, col_indices,
         "sp_spmm_batched")
 
 
-def sp_sddmm(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, alpha, out,
-             stream=None):
+def sp_sddmm(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, out, stream=None):
     _check(lib().sp_sddmm(
         m, k, d, nnz, _ptr(row_indices, _I32, "row_indices", True),
         _ptr(row_offsets, _I32, "row_offsets"), _ptr(col_indices, _I32, "col_indices", True),
-        _ptr(x, _F32, "x", True), _ptr(y, _F32, "y", True), float(alpha),
+        _ptr(x, _F32, "x", True), _ptr(y, _F32, "y", True),
         _ptr(out, _F32, "out", True), _stream(stream)), "sp_sddmm")
 
 
-def sp_sddmm_balanced(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, alpha, out,
+def sp_sddmm_balanced(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y, out,
                       stream=None):
     _check(lib().sp_sddmm_balanced(
         m, k, d, nnz, _ptr(row_indices, _I32, "row_indices", True),
         _ptr(row_offsets, _I32, "row_offsets"), _ptr(col_indices, _I32, "col_indices", True),
-        _ptr(x, _F32, "x", True), _ptr(y, _F32, "y", True), float(alpha),
+        _ptr(x, _F32, "x", True), _ptr(y, _F32, "y", True),
         _ptr(out, _F32, "out", True), _stream(stream)), "sp_sddmm_balanced")
 
 
@@ -443,6 +442,6 @@ def sddmm(mask: CsrMatrix, x: torch.Tensor, y: torch.Tensor, alpha: float = 1.0,
     if m != mask.m or y.shape != (mask.k, d):
         raise ValueError("shape mismatch between mask, x and y")
     o = out if out is not None else torch.empty(mask.nnz, dtype=_F32, device=x.device)
-    sp_sddmm(mask.m, mask.k, d, mask.nnz, mask.row_indices, mask.row_offsets,
-             mask.col_indices, x, y, alpha, o, stream)
+    sp_sddmm_batched(mask.m, mask.k, d, mask.nnz, mask.row_indices, mask.row_offsets,
+                     mask.col_indices, x, y, alpha, o, 1, 0, 0, 0, stream)
     return o

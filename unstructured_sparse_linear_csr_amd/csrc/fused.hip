@@ -3,8 +3,9 @@
 // SpMM and SDDMM for DL workloads), each kernel alone leaves the chip
 // two-thirds idle -- a few thousand one-wave workgroups, each a short chain
 // of dependent loads -- and pays its own launch.  Here the grid is the two
-// grids end to end: workgroup b < spmm_blocks runs the wide SpMM body on
-// SpMM work unit b, the rest run the SDDMM row body, so both sets of waves are
+// grids end to end: workgroups [0, gridDim.x - spmm_blocks) run the SDDMM row
+// body on SDDMM work unit b, the remaining spmm_blocks run the wide SpMM body
+// on SpMM work unit b - (gridDim.x - spmm_blocks), so both sets of waves are
 // resident together and their latencies overlap.  Each body is the same code
 // the separate launches run, so results are bit-identical to them.
 //

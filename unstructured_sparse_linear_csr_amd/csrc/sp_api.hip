@@ -389,20 +389,20 @@ sp_status_t sp_sddmm_batched(int m, int k, int d, int nnz, const int *row_indice
 
 sp_status_t sp_sddmm(int m, int k, int d, int nnz, const int *row_indices,
                      const int *row_offsets, const int *col_indices, const float *x,
-                     const float *y, float alpha, float *out, sp_stream_t stream)
+                     const float *y, float *out, sp_stream_t stream)
 {
     return sp_sddmm_batched(m, k, d, nnz, row_indices, row_offsets, col_indices, x, y,
-                            alpha, out, 1, 0, 0, 0, stream);
+                            1.f, out, 1, 0, 0, 0, stream);
 }
 
 sp_status_t sp_sddmm_balanced(int m, int k, int d, int nnz, const int *row_indices,
                               const int *row_offsets, const int *col_indices, const float *x,
-                              const float *y, float alpha, float *out, sp_stream_t stream)
+                              const float *y, float *out, sp_stream_t stream)
 {
     spk::SddmmArgs a;
     bool work = false;
     const sp_status_t st = sddmm_prepare(m, k, d, nnz, row_indices, row_offsets, col_indices,
-                                         nullptr, spk::Dtype::f32, x, y, SP_Y_KD, alpha, 0.f,
+                                         nullptr, spk::Dtype::f32, x, y, SP_Y_KD, 1.f, 0.f,
                                          out, 1, 0, 0, 0, 0, &a, &work);
     if (st != SP_SUCCESS || !work) return st;
     a.parts = 4;  // a workgroup of waves per row, each taking every 4th window of 64 entries

@@ -684,7 +684,9 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
             lds_kvec = 8;
             lds_eb = 2;
         } else {
-            lds_kvec = (a.n % 4 == 0 && aligned(a.b, 8) && a.stride_b % 4 == 0) ? 4 : 1;
+            // C is stored in fp32 vectors of 4 as well
+            lds_kvec = (a.n % 4 == 0 && aligned(a.b, 8) && a.stride_b % 4 == 0 &&
+                        aligned16(a.c) && a.stride_c % 4 == 0) ? 4 : 1;
         }
         lds_nv = (a.n + lds_kvec - 1) / lds_kvec;
         lds_ok = buf && lds_nv <= 4 && (long long)a.nnz * 4 <= (1LL << 31);
