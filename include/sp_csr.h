@@ -116,9 +116,37 @@ sp_status_t sp_csr_fill_dense(int m, int k, const unsigned char *mask,
  * longest first, rows of equal count by ascending row index (a unique,
  * deterministic order).
  *   row_offsets  int32[m+1] (CSR row offsets)
- *   row_indices  int32[m], output */
+ *   row_indices  int32[m], output
+ * Workspace-free: each row's slot is its rank among all rows' (length, index)
+ * keys, m^2 comparisons -- a few microseconds up to ~16 K rows; above that
+ * sp_row_swizzle_ws gives the same order in time linear in m. */
 sp_status_t sp_row_swizzle(int m, const int *row_offsets, int *row_indices,
                            sp_stream_t stream);
+
+/* *bytes = the device workspace sp_row_swizzle_ws needs for m rows: 0 up to
+ * 16,384 rows, else 16 bytes per row plus 1 KiB per 4,096 rows (rounded up to
+ * 256-byte multiples).  Host arithmetic only; m < 0 or bytes == NULL returns
+ * SP_ERROR_INVALID_VALUE. */
+sp_status_t sp_row_swizzle_workspace(int m, size_t *bytes);
+
+/* sp_row_swizzle for structures of many rows ("Interesting ideas" I4 of the
+ * card; the order is the same, bit for bit): above 16,384 rows a stable radix
+ * sort of the rows by (k - length), 8 bits per pass, ceil(log2(k + 1) / 8)
+ * passes, each three launches linear in m (two passes for k <= 65,535); at
+ * most 16,384 rows, sp_row_swizzle's rank sort (no workspace used).
+ *   k            columns of the matrix: every row holds at most k entries
+ *                (true of any valid structure; a longer row is ordered as if
+ *                it had k entries)
+ *   row_offsets  int32[m+1];  row_indices  int32[m], output
+ *   workspace    device memory of at least sp_row_swizzle_workspace(m) bytes,
+ *                256-byte aligned, not overlapping the arguments (may be NULL
+ *                when that size is 0); contents on entry do not matter and on
+ *                return are unspecified; calls sharing one on overlapping
+ *                streams race.
+ * Errors: m < 0, k < 0, a NULL array that must exist, or a missing, short or
+ * misaligned workspace returns SP_ERROR_INVALID_VALUE. */
+sp_status_t sp_row_swizzle_ws(int m, int k, const int *row_offsets, int *row_indices,
+                              void *workspace, size_t workspace_bytes, sp_stream_t stream);
 
 /* CSR row offsets and the swizzled row order from row lengths in one launch
  * (the order depends on the lengths only): row_offsets as

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 24, declared
+    assert len(declared) == 26, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -343,6 +343,32 @@ def test_build_and_swizzle_validation(lib):
     assert lib.sp_row_swizzle(-1, FAKE, FAKE, s) == INVALID
     assert lib.sp_row_swizzle(3, NULL, FAKE, s) == INVALID
     assert lib.sp_row_swizzle(3, FAKE, NULL, s) == INVALID
+
+
+def test_row_swizzle_ws_validation(lib):
+    s = NULL
+    size = ctypes.c_size_t(0)
+    q = lib.sp_row_swizzle_workspace
+    assert q(-1, ctypes.byref(size)) == INVALID
+    assert q(5, None) == INVALID
+    # no workspace up to the rank sort's row limit
+    assert q(16384, ctypes.byref(size)) == OK and size.value == 0
+    assert q(16385, ctypes.byref(size)) == OK
+    # four arrays of m ints and the radix tile counters, 256-byte multiples
+    arr = (16385 * 4 + 255) // 256 * 256
+    hist = (256 * (5 + 1) * 4 + 255) // 256 * 256
+    assert size.value == 4 * arr + hist
+    need = size.value
+    f = lib.sp_row_swizzle_ws
+    big = ctypes.c_void_p(0x100000)
+    assert f(-1, 4, FAKE, FAKE, NULL, 0, s) == INVALID
+    assert f(5, -1, FAKE, FAKE, NULL, 0, s) == INVALID
+    assert f(5, 4, NULL, FAKE, NULL, 0, s) == INVALID
+    assert f(5, 4, FAKE, NULL, NULL, 0, s) == INVALID
+    assert f(0, 4, FAKE, NULL, NULL, 0, s) == OK              # nothing to order
+    assert f(16385, 9, FAKE, FAKE, NULL, need, s) == INVALID   # workspace missing
+    assert f(16385, 9, FAKE, FAKE, big, need - 1, s) == INVALID  # too short
+    assert f(16385, 9, FAKE, FAKE, ctypes.c_void_p(0x100010), need, s) == INVALID  # misaligned
 
 
 def test_softmax_validation(lib):

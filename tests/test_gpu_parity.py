@@ -162,6 +162,53 @@ def test_build_from_lengths_bit_exact(name):
     assert np.array_equal(host(ri), oracle.row_swizzle(ro_o)), name
 
 
+# Many rows: the workspace form (radix sort above 16,384 rows).  Keys k - length
+# take 1 pass for k < 256, 2 up to k < 65,536, 3 beyond; the rows include
+# ties, empty rows and rows of length k (key 0).
+def _swizzle_ws_cases():
+    rng = np.random.default_rng(12)
+    lstm = inputs.lstm(0.9)["a"].lengths
+    return {
+        "limit_16384_k40": (rng.integers(0, 41, 16384).astype(np.int32), 40),
+        "just_above_16385_k40": (rng.integers(0, 41, 16385).astype(np.int32), 40),
+        "one_pass_k255": (rng.integers(0, 256, 40000).astype(np.int32), 255),
+        "two_passes_k256": (rng.integers(0, 257, 40000).astype(np.int32), 256),
+        "lstm_rows_x8_65536": (np.tile(lstm, 8), 2048),
+        "ties_65536_k9": (rng.integers(0, 10, 65536).astype(np.int32), 9),
+        "three_passes_k70000": (rng.integers(0, 70001, 50000).astype(np.int32), 70000),
+        "all_empty_30000_k0": (np.zeros(30000, np.int32), 0),
+        "rows_1100000_k8192": (rng.integers(0, 1639, 1100000).astype(np.int32), 8192),
+    }
+
+
+@pytest.mark.parametrize("name", list(_swizzle_ws_cases()))
+def test_row_swizzle_ws_bit_exact(name):
+    lengths, k = _swizzle_ws_cases()[name]
+    m = lengths.shape[0]
+    ro = oracle.csr_offsets_from_lengths(lengths)
+    note(f"row_swizzle_ws {name} m={m} k={k}")
+    ws_bytes = sp.sp_row_swizzle_workspace(m)
+    assert (ws_bytes == 0) == (m <= 16384)
+    ws = torch.full((max(ws_bytes, 1),), 0xAB, dtype=torch.uint8, device="cuda")
+    ri = torch.full((m,), -7, dtype=torch.int32, device="cuda")
+    sp.sp_row_swizzle_ws(m, k, dev(ro), ri, ws if ws_bytes else None)
+    assert np.array_equal(host(ri), oracle.row_swizzle(ro)), name
+
+
+def test_row_swizzle_ws_matches_rank_sort_65536():
+    # both device methods at m = 65,536 give the one order
+    lengths = np.tile(inputs.lstm(0.9)["a"].lengths, 8)
+    m = lengths.shape[0]
+    ro = dev(oracle.csr_offsets_from_lengths(lengths))
+    note("row_swizzle rank vs radix m=65536")
+    ri_rank = torch.empty(m, dtype=torch.int32, device="cuda")
+    sp.sp_row_swizzle(m, ro, ri_rank)
+    ws = torch.empty(sp.sp_row_swizzle_workspace(m), dtype=torch.uint8, device="cuda")
+    ri_radix = torch.empty(m, dtype=torch.int32, device="cuda")
+    sp.sp_row_swizzle_ws(m, 2048, ro, ri_radix, ws)
+    assert np.array_equal(host(ri_rank), host(ri_radix))
+
+
 # ------------------------------------------------------------------ SpMM, workloads
 
 def test_spmm_tiny():

@@ -39,6 +39,8 @@ SIGNATURES = {
     "sp_csr_count_dense": ([_c_int, _c_int, _vp, _vp, _vp], _c_int),
     "sp_csr_fill_dense": ([_c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp], _c_int),
     "sp_row_swizzle": ([_c_int, _vp, _vp, _vp], _c_int),
+    "sp_row_swizzle_workspace": ([_c_int, ctypes.POINTER(ctypes.c_size_t)], _c_int),
+    "sp_row_swizzle_ws": ([_c_int, _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp], _c_int),
     "sp_csr_build_from_lengths": ([_c_int, _vp, _vp, _vp, _vp], _c_int),
     "sp_spmm": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
                 _c_int),
@@ -171,6 +173,21 @@ def sp_row_swizzle(m, row_offsets, row_indices, stream=None):
     _check(lib().sp_row_swizzle(
         m, _ptr(row_offsets, _I32, "row_offsets"), _ptr(row_indices, _I32, "row_indices", True),
         _stream(stream)), "sp_row_swizzle")
+
+
+def sp_row_swizzle_workspace(m) -> int:
+    size = ctypes.c_size_t(0)
+    _check(lib().sp_row_swizzle_workspace(m, ctypes.byref(size)), "sp_row_swizzle_workspace")
+    return size.value
+
+
+def sp_row_swizzle_ws(m, k, row_offsets, row_indices, workspace, stream=None):
+    """workspace: a uint8 device tensor of at least sp_row_swizzle_workspace(m)
+    bytes, or None when that is 0."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sp_row_swizzle_ws(
+        m, k, _ptr(row_offsets, _I32, "row_offsets"), _ptr(row_indices, _I32, "row_indices", True),
+        _ptr(workspace, _U8, "workspace", True), ws_bytes, _stream(stream)), "sp_row_swizzle_ws")
 
 
 def sp_csr_build_from_lengths(m, lengths, row_offsets, row_indices, stream=None):

@@ -12,6 +12,15 @@
 // is m^2 64-bit comparisons, served from LDS as broadcast reads; the pass runs
 // once per sparsity structure and its order is reused by every SpMM and SDDMM
 // on that structure.
+//
+// Many rows (above kRankMaxRows) with a caller workspace: the same order by a
+// stable radix sort of the keys k - length (in [0, k] for a structure whose
+// rows hold at most k distinct columns), carrying the row index; ascending
+// keys are descending lengths and the sort's stability keeps rows of equal
+// length in ascending index order.  ceil(log2(k + 1) / 8) passes of three
+// launches each, linear in m.
+#include <algorithm>
+
 #include "sp_device.h"
 #include "sp_launch.h"
 #include "sp_scan.h"
@@ -27,6 +36,8 @@ constexpr int kSwizzleThreads = 256;
 constexpr int kFewRows = 4096;
 template <int kLanes> constexpr int rows_per_block() { return kSwizzleThreads / kLanes; }
 constexpr int kSwizzleTile = 2048;  // keys staged in LDS per pass (16 KB)
+// Above this many rows the workspace form takes the radix sort.
+constexpr int kRankMaxRows = 16384;
 
 __device__ __forceinline__ unsigned long long row_key(int length, int row)
 {
@@ -135,7 +146,60 @@ hipError_t launch_swizzle_t(int m, const int *row_offsets, int *row_indices, hip
     return hipGetLastError();
 }
 
+// keys[i] = k - length of row i, clamped to [0, k]: a row longer than k (not a
+// valid structure) sorts with the rows of length k.
+__global__ __launch_bounds__(256) void swizzle_keys_kernel(int m, int k,
+                                                           const int *__restrict__ row_offsets,
+                                                           int *__restrict__ keys)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= m) return;
+    const long long key = (long long)k - ((long long)row_offsets[i + 1] - row_offsets[i]);
+    keys[i] = (int)(key < 0 ? 0 : key > k ? k : key);
+}
+
+struct SwizzleWorkspace {
+    int *keys[2], *vals[2], *hist;
+    size_t bytes;
+};
+
+SwizzleWorkspace carve_swizzle(int m, void *base)
+{
+    const size_t arr = align256((size_t)m * sizeof(int));
+    char *p = static_cast<char *>(base);
+    SwizzleWorkspace w;
+    w.keys[0] = reinterpret_cast<int *>(p);
+    w.keys[1] = reinterpret_cast<int *>(p + arr);
+    w.vals[0] = reinterpret_cast<int *>(p + 2 * arr);
+    w.vals[1] = reinterpret_cast<int *>(p + 3 * arr);
+    w.hist = reinterpret_cast<int *>(p + 4 * arr);
+    w.bytes = 4 * arr + radix_hist_bytes(m);
+    return w;
+}
+
 }  // namespace
+
+size_t row_swizzle_workspace_bytes(int m)
+{
+    return m <= kRankMaxRows ? 0 : carve_swizzle(m, nullptr).bytes;
+}
+
+hipError_t launch_row_swizzle_ws(int m, int k, const int *row_offsets, int *row_indices,
+                                 void *workspace, hipStream_t stream)
+{
+    if (m <= kRankMaxRows) return launch_row_swizzle(m, row_offsets, row_indices, stream);
+    const SwizzleWorkspace w = carve_swizzle(m, workspace);
+    // The initial keys go to keys[1]; the first pass writes keys[0] (see
+    // launch_radix_sort), the second keys[1] again.
+    hipLaunchKernelGGL(swizzle_keys_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0,
+                       stream, m, k, row_offsets, w.keys[1]);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // keys in [0, k]; at least one pass, so the values always reach row_indices
+    const int passes = std::max(1, radix_passes((long long)k + 1));
+    return launch_radix_sort(m, passes, w.keys[1], nullptr, w.keys, w.vals, row_indices,
+                             w.hist, stream, nullptr, nullptr);
+}
 
 hipError_t launch_build_and_swizzle(int m, const int *lengths, int *row_offsets,
                                    int *row_indices, hipStream_t stream)

@@ -203,6 +203,27 @@ sp_status_t sp_row_swizzle(int m, const int *row_offsets, int *row_indices,
                                             as_stream(stream)));
 }
 
+sp_status_t sp_row_swizzle_workspace(int m, size_t *bytes)
+{
+    if (m < 0 || bytes == nullptr) return SP_ERROR_INVALID_VALUE;
+    *bytes = spk::row_swizzle_workspace_bytes(m);
+    return SP_SUCCESS;
+}
+
+sp_status_t sp_row_swizzle_ws(int m, int k, const int *row_offsets, int *row_indices,
+                              void *workspace, size_t workspace_bytes, sp_stream_t stream)
+{
+    if (m < 0 || k < 0 || !need(row_offsets, m) || !need(row_indices, m))
+        return SP_ERROR_INVALID_VALUE;
+    if (m == 0) return SP_SUCCESS;
+    const size_t want = spk::row_swizzle_workspace_bytes(m);
+    if (want > 0 && (workspace == nullptr || workspace_bytes < want ||
+                     reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+        return SP_ERROR_INVALID_VALUE;
+    return from_hip(spk::launch_row_swizzle_ws(m, k, row_offsets, row_indices, workspace,
+                                               as_stream(stream)));
+}
+
 sp_status_t sp_csr_build_from_lengths(int m, const int *lengths, int *row_offsets,
                                       int *row_indices, sp_stream_t stream)
 {

@@ -64,6 +64,11 @@ hipError_t launch_build_and_swizzle(int m, const int *lengths, int *row_offsets,
                                    int *row_indices, hipStream_t stream);
 hipError_t launch_row_swizzle(int m, const int *row_offsets, int *row_indices,
                               hipStream_t stream);
+// The workspace form: the rank sort up to its row limit (no workspace), a
+// radix sort above it in row_swizzle_workspace_bytes(m) bytes of workspace.
+size_t row_swizzle_workspace_bytes(int m);
+hipError_t launch_row_swizzle_ws(int m, int k, const int *row_offsets, int *row_indices,
+                                 void *workspace, hipStream_t stream);
 hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream);
 hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream);
 hipError_t launch_spmm_sddmm(const SpmmArgs &x, const SddmmArgs &y, hipStream_t stream);
@@ -72,6 +77,21 @@ hipError_t launch_row_softmax(int m, const int *row_indices, const int *row_offs
                               const float *in, float *out, int batch, long long stride_in,
                               long long stride_out, hipStream_t stream);
 hipError_t launch_fill_zero(float *dst, long long count, hipStream_t stream);
+size_t align256(size_t b);
+// Stable least-significant-digit radix sort of n (key, value) int pairs, 8-bit
+// digits, `passes` passes (keys in [0, 2^(8 * passes))), each pass three
+// launches (tile digit counts, per-digit scan over tiles, stable scatter).
+// keys_in / vals_in are read only (vals_in NULL: the identity 0..n-1); passes
+// alternate between keys_buf[0/1] and vals_buf[0/1] (n ints each); the last
+// pass writes its values to vals_last when that is not NULL.  hist needs
+// radix_hist_bytes(n).  The sorted arrays' addresses are returned through
+// keys_sorted / vals_sorted (the inputs themselves when passes == 0).
+size_t radix_hist_bytes(int n);
+int radix_passes(long long bound);  // passes for keys in [0, bound)
+hipError_t launch_radix_sort(int n, int passes, const int *keys_in, const int *vals_in,
+                             int *const keys_buf[2], int *const vals_buf[2], int *vals_last,
+                             int *hist, hipStream_t stream, const int **keys_sorted,
+                             const int **vals_sorted);
 size_t transpose_workspace_bytes(int nnz);
 hipError_t launch_csr_transpose(int m, int k, int nnz, const int *row_offsets,
                                 const int *col_indices, const float *values,

@@ -330,13 +330,16 @@ struct Workspace {
     size_t bytes;
 };
 
+}  // namespace
+
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+namespace {
 
 Workspace carve(int nnz, void *base)
 {
     const size_t arr = align256((size_t)std::max(nnz, 1) * sizeof(int));
-    const int tiles = (nnz + kTile - 1) / kTile;
-    const size_t hist = align256((size_t)kDigits * (size_t)(tiles + 1) * sizeof(int));
+    const size_t hist = radix_hist_bytes(nnz);
     Workspace w;
     char *p = static_cast<char *>(base);
     w.keys[0] = reinterpret_cast<int *>(p);
@@ -405,6 +408,49 @@ hipError_t launch_count_transpose(int m, int k, int nnz, int rows_per_range,
 
 size_t transpose_workspace_bytes(int nnz) { return carve(nnz, nullptr).bytes; }
 
+size_t radix_hist_bytes(int n)
+{
+    const int tiles = (n + kTile - 1) / kTile;
+    return align256((size_t)kDigits * (size_t)(tiles + 1) * sizeof(int));
+}
+
+int radix_passes(long long bound)
+{
+    int bits = 0;
+    while (bits < 31 && (1LL << bits) < bound) ++bits;  // keys lie in [0, 2^bits)
+    return (bits + 7) / 8;
+}
+
+hipError_t launch_radix_sort(int n, int passes, const int *keys_in, const int *vals_in,
+                             int *const keys_buf[2], int *const vals_buf[2], int *vals_last,
+                             int *hist, hipStream_t stream, const int **keys_sorted,
+                             const int **vals_sorted)
+{
+    hipError_t e;
+    const int tiles = (n + kTile - 1) / kTile;
+    const int *keys = keys_in;
+    const int *vals = vals_in;
+    for (int pass = 0; pass < passes; ++pass) {
+        const int shift = 8 * pass;
+        int *keys_out = keys_buf[pass & 1];
+        int *vals_out = (pass == passes - 1 && vals_last) ? vals_last : vals_buf[pass & 1];
+        hipLaunchKernelGGL(radix_upsweep_kernel, dim3((unsigned)tiles), dim3(kSortThreads), 0,
+                           stream, n, shift, keys, hist, tiles);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(digit_scan_kernel, dim3(kDigits), dim3(kDigitScanThreads), 0, stream,
+                           tiles, hist);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(radix_downsweep_kernel, dim3((unsigned)tiles), dim3(kSortThreads), 0,
+                           stream, n, shift, keys, vals, keys_out, vals_out, hist, tiles);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        keys = keys_out;
+        vals = vals_out;
+    }
+    if (keys_sorted) *keys_sorted = keys;
+    if (vals_sorted) *vals_sorted = vals;
+    return hipSuccess;
+}
+
 hipError_t launch_csr_transpose(int m, int k, int nnz, const int *row_offsets,
                                 const int *col_indices, const float *values,
                                 int *t_row_offsets, int *t_col_indices, float *t_values,
@@ -416,33 +462,17 @@ hipError_t launch_csr_transpose(int m, int k, int nnz, const int *row_offsets,
     if (const int s = count_rows_per_range(m, k, nnz))
         return launch_count_transpose(m, k, nnz, s, row_offsets, col_indices, values,
                                       t_row_offsets, t_col_indices, t_values, t_perm, w, stream);
-    const int tiles = (nnz + kTile - 1) / kTile;
-    int bits = 0;
-    while (bits < 31 && (1LL << bits) < (long long)k) ++bits;  // columns lie in [0, 2^bits)
-    const int passes = (bits + 7) / 8;
 
     hipLaunchKernelGGL(expand_rows_kernel, dim3((unsigned)m), dim3(kWave), 0, stream,
                        row_offsets, w.rowid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    // Columns lie in [0, k).  With no pass (k == 1) every column is 0: the
+    // entries are already in order.
     const int *keys = col_indices;
     const int *vals = nullptr;
-    for (int pass = 0; pass < passes; ++pass) {
-        const int shift = 8 * pass;
-        int *keys_out = w.keys[pass & 1];
-        int *vals_out = w.vals[pass & 1];
-        hipLaunchKernelGGL(radix_upsweep_kernel, dim3((unsigned)tiles), dim3(kSortThreads), 0,
-                           stream, nnz, shift, keys, w.hist, tiles);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(digit_scan_kernel, dim3(kDigits), dim3(kDigitScanThreads), 0, stream,
-                           tiles, w.hist);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(radix_downsweep_kernel, dim3((unsigned)tiles), dim3(kSortThreads), 0,
-                           stream, nnz, shift, keys, vals, keys_out, vals_out, w.hist, tiles);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        keys = keys_out;
-        vals = vals_out;
-    }
-    // With no pass (k == 1) every column is 0: the entries are already in order.
+    if ((e = launch_radix_sort(nnz, radix_passes(k), col_indices, nullptr, w.keys, w.vals,
+                               nullptr, w.hist, stream, &keys, &vals)) != hipSuccess)
+        return e;
     hipLaunchKernelGGL(offsets_from_sorted_kernel, dim3(blocks_for((long long)nnz + 1)),
                        dim3(256), 0, stream, nnz, k, keys, t_row_offsets);
     if ((e = hipGetLastError()) != hipSuccess) return e;
