@@ -148,6 +148,23 @@ sp_status_t sp_row_swizzle_workspace(int m, size_t *bytes);
 sp_status_t sp_row_swizzle_ws(int m, int k, const int *row_offsets, int *row_indices,
                               void *workspace, size_t workspace_bytes, sp_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * sp_row_swizzle_ws without a workspace argument, the same order bit for bit.
+ * Above 16,384 rows the radix sort runs in a 32 MiB scratch array the library
+ * itself holds on each GPU it runs on (a device global, present from when the
+ * library is first used there until the process ends); the call allocates and
+ * frees nothing.  Every call on one GPU shares that GPU's array, so calls that
+ * may overlap in time on one GPU (several streams, several host threads) race
+ * and give unspecified orders; calls in one stream's order are safe.
+ *   m            rows, at most SP_ROW_SWIZZLE_NOALLOC_MAX_ROWS
+ *   k, row_offsets, row_indices   as sp_row_swizzle_ws
+ * Errors: as sp_row_swizzle_ws, and m > SP_ROW_SWIZZLE_NOALLOC_MAX_ROWS returns
+ * SP_ERROR_INVALID_VALUE before any HIP call. */
+#define SP_ROW_SWIZZLE_NOALLOC_MAX_ROWS 2000000
+sp_status_t sp_row_swizzle_noalloc(int m, int k, const int *row_offsets, int *row_indices,
+                                   sp_stream_t stream);
+
 /* CSR row offsets and the swizzled row order from row lengths in one launch
  * (the order depends on the lengths only): row_offsets as
  * sp_csr_offsets_from_lengths writes them and row_indices as sp_row_swizzle

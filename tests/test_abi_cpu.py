@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 26, declared
+    assert len(declared) == 27, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -343,6 +343,18 @@ def test_build_and_swizzle_validation(lib):
     assert lib.sp_row_swizzle(-1, FAKE, FAKE, s) == INVALID
     assert lib.sp_row_swizzle(3, NULL, FAKE, s) == INVALID
     assert lib.sp_row_swizzle(3, FAKE, NULL, s) == INVALID
+
+
+def test_row_swizzle_noalloc_validation(lib):
+    s = NULL
+    f = lib.sp_row_swizzle_noalloc
+    top = binding.SP_ROW_SWIZZLE_NOALLOC_MAX_ROWS
+    assert f(-1, 4, FAKE, FAKE, s) == INVALID
+    assert f(5, -1, FAKE, FAKE, s) == INVALID
+    assert f(5, 4, NULL, FAKE, s) == INVALID
+    assert f(5, 4, FAKE, NULL, s) == INVALID
+    assert f(top + 1, 4, FAKE, FAKE, s) == INVALID     # beyond the scratch array
+    assert f(0, 4, FAKE, NULL, s) == OK
 
 
 def test_row_swizzle_ws_validation(lib):

@@ -41,6 +41,7 @@ SIGNATURES = {
     "sp_row_swizzle": ([_c_int, _vp, _vp, _vp], _c_int),
     "sp_row_swizzle_workspace": ([_c_int, ctypes.POINTER(ctypes.c_size_t)], _c_int),
     "sp_row_swizzle_ws": ([_c_int, _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp], _c_int),
+    "sp_row_swizzle_noalloc": ([_c_int, _c_int, _vp, _vp, _vp], _c_int),
     "sp_csr_build_from_lengths": ([_c_int, _vp, _vp, _vp, _vp], _c_int),
     "sp_spmm": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
                 _c_int),
@@ -188,6 +189,15 @@ def sp_row_swizzle_ws(m, k, row_offsets, row_indices, workspace, stream=None):
     _check(lib().sp_row_swizzle_ws(
         m, k, _ptr(row_offsets, _I32, "row_offsets"), _ptr(row_indices, _I32, "row_indices", True),
         _ptr(workspace, _U8, "workspace", True), ws_bytes, _stream(stream)), "sp_row_swizzle_ws")
+
+
+SP_ROW_SWIZZLE_NOALLOC_MAX_ROWS = 2000000
+
+
+def sp_row_swizzle_noalloc(m, k, row_offsets, row_indices, stream=None):
+    _check(lib().sp_row_swizzle_noalloc(
+        m, k, _ptr(row_offsets, _I32, "row_offsets"), _ptr(row_indices, _I32, "row_indices", True),
+        _stream(stream)), "sp_row_swizzle_noalloc")
 
 
 def sp_csr_build_from_lengths(m, lengths, row_offsets, row_indices, stream=None):

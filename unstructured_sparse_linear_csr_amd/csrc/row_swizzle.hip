@@ -20,6 +20,7 @@
 // length in ascending index order.  ceil(log2(k + 1) / 8) passes of three
 // launches each, linear in m.
 #include <algorithm>
+#include <mutex>
 
 #include "sp_device.h"
 #include "sp_launch.h"
@@ -147,14 +148,16 @@ hipError_t launch_swizzle_t(int m, const int *row_offsets, int *row_indices, hip
 }
 
 // keys[i] = k - length of row i, clamped to [0, k]: a row longer than k (not a
-// valid structure) sorts with the rows of length k.
+// valid structure) sorts with the rows of length k.  The length is the 32-bit
+// difference of the offsets, as the rank sort takes it.
 __global__ __launch_bounds__(256) void swizzle_keys_kernel(int m, int k,
                                                            const int *__restrict__ row_offsets,
                                                            int *__restrict__ keys)
 {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i >= m) return;
-    const long long key = (long long)k - ((long long)row_offsets[i + 1] - row_offsets[i]);
+    const int len = (int)((unsigned)row_offsets[i + 1] - (unsigned)row_offsets[i]);
+    const long long key = (long long)k - len;
     keys[i] = (int)(key < 0 ? 0 : key > k ? k : key);
 }
 
@@ -182,6 +185,60 @@ SwizzleWorkspace carve_swizzle(int m, void *base)
 size_t row_swizzle_workspace_bytes(int m)
 {
     return m <= kRankMaxRows ? 0 : carve_swizzle(m, nullptr).bytes;
+}
+
+// ---- the allocation-free form
+// The radix sort's workspace for up to kNoAllocMaxRows rows, as a device
+// global: every GPU the library runs on holds its own copy, from when the code
+// object is loaded there until the process ends.  Nothing in it needs
+// clearing between calls (every word the sort reads was written earlier in the
+// same call), and calls that overlap on one GPU share it and race.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.  In host code the name `scratch` denotes a host-side
+// stand-in, so only this address may be handed to kernels.
+hipError_t scratch_address(void **out)
+{
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return e;
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[device] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (ptr == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[device] = ptr;
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+}
+
+}  // namespace
+
+bool row_swizzle_noalloc_fits(int m)
+{
+    return m >= 0 && row_swizzle_workspace_bytes(m) <= kScratchBytes;
+}
+
+hipError_t launch_row_swizzle_noalloc(int m, int k, const int *row_offsets, int *row_indices,
+                                      hipStream_t stream)
+{
+    if (m <= kRankMaxRows) return launch_row_swizzle(m, row_offsets, row_indices, stream);
+    if (!row_swizzle_noalloc_fits(m)) return hipErrorInvalidValue;
+    void *ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    return launch_row_swizzle_ws(m, k, row_offsets, row_indices, ws, stream);
 }
 
 hipError_t launch_row_swizzle_ws(int m, int k, const int *row_offsets, int *row_indices,

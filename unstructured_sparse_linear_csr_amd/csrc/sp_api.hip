@@ -224,6 +224,18 @@ sp_status_t sp_row_swizzle_ws(int m, int k, const int *row_offsets, int *row_ind
                                                as_stream(stream)));
 }
 
+sp_status_t sp_row_swizzle_noalloc(int m, int k, const int *row_offsets, int *row_indices,
+                                   sp_stream_t stream)
+{
+    if (m < 0 || k < 0 || !need(row_offsets, m) || !need(row_indices, m))
+        return SP_ERROR_INVALID_VALUE;
+    if (m > SP_ROW_SWIZZLE_NOALLOC_MAX_ROWS || !spk::row_swizzle_noalloc_fits(m))
+        return SP_ERROR_INVALID_VALUE;
+    if (m == 0) return SP_SUCCESS;
+    return from_hip(spk::launch_row_swizzle_noalloc(m, k, row_offsets, row_indices,
+                                                    as_stream(stream)));
+}
+
 sp_status_t sp_csr_build_from_lengths(int m, const int *lengths, int *row_offsets,
                                       int *row_indices, sp_stream_t stream)
 {

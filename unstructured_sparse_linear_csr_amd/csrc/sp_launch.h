@@ -69,6 +69,12 @@ hipError_t launch_row_swizzle(int m, const int *row_offsets, int *row_indices,
 size_t row_swizzle_workspace_bytes(int m);
 hipError_t launch_row_swizzle_ws(int m, int k, const int *row_offsets, int *row_indices,
                                  void *workspace, hipStream_t stream);
+// The workspace form on the library's own per-device scratch array (for
+// callers that cannot allocate); row_swizzle_noalloc_fits(m) says whether m
+// rows fit it.
+bool row_swizzle_noalloc_fits(int m);
+hipError_t launch_row_swizzle_noalloc(int m, int k, const int *row_offsets, int *row_indices,
+                                      hipStream_t stream);
 hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream);
 hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream);
 hipError_t launch_spmm_sddmm(const SpmmArgs &x, const SddmmArgs &y, hipStream_t stream);
