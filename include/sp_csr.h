@@ -352,6 +352,27 @@ sp_status_t sp_spmm_ex(int m, int k, int n, int nnz, const int *row_indices, int
                        const void *b, float *c, int batch, long long stride_values,
                        long long stride_b, long long stride_c, sp_stream_t stream);
 
+/* Which kernel sp_spmm_ex (and so sp_spmm / sp_spmm_batched) would run for
+ * these arguments: *name is set to a static string --
+ *   "wide"      one wave per row strip, B rows gathered from L2;
+ *   "panel"     B staged in LDS, shared by a panel of 64 rows (rows per panel
+ *               times density at least 4, n >= 64, fp32, one batch entry);
+ *   "narrow"    lanes over entries for B of at most 16 columns;
+ *   "lds"       the streaming kernel, narrow B copied into LDS once per CU;
+ *   "split"     few long rows cut into four parts per workgroup;
+ *   "none"      nothing to launch (m, n or batch is 0);
+ *   "unsupported" sizes beyond the launch limits.
+ * The choice depends on the sizes, the element type, the batch and strides,
+ * and the alignment of values, col_indices, b and c, which are not
+ * dereferenced (they may be any pointers with the caller's alignment; NULL is
+ * accepted where sp_spmm_ex would accept it).  It also reads the current
+ * device's compute-unit count and LDS size.  Host-only; enqueues nothing.
+ * An unknown dtype, invalid sizes or NULL `name` return SP_ERROR_INVALID_VALUE. */
+sp_status_t sp_spmm_kernel_name(int m, int k, int n, int nnz, int dtype, const void *values,
+                                const int *col_indices, const void *b, const float *c,
+                                int batch, long long stride_values, long long stride_b,
+                                long long stride_c, const char **name);
+
 /* sp_sddmm_batched with X and Y of element type `dtype` (strides in elements
  * of that type); out is fp32.  SP_DTYPE_F32 is exactly sp_sddmm_batched.  An
  * unknown dtype returns SP_ERROR_INVALID_VALUE. */

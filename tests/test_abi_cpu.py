@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 27, declared
+    assert len(declared) == 28, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -343,6 +343,22 @@ def test_build_and_swizzle_validation(lib):
     assert lib.sp_row_swizzle(-1, FAKE, FAKE, s) == INVALID
     assert lib.sp_row_swizzle(3, NULL, FAKE, s) == INVALID
     assert lib.sp_row_swizzle(3, FAKE, NULL, s) == INVALID
+
+
+def test_spmm_kernel_name(lib):
+    f = lib.sp_spmm_kernel_name
+    name = ctypes.c_char_p()
+    al = ctypes.c_void_p(0x10000)                     # 16-byte aligned stand-ins
+    assert f(8, 8, 4, 8, 0, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == OK
+    assert name.value == b"narrow"                      # fp32, n <= 16 columns
+    assert f(0, 8, 4, 8, 0, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == OK
+    assert name.value == b"none"
+    # 16-bit types never take the fp32 narrow kernel
+    assert f(8, 8, 512, 8, 1, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == OK
+    assert name.value in (b"wide", b"split")
+    assert f(8, 8, 4, 8, 7, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == INVALID
+    assert f(-1, 8, 4, 8, 0, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == INVALID
+    assert f(8, 8, 4, 8, 0, al, al, al, al, 1, 0, 0, 0, None) == INVALID
 
 
 def test_row_swizzle_noalloc_validation(lib):

@@ -261,6 +261,27 @@ sp_status_t sp_spmm_ex(int m, int k, int n, int nnz, const int *row_indices, int
     return from_hip(spk::launch_spmm(a, as_stream(stream)));
 }
 
+sp_status_t sp_spmm_kernel_name(int m, int k, int n, int nnz, int dtype, const void *values,
+                                const int *col_indices, const void *b, const float *c,
+                                int batch, long long stride_values, long long stride_b,
+                                long long stride_c, const char **name)
+{
+    if (name == nullptr) return SP_ERROR_INVALID_VALUE;
+    spk::Dtype dt;
+    if (!dtype_of(dtype, &dt)) return SP_ERROR_INVALID_VALUE;
+    // The choice depends on sizes, element type and pointer alignment only, so
+    // stand-ins take the place of the arrays the plan does not look at.
+    static const int kStandIn[2] = {0, 0};
+    spk::SpmmArgs a;
+    bool work = false;
+    const sp_status_t st = spmm_prepare(m, k, n, nnz, nullptr, dt, values, kStandIn, col_indices,
+                                        b, const_cast<float *>(c), batch, stride_values,
+                                        stride_b, stride_c, &a, &work);
+    if (st != SP_SUCCESS) return st;
+    *name = work ? spk::spmm_kernel_name(a) : "none";
+    return SP_SUCCESS;
+}
+
 sp_status_t sp_spmm_sddmm(int m, int k, int n, int nnz, const int *row_indices,
                           const float *values, const int *row_offsets, const int *col_indices,
                           const float *b, float *c, int s_m, int s_k, int d, int s_nnz,

@@ -4,13 +4,16 @@
 
 #include "sp_launch.h"
 #include "sddmm_rows.h"
+#include "spmm_panel.h"
 #include "spmm_wide.h"
 
 namespace spk {
 
 struct SpmmPlan {
-    enum Kind { kWide, kNarrow, kLds, kBalanced, kSplit } kind;
+    enum Kind { kWide, kNarrow, kLds, kBalanced, kSplit, kPanel } kind;
     spmm_detail::SpmmParams p;
+    spmm_detail::PanelParams q;  // panel kernel
+    int panel = 0;               // panel kernel: 0 many tiles (64-row panels), 1 few (32)
     Dtype dtype;
     bool vec, vec_csr, buf;
     int lpr;     // wide: lanes per row

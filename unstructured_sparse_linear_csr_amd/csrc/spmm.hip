@@ -2,12 +2,14 @@
 // ("Sparse GPU Kernels for Deep Learning", summary card, "Summary").  The wide
 // kernel's body, and the design notes for it, are in spmm_wide.h; this file
 // holds the narrow-B kernels and the variant selection.
+#include <algorithm>
 #include <type_traits>
 
 #include "sp_device.h"
 #include "sp_launch.h"
 #include "sp_types.h"
 #include "sp_plan.h"
+#include "spmm_panel.h"
 #include "spmm_wide.h"
 
 namespace spk {
@@ -21,6 +23,73 @@ template <typename E, int kLpr, int kVec, bool kVecCsr, bool kBuf>
 __global__ __launch_bounds__(kWave) void spmm_kernel(SpmmParams p)
 {
     spmm_wide_body<E, kLpr, kVec, kVecCsr, kBuf>(p, wide_work(p, blockIdx.x));
+}
+
+#ifndef SP_PANEL_MIN_REUSE
+#define SP_PANEL_MIN_REUSE 4.0
+#endif
+constexpr double kPanelMinReuse = SP_PANEL_MIN_REUSE;
+
+// B staged in LDS per row panel (spmm_panel.h).  Column tiles are the outer
+// units of the XCD order, so the workgroups sharing a tile share an L2.  Two
+// shapes, both 128-column tiles of 16 lanes x 8 columns per row and 8 waves:
+//   kPanelMany: panels of 64 rows, chunks of 128 B rows in two buffers -- for
+//     problems with many column tiles (the ResNet-50 1x1 layer: 49 tiles);
+//   kPanelFew: panels of 32 rows, chunks of 224 B rows in one buffer with
+//     128-entry windows -- for one or two tiles over many rows (the LSTM layer),
+//     where 64-row panels would leave half the CUs idle.
+using PanelMany = PanelShape<16, 2, 8, 2, 4, 128, 2>;
+using PanelFew = PanelShape<16, 2, 8, 1, 8, 224, 1>;
+
+template <class S, int kLpr, int kVecs, int kWaves, int kRounds, int kEpl, int kKc, int kBufs>
+__global__ __launch_bounds__(S::kThreads) void spmm_panel_kernel(SpmmParams p, PanelParams q)
+{
+    spmm_panel_body<kLpr, kVecs, kWaves, kRounds, kEpl, kKc, kBufs>(
+        p, q, xcd_work_index(q.tiles, q.panels));
+}
+
+template <class S> struct PanelKernel;
+template <> struct PanelKernel<PanelMany> {
+    static constexpr auto fn = &spmm_panel_kernel<PanelMany, 16, 2, 8, 2, 4, 128, 2>;
+};
+template <> struct PanelKernel<PanelFew> {
+    static constexpr auto fn = &spmm_panel_kernel<PanelFew, 16, 2, 8, 1, 8, 224, 1>;
+};
+
+template <class S>
+hipError_t launch_panel_t(const SpmmParams &p, const PanelParams &q, hipStream_t s)
+{
+    const size_t lds = S::lds_bytes(q.chunks);
+    const auto fn = PanelKernel<S>::fn;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3((unsigned)xcd_grid(q.tiles, q.panels)), dim3(S::kThreads), lds, s,
+                       p, q);
+    return hipGetLastError();
+}
+
+// The panel shape for an m x k by k x n problem with nnz entries on a GPU of
+// `cus` compute units and `lds_max` bytes of LDS per workgroup: the first of
+// kPanelMany, kPanelFew whose launch gives every CU a workgroup and whose
+// panels touch each staged B row at least kPanelMinReuse times on average
+// (rows per panel x density); 0 when neither does.
+template <class S>
+bool panel_fits(const SpmmArgs &a, int cus, int lds_max, PanelParams *q)
+{
+    const int chunks = (a.k + S::kKcRows - 1) / S::kKcRows;
+    const long long panels = ((long long)a.m + S::kRows - 1) / S::kRows;
+    const long long tiles = ((long long)a.n + S::kT - 1) / S::kT;
+    if (a.n < S::kT || tiles * panels < cus || (long long)lds_max < (long long)S::lds_bytes(chunks))
+        return false;
+    if ((double)std::min(a.m, S::kRows) * a.nnz < kPanelMinReuse * (double)a.m * (double)a.k)
+        return false;
+    if (tiles * panels > 0x7fffffffLL) return false;
+    q->k = a.k;
+    q->chunks = chunks;
+    q->panels = (int)panels;
+    q->tiles = (int)tiles;
+    return true;
 }
 
 // Wide B with balanced waves (64 lanes per row, one column tile of 64 kVec
@@ -733,6 +802,19 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
             (long long)a.batch * tiles * row_blocks < 2LL * kSimdsPerCu * cus)
             plan->kind = SpmmPlan::kSplit;
     }
+    // B shared in LDS by a panel of rows: fp32 vector paths, one batch entry.
+    if (f32 && vec && vec_csr && a.batch == 1 && a.k > 0 && a.m > 0) {
+        int cus = 0, lds_max = 0;
+        if (device_limits(&cus, &lds_max)) {
+            if (panel_fits<PanelMany>(a, cus, lds_max, &plan->q)) {
+                plan->kind = SpmmPlan::kPanel;
+                plan->panel = 0;
+            } else if (panel_fits<PanelFew>(a, cus, lds_max, &plan->q)) {
+                plan->kind = SpmmPlan::kPanel;
+                plan->panel = 1;
+            }
+        }
+    }
     if (narrow) plan->kind = SpmmPlan::kNarrow;
     if (lds_ok) {
         // B in LDS when it fits and every CU has at least as many entries to
@@ -771,6 +853,9 @@ hipError_t run_spmm(const SpmmPlan &plan, hipStream_t stream)
 {
     const SpmmParams &p = plan.p;
     switch (plan.kind) {
+    case SpmmPlan::kPanel:
+        return plan.panel == 0 ? launch_panel_t<PanelMany>(p, plan.q, stream)
+                               : launch_panel_t<PanelFew>(p, plan.q, stream);
     case SpmmPlan::kLds:
         switch (plan.dtype) {
         case Dtype::f16:
@@ -823,6 +908,21 @@ hipError_t run_spmm(const SpmmPlan &plan, hipStream_t stream)
     default:
         return launch_wide<float, 4>(plan.vec, plan.lpr, p, plan.vec_csr, plan.buf, stream);
     }
+}
+
+const char *spmm_kernel_name(const SpmmArgs &a)
+{
+    SpmmPlan plan;
+    if (plan_spmm(a, &plan) != hipSuccess) return "unsupported";
+    switch (plan.kind) {
+    case SpmmPlan::kWide: return "wide";
+    case SpmmPlan::kNarrow: return "narrow";
+    case SpmmPlan::kLds: return "lds";
+    case SpmmPlan::kBalanced: return "balanced";
+    case SpmmPlan::kSplit: return "split";
+    case SpmmPlan::kPanel: return "panel";
+    }
+    return "unknown";
 }
 
 hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream)
