@@ -4,16 +4,25 @@
 A step is one pass of the whole hot path over the Transformer-FFN workload
 (A 2048x512 at 90 % sparsity, row lengths N(51.2, 5.12); B 512x256; companion
 SDDMM with dY 2048x256 and X 512x256): CSR row offsets and the row swizzle
-from the row lengths (one launch), SpMM C = A B and SDDMM dA = (dY X^T) at
-A's entries -- three kernels, captured in a HIP graph and replayed.  Inputs are resident in
-HBM before timing starts.
+from the row lengths (one launch), then SpMM C = A B and SDDMM dA = (dY X^T)
+at A's entries in one launch, captured in a HIP graph and replayed.  Inputs
+are resident in HBM before timing starts.
 
 Prints one JSON line:
   value        useful GFLOP/s of the step, (2 nnz n + 2 nnz d) / step time
-  roofline     the SpMM kernel: algorithmic (compulsory) bytes per launch over
-               its average launch duration, against 8 TB/s HBM peak
+  roofline     the step's dominant launch (SpMM + SDDMM): algorithmic
+               (compulsory) bytes per launch over its average launch duration,
+               against 8 TB/s HBM peak
   cpu_baseline the C oracle timed on this host's cores on the same inputs
   kernels      per-kernel average durations, GFLOP/s and GB/s
+  records      every seeded workload (tiny, Transformer FFN, ResNet-50 1x1,
+               LSTM sweep, sparse attention x 32 heads, lognormal imbalance,
+               row swizzle at 65,536 and 1.1 M rows): warm and cold (after a
+               1 GiB write) times, GFLOP/s, compulsory GB/s and the fraction of
+               min(FP32 peak, arithmetic intensity x HBM peak), the smaller
+               term named
+  breakeven    LSTM-sized SpMM against dense fp32 GEMM
+  streaming    a 430 MB-CSR SpMM where HBM bandwidth binds
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -76,6 +85,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent timing the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload records (tiny, FFN, ResNet, attention, "
+                         "imbalance, swizzle, latency)")
     ap.add_argument("--no-breakeven", action="store_true",
                     help="skip the LSTM-sized sparsity sweep against dense GEMM")
     ap.add_argument("--suite", metavar="JSONL", default=None,
@@ -91,6 +103,12 @@ def parse_args():
     ap.add_argument("--profile-launches", type=int, default=0,
                     help="only run this many eager launches of each kernel "
                          "(for rocprofv3 counter passes) and exit")
+    ap.add_argument("--profile-workloads", default="ffn",
+                    help="with --profile-launches: comma-separated workloads to launch -- "
+                         "ffn (the step's kernels), resnet, lstm90, lstm50, attention")
+    ap.add_argument("--profile-cold", action="store_true",
+                    help="with --profile-launches: write a 1 GiB buffer before every "
+                         "launch, so the byte counters see HBM traffic")
     return ap.parse_args()
 
 
@@ -207,6 +225,197 @@ def spmm_record(name, m, k, n, nnz, us, extra=None) -> dict:
     return rec
 
 
+def roofline_of(flops: float, byts: float, us: float) -> dict:
+    """Achieved rate of one kernel run against the published roofline: the
+    attainable rate is min(FP32 vector peak, arithmetic intensity x HBM peak)
+    over the run's compulsory bytes; `bound` names the smaller term.  The
+    build's unpacked-FMA ceiling (78.6 TFLOP/s) is given beside it."""
+    s = us * 1e-6
+    gflops = flops / s / 1e9
+    gbs = byts / s / 1e9
+    if flops == 0:  # pure data movement (the row softmax): the HBM roof alone
+        return {"gflops": 0.0, "compulsory_gbs": gbs, "ai_flop_per_byte": 0.0,
+                "attainable_gflops": None, "bound": "hbm", "frac": gbs / HBM_PEAK_GBS,
+                "frac_hbm_peak": gbs / HBM_PEAK_GBS, "frac_fp32_unpacked": 0.0}
+    ai = flops / byts
+    hbm_term = ai * HBM_PEAK_GBS                     # GFLOP/s
+    fp32_term = FP32_VECTOR_PEAK_TFLOPS * 1e3
+    attainable = min(hbm_term, fp32_term)
+    return {"gflops": gflops, "compulsory_gbs": gbs,
+            "ai_flop_per_byte": ai, "attainable_gflops": attainable,
+            "bound": "hbm" if hbm_term < fp32_term else "fp32",
+            "frac": gflops / attainable,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+            "frac_fp32_unpacked": gflops / (FP32_FMA_PEAK_TFLOPS * 1e3)}
+
+
+def kernel_record(torch, config, kind, workload, fn, flops, byts, flush, reps, extra=None):
+    """Warm (graph of back-to-back launches) and cold (single launches after a
+    1 GiB write) timings of one kernel run, with its roofline figures."""
+    us = graph_time_us(torch, fn, reps)
+    rec = {"config": config, "kernel": kind, "workload": workload, "us": us,
+           "cold_us": cold_time_us(torch, fn, flush) if flush is not None else None,
+           "flops": flops, "compulsory_bytes": byts}
+    rec.update(roofline_of(flops, byts, us))
+    if extra:
+        rec.update(extra)
+    log(f"[{config}] {kind} {workload}: {us:.2f} us warm, "
+        f"{rec['cold_us'] or 0:.2f} us cold, {rec['gflops']:.0f} GFLOP/s, "
+        f"{100 * rec['frac']:.1f} % of the {rec['bound']} roof")
+    return rec
+
+
+def config_records(torch, sp, inputs, dev, flush) -> list:
+    """One record per kernel run of each seeded workload: tiny SpMM and SDDMM;
+    Transformer-FFN SpMM and SDDMM alone; ResNet-50 1x1 SpMM; sparse attention
+    over 32 heads (scores, row softmax, weighted sum, and the one-pass form);
+    the lognormal-row imbalance SpMM and SDDMM swizzled, natural and balanced;
+    the row swizzle at 65,536 and 1.1 M rows (rank sort and radix sort); and
+    single-launch latencies.  The LSTM sweep is recorded by lstm_breakeven."""
+    recs = []
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    def kname(m, k, n, nnz, vals, cols, b, c):
+        return sp.sp_spmm_kernel_name(m, k, n, nnz, vals, cols, b, c)
+
+    # ---- tiny (256 x 256, p = 0.2): SpMM n = 64, SDDMM d = 32
+    wt = inputs.tiny()
+    at = sp.csr_from_dense(up(wt["mask"]), up(wt["dense_values"]))
+    sp.row_swizzle(at)
+    bt, xt, yt = up(wt["b"]), up(wt["x"]), up(wt["y"])
+    ct = torch.empty(wt["m"], wt["n"], device=dev)
+    ot = torch.empty(at.nnz, device=dev)
+    fns = {
+        "spmm": lambda: sp.sp_spmm(at.m, at.k, wt["n"], at.nnz, at.row_indices, at.values,
+                                   at.row_offsets, at.col_indices, bt, ct),
+        "sddmm": lambda: sp.sp_sddmm(at.m, at.k, wt["d"], at.nnz, at.row_indices,
+                                     at.row_offsets, at.col_indices, xt, yt, ot)}
+    recs.append(kernel_record(torch, "tiny", "spmm", wt["name"], fns["spmm"],
+                              2.0 * at.nnz * wt["n"], spmm_bytes(at.m, at.k, wt["n"], at.nnz),
+                              flush, 200, {"m": at.m, "k": at.k, "n": wt["n"], "nnz": at.nnz,
+                                           "single_launch_us": latency_us(torch, fns["spmm"]),
+                                           "variant": kname(at.m, at.k, wt["n"], at.nnz,
+                                                            at.values, at.col_indices, bt, ct)}))
+    recs.append(kernel_record(torch, "tiny", "sddmm", wt["name"], fns["sddmm"],
+                              2.0 * at.nnz * wt["d"], sddmm_bytes(at.m, at.k, wt["d"], at.nnz),
+                              flush, 200, {"m": at.m, "k": at.k, "d": wt["d"], "nnz": at.nnz,
+                                           "single_launch_us": latency_us(torch, fns["sddmm"])}))
+
+    # ---- Transformer FFN (2048 x 512 at 90 %): the SpMM and the SDDMM alone,
+    # and the imbalance workload (lognormal rows): swizzled, natural, balanced
+    for w, cfg in ((inputs.transformer_ffn(), "transformer_ffn"),
+                   (inputs.imbalance(), "imbalance")):
+        a = w["a"]
+        m, k, n, d, nnz = w["m"], w["k"], w["n"], w["d"], a.nnz
+        ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+        b, x, y = up(w["b"]), up(w["x"]), up(w["y"])
+        c = torch.empty(m, n, device=dev)
+        out = torch.empty(nnz, device=dev)
+        orders = ((True, False) if cfg == "imbalance" else (True,))
+        for swz in orders:
+            order = ri if swz else None
+            tag = {"swizzle": swz, "m": m, "k": k, "n": n, "d": d, "nnz": nnz}
+            fn = lambda: sp.sp_spmm(m, k, n, nnz, order, vals, ro, cols, b, c)
+            ex = dict(tag, variant=kname(m, k, n, nnz, vals, cols, b, c))
+            if cfg != "imbalance":
+                ex["single_launch_us"] = latency_us(torch, fn)
+            recs.append(kernel_record(torch, cfg, "spmm", w["name"], fn, 2.0 * nnz * n,
+                                      spmm_bytes(m, k, n, nnz), flush, 200, ex))
+            sfn = lambda: sp.sp_sddmm(m, k, d, nnz, order, ro, cols, x, y, out)
+            ex = dict(tag)
+            if cfg != "imbalance":
+                ex["single_launch_us"] = latency_us(torch, sfn)
+            recs.append(kernel_record(torch, cfg, "sddmm", w["name"], sfn, 2.0 * nnz * d,
+                                      sddmm_bytes(m, k, d, nnz), flush, 200, ex))
+            if cfg == "imbalance":
+                bfn = lambda: sp.sp_spmm_balanced(m, k, n, nnz, order, vals, ro, cols, b, c)
+                recs.append(kernel_record(torch, cfg, "spmm_balanced", w["name"], bfn,
+                                          2.0 * nnz * n, spmm_bytes(m, k, n, nnz), flush, 200,
+                                          tag))
+                bsfn = lambda: sp.sp_sddmm_balanced(m, k, d, nnz, order, ro, cols, x, y, out)
+                recs.append(kernel_record(torch, cfg, "sddmm_balanced", w["name"], bsfn,
+                                          2.0 * nnz * d, sddmm_bytes(m, k, d, nnz), flush, 200,
+                                          tag))
+
+    # ---- ResNet-50 1x1 conv (1024 x 256 at 70 %, N = 6272)
+    w = inputs.resnet_1x1()
+    a = w["a"]
+    m, k, n, nnz = w["m"], w["k"], w["n"], a.nnz
+    ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+    b = up(w["b"])
+    c = torch.empty(m, n, device=dev)
+    fn = lambda: sp.sp_spmm(m, k, n, nnz, ri, vals, ro, cols, b, c)
+    recs.append(kernel_record(torch, "resnet50_1x1", "spmm", w["name"], fn, 2.0 * nnz * n,
+                              spmm_bytes(m, k, n, nnz), flush, 50,
+                              {"m": m, "k": k, "n": n, "nnz": nnz,
+                               "variant": kname(m, k, n, nnz, vals, cols, b, c)}))
+    del b, c
+
+    # ---- sparse attention: 32 (batch, head) pairs over one 4096 x 4096 mask
+    w = inputs.sparse_attention()
+    bh, seq, hd = w["batch"], w["seq"], w["head_dim"]
+    mk = up(w["mask"])
+    ro = torch.empty(seq + 1, dtype=torch.int32, device=dev)
+    sp.sp_csr_count_dense(seq, seq, mk, ro)
+    nnz = int(ro[seq].item())
+    cols = torch.empty(nnz, dtype=torch.int32, device=dev)
+    sp.sp_csr_fill_dense(seq, seq, mk, None, ro, cols, None)
+    ri = torch.empty(seq, dtype=torch.int32, device=dev)
+    sp.sp_row_swizzle(seq, ro, ri)
+    q, kk, v = up(w["q"]), up(w["k"]), up(w["v"])
+    s_out = torch.empty(bh, nnz, device=dev)
+    p_vals = torch.full((bh, nnz), 1.0 / 80.0, device=dev)
+    o = torch.empty(bh, seq, hd, device=dev)
+    tag = {"batch": bh, "seq": seq, "head_dim": hd, "nnz_per_head": nnz}
+    sfn = lambda: sp.sp_sddmm_batched(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125, s_out,
+                                      bh, seq * hd, seq * hd, nnz)
+    smfn = lambda: sp.sp_csr_row_softmax(seq, nnz, ri, ro, s_out, s_out, bh, nnz, nnz)
+    pfn = lambda: sp.sp_spmm_batched(seq, seq, hd, nnz, ri, p_vals, ro, cols, v, o, bh, nnz,
+                                     seq * hd, seq * hd)
+    afn = lambda: sp.sp_sparse_attention(seq, seq, hd, nnz, ri, ro, cols, q, kk, v, 0.125, o,
+                                         bh, seq * hd, seq * hd, seq * hd, seq * hd)
+    sb, pb = sddmm_bytes(seq, seq, hd, nnz), spmm_bytes(seq, seq, hd, nnz)
+    recs.append(kernel_record(torch, "sparse_attention", "sddmm_x32", w["name"], sfn,
+                              2.0 * bh * nnz * hd, bh * sb, flush, 20, tag))
+    # the softmax moves 8 bytes per entry (read, write) and does no FMA work
+    recs.append(kernel_record(torch, "sparse_attention", "row_softmax_x32", w["name"], smfn,
+                              0.0, bh * 8.0 * nnz + 8 * seq, flush, 20, tag))
+    recs.append(kernel_record(torch, "sparse_attention", "spmm_x32", w["name"], pfn,
+                              2.0 * bh * nnz * hd, bh * pb, flush, 20, tag))
+    recs.append(kernel_record(torch, "sparse_attention", "attention_one_pass_x32", w["name"], afn,
+                              4.0 * bh * nnz * hd, bh * (4 * seq * hd * 3 + 4 * seq * hd
+                                                         + 4 * nnz + 8 * seq), flush, 20, tag))
+    del q, kk, v, s_out, p_vals, o
+
+    # ---- the row swizzle of many rows: the rank sort (no workspace) against
+    # the radix sort (workspace form), at 65,536 and 1,100,000 rows
+    for m, seed in ((65536, 31), (1100000, 32)):
+        k = 8192
+        lengths = np.random.default_rng(seed).integers(0, 1639, m).astype(np.int32)
+        ro = torch.empty(m + 1, dtype=torch.int32, device=dev)
+        sp.sp_csr_offsets_from_lengths(m, up(lengths), ro)
+        ri = torch.empty(m, dtype=torch.int32, device=dev)
+        ws = torch.empty(sp.sp_row_swizzle_workspace(m), dtype=torch.uint8, device=dev)
+        radix = lambda: sp.sp_row_swizzle_ws(m, k, ro, ri, ws)
+        rank = lambda: sp.sp_row_swizzle(m, ro, ri)
+        rec = {"config": "row_swizzle", "kernel": "row_swizzle", "m": m, "k": k,
+               "radix_us": graph_time_us(torch, radix, 20),
+               "rank_us": graph_time_us(torch, rank, 3 if m > 100000 else 10)}
+        log(f"[row_swizzle] m={m}: radix {rec['radix_us']:.1f} us, rank {rec['rank_us']:.1f} us")
+        recs.append(rec)
+
+    # ---- single-launch latency at 98 % sparsity (LSTM layer)
+    wl = inputs.lstm(0.98)
+    rol, ril, coll, vall = upload_csr(torch, sp, dev, wl["a"])
+    bl = up(wl["b"])
+    cl = torch.empty(wl["m"], wl["n"], device=dev)
+    nl = wl["a"].nnz
+    fn = lambda: sp.sp_spmm(wl["m"], wl["k"], wl["n"], nl, ril, vall, rol, coll, bl, cl)
+    recs.append({"config": "lstm", "kernel": "spmm_latency", "workload": wl["name"],
+                 "single_launch_us": latency_us(torch, fn), "graph_us": graph_time_us(torch, fn, 200)})
+    return recs
+
+
 def upload_csr(torch, sp, dev, rl):
     """Device CSR of row lists: lengths, columns and values uploaded, offsets
     and the swizzled row order computed on the device."""
@@ -235,18 +444,24 @@ def lstm_breakeven(torch, sp, inputs, dev, reps=50, records=None, flush=None):
         b = torch.from_numpy(w["b"]).to(dev)
         c = torch.empty(m, n, device=dev)
         fn = lambda: sp.sp_spmm(m, k, n, a.nnz, ri, vals, ro, cols, b, c)
-        times[s] = graph_time_us(torch, fn, reps)
         if records is not None:
-            cold = cold_time_us(torch, fn, flush) if flush is not None else None
-            records.append(spmm_record(w["name"], m, k, n, a.nnz, times[s],
-                                       {"sparsity": s, "cold_us": cold}))
+            rec = kernel_record(torch, "lstm", "spmm", w["name"], fn, 2.0 * a.nnz * n,
+                                spmm_bytes(m, k, n, a.nnz), flush, reps,
+                                {"sparsity": s, "m": m, "k": k, "n": n, "nnz": a.nnz,
+                                 "variant": sp.sp_spmm_kernel_name(m, k, n, a.nnz, vals, cols,
+                                                                   b, c)})
+            records.append(rec)
+            times[s] = rec["us"]
+        else:
+            times[s] = graph_time_us(torch, fn, reps)
         if dense_us is None:
             # The dense operand of the comparison: A with every entry present.
             dense_a = torch.from_numpy(inputs.random_dense(5, m, k, std=0.02)).to(dev)
             dfn = lambda: torch.mm(dense_a, b, out=c)
             dense_us = graph_time_us(torch, dfn, reps)
             if records is not None:
-                records.append({"record": "dense_gemm", "workload": "lstm_8192x2048x128_dense",
+                records.append({"config": "lstm", "kernel": "dense_gemm",
+                                "workload": "lstm_8192x2048x128_dense",
                                 "m": m, "k": k, "n": n, "us": dense_us,
                                 "gflops": 2.0 * m * k * n / (dense_us * 1e-6) / 1e9,
                                 "precision": "fp32 (TF32 off, matmul precision 'highest')"})
@@ -263,6 +478,49 @@ def lstm_breakeven(torch, sp, inputs, dev, reps=50, records=None, flush=None):
             "breakeven_sparsity": breakeven,
             "note": ("sparsity where SpMM time equals dense fp32 GEMM time, "
                      "linearly interpolated; null if the sweep has no crossing")}
+
+
+def profile_workload_fns(torch, sp, inputs, dev, wanted):
+    """Launch functions of the named workloads, for rocprofv3 passes: resnet
+    (the ResNet-50 1x1 SpMM), lstm90 / lstm50 (the LSTM-sized SpMM at 90 % and
+    50 %), attention (the four sparse-attention kernels over 32 heads)."""
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    fns = []
+    for name, w in (("resnet", inputs.resnet_1x1), ("lstm90", lambda: inputs.lstm(0.9)),
+                    ("lstm50", lambda: inputs.lstm(0.5))):
+        if name not in wanted:
+            continue
+        w = w()
+        a = w["a"]
+        ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+        b = up(w["b"])
+        c = torch.empty(w["m"], w["n"], device=dev)
+        fns.append(lambda m=w["m"], k=w["k"], n=w["n"], nnz=a.nnz, ri=ri, vals=vals, ro=ro,
+                   cols=cols, b=b, c=c: sp.sp_spmm(m, k, n, nnz, ri, vals, ro, cols, b, c))
+    if "attention" in wanted:
+        w = inputs.sparse_attention()
+        bh, seq, hd = w["batch"], w["seq"], w["head_dim"]
+        mk = up(w["mask"])
+        ro = torch.empty(seq + 1, dtype=torch.int32, device=dev)
+        sp.sp_csr_count_dense(seq, seq, mk, ro)
+        nnz = int(ro[seq].item())
+        cols = torch.empty(nnz, dtype=torch.int32, device=dev)
+        sp.sp_csr_fill_dense(seq, seq, mk, None, ro, cols, None)
+        ri = torch.empty(seq, dtype=torch.int32, device=dev)
+        sp.sp_row_swizzle(seq, ro, ri)
+        q, kk, v = up(w["q"]), up(w["k"]), up(w["v"])
+        s_out = torch.empty(bh, nnz, device=dev)
+        p_vals = torch.full((bh, nnz), 1.0 / 80.0, device=dev)
+        o = torch.empty(bh, seq, hd, device=dev)
+        fns += [lambda: sp.sp_sddmm_batched(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125,
+                                            s_out, bh, seq * hd, seq * hd, nnz),
+                lambda: sp.sp_csr_row_softmax(seq, nnz, ri, ro, s_out, s_out, bh, nnz, nnz),
+                lambda: sp.sp_spmm_batched(seq, seq, hd, nnz, ri, p_vals, ro, cols, v, o, bh,
+                                           nnz, seq * hd, seq * hd),
+                lambda: sp.sp_sparse_attention(seq, seq, hd, nnz, ri, ro, cols, q, kk, v,
+                                               0.125, o, bh, seq * hd, seq * hd, seq * hd,
+                                               seq * hd)]
+    return fns
 
 
 def stream_setup(torch, sp, inputs, dev, dtype=None):
@@ -401,66 +659,36 @@ def lowp_records(torch, sp, inputs, dev, flush) -> list:
 
 
 def run_suite(torch, sp, inputs, dev, path: str) -> None:
-    """Every workload, warm (graph back-to-back) and cold (after flushing the
-    caches), one JSON record per kernel run."""
+    """Beyond the default records: the general SDDMM (mask values, accumulation,
+    Y stored k x d / d x k, with and without a workspace), the backward pass
+    (transpose, values, A^T dY), 16-bit operands, the sparse-attention
+    compositions (scores with K given d x k, scores + softmax in one pass, the
+    all-device pipelines) and the streaming SpMM at n = 8 and 4.  Warm (graph
+    back-to-back) and cold (after flushing the caches), one JSON record per
+    kernel run."""
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB > caches
     flush.zero_()
     recs = []
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
-    # Transformer FFN SpMM + SDDMM, and the lognormal imbalance variant with
-    # and without the swizzled row order.
-    for w in (inputs.transformer_ffn(), inputs.imbalance()):
-        a = w["a"]
-        m, k, n, d = w["m"], w["k"], w["n"], w["d"]
-        ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
-        b, x, y = up(w["b"]), up(w["x"]), up(w["y"])
-        c = torch.empty(m, n, device=dev)
-        out = torch.empty(a.nnz, device=dev)
-        for swz in (True, False):
-            order = ri if swz else None
-            fn = lambda: sp.sp_spmm(m, k, n, a.nnz, order, vals, ro, cols, b, c)
-            recs.append(spmm_record(w["name"], m, k, n, a.nnz, graph_time_us(torch, fn, 200),
-                                    {"swizzle": swz, "cold_us": cold_time_us(torch, fn, flush)}))
-            bfn = lambda: sp.sp_spmm_balanced(m, k, n, a.nnz, order, vals, ro, cols, b, c)
-            recs.append(spmm_record(w["name"], m, k, n, a.nnz, graph_time_us(torch, bfn, 200),
-                                    {"swizzle": swz, "kernel": "balanced",
-                                     "cold_us": cold_time_us(torch, bfn, flush)}))
-            sfn = lambda: sp.sp_sddmm(m, k, d, a.nnz, order, ro, cols, x, y, out)
-            us = graph_time_us(torch, sfn, 200)
-            recs.append({"record": "sddmm", "workload": w["name"], "m": m, "k": k, "d": d,
-                         "nnz": a.nnz, "swizzle": swz, "us": us,
-                         "cold_us": cold_time_us(torch, sfn, flush),
-                         "gflops": 2.0 * a.nnz * d / (us * 1e-6) / 1e9,
-                         "compulsory_gbs": sddmm_bytes(m, k, d, a.nnz) / (us * 1e-6) / 1e9})
-            bsfn = lambda: sp.sp_sddmm_balanced(m, k, d, a.nnz, order, ro, cols, x, y, out)
-            us = graph_time_us(torch, bsfn, 200)
-            recs.append({"record": "sddmm", "workload": w["name"], "m": m, "k": k, "d": d,
-                         "nnz": a.nnz, "swizzle": swz, "kernel": "balanced", "us": us,
-                         "cold_us": cold_time_us(torch, bsfn, flush),
-                         "gflops": 2.0 * a.nnz * d / (us * 1e-6) / 1e9,
-                         "compulsory_gbs": sddmm_bytes(m, k, d, a.nnz) / (us * 1e-6) / 1e9})
-        recs.append({"record": "row_swizzle", "workload": w["name"], "m": m,
-                     "us": graph_time_us(torch, lambda: sp.sp_row_swizzle(m, ro, ri), 200)})
-        if w["name"] != inputs.transformer_ffn()["name"]:
-            continue
-        # General SDDMM on the same shapes: the mask's values as the element-wise
-        # scale and accumulation into the previous output, with Y stored k x d
-        # and d x k.
-        # (d x k once more with a workspace: Y transposed there first).
-        y_dk = y.t().contiguous()
-        ws = torch.empty(sp.sp_sddmm_general_workspace(k, d), dtype=torch.uint8, device=dev)
-        for layout, yy, wsp, name in ((sp.SP_Y_KD, y, None, "kd"), (sp.SP_Y_DK, y_dk, None, "dk"),
-                                      (sp.SP_Y_DK, y_dk, ws, "dk_workspace")):
-            gfn = lambda: sp.sp_sddmm_general(m, k, d, a.nnz, ri, ro, cols, vals, x, yy,
-                                              layout, 0.5, 1.0, out, workspace=wsp)
-            us = graph_time_us(torch, gfn, 200)
-            recs.append({"record": "sddmm_general", "workload": w["name"], "m": m, "k": k,
-                         "d": d, "nnz": a.nnz, "y_layout": name, "mask_values": True,
-                         "beta": 1.0, "us": us,
-                         "cold_us": cold_time_us(torch, gfn, flush),
-                         "gflops": 2.0 * a.nnz * d / (us * 1e-6) / 1e9,
-                         "compulsory_gbs": (sddmm_bytes(m, k, d, a.nnz) + 8 * a.nnz)
-                         / (us * 1e-6) / 1e9})
+    # General SDDMM on the Transformer-FFN shapes: the mask's values as the
+    # element-wise scale and accumulation into the previous output, with Y
+    # stored k x d and d x k (d x k once more with a workspace: Y transposed
+    # there first).
+    w = inputs.transformer_ffn()
+    a = w["a"]
+    m, k, d = w["m"], w["k"], w["d"]
+    ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+    x, y = up(w["x"]), up(w["y"])
+    out = torch.empty(a.nnz, device=dev)
+    y_dk = y.t().contiguous()
+    ws = torch.empty(sp.sp_sddmm_general_workspace(k, d), dtype=torch.uint8, device=dev)
+    for layout, yy, wsp, name in ((sp.SP_Y_KD, y, None, "kd"), (sp.SP_Y_DK, y_dk, None, "dk"),
+                                  (sp.SP_Y_DK, y_dk, ws, "dk_workspace")):
+        gfn = lambda: sp.sp_sddmm_general(m, k, d, a.nnz, ri, ro, cols, vals, x, yy,
+                                          layout, 0.5, 1.0, out, workspace=wsp)
+        recs.append(kernel_record(torch, "transformer_ffn", "sddmm_general_" + name, w["name"],
+                                  gfn, 2.0 * a.nnz * d, sddmm_bytes(m, k, d, a.nnz) + 8 * a.nnz,
+                                  flush, 200, {"mask_values": True, "beta": 1.0}))
     # Backward pass of a sparse layer: A^T in CSR (once per structure; the
     # values of a new A follow through the permutation), then dX = A^T dY on
     # the swizzled rows of A^T.
@@ -468,21 +696,7 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
         recs.extend(backward_records(torch, sp, inputs, dev, w, flush))
     # Mixed precision: values and B (X and Y) in 16-bit, fp32 arithmetic.
     recs.extend(lowp_records(torch, sp, inputs, dev, flush))
-    # ResNet-50 1x1 conv
-    w = inputs.resnet_1x1()
-    a = w["a"]
-    ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
-    b = up(w["b"])
-    c = torch.empty(w["m"], w["n"], device=dev)
-    fn = lambda: sp.sp_spmm(w["m"], w["k"], w["n"], a.nnz, ri, vals, ro, cols, b, c)
-    recs.append(spmm_record(w["name"], w["m"], w["k"], w["n"], a.nnz, graph_time_us(torch, fn, 50),
-                            {"cold_us": cold_time_us(torch, fn, flush)}))
-    # LSTM sweep with the dense comparison
-    be = lstm_breakeven(torch, sp, inputs, dev, records=recs, flush=flush)
-    recs.append({"record": "breakeven", **be})
-    # Sparse attention over one shared mask: batched SDDMM (scores, scale
-    # 1/8), the row softmax in place, batched SpMM (P V), each alone and the
-    # three as one graph; and the scores with K given d x k.
+    # Sparse attention compositions over one shared mask.
     w = inputs.sparse_attention()
     bh, seq, hd = w["batch"], w["seq"], w["head_dim"]
     mk = up(w["mask"])
@@ -495,12 +709,7 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
     sp.sp_row_swizzle(seq, ro, ri)
     q, kk, v = up(w["q"]), up(w["k"]), up(w["v"])
     s_out = torch.empty(bh, nnz, device=dev)
-    p_vals = torch.full((bh, nnz), 1.0 / 80.0, device=dev)
     o = torch.empty(bh, seq, hd, device=dev)
-    sfn = lambda: sp.sp_sddmm_batched(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125, s_out,
-                                      bh, seq * hd, seq * hd, nnz)
-    pfn = lambda: sp.sp_spmm_batched(seq, seq, hd, nnz, ri, p_vals, ro, cols, v, o, bh,
-                                     nnz, seq * hd, seq * hd)
     kt = kk.transpose(1, 2).contiguous()
     tfn = lambda: sp.sp_sddmm_general(seq, seq, hd, nnz, ri, ro, cols, None, q, kt,
                                       sp.SP_Y_DK, 0.125, 0.0, s_out, bh, 0, seq * hd,
@@ -510,85 +719,38 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
     twfn = lambda: sp.sp_sddmm_general(seq, seq, hd, nnz, ri, ro, cols, None, q, kt,
                                        sp.SP_Y_DK, 0.125, 0.0, s_out, bh, 0, seq * hd,
                                        seq * hd, nnz, workspace=kt_ws)
+    sfn = lambda: sp.sp_sddmm_batched(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125, s_out,
+                                      bh, seq * hd, seq * hd, nnz)
     smfn = lambda: sp.sp_csr_row_softmax(seq, nnz, ri, ro, s_out, s_out, bh, nnz, nnz)
+    fsfn = lambda: sp.sp_sddmm_softmax(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125, s_out,
+                                       bh, seq * hd, seq * hd, nnz)
+    pv = lambda: sp.sp_spmm_batched(seq, seq, hd, nnz, ri, s_out, ro, cols, v, o, bh, nnz,
+                                    seq * hd, seq * hd)
 
     def attention():
         sfn()
         smfn()
-        sp.sp_spmm_batched(seq, seq, hd, nnz, ri, s_out, ro, cols, v, o, bh, nnz, seq * hd,
-                           seq * hd)
-
-    fsfn = lambda: sp.sp_sddmm_softmax(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125, s_out,
-                                       bh, seq * hd, seq * hd, nnz)
+        pv()
 
     def attention_fused():
         fsfn()
-        sp.sp_spmm_batched(seq, seq, hd, nnz, ri, s_out, ro, cols, v, o, bh, nnz, seq * hd,
-                           seq * hd)
+        pv()
 
-    vfn = lambda: sp.sp_sparse_attention(seq, seq, hd, nnz, ri, ro, cols, q, kk, v, 0.125, o,
-                                         bh, seq * hd, seq * hd, seq * hd, seq * hd)
-    for kind, fn in (("sddmm_batched", sfn), ("sddmm_general_dk_batched", tfn),
-                     ("sddmm_general_dk_workspace_batched", twfn),
-                     ("row_softmax_batched", smfn), ("sddmm_softmax_batched", fsfn),
-                     ("spmm_batched", pfn), ("attention_all_device", attention),
-                     ("attention_all_device_fused_scores", attention_fused),
-                     ("attention_one_pass", vfn)):
-        us = graph_time_us(torch, fn, 20)
-        flops = 2.0 * bh * nnz * hd
-        if kind == "row_softmax_batched":
-            flops = 0.0
-            byts = bh * 8 * nnz + 8 * seq
-        elif kind.startswith("attention_"):
-            flops = 4.0 * bh * nnz * hd
-            byts = bh * (sddmm_bytes(seq, seq, hd, nnz) + 8 * nnz
-                         + spmm_bytes(seq, seq, hd, nnz))
-        else:
-            byts = bh * (sddmm_bytes(seq, seq, hd, nnz) if kind.startswith("sddmm")
-                         else spmm_bytes(seq, seq, hd, nnz))
-        recs.append({"record": kind, "workload": w["name"], "batch": bh, "seq": seq,
-                     "head_dim": hd, "nnz_per_head": nnz, "us": us,
-                     "cold_us": cold_time_us(torch, fn, flush),
-                     "gflops": flops / (us * 1e-6) / 1e9,
-                     "compulsory_gbs": byts / (us * 1e-6) / 1e9})
-    # Single-launch latency where launch overhead exceeds the roofline time:
-    # the tiny problem (256x256 at 80 %), the Transformer FFN and the LSTM
-    # layer at 98 %, one eager call at a time beside the graph-batched average.
-    lat = []
-    wt = inputs.tiny()
-    at = sp.csr_from_dense(up(wt["mask"]), up(wt["dense_values"]))
-    sp.row_swizzle(at)
-    bt, xt, yt = up(wt["b"]), up(wt["x"]), up(wt["y"])
-    ct = torch.empty(wt["m"], wt["n"], device=dev)
-    ot = torch.empty(at.nnz, device=dev)
-    lat.append((wt["name"], "spmm", at.nnz,
-                lambda: sp.sp_spmm(at.m, at.k, wt["n"], at.nnz, at.row_indices, at.values,
-                                   at.row_offsets, at.col_indices, bt, ct)))
-    lat.append((wt["name"], "sddmm", at.nnz,
-                lambda: sp.sp_sddmm(at.m, at.k, wt["d"], at.nnz, at.row_indices,
-                                    at.row_offsets, at.col_indices, xt, yt, ot)))
-    wf = inputs.transformer_ffn()
-    rof, rif, colf, valf = upload_csr(torch, sp, dev, wf["a"])
-    bf, xf, yf = up(wf["b"]), up(wf["x"]), up(wf["y"])
-    cf = torch.empty(wf["m"], wf["n"], device=dev)
-    of = torch.empty(wf["a"].nnz, device=dev)
-    nf = wf["a"].nnz
-    lat.append((wf["name"], "spmm", nf,
-                lambda: sp.sp_spmm(wf["m"], wf["k"], wf["n"], nf, rif, valf, rof, colf, bf, cf)))
-    lat.append((wf["name"], "sddmm", nf,
-                lambda: sp.sp_sddmm(wf["m"], wf["k"], wf["d"], nf, rif, rof, colf, xf, yf, of)))
-    wl = inputs.lstm(0.98)
-    rol, ril, coll, vall = upload_csr(torch, sp, dev, wl["a"])
-    bl = up(wl["b"])
-    cl = torch.empty(wl["m"], wl["n"], device=dev)
-    nl = wl["a"].nnz
-    lat.append((wl["name"], "spmm", nl,
-                lambda: sp.sp_spmm(wl["m"], wl["k"], wl["n"], nl, ril, vall, rol, coll, bl, cl)))
-    for name, kern, nnz, fn in lat:
-        recs.append({"record": "latency", "workload": name, "kernel": kern, "nnz": nnz,
-                     "single_us": latency_us(torch, fn), "graph_us": graph_time_us(torch, fn, 200)})
+    sb, pb = sddmm_bytes(seq, seq, hd, nnz), spmm_bytes(seq, seq, hd, nnz)
+    for kind, fn, flops, byts in (
+            ("sddmm_general_dk_x32", tfn, 2.0 * bh * nnz * hd, bh * sb),
+            ("sddmm_general_dk_workspace_x32", twfn, 2.0 * bh * nnz * hd, bh * sb),
+            ("sddmm_softmax_x32", fsfn, 2.0 * bh * nnz * hd, bh * sb),
+            ("attention_all_device_x32", attention, 4.0 * bh * nnz * hd,
+             bh * (sb + 8 * nnz + pb)),
+            ("attention_all_device_fused_scores_x32", attention_fused, 4.0 * bh * nnz * hd,
+             bh * (sb + pb))):
+        recs.append(kernel_record(torch, "sparse_attention", kind, w["name"], fn, flops, byts,
+                                  flush, 20, {"batch": bh, "seq": seq, "head_dim": hd,
+                                              "nnz_per_head": nnz}))
+    del q, kk, v, kt, s_out, o, kt_ws
     # The streaming regime: CSR far larger than every cache, n = 8 and n = 4
-    # (B in LDS), natural and swizzled row order.
+    # (B in LDS), natural and swizzled row order, fp32 and 16-bit.
     for n_cols in (8, 4):
         w = inputs.hbm_stream(n=n_cols)
         a = w["a"]
@@ -597,31 +759,22 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
         c = torch.empty(w["m"], w["n"], device=dev)
         for order in (None, ri):
             fn = lambda: sp.sp_spmm(w["m"], w["k"], w["n"], a.nnz, order, vals, ro, cols, b, c)
-            recs.append(spmm_record(w["name"], w["m"], w["k"], w["n"], a.nnz,
-                                    graph_time_us(torch, fn, 20),
-                                    {"cold_us": cold_time_us(torch, fn, flush),
-                                     "csr_bytes": 8 * a.nnz, "swizzle": order is not None}))
-        # 16-bit values and B: the CSR streams 6 bytes per entry
+            recs.append(kernel_record(torch, "hbm_stream", "spmm", w["name"], fn,
+                                      2.0 * a.nnz * w["n"],
+                                      spmm_bytes(w["m"], w["k"], w["n"], a.nnz), flush, 20,
+                                      {"swizzle": order is not None}))
         for tag, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
             v16, b16 = vals.to(tdt), b.to(tdt)
             fn = lambda: sp.sp_spmm_ex(w["m"], w["k"], w["n"], a.nnz, None, v16, ro, cols,
                                        b16, c)
-            us = graph_time_us(torch, fn, 20)
             byts = 6 * a.nnz + 4 * (w["m"] + 1) + 2 * w["k"] * w["n"] + 4 * w["m"] * w["n"]
-            recs.append({"record": "spmm_" + tag, "workload": w["name"], "m": w["m"],
-                         "k": w["k"], "n": w["n"], "nnz": a.nnz, "us": us,
-                         "cold_us": cold_time_us(torch, fn, flush),
-                         "gflops": 2.0 * a.nnz * w["n"] / (us * 1e-6) / 1e9,
-                         "compulsory_gbs": byts / (us * 1e-6) / 1e9,
-                         "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS})
+            recs.append(kernel_record(torch, "hbm_stream", "spmm_" + tag, w["name"], fn,
+                                      2.0 * a.nnz * w["n"], byts, flush, 20))
             del v16, b16
         del a, ro, ri, cols, vals
     with open(path, "w") as f:
         for r in recs:
             f.write(json.dumps(r) + "\n")
-    for r in recs:
-        log(json.dumps({kk: (round(vv, 3) if isinstance(vv, float) else vv)
-                        for kk, vv in r.items() if not isinstance(vv, dict)}))
 
 
 def main() -> int:
@@ -683,18 +836,30 @@ def main() -> int:
     if args.profile_launches:
         step()
         torch.cuda.synchronize()
-        for fn in (k_build, k_offsets, k_swizzle, k_spmm, k_sddmm, k_fused):
+        flush = None
+        if args.profile_cold:
+            flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+            flush.zero_()
+
+        def launches(fn):
             for _ in range(args.profile_launches):
+                if flush is not None:
+                    flush.add_(1.0)
                 fn()
+
+        wanted = set(args.profile_workloads.split(","))
+        if "ffn" in wanted:
+            for fn in (k_build, k_offsets, k_swizzle, k_spmm, k_sddmm, k_fused):
+                launches(fn)
+        for fn in profile_workload_fns(torch, sp, inputs, dev, wanted):
+            launches(fn)
         if args.profile_stream:
             fn, _ = stream_setup(torch, sp, inputs, dev)
-            for _ in range(args.profile_launches):
-                fn()
+            launches(fn)
         # a plain copy of known size, to calibrate the byte counters
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
         dst = torch.empty_like(src)
-        for _ in range(args.profile_launches):
-            dst.copy_(src)
+        launches(lambda: dst.copy_(src))
         torch.cuda.synchronize()
         log("profile launches done")
         return 0
@@ -796,8 +961,20 @@ def main() -> int:
         "kernels": kernels,
     }
 
+    # Every seeded workload, warm and cold, against its roofline; the LSTM
+    # sweep with its dense comparison gives the break-even sparsity.
+    flush = None
+    if not args.no_configs or not args.no_breakeven:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB > L2 + MALL
+        flush.zero_()
+    records = []
+    if not args.no_configs:
+        records.extend(config_records(torch, sp, inputs, dev, flush))
     if not args.no_breakeven:
-        result["breakeven"] = lstm_breakeven(torch, sp, inputs, dev)
+        result["breakeven"] = lstm_breakeven(torch, sp, inputs, dev, records=records, flush=flush)
+    if records:
+        result["records"] = records
+    del flush
 
     if not args.no_stream:
         result["streaming"] = stream_record(torch, sp, inputs, dev)
