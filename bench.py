@@ -105,7 +105,9 @@ def parse_args():
                          "(for rocprofv3 counter passes) and exit")
     ap.add_argument("--profile-workloads", default="ffn",
                     help="with --profile-launches: comma-separated workloads to launch -- "
-                         "ffn (the step's kernels), resnet, lstm90, lstm50, attention")
+                         "ffn (the step's kernels), resnet, lstm90, lstm50, attention; "
+                         "resnet_wide, lstm50_wide: the same SpMM as a 2-entry batch, "
+                         "which takes the wide kernel")
     ap.add_argument("--profile-cold", action="store_true",
                     help="with --profile-launches: write a 1 GiB buffer before every "
                          "launch, so the byte counters see HBM traffic")
@@ -483,20 +485,34 @@ def lstm_breakeven(torch, sp, inputs, dev, reps=50, records=None, flush=None):
 def profile_workload_fns(torch, sp, inputs, dev, wanted):
     """Launch functions of the named workloads, for rocprofv3 passes: resnet
     (the ResNet-50 1x1 SpMM), lstm90 / lstm50 (the LSTM-sized SpMM at 90 % and
-    50 %), attention (the four sparse-attention kernels over 32 heads)."""
+    50 %), attention (the four sparse-attention kernels over 32 heads), and
+    resnet_wide / lstm50_wide (the SpMM on the wide kernel, as a 2-entry
+    batch)."""
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
     fns = []
-    for name, w in (("resnet", inputs.resnet_1x1), ("lstm90", lambda: inputs.lstm(0.9)),
-                    ("lstm50", lambda: inputs.lstm(0.5))):
-        if name not in wanted:
-            continue
-        w = w()
-        a = w["a"]
-        ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
-        b = up(w["b"])
-        c = torch.empty(w["m"], w["n"], device=dev)
-        fns.append(lambda m=w["m"], k=w["k"], n=w["n"], nnz=a.nnz, ri=ri, vals=vals, ro=ro,
-                   cols=cols, b=b, c=c: sp.sp_spmm(m, k, n, nnz, ri, vals, ro, cols, b, c))
+    gens = {"resnet": inputs.resnet_1x1, "lstm90": lambda: inputs.lstm(0.9),
+            "lstm50": lambda: inputs.lstm(0.5)}
+    for name, gen in gens.items():
+        # "<name>_wide": the same problem twice as a 2-entry batch (shared A
+        # and B), which never takes the panel kernel: the wide kernel's
+        # counters for the problem are half the dispatch's
+        for wide in (False, True):
+            if (name + ("_wide" if wide else "")) not in wanted:
+                continue
+            w = gen()
+            a = w["a"]
+            ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+            b = up(w["b"])
+            m, k, n, nnz = w["m"], w["k"], w["n"], a.nnz
+            if wide:
+                c = torch.empty(2, m, n, device=dev)
+                fns.append(lambda m=m, k=k, n=n, nnz=nnz, ri=ri, vals=vals, ro=ro, cols=cols,
+                           b=b, c=c: sp.sp_spmm_batched(m, k, n, nnz, ri, vals, ro, cols, b, c,
+                                                        2, 0, 0, m * n))
+            else:
+                c = torch.empty(m, n, device=dev)
+                fns.append(lambda m=m, k=k, n=n, nnz=nnz, ri=ri, vals=vals, ro=ro, cols=cols,
+                           b=b, c=c: sp.sp_spmm(m, k, n, nnz, ri, vals, ro, cols, b, c))
     if "attention" in wanted:
         w = inputs.sparse_attention()
         bh, seq, hd = w["batch"], w["seq"], w["head_dim"]
