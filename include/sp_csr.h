@@ -30,10 +30,12 @@
  *
  * Row order.  `row_indices` (int32[m], a permutation of 0..m-1, or NULL for
  * the identity) gives the order in which rows are handed to the GPU's workers:
- * the r-th work slot handles row row_indices[r].  It changes scheduling only,
- * never results (sp_spmm_balanced, which also groups rows by it, is the one
- * exception: there it can change rounding); sp_row_swizzle computes the
- * balanced order.
+ * the r-th work slot handles row row_indices[r]; sp_row_swizzle computes the
+ * balanced order.  It changes scheduling, not results, with one exception:
+ * the balanced SpMM kernel (sp_spmm_balanced, and sp_spmm itself on wide B
+ * when a row order is given) groups rows four at a time in that order, and a
+ * group whose rows differ much in length splits its entries over four waves,
+ * which changes rounding (deterministically for a given order).
  *
  * Errors.  Return codes only; nothing is thrown and nothing aborts.  Argument
  * checks happen on the host before any HIP call: a negative size, a NULL
@@ -187,10 +189,14 @@ sp_status_t sp_csr_build_from_lengths(int m, const int *lengths, int *row_offset
  *   b            fp32[k*n];  c  fp32[m*n], output
  * Sizes: m, k, n, nnz >= 0 and m*n, k*n < 2^62.  m == 0 or n == 0 enqueues
  * nothing.  Each output element is summed in an order fixed by the shapes
- * alone: in entry order (wide B); per-lane partial sums added by a fixed tree
- * (B of at most 16 columns); four consecutive parts of the row, each in entry
- * order, added in order (few rows averaging 256 entries or more).  Results are
- * deterministic run to run and do not depend on row_indices. */
+ * alone: in entry order (wide B, and B staged in LDS by row panels); per-lane
+ * partial sums added by a fixed tree (B of at most 16 columns); four
+ * consecutive parts of the row, each in entry order, added in order (few rows
+ * averaging 256 entries or more).  With a row order given, B of more than 128
+ * fp32 columns and one batch entry, the balanced kernel of sp_spmm_balanced
+ * runs instead (the card's I4: the swizzled order pairs long rows with short
+ * ones in its groups), so rows of a skewed group are summed as that entry
+ * point describes.  Results are deterministic run to run. */
 sp_status_t sp_spmm(int m, int k, int n, int nnz, const int *row_indices,
                     const float *values, const int *row_offsets,
                     const int *col_indices, const float *b, float *c,
@@ -199,15 +205,18 @@ sp_status_t sp_spmm(int m, int k, int n, int nnz, const int *row_indices,
 /* sp_spmm for row-length distributions with a heavy tail ("Interesting
  * ideas" I4 of the card: balancing kept separate from the kernels).  With
  * every wave of a launch resident at once, as on this GPU at these sizes, the
- * order rows are handed out in cannot balance anything: the longest row's
- * chain of loads sets the duration.  Here, for B of more than 128 fp32
+ * order rows are handed out in cannot balance anything by itself: the longest
+ * row's chain of loads sets the duration.  Here, for B of more than 128 fp32
  * columns, workgroups of 4 waves take 4 rows in serpentine order over the
- * work slots (in the swizzled order: long rows with short ones) and split the
- * group's entries evenly across the waves, adding the pieces' partial sums in
- * a fixed order.  Results are deterministic for a given row order and within
- * rounding of sp_spmm (pieces are summed separately).  On rows of uniform
- * length it is slower than sp_spmm (4-wave groups, an extra LDS pass);
- * narrower B takes sp_spmm's kernels.  Arguments as sp_spmm. */
+ * work slots (slots g, 2G-1-g, 2G+g, 4G-1-g of G groups: in the swizzled
+ * order, long rows with short ones).  A group whose longest row holds at most
+ * 1.5 times the group's mean runs one row per wave, summed in entry order as
+ * sp_spmm's wide kernel sums it; any other group splits its entries (taken
+ * row after row) into 4 equal parts, one per wave, and adds the parts'
+ * partial sums of each row in order.  Results are deterministic for a given
+ * row order and within rounding of sp_spmm.  sp_spmm runs this kernel by
+ * itself when given a row order on one batch entry of such B; narrower B takes
+ * sp_spmm's kernels.  Arguments as sp_spmm. */
 sp_status_t sp_spmm_balanced(int m, int k, int n, int nnz, const int *row_indices,
                              const float *values, const int *row_offsets,
                              const int *col_indices, const float *b, float *c,
@@ -249,14 +258,16 @@ sp_status_t sp_sddmm(int m, int k, int d, int nnz, const int *row_indices,
                      sp_stream_t stream);
 
 /* sp_sddmm for row-length distributions with a heavy tail ("Interesting
- * ideas" I4 of the card: balancing kept separate from the kernels).  sp_sddmm
- * gives each row one wave, which walks the row's windows of 64 entries in
- * turn, so with every wave resident at once the longest row's chain of
- * windows sets the duration.  Here each row slot gets a workgroup of 4 waves
- * and wave j takes windows j, j + 4, j + 8, ... of the row; entries need no
- * combine step, so outputs are bit-identical to sp_sddmm.  Rows of at most 64
- * entries leave three of their four waves idle (they exit at once), which
- * costs about nothing at these sizes.  Arguments, errors and results as
+ * ideas" I4 of the card: balancing kept separate from the kernels).  One wave
+ * per row walks the row's windows of 64 entries in turn, so with every wave
+ * resident at once the longest row's chain of windows would set the
+ * duration.  Here each row slot gets a workgroup of 4 waves and wave j takes
+ * windows j, j + 4, j + 8, ... of the row; entries need no combine step, so
+ * outputs are bit-identical to the one-wave form.  Rows of at most 64 entries
+ * leave three of their four waves idle (they exit at once), which costs about
+ * nothing at these sizes.  sp_sddmm (and any SDDMM entry point on one batch
+ * entry) takes this form by itself when the rows average 16 entries or more;
+ * this entry point takes it always.  Arguments, errors and results as
  * sp_sddmm. */
 sp_status_t sp_sddmm_balanced(int m, int k, int d, int nnz, const int *row_indices,
                               const int *row_offsets, const int *col_indices, const float *x,
@@ -355,23 +366,28 @@ sp_status_t sp_spmm_ex(int m, int k, int n, int nnz, const int *row_indices, int
 /* Which kernel sp_spmm_ex (and so sp_spmm / sp_spmm_batched) would run for
  * these arguments: *name is set to a static string --
  *   "wide"      one wave per row strip, B rows gathered from L2;
- *   "panel"     B staged in LDS, shared by a panel of 64 rows (rows per panel
- *               times density at least 4, n >= 64, fp32, one batch entry);
+ *   "balanced"  sp_spmm_balanced's kernel: wide B (more than 128 fp32
+ *               columns), one batch entry and a row order given;
+ *   "panel"     B staged in LDS and shared by a panel of 32 or 64 rows (fp32,
+ *               one batch entry, n of at least one 128-column tile, enough
+ *               panels to give every CU one, rows per panel times density at
+ *               least 4);
  *   "narrow"    lanes over entries for B of at most 16 columns;
  *   "lds"       the streaming kernel, narrow B copied into LDS once per CU;
  *   "split"     few long rows cut into four parts per workgroup;
  *   "none"      nothing to launch (m, n or batch is 0);
  *   "unsupported" sizes beyond the launch limits.
  * The choice depends on the sizes, the element type, the batch and strides,
- * and the alignment of values, col_indices, b and c, which are not
- * dereferenced (they may be any pointers with the caller's alignment; NULL is
- * accepted where sp_spmm_ex would accept it).  It also reads the current
- * device's compute-unit count and LDS size.  Host-only; enqueues nothing.
- * An unknown dtype, invalid sizes or NULL `name` return SP_ERROR_INVALID_VALUE. */
-sp_status_t sp_spmm_kernel_name(int m, int k, int n, int nnz, int dtype, const void *values,
-                                const int *col_indices, const void *b, const float *c,
-                                int batch, long long stride_values, long long stride_b,
-                                long long stride_c, const char **name);
+ * whether row_indices is NULL, and the alignment of values, col_indices, b and
+ * c; no array is dereferenced (any pointers with the caller's alignment will
+ * do; NULL is accepted where sp_spmm_ex would accept it).  It also reads the
+ * current device's compute-unit count and LDS size.  Host-only; enqueues
+ * nothing.  An unknown dtype, invalid sizes or NULL `name` return
+ * SP_ERROR_INVALID_VALUE. */
+sp_status_t sp_spmm_kernel_name(int m, int k, int n, int nnz, const int *row_indices, int dtype,
+                                const void *values, const int *col_indices, const void *b,
+                                const float *c, int batch, long long stride_values,
+                                long long stride_b, long long stride_c, const char **name);
 
 /* sp_sddmm_batched with X and Y of element type `dtype` (strides in elements
  * of that type); out is fp32.  SP_DTYPE_F32 is exactly sp_sddmm_batched.  An
@@ -395,9 +411,10 @@ sp_status_t sp_sddmm_ex(int m, int k, int d, int nnz, const int *row_indices,
  * whose sparsity structures may be the same arrays or different ones -- enqueued as one launch when both take their fp32 vector
  * paths (16-byte aligned operands, B and Y under 2 GiB, n % 4 == 0,
  * d % 4 == 0, d <= 256), otherwise as the two separate launches.  Results
- * are bit-identical to calling the two entry points.  Arguments are checked
- * as those entry points check them; c and out must not overlap each other or
- * any input. */
+ * are bit-identical to calling the two entry points, the SpMM with a NULL row
+ * order (the pair sums every SpMM row in entry order; row_indices only
+ * schedules).  Arguments are checked as those entry points check them; c and
+ * out must not overlap each other or any input. */
 sp_status_t sp_spmm_sddmm(int m, int k, int n, int nnz, const int *row_indices,
                           const float *values, const int *row_offsets, const int *col_indices,
                           const float *b, float *c, int s_m, int s_k, int d, int s_nnz,

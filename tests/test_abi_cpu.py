@@ -349,16 +349,19 @@ def test_spmm_kernel_name(lib):
     f = lib.sp_spmm_kernel_name
     name = ctypes.c_char_p()
     al = ctypes.c_void_p(0x10000)                     # 16-byte aligned stand-ins
-    assert f(8, 8, 4, 8, 0, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == OK
+    assert f(8, 8, 4, 8, NULL, 0, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == OK
     assert name.value == b"narrow"                      # fp32, n <= 16 columns
-    assert f(0, 8, 4, 8, 0, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == OK
+    assert f(0, 8, 4, 8, NULL, 0, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == OK
     assert name.value == b"none"
     # 16-bit types never take the fp32 narrow kernel
-    assert f(8, 8, 512, 8, 1, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == OK
+    assert f(8, 8, 512, 8, NULL, 1, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == OK
     assert name.value in (b"wide", b"split")
-    assert f(8, 8, 4, 8, 7, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == INVALID
-    assert f(-1, 8, 4, 8, 0, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == INVALID
-    assert f(8, 8, 4, 8, 0, al, al, al, al, 1, 0, 0, 0, None) == INVALID
+    # a row order on wide B, one batch entry: the balanced kernel
+    assert f(8, 8, 512, 8, al, 0, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == OK
+    assert name.value == b"balanced"
+    assert f(8, 8, 4, 8, NULL, 7, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == INVALID
+    assert f(-1, 8, 4, 8, NULL, 0, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == INVALID
+    assert f(8, 8, 4, 8, NULL, 0, al, al, al, al, 1, 0, 0, 0, None) == INVALID
 
 
 def test_row_swizzle_noalloc_validation(lib):

@@ -1,7 +1,8 @@
 """GPU checks of sp_spmm_sddmm: one launch carrying an SpMM and an SDDMM must
-give exactly (bit for bit) what the two separate entry points give, whether
-the pair is fused or falls back to two launches, and meet the oracle's
-tolerance."""
+give exactly (bit for bit) what the two separate entry points give -- the
+SpMM as sp_spmm gives it in the natural row order (every row summed in entry
+order) -- whether the pair is fused or falls back to two launches, and meet
+the oracle's tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -50,9 +51,11 @@ class Pair:
         return host(c), host(out)
 
     def separate(self):
+        # the pair's SpMM sums every row in entry order: sp_spmm's result in
+        # the natural row order (row order changes no sum of those kernels)
         c = torch.full((self.a.m, self.n), float("nan"), device="cuda")
         out = torch.full((self.s.nnz,), float("nan"), device="cuda")
-        sp.sp_spmm(self.a.m, self.a.k, self.n, self.a.nnz, self.ri_a, self.a.d_vals,
+        sp.sp_spmm(self.a.m, self.a.k, self.n, self.a.nnz, None, self.a.d_vals,
                    self.a.d_ro, self.a.d_ci, self.b, c)
         sp.sp_sddmm_batched(self.s.m, self.s.k, self.d, self.s.nnz, self.ri_s, self.s.d_ro,
                             self.s.d_ci, self.x, self.y, self.alpha, out, 1, 0, 0, 0)

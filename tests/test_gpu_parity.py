@@ -264,16 +264,38 @@ def test_spmm_lstm_whole(sparsity):
     check_close(c, ref, s, f"spmm lstm {sparsity}")
 
 
-def test_spmm_imbalance_swizzle_on_and_off_bit_equal():
+def test_spmm_imbalance_swizzle_on_and_off():
+    # In the natural order every row is summed in entry order; in the swizzled
+    # order sp_spmm runs the balanced kernel, whose skewed groups of four rows
+    # split their entries over four waves: both meet the tolerance, and the
+    # swizzled call is sp_spmm_balanced's, bit for bit, run to run.
     w = inputs.imbalance()
     a = csr_of_row_lists(w["a"])
+    ri = swizzle(a)
     note("spmm imbalance lognormal cov0.5, swizzle on/off")
     c_off = run_spmm(a, w["b"])
-    c_on = run_spmm(a, w["b"], row_indices=swizzle(a))
-    # Row order changes scheduling only: each row is summed the same way.
-    assert np.array_equal(c_on.view(np.int32), c_off.view(np.int32))
+    c_on = run_spmm(a, w["b"], row_indices=ri)
     ref, s = oracle.spmm(a.m, a.k, w["n"], a.ro, a.ci, a.vals, w["b"])
-    check_close(c_on, ref, s, "spmm imbalance")
+    check_close(c_off, ref, s, "spmm imbalance natural")
+    check_close(c_on, ref, s, "spmm imbalance swizzled")
+    assert np.array_equal(c_on.view(np.int32), run_spmm(a, w["b"], row_indices=ri).view(np.int32))
+    b = dev(w["b"])
+    c = torch.empty(a.m, w["n"], device="cuda")
+    assert sp.sp_spmm_kernel_name(a.m, a.k, w["n"], a.nnz, a.d_vals, a.d_ci, b, c,
+                                  row_indices=ri) == "balanced"
+    sp.sp_spmm_balanced(a.m, a.k, w["n"], a.nnz, ri, a.d_vals, a.d_ro, a.d_ci, b, c)
+    assert np.array_equal(c_on.view(np.int32), host(c).view(np.int32))
+
+
+def test_spmm_uniform_rows_swizzle_on_and_off_bit_equal():
+    # Rows of similar length: the balanced kernel's groups run one row per
+    # wave, summed as the wide kernel sums them in any order.
+    w = inputs.transformer_ffn()
+    a = csr_of_row_lists(w["a"])
+    note("spmm transformer_ffn swizzle on/off")
+    c_off = run_spmm(a, w["b"])
+    c_on = run_spmm(a, w["b"], row_indices=swizzle(a))
+    assert np.array_equal(c_on.view(np.int32), c_off.view(np.int32))
 
 
 # ------------------------------------------------------------------ SpMM, exact cases

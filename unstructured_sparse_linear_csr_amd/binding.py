@@ -77,7 +77,7 @@ SIGNATURES = {
                             _c_int),
     "sp_spmm_ex": ([_c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp,
                     _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
-    "sp_spmm_kernel_name": ([_c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp,
+    "sp_spmm_kernel_name": ([_c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp,
                              _c_int, _c_ll, _c_ll, _c_ll,
                              ctypes.POINTER(ctypes.c_char_p)], _c_int),
     "sp_sddmm_ex": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
@@ -318,16 +318,18 @@ def sp_spmm_balanced(m, k, n, nnz, row_indices, values, row_offsets, col_indices
 
 
 def sp_spmm_kernel_name(m, k, n, nnz, values, col_indices, b, c, batch=1, stride_values=0,
-                        stride_b=0, stride_c=0, dtype=None) -> str:
-    """The kernel sp_spmm_ex would run for these tensors (alignment and sizes)."""
+                        stride_b=0, stride_c=0, dtype=None, row_indices=None) -> str:
+    """The kernel sp_spmm_ex would run for these tensors (sizes, alignment,
+    and whether a row order is given)."""
     if dtype is None:
         dtype = {torch.float32: SP_DTYPE_F32, torch.float16: SP_DTYPE_F16,
                  torch.bfloat16: SP_DTYPE_BF16}[b.dtype]
     name = ctypes.c_char_p()
     addr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else None)
-    _check(lib().sp_spmm_kernel_name(m, k, n, nnz, dtype, addr(values), addr(col_indices),
-                                     addr(b), addr(c), batch, stride_values, stride_b, stride_c,
-                                     ctypes.byref(name)), "sp_spmm_kernel_name")
+    _check(lib().sp_spmm_kernel_name(m, k, n, nnz, addr(row_indices), dtype, addr(values),
+                                     addr(col_indices), addr(b), addr(c), batch, stride_values,
+                                     stride_b, stride_c, ctypes.byref(name)),
+           "sp_spmm_kernel_name")
     return name.value.decode()
 
 

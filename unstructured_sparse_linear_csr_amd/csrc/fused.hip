@@ -83,7 +83,10 @@ hipError_t launch_spmm_sddmm(const SpmmArgs &x, const SddmmArgs &y, hipStream_t 
 {
     SpmmPlan px;
     SddmmPlan py;
-    hipError_t e = plan_spmm(x, &px);
+    // The pair's SpMM sums every row in entry order (the wide kernel's body).
+    SpmmArgs xs = x;
+    xs.auto_balance = false;
+    hipError_t e = plan_spmm(xs, &px);
     if (e != hipSuccess) return e;
     e = plan_sddmm(y, &py);
     if (e != hipSuccess) return e;

@@ -237,7 +237,16 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
     plan->t_batch = 0;
     if (a.m == 0 || a.nnz == 0) return hipSuccess;
     if (xcd_grid(a.batch, a.m) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    plan->split = !a.softmax && a.parts > 1;  // the softmax needs whole rows
+    // A row's 64-entry windows spread over a workgroup of waves (outputs are
+    // bit-identical: an entry needs no combine step): on request, and by
+    // default for one batch entry whose rows average 16 entries or more.  A
+    // row of one window leaves the other waves nothing to do (they exit at
+    // once), so uniform rows lose little while the longest rows of a
+    // heavy-tailed structure no longer set the launch's duration (the card's
+    // I4).  Batched problems keep one wave per row slot: their many row slots
+    // already fill the GPU.  The softmax needs whole rows.
+    const bool auto_split = a.batch == 1 && (long long)a.nnz >= 16LL * a.m;
+    plan->split = !a.softmax && (a.parts > 1 || auto_split);
     SddmmParams &p = plan->p;
     p.m = a.m;
     p.batch = a.batch;

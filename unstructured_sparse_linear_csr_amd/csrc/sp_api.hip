@@ -261,10 +261,10 @@ sp_status_t sp_spmm_ex(int m, int k, int n, int nnz, const int *row_indices, int
     return from_hip(spk::launch_spmm(a, as_stream(stream)));
 }
 
-sp_status_t sp_spmm_kernel_name(int m, int k, int n, int nnz, int dtype, const void *values,
-                                const int *col_indices, const void *b, const float *c,
-                                int batch, long long stride_values, long long stride_b,
-                                long long stride_c, const char **name)
+sp_status_t sp_spmm_kernel_name(int m, int k, int n, int nnz, const int *row_indices, int dtype,
+                                const void *values, const int *col_indices, const void *b,
+                                const float *c, int batch, long long stride_values,
+                                long long stride_b, long long stride_c, const char **name)
 {
     if (name == nullptr) return SP_ERROR_INVALID_VALUE;
     spk::Dtype dt;
@@ -274,7 +274,7 @@ sp_status_t sp_spmm_kernel_name(int m, int k, int n, int nnz, int dtype, const v
     static const int kStandIn[2] = {0, 0};
     spk::SpmmArgs a;
     bool work = false;
-    const sp_status_t st = spmm_prepare(m, k, n, nnz, nullptr, dt, values, kStandIn, col_indices,
+    const sp_status_t st = spmm_prepare(m, k, n, nnz, row_indices, dt, values, kStandIn, col_indices,
                                         b, const_cast<float *>(c), batch, stride_values,
                                         stride_b, stride_c, &a, &work);
     if (st != SP_SUCCESS) return st;

@@ -20,6 +20,9 @@ struct SpmmArgs {
     long long stride_values, stride_b, stride_c;  // elements
     Dtype dtype = Dtype::f32;
     bool balanced = false;  // wide B: waves share each group's entries evenly
+    // wide B, one batch entry, a row order given: the balanced kernel (its
+    // groups of rows of similar length run as the wide kernel does)
+    bool auto_balance = true;
 };
 
 struct SddmmArgs {

@@ -96,16 +96,20 @@ bool panel_fits(const SpmmArgs &a, int cus, int lds_max, PanelParams *q)
 // columns per workgroup).  A workgroup of kBalWaves waves takes kBalWaves
 // rows chosen in serpentine order over the work slots -- g, 2G-1-g, 2G+g,
 // 4G-1-g for group g of G -- so that, in the swizzled order (rows by nonzero
-// count, longest first), each group pairs long rows with short ones.  The
-// group's entries, taken as one sequence (row after row), are cut into
-// kBalWaves equal parts, one per wave; a wave accumulates each row piece of
-// its part (the wide kernel's staging and gathers, with a wave-local barrier
-// since the waves run different numbers of windows) and leaves the partial
-// sums in LDS; then wave j adds row j's partial sums in wave order and writes
-// the row.  Every wave thus streams about the group's mean row length, and
-// the longest row no longer sets the launch's duration.  Summation: in entry
-// order within a piece, pieces in order; deterministic for a given row order.
+// count, longest first), each group pairs long rows with short ones.  A group
+// whose longest row holds at most kBalSkew times the group's mean row length
+// runs one row per wave, exactly as the wide kernel does (same staging, same
+// summation).  Otherwise the group's entries, taken as one sequence (row after
+// row), are cut into kBalWaves equal parts, one per wave; a wave accumulates
+// each row piece of its part (the wide kernel's staging and gathers, with a
+// wave-local barrier since the waves run different numbers of windows) and
+// leaves the partial sums in LDS; then wave j adds row j's partial sums in
+// wave order and writes the row.  Every wave thus streams about the group's
+// mean row length, and the longest row no longer sets the launch's duration.
+// Summation: in entry order within a piece, pieces in order; deterministic for
+// a given row order.
 constexpr int kBalWaves = 4;
+constexpr int kBalSkewNum = 3, kBalSkewDen = 2;  // kBalSkew = 1.5
 
 template <typename E, int kVec, bool kVecCsr, bool kBuf>
 __global__ __launch_bounds__(kBalWaves * kWave) void spmm_balanced_kernel(SpmmParams p)
@@ -144,9 +148,13 @@ __global__ __launch_bounds__(kBalWaves * kWave) void spmm_balanced_kernel(SpmmPa
     }
     __syncthreads();
     int cum[kBalWaves + 1];
+    int longest = 0;
     cum[0] = 0;
 #pragma unroll
-    for (int j = 0; j < kBalWaves; ++j) cum[j + 1] = cum[j] + s_len[j];
+    for (int j = 0; j < kBalWaves; ++j) {
+        cum[j + 1] = cum[j] + s_len[j];
+        longest = max(longest, s_len[j]);
+    }
     const long long total = cum[kBalWaves];
     auto part_lo = [&](int v) { return (int)(total * v / kBalWaves); };
 
@@ -154,6 +162,20 @@ __global__ __launch_bounds__(kBalWaves * kWave) void spmm_balanced_kernel(SpmmPa
     const E *__restrict__ bz = static_cast<const E *>(p.b) + z * p.stride_b;
     const int col0 = (tile * kWave + lane) * kVec;
     const bool col_ok = col0 < p.n;
+    float *cz = p.c + z * p.stride_c;
+    // Rows of similar length (uniform over the workgroup): one row per wave.
+    if ((long long)kBalWaves * kBalSkewDen * longest <= (long long)kBalSkewNum * total) {
+        const int row = s_row[wave];
+        if (row < 0) return;
+        float acc[kVec];
+#pragma unroll
+        for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
+        wide_accumulate<E, kWave, kVec, kVecCsr, kBuf, true>(
+            p, vals, bz, s_p0[wave], s_p0[wave] + s_len[wave], lane, col0, col_ok,
+            s_off + wave * kPitch, s_val + wave * kPitch, acc);
+        if (col_ok) V::store(cz + (size_t)row * (size_t)p.n + col0, acc);
+        return;
+    }
     const int lo_w = part_lo(wave), hi_w = part_lo(wave + 1);
 #pragma unroll
     for (int j = 0; j < kBalWaves; ++j) {
@@ -182,7 +204,6 @@ __global__ __launch_bounds__(kBalWaves * kWave) void spmm_balanced_kernel(SpmmPa
             for (int t = 0; t < kVec; ++t) acc[t] += s_part[wave][v][lane * kVec + t];
         }
     }
-    float *cz = p.c + z * p.stride_c;
     V::store(cz + (size_t)row * (size_t)p.n + col0, acc);
 }
 
@@ -791,10 +812,13 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
     plan->e = nv <= 1 ? 1 : nv <= 2 ? 2 : 4;
     plan->blocks = 0;
     plan->kind = SpmmPlan::kWide;
-    if (lpr == kWave && a.balanced) {
-        // groups of kBalWaves rows in place of row blocks
+    // The balanced kernel (groups of kBalWaves rows in place of row blocks): on
+    // request; and by default for one batch entry in a given row order -- the
+    // swizzled order of the card's I4 is what makes its serpentine groups pair
+    // long rows with short ones -- unless the problem is a few long rows.
+    const bool balance_ok = lpr == kWave;
+    if (balance_ok && a.balanced) {
         plan->kind = SpmmPlan::kBalanced;
-        p.row_blocks = (int)(((long long)a.m + kBalWaves - 1) / kBalWaves);
     } else if (vec_csr && buf && (long long)a.nnz >= kSplitMinLength * (long long)a.m) {
         // Few, long rows: fewer than two waves per SIMD in the wide launch.
         int cus = 0, lds_max = 0;
@@ -802,8 +826,13 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
             (long long)a.batch * tiles * row_blocks < 2LL * kSimdsPerCu * cus)
             plan->kind = SpmmPlan::kSplit;
     }
+    if (plan->kind == SpmmPlan::kWide && balance_ok && a.auto_balance &&
+        a.row_indices != nullptr && a.batch == 1)
+        plan->kind = SpmmPlan::kBalanced;
+    if (plan->kind == SpmmPlan::kBalanced)
+        p.row_blocks = (int)(((long long)a.m + kBalWaves - 1) / kBalWaves);
     // B shared in LDS by a panel of rows: fp32 vector paths, one batch entry.
-    if (f32 && vec && vec_csr && a.batch == 1 && a.k > 0 && a.m > 0) {
+    if (f32 && vec && vec_csr && a.batch == 1 && a.k > 0 && a.m > 0 && !a.balanced) {
         int cus = 0, lds_max = 0;
         if (device_limits(&cus, &lds_max)) {
             if (panel_fits<PanelMany>(a, cus, lds_max, &plan->q)) {
