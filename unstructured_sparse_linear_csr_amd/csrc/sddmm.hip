@@ -85,6 +85,688 @@ __global__ __launch_bounds__(kWave) void sddmm_cols_kernel(SddmmParams p)
     }
 }
 
+// Y stored d x k without a workspace: the columns of Y a panel of rows
+// touches are staged through LDS, transposed.
+// A workgroup of four waves owns a panel of kRows consecutive row slots (in
+// the given row order) and one of q.splits contiguous ranges of Y's columns;
+// wave w owns the panel's rows w, w + 4, ...  The panel's X rows are copied
+// into LDS once.  Each row keeps a cursor to its next pending CSR entry.  The
+// range is walked in chunks: a chunk starts at the smallest pending column of
+// the panel and ends before the (q.kc + 1)-th distinct column the panel's
+// pending entries touch, so one chunk can span many columns when few of them
+// are touched.  Per chunk:
+//  scan     each wave loads 64-entry windows of column indices for all its
+//           rows at once (kRounds windows per row, kept in registers) and
+//           sets one bit per touched column in a bitmap of the next kDkSpan
+//           columns;
+//  cut      a block prefix over the bitmap's words ranks the touched columns;
+//           the chunk ends at the column of rank q.kc, at the bitmap's end, or
+//           where a row's loaded windows end, whichever comes first;
+//  stage    the chunk's touched columns of Y are gathered (consecutive threads
+//           take consecutive columns) into LDS rows, one per rank;
+//  table    each wave writes, per row, the LDS row of each of its entries in
+//           the chunk;
+//  compute  each wave walks its rows: a row with kDkLaneMin or more entries in
+//           the chunk gives each entry one lane, which sums the d products in
+//           l order with FMA (X read by all lanes at once); a row with fewer
+//           gives each entry 16 lanes, each lane summing its kNv vectors (16
+//           apart) in order with FMA, and the 16 partial sums are added by the
+//           DPP tree of group_sum.
+// Staged rows have a pitch of an odd number of 16-byte units (16 lanes
+// reading 16 bytes from 16 different rows hit distinct banks when the rows
+// are consecutive) and are zero-padded to whole vectors (padding adds
+// 0 * 0, which leaves a sum unchanged).  Only the columns a panel touches are
+// read from Y, once per panel and column range.
+constexpr int kDkBatch = 8;      // staged vectors per thread in flight
+constexpr int kDkSpan = 8192;    // columns covered by a chunk's bitmap (one word per thread)
+constexpr int kDkLaneMin = 32;   // entries of a row in a chunk from which each gets one lane
+
+template <int kNv>
+struct DkShape {
+    // kNv: vectors per lane of the 16-lane path (0: d too large for it)
+    static constexpr int kRows = kNv == 0 ? 8 : kNv == 8 ? 16 : 32;
+    static constexpr int kRounds = kNv == 1 || kNv == 2 ? 2 : 1;  // windows per row per chunk
+};
+
+template <int kNv>
+__global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p, DkPanelParams q)
+{
+    using S = DkShape<kNv>;
+    constexpr int kRows = S::kRows;
+    constexpr int kRounds = S::kRounds;
+    constexpr int kWaves = 4;
+    constexpr int kThreads = kWaves * kWave;
+    constexpr int kRpw = kRows / kWaves;  // rows per wave
+    constexpr int kTab = kRounds * kWave; // table entries per row
+    constexpr int kWords = kDkSpan / 32;
+    constexpr int kG = 16, kNg = kWave / kG;  // 16-lane path: lanes per entry, entries per step
+    static_assert(kWords == kThreads, "one bitmap word per thread");
+    extern __shared__ __align__(16) unsigned char lds[];
+
+    const long long units = (long long)q.panels * q.splits;
+    const long long w = xcd_work_index(p.batch, units);
+    if (w < 0) return;
+    const long long z = w / units;
+    const int rem = (int)(w - z * units);
+    const int panel = rem / q.splits;
+    const int split = rem - panel * q.splits;
+    const int slot0 = panel * kRows;
+    const int nrows = min(kRows, p.m - slot0);
+    const int cb = (int)((long long)p.k * split / q.splits);
+    const int ce = (int)((long long)p.k * (split + 1) / q.splits);
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int g = lane / kG;
+    const int gl = lane - g * kG;
+    const int dv = (p.d + 3) / 4;  // 16-byte vectors per staged row
+
+    unsigned *s_tab = reinterpret_cast<unsigned *>(lds + q.off_tab) + wave * kRpw * kTab;
+    unsigned *s_bits = reinterpret_cast<unsigned *>(lds + q.off_bits);  // two bitmaps
+    unsigned *s_rank = reinterpret_cast<unsigned *>(lds + q.off_rank);  // touched columns below each word
+    int *s_col = reinterpret_cast<int *>(lds + q.off_col);              // column of each rank
+    int *s_misc = reinterpret_cast<int *>(lds + q.off_misc);
+    int *s_wmin = s_misc;       // [4] smallest pending column past the chunk, per wave
+    int *s_wlim = s_misc + 4;   // [4] end of the loaded windows, per wave
+    int *s_wsum = s_misc + 8;   // [4] touched columns per wave's words
+    int *s_cut = s_misc + 12;   // [1] column of rank q.kc
+
+    const float *__restrict__ xz = static_cast<const float *>(p.x) + z * p.stride_x;
+    const float *__restrict__ yz = static_cast<const float *>(p.y) + z * p.stride_y;
+    const int *__restrict__ ci = p.col_indices;
+
+    // X rows of the panel, zero-padded to whole vectors; kDkBatch vectors per
+    // thread in flight before they are stored.
+    const bool xvec = p.d % 4 == 0 && (reinterpret_cast<uintptr_t>(xz) & 15u) == 0;
+    for (int i0 = 0; i0 < nrows * dv; i0 += kDkBatch * kThreads) {
+        float4 xv[kDkBatch];
+#pragma unroll
+        for (int u = 0; u < kDkBatch; ++u) {
+            const int i = i0 + u * kThreads + tid;
+            const int r = i / dv, e = (i - r * dv) * 4;
+            xv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (i < nrows * dv) {
+                const int row = p.row_indices ? p.row_indices[slot0 + r] : slot0 + r;
+                const float *src = xz + (size_t)row * (size_t)p.d + e;
+                if (xvec) {
+                    xv[u] = *reinterpret_cast<const float4 *>(src);
+                } else {
+                    xv[u].x = src[0];
+                    if (e + 1 < p.d) xv[u].y = src[1];
+                    if (e + 2 < p.d) xv[u].z = src[2];
+                    if (e + 3 < p.d) xv[u].w = src[3];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kDkBatch; ++u) {
+            const int i = i0 + u * kThreads + tid;
+            const int r = i / dv, v = i - r * dv;
+            if (i < nrows * dv)
+                *reinterpret_cast<float4 *>(lds + (unsigned)r * q.x_pitch + (unsigned)v * 16u) = xv[u];
+        }
+    }
+    s_bits[tid] = 0u;
+    s_bits[kWords + tid] = 0u;
+
+    // This wave's rows: lane i < kRpw holds row wave + 4 i's cursor, end and
+    // (per chunk) entry count.
+    int my_cur = 0, my_end = 0, my_n = 0;
+    if (lane < kRpw && wave + kWaves * lane < nrows) {
+        const int r = wave + kWaves * lane;
+        const int row = p.row_indices ? p.row_indices[slot0 + r] : slot0 + r;
+        my_cur = p.row_offsets[row];
+        my_end = p.row_offsets[row + 1];
+    }
+    unsigned live_rows = 0;  // bit i: row wave + 4 i exists
+#pragma unroll
+    for (int i = 0; i < kRpw; ++i)
+        if (wave + kWaves * i < nrows) live_rows |= 1u << i;
+    // Cursors to each row's first entry in the range; wm = the smallest
+    // pending column of the wave's rows (INT_MAX: none).
+    int wm = INT_MAX;
+    {
+        unsigned act = live_rows;
+        while (act != 0u) {
+            int col[kRpw];
+#pragma unroll
+            for (int i = 0; i < kRpw; ++i) {
+                const int base = __builtin_amdgcn_readlane(my_cur, i);
+                const int end = __builtin_amdgcn_readlane(my_end, i);
+                col[i] = (act >> i & 1u) && lane < end - base ? ci[base + lane] : INT_MAX;
+            }
+#pragma unroll
+            for (int i = 0; i < kRpw; ++i) {
+                if (!(act >> i & 1u)) continue;
+                const int cnt = (int)__popcll(__builtin_amdgcn_ballot_w64(col[i] < cb));
+                if (lane == i) my_cur += cnt;
+                if (cnt < kWave) {
+                    wm = min(wm, __builtin_amdgcn_readlane(col[i], cnt));
+                    act &= ~(1u << i);
+                }
+            }
+        }
+    }
+    if (lane == 0) s_wmin[wave] = wm;
+    __syncthreads();
+    int chunk0 = min(min(s_wmin[0], s_wmin[1]), min(s_wmin[2], s_wmin[3]));
+
+    for (int chunk = 0; chunk0 < ce; ++chunk) {
+        unsigned *bits = s_bits + (chunk & 1) * kWords;
+        const int limw = (int)min((long long)chunk0 + kDkSpan, (long long)ce);
+        // ---- scan: col[i][t] = column of row i's entry 64 t + lane from its
+        // cursor (INT_MAX past the row); rows whose kRounds windows all lie
+        // below limw bound the chunk at their next entry's column (wl).
+        int col[kRpw][kRounds];
+        unsigned loaded = 0;  // bit i * kRounds + t: window t of row i was loaded
+        int wl = limw;
+        {
+            unsigned act = live_rows;
+#pragma unroll
+            for (int t = 0; t < kRounds; ++t) {
+#pragma unroll
+                for (int i = 0; i < kRpw; ++i) {
+                    const int base = __builtin_amdgcn_readlane(my_cur, i) + kWave * t;
+                    const int end = __builtin_amdgcn_readlane(my_end, i);
+                    col[i][t] = (act >> i & 1u) && lane < end - base ? ci[base + lane] : INT_MAX;
+                }
+#pragma unroll
+                for (int i = 0; i < kRpw; ++i) {
+                    if (!(act >> i & 1u)) continue;
+                    loaded |= 1u << (i * kRounds + t);
+                    const int c = col[i][t];
+                    const bool in = c < limw;
+                    const int cnt = (int)__popcll(__builtin_amdgcn_ballot_w64(in));
+                    // (columns ascend within a row; the range check only keeps
+                    // LDS accesses in bounds for input that breaks that)
+                    const unsigned rel = (unsigned)(c - chunk0);
+                    if (in && rel < (unsigned)kDkSpan) atomicOr(&bits[rel >> 5], 1u << (rel & 31u));
+                    if (cnt < kWave) act &= ~(1u << i);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kRpw; ++i) {
+                if (!(act >> i & 1u)) continue;
+                const int at = __builtin_amdgcn_readlane(my_cur, i) + kTab;
+                wl = min(wl, at < __builtin_amdgcn_readlane(my_end, i) ? ci[at] : INT_MAX);
+            }
+        }
+        if (lane == 0) s_wlim[wave] = wl;
+        __syncthreads();
+        // ---- cut: rank the touched columns below lim0; end the chunk at the
+        // column of rank q.kc when there are more
+        const int lim0 = min(min(s_wlim[0], s_wlim[1]), min(s_wlim[2], s_wlim[3]));
+        const unsigned word = bits[tid];
+        const int wbase = tid * 32;  // first column of this word, relative to chunk0
+        auto below = [](int nbits) {
+            return nbits >= 32 ? 0xffffffffu : nbits <= 0 ? 0u : (1u << nbits) - 1u;
+        };
+        const unsigned word0 = word & below(lim0 - chunk0 - wbase);
+        const int cnt = __popc(word0);
+        const int incl = wave_inclusive_sum(cnt);
+        if (lane == kWave - 1) s_wsum[wave] = incl;
+        __syncthreads();
+        int excl = incl - cnt, total = 0;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            const int sv = s_wsum[v];
+            if (v < wave) excl += sv;
+            total += sv;
+        }
+        s_rank[tid] = (unsigned)excl;
+        if (total > q.kc && excl <= q.kc && q.kc < excl + cnt) {
+            // this word holds rank q.kc: its column ends the chunk
+            unsigned wb = word0;
+            for (int j = q.kc - excl; j > 0; --j) wb &= wb - 1u;
+            *s_cut = chunk0 + wbase + (int)__builtin_ctz(wb);
+        }
+        __syncthreads();
+        const int lim = total > q.kc ? *s_cut : lim0;
+        const int ns = min(total, q.kc);
+        {
+            unsigned wb = word0 & below(lim - chunk0 - wbase);
+            for (int j = excl; wb != 0u; ++j) {
+                s_col[j] = chunk0 + wbase + (int)__builtin_ctz(wb);
+                wb &= wb - 1u;
+            }
+        }
+        // the other bitmap is free (last read before this chunk's first barrier)
+        s_bits[((chunk + 1) & 1) * kWords + tid] = 0u;
+        __syncthreads();
+        // ---- stage the touched columns of Y, in rank order
+        for (int i0 = 0; i0 < ns * dv; i0 += kDkBatch * kThreads) {
+            float el[kDkBatch][4];
+#pragma unroll
+            for (int u = 0; u < kDkBatch; ++u) {
+                const int i = i0 + u * kThreads + tid;
+                const int v = i / ns, s = i - v * ns;
+                const bool ok = i < ns * dv;
+                const size_t c = ok ? (size_t)s_col[s] : 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    el[u][j] = ok && 4 * v + j < p.d ? yz[(size_t)(4 * v + j) * (size_t)p.k + c] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kDkBatch; ++u) {
+                const int i = i0 + u * kThreads + tid;
+                const int v = i / ns, s = i - v * ns;
+                if (i < ns * dv)
+                    *reinterpret_cast<float4 *>(lds + q.off_y + (unsigned)s * q.y_pitch +
+                                                (unsigned)v * 16u) =
+                        make_float4(el[u][0], el[u][1], el[u][2], el[u][3]);
+            }
+        }
+        // ---- table: per row, the entries in the chunk (a prefix of its
+        // loaded windows), the LDS row of each, and the next pending column
+        wm = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < kRpw; ++i) {
+            int n = 0;
+#pragma unroll
+            for (int t = 0; t < kRounds; ++t)
+                if (loaded >> (i * kRounds + t) & 1u)
+                    n += (int)__popcll(__builtin_amdgcn_ballot_w64(col[i][t] < lim));
+            if (lane == i) my_n = n;
+            // the entry after the chunk: in the loaded windows, unless all of
+            // them were taken (then it is the one that bounded the chunk)
+            int next = INT_MAX;
+#pragma unroll
+            for (int t = 0; t < kRounds; ++t)
+                if (n >> 6 == t && (loaded >> (i * kRounds + t) & 1u))
+                    next = __builtin_amdgcn_readlane(col[i][t], n & 63);
+            if (n == kTab) {
+                const int at = __builtin_amdgcn_readlane(my_cur, i) + kTab;
+                if (at < __builtin_amdgcn_readlane(my_end, i)) next = ci[at];
+            }
+            if (live_rows >> i & 1u) wm = min(wm, next);
+#pragma unroll
+            for (int t = 0; t < kRounds; ++t) {
+                if (kWave * t < n && kWave * t + lane < n) {
+                    const unsigned rel = (unsigned)(col[i][t] - chunk0);
+                    unsigned off = q.off_y;
+                    if (rel < (unsigned)(lim - chunk0)) {
+                        const unsigned wd = rel >> 5, b = rel & 31u;
+                        off += (s_rank[wd] + (unsigned)__popc(bits[wd] & ((1u << b) - 1u))) * q.y_pitch;
+                    }
+                    s_tab[i * kTab + kWave * t + lane] = off;
+                }
+            }
+        }
+        if (lane == 0) s_wmin[wave] = wm;
+        __syncthreads();
+        const int next0 = min(min(s_wmin[0], s_wmin[1]), min(s_wmin[2], s_wmin[3]));
+        // ---- compute
+        for (int i = 0; i < kRpw; ++i) {
+            const int n = __builtin_amdgcn_readlane(my_n, i);
+            if (n == 0) continue;
+            const int cur = __builtin_amdgcn_readlane(my_cur, i);
+            const unsigned char *xr = lds + (unsigned)(wave + kWaves * i) * q.x_pitch;
+            const unsigned *tab = s_tab + i * kTab;
+            if (kNv == 0 || n >= kDkLaneMin) {
+                for (int t0 = 0; t0 < n; t0 += kWave) {
+                    if (t0 + lane < n) {
+                        const unsigned char *yr = lds + tab[t0 + lane];
+                        float acc = 0.f;
+#pragma unroll 4
+                        for (int v = 0; v < dv; ++v) {
+                            const float4 xv = *reinterpret_cast<const float4 *>(xr + v * 16);
+                            const float4 yv = *reinterpret_cast<const float4 *>(yr + v * 16);
+                            acc = fmaf(xv.x, yv.x, acc);
+                            acc = fmaf(xv.y, yv.y, acc);
+                            acc = fmaf(xv.z, yv.z, acc);
+                            acc = fmaf(xv.w, yv.w, acc);
+                        }
+                        store_entry(p, z, cur + t0 + lane, acc);
+                    }
+                }
+            } else if constexpr (kNv > 0) {
+                // fewer than kDkLaneMin entries: one window of 16-lane groups
+                float4 xv[kNv];
+#pragma unroll
+                for (int v = 0; v < kNv; ++v)
+                    xv[v] = v * kG + gl < dv
+                                ? *reinterpret_cast<const float4 *>(xr + (v * kG + gl) * 16)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+                const int steps = (n + kNg - 1) / kNg;
+                float res = 0.f;
+                for (int s = 0; s < steps; ++s) {
+                    const int j = s * kNg + g;
+                    const unsigned char *yr = lds + tab[j < n ? j : 0];
+                    float acc = 0.f;
+#pragma unroll
+                    for (int v = 0; v < kNv; ++v) {
+                        if (v * kG + gl < dv) {
+                            const float4 yv = *reinterpret_cast<const float4 *>(yr + (v * kG + gl) * 16);
+                            acc = fmaf(xv[v].x, yv.x, acc);
+                            acc = fmaf(xv[v].y, yv.y, acc);
+                            acc = fmaf(xv[v].z, yv.z, acc);
+                            acc = fmaf(xv[v].w, yv.w, acc);
+                        }
+                    }
+                    const float sum = group_sum<kG>(acc);
+                    if (gl == s) res = sum;
+                }
+                const int jo = gl * kNg + g;  // the entry whose sum this lane kept
+                if (jo < n) store_entry(p, z, cur + jo, res);
+            }
+        }
+        my_cur += my_n;
+        chunk0 = next0;
+    }
+}
+
+// Y stored d x k without a workspace, for masks that touch most columns of a
+// tile: a workgroup of four waves owns a panel of kRows consecutive row slots
+// and one tile of at most kDkTileCols consecutive columns [c0, c1) of Y, which
+// it stages whole.  All global reads are issued before the workgroup's one
+// barrier, in three dependent levels: the panel's row ids; then the tile of Y
+// (16-byte reads along Y's rows: 16 lanes cover one row of the tile, each
+// writing its 4 columns into 4 transposed LDS rows), the panel's X rows and
+// the rows' CSR bounds; then per row a 64-entry window from the row's start
+// of column indices, mask values and prior outputs.  A row's first entry at
+// or past c0 is found in that window (or, for longer rows, by a 64-way search
+// and a window read from there); its entries in the tile (at most 64) are
+// shifted to lanes 0, 1, ...  Each wave then takes its rows' entries in the
+// tile one after another, 64 to a pass: each entry gets one lane, which sums
+// its d products in l order with FMA (X and Y rows read from LDS), so lanes
+// are not left idle by rows with few entries in the tile.
+constexpr int kDkTileCols = 64;
+constexpr int kDkTileYBatch = 16;  // Y vectors per thread per batch (d <= 256: one batch)
+
+template <int kNv, bool kVec>
+__global__ __launch_bounds__(4 * kWave) void sddmm_dk_tile_kernel(SddmmParams p, DkPanelParams q)
+{
+    using S = DkShape<kNv>;
+    constexpr int kRows = S::kRows;
+    constexpr int kWaves = 4;
+    constexpr int kThreads = kWaves * kWave;
+    constexpr int kRpw = kRows / kWaves;
+    constexpr int kXItems = 8;  // X vectors per thread per batch
+    extern __shared__ __align__(16) unsigned char lds[];
+
+    const long long units = (long long)q.panels * q.splits;  // splits = tiles per panel
+    const long long w = xcd_work_index(p.batch, units);
+    if (w < 0) return;
+    const long long z = w / units;
+    const int rem = (int)(w - z * units);
+    const int panel = rem / q.splits;
+    const int tile = rem - panel * q.splits;
+    const int slot0 = panel * kRows;
+    const int nrows = min(kRows, p.m - slot0);
+    const int c0 = tile * q.kc;
+    const int c1 = min(c0 + q.kc, p.k);
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int dv = (p.d + 3) / 4;
+    const int dl = 4 * dv;                 // staged elements per row (d padded)
+    const int cq = (c1 - c0 + 3) / 4;      // column quads in the tile (<= 16)
+
+    const float *__restrict__ xz = static_cast<const float *>(p.x) + z * p.stride_x;
+    const float *__restrict__ yz = static_cast<const float *>(p.y) + z * p.stride_y;
+    const int *__restrict__ ci = p.col_indices;
+    // row id of panel row r, read from a valid stand-in array when there is
+    // no row order (row_offsets has m + 1 entries)
+    const int *rsrc = p.row_indices ? p.row_indices : p.row_offsets;
+    auto row_of = [&](int r) {
+        const int v = rsrc[slot0 + r];
+        return p.row_indices ? v : slot0 + r;
+    };
+
+    // Every load below is unconditional and from a valid address: surplus
+    // items repeat the last item (loading and storing the same value again),
+    // and no value is chosen between a load and a constant.  (A load under a
+    // branch, or one the compiler turns into a branch, makes it wait for every
+    // load in flight where the branches join, which would serialise the
+    // levels.)
+    // ---- level 1: row ids of this wave's rows (lane i < kRpw: row wave + 4 i)
+    // and of the X rows this thread stages (thread -> vector tid % dvp of rows
+    // tid / dvp + u * (256 / dvp), dvp = 2^q.x_shift >= dv)
+    const int my_r = wave + kWaves * lane;
+    const bool my_ok = lane < kRpw && my_r < nrows;
+    const int my_row = row_of(my_ok ? my_r : 0);
+    const int xsh = q.x_shift;
+    const int xv_i = min(tid & ((1 << xsh) - 1), dv - 1);
+    const int xr0 = tid >> xsh;
+    const int xstep = kThreads >> xsh;
+    int xrow[kXItems];
+#pragma unroll
+    for (int u = 0; u < kXItems; ++u) xrow[u] = row_of(min(xr0 + u * xstep, nrows - 1));
+    __builtin_amdgcn_sched_barrier(0);  // issue each level's loads together
+    // ---- level 2a: the tile of Y: item i -> element row l = i / cq, column
+    // quad i % cq; i / cq as (i * ceil(2^20 / cq)) >> 20, exact for
+    // i < 2^14 and cq <= 16 (the error stays below 1/64 < 1/cq)
+    const int ny = p.d * cq;  // items
+    const unsigned long long cq_magic = ((1u << 20) + (unsigned)cq - 1u) / (unsigned)cq;
+    auto y_item = [&](int i, int &l, int &qd) {
+        i = min(i, ny - 1);
+        l = (int)(((unsigned long long)(unsigned)i * cq_magic) >> 20);
+        qd = i - l * cq;
+    };
+    auto load_y = [&](int i) {
+        int l, qd;
+        y_item(i, l, qd);
+        const float *src = yz + (size_t)l * (size_t)p.k + (c0 + 4 * qd);
+        float4 v;
+        if constexpr (kVec) {  // k % 4 == 0, so the quad lies inside the row
+            v = *reinterpret_cast<const float4 *>(src);
+        } else {
+            const int last = c1 - 1 - (c0 + 4 * qd);  // >= 0
+            v.x = src[0];
+            v.y = src[min(1, last)];
+            v.z = src[min(2, last)];
+            v.w = src[min(3, last)];
+        }
+        return v;
+    };
+    auto store_y = [&](int i, const float4 &v) {
+        int l, qd;
+        y_item(i, l, qd);
+        float *dst = reinterpret_cast<float *>(lds + q.off_y + (unsigned)(4 * qd) * q.y_pitch) + l;
+        const unsigned pf = q.y_pitch / 4u;
+        dst[0] = v.x;
+        dst[pf] = v.y;
+        dst[2 * pf] = v.z;
+        dst[3 * pf] = v.w;
+    };
+    float4 yb[kDkTileYBatch];
+#pragma unroll
+    for (int u = 0; u < kDkTileYBatch; ++u) yb[u] = load_y(u * kThreads + tid);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- level 2b: this wave's CSR bounds, then the panel's X rows
+    auto load_x = [&](int row) {
+        const int e = 4 * xv_i;
+        const float *src = xz + (size_t)row * (size_t)p.d + e;
+        float4 v;
+        if constexpr (kVec) {  // d % 4 == 0
+            v = *reinterpret_cast<const float4 *>(src);
+        } else {
+            const int last = p.d - 1 - e;  // >= 0
+            v.x = src[0];
+            v.y = src[min(1, last)];
+            v.z = src[min(2, last)];
+            v.w = src[min(3, last)];
+        }
+        return v;
+    };
+    int my_start = p.row_offsets[my_row];
+    int my_end = p.row_offsets[my_row + 1];
+    __builtin_amdgcn_sched_barrier(0);
+    float4 xb[kXItems];
+#pragma unroll
+    for (int u = 0; u < kXItems; ++u) xb[u] = load_x(xrow[u]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!my_ok) my_start = my_end = 0;
+    // ---- level 3: per row, the 64-entry window from its start (mask values
+    // and prior outputs read from a valid stand-in array when absent)
+    const float *__restrict__ vz = p.mask_values ? p.mask_values + z * p.stride_values : nullptr;
+    float *__restrict__ oz = p.out + z * p.stride_out;
+    const float *vsrc = vz ? vz : reinterpret_cast<const float *>(ci);
+    const float *psrc = p.beta != 0.f ? oz : reinterpret_cast<const float *>(ci);
+    int win[kRpw];
+    float mvw[kRpw], prw[kRpw];
+#pragma unroll
+    for (int i = 0; i < kRpw; ++i) {
+        const int s = __builtin_amdgcn_readlane(my_start, i);
+        const int e = __builtin_amdgcn_readlane(my_end, i);
+        const bool in = lane < e - s;
+        const int at = in ? s + lane : 0;  // nnz > 0 here, so entry 0 exists
+        const int c = ci[at];
+        const float mvv = vsrc[at];
+        const float prv = psrc[at];
+        win[i] = in ? c : INT_MAX;
+        mvw[i] = vz ? mvv : 1.f;
+        prw[i] = p.beta != 0.f ? prv : 0.f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- stage Y (more batches when d * cq > 16 * 256) and its zero rows
+    // l in [d, 4 dv) (X's padding is zero, but 0 * NaN is not)
+#pragma unroll
+    for (int u = 0; u < kDkTileYBatch; ++u) store_y(u * kThreads + tid, yb[u]);
+    for (int i0 = kDkTileYBatch * kThreads; i0 < ny; i0 += kDkTileYBatch * kThreads) {
+#pragma unroll
+        for (int u = 0; u < kDkTileYBatch; ++u) yb[u] = load_y(i0 + u * kThreads + tid);
+#pragma unroll
+        for (int u = 0; u < kDkTileYBatch; ++u) store_y(i0 + u * kThreads + tid, yb[u]);
+    }
+    for (int i = tid; i < (dl - p.d) * 4 * cq; i += kThreads) {
+        const int c = i / (dl - p.d), l = p.d + (i - c * (dl - p.d));
+        reinterpret_cast<float *>(lds + q.off_y + (unsigned)c * q.y_pitch)[l] = 0.f;
+    }
+    // ---- stage X (zero beyond d: the loads repeat element d - 1)
+#pragma unroll
+    for (int u = 0; u < kXItems; ++u) {
+        const int r = min(xr0 + u * xstep, nrows - 1);
+        float4 v = xb[u];
+        if constexpr (!kVec) {
+            const int e = 4 * xv_i;
+            if (e + 1 >= p.d) v.y = 0.f;
+            if (e + 2 >= p.d) v.z = 0.f;
+            if (e + 3 >= p.d) v.w = 0.f;
+        }
+        *reinterpret_cast<float4 *>(lds + (unsigned)r * q.x_pitch + (unsigned)xv_i * 16u) = v;
+    }
+    for (int r0 = kXItems * xstep; r0 < nrows; r0 += kXItems * xstep) {  // more rows than one batch
+        for (int u = 0; u < kXItems; ++u) {
+            const int r = min(r0 + xr0 + u * xstep, nrows - 1);
+            float4 v = load_x(row_of(r));
+            if constexpr (!kVec) {
+                const int e = 4 * xv_i;
+                if (e + 1 >= p.d) v.y = 0.f;
+                if (e + 2 >= p.d) v.z = 0.f;
+                if (e + 3 >= p.d) v.w = 0.f;
+            }
+            *reinterpret_cast<float4 *>(lds + (unsigned)r * q.x_pitch + (unsigned)xv_i * 16u) = v;
+        }
+    }
+    // ---- each row's entries in the tile: base (first entry >= c0), count,
+    // and per lane j < count entry j's column, mask value and prior output
+    int base[kRpw], cnt[kRpw], colt[kRpw];
+    float mv[kRpw], pr[kRpw];
+#pragma unroll
+    for (int i = 0; i < kRpw; ++i) {
+        const int s = __builtin_amdgcn_readlane(my_start, i);
+        const int e = __builtin_amdgcn_readlane(my_end, i);
+        const int below = (int)__popcll(__builtin_amdgcn_ballot_w64(win[i] < c0));
+        const bool past = __builtin_amdgcn_ballot_w64(win[i] >= c1) != 0ull;  // INT_MAX past the end
+        if (below < kWave && past) {
+            // (cross-lane reads with every lane active: a lane reads another's
+            // register only while that lane is active)
+            const int src = min(lane + below, kWave - 1);
+            base[i] = s + below;
+            colt[i] = __shfl(win[i], src);
+            mv[i] = __shfl(mvw[i], src);
+            pr[i] = __shfl(prw[i], src);
+            if (lane + below >= kWave) colt[i] = INT_MAX;
+            cnt[i] = (int)__popcll(__builtin_amdgcn_ballot_w64(win[i] >= c0 && win[i] < c1));
+        } else {
+            // the tile's entries reach past the window: find the first entry
+            // >= c0 (64-way search beyond the window when all of it is below)
+            // and read a window from there
+            int b = s + below;
+            if (below == kWave) {
+                int lo = s + kWave, hi = e;
+                while (hi - lo > kWave) {
+                    const int step = (hi - lo + kWave - 1) / kWave;
+                    const int at = lo + lane * step;
+                    const int c = at < hi ? ci[at] : INT_MAX;
+                    const int nb = (int)__popcll(__builtin_amdgcn_ballot_w64(c < c0));
+                    const int nlo = nb == 0 ? lo : lo + (nb - 1) * step + 1;
+                    hi = min(hi, lo + nb * step);
+                    lo = nlo;
+                }
+                const int c = lane < hi - lo ? ci[lo + lane] : INT_MAX;
+                b = lo + (int)__popcll(__builtin_amdgcn_ballot_w64(c < c0));
+            }
+            base[i] = b;
+            const bool in = lane < e - b;
+            const int at = in ? b + lane : 0;
+            const int cr = ci[at];
+            const float mvv = vsrc[at];
+            const float prv = psrc[at];
+            const int c = in ? cr : INT_MAX;
+            colt[i] = c < c1 ? c : INT_MAX;
+            cnt[i] = (int)__popcll(__builtin_amdgcn_ballot_w64(c < c1));
+            mv[i] = vz ? mvv : 1.f;
+            pr[i] = p.beta != 0.f ? prv : 0.f;
+        }
+    }
+    __syncthreads();
+    // ---- compute: the wave's entries in the tile, rows after one another,
+    // 64 to a pass, one lane each
+    int pre[kRpw];
+    int total = 0;
+#pragma unroll
+    for (int i = 0; i < kRpw; ++i) {
+        pre[i] = total;
+        total += cnt[i];
+    }
+    for (int t0 = 0; t0 < total; t0 += kWave) {
+        const int e = t0 + lane;
+        // entry e's row i (the last row starting at or before e) and its
+        // column, mask value, prior output and position, gathered from the
+        // lanes that hold them (cross-lane reads with every lane active)
+        int col = INT_MAX, at = 0, xrow = 0;
+        float v = 1.f, prior = 0.f;
+#pragma unroll
+        for (int i = 0; i < kRpw; ++i) {
+            if (cnt[i] == 0 || pre[i] >= t0 + kWave || pre[i] + cnt[i] <= t0) continue;
+            const int j = min(max(e - pre[i], 0), kWave - 1);
+            const int ci_ = __shfl(colt[i], j);
+            const float mv_ = __shfl(mv[i], j);
+            const float pr_ = __shfl(pr[i], j);
+            if (e >= pre[i] && e < pre[i] + cnt[i]) {
+                col = ci_;
+                v = mv_;
+                prior = pr_;
+                at = base[i] + (e - pre[i]);
+                xrow = wave + kWaves * i;
+            }
+        }
+        if (e < total) {
+            // (columns ascend within a row; the range check only keeps LDS
+            // reads in bounds for input that breaks that)
+            const unsigned rel = (unsigned)(col - c0);
+            const unsigned char *yr =
+                lds + q.off_y + (rel < (unsigned)(c1 - c0) ? rel : 0u) * q.y_pitch;
+            const unsigned char *xr = lds + (unsigned)xrow * q.x_pitch;
+            float acc = 0.f;
+#pragma unroll 4
+            for (int u = 0; u < dv; ++u) {
+                const float4 xv = *reinterpret_cast<const float4 *>(xr + u * 16);
+                const float4 yv = *reinterpret_cast<const float4 *>(yr + u * 16);
+                acc = fmaf(xv.x, yv.x, acc);
+                acc = fmaf(xv.y, yv.y, acc);
+                acc = fmaf(xv.z, yv.z, acc);
+                acc = fmaf(xv.w, yv.w, acc);
+            }
+            float r = p.alpha * v * acc;
+            if (p.beta != 0.f) r = fmaf(p.beta, prior, r);
+            oz[at] = r;
+        }
+    }
+}
+
 // out_z = in_z^T for a rows x cols matrix in_z (row-major, z = blockIdx.z):
 // 32 x 32 tiles through LDS (one padding column, so the transposed reads hit
 // distinct banks), 256 threads reading 4 rows each.  (c_base, r_base) is the
@@ -211,6 +893,132 @@ inline bool aligned16(const void *ptr)
     return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0;
 }
 
+template <int kNv>
+hipError_t launch_dk_t(const SddmmParams &p, const DkPanelParams &q, hipStream_t s)
+{
+    const auto fn = sddmm_dk_panel_kernel<kNv>;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)q.lds);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)xcd_grid(p.batch, (long long)q.panels * q.splits));
+    hipLaunchKernelGGL(fn, grid, dim3(4 * kWave), q.lds, s, p, q);
+    return hipGetLastError();
+}
+
+template <int kNv, bool kVec>
+hipError_t launch_dk_tile_t(const SddmmParams &p, const DkPanelParams &q, hipStream_t s)
+{
+    const auto fn = sddmm_dk_tile_kernel<kNv, kVec>;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)q.lds);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)xcd_grid(p.batch, (long long)q.panels * q.splits));
+    hipLaunchKernelGGL(fn, grid, dim3(4 * kWave), q.lds, s, p, q);
+    return hipGetLastError();
+}
+
+template <bool kVec>
+hipError_t launch_dk_tile_v(const SddmmParams &p, const DkPanelParams &q, hipStream_t s)
+{
+    switch (q.nv) {
+    case 1: return launch_dk_tile_t<1, kVec>(p, q, s);
+    case 2: return launch_dk_tile_t<2, kVec>(p, q, s);
+    case 4: return launch_dk_tile_t<4, kVec>(p, q, s);
+    case 8: return launch_dk_tile_t<8, kVec>(p, q, s);
+    default: return launch_dk_tile_t<0, kVec>(p, q, s);
+    }
+}
+
+hipError_t launch_dk_tile(const SddmmParams &p, const DkPanelParams &q, bool vec, hipStream_t s)
+{
+    return vec ? launch_dk_tile_v<true>(p, q, s) : launch_dk_tile_v<false>(p, q, s);
+}
+
+hipError_t launch_dk(const SddmmParams &p, const DkPanelParams &q, hipStream_t s)
+{
+    switch (q.nv) {
+    case 1: return launch_dk_t<1>(p, q, s);
+    case 2: return launch_dk_t<2>(p, q, s);
+    case 4: return launch_dk_t<4>(p, q, s);
+    case 8: return launch_dk_t<8>(p, q, s);
+    default: return launch_dk_t<0>(p, q, s);
+    }
+}
+
+// LDS per workgroup of the d x k panel kernel: two workgroups per CU.
+constexpr unsigned kDkLdsBudget = 76u * 1024u;
+constexpr int kDkTargetGroups = 512;  // workgroups wanted before splitting Y's columns
+constexpr double kDkTileDensity = 0.05;  // mean mask density from which the tile kernel runs
+
+// The d x k panel kernel's shape for fp32 operands, or false when LDS cannot
+// hold a useful chunk (d beyond about 1000) or the launch would be too large.
+bool plan_dk_panel(const SddmmArgs &a, SddmmPlan *plan)
+{
+    if (a.dtype != Dtype::f32 || a.d <= 0 || a.k <= 0 || a.softmax) return false;
+    const int dv = (a.d + 3) / 4;  // 16-byte vectors per staged row
+    DkPanelParams &q = plan->dk;
+    q.nv = dv <= 16 ? 1 : dv <= 32 ? 2 : dv <= 64 ? 4 : dv <= 128 ? 8 : 0;
+    int rounds = 1;
+    switch (q.nv) {  // DkShape's rows and windows per row
+    case 1: q.rows = DkShape<1>::kRows; rounds = DkShape<1>::kRounds; break;
+    case 2: q.rows = DkShape<2>::kRows; rounds = DkShape<2>::kRounds; break;
+    case 4: q.rows = DkShape<4>::kRows; rounds = DkShape<4>::kRounds; break;
+    case 8: q.rows = DkShape<8>::kRows; rounds = DkShape<8>::kRounds; break;
+    default: q.rows = DkShape<0>::kRows; rounds = DkShape<0>::kRounds; break;
+    }
+    q.x_pitch = q.y_pitch = 16u * ((unsigned)dv | 1u);  // an odd number of 16-byte units
+    const unsigned tab = (unsigned)q.rows * (unsigned)rounds * kWave * 4u;
+    const unsigned tables = tab + 2u * 1024u + 1024u + 1024u + 64u;
+    const unsigned fixed = (unsigned)q.rows * q.x_pitch + tables;
+    if (fixed >= kDkLdsBudget) return false;
+    // Masks that touch most columns of a tile (a mean density of 1/20 or more
+    // leaves few columns of a 32-row tile untouched) take the dense-tile
+    // kernel, one tile per workgroup; sparser ones the panel kernel.
+    const double density = (double)a.nnz / ((double)a.m * (double)a.k);
+    if (density >= kDkTileDensity && dv <= 256) {
+        const unsigned xbytes = (unsigned)q.rows * q.x_pitch;
+        if (xbytes < kDkLdsBudget) {
+            const int kc = (int)std::min<unsigned>(kDkTileCols, (kDkLdsBudget - xbytes) / q.y_pitch) & ~3;
+            if (kc >= 8) {
+                q.kc = kc;
+                q.panels = (a.m + q.rows - 1) / q.rows;
+                q.splits = (a.k + kc - 1) / kc;
+                if (xcd_grid(a.batch, (long long)q.panels * q.splits) <= 0x7fffffffLL) {
+                    q.x_shift = 0;
+                    while ((1 << q.x_shift) < dv) ++q.x_shift;  // X vectors per row, to a power of 2
+
+                    q.off_y = xbytes;
+                    q.lds = xbytes + (unsigned)kc * q.y_pitch;
+                    // 16-byte reads of X and Y rows: d % 4 == 0, k % 4 == 0, aligned
+                    plan->vec = a.d % 4 == 0 && a.k % 4 == 0 && aligned16(a.x) && aligned16(a.y) &&
+                                a.stride_x % 4 == 0 && a.stride_y % 4 == 0;
+                    plan->kind = SddmmPlan::kDkTile;
+                    return true;
+                }
+            }
+        }
+    }
+    q.kc = (int)std::min<unsigned>(256u, (kDkLdsBudget - fixed) / q.y_pitch);
+    if (q.kc < 8) return false;
+    q.panels = (a.m + q.rows - 1) / q.rows;
+    const long long units = (long long)a.batch * q.panels;
+    const long long want = (kDkTargetGroups + units - 1) / units;
+    const long long most = std::max<long long>(1, a.k / (2LL * q.kc));
+    q.splits = (int)std::max<long long>(1, std::min(want, most));
+    if (xcd_grid(a.batch, (long long)q.panels * q.splits) > 0x7fffffffLL) return false;
+    q.off_y = (unsigned)q.rows * q.x_pitch;
+    q.off_tab = q.off_y + (unsigned)q.kc * q.y_pitch;
+    q.off_bits = q.off_tab + tab;
+    q.off_rank = q.off_bits + 2u * 1024u;
+    q.off_col = q.off_rank + 1024u;
+    q.off_misc = q.off_col + 1024u;
+    q.lds = q.off_misc + 64u;
+    plan->kind = SddmmPlan::kDkPanel;
+    return true;
+}
+
 }  // namespace
 
 hipError_t launch_fill_zero(float *dst, long long count, hipStream_t stream)
@@ -273,7 +1081,7 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
     p.y_bytes = buf ? (unsigned)((long long)a.k * a.d * eb) : 0u;
     plan->buf = buf;
     if (a.y_layout == 1 && a.workspace == nullptr) {
-        plan->kind = SddmmPlan::kCols;
+        if (!plan_dk_panel(a, plan)) plan->kind = SddmmPlan::kCols;
         return hipSuccess;
     }
     if (a.y_layout == 1) {
@@ -336,6 +1144,10 @@ hipError_t run_sddmm(const SddmmPlan &plan, hipStream_t stream)
         }
         return hipSuccess;
     }
+    case SddmmPlan::kDkPanel:
+        return launch_dk(p, plan.dk, stream);
+    case SddmmPlan::kDkTile:
+        return launch_dk_tile(p, plan.dk, plan.vec, stream);
     case SddmmPlan::kCols:
         switch (plan.dtype) {
         case Dtype::f16: return launch_cols<_Float16>(plan.buf, p, stream);

@@ -22,8 +22,20 @@ struct SpmmPlan {
     int lds_kvec = 0;  // LDS kernel: B elements per LDS vector (8: 16-bit B kept 16-bit)
 };
 
+// Y stored d x k without a workspace (sddmm.hip): panels of `rows` row slots,
+// each over `splits` contiguous ranges of Y's columns, staging up to `kc`
+// touched columns at a time; byte offsets of the dynamic LDS regions.
+struct DkPanelParams {
+    int rows, kc, splits, panels;
+    int nv;  // vectors per lane of the 16-lane path (0: one lane per entry only)
+    int x_shift;  // tile kernel: log2 of X's vectors per row rounded up to a power of 2
+    unsigned x_pitch, y_pitch;  // LDS bytes per staged X row / Y column
+    unsigned off_y, off_tab, off_bits, off_rank, off_col, off_misc;
+    unsigned lds;
+};
+
 struct SddmmPlan {
-    enum Kind { kNothing, kFill, kCols, kRows } kind;
+    enum Kind { kNothing, kFill, kCols, kRows, kDkPanel, kDkTile } kind;
     sddmm_detail::SddmmParams p;
     Dtype dtype;
     bool vec, buf;
@@ -34,6 +46,7 @@ struct SddmmPlan {
     const void *t_src;        // NULL: no transpose
     long long t_src_stride;   // elements between batch entries of the d x k source
     int t_batch;              // source operands to transpose (1 when shared)
+    DkPanelParams dk;         // kDkPanel, kDkTile (splits = column tiles per panel)
 };
 
 // hipErrorInvalidConfiguration when the grid would exceed the launch limits.

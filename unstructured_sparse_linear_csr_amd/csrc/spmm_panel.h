@@ -293,7 +293,8 @@ __device__ __forceinline__ void spmm_panel_body(const SpmmParams &p, const Panel
                     float val[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        const bool in = (unsigned)(e + t - cur[r]) < span && cc[t] < kend;
+                        const bool in = (unsigned)(e + t - cur[r]) < span &&
+                                        (unsigned)(cc[t] - k0) < (unsigned)(kend - k0);
                         off[t] = in ? (cc[t] - k0) * (kT * 4) : zoff;
                         val[t] = in ? vv[t] : 0.f;
                         taken += in;
