@@ -308,14 +308,20 @@ typedef enum sp_y_layout {
  *                transposed into it (one k x d copy per batch entry, or one
  *                shared copy when stride_y = 0) and the SP_Y_KD kernels run on
  *                that copy: the same results bit for bit as SP_Y_KD on the
- *                caller's own transpose.  Without one, SP_Y_DK gathers single
- *                elements along rows of Y, several times slower.  The
+ *                caller's own transpose.  Without one, SP_Y_DK stages Y
+ *                through LDS, transposed: for d <= 1024, masks of mean density
+ *                1/20 or more by tiles of up to 64 columns (each output summed
+ *                by 16 lanes, each in order over every 16th 4-element vector,
+ *                then added pairwise across the lanes), sparser masks by the
+ *                columns each panel of rows touches (each output summed in l
+ *                order by one lane); beyond d = 1024 single elements are
+ *                gathered along rows of Y (summed in l order).  The
  *                workspace is the caller's; its contents after the call are
  *                unspecified, and calls that share one on overlapping streams
  *                race.
  * Everything else as sp_sddmm_batched, which is this call with mask_values =
- * NULL, y_layout = SP_Y_KD, beta = 0 and no workspace.  Each output's dot
- * product is summed in l order per entry; deterministic run to run. */
+ * NULL, y_layout = SP_Y_KD, beta = 0 and no workspace.  Deterministic run to
+ * run. */
 sp_status_t sp_sddmm_general(int m, int k, int d, int nnz, const int *row_indices,
                              const int *row_offsets, const int *col_indices,
                              const float *mask_values, const float *x, const float *y,

@@ -1,13 +1,12 @@
 """GPU parity of the general SDDMM with Y stored d x k and no workspace.
 
-For fp32 operands and d up to about 1100, the call stages Y through LDS,
+For fp32 operands and d up to 1024, the call stages Y through LDS,
 transposed: masks of mean density 1/20 or more by tiles of up to 64
-consecutive columns (one per workgroup, staged whole), sparser masks by the
-columns each panel of rows touches (chunks of up to a few hundred distinct
-columns).  In both, an entry of a row with 32 or more entries in the tile or
-chunk gets one lane, which sums its d products in l order with FMA, and an
-entry of a row with fewer gets 16 lanes whose partial sums meet in a DPP
-tree.  Every output is checked against the oracle within
+consecutive columns (one per workgroup, staged whole), where each entry gets
+16 lanes whose partial sums meet in a DPP tree; sparser masks by the columns
+each panel of rows touches (chunks of up to 256 distinct columns), where
+each entry gets one lane, which sums its d products in l order with FMA.
+Every output is checked against the oracle within
 |gpu - oracle| <= 1e-5 * (|alpha v| sum|x y| + |beta prior|), and so is the
 same call with a workspace (Y transposed there first).  With small-integer
 operands every partial sum is exact in fp32, so the outputs must equal the
@@ -157,10 +156,9 @@ def test_depths(d, dense):
                 f"dk d={d} dense={dense} exact")
 
 
-@pytest.mark.parametrize("d", [1100, 2000])
+@pytest.mark.parametrize("d", [1025, 2000])
 def test_depths_beyond_panel(d):
-    # 1100: eight-row panels of eight staged columns; 2000: LDS cannot hold a
-    # useful chunk and the element-gather kernel runs
+    # beyond d = 1024 the element-gather kernel runs
     m, k = 70, 150
     a = random_csr(640 + d, m, k, 0, 60)
     x = inputs.random_dense(641 + d, m, d)
@@ -208,8 +206,8 @@ def test_rows_of_thousands_of_entries():
 @pytest.mark.parametrize("d", [16, 64, 256])
 def test_tiles_of_long_dense_rows(d):
     # tiles (density 60 %): rows of ~2500 entries, so a tile's first entry lies
-    # beyond the first 64-entry window (64-way search), rows with 32 or more
-    # entries in a tile (one lane per entry) and the last, ragged tile
+    # beyond the first 64-entry window (64-way search), and the last, ragged
+    # tile
     m, k = 96, 4100
     a = random_csr(700 + d, m, k, 2000, 2900)
     x = inputs.random_dense(701 + d, m, d)

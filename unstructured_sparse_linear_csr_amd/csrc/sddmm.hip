@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kWave) void sddmm_cols_kernel(SddmmParams p)
     }
 }
 
-// Y stored d x k without a workspace: the columns of Y a panel of rows
-// touches are staged through LDS, transposed.
+// Y stored d x k without a workspace, for sparse masks: the columns of Y a
+// panel of rows touches are staged through LDS, transposed.
 // A workgroup of four waves owns a panel of kRows consecutive row slots (in
 // the given row order) and one of q.splits contiguous ranges of Y's columns;
 // wave w owns the panel's rows w, w + 4, ...  The panel's X rows are copied
@@ -106,40 +106,77 @@ __global__ __launch_bounds__(kWave) void sddmm_cols_kernel(SddmmParams p)
 //           take consecutive columns) into LDS rows, one per rank;
 //  table    each wave writes, per row, the LDS row of each of its entries in
 //           the chunk;
-//  compute  each wave walks its rows: a row with kDkLaneMin or more entries in
-//           the chunk gives each entry one lane, which sums the d products in
-//           l order with FMA (X read by all lanes at once); a row with fewer
-//           gives each entry 16 lanes, each lane summing its kNv vectors (16
-//           apart) in order with FMA, and the 16 partial sums are added by the
-//           DPP tree of group_sum.
+//  compute  each wave takes its rows' entries in the chunk one after another,
+//           64 to a pass: each entry gets one lane, which sums its d products
+//           in l order with FMA (X and Y rows read from LDS), so rows with few
+//           entries in a chunk leave no lane idle.
 // Staged rows have a pitch of an odd number of 16-byte units (16 lanes
 // reading 16 bytes from 16 different rows hit distinct banks when the rows
 // are consecutive) and are zero-padded to whole vectors (padding adds
 // 0 * 0, which leaves a sum unchanged).  Only the columns a panel touches are
 // read from Y, once per panel and column range.
-constexpr int kDkBatch = 8;      // staged vectors per thread in flight
-constexpr int kDkSpan = 8192;    // columns covered by a chunk's bitmap (one word per thread)
-constexpr int kDkLaneMin = 32;   // entries of a row in a chunk from which each gets one lane
+// Global loads are unconditional and from valid addresses: surplus items
+// repeat the last item, and values are chosen only after loading.  (A load
+// under a branch makes the compiler wait for every load in flight where the
+// branches join, which would serialise the loads.)
+constexpr int kDkSpan = 8192;   // columns covered by a chunk's bitmap (one word per thread)
+constexpr int kDkYBatch = 16;   // staged Y vectors per thread in flight
+constexpr int kDkXItems = 8;    // staged X vectors per thread in flight
 
-template <int kNv>
-struct DkShape {
-    // kNv: vectors per lane of the 16-lane path (0: d too large for it)
-    static constexpr int kRows = kNv == 0 ? 8 : kNv == 8 ? 16 : 32;
-    static constexpr int kRounds = kNv == 1 || kNv == 2 ? 2 : 1;  // windows per row per chunk
-};
+// Panel heights and windows per row per chunk, by 16-byte vectors per row.
+__host__ __device__ constexpr int dk_rows(int dv) { return dv <= 64 ? 32 : dv <= 128 ? 16 : 8; }
+__host__ __device__ constexpr int dk_rounds(int dv) { return dv <= 32 ? 2 : 1; }
 
-template <int kNv>
+// X rows of a panel into LDS: thread -> vector tid % 2^xsh of rows
+// tid / 2^xsh + u * (kThreads >> xsh) (2^xsh >= dv; kDkXItems * (kThreads >>
+// xsh) covers the panel's rows), zero beyond d.
+template <int kThreads, bool kVec, class RowOf>
+__device__ __forceinline__ void dk_stage_x(const SddmmParams &p, const float *xz, int nrows,
+                                           int xsh, unsigned x_pitch, unsigned char *lds,
+                                           RowOf row_of)
+{
+    const int tid = threadIdx.x;
+    const int dv = (p.d + 3) / 4;
+    const int xv = min(tid & ((1 << xsh) - 1), dv - 1);
+    const int xr0 = tid >> xsh;
+    const int xstep = kThreads >> xsh;
+    int xrow[kDkXItems];
+#pragma unroll
+    for (int u = 0; u < kDkXItems; ++u) xrow[u] = row_of(min(xr0 + u * xstep, nrows - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    float4 xb[kDkXItems];
+    const int e = 4 * xv;
+#pragma unroll
+    for (int u = 0; u < kDkXItems; ++u) {
+        const float *src = xz + (size_t)xrow[u] * (size_t)p.d + e;
+        if constexpr (kVec) {  // d % 4 == 0
+            xb[u] = *reinterpret_cast<const float4 *>(src);
+        } else {
+            const int last = p.d - 1 - e;  // >= 0
+            xb[u] = make_float4(src[0], src[min(1, last)], src[min(2, last)], src[min(3, last)]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kDkXItems; ++u) {
+        const int r = min(xr0 + u * xstep, nrows - 1);
+        float4 v = xb[u];
+        if constexpr (!kVec) {
+            if (e + 1 >= p.d) v.y = 0.f;
+            if (e + 2 >= p.d) v.z = 0.f;
+            if (e + 3 >= p.d) v.w = 0.f;
+        }
+        *reinterpret_cast<float4 *>(lds + (unsigned)r * x_pitch + (unsigned)xv * 16u) = v;
+    }
+}
+
+template <int kRows, int kRounds, bool kVec>
 __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p, DkPanelParams q)
 {
-    using S = DkShape<kNv>;
-    constexpr int kRows = S::kRows;
-    constexpr int kRounds = S::kRounds;
     constexpr int kWaves = 4;
     constexpr int kThreads = kWaves * kWave;
     constexpr int kRpw = kRows / kWaves;  // rows per wave
     constexpr int kTab = kRounds * kWave; // table entries per row
     constexpr int kWords = kDkSpan / 32;
-    constexpr int kG = 16, kNg = kWave / kG;  // 16-lane path: lanes per entry, entries per step
     static_assert(kWords == kThreads, "one bitmap word per thread");
     extern __shared__ __align__(16) unsigned char lds[];
 
@@ -157,8 +194,6 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int g = lane / kG;
-    const int gl = lane - g * kG;
     const int dv = (p.d + 3) / 4;  // 16-byte vectors per staged row
 
     unsigned *s_tab = reinterpret_cast<unsigned *>(lds + q.off_tab) + wave * kRpw * kTab;
@@ -174,50 +209,34 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
     const float *__restrict__ xz = static_cast<const float *>(p.x) + z * p.stride_x;
     const float *__restrict__ yz = static_cast<const float *>(p.y) + z * p.stride_y;
     const int *__restrict__ ci = p.col_indices;
-
-    // X rows of the panel, zero-padded to whole vectors; kDkBatch vectors per
-    // thread in flight before they are stored.
-    const bool xvec = p.d % 4 == 0 && (reinterpret_cast<uintptr_t>(xz) & 15u) == 0;
-    for (int i0 = 0; i0 < nrows * dv; i0 += kDkBatch * kThreads) {
-        float4 xv[kDkBatch];
-#pragma unroll
-        for (int u = 0; u < kDkBatch; ++u) {
-            const int i = i0 + u * kThreads + tid;
-            const int r = i / dv, e = (i - r * dv) * 4;
-            xv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (i < nrows * dv) {
-                const int row = p.row_indices ? p.row_indices[slot0 + r] : slot0 + r;
-                const float *src = xz + (size_t)row * (size_t)p.d + e;
-                if (xvec) {
-                    xv[u] = *reinterpret_cast<const float4 *>(src);
-                } else {
-                    xv[u].x = src[0];
-                    if (e + 1 < p.d) xv[u].y = src[1];
-                    if (e + 2 < p.d) xv[u].z = src[2];
-                    if (e + 3 < p.d) xv[u].w = src[3];
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kDkBatch; ++u) {
-            const int i = i0 + u * kThreads + tid;
-            const int r = i / dv, v = i - r * dv;
-            if (i < nrows * dv)
-                *reinterpret_cast<float4 *>(lds + (unsigned)r * q.x_pitch + (unsigned)v * 16u) = xv[u];
-        }
-    }
-    s_bits[tid] = 0u;
-    s_bits[kWords + tid] = 0u;
+    // row id of panel row r, read from a valid stand-in array when there is
+    // no row order (row_offsets has m + 1 entries)
+    const int *rsrc = p.row_indices ? p.row_indices : p.row_offsets;
+    auto row_of = [&](int r) {
+        const int v = rsrc[slot0 + r];
+        return p.row_indices ? v : slot0 + r;
+    };
+    // column index of entry at, or INT_MAX when ok is false (entry 0 exists:
+    // nnz > 0 here)
+    auto col_at = [&](bool ok, int at) {
+        const int c = ci[ok ? at : 0];
+        return ok ? c : INT_MAX;
+    };
 
     // This wave's rows: lane i < kRpw holds row wave + 4 i's cursor, end and
     // (per chunk) entry count.
-    int my_cur = 0, my_end = 0, my_n = 0;
-    if (lane < kRpw && wave + kWaves * lane < nrows) {
-        const int r = wave + kWaves * lane;
-        const int row = p.row_indices ? p.row_indices[slot0 + r] : slot0 + r;
-        my_cur = p.row_offsets[row];
-        my_end = p.row_offsets[row + 1];
-    }
+    const int my_r = wave + kWaves * lane;
+    const bool my_ok = lane < kRpw && my_r < nrows;
+    const int my_row = row_of(my_ok ? my_r : 0);
+    __builtin_amdgcn_sched_barrier(0);
+    int my_cur = p.row_offsets[my_row];
+    int my_end = p.row_offsets[my_row + 1];
+    __builtin_amdgcn_sched_barrier(0);
+    dk_stage_x<kThreads, kVec>(p, xz, nrows, q.x_shift, q.x_pitch, lds, row_of);
+    if (!my_ok) my_cur = my_end = 0;
+    int my_n = 0;
+    s_bits[tid] = 0u;
+    s_bits[kWords + tid] = 0u;
     unsigned live_rows = 0;  // bit i: row wave + 4 i exists
 #pragma unroll
     for (int i = 0; i < kRpw; ++i)
@@ -233,7 +252,7 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
             for (int i = 0; i < kRpw; ++i) {
                 const int base = __builtin_amdgcn_readlane(my_cur, i);
                 const int end = __builtin_amdgcn_readlane(my_end, i);
-                col[i] = (act >> i & 1u) && lane < end - base ? ci[base + lane] : INT_MAX;
+                col[i] = col_at((act >> i & 1u) && lane < end - base, base + lane);
             }
 #pragma unroll
             for (int i = 0; i < kRpw; ++i) {
@@ -250,6 +269,12 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
     if (lane == 0) s_wmin[wave] = wm;
     __syncthreads();
     int chunk0 = min(min(s_wmin[0], s_wmin[1]), min(s_wmin[2], s_wmin[3]));
+
+    // epilogue operands, read from a valid stand-in array when absent
+    const float *__restrict__ vz = p.mask_values ? p.mask_values + z * p.stride_values : nullptr;
+    float *__restrict__ oz = p.out + z * p.stride_out;
+    const float *vsrc = vz ? vz : reinterpret_cast<const float *>(ci);
+    const float *psrc = p.beta != 0.f ? oz : reinterpret_cast<const float *>(ci);
 
     for (int chunk = 0; chunk0 < ce; ++chunk) {
         unsigned *bits = s_bits + (chunk & 1) * kWords;
@@ -268,7 +293,7 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
                 for (int i = 0; i < kRpw; ++i) {
                     const int base = __builtin_amdgcn_readlane(my_cur, i) + kWave * t;
                     const int end = __builtin_amdgcn_readlane(my_end, i);
-                    col[i][t] = (act >> i & 1u) && lane < end - base ? ci[base + lane] : INT_MAX;
+                    col[i][t] = col_at((act >> i & 1u) && lane < end - base, base + lane);
                 }
 #pragma unroll
                 for (int i = 0; i < kRpw; ++i) {
@@ -288,7 +313,8 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
             for (int i = 0; i < kRpw; ++i) {
                 if (!(act >> i & 1u)) continue;
                 const int at = __builtin_amdgcn_readlane(my_cur, i) + kTab;
-                wl = min(wl, at < __builtin_amdgcn_readlane(my_end, i) ? ci[at] : INT_MAX);
+                const int c = col_at(at < __builtin_amdgcn_readlane(my_end, i), at);
+                wl = min(wl, c);
             }
         }
         if (lane == 0) s_wlim[wave] = wl;
@@ -333,27 +359,49 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
         // the other bitmap is free (last read before this chunk's first barrier)
         s_bits[((chunk + 1) & 1) * kWords + tid] = 0u;
         __syncthreads();
-        // ---- stage the touched columns of Y, in rank order
-        for (int i0 = 0; i0 < ns * dv; i0 += kDkBatch * kThreads) {
-            float el[kDkBatch][4];
+        // ---- stage the touched columns of Y in rank order: item i -> rank
+        // i % ns, vector i / ns (i / ns as a multiply by ceil(2^25 / ns) and a
+        // shift, exact for i < 2^16 and ns <= 256); surplus items repeat the
+        // last one
+        {
+            const int nitems = ns * dv;
+            const unsigned long long magic = ((1u << 25) + (unsigned)ns - 1u) / (unsigned)ns;
+            for (int i0 = 0; i0 < nitems; i0 += kDkYBatch * kThreads) {
+                float4 yb[kDkYBatch];
+                int sl[kDkYBatch], vv[kDkYBatch];
 #pragma unroll
-            for (int u = 0; u < kDkBatch; ++u) {
-                const int i = i0 + u * kThreads + tid;
-                const int v = i / ns, s = i - v * ns;
-                const bool ok = i < ns * dv;
-                const size_t c = ok ? (size_t)s_col[s] : 0;
+                for (int u = 0; u < kDkYBatch; ++u) {
+                    const int i = min(i0 + u * kThreads + tid, nitems - 1);
+                    vv[u] = (int)(((unsigned long long)(unsigned)i * magic) >> 25);
+                    sl[u] = i - vv[u] * ns;
+                }
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    el[u][j] = ok && 4 * v + j < p.d ? yz[(size_t)(4 * v + j) * (size_t)p.k + c] : 0.f;
-            }
+                for (int u = 0; u < kDkYBatch; ++u) {
+                    const size_t c = (size_t)s_col[sl[u]];
+                    const int l = 4 * vv[u];
+                    const float *src = yz + (size_t)l * (size_t)p.k + c;
+                    if constexpr (kVec) {  // d % 4 == 0: all four rows exist
+                        yb[u] = make_float4(src[0], src[(size_t)p.k], src[2 * (size_t)p.k],
+                                            src[3 * (size_t)p.k]);
+                    } else {
+                        const int last = p.d - 1 - l;  // >= 0
+                        yb[u] = make_float4(src[0], src[(size_t)min(1, last) * (size_t)p.k],
+                                            src[(size_t)min(2, last) * (size_t)p.k],
+                                            src[(size_t)min(3, last) * (size_t)p.k]);
+                    }
+                }
 #pragma unroll
-            for (int u = 0; u < kDkBatch; ++u) {
-                const int i = i0 + u * kThreads + tid;
-                const int v = i / ns, s = i - v * ns;
-                if (i < ns * dv)
-                    *reinterpret_cast<float4 *>(lds + q.off_y + (unsigned)s * q.y_pitch +
-                                                (unsigned)v * 16u) =
-                        make_float4(el[u][0], el[u][1], el[u][2], el[u][3]);
+                for (int u = 0; u < kDkYBatch; ++u) {
+                    float4 v = yb[u];
+                    if constexpr (!kVec) {
+                        const int l = 4 * vv[u];
+                        if (l + 1 >= p.d) v.y = 0.f;
+                        if (l + 2 >= p.d) v.z = 0.f;
+                        if (l + 3 >= p.d) v.w = 0.f;
+                    }
+                    *reinterpret_cast<float4 *>(lds + q.off_y + (unsigned)sl[u] * q.y_pitch +
+                                                (unsigned)vv[u] * 16u) = v;
+                }
             }
         }
         // ---- table: per row, the entries in the chunk (a prefix of its
@@ -376,7 +424,7 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
                     next = __builtin_amdgcn_readlane(col[i][t], n & 63);
             if (n == kTab) {
                 const int at = __builtin_amdgcn_readlane(my_cur, i) + kTab;
-                if (at < __builtin_amdgcn_readlane(my_end, i)) next = ci[at];
+                next = col_at(at < __builtin_amdgcn_readlane(my_end, i), at);
             }
             if (live_rows >> i & 1u) wm = min(wm, next);
 #pragma unroll
@@ -395,59 +443,48 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
         if (lane == 0) s_wmin[wave] = wm;
         __syncthreads();
         const int next0 = min(min(s_wmin[0], s_wmin[1]), min(s_wmin[2], s_wmin[3]));
-        // ---- compute
+        // ---- compute: the wave's entries in the chunk, rows after one
+        // another, 64 to a pass, one lane each
+        int pre[kRpw], cur[kRpw], n[kRpw];
+        int total_w = 0;
+#pragma unroll
         for (int i = 0; i < kRpw; ++i) {
-            const int n = __builtin_amdgcn_readlane(my_n, i);
-            if (n == 0) continue;
-            const int cur = __builtin_amdgcn_readlane(my_cur, i);
-            const unsigned char *xr = lds + (unsigned)(wave + kWaves * i) * q.x_pitch;
-            const unsigned *tab = s_tab + i * kTab;
-            if (kNv == 0 || n >= kDkLaneMin) {
-                for (int t0 = 0; t0 < n; t0 += kWave) {
-                    if (t0 + lane < n) {
-                        const unsigned char *yr = lds + tab[t0 + lane];
-                        float acc = 0.f;
+            n[i] = __builtin_amdgcn_readlane(my_n, i);
+            cur[i] = __builtin_amdgcn_readlane(my_cur, i);
+            pre[i] = total_w;
+            total_w += n[i];
+        }
+        for (int t0 = 0; t0 < total_w; t0 += kWave) {
+            const int e = t0 + lane;
+            int ri = 0, j = 0, at = 0;
+#pragma unroll
+            for (int i = 0; i < kRpw; ++i) {
+                if (e >= pre[i] && e < pre[i] + n[i]) {
+                    ri = i;
+                    j = e - pre[i];
+                    at = cur[i] + j;
+                }
+            }
+            const bool ok = e < total_w;
+            const float v = vsrc[at];  // at = 0 for idle lanes: a valid entry
+            const float prior = psrc[at];
+            const unsigned off = s_tab[ri * kTab + j];
+            if (ok) {
+                const unsigned char *yr = lds + off;
+                const unsigned char *xr = lds + (unsigned)(wave + kWaves * ri) * q.x_pitch;
+                float acc = 0.f;
 #pragma unroll 4
-                        for (int v = 0; v < dv; ++v) {
-                            const float4 xv = *reinterpret_cast<const float4 *>(xr + v * 16);
-                            const float4 yv = *reinterpret_cast<const float4 *>(yr + v * 16);
-                            acc = fmaf(xv.x, yv.x, acc);
-                            acc = fmaf(xv.y, yv.y, acc);
-                            acc = fmaf(xv.z, yv.z, acc);
-                            acc = fmaf(xv.w, yv.w, acc);
-                        }
-                        store_entry(p, z, cur + t0 + lane, acc);
-                    }
+                for (int u = 0; u < dv; ++u) {
+                    const float4 xv = *reinterpret_cast<const float4 *>(xr + u * 16);
+                    const float4 yv = *reinterpret_cast<const float4 *>(yr + u * 16);
+                    acc = fmaf(xv.x, yv.x, acc);
+                    acc = fmaf(xv.y, yv.y, acc);
+                    acc = fmaf(xv.z, yv.z, acc);
+                    acc = fmaf(xv.w, yv.w, acc);
                 }
-            } else if constexpr (kNv > 0) {
-                // fewer than kDkLaneMin entries: one window of 16-lane groups
-                float4 xv[kNv];
-#pragma unroll
-                for (int v = 0; v < kNv; ++v)
-                    xv[v] = v * kG + gl < dv
-                                ? *reinterpret_cast<const float4 *>(xr + (v * kG + gl) * 16)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-                const int steps = (n + kNg - 1) / kNg;
-                float res = 0.f;
-                for (int s = 0; s < steps; ++s) {
-                    const int j = s * kNg + g;
-                    const unsigned char *yr = lds + tab[j < n ? j : 0];
-                    float acc = 0.f;
-#pragma unroll
-                    for (int v = 0; v < kNv; ++v) {
-                        if (v * kG + gl < dv) {
-                            const float4 yv = *reinterpret_cast<const float4 *>(yr + (v * kG + gl) * 16);
-                            acc = fmaf(xv[v].x, yv.x, acc);
-                            acc = fmaf(xv[v].y, yv.y, acc);
-                            acc = fmaf(xv[v].z, yv.z, acc);
-                            acc = fmaf(xv[v].w, yv.w, acc);
-                        }
-                    }
-                    const float sum = group_sum<kG>(acc);
-                    if (gl == s) res = sum;
-                }
-                const int jo = gl * kNg + g;  // the entry whose sum this lane kept
-                if (jo < n) store_entry(p, z, cur + jo, res);
+                float r = p.alpha * (vz ? v : 1.f) * acc;
+                if (p.beta != 0.f) r = fmaf(p.beta, prior, r);
+                oz[at] = r;
             }
         }
         my_cur += my_n;
@@ -456,32 +493,31 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
 }
 
 // Y stored d x k without a workspace, for masks that touch most columns of a
-// tile: a workgroup of four waves owns a panel of kRows consecutive row slots
-// and one tile of at most kDkTileCols consecutive columns [c0, c1) of Y, which
-// it stages whole.  All global reads are issued before the workgroup's one
-// barrier, in three dependent levels: the panel's row ids; then the tile of Y
-// (16-byte reads along Y's rows: 16 lanes cover one row of the tile, each
-// writing its 4 columns into 4 transposed LDS rows), the panel's X rows and
-// the rows' CSR bounds; then per row a 64-entry window from the row's start
-// of column indices, mask values and prior outputs.  A row's first entry at
-// or past c0 is found in that window (or, for longer rows, by a 64-way search
-// and a window read from there); its entries in the tile (at most 64) are
-// shifted to lanes 0, 1, ...  Each wave then takes its rows' entries in the
-// tile one after another, 64 to a pass: each entry gets one lane, which sums
-// its d products in l order with FMA (X and Y rows read from LDS), so lanes
-// are not left idle by rows with few entries in the tile.
+// tile: a workgroup of kWaves waves owns a panel of kRows consecutive rows and
+// one tile of at most kDkTileCols consecutive columns [c0, c1) of Y, which it
+// stages whole.  X is read once per tile and Y once per panel, so the largest
+// tiles LDS holds read the least: 64 x 64 (eight waves, one workgroup per CU)
+// for d <= 256.  Panels are runs of consecutive rows whatever the row order
+// (the order only schedules work).
+// All global reads are issued before the workgroup's one barrier, in two
+// dependent levels: the tile of Y (16-byte reads along Y's rows, each lane
+// writing its 4 columns into 4 transposed LDS rows), the rows' CSR bounds and
+// the panel's X rows; then per row a 64-entry window of column indices from
+// the row's start.  A row's first entry at or past c0 is found in that window
+// (or, for longer rows, by a 64-way search and a window read from there); its
+// entries in the tile (at most 64) are listed per wave, rows after one
+// another.  Each listed entry gets 16 lanes, 4 entries a step: lane gl sums
+// vectors gl, gl + 16, ... of the entry's X and Y rows in order with FMA (16
+// lanes read 256 contiguous bytes of one LDS row, so no bank conflicts,
+// whatever the columns), and group_sum adds the 16 partial sums.
 constexpr int kDkTileCols = 64;
 constexpr int kDkTileYBatch = 16;  // Y vectors per thread per batch (d <= 256: one batch)
 
-template <int kNv, bool kVec>
-__global__ __launch_bounds__(4 * kWave) void sddmm_dk_tile_kernel(SddmmParams p, DkPanelParams q)
+template <int kRows, int kWaves, int kNv, bool kVec>
+__global__ __launch_bounds__(kWaves * kWave) void sddmm_dk_tile_kernel(SddmmParams p, DkPanelParams q)
 {
-    using S = DkShape<kNv>;
-    constexpr int kRows = S::kRows;
-    constexpr int kWaves = 4;
     constexpr int kThreads = kWaves * kWave;
     constexpr int kRpw = kRows / kWaves;
-    constexpr int kXItems = 8;  // X vectors per thread per batch
     extern __shared__ __align__(16) unsigned char lds[];
 
     const long long units = (long long)q.panels * q.splits;  // splits = tiles per panel
@@ -499,19 +535,16 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_tile_kernel(SddmmParams p,
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int dv = (p.d + 3) / 4;
-    const int dl = 4 * dv;                 // staged elements per row (d padded)
     const int cq = (c1 - c0 + 3) / 4;      // column quads in the tile (<= 16)
 
     const float *__restrict__ xz = static_cast<const float *>(p.x) + z * p.stride_x;
     const float *__restrict__ yz = static_cast<const float *>(p.y) + z * p.stride_y;
     const int *__restrict__ ci = p.col_indices;
-    // row id of panel row r, read from a valid stand-in array when there is
-    // no row order (row_offsets has m + 1 entries)
-    const int *rsrc = p.row_indices ? p.row_indices : p.row_offsets;
-    auto row_of = [&](int r) {
-        const int v = rsrc[slot0 + r];
-        return p.row_indices ? v : slot0 + r;
-    };
+    // Panels are runs of consecutive rows whatever the row order: the order
+    // only schedules work (results do not depend on it), and tiles whose
+    // columns are mostly touched need no balancing, so the row ids cost no
+    // read.
+    auto row_of = [&](int r) { return slot0 + r; };
 
     // Every load below is unconditional and from a valid address: surplus
     // items repeat the last item (loading and storing the same value again),
@@ -519,21 +552,11 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_tile_kernel(SddmmParams p,
     // branch, or one the compiler turns into a branch, makes it wait for every
     // load in flight where the branches join, which would serialise the
     // levels.)
-    // ---- level 1: row ids of this wave's rows (lane i < kRpw: row wave + 4 i)
-    // and of the X rows this thread stages (thread -> vector tid % dvp of rows
-    // tid / dvp + u * (256 / dvp), dvp = 2^q.x_shift >= dv)
+    // this wave's rows (lane i < kRpw: row wave + 4 i)
     const int my_r = wave + kWaves * lane;
     const bool my_ok = lane < kRpw && my_r < nrows;
     const int my_row = row_of(my_ok ? my_r : 0);
-    const int xsh = q.x_shift;
-    const int xv_i = min(tid & ((1 << xsh) - 1), dv - 1);
-    const int xr0 = tid >> xsh;
-    const int xstep = kThreads >> xsh;
-    int xrow[kXItems];
-#pragma unroll
-    for (int u = 0; u < kXItems; ++u) xrow[u] = row_of(min(xr0 + u * xstep, nrows - 1));
-    __builtin_amdgcn_sched_barrier(0);  // issue each level's loads together
-    // ---- level 2a: the tile of Y: item i -> element row l = i / cq, column
+    // ---- level 1a: the tile of Y: item i -> element row l = i / cq, column
     // quad i % cq; i / cq as (i * ceil(2^20 / cq)) >> 20, exact for
     // i < 2^14 and cq <= 16 (the error stays below 1/64 < 1/cq)
     const int ny = p.d * cq;  // items
@@ -573,50 +596,22 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_tile_kernel(SddmmParams p,
 #pragma unroll
     for (int u = 0; u < kDkTileYBatch; ++u) yb[u] = load_y(u * kThreads + tid);
     __builtin_amdgcn_sched_barrier(0);
-    // ---- level 2b: this wave's CSR bounds, then the panel's X rows
-    auto load_x = [&](int row) {
-        const int e = 4 * xv_i;
-        const float *src = xz + (size_t)row * (size_t)p.d + e;
-        float4 v;
-        if constexpr (kVec) {  // d % 4 == 0
-            v = *reinterpret_cast<const float4 *>(src);
-        } else {
-            const int last = p.d - 1 - e;  // >= 0
-            v.x = src[0];
-            v.y = src[min(1, last)];
-            v.z = src[min(2, last)];
-            v.w = src[min(3, last)];
-        }
-        return v;
-    };
+    // ---- level 1b: this wave's CSR bounds, then the panel's X rows
     int my_start = p.row_offsets[my_row];
     int my_end = p.row_offsets[my_row + 1];
     __builtin_amdgcn_sched_barrier(0);
-    float4 xb[kXItems];
-#pragma unroll
-    for (int u = 0; u < kXItems; ++u) xb[u] = load_x(xrow[u]);
-    __builtin_amdgcn_sched_barrier(0);
+    dk_stage_x<kThreads, kVec>(p, xz, nrows, q.x_shift, q.x_pitch, lds, row_of);
     if (!my_ok) my_start = my_end = 0;
-    // ---- level 3: per row, the 64-entry window from its start (mask values
-    // and prior outputs read from a valid stand-in array when absent)
-    const float *__restrict__ vz = p.mask_values ? p.mask_values + z * p.stride_values : nullptr;
-    float *__restrict__ oz = p.out + z * p.stride_out;
-    const float *vsrc = vz ? vz : reinterpret_cast<const float *>(ci);
-    const float *psrc = p.beta != 0.f ? oz : reinterpret_cast<const float *>(ci);
+    // ---- level 2: per row, the 64-entry window of column indices from its
+    // start
     int win[kRpw];
-    float mvw[kRpw], prw[kRpw];
 #pragma unroll
     for (int i = 0; i < kRpw; ++i) {
         const int s = __builtin_amdgcn_readlane(my_start, i);
         const int e = __builtin_amdgcn_readlane(my_end, i);
         const bool in = lane < e - s;
-        const int at = in ? s + lane : 0;  // nnz > 0 here, so entry 0 exists
-        const int c = ci[at];
-        const float mvv = vsrc[at];
-        const float prv = psrc[at];
+        const int c = ci[in ? s + lane : 0];  // nnz > 0 here, so entry 0 exists
         win[i] = in ? c : INT_MAX;
-        mvw[i] = vz ? mvv : 1.f;
-        prw[i] = p.beta != 0.f ? prv : 0.f;
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- stage Y (more batches when d * cq > 16 * 256) and its zero rows
@@ -629,40 +624,19 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_tile_kernel(SddmmParams p,
 #pragma unroll
         for (int u = 0; u < kDkTileYBatch; ++u) store_y(i0 + u * kThreads + tid, yb[u]);
     }
-    for (int i = tid; i < (dl - p.d) * 4 * cq; i += kThreads) {
-        const int c = i / (dl - p.d), l = p.d + (i - c * (dl - p.d));
-        reinterpret_cast<float *>(lds + q.off_y + (unsigned)c * q.y_pitch)[l] = 0.f;
-    }
-    // ---- stage X (zero beyond d: the loads repeat element d - 1)
-#pragma unroll
-    for (int u = 0; u < kXItems; ++u) {
-        const int r = min(xr0 + u * xstep, nrows - 1);
-        float4 v = xb[u];
-        if constexpr (!kVec) {
-            const int e = 4 * xv_i;
-            if (e + 1 >= p.d) v.y = 0.f;
-            if (e + 2 >= p.d) v.z = 0.f;
-            if (e + 3 >= p.d) v.w = 0.f;
-        }
-        *reinterpret_cast<float4 *>(lds + (unsigned)r * q.x_pitch + (unsigned)xv_i * 16u) = v;
-    }
-    for (int r0 = kXItems * xstep; r0 < nrows; r0 += kXItems * xstep) {  // more rows than one batch
-        for (int u = 0; u < kXItems; ++u) {
-            const int r = min(r0 + xr0 + u * xstep, nrows - 1);
-            float4 v = load_x(row_of(r));
-            if constexpr (!kVec) {
-                const int e = 4 * xv_i;
-                if (e + 1 >= p.d) v.y = 0.f;
-                if (e + 2 >= p.d) v.z = 0.f;
-                if (e + 3 >= p.d) v.w = 0.f;
-            }
-            *reinterpret_cast<float4 *>(lds + (unsigned)r * q.x_pitch + (unsigned)xv_i * 16u) = v;
-        }
+    // zero rows l in [d, 64 kNv) of the staged columns, and the same elements
+    // of the staged X rows (the 16-lane groups read whole groups of vectors)
+    constexpr int kPad = 64 * kNv;  // staged elements per row
+    for (int i = tid; i < (kPad - p.d) * (4 * cq + kRows); i += kThreads) {
+        const int c = i / (kPad - p.d), l = p.d + (i - c * (kPad - p.d));
+        float *row = c < 4 * cq
+                         ? reinterpret_cast<float *>(lds + q.off_y + (unsigned)c * q.y_pitch)
+                         : reinterpret_cast<float *>(lds + (unsigned)(c - 4 * cq) * q.x_pitch);
+        row[l] = 0.f;
     }
     // ---- each row's entries in the tile: base (first entry >= c0), count,
-    // and per lane j < count entry j's column, mask value and prior output
+    // and per lane j < count entry j's column
     int base[kRpw], cnt[kRpw], colt[kRpw];
-    float mv[kRpw], pr[kRpw];
 #pragma unroll
     for (int i = 0; i < kRpw; ++i) {
         const int s = __builtin_amdgcn_readlane(my_start, i);
@@ -675,8 +649,6 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_tile_kernel(SddmmParams p,
             const int src = min(lane + below, kWave - 1);
             base[i] = s + below;
             colt[i] = __shfl(win[i], src);
-            mv[i] = __shfl(mvw[i], src);
-            pr[i] = __shfl(prw[i], src);
             if (lane + below >= kWave) colt[i] = INT_MAX;
             cnt[i] = (int)__popcll(__builtin_amdgcn_ballot_w64(win[i] >= c0 && win[i] < c1));
         } else {
@@ -700,67 +672,98 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_tile_kernel(SddmmParams p,
             }
             base[i] = b;
             const bool in = lane < e - b;
-            const int at = in ? b + lane : 0;
-            const int cr = ci[at];
-            const float mvv = vsrc[at];
-            const float prv = psrc[at];
+            const int cr = ci[in ? b + lane : 0];
             const int c = in ? cr : INT_MAX;
             colt[i] = c < c1 ? c : INT_MAX;
             cnt[i] = (int)__popcll(__builtin_amdgcn_ballot_w64(c < c1));
-            mv[i] = vz ? mvv : 1.f;
-            pr[i] = p.beta != 0.f ? prv : 0.f;
         }
     }
-    __syncthreads();
-    // ---- compute: the wave's entries in the tile, rows after one another,
-    // 64 to a pass, one lane each
+    // epilogue operands, read from a valid stand-in array when absent
+    const float *__restrict__ vz = p.mask_values ? p.mask_values + z * p.stride_values : nullptr;
+    float *__restrict__ oz = p.out + z * p.stride_out;
+    const float *vsrc = vz ? vz : reinterpret_cast<const float *>(ci);
+    const float *psrc = p.beta != 0.f ? oz : reinterpret_cast<const float *>(ci);
+    // ---- the wave's entries in the tile, rows after one another: list entry
+    // e = pre[i] + j is row i's j-th, coded (row << 6) | (column - c0)
+    unsigned short *s_list =
+        reinterpret_cast<unsigned short *>(lds + q.off_tab) + wave * (kRpw * kWave);
     int pre[kRpw];
     int total = 0;
 #pragma unroll
     for (int i = 0; i < kRpw; ++i) {
         pre[i] = total;
         total += cnt[i];
-    }
-    for (int t0 = 0; t0 < total; t0 += kWave) {
-        const int e = t0 + lane;
-        // entry e's row i (the last row starting at or before e) and its
-        // column, mask value, prior output and position, gathered from the
-        // lanes that hold them (cross-lane reads with every lane active)
-        int col = INT_MAX, at = 0, xrow = 0;
-        float v = 1.f, prior = 0.f;
-#pragma unroll
-        for (int i = 0; i < kRpw; ++i) {
-            if (cnt[i] == 0 || pre[i] >= t0 + kWave || pre[i] + cnt[i] <= t0) continue;
-            const int j = min(max(e - pre[i], 0), kWave - 1);
-            const int ci_ = __shfl(colt[i], j);
-            const float mv_ = __shfl(mv[i], j);
-            const float pr_ = __shfl(pr[i], j);
-            if (e >= pre[i] && e < pre[i] + cnt[i]) {
-                col = ci_;
-                v = mv_;
-                prior = pr_;
-                at = base[i] + (e - pre[i]);
-                xrow = wave + kWaves * i;
-            }
-        }
-        if (e < total) {
+        if (lane < cnt[i]) {
             // (columns ascend within a row; the range check only keeps LDS
             // reads in bounds for input that breaks that)
-            const unsigned rel = (unsigned)(col - c0);
-            const unsigned char *yr =
-                lds + q.off_y + (rel < (unsigned)(c1 - c0) ? rel : 0u) * q.y_pitch;
-            const unsigned char *xr = lds + (unsigned)xrow * q.x_pitch;
-            float acc = 0.f;
-#pragma unroll 4
-            for (int u = 0; u < dv; ++u) {
-                const float4 xv = *reinterpret_cast<const float4 *>(xr + u * 16);
-                const float4 yv = *reinterpret_cast<const float4 *>(yr + u * 16);
-                acc = fmaf(xv.x, yv.x, acc);
-                acc = fmaf(xv.y, yv.y, acc);
-                acc = fmaf(xv.z, yv.z, acc);
-                acc = fmaf(xv.w, yv.w, acc);
+            const unsigned rel = (unsigned)(colt[i] - c0);
+            s_list[pre[i] + lane] = (unsigned short)((i << 6) | (rel < (unsigned)(c1 - c0) ? rel : 0u));
+        }
+    }
+    // ---- compute: 64 list entries per pass, 16 lanes per entry (4 entries a
+    // step): lane gl of a group sums vectors gl, gl + 16, ... of the X and Y
+    // rows in order with FMA (16 lanes read 256 contiguous bytes of one row:
+    // no bank conflicts), group_sum adds the 16 partial sums, and lane
+    // (g, gl) keeps the sum of step gl, entry t0 + 4 gl + g, which it writes.
+    constexpr int kG = 16, kNg = kWave / kG;
+    const int g = lane / kG;
+    const int gl = lane - g * kG;
+    // the position of list entry e, and its epilogue operands
+    auto position = [&](int e) {
+        int at = 0;
+#pragma unroll
+        for (int i = 0; i < kRpw; ++i)
+            if (e >= pre[i] && e < pre[i] + cnt[i]) at = base[i] + (e - pre[i]);
+        return at;
+    };
+    // the first pass's operands are read before the barrier, which waits
+    // only for LDS: their latency overlaps it and the first steps
+    int at = position(gl * kNg + g);
+    float v = vsrc[at];
+    float prior = psrc[at];
+    __syncthreads();
+    for (int t0 = 0; t0 < total; t0 += kWave) {
+        const int live = min(kWave, total - t0);
+        const int eo = t0 + gl * kNg + g;  // the entry this lane writes
+        if (t0 > 0) {
+            at = position(eo);
+            v = vsrc[at];
+            prior = psrc[at];
+        }
+        const int steps = (live + kNg - 1) / kNg;
+        float kept = 0.f;
+        // two steps at a time (one for kNv > 4, for registers), so that their
+        // LDS reads overlap
+        constexpr int kH = kNv <= 4 ? 2 : 1;
+        for (int st = 0; st < steps; st += kH) {
+            float4 xv[kH][kNv], yv[kH][kNv];
+#pragma unroll
+            for (int h = 0; h < kH; ++h) {
+                const unsigned code = s_list[min(t0 + (st + h) * kNg + g, total - 1)];
+                const unsigned char *xr = lds + (unsigned)(wave + kWaves * (int)(code >> 6)) * q.x_pitch;
+                const unsigned char *yr = lds + q.off_y + (code & 63u) * q.y_pitch;
+#pragma unroll
+                for (int u = 0; u < kNv; ++u) {
+                    xv[h][u] = *reinterpret_cast<const float4 *>(xr + (u * kG + gl) * 16);
+                    yv[h][u] = *reinterpret_cast<const float4 *>(yr + (u * kG + gl) * 16);
+                }
             }
-            float r = p.alpha * v * acc;
+#pragma unroll
+            for (int h = 0; h < kH; ++h) {
+                float acc = 0.f;
+#pragma unroll
+                for (int u = 0; u < kNv; ++u) {
+                    acc = fmaf(xv[h][u].x, yv[h][u].x, acc);
+                    acc = fmaf(xv[h][u].y, yv[h][u].y, acc);
+                    acc = fmaf(xv[h][u].z, yv[h][u].z, acc);
+                    acc = fmaf(xv[h][u].w, yv[h][u].w, acc);
+                }
+                const float sum = group_sum<kG>(acc);
+                if (gl == st + h) kept = sum;  // (a step past the last holds no entry this lane writes)
+            }
+        }
+        if (eo < total) {
+            float r = p.alpha * (vz ? v : 1.f) * kept;
             if (p.beta != 0.f) r = fmaf(p.beta, prior, r);
             oz[at] = r;
         }
@@ -893,128 +896,122 @@ inline bool aligned16(const void *ptr)
     return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0;
 }
 
-template <int kNv>
-hipError_t launch_dk_t(const SddmmParams &p, const DkPanelParams &q, hipStream_t s)
+// waves: the kernel's workgroup size in waves (its launch bound)
+template <class Kernel>
+hipError_t launch_dk_fn(Kernel fn, int waves, const SddmmParams &p, const DkPanelParams &q,
+                        hipStream_t s)
 {
-    const auto fn = sddmm_dk_panel_kernel<kNv>;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)q.lds);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)xcd_grid(p.batch, (long long)q.panels * q.splits));
-    hipLaunchKernelGGL(fn, grid, dim3(4 * kWave), q.lds, s, p, q);
-    return hipGetLastError();
-}
-
-template <int kNv, bool kVec>
-hipError_t launch_dk_tile_t(const SddmmParams &p, const DkPanelParams &q, hipStream_t s)
-{
-    const auto fn = sddmm_dk_tile_kernel<kNv, kVec>;
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)q.lds);
-    if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)xcd_grid(p.batch, (long long)q.panels * q.splits));
-    hipLaunchKernelGGL(fn, grid, dim3(4 * kWave), q.lds, s, p, q);
+    hipLaunchKernelGGL(fn, grid, dim3(waves * kWave), q.lds, s, p, q);
     return hipGetLastError();
 }
 
 template <bool kVec>
-hipError_t launch_dk_tile_v(const SddmmParams &p, const DkPanelParams &q, hipStream_t s)
+hipError_t launch_dk_v(bool tile, const SddmmParams &p, const DkPanelParams &q, hipStream_t s)
 {
-    switch (q.nv) {
-    case 1: return launch_dk_tile_t<1, kVec>(p, q, s);
-    case 2: return launch_dk_tile_t<2, kVec>(p, q, s);
-    case 4: return launch_dk_tile_t<4, kVec>(p, q, s);
-    case 8: return launch_dk_tile_t<8, kVec>(p, q, s);
-    default: return launch_dk_tile_t<0, kVec>(p, q, s);
+    if (tile) {
+        switch (q.nv) {
+        case 1: return launch_dk_fn(sddmm_dk_tile_kernel<64, 8, 1, kVec>, 8, p, q, s);
+        case 2: return launch_dk_fn(sddmm_dk_tile_kernel<64, 8, 2, kVec>, 8, p, q, s);
+        case 4: return launch_dk_fn(sddmm_dk_tile_kernel<64, 8, 4, kVec>, 8, p, q, s);
+        case 8: return launch_dk_fn(sddmm_dk_tile_kernel<16, 4, 8, kVec>, 4, p, q, s);
+        default: return launch_dk_fn(sddmm_dk_tile_kernel<8, 4, 16, kVec>, 4, p, q, s);
+        }
+    }
+    switch (q.rows * 4 + q.rounds) {
+    case 32 * 4 + 2: return launch_dk_fn(sddmm_dk_panel_kernel<32, 2, kVec>, 4, p, q, s);
+    case 32 * 4 + 1: return launch_dk_fn(sddmm_dk_panel_kernel<32, 1, kVec>, 4, p, q, s);
+    case 16 * 4 + 1: return launch_dk_fn(sddmm_dk_panel_kernel<16, 1, kVec>, 4, p, q, s);
+    default: return launch_dk_fn(sddmm_dk_panel_kernel<8, 1, kVec>, 4, p, q, s);
     }
 }
 
-hipError_t launch_dk_tile(const SddmmParams &p, const DkPanelParams &q, bool vec, hipStream_t s)
+hipError_t launch_dk(bool tile, const SddmmParams &p, const DkPanelParams &q, bool vec,
+                     hipStream_t s)
 {
-    return vec ? launch_dk_tile_v<true>(p, q, s) : launch_dk_tile_v<false>(p, q, s);
-}
-
-hipError_t launch_dk(const SddmmParams &p, const DkPanelParams &q, hipStream_t s)
-{
-    switch (q.nv) {
-    case 1: return launch_dk_t<1>(p, q, s);
-    case 2: return launch_dk_t<2>(p, q, s);
-    case 4: return launch_dk_t<4>(p, q, s);
-    case 8: return launch_dk_t<8>(p, q, s);
-    default: return launch_dk_t<0>(p, q, s);
-    }
+    return vec ? launch_dk_v<true>(tile, p, q, s) : launch_dk_v<false>(tile, p, q, s);
 }
 
 // LDS per workgroup of the d x k panel kernel: two workgroups per CU.
 constexpr unsigned kDkLdsBudget = 76u * 1024u;
 constexpr int kDkTargetGroups = 512;  // workgroups wanted before splitting Y's columns
 constexpr double kDkTileDensity = 0.05;  // mean mask density from which the tile kernel runs
+constexpr unsigned kDkTileLdsBudget = 150u * 1024u;  // 64-row tiles: one workgroup per CU
 
-// The d x k panel kernel's shape for fp32 operands, or false when LDS cannot
-// hold a useful chunk (d beyond about 1000) or the launch would be too large.
+// The shape of the d x k kernels for fp32 operands, or false when they do not
+// apply (d beyond 1024, or LDS cannot hold a useful chunk).  Masks of mean
+// density 1/20 or more (few columns of a 32-row tile untouched) take the tile
+// kernel, one tile per workgroup; sparser ones the panel kernel.
 bool plan_dk_panel(const SddmmArgs &a, SddmmPlan *plan)
 {
     if (a.dtype != Dtype::f32 || a.d <= 0 || a.k <= 0 || a.softmax) return false;
     const int dv = (a.d + 3) / 4;  // 16-byte vectors per staged row
+    if (dv > 256) return false;
     DkPanelParams &q = plan->dk;
-    q.nv = dv <= 16 ? 1 : dv <= 32 ? 2 : dv <= 64 ? 4 : dv <= 128 ? 8 : 0;
-    int rounds = 1;
-    switch (q.nv) {  // DkShape's rows and windows per row
-    case 1: q.rows = DkShape<1>::kRows; rounds = DkShape<1>::kRounds; break;
-    case 2: q.rows = DkShape<2>::kRows; rounds = DkShape<2>::kRounds; break;
-    case 4: q.rows = DkShape<4>::kRows; rounds = DkShape<4>::kRounds; break;
-    case 8: q.rows = DkShape<8>::kRows; rounds = DkShape<8>::kRounds; break;
-    default: q.rows = DkShape<0>::kRows; rounds = DkShape<0>::kRounds; break;
-    }
+    q.rows = dk_rows(dv);
+    q.rounds = dk_rounds(dv);
     q.x_pitch = q.y_pitch = 16u * ((unsigned)dv | 1u);  // an odd number of 16-byte units
-    const unsigned tab = (unsigned)q.rows * (unsigned)rounds * kWave * 4u;
-    const unsigned tables = tab + 2u * 1024u + 1024u + 1024u + 64u;
-    const unsigned fixed = (unsigned)q.rows * q.x_pitch + tables;
-    if (fixed >= kDkLdsBudget) return false;
-    // Masks that touch most columns of a tile (a mean density of 1/20 or more
-    // leaves few columns of a 32-row tile untouched) take the dense-tile
-    // kernel, one tile per workgroup; sparser ones the panel kernel.
+    q.x_shift = 0;
+    while ((1 << q.x_shift) < dv) ++q.x_shift;  // X's vectors per row, to a power of 2
+    q.panels = (a.m + q.rows - 1) / q.rows;
+    const unsigned xbytes = (unsigned)q.rows * q.x_pitch;
+    const bool xvec = a.d % 4 == 0 && aligned16(a.x) && a.stride_x % 4 == 0;
     const double density = (double)a.nnz / ((double)a.m * (double)a.k);
-    if (density >= kDkTileDensity && dv <= 256) {
-        const unsigned xbytes = (unsigned)q.rows * q.x_pitch;
-        if (xbytes < kDkLdsBudget) {
-            const int kc = (int)std::min<unsigned>(kDkTileCols, (kDkLdsBudget - xbytes) / q.y_pitch) & ~3;
-            if (kc >= 8) {
-                q.kc = kc;
-                q.panels = (a.m + q.rows - 1) / q.rows;
-                q.splits = (a.k + kc - 1) / kc;
-                if (xcd_grid(a.batch, (long long)q.panels * q.splits) <= 0x7fffffffLL) {
-                    q.x_shift = 0;
-                    while ((1 << q.x_shift) < dv) ++q.x_shift;  // X vectors per row, to a power of 2
-
-                    q.off_y = xbytes;
-                    q.lds = xbytes + (unsigned)kc * q.y_pitch;
-                    // 16-byte reads of X and Y rows: d % 4 == 0, k % 4 == 0, aligned
-                    plan->vec = a.d % 4 == 0 && a.k % 4 == 0 && aligned16(a.x) && aligned16(a.y) &&
-                                a.stride_x % 4 == 0 && a.stride_y % 4 == 0;
-                    plan->kind = SddmmPlan::kDkTile;
-                    return true;
-                }
+    if (density >= kDkTileDensity) {
+        // 64 x 64 tiles with eight waves when LDS holds them (d <= 256), else
+        // the panel kernel's heights with four waves and the widest tile
+        // that leaves room for two workgroups per CU
+        // 16 lanes per entry read kNv vectors each: rows padded to 16 kNv
+        // vectors (and one more, so that a pitch is an odd number of 16 bytes)
+        q.nv = dv <= 16 ? 1 : dv <= 32 ? 2 : dv <= 64 ? 4 : dv <= 128 ? 8 : 16;
+        q.rows = q.nv <= 4 ? 64 : q.nv == 8 ? 16 : 8;
+        q.x_pitch = q.y_pitch = 16u * (16u * (unsigned)q.nv + 1u);
+        const unsigned xb = (unsigned)q.rows * q.x_pitch;
+        const unsigned list = (unsigned)q.rows * kWave * 2u;
+        const unsigned budget = q.rows == 64 ? kDkTileLdsBudget : kDkLdsBudget;
+        int kc = xb + list < budget
+                     ? (int)std::min<unsigned>(kDkTileCols, (budget - xb - list) / q.y_pitch) & ~3
+                     : 0;
+        q.panels = (a.m + q.rows - 1) / q.rows;
+        if (kc >= 8) {
+            q.kc = kc;
+            q.splits = (a.k + kc - 1) / kc;
+            if (xcd_grid(a.batch, (long long)q.panels * q.splits) <= 0x7fffffffLL) {
+                q.off_y = xb;
+                q.off_tab = xb + (unsigned)kc * q.y_pitch;  // per-wave entry lists
+                q.lds = q.off_tab + (unsigned)q.rows * kWave * 2u;
+                // 16-byte reads of X and Y rows
+                plan->vec = xvec && a.k % 4 == 0 && aligned16(a.y) && a.stride_y % 4 == 0;
+                plan->kind = SddmmPlan::kDkTile;
+                return true;
             }
         }
     }
+    q.rows = dk_rows(dv);
+    q.x_pitch = q.y_pitch = 16u * ((unsigned)dv | 1u);
+    q.panels = (a.m + q.rows - 1) / q.rows;
+    const unsigned tab = (unsigned)q.rows * (unsigned)q.rounds * kWave * 4u;
+    const unsigned fixed = xbytes + tab + 2u * 1024u + 1024u + 1024u + 64u;
+    if (fixed >= kDkLdsBudget) return false;
     q.kc = (int)std::min<unsigned>(256u, (kDkLdsBudget - fixed) / q.y_pitch);
     if (q.kc < 8) return false;
-    q.panels = (a.m + q.rows - 1) / q.rows;
     const long long units = (long long)a.batch * q.panels;
     const long long want = (kDkTargetGroups + units - 1) / units;
     const long long most = std::max<long long>(1, a.k / (2LL * q.kc));
     q.splits = (int)std::max<long long>(1, std::min(want, most));
     if (xcd_grid(a.batch, (long long)q.panels * q.splits) > 0x7fffffffLL) return false;
-    q.off_y = (unsigned)q.rows * q.x_pitch;
+    q.off_y = xbytes;
     q.off_tab = q.off_y + (unsigned)q.kc * q.y_pitch;
     q.off_bits = q.off_tab + tab;
     q.off_rank = q.off_bits + 2u * 1024u;
     q.off_col = q.off_rank + 1024u;
     q.off_misc = q.off_col + 1024u;
     q.lds = q.off_misc + 64u;
+    plan->vec = xvec;
     plan->kind = SddmmPlan::kDkPanel;
     return true;
 }
@@ -1145,9 +1142,9 @@ hipError_t run_sddmm(const SddmmPlan &plan, hipStream_t stream)
         return hipSuccess;
     }
     case SddmmPlan::kDkPanel:
-        return launch_dk(p, plan.dk, stream);
+        return launch_dk(false, p, plan.dk, plan.vec, stream);
     case SddmmPlan::kDkTile:
-        return launch_dk_tile(p, plan.dk, plan.vec, stream);
+        return launch_dk(true, p, plan.dk, plan.vec, stream);
     case SddmmPlan::kCols:
         switch (plan.dtype) {
         case Dtype::f16: return launch_cols<_Float16>(plan.buf, p, stream);

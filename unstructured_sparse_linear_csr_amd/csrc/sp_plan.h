@@ -27,8 +27,9 @@ struct SpmmPlan {
 // touched columns at a time; byte offsets of the dynamic LDS regions.
 struct DkPanelParams {
     int rows, kc, splits, panels;
-    int nv;  // vectors per lane of the 16-lane path (0: one lane per entry only)
-    int x_shift;  // tile kernel: log2 of X's vectors per row rounded up to a power of 2
+    int rounds;  // panel kernel: 64-entry windows per row per chunk
+    int nv;      // tile kernel: vectors per lane of a 16-lane group
+    int x_shift;  // log2 of X's vectors per row rounded up to a power of 2
     unsigned x_pitch, y_pitch;  // LDS bytes per staged X row / Y column
     unsigned off_y, off_tab, off_bits, off_rank, off_col, off_misc;
     unsigned lds;
