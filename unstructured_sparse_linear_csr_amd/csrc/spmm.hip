@@ -460,36 +460,51 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
 
     const int *__restrict__ order = p.row_indices;
     const int *__restrict__ offsets = p.row_offsets;
-    float *__restrict__ c_out = p.c + col_base;
     const int stride = groups * kLdsWaves;
-    const int first = group * kLdsWaves + tid / kWave;
+    // wave-uniform (scalar), so that every branch on the rows is a scalar one
+    const int first = __builtin_amdgcn_readfirstlane(group * kLdsWaves + tid / kWave);
     if (first >= p.m) return;  // no LDS barrier follows
     const int rows_of_wave = (p.m - first + stride - 1) / stride;
 
     int meta_row = 0, meta_p0 = 0, meta_p1 = 0, meta_base = 0;
+    // Row metadata of 64 of the wave's rows, one per lane; the loads are
+    // unconditional, from valid addresses (row_offsets stands in for a missing
+    // row order), so no branch surrounds them.
     auto load_meta = [&](int t0) {
         const int t = t0 + lane;
-        const int sl = first + t * stride;
         const bool ok = t < rows_of_wave;
-        meta_row = ok ? (order ? order[sl] : sl) : 0;
-        meta_p0 = ok ? offsets[meta_row] : 0;
-        meta_p1 = ok ? offsets[meta_row + 1] : 0;
-        meta_base = t0;
+        const int sl = ok ? first + t * stride : first;
+        const int o = (order ? order : offsets)[sl];
+        const int row = order ? o : sl;
+        const int q0 = offsets[row];
+        const int q1 = offsets[row + 1];
+        meta_row = ok ? row : 0;
+        meta_p0 = ok ? q0 : 0;
+        meta_p1 = ok ? q1 : 0;
+        meta_base = __builtin_amdgcn_readfirstlane(t0);
     };
     struct Batch {
         int t, row, p0, p1, base;  // base: first entry of the batch (a multiple of 4)
+    };
+    // Batch fields are wave-uniform (scalar registers), so the choices below
+    // are scalar branches: a divergent branch around the metadata loads would
+    // make the compiler wait for every load in flight where it joins.
+    auto uniform = [](Batch b) -> Batch {
+        return {__builtin_amdgcn_readfirstlane(b.t), __builtin_amdgcn_readfirstlane(b.row),
+                __builtin_amdgcn_readfirstlane(b.p0), __builtin_amdgcn_readfirstlane(b.p1),
+                __builtin_amdgcn_readfirstlane(b.base)};
     };
     auto row_batch = [&](int t) -> Batch {
         if (t - meta_base >= kWave) load_meta(t);
         const int j = t - meta_base;
         const int p0 = __builtin_amdgcn_readlane(meta_p0, j);
-        return {t, __builtin_amdgcn_readlane(meta_row, j), p0,
-                __builtin_amdgcn_readlane(meta_p1, j), p0 & ~3};
+        return uniform({t, __builtin_amdgcn_readlane(meta_row, j), p0,
+                        __builtin_amdgcn_readlane(meta_p1, j), p0 & ~3});
     };
     auto next_of = [&](const Batch &cur) -> Batch {
         if (cur.base + kBatch < cur.p1)
-            return {cur.t, cur.row, cur.p0, cur.p1, cur.base + kBatch};
-        if (cur.t + 1 >= rows_of_wave) return {rows_of_wave, -1, 0, 0, 0};  // empty
+            return uniform({cur.t, cur.row, cur.p0, cur.p1, cur.base + kBatch});
+        if (cur.t + 1 >= rows_of_wave) return uniform({rows_of_wave, -1, 0, 0, 0});  // empty
         return row_batch(cur.t + 1);
     };
 
@@ -567,14 +582,35 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
     float acc[kVec];
 #pragma unroll
     for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
+    // C is written through a buffer resource: a lane that does not hold the
+    // row's sum stores to an out-of-range offset, which the hardware drops.
+    // A store under a branch would leave the compiler unsure how many memory
+    // operations are in flight, and it would then wait for all of them at
+    // the top of every batch, draining the loads kept in flight.
+    const __amdgpu_buffer_rsrc_t rcs =
+        __builtin_amdgcn_make_buffer_rsrc(p.c, 0, (int)p.c_bytes, 0x00020000);
     auto finish_row = [&](int r) {
 #pragma unroll
         for (int t = 0; t < kVec; ++t) acc[t] = strided_wave_sum<kE>(acc[t]);
-        if (s == 0 && col_ok) V::store(c_out + (size_t)r * (size_t)p.n + col0, acc);
+        const unsigned off =
+            s == 0 && col_ok ? (unsigned)(((size_t)r * (size_t)p.n + col_base + col0) * 4u)
+                             : kOutOfRange;
+        if constexpr (kVec == 1) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[0]), rcs, (int)off, 0, 0);
+        } else {
+#pragma unroll
+            for (int h = 0; h < kVec / 4; ++h) {
+                const unsigned v4 __attribute__((ext_vector_type(4))) = {
+                    __float_as_uint(acc[4 * h]), __float_as_uint(acc[4 * h + 1]),
+                    __float_as_uint(acc[4 * h + 2]), __float_as_uint(acc[4 * h + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(v4, rcs, (int)(off + 16u * h), 0, 0);
+            }
+        }
 #pragma unroll
         for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
     };
 
+    meta_base = __builtin_amdgcn_readfirstlane(meta_base);
     load_meta(0);
     Batch cur = row_batch(0);
     Seg sa[kSteps], sb[kSteps];
@@ -861,8 +897,11 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
         const int slices = slice_v > 0 ? (int)((lds_nv + slice_v - 1) / slice_v) : 0;
         if (slices > 0) slice_v = (lds_nv + slices - 1) / slices;
         const int groups = slices > 1 ? cus / slices / 8 * 8 : cus;
+        const long long c_bytes = (long long)a.m * a.n * 4;  // C through a buffer resource
         if (a.batch == 1 && cus > 0 && vec_csr && a.nnz >= 4 && slices > 0 && groups > 0 &&
+            c_bytes < (1LL << 31) &&
             (long long)a.nnz >= (long long)groups * a.k * slice_v * lds_kvec) {
+            p.c_bytes = (unsigned)c_bytes;
             const long long want = ((long long)a.m + kLdsWaves - 1) / kLdsWaves;
             long long g = want < groups ? want : groups;
             if (slices > 1) g = (g + 7) / 8 * 8;  // whole XCD rounds

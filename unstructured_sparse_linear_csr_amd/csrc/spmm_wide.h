@@ -54,6 +54,7 @@ struct SpmmParams {
     int m, n, nnz, row_blocks, tiles, batch;
     unsigned b_bytes;    // bytes of one B operand (buffer path)
     unsigned csr_bytes;  // bytes of col_indices (= of one values array), narrow kernel
+    unsigned c_bytes;    // LDS kernel: bytes of C (stored through a buffer resource)
     // LDS kernel: B's columns in slices of lds_slice_n, one slice per
     // workgroup (lds_slices = 1: all of B); k = rows of B
     int k, lds_slices, lds_slice_n;
