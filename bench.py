@@ -107,7 +107,8 @@ def parse_args():
                     help="with --profile-launches: comma-separated workloads to launch -- "
                          "ffn (the step's kernels), resnet, lstm90, lstm50, attention; "
                          "resnet_wide, lstm50_wide: the same SpMM as a 2-entry batch, "
-                         "which takes the wide kernel")
+                         "which takes the wide kernel; stream8: the streaming-regime "
+                         "SpMM with B 8 columns wide (two column slices)")
     ap.add_argument("--profile-cold", action="store_true",
                     help="with --profile-launches: write a 1 GiB buffer before every "
                          "launch, so the byte counters see HBM traffic")
@@ -539,12 +540,12 @@ def profile_workload_fns(torch, sp, inputs, dev, wanted):
     return fns
 
 
-def stream_setup(torch, sp, inputs, dev, dtype=None):
+def stream_setup(torch, sp, inputs, dev, dtype=None, n=4):
     """The streaming regime: A 65536 x 8192 at 90 % sparsity (53.7 M entries,
-    430 MB of CSR, far beyond L2 and MALL), B 8192 x 4 held in LDS, natural
-    row order; values and B fp32, or of the 16-bit torch `dtype`.  Returns
-    (launch, workload description)."""
-    w = inputs.hbm_stream(n=4)
+    430 MB of CSR, far beyond L2 and MALL), B 8192 x n held in LDS (n = 8:
+    in two column slices), natural row order; values and B fp32, or of the
+    16-bit torch `dtype`.  Returns (launch, workload description)."""
+    w = inputs.hbm_stream(n=n)
     a = w["a"]
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
     ro = up(np.concatenate([[0], np.cumsum(a.lengths)]).astype(np.int32))
@@ -871,6 +872,9 @@ def main() -> int:
             launches(fn)
         if args.profile_stream:
             fn, _ = stream_setup(torch, sp, inputs, dev)
+            launches(fn)
+        if "stream8" in wanted:
+            fn, _ = stream_setup(torch, sp, inputs, dev, n=8)
             launches(fn)
         # a plain copy of known size, to calibrate the byte counters
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB

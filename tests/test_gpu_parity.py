@@ -366,7 +366,11 @@ def test_spmm_lds_resident_b(n):
     a = csr_of_row_lists(inputs.random_row_lists(81 + n, m, k, lengths))
     b = inputs.random_dense(82 + n, k, n)
     note(f"spmm lds-resident B n={n} nnz={a.nnz}")
-    c = run_spmm(a, b, row_indices=swizzle(a))
+    ri = swizzle(a)
+    cd = torch.empty(m, n, device="cuda")
+    assert sp.sp_spmm_kernel_name(m, k, n, a.nnz, a.d_vals, a.d_ci, dev(b), cd,
+                                  row_indices=ri) == "lds"
+    c = run_spmm(a, b, row_indices=ri)
     ref, s = oracle.spmm(m, k, n, a.ro, a.ci, a.vals, b)
     check_close(c, ref, s, f"spmm lds n={n}")
     # one-entry rows through the same kernel are exact
@@ -391,7 +395,11 @@ def test_spmm_lds_column_slices(k, n, m):
     a = csr_of_row_lists(inputs.random_row_lists(85 + n + k, m, k, lengths))
     b = inputs.random_dense(86 + n + k, k, n)
     note(f"spmm lds column slices k={k} n={n} m={m} nnz={a.nnz}")
-    c = run_spmm(a, b, row_indices=swizzle(a))
+    ri = swizzle(a)
+    cd = torch.empty(m, n, device="cuda")
+    assert sp.sp_spmm_kernel_name(m, k, n, a.nnz, a.d_vals, a.d_ci, dev(b), cd,
+                                  row_indices=ri) == "lds"
+    c = run_spmm(a, b, row_indices=ri)
     ref, s = oracle.spmm(m, k, n, a.ro, a.ci, a.vals, b)
     check_close(c, ref, s, f"spmm lds slices k={k} n={n}")
     assert np.all(c[lengths == 0] == 0)

@@ -615,6 +615,11 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
     Batch cur = row_batch(0);
     Seg sa[kSteps], sb[kSteps];
     load(cur, sa);
+    // One exit, at the end: a second exit after the first half would give the
+    // loop header an edge on which the first half's loads are still pending,
+    // and the compiler would then wait for every load in flight at the top of
+    // each iteration.  When the first half reaches the empty batch, the second
+    // half runs on it as a no-op (out-of-range loads, zero terms, no row end).
     for (;;) {
         // Issued unconditionally (an empty next batch is all out of range),
         // which keeps the compiler's wait counts exact.
@@ -623,7 +628,6 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
         keep_issued_above();
         consume(cur, sa, acc);
         if (nb.t != cur.t) finish_row(cur.row);
-        if (nb.row < 0) break;
         cur = nb;
         const Batch na = next_of(cur);
         load(na, sa);
