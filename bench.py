@@ -108,7 +108,9 @@ def parse_args():
                          "ffn (the step's kernels), resnet, lstm90, lstm50, attention; "
                          "resnet_wide, lstm50_wide: the same SpMM as a 2-entry batch, "
                          "which takes the wide kernel; stream8: the streaming-regime "
-                         "SpMM with B 8 columns wide (two column slices)")
+                         "SpMM with B 8 columns wide (two column slices); ffn_dk, "
+                         "attention_dk: the general SDDMM with Y stored d x k and no "
+                         "workspace")
     ap.add_argument("--profile-cold", action="store_true",
                     help="with --profile-launches: write a 1 GiB buffer before every "
                          "launch, so the byte counters see HBM traffic")
@@ -486,9 +488,10 @@ def lstm_breakeven(torch, sp, inputs, dev, reps=50, records=None, flush=None):
 def profile_workload_fns(torch, sp, inputs, dev, wanted):
     """Launch functions of the named workloads, for rocprofv3 passes: resnet
     (the ResNet-50 1x1 SpMM), lstm90 / lstm50 (the LSTM-sized SpMM at 90 % and
-    50 %), attention (the four sparse-attention kernels over 32 heads), and
+    50 %), attention (the four sparse-attention kernels over 32 heads),
     resnet_wide / lstm50_wide (the SpMM on the wide kernel, as a 2-entry
-    batch)."""
+    batch), and ffn_dk / attention_dk (the general SDDMM with Y stored d x k,
+    no workspace)."""
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
     fns = []
     gens = {"resnet": inputs.resnet_1x1, "lstm90": lambda: inputs.lstm(0.9),
@@ -514,7 +517,17 @@ def profile_workload_fns(torch, sp, inputs, dev, wanted):
                 c = torch.empty(m, n, device=dev)
                 fns.append(lambda m=m, k=k, n=n, nnz=nnz, ri=ri, vals=vals, ro=ro, cols=cols,
                            b=b, c=c: sp.sp_spmm(m, k, n, nnz, ri, vals, ro, cols, b, c))
-    if "attention" in wanted:
+    if "ffn_dk" in wanted:
+        # the general SDDMM on the FFN shapes, Y stored d x k, no workspace
+        w = inputs.transformer_ffn()
+        a = w["a"]
+        m, k, d = w["m"], w["k"], w["d"]
+        ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+        x, y_dk = up(w["x"]), up(w["y"]).t().contiguous()
+        out = torch.zeros(a.nnz, device=dev)
+        fns.append(lambda: sp.sp_sddmm_general(m, k, d, a.nnz, ri, ro, cols, vals, x, y_dk,
+                                               sp.SP_Y_DK, 0.5, 1.0, out))
+    if "attention" in wanted or "attention_dk" in wanted:
         w = inputs.sparse_attention()
         bh, seq, hd = w["batch"], w["seq"], w["head_dim"]
         mk = up(w["mask"])
@@ -529,6 +542,14 @@ def profile_workload_fns(torch, sp, inputs, dev, wanted):
         s_out = torch.empty(bh, nnz, device=dev)
         p_vals = torch.full((bh, nnz), 1.0 / 80.0, device=dev)
         o = torch.empty(bh, seq, hd, device=dev)
+        if "attention_dk" in wanted:
+            # the scores with K stored d x k per head, no workspace
+            kt = kk.transpose(1, 2).contiguous()
+            fns.append(lambda: sp.sp_sddmm_general(seq, seq, hd, nnz, ri, ro, cols, None, q,
+                                                   kt, sp.SP_Y_DK, 0.125, 0.0, s_out, bh, 0,
+                                                   seq * hd, seq * hd, nnz))
+        if "attention" not in wanted:
+            return fns
         fns += [lambda: sp.sp_sddmm_batched(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125,
                                             s_out, bh, seq * hd, seq * hd, nnz),
                 lambda: sp.sp_csr_row_softmax(seq, nnz, ri, ro, s_out, s_out, bh, nnz, nnz),

@@ -131,6 +131,25 @@ __device__ __forceinline__ float strided_wave_sum(float v)
 // arithmetic on the previous batch: otherwise the scheduler interleaves the
 // two to shorten register lifetimes, the two buffers share registers, and
 // every batch waits for all outstanding gathers.
+// A value of T (4, 8 or 16 bytes) read from 32-bit LDS address `addr`: the
+// address stays an LDS one, so the read is a single ds_read with no generic-
+// to-LDS conversion, and the address arithmetic before it can fold the base.
+template <class T> __device__ __forceinline__ T lds_read(unsigned addr)
+{
+    static_assert(sizeof(T) % 4 == 0 && sizeof(T) <= 16, "4 to 16 bytes");
+    using W = unsigned __attribute__((ext_vector_type(sizeof(T) / 4)));
+    const W w = *(const __attribute__((address_space(3))) W *)(size_t)addr;
+    T t;
+    __builtin_memcpy(&t, &w, sizeof(T));
+    return t;
+}
+
+// The 32-bit LDS address of a pointer into LDS.
+template <class T> __device__ __forceinline__ unsigned lds_address(const T *p)
+{
+    return (unsigned)(size_t)(const __attribute__((address_space(3))) T *)p;
+}
+
 __device__ __forceinline__ void keep_issued_above()
 {
     asm volatile("" ::: "memory");

@@ -521,7 +521,7 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
             // 16-bit: from the segment's own start, its dwords past the end
             // reading as zeros (range-checked per dword)
             const unsigned off = !any ? kOutOfRange
-                                      : (unsigned)(kEb == 2 || e + 4 <= p.nnz ? e : last4) * 4u;
+                                      : (unsigned)(kEb == 2 ? e : min(e, last4)) * 4u;
             const auto c4 = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)off, 0, 0);
             sg[u].c = make_int4((int)c4[0], (int)c4[1], (int)c4[2], (int)c4[3]);
             if constexpr (kEb == 4) {
@@ -538,22 +538,25 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
         }
     };
     const unsigned row_bytes = (unsigned)wv * sizeof(VecT);   // one row of B in LDS
-    const unsigned lane_bytes = (unsigned)v * sizeof(VecT);
-    const unsigned zero_bytes = (unsigned)total * sizeof(VecT);
+    // 32-bit LDS addresses of this lane's vector in B's first row and of the
+    // zero vector, so that each entry's address is one multiply-add
+    const unsigned lds_b = lds_address(s_bv);
+    const unsigned lds_lane = lds_b + (unsigned)v * sizeof(VecT);
+    const unsigned lds_zero = lds_b + (unsigned)total * sizeof(VecT);
     auto consume = [&](const Batch &b, const Seg (&sg)[kSteps], float *acc) {
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
             const int e = b.base + (u * kS + s) * 4;
             // The segment was loaded from entry e_ld: e, or (fp32) last4 for the
             // array's final segment (whose positions before e belong to the
-            // segment before it).  Position t holds entry e_ld + t, which is
-            // this lane's when lo <= e_ld + t < p1 with lo = max(p0, e); an
-            // idle lane (no column vector) takes none.
-            const int e_ld = kEb == 2 || e + 4 <= p.nnz ? e : last4;
+            // segment before it; e + 4 > nnz exactly when e > last4).
+            // Position t holds entry e_ld + t, which is this lane's when
+            // lo <= e_ld + t < p1 with lo = max(p0, e); an idle lane (no
+            // column vector) takes none.
+            const int e_ld = kEb == 2 ? e : min(e, last4);
             const int lo = max(b.p0, e);
             const unsigned span = (col_ok && b.p1 > lo) ? (unsigned)(b.p1 - lo) : 0u;
             const int d = e_ld - lo;
-            const char *s_bytes = reinterpret_cast<const char *>(s_bv);
             const int cs[4] = {sg[u].c.x, sg[u].c.y, sg[u].c.z, sg[u].c.w};
             float vs[4] = {sg[u].v.x, sg[u].v.y, sg[u].v.z, sg[u].v.w};
             if constexpr (kEb == 2) {
@@ -568,12 +571,12 @@ __global__ __launch_bounds__(kLdsThreads) void spmm_lds_kernel(SpmmParams p)
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const bool in_row = (unsigned)(d + t) < span;
-                // Byte offset of row col of B, this lane's vector (or of the
-                // zero vector); 16-byte aligned, so the read is one ds_read_b128.
-                const unsigned off =
-                    in_row ? __umul24((unsigned)cs[t], row_bytes) + lane_bytes : zero_bytes;
+                // Address of row col of B, this lane's vector (or of the zero
+                // vector); 16-byte aligned, so the read is one ds_read_b128.
+                const unsigned a =
+                    in_row ? __umul24((unsigned)cs[t], row_bytes) + lds_lane : lds_zero;
                 val[t] = in_row ? vs[t] : 0.f;
-                bv[t] = *reinterpret_cast<const VecT *>(s_bytes + off);
+                bv[t] = lds_read<VecT>(a);
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) V::fma(val[t], bv[t], acc);
