@@ -280,8 +280,9 @@ def config_records(torch, sp, inputs, dev, flush) -> list:
     recs = []
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
-    def kname(m, k, n, nnz, vals, cols, b, c):
-        return sp.sp_spmm_kernel_name(m, k, n, nnz, vals, cols, b, c)
+    def kname(m, k, n, nnz, vals, cols, b, c, order):
+        # the kernel the timed call (same row order) runs
+        return sp.sp_spmm_kernel_name(m, k, n, nnz, vals, cols, b, c, row_indices=order)
 
     # ---- tiny (256 x 256, p = 0.2): SpMM n = 64, SDDMM d = 32
     wt = inputs.tiny()
@@ -300,7 +301,8 @@ def config_records(torch, sp, inputs, dev, flush) -> list:
                               flush, 200, {"m": at.m, "k": at.k, "n": wt["n"], "nnz": at.nnz,
                                            "single_launch_us": latency_us(torch, fns["spmm"]),
                                            "variant": kname(at.m, at.k, wt["n"], at.nnz,
-                                                            at.values, at.col_indices, bt, ct)}))
+                                                            at.values, at.col_indices, bt, ct,
+                                                            at.row_indices)}))
     recs.append(kernel_record(torch, "tiny", "sddmm", wt["name"], fns["sddmm"],
                               2.0 * at.nnz * wt["d"], sddmm_bytes(at.m, at.k, wt["d"], at.nnz),
                               flush, 200, {"m": at.m, "k": at.k, "d": wt["d"], "nnz": at.nnz,
@@ -321,7 +323,7 @@ def config_records(torch, sp, inputs, dev, flush) -> list:
             order = ri if swz else None
             tag = {"swizzle": swz, "m": m, "k": k, "n": n, "d": d, "nnz": nnz}
             fn = lambda: sp.sp_spmm(m, k, n, nnz, order, vals, ro, cols, b, c)
-            ex = dict(tag, variant=kname(m, k, n, nnz, vals, cols, b, c))
+            ex = dict(tag, variant=kname(m, k, n, nnz, vals, cols, b, c, order))
             if cfg != "imbalance":
                 ex["single_launch_us"] = latency_us(torch, fn)
             recs.append(kernel_record(torch, cfg, "spmm", w["name"], fn, 2.0 * nnz * n,
@@ -353,7 +355,7 @@ def config_records(torch, sp, inputs, dev, flush) -> list:
     recs.append(kernel_record(torch, "resnet50_1x1", "spmm", w["name"], fn, 2.0 * nnz * n,
                               spmm_bytes(m, k, n, nnz), flush, 50,
                               {"m": m, "k": k, "n": n, "nnz": nnz,
-                               "variant": kname(m, k, n, nnz, vals, cols, b, c)}))
+                               "variant": kname(m, k, n, nnz, vals, cols, b, c, ri)}))
     del b, c
 
     # ---- sparse attention: 32 (batch, head) pairs over one 4096 x 4096 mask
@@ -454,7 +456,7 @@ def lstm_breakeven(torch, sp, inputs, dev, reps=50, records=None, flush=None):
                                 spmm_bytes(m, k, n, a.nnz), flush, reps,
                                 {"sparsity": s, "m": m, "k": k, "n": n, "nnz": a.nnz,
                                  "variant": sp.sp_spmm_kernel_name(m, k, n, a.nnz, vals, cols,
-                                                                   b, c)})
+                                                                   b, c, row_indices=ri)})
             records.append(rec)
             times[s] = rec["us"]
         else:

@@ -11,9 +11,11 @@
  * ---------------------------------------
  * Pointers.  Every array argument is a DEVICE pointer (memory the caller got
  * from hipMalloc or an allocator on top of it, e.g. a torch tensor).  The
- * library never allocates, frees or retains caller memory, keeps no mutable
- * global state, and is safe to call from several host threads at once.
- * Outputs must not overlap inputs.
+ * library never allocates, frees or retains caller memory and keeps no
+ * mutable global state -- except the per-GPU scratch array that
+ * sp_row_swizzle_noalloc sorts in, which that entry point describes -- and is
+ * safe to call from several host threads at once.  Outputs must not overlap
+ * inputs.
  *
  * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Every call
  * only enqueues work on `stream` and returns without synchronising.  The
