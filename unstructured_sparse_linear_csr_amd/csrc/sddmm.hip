@@ -129,44 +129,66 @@ __host__ __device__ constexpr int dk_rounds(int dv) { return dv <= 32 ? 2 : 1; }
 
 // X rows of a panel into LDS: thread -> vector tid % 2^xsh of rows
 // tid / 2^xsh + u * (kThreads >> xsh) (2^xsh >= dv; kDkXItems * (kThreads >>
-// xsh) covers the panel's rows), zero beyond d.
+// xsh) covers the panel's rows), zero beyond d.  Loaded into registers by
+// load(), written to LDS by store(), so that a caller can issue other loads
+// in between (a write waits for its load, and loads complete in order).
+template <int kThreads, bool kVec>
+struct DkStageX {
+    float4 xb[kDkXItems];
+    int xv, xr0, xstep;
+
+    template <class RowOf>
+    __device__ __forceinline__ void load(const SddmmParams &p, const float *xz, int nrows, int xsh,
+                                         RowOf row_of)
+    {
+        const int tid = threadIdx.x;
+        const int dv = (p.d + 3) / 4;
+        xv = min(tid & ((1 << xsh) - 1), dv - 1);
+        xr0 = tid >> xsh;
+        xstep = kThreads >> xsh;
+        int xrow[kDkXItems];
+#pragma unroll
+        for (int u = 0; u < kDkXItems; ++u) xrow[u] = row_of(min(xr0 + u * xstep, nrows - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        const int e = 4 * xv;
+#pragma unroll
+        for (int u = 0; u < kDkXItems; ++u) {
+            const float *src = xz + (size_t)xrow[u] * (size_t)p.d + e;
+            if constexpr (kVec) {  // d % 4 == 0
+                xb[u] = *reinterpret_cast<const float4 *>(src);
+            } else {
+                const int last = p.d - 1 - e;  // >= 0
+                xb[u] = make_float4(src[0], src[min(1, last)], src[min(2, last)], src[min(3, last)]);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(const SddmmParams &p, int nrows, unsigned x_pitch,
+                                          unsigned char *lds)
+    {
+        const int e = 4 * xv;
+#pragma unroll
+        for (int u = 0; u < kDkXItems; ++u) {
+            const int r = min(xr0 + u * xstep, nrows - 1);
+            float4 v = xb[u];
+            if constexpr (!kVec) {
+                if (e + 1 >= p.d) v.y = 0.f;
+                if (e + 2 >= p.d) v.z = 0.f;
+                if (e + 3 >= p.d) v.w = 0.f;
+            }
+            *reinterpret_cast<float4 *>(lds + (unsigned)r * x_pitch + (unsigned)xv * 16u) = v;
+        }
+    }
+};
+
 template <int kThreads, bool kVec, class RowOf>
 __device__ __forceinline__ void dk_stage_x(const SddmmParams &p, const float *xz, int nrows,
                                            int xsh, unsigned x_pitch, unsigned char *lds,
                                            RowOf row_of)
 {
-    const int tid = threadIdx.x;
-    const int dv = (p.d + 3) / 4;
-    const int xv = min(tid & ((1 << xsh) - 1), dv - 1);
-    const int xr0 = tid >> xsh;
-    const int xstep = kThreads >> xsh;
-    int xrow[kDkXItems];
-#pragma unroll
-    for (int u = 0; u < kDkXItems; ++u) xrow[u] = row_of(min(xr0 + u * xstep, nrows - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    float4 xb[kDkXItems];
-    const int e = 4 * xv;
-#pragma unroll
-    for (int u = 0; u < kDkXItems; ++u) {
-        const float *src = xz + (size_t)xrow[u] * (size_t)p.d + e;
-        if constexpr (kVec) {  // d % 4 == 0
-            xb[u] = *reinterpret_cast<const float4 *>(src);
-        } else {
-            const int last = p.d - 1 - e;  // >= 0
-            xb[u] = make_float4(src[0], src[min(1, last)], src[min(2, last)], src[min(3, last)]);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < kDkXItems; ++u) {
-        const int r = min(xr0 + u * xstep, nrows - 1);
-        float4 v = xb[u];
-        if constexpr (!kVec) {
-            if (e + 1 >= p.d) v.y = 0.f;
-            if (e + 2 >= p.d) v.z = 0.f;
-            if (e + 3 >= p.d) v.w = 0.f;
-        }
-        *reinterpret_cast<float4 *>(lds + (unsigned)r * x_pitch + (unsigned)xv * 16u) = v;
-    }
+    DkStageX<kThreads, kVec> sx;
+    sx.load(p, xz, nrows, xsh, row_of);
+    sx.store(p, nrows, x_pitch, lds);
 }
 
 template <int kRows, int kRounds, bool kVec>
@@ -511,7 +533,7 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
 // lanes read 256 contiguous bytes of one LDS row, so no bank conflicts,
 // whatever the columns), and group_sum adds the 16 partial sums.
 constexpr int kDkTileCols = 64;
-constexpr int kDkTileYBatch = 16;  // Y vectors per thread per batch (d <= 256: one batch)
+constexpr int kDkTileYItems = 4096;  // Y vectors per batch: d <= 256 at 16 column quads is one
 
 template <int kRows, int kWaves, int kNv, bool kVec>
 __global__ __launch_bounds__(kWaves * kWave) void sddmm_dk_tile_kernel(SddmmParams p, DkPanelParams q)
@@ -592,18 +614,21 @@ __global__ __launch_bounds__(kWaves * kWave) void sddmm_dk_tile_kernel(SddmmPara
         dst[2 * pf] = v.z;
         dst[3 * pf] = v.w;
     };
-    float4 yb[kDkTileYBatch];
+    constexpr int kYB = kDkTileYItems / kThreads;  // Y vectors per thread per batch
+    float4 yb[kYB];
 #pragma unroll
-    for (int u = 0; u < kDkTileYBatch; ++u) yb[u] = load_y(u * kThreads + tid);
+    for (int u = 0; u < kYB; ++u) yb[u] = load_y(u * kThreads + tid);
     __builtin_amdgcn_sched_barrier(0);
     // ---- level 1b: this wave's CSR bounds, then the panel's X rows
     int my_start = p.row_offsets[my_row];
     int my_end = p.row_offsets[my_row + 1];
     __builtin_amdgcn_sched_barrier(0);
-    dk_stage_x<kThreads, kVec>(p, xz, nrows, q.x_shift, q.x_pitch, lds, row_of);
+    DkStageX<kThreads, kVec> sx;
+    sx.load(p, xz, nrows, q.x_shift, row_of);
+    __builtin_amdgcn_sched_barrier(0);
     if (!my_ok) my_start = my_end = 0;
     // ---- level 2: per row, the 64-entry window of column indices from its
-    // start
+    // start (issued before X is written to LDS, which waits for X's loads)
     int win[kRpw];
 #pragma unroll
     for (int i = 0; i < kRpw; ++i) {
@@ -614,15 +639,16 @@ __global__ __launch_bounds__(kWaves * kWave) void sddmm_dk_tile_kernel(SddmmPara
         win[i] = in ? c : INT_MAX;
     }
     __builtin_amdgcn_sched_barrier(0);
-    // ---- stage Y (more batches when d * cq > 16 * 256) and its zero rows
+    sx.store(p, nrows, q.x_pitch, lds);
+    // ---- stage Y (more batches when d * cq > 4096) and its zero rows
     // l in [d, 4 dv) (X's padding is zero, but 0 * NaN is not)
 #pragma unroll
-    for (int u = 0; u < kDkTileYBatch; ++u) store_y(u * kThreads + tid, yb[u]);
-    for (int i0 = kDkTileYBatch * kThreads; i0 < ny; i0 += kDkTileYBatch * kThreads) {
+    for (int u = 0; u < kYB; ++u) store_y(u * kThreads + tid, yb[u]);
+    for (int i0 = kYB * kThreads; i0 < ny; i0 += kYB * kThreads) {
 #pragma unroll
-        for (int u = 0; u < kDkTileYBatch; ++u) yb[u] = load_y(i0 + u * kThreads + tid);
+        for (int u = 0; u < kYB; ++u) yb[u] = load_y(i0 + u * kThreads + tid);
 #pragma unroll
-        for (int u = 0; u < kDkTileYBatch; ++u) store_y(i0 + u * kThreads + tid, yb[u]);
+        for (int u = 0; u < kYB; ++u) store_y(i0 + u * kThreads + tid, yb[u]);
     }
     // zero rows l in [d, 64 kNv) of the staged columns, and the same elements
     // of the staged X rows (the 16-lane groups read whole groups of vectors)
