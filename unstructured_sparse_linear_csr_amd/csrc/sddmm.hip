@@ -254,7 +254,9 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
     int my_cur = p.row_offsets[my_row];
     int my_end = p.row_offsets[my_row + 1];
     __builtin_amdgcn_sched_barrier(0);
-    dk_stage_x<kThreads, kVec>(p, xz, nrows, q.x_shift, q.x_pitch, lds, row_of);
+    DkStageX<kThreads, kVec> sx;
+    sx.load(p, xz, nrows, q.x_shift, row_of);
+    __builtin_amdgcn_sched_barrier(0);
     if (!my_ok) my_cur = my_end = 0;
     int my_n = 0;
     s_bits[tid] = 0u;
@@ -288,6 +290,9 @@ __global__ __launch_bounds__(4 * kWave) void sddmm_dk_panel_kernel(SddmmParams p
             }
         }
     }
+    // X into LDS after the rows' first column loads are issued (a write
+    // waits for its load, and loads complete in order)
+    sx.store(p, nrows, q.x_pitch, lds);
     if (lane == 0) s_wmin[wave] = wm;
     __syncthreads();
     int chunk0 = min(min(s_wmin[0], s_wmin[1]), min(s_wmin[2], s_wmin[3]));
