@@ -110,7 +110,8 @@ def parse_args():
                          "which takes the wide kernel; stream8: the streaming-regime "
                          "SpMM with B 8 columns wide (two column slices); ffn_dk, "
                          "attention_dk: the general SDDMM with Y stored d x k and no "
-                         "workspace")
+                         "workspace; imbalance: the lognormal-row SpMM (swizzled, "
+                         "natural) and SDDMM; transpose: the LSTM layer's CSR transpose")
     ap.add_argument("--profile-cold", action="store_true",
                     help="with --profile-launches: write a 1 GiB buffer before every "
                          "launch, so the byte counters see HBM traffic")
@@ -496,6 +497,23 @@ def profile_workload_fns(torch, sp, inputs, dev, wanted):
     no workspace)."""
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
     fns = []
+
+    def imbalance_fns():
+        # lognormal rows: the SpMM swizzled (the balanced kernel) and natural
+        # (the wide kernel), and the SDDMM swizzled (windows on four waves)
+        if "imbalance" not in wanted:
+            return []
+        w = inputs.imbalance()
+        a = w["a"]
+        m, k, n, d, nnz = w["m"], w["k"], w["n"], w["d"], a.nnz
+        ro, ri, cols, vals = upload_csr(torch, sp, dev, a)
+        b, x, y = up(w["b"]), up(w["x"]), up(w["y"])
+        c = torch.empty(m, n, device=dev)
+        out = torch.empty(nnz, device=dev)
+        return [lambda: sp.sp_spmm(m, k, n, nnz, ri, vals, ro, cols, b, c),
+                lambda: sp.sp_spmm(m, k, n, nnz, None, vals, ro, cols, b, c),
+                lambda: sp.sp_sddmm(m, k, d, nnz, ri, ro, cols, x, y, out)]
+
     gens = {"resnet": inputs.resnet_1x1, "lstm90": lambda: inputs.lstm(0.9),
             "lstm50": lambda: inputs.lstm(0.5)}
     for name, gen in gens.items():
@@ -551,7 +569,7 @@ def profile_workload_fns(torch, sp, inputs, dev, wanted):
                                                    kt, sp.SP_Y_DK, 0.125, 0.0, s_out, bh, 0,
                                                    seq * hd, seq * hd, nnz))
         if "attention" not in wanted:
-            return fns
+            return fns + imbalance_fns()
         fns += [lambda: sp.sp_sddmm_batched(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125,
                                             s_out, bh, seq * hd, seq * hd, nnz),
                 lambda: sp.sp_csr_row_softmax(seq, nnz, ri, ro, s_out, s_out, bh, nnz, nnz),
@@ -560,7 +578,7 @@ def profile_workload_fns(torch, sp, inputs, dev, wanted):
                 lambda: sp.sp_sparse_attention(seq, seq, hd, nnz, ri, ro, cols, q, kk, v,
                                                0.125, o, bh, seq * hd, seq * hd, seq * hd,
                                                seq * hd)]
-    return fns
+    return fns + imbalance_fns()
 
 
 def stream_setup(torch, sp, inputs, dev, dtype=None, n=4):
@@ -899,6 +917,21 @@ def main() -> int:
         if "stream8" in wanted:
             fn, _ = stream_setup(torch, sp, inputs, dev, n=8)
             launches(fn)
+        if "transpose" in wanted:
+            # the CSR transpose of the LSTM layer at 90 % (radix method: a
+            # chain of launches per call)
+            w = inputs.lstm(0.9)
+            a = w["a"]
+            m, k, nnz = w["m"], w["k"], a.nnz
+            ro, _, cols, vals = upload_csr(torch, sp, dev, a)
+            ws = torch.empty(sp.sp_csr_transpose_workspace(m, k, nnz), dtype=torch.uint8,
+                             device=dev)
+            t_ro = torch.empty(k + 1, dtype=torch.int32, device=dev)
+            t_ci = torch.empty(nnz, dtype=torch.int32, device=dev)
+            t_v = torch.empty(nnz, device=dev)
+            t_p = torch.empty(nnz, dtype=torch.int32, device=dev)
+            launches(lambda: sp.sp_csr_transpose(m, k, nnz, ro, cols, vals, t_ro, t_ci, t_v,
+                                                 t_p, ws))
         # a plain copy of known size, to calibrate the byte counters
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
         dst = torch.empty_like(src)
