@@ -76,7 +76,7 @@ def test_transpose_hand_example():
 
 
 # Columns across 0 to 4 radix passes, nnz across one tile, several tiles and a
-# ragged last tile, empty rows and columns.  With k <= 16384 (and nnz <= 2^24)
+# ragged last tile, empty rows and columns.  With k <= 16384 (and nnz <= 2^18)
 # the counting method runs instead: rows longer than its 2048-entry LDS piece,
 # k at its LDS limit, ranges of 1024 mostly empty rows, and k one past the
 # limit (the radix method again).
@@ -92,6 +92,11 @@ CASES = [
     ("count_k16384", 289, 2500, 16384, 120),
     ("count_sparse_rows", 290, 100000, 50, 1),
     ("radix_k16385", 291, 2500, 16385, 120),
+    # the radix method with each entry's row carried in its key above the two
+    # column passes: 32,768 rows are the most that fit (15 bits above 16), one
+    # more row takes the row-id array instead
+    ("radix_row_in_key_2p15", 292, 32768, 300, 20),
+    ("radix_row_id_array_2p15_plus1", 293, 32769, 300, 20),
 ]
 
 

@@ -74,6 +74,19 @@ __global__ __launch_bounds__(kWave) void expand_rows_kernel(const int *__restric
     for (int p = row_offsets[row] + (int)threadIdx.x; p < p1; p += kWave) rowid[p] = row;
 }
 
+// key[p] = (row << row_shift) | col_indices[p] for the entries p of each row
+// (one wave per row): the row rides in the key's bits above the sorted ones.
+__global__ __launch_bounds__(kWave) void pack_keys_kernel(const int *__restrict__ row_offsets,
+                                                          const int *__restrict__ col_indices,
+                                                          int row_shift, int *__restrict__ key)
+{
+    const int row = blockIdx.x;
+    const int p1 = row_offsets[row + 1];
+    const int hi = row << row_shift;
+    for (int p = row_offsets[row] + (int)threadIdx.x; p < p1; p += kWave)
+        key[p] = hi | col_indices[p];
+}
+
 // hist[d * (tiles + 1) + b + 1] = number of entries of tile b whose digit is d.
 __global__ __launch_bounds__(kSortThreads) void radix_upsweep_kernel(
     int nnz, int shift, const int *__restrict__ keys, int *__restrict__ hist, int tiles)
@@ -186,7 +199,7 @@ __global__ __launch_bounds__(256) void offsets_from_sorted_kernel(int nnz, int k
     const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
     if (q > nnz) return;
     const long long prev = q > 0 ? keys[q - 1] : -1;
-    const long long cur = q < nnz ? keys[q] : k;
+    const long long cur = q < nnz ? min(keys[q], k) : k;  // (min: as in the packed form)
     for (long long c = prev + 1; c <= cur; ++c) t_row_offsets[c] = (int)q;
 }
 
@@ -200,6 +213,31 @@ __global__ __launch_bounds__(256) void transpose_finish_kernel(
     if (q >= nnz) return;
     const int p = perm ? perm[q] : (int)q;
     t_col_indices[q] = rowid[p];
+    if (t_values) t_values[q] = values[p];
+    if (t_perm) t_perm[q] = p;
+}
+
+// Entry q of A^T from packed keys sorted by column (column in the bits below
+// row_shift, row above): its row of A and, through perm, its value and source
+// entry; position q also writes t_row_offsets[c] for every column c in
+// (column of q - 1, column of q] (through k at q = nnz), as
+// offsets_from_sorted_kernel does.
+__global__ __launch_bounds__(256) void transpose_finish_packed_kernel(
+    int nnz, int k, int row_shift, const int *__restrict__ keys, const int *__restrict__ perm,
+    const float *__restrict__ values, int *__restrict__ t_row_offsets,
+    int *__restrict__ t_col_indices, float *__restrict__ t_values, int *__restrict__ t_perm)
+{
+    const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (q > nnz) return;
+    const int mask = (1 << row_shift) - 1;
+    // (min: a column index outside [0, k), which valid input never holds,
+    // still writes no offset past t_row_offsets[k])
+    const long long prev = q > 0 ? (keys[q - 1] & mask) : -1;
+    const long long cur = q < nnz ? min(keys[q] & mask, k) : k;
+    for (long long c = prev + 1; c <= cur; ++c) t_row_offsets[c] = (int)q;
+    if (q == nnz) return;
+    const int p = perm[q];
+    t_col_indices[q] = keys[q] >> row_shift;
     if (t_values) t_values[q] = values[p];
     if (t_perm) t_perm[q] = p;
 }
@@ -463,14 +501,35 @@ hipError_t launch_csr_transpose(int m, int k, int nnz, const int *row_offsets,
         return launch_count_transpose(m, k, nnz, s, row_offsets, col_indices, values,
                                       t_row_offsets, t_col_indices, t_values, t_perm, w, stream);
 
+    // Columns lie in [0, k): the sort looks at the low 8 * passes bits.  When
+    // the row fits above them in a non-negative int, it rides in the key, so
+    // the sorted keys give A^T's column indices (rows of A) with no gather.
+    // With no pass (k == 1) every column is 0: the entries are already in
+    // order.
+    const int passes = radix_passes(k);
+    const int row_shift = 8 * passes;
+    int row_bits = 0;
+    while (row_bits < 31 && (1LL << row_bits) < (long long)m) ++row_bits;
+    if (passes > 0 && row_shift + row_bits <= 31) {
+        hipLaunchKernelGGL(pack_keys_kernel, dim3((unsigned)m), dim3(kWave), 0, stream,
+                           row_offsets, col_indices, row_shift, w.rowid);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int *pkeys = nullptr;
+        const int *perm = nullptr;
+        if ((e = launch_radix_sort(nnz, passes, w.rowid, nullptr, w.keys, w.vals, nullptr,
+                                   w.hist, stream, &pkeys, &perm)) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(transpose_finish_packed_kernel, dim3(blocks_for((long long)nnz + 1)),
+                           dim3(256), 0, stream, nnz, k, row_shift, pkeys, perm, values,
+                           t_row_offsets, t_col_indices, t_values, t_perm);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(expand_rows_kernel, dim3((unsigned)m), dim3(kWave), 0, stream,
                        row_offsets, w.rowid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // Columns lie in [0, k).  With no pass (k == 1) every column is 0: the
-    // entries are already in order.
     const int *keys = col_indices;
     const int *vals = nullptr;
-    if ((e = launch_radix_sort(nnz, radix_passes(k), col_indices, nullptr, w.keys, w.vals,
+    if ((e = launch_radix_sort(nnz, passes, col_indices, nullptr, w.keys, w.vals,
                                nullptr, w.hist, stream, &keys, &vals)) != hipSuccess)
         return e;
     hipLaunchKernelGGL(offsets_from_sorted_kernel, dim3(blocks_for((long long)nnz + 1)),
