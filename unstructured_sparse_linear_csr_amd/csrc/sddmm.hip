@@ -619,6 +619,7 @@ __global__ __launch_bounds__(kWaves * kWave) void sddmm_dk_tile_kernel(SddmmPara
         dst[2 * pf] = v.z;
         dst[3 * pf] = v.w;
     };
+    static_assert(kDkTileYItems % kThreads == 0, "whole Y batches per thread");
     constexpr int kYB = kDkTileYItems / kThreads;  // Y vectors per thread per batch
     float4 yb[kYB];
 #pragma unroll
