@@ -196,9 +196,12 @@ sp_status_t sp_csr_build_from_lengths(int m, const int *lengths, int *row_offset
  * consecutive parts of the row, each in entry order, added in order (few rows
  * averaging 256 entries or more).  With a row order given, B of more than 128
  * fp32 columns and one batch entry, the balanced kernel of sp_spmm_balanced
- * runs instead (the card's I4: the swizzled order pairs long rows with short
- * ones in its groups), so rows of a skewed group are summed as that entry
- * point describes.  Results are deterministic run to run. */
+ * runs instead of the wide one (the card's I4: the swizzled order pairs long
+ * rows with short ones in its groups), so rows of a skewed group are summed as
+ * that entry point describes -- unless B is staged in LDS by row panels, which
+ * takes precedence (fp32 one-batch problems whose panels fill every CU and
+ * touch each staged B row at least 4 times on average).  sp_spmm_kernel_name
+ * reports the choice.  Results are deterministic run to run. */
 sp_status_t sp_spmm(int m, int k, int n, int nnz, const int *row_indices,
                     const float *values, const int *row_offsets,
                     const int *col_indices, const float *b, float *c,
@@ -217,8 +220,9 @@ sp_status_t sp_spmm(int m, int k, int n, int nnz, const int *row_indices,
  * row after row) into 4 equal parts, one per wave, and adds the parts'
  * partial sums of each row in order.  Results are deterministic for a given
  * row order and within rounding of sp_spmm.  sp_spmm runs this kernel by
- * itself when given a row order on one batch entry of such B; narrower B takes
- * sp_spmm's kernels.  Arguments as sp_spmm. */
+ * itself when given a row order on one batch entry of such B (unless it stages
+ * B by row panels); narrower B takes sp_spmm's kernels.  Arguments as
+ * sp_spmm. */
 sp_status_t sp_spmm_balanced(int m, int k, int n, int nnz, const int *row_indices,
                              const float *values, const int *row_offsets,
                              const int *col_indices, const float *b, float *c,
