@@ -401,6 +401,33 @@ sp_status_t sp_spmm_kernel_name(int m, int k, int n, int nnz, const int *row_ind
                                 const float *c, int batch, long long stride_values,
                                 long long stride_b, long long stride_c, const char **name);
 
+/* The name of the kernel sp_sddmm_general (and, for fp32 X and Y,
+ * sp_sddmm_batched, sp_sddmm_ex) would run for these arguments:
+ *   "multirow"  several short rows per wave (fp32, 16-byte-aligned X and Y,
+ *               d a multiple of 4 from 20 to 64, row slots not split);
+ *   "rows"      one wave per row slot;
+ *   "split"     one batch entry whose rows average 16 entries or more: a
+ *               row's 64-entry windows spread over a workgroup of 4 waves;
+ *   "columns"   Y stored d x k, lanes over entries (no workspace);
+ *   "dk_panel"  Y stored d x k, the touched columns staged per row panel;
+ *   "dk_tile"   Y stored d x k, dense enough for X and Y tiles in LDS;
+ *   "fill"      d = 0 with no mask values and beta = 0 (outputs set to 0);
+ *   "none"      nothing to launch (m, nnz or batch is 0);
+ *   "unsupported" sizes beyond the launch limits.
+ * With a d x k Y and a workspace, the names are those of the k x d kernels
+ * run after the transpose.  The choice depends on the sizes, the element
+ * type, the batch and strides, whether mask_values and workspace are NULL,
+ * beta == 0, y_layout and the alignment of x, y and the workspace; no array
+ * is dereferenced (NULL is accepted where sp_sddmm_general would accept it).
+ * It may read the current device's compute-unit count and LDS size.
+ * Host-only; enqueues nothing.  An unknown dtype, invalid arguments or NULL
+ * `name` return SP_ERROR_INVALID_VALUE. */
+sp_status_t sp_sddmm_kernel_name(int m, int k, int d, int nnz, int dtype,
+                                 const float *mask_values, const void *x, const void *y,
+                                 int y_layout, float beta, int batch, long long stride_values,
+                                 long long stride_x, long long stride_y, long long stride_out,
+                                 void *workspace, size_t workspace_bytes, const char **name);
+
 /* sp_sddmm_batched with X and Y of element type `dtype` (strides in elements
  * of that type); out is fp32.  SP_DTYPE_F32 is exactly sp_sddmm_batched.  An
  * unknown dtype returns SP_ERROR_INVALID_VALUE. */

@@ -36,7 +36,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     declared = _declared_functions()
-    assert len(declared) == 28, declared
+    assert len(declared) == 29, declared
     assert sorted(binding.SIGNATURES) == declared
     for name in declared:
         assert getattr(lib, name) is not None
@@ -362,6 +362,40 @@ def test_spmm_kernel_name(lib):
     assert f(8, 8, 4, 8, NULL, 7, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == INVALID
     assert f(-1, 8, 4, 8, NULL, 0, al, al, al, al, 1, 0, 0, 0, ctypes.byref(name)) == INVALID
     assert f(8, 8, 4, 8, NULL, 0, al, al, al, al, 1, 0, 0, 0, None) == INVALID
+
+
+def test_sddmm_kernel_name(lib):
+    f = lib.sp_sddmm_kernel_name
+    name = ctypes.c_char_p()
+    al = ctypes.c_void_p(0x10000)                     # 16-byte aligned stand-ins
+    odd = ctypes.c_void_p(0x10004)
+    nm = lambda: name.value
+
+    def call(m, k, d, nnz, dtype=0, mask=NULL, x=al, y=al, layout=0, beta=0.0, batch=1,
+             sv=0, sx=0, sy=0, so=0, ws=NULL, ws_bytes=0, out=True):
+        return f(m, k, d, nnz, dtype, mask, x, y, layout, beta, batch, sv, sx, sy, so, ws,
+                 ws_bytes, ctypes.byref(name) if out else None)
+
+    # sparse-attention scores: 32 heads, d = 64, ~80 entries per row
+    assert call(4096, 4096, 64, 325664, batch=32, sx=4096 * 64, sy=4096 * 64,
+                so=325664) == OK and nm() == b"multirow"
+    assert call(100, 100, 20, 500) == OK and nm() == b"multirow"   # d = 20: groups of 8
+    # one batch entry whose rows average 16 entries or more: split over waves
+    assert call(64, 64, 64, 64 * 16) == OK and nm() == b"split"
+    # d = 16 (4 lanes per entry), d = 68 (two vectors per lane), misaligned X, bf16:
+    # one row per wave
+    assert call(100, 100, 16, 500) == OK and nm() == b"rows"
+    assert call(100, 100, 68, 500) == OK and nm() == b"rows"
+    assert call(100, 100, 64, 500, x=odd) == OK and nm() == b"rows"
+    assert call(100, 100, 64, 500, dtype=2) == OK and nm() == b"rows"
+    assert call(100, 100, 0, 500) == OK and nm() == b"fill"
+    assert call(100, 100, 64, 500, layout=1) == OK and nm() in (b"dk_panel", b"dk_tile",
+                                                                   b"columns")
+    assert call(0, 100, 64, 500) == OK and nm() == b"none"
+    assert call(100, 100, 64, 500, dtype=7) == INVALID
+    assert call(-1, 100, 64, 500) == INVALID
+    assert call(100, 100, 64, 500, layout=2) == INVALID
+    assert call(100, 100, 64, 500, out=False) == INVALID
 
 
 def test_row_swizzle_noalloc_validation(lib):

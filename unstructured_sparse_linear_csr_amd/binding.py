@@ -80,6 +80,9 @@ SIGNATURES = {
     "sp_spmm_kernel_name": ([_c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp,
                              _c_int, _c_ll, _c_ll, _c_ll,
                              ctypes.POINTER(ctypes.c_char_p)], _c_int),
+    "sp_sddmm_kernel_name": ([_c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int,
+                              _c_float, _c_int, _c_ll, _c_ll, _c_ll, _c_ll, _vp, ctypes.c_size_t,
+                              ctypes.POINTER(ctypes.c_char_p)], _c_int),
     "sp_sddmm_ex": ([_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
                      _c_float, _vp, _c_int, _c_ll, _c_ll, _c_ll, _vp], _c_int),
 }
@@ -330,6 +333,25 @@ def sp_spmm_kernel_name(m, k, n, nnz, values, col_indices, b, c, batch=1, stride
                                      addr(col_indices), addr(b), addr(c), batch, stride_values,
                                      stride_b, stride_c, ctypes.byref(name)),
            "sp_spmm_kernel_name")
+    return name.value.decode()
+
+
+def sp_sddmm_kernel_name(m, k, d, nnz, x, y, batch=1, stride_x=0, stride_y=0, stride_out=0,
+                         mask_values=None, stride_values=0, beta=0.0, y_layout=SP_Y_KD,
+                         workspace=None, dtype=None) -> str:
+    """The kernel sp_sddmm_general would run for these tensors (sizes,
+    alignment, mask values, beta, Y's layout and the workspace)."""
+    if dtype is None:
+        dtype = {torch.float32: SP_DTYPE_F32, torch.float16: SP_DTYPE_F16,
+                 torch.bfloat16: SP_DTYPE_BF16}[x.dtype]
+    name = ctypes.c_char_p()
+    addr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else None)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().sp_sddmm_kernel_name(m, k, d, nnz, dtype, addr(mask_values), addr(x), addr(y),
+                                      y_layout, float(beta), batch, stride_values, stride_x,
+                                      stride_y, stride_out, addr(workspace), ws_bytes,
+                                      ctypes.byref(name)),
+           "sp_sddmm_kernel_name")
     return name.value.decode()
 
 

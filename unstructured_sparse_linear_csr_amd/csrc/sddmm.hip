@@ -30,6 +30,146 @@ __global__ __launch_bounds__(kSplitParts * kWave) void sddmm_split_kernel(SddmmP
     sddmm_rows_body<E, kG, kNv, kVec, false, kSplitParts>(p, rows_work(p, blockIdx.x));
 }
 
+// Many short rows of small depth (fp32, 16-byte vectors, d <= 4 kG): kR =
+// 64 / kG rows per wave, one per group of kG lanes, lane gl of a group holding
+// X[row][4 gl .. 4 gl + 3] in registers.  One wave per row (the kernels
+// above) pays the row's dependent start -- row order, offsets, X, column
+// window, staging -- once per row; with tens of thousands of rows of a few
+// dozen entries (sparse attention: 32 heads x 4096 rows of ~80) that start,
+// repeated round after round of resident waves, is most of the time.  Here a
+// wave takes kR rows at once and walks them together: chunk c of a group's
+// row is its entries c kG ... c kG + kG - 1, one column index per lane
+// (read one chunk ahead); step t of the chunk gathers entry t's Y row (kG
+// lanes x 16 bytes, its offset taken from lane t by ds_bpermute), takes the
+// lane's 4-element dot product and the group's butterfly sum, and lane t
+// keeps it; after kG steps each lane writes its entry.  Steps are issued in
+// double-buffered batches of kU.  Every load and store goes through a buffer
+// resource, with an out-of-range offset for lanes and entries that have none
+// (read as zero, store dropped), so nothing branches on lane data.  Each
+// output is summed exactly as the one-row kernels sum it (V::dot over the
+// lane's vector, then group_sum<kG>), so results are bit-identical to them.
+template <int kG>
+__global__ __launch_bounds__(kWave) void sddmm_multirow_kernel(SddmmParams p)
+{
+    constexpr int kR = kWave / kG;   // rows per wave
+    constexpr int kC = kG;           // entries per chunk: one column index per lane
+    constexpr int kU = 4;            // steps per batch of gathers
+    constexpr int kBpc = kC / kU;    // batches per chunk
+    static_assert(kC % kU == 0, "whole batches per chunk");
+    using V = GVec<float, 4>;
+
+    const long long units = ((long long)p.m + kR - 1) / kR;
+    const long long w = xcd_work_index(p.batch, units);
+    if (w < 0) return;
+    const long long z = w / units;
+    const int unit = (int)(w - z * units);
+    const int lane = threadIdx.x;
+    const int grp = lane / kG;
+    const int gl = lane - grp * kG;
+
+    // this group's row; a slot past m takes slot 0's row as a stand-in, with
+    // no entries (loads stay unconditional and in bounds)
+    const int slot = unit * kR + grp;
+    const bool has = slot < p.m;
+    const int sl = has ? slot : 0;
+    const int *rsrc = p.row_indices ? p.row_indices : p.row_offsets;
+    const int rv = rsrc[sl];
+    const int row = p.row_indices ? rv : sl;
+    const int p0 = p.row_offsets[row];
+    const int len = has ? p.row_offsets[row + 1] - p0 : 0;
+
+    const unsigned rowbytes = (unsigned)p.d * 4u;
+    const float *xz = static_cast<const float *>(p.x) + z * p.stride_x;
+    const float *yz = static_cast<const float *>(p.y) + z * p.stride_y;
+    float *oz = p.out + z * p.stride_out;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(xz), 0, (int)((unsigned)p.m * rowbytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(yz), 0, (int)p.y_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int *>(p.col_indices), 0, (int)((unsigned)p.nnz * 4u), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ro =
+        __builtin_amdgcn_make_buffer_rsrc(oz, 0, (int)((unsigned)p.nnz * 4u), 0x00020000);
+
+    // lanes past d (d < 4 kG) gather nothing: their offsets get the top bit
+    const bool lane_ok = 4 * gl < p.d;
+    const unsigned lane_mask = lane_ok ? 0u : kOutOfRange;
+    const V::T xr = V::buf_load(rx, has && lane_ok ? (unsigned)row * rowbytes + 16u * gl
+                                                   : kOutOfRange);
+
+    // chunk c's Y-row offset of this lane's entry (out of range past the row)
+    auto chunk_offsets = [&](int c) -> unsigned {
+        const int j = c * kC + gl;
+        const bool ok = j < len;
+        const unsigned col =
+            __builtin_amdgcn_raw_buffer_load_b32(rc, (int)(ok ? (unsigned)(p0 + j) * 4u : kOutOfRange), 0, 0);
+        return col * rowbytes + (ok ? 0u : kOutOfRange);
+    };
+    // chunks of the wave: the most any of its rows needs (wave-uniform)
+    const int nch = __builtin_amdgcn_readfirstlane(
+        group_reduce<kWave>((len + kC - 1) / kC, OpMax{}));
+    if (nch == 0) return;
+    const int batches = nch * kBpc;
+
+    unsigned off_c = chunk_offsets(0);  // the current chunk's offsets
+    unsigned off_n = chunk_offsets(1);  // the next chunk's
+    const int src0 = 4 * grp * kG;      // ds_bpermute byte address of lane 0 of the group
+    auto issue = [&](int b, V::T (&yy)[kU]) {
+        // batch b: steps (b % kBpc) kU ... of chunk b / kBpc, whose offsets are
+        // off_c, or off_n for the first batch of the next chunk
+        const unsigned src = (b % kBpc == 0 && b > 0) ? off_n : off_c;
+        const int t0 = (b % kBpc) * kU;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const unsigned o = (unsigned)__builtin_amdgcn_ds_bpermute(src0 + 4 * (t0 + u), (int)src);
+            // (a batch past the last reads out of range: zeros, no branch)
+            yy[u] = V::buf_load(ry, b < batches ? (o + 16u * gl) | lane_mask : kOutOfRange);
+        }
+    };
+    float res = 0.f;
+    auto consume = [&](int b, const V::T (&yy)[kU]) {
+        const int t0 = (b % kBpc) * kU;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const float sum = group_sum<kG>(V::dot(xr, yy[u], 0.f));
+            res = gl == t0 + u ? sum : res;
+        }
+        if (b % kBpc == kBpc - 1) {
+            // the chunk is done: lane gl holds its entry's sum
+            const int c = b / kBpc;
+            const int j = c * kC + gl;
+            const unsigned oo = j < len ? (unsigned)(p0 + j) * 4u : kOutOfRange;
+            float scale = p.alpha;
+            if (p.mask_values) {
+                const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<float *>(p.mask_values + z * p.stride_values), 0,
+                    (int)((unsigned)p.nnz * 4u), 0x00020000);
+                scale *= __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, (int)oo, 0, 0));
+            }
+            float r = scale * res;
+            if (p.beta != 0.f)
+                r = fmaf(p.beta, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, (int)oo, 0, 0)), r);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(r), ro, (int)oo, 0, 0);
+            off_c = off_n;
+            off_n = chunk_offsets(c + 2);
+        }
+    };
+
+    V::T ya[kU], yb[kU];
+    issue(0, ya);
+    // one exit, at the end (a second exit would leave pending loads on an
+    // edge into the loop header, and the compiler would then wait for every
+    // load in flight at its top)
+    for (int b = 0; b < batches; b += 2) {
+        issue(b + 1, yb);
+        keep_issued_above();
+        consume(b, ya);
+        issue(b + 2, ya);
+        keep_issued_above();
+        consume(b + 1, yb);
+    }
+}
+
 // Y stored d x k (the operand not transposed): Yop(c, l) = Y[l][c].  One wave
 // per row slot as above, but lanes are dealt to entries, 64 at a time: for each
 // l the wave gathers Y[l][c] of its 64 columns -- all within row l of Y, whose
@@ -877,6 +1017,17 @@ hipError_t launch_t(const SddmmParams &p, bool split, hipStream_t s)
     return hipGetLastError();
 }
 
+hipError_t launch_multirow(int g, const SddmmParams &p, hipStream_t s)
+{
+    const long long units = ((long long)p.m + kWave / g - 1) / (kWave / g);
+    const dim3 grid((unsigned)xcd_grid(p.batch, units));
+    if (g == 8)
+        hipLaunchKernelGGL(sddmm_multirow_kernel<8>, grid, dim3(kWave), 0, s, p);
+    else
+        hipLaunchKernelGGL(sddmm_multirow_kernel<16>, grid, dim3(kWave), 0, s, p);
+    return hipGetLastError();
+}
+
 template <typename E, int kG, int kVec, bool kSm>
 hipError_t launch_nv(int nv, const SddmmParams &p, bool split, hipStream_t s)
 {
@@ -1069,6 +1220,7 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
     plan->dtype = a.dtype;
     plan->softmax = false;
     plan->split = false;
+    plan->multirow = false;
     plan->t_src = nullptr;
     plan->t_src_stride = 0;
     plan->t_batch = 0;
@@ -1141,6 +1293,15 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
     plan->vec = vec;
     plan->g = g;
     plan->nv = nv;
+    // Rows of at most 64 fp32 (one vector per lane, 8 or 16 lanes per entry)
+    // not split over waves: several rows per wave (sddmm_multirow_kernel).
+    // Its buffer resources need X, Y and the outputs of one batch entry under
+    // 2 GiB.
+    const int rpw = kWave / g;
+    plan->multirow = a.dtype == Dtype::f32 && vec && !a.softmax && !plan->split && nv == 1 &&
+                     (g == 8 || g == 16) && buf && (long long)a.nnz * 4 < (1LL << 31) &&
+                     (long long)a.m * a.d * 4 < (1LL << 31) &&
+                     xcd_grid(a.batch, ((long long)a.m + rpw - 1) / rpw) <= 0x7fffffffLL;
     return hipSuccess;
 }
 
@@ -1186,6 +1347,7 @@ hipError_t run_sddmm(const SddmmPlan &plan, hipStream_t stream)
     default:
         break;
     }
+    if (plan.multirow) return launch_multirow(plan.g, p, stream);
     const bool sm = plan.softmax, sp = plan.split;
     switch (plan.dtype) {
     case Dtype::f16:
@@ -1193,6 +1355,21 @@ hipError_t run_sddmm(const SddmmPlan &plan, hipStream_t stream)
     case Dtype::bf16: return launch_typed<bf16, 8>(plan.vec, sm, sp, plan.g, plan.nv, p, stream);
     default: return launch_typed<float, 4>(plan.vec, sm, sp, plan.g, plan.nv, p, stream);
     }
+}
+
+const char *sddmm_kernel_name(const SddmmArgs &a)
+{
+    SddmmPlan plan;
+    if (plan_sddmm(a, &plan) != hipSuccess) return "unsupported";
+    switch (plan.kind) {
+    case SddmmPlan::kNothing: return "none";
+    case SddmmPlan::kFill: return "fill";
+    case SddmmPlan::kCols: return "columns";
+    case SddmmPlan::kDkPanel: return "dk_panel";
+    case SddmmPlan::kDkTile: return "dk_tile";
+    case SddmmPlan::kRows: return plan.multirow ? "multirow" : plan.split ? "split" : "rows";
+    }
+    return "unknown";
 }
 
 hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream)

@@ -282,6 +282,29 @@ sp_status_t sp_spmm_kernel_name(int m, int k, int n, int nnz, const int *row_ind
     return SP_SUCCESS;
 }
 
+sp_status_t sp_sddmm_kernel_name(int m, int k, int d, int nnz, int dtype,
+                                 const float *mask_values, const void *x, const void *y,
+                                 int y_layout, float beta, int batch, long long stride_values,
+                                 long long stride_x, long long stride_y, long long stride_out,
+                                 void *workspace, size_t workspace_bytes, const char **name)
+{
+    if (name == nullptr) return SP_ERROR_INVALID_VALUE;
+    spk::Dtype dt;
+    if (!dtype_of(dtype, &dt)) return SP_ERROR_INVALID_VALUE;
+    // As for SpMM: the arrays the plan does not look at get stand-ins.
+    static const int kStandIn[2] = {0, 0};
+    static float kOutStandIn[1] = {0.f};
+    spk::SddmmArgs a;
+    bool work = false;
+    const sp_status_t st = sddmm_prepare(m, k, d, nnz, nullptr, kStandIn, kStandIn, mask_values,
+                                         dt, x, y, y_layout, 1.f, beta, kOutStandIn, batch,
+                                         stride_values, stride_x, stride_y, stride_out, &a,
+                                         &work, workspace, workspace_bytes);
+    if (st != SP_SUCCESS) return st;
+    *name = work ? spk::sddmm_kernel_name(a) : "none";
+    return SP_SUCCESS;
+}
+
 sp_status_t sp_spmm_sddmm(int m, int k, int n, int nnz, const int *row_indices,
                           const float *values, const int *row_offsets, const int *col_indices,
                           const float *b, float *c, int s_m, int s_k, int d, int s_nnz,

@@ -81,6 +81,7 @@ hipError_t launch_row_swizzle_noalloc(int m, int k, const int *row_offsets, int 
 hipError_t launch_spmm(const SpmmArgs &a, hipStream_t stream);
 // Name of the kernel launch_spmm would run for `a` (host-only).
 const char *spmm_kernel_name(const SpmmArgs &a);
+const char *sddmm_kernel_name(const SddmmArgs &a);
 hipError_t launch_sddmm(const SddmmArgs &a, hipStream_t stream);
 hipError_t launch_spmm_sddmm(const SpmmArgs &x, const SddmmArgs &y, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream);

@@ -42,6 +42,7 @@ struct SddmmPlan {
     bool vec, buf;
     bool softmax;  // rows kernel: row softmax of the scores before they are written
     bool split;    // rows kernel: a workgroup of waves per row, sharing its windows
+    bool multirow; // rows kernel: several rows per wave (small depth, many short rows)
     int g, nv;     // rows kernel: lanes per entry, vectors per lane (0: generic loop)
     // Y stored d x k with a workspace: transpose it into p.y first
     const void *t_src;        // NULL: no transpose
