@@ -378,6 +378,9 @@ def test_sddmm_kernel_name(lib):
 
     # sparse-attention scores: 32 heads, d = 64, ~80 entries per row
     assert call(4096, 4096, 64, 325664, batch=32, sx=4096 * 64, sy=4096 * 64,
+                so=325664) == OK and nm() == b"panel_union"
+    # the same beyond the panel-union kernel's 65,536 columns: several rows per wave
+    assert call(4096, 65537, 64, 325664, batch=32, sx=4096 * 64, sy=65537 * 64,
                 so=325664) == OK and nm() == b"multirow"
     assert call(100, 100, 20, 500) == OK and nm() == b"multirow"   # d = 20: groups of 8
     # one batch entry whose rows average 16 entries or more: split over waves

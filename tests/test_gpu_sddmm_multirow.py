@@ -2,9 +2,9 @@
 
 It takes fp32 problems whose depth d is a multiple of 4 from 20 to 64 (8 or 16
 lanes per entry, one 16-byte vector of the X row per lane) when row slots are
-not split over waves: sparse-attention scores are the case it is built for
-(SDDMM as used for the attention scores, "Sparse GPU Kernels for Deep
-Learning", Sections 5 and 7.3).  Each output is summed exactly as the one-row
+not split over waves (SDDMM, "Sparse GPU Kernels for Deep Learning", Section
+5).  Batched problems on at most 65,536 columns take the panel-union kernel
+(its own tests), so the batched cases here use K = 65,600 columns.  Each output is summed exactly as the one-row
 kernels sum it, so the default entry points' results must equal, bit for bit,
 those of sp_sddmm_balanced (one batch entry, a row's windows split over a
 workgroup of waves, which never takes this kernel), and both must meet the
@@ -23,6 +23,8 @@ from gpu_util import DevCsr, check_close, csr_of_row_lists, dev, host, note
 
 pytestmark = pytest.mark.gpu
 
+# beyond the panel-union kernel's 65,536 columns
+WIDE_K = 65600
 # row lengths around the chunk (8 or 16 entries) and batch (4 entries) sizes
 MIXED = [0, 1, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 0, 2]
 
@@ -78,26 +80,12 @@ def check_entry(a: DevCsr, got, x, y, alpha, ri, what):
     check_close(got, alpha * s, abs(alpha) * s_abs, what)
 
 
-def test_attention_heads():
-    """Four heads of the sparse-attention scores (seq 4096, head dim 64, band-plus-
-    stride mask), swizzled rows, alpha = 1/8."""
-    w = inputs.sparse_attention(batch=1, heads=4)
-    ro, ci, _ = oracle.csr_from_dense(w["mask"])
-    a = DevCsr(w["seq"], w["seq"], ro, ci)
-    ri = swizzle(a)
-    note(f"multirow sddmm attention 4 heads nnz={a.nnz}")
-    got, name = batched(a, list(w["q"]), list(w["k"]), 0.125, ri)
-    assert name == "multirow"
-    for z in range(4):
-        check_entry(a, got[z], w["q"][z], w["k"][z], 0.125, ri, f"head {z}")
-
-
 @pytest.mark.parametrize("d", [20, 24, 28, 32, 36, 44, 48, 60, 64])
 def test_depths_and_lengths(d):
     """Every depth the kernel takes (8 lanes per entry up to d = 32, 16 above),
     lanes past d idle, rows of 0 to 100 entries, m not a multiple of the rows
     per wave, three batch entries with their own X and Y."""
-    a = mixed_csr(d, 301, 777)
+    a = mixed_csr(d, 301, WIDE_K)
     xs = [inputs.random_dense(100 * d + z, a.m, d) for z in range(3)]
     ys = [inputs.random_dense(200 * d + z, a.k, d) for z in range(3)]
     note(f"multirow sddmm d={d} m={a.m} nnz={a.nnz}")
@@ -111,7 +99,7 @@ def test_depths_and_lengths(d):
 def test_shared_operand(shared):
     """One X (or one Y) shared by every batch entry (stride 0)."""
     d = 64
-    a = mixed_csr(7, 123, 500)
+    a = mixed_csr(7, 123, WIDE_K)
     xs = [inputs.random_dense(10 + z, a.m, d) for z in range(3)]
     ys = [inputs.random_dense(20 + z, a.k, d) for z in range(3)]
     if shared == "x":
@@ -134,7 +122,7 @@ def test_shared_operand(shared):
 ])
 @pytest.mark.parametrize("d", [32, 64])
 def test_ragged(m, lengths, d):
-    a = mixed_csr(m + d, m, 2500, lengths)
+    a = mixed_csr(m + d, m, WIDE_K, lengths)
     x = inputs.random_dense(1 + m, m, d)
     y = inputs.random_dense(2 + m, a.k, d)
     note(f"multirow sddmm ragged m={m} d={d} nnz={a.nnz}")
@@ -177,6 +165,11 @@ def test_not_taken_outside_its_shapes():
         y = torch.zeros(nb, a.k, d, device="cuda")
         name = sp.sp_sddmm_kernel_name(a.m, a.k, d, a.nnz, x, y, nb, a.m * d, a.k * d, a.nnz)
         assert name == ("split" if nb == 1 else "rows"), (d, nb, name)
+    # one batch entry of short rows: this kernel
+    s = mixed_csr(6, 64, 300, [3])
+    x = torch.zeros(s.m, 64, device="cuda")
+    y = torch.zeros(s.k, 64, device="cuda")
+    assert sp.sp_sddmm_kernel_name(s.m, s.k, 64, s.nnz, x, y) == "multirow"
     xb = torch.zeros(2, a.m, 64, device="cuda", dtype=torch.bfloat16)
     yb = torch.zeros(2, a.k, 64, device="cuda", dtype=torch.bfloat16)
     assert sp.sp_sddmm_kernel_name(a.m, a.k, 64, a.nnz, xb, yb, 2, a.m * 64, a.k * 64,

@@ -48,33 +48,22 @@ __global__ __launch_bounds__(kSplitParts * kWave) void sddmm_split_kernel(SddmmP
 // (read as zero, store dropped), so nothing branches on lane data.  Each
 // output is summed exactly as the one-row kernels sum it (V::dot over the
 // lane's vector, then group_sum<kG>), so results are bit-identical to them.
+//
+// multirow_rows is the walk of one wave over its rows (batch entry z; the
+// group of lane l takes `row` if `has`, else nothing); the kernel maps row
+// slots to rows through the row order.
 template <int kG>
-__global__ __launch_bounds__(kWave) void sddmm_multirow_kernel(SddmmParams p)
+__device__ __forceinline__ void multirow_rows(const SddmmParams &p, long long z, bool has,
+                                              int row)
 {
-    constexpr int kR = kWave / kG;   // rows per wave
     constexpr int kC = kG;           // entries per chunk: one column index per lane
     constexpr int kU = 4;            // steps per batch of gathers
     constexpr int kBpc = kC / kU;    // batches per chunk
     static_assert(kC % kU == 0, "whole batches per chunk");
     using V = GVec<float, 4>;
-
-    const long long units = ((long long)p.m + kR - 1) / kR;
-    const long long w = xcd_work_index(p.batch, units);
-    if (w < 0) return;
-    const long long z = w / units;
-    const int unit = (int)(w - z * units);
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x % kWave;
     const int grp = lane / kG;
     const int gl = lane - grp * kG;
-
-    // this group's row; a slot past m takes slot 0's row as a stand-in, with
-    // no entries (loads stay unconditional and in bounds)
-    const int slot = unit * kR + grp;
-    const bool has = slot < p.m;
-    const int sl = has ? slot : 0;
-    const int *rsrc = p.row_indices ? p.row_indices : p.row_offsets;
-    const int rv = rsrc[sl];
-    const int row = p.row_indices ? rv : sl;
     const int p0 = p.row_offsets[row];
     const int len = has ? p.row_offsets[row + 1] - p0 : 0;
 
@@ -167,6 +156,228 @@ __global__ __launch_bounds__(kWave) void sddmm_multirow_kernel(SddmmParams p)
         issue(b + 2, ya);
         keep_issued_above();
         consume(b + 1, yb);
+    }
+}
+
+template <int kG>
+__global__ __launch_bounds__(kWave) void sddmm_multirow_kernel(SddmmParams p)
+{
+    constexpr int kR = kWave / kG;   // rows per wave
+    const long long units = ((long long)p.m + kR - 1) / kR;
+    const long long w = xcd_work_index(p.batch, units);
+    if (w < 0) return;
+    const long long z = w / units;
+    const int unit = (int)(w - z * units);
+    // this group's row; a slot past m takes slot 0's row as a stand-in, with
+    // no entries (loads stay unconditional and in bounds)
+    const int slot = unit * kR + (int)threadIdx.x / kG;
+    const bool has = slot < p.m;
+    const int sl = has ? slot : 0;
+    const int *rsrc = p.row_indices ? p.row_indices : p.row_offsets;
+    const int rv = rsrc[sl];
+    multirow_rows<kG>(p, z, has, p.row_indices ? rv : sl);
+}
+
+// Batched scores on masks whose neighbouring rows share most of their columns
+// (sparse attention's band): a workgroup of kUnWaves waves takes a panel of
+// kUnRows consecutive rows and kUnWaves batch entries, one per wave.  It first
+// forms the union of the panel's columns once for all of them: a bitmap of the
+// k columns in LDS, each set bit's rank (a prefix sum of the words' popcounts)
+// its slot in the union, the union's columns in slot order, and for every
+// (panel row, slot) the entry it holds, if any.  Each wave then computes the
+// dense 16 x U block X[panel] Y[union]^T of its batch entry in 16 x 16 tiles
+// with v_mfma_f32_16x16x4f32 -- every union column's Y row is loaded once per
+// panel instead of once per entry -- and stores the tile values that are mask
+// entries.  The 64 lanes split d four ways (lane l holds elements
+// kG (l/16) ... kG (l/16) + kG - 1 of X's row l % 16 and of union column
+// 16 T + l % 16's Y row); MFMA step t multiplies element kG q + t of both, so
+// the kG steps of a tile cover all of d.  A panel whose union is large against
+// its entry count (tile slots above kUnReuse per entry, or more than
+// kUnMaxCols columns) would spend more on products no entry needs than a
+// per-entry gather costs; its waves run the multi-row walk above on the
+// panel's rows instead.  Y rows that a tile's padding columns or lanes past d
+// would read come from an out-of-range buffer offset (zeros), and only mask
+// entries are stored.  Sums differ in rounding from the per-entry kernels
+// (the MFMA's accumulation order), within the same bound.
+constexpr int kUnRows = 16;          // rows per panel: the MFMA tile's height
+constexpr int kUnWaves = 4;          // batch entries per workgroup, one per wave
+constexpr int kUnThreads = kUnWaves * kWave;
+constexpr int kUnMaxCols = 256;      // distinct columns per panel on the tile path
+constexpr int kUnMaxK = 65536;       // columns the LDS bitmap covers
+constexpr int kUnReuse = 6;          // tile slots per entry the tile path accepts
+
+// Dynamic LDS of the union kernel: the bitmap and its per-word ranks.
+size_t union_dynamic_lds(int k) { return 2 * sizeof(unsigned) * (size_t)((k + 31) / 32); }
+
+template <int kG>
+__global__ __launch_bounds__(kUnThreads) void sddmm_union_kernel(SddmmParams p)
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    using V = GVec<float, 4>;
+    constexpr int kS = kG;   // MFMA steps per tile: elements of d per lane
+    __shared__ unsigned short s_emap[kUnRows * kUnMaxCols];  // 1 + entry - e0, 0 = none
+    __shared__ int s_ucol[kUnMaxCols];
+    __shared__ int s_ro[kUnRows + 1];
+    __shared__ int s_wsum[kUnWaves];
+    extern __shared__ unsigned s_dyn[];
+    const int nw = (p.k + 31) >> 5;
+    unsigned *s_bits = s_dyn;
+    unsigned *s_rank = s_dyn + nw;
+
+    const int panels = (p.m + kUnRows - 1) / kUnRows;
+    const int groups = (p.batch + kUnWaves - 1) / kUnWaves;
+    const long long w = xcd_work_index(groups, panels);
+    if (w < 0) return;
+    const int hg = (int)(w / panels);
+    const int r0 = (int)(w - (long long)hg * panels) * kUnRows;
+    const int nr = min(kUnRows, p.m - r0);
+    const int tid = threadIdx.x;
+    // (uniform in the wave; the buffer resources below depend on it)
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
+
+    if (tid <= kUnRows) s_ro[tid] = p.row_offsets[r0 + min(tid, nr)];
+    for (int i = tid; i < nw; i += kUnThreads) s_bits[i] = 0u;
+    __syncthreads();
+    const int e0 = s_ro[0];
+    const int pn = s_ro[kUnRows] - e0;
+    if (pn == 0) return;  // every thread: the panel has no entries
+    // mark the panel's columns, 16 threads per row
+    const int mr = tid / 16, mq = tid % 16;
+    for (int j = s_ro[mr] + mq; j < s_ro[mr + 1]; j += 16) {
+        const unsigned c = (unsigned)p.col_indices[j];
+        if (c < (unsigned)p.k) atomicOr(&s_bits[c >> 5], 1u << (c & 31));
+    }
+    __syncthreads();
+    // rank of each word's first bit: this thread's words, then the block's
+    const int wpt = (nw + kUnThreads - 1) / kUnThreads;
+    const int w0 = tid * wpt;
+    int cnt = 0;
+    for (int j = 0; j < wpt; ++j) cnt += w0 + j < nw ? __popc(s_bits[w0 + j]) : 0;
+    const int incl = wave_inclusive_sum(cnt);
+    if (lane == kWave - 1) s_wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - cnt, nu = 0;
+#pragma unroll
+    for (int v = 0; v < kUnWaves; ++v) {
+        run += v < wave ? s_wsum[v] : 0;
+        nu += s_wsum[v];
+    }
+    const int ntiles = (nu + 15) / 16;
+    const bool tiles = nu <= kUnMaxCols && pn < 65535 && 256 * ntiles <= kUnReuse * pn;
+    const int z = hg * kUnWaves + wave;
+    if (!tiles) {
+        // the same decision in every thread: no barrier follows
+        if (z >= p.batch) return;
+        constexpr int kR = kWave / kG;
+#pragma unroll 1
+        for (int u = 0; u < kUnRows / kR; ++u) {
+            const int slot = u * kR + lane / kG;
+            multirow_rows<kG>(p, z, slot < nr, slot < nr ? r0 + slot : r0);
+        }
+        return;
+    }
+    // the union's columns in rank order; the (row, slot) map cleared
+    for (int j = 0; j < wpt; ++j) {
+        const int wi = w0 + j;
+        if (wi < nw) {
+            unsigned bits = s_bits[wi];
+            s_rank[wi] = run;
+            while (bits) {
+                s_ucol[run++] = wi * 32 + __builtin_ctz(bits);
+                bits &= bits - 1u;
+            }
+        }
+    }
+    const int width = ntiles * 16;
+    for (int i = tid; i < kUnRows * width; i += kUnThreads)
+        s_emap[(i / width) * kUnMaxCols + i % width] = 0;
+    __syncthreads();
+    for (int j = s_ro[mr] + mq; j < s_ro[mr + 1]; j += 16) {
+        const unsigned c = (unsigned)p.col_indices[j];
+        if (c < (unsigned)p.k) {
+            const int slot = s_rank[c >> 5] + __popc(s_bits[c >> 5] & ((1u << (c & 31)) - 1u));
+            s_emap[mr * kUnMaxCols + slot] = (unsigned short)(j - e0 + 1);
+        }
+    }
+    __syncthreads();
+    if (z >= p.batch) return;
+
+    const unsigned rowbytes = (unsigned)p.d * 4u;
+    const float *xz = static_cast<const float *>(p.x) + z * p.stride_x;
+    const float *yz = static_cast<const float *>(p.y) + z * p.stride_y;
+    float *oz = p.out + z * p.stride_out;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(xz), 0, (int)((unsigned)p.m * rowbytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(yz), 0, (int)p.y_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ro =
+        __builtin_amdgcn_make_buffer_rsrc(oz, 0, (int)((unsigned)p.nnz * 4u), 0x00020000);
+    const int jl = lane % 16;   // the lane's row of X, column of the tile
+    const int q = lane / 16;    // the lane's quarter of d
+    // byte offsets of the lane's kS / 4 vectors within a row (out of range past d)
+    unsigned voff[kS / 4];
+#pragma unroll
+    for (int v = 0; v < kS / 4; ++v) {
+        const int e = q * kS + 4 * v;
+        voff[v] = e < p.d ? (unsigned)e * 4u : kOutOfRange;
+    }
+    float xa[kS];
+    {
+        const unsigned base = jl < nr ? (unsigned)(r0 + jl) * rowbytes : kOutOfRange;
+#pragma unroll
+        for (int v = 0; v < kS / 4; ++v) {
+            const V::T t = V::buf_load(rx, base + voff[v] | (base & kOutOfRange));
+            memcpy(&xa[4 * v], &t, sizeof(t));
+        }
+    }
+    auto load_tile = [&](int T, float (&yb)[kS]) {
+        const int u = 16 * T + jl;
+        const unsigned base =
+            u < nu ? (unsigned)s_ucol[min(u, kUnMaxCols - 1)] * rowbytes : kOutOfRange;
+#pragma unroll
+        for (int v = 0; v < kS / 4; ++v) {
+            const V::T t = V::buf_load(ry, base + voff[v] | (base & kOutOfRange));
+            memcpy(&yb[4 * v], &t, sizeof(t));
+        }
+    };
+    const float alpha = p.alpha, beta = p.beta;
+    const float *mvz = p.mask_values ? p.mask_values + z * p.stride_values : nullptr;
+    auto tile_out = [&](int T, const float (&yb)[kS]) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < kS; ++t)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[t], yb[t], acc, 0, 0, 0);
+        // lane l holds rows 4 (l / 16) .. + 3 of tile column l % 16
+        const int u = 16 * T + jl;
+        const int uc = min(u, kUnMaxCols - 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const unsigned idx = u < nu ? s_emap[(4 * q + r) * kUnMaxCols + uc] : 0u;
+            const unsigned oo = idx ? (unsigned)(e0 + (int)idx - 1) * 4u : kOutOfRange;
+            float scale = alpha;
+            if (mvz) {
+                const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<float *>(mvz), 0, (int)((unsigned)p.nnz * 4u), 0x00020000);
+                scale *= __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, (int)oo, 0, 0));
+            }
+            float res = scale * acc[r];
+            if (beta != 0.f)
+                res = fmaf(beta, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, (int)oo, 0, 0)),
+                           res);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res), ro, (int)oo, 0, 0);
+        }
+    };
+    float ya[kS], yb[kS];
+    load_tile(0, ya);
+    // one exit, at the end (as in the multi-row walk)
+    for (int T = 0; T < ntiles; T += 2) {
+        load_tile(T + 1, yb);
+        keep_issued_above();
+        tile_out(T, ya);
+        load_tile(T + 2, ya);
+        keep_issued_above();
+        tile_out(T + 1, yb);
     }
 }
 
@@ -1028,6 +1239,19 @@ hipError_t launch_multirow(int g, const SddmmParams &p, hipStream_t s)
     return hipGetLastError();
 }
 
+hipError_t launch_union(int g, const SddmmParams &p, hipStream_t s)
+{
+    const long long panels = ((long long)p.m + kUnRows - 1) / kUnRows;
+    const long long groups = ((long long)p.batch + kUnWaves - 1) / kUnWaves;
+    const dim3 grid((unsigned)xcd_grid(groups, panels));
+    const size_t lds = union_dynamic_lds(p.k);
+    if (g == 8)
+        hipLaunchKernelGGL(sddmm_union_kernel<8>, grid, dim3(kUnThreads), lds, s, p);
+    else
+        hipLaunchKernelGGL(sddmm_union_kernel<16>, grid, dim3(kUnThreads), lds, s, p);
+    return hipGetLastError();
+}
+
 template <typename E, int kG, int kVec, bool kSm>
 hipError_t launch_nv(int nv, const SddmmParams &p, bool split, hipStream_t s)
 {
@@ -1221,6 +1445,7 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
     plan->softmax = false;
     plan->split = false;
     plan->multirow = false;
+    plan->panel_union = false;
     plan->t_src = nullptr;
     plan->t_src_stride = 0;
     plan->t_batch = 0;
@@ -1302,6 +1527,12 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
                      (g == 8 || g == 16) && buf && (long long)a.nnz * 4 < (1LL << 31) &&
                      (long long)a.m * a.d * 4 < (1LL << 31) &&
                      xcd_grid(a.batch, ((long long)a.m + rpw - 1) / rpw) <= 0x7fffffffLL;
+    // Batched problems on up to kUnMaxK columns: the panel-union kernel, which
+    // falls back to the multi-row walk panel by panel where columns are not
+    // shared.  One batch entry would leave three of its four waves idle.
+    plan->panel_union = plan->multirow && a.batch >= 2 && a.k <= kUnMaxK &&
+                        xcd_grid((a.batch + kUnWaves - 1) / kUnWaves,
+                                 ((long long)a.m + kUnRows - 1) / kUnRows) <= 0x7fffffffLL;
     return hipSuccess;
 }
 
@@ -1347,6 +1578,7 @@ hipError_t run_sddmm(const SddmmPlan &plan, hipStream_t stream)
     default:
         break;
     }
+    if (plan.panel_union) return launch_union(plan.g, p, stream);
     if (plan.multirow) return launch_multirow(plan.g, p, stream);
     const bool sm = plan.softmax, sp = plan.split;
     switch (plan.dtype) {
@@ -1367,7 +1599,11 @@ const char *sddmm_kernel_name(const SddmmArgs &a)
     case SddmmPlan::kCols: return "columns";
     case SddmmPlan::kDkPanel: return "dk_panel";
     case SddmmPlan::kDkTile: return "dk_tile";
-    case SddmmPlan::kRows: return plan.multirow ? "multirow" : plan.split ? "split" : "rows";
+    case SddmmPlan::kRows:
+        return plan.panel_union ? "panel_union"
+               : plan.multirow  ? "multirow"
+               : plan.split     ? "split"
+                                : "rows";
     }
     return "unknown";
 }

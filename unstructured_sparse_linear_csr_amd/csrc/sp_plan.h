@@ -43,6 +43,7 @@ struct SddmmPlan {
     bool softmax;  // rows kernel: row softmax of the scores before they are written
     bool split;    // rows kernel: a workgroup of waves per row, sharing its windows
     bool multirow; // rows kernel: several rows per wave (small depth, many short rows)
+    bool panel_union;  // multi-row problems, batched: shared-column panels as MFMA tiles
     int g, nv;     // rows kernel: lanes per entry, vectors per lane (0: generic loop)
     // Y stored d x k with a workspace: transpose it into p.y first
     const void *t_src;        // NULL: no transpose
