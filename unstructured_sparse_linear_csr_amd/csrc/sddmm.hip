@@ -188,10 +188,11 @@ __global__ __launch_bounds__(kWave) void sddmm_multirow_kernel(SddmmParams p)
 // dense 16 x U block X[panel] Y[union]^T of its batch entry in 16 x 16 tiles
 // with v_mfma_f32_16x16x4f32 -- every union column's Y row is loaded once per
 // panel instead of once per entry -- and stores the tile values that are mask
-// entries.  The 64 lanes split d four ways (lane l holds elements
-// kG (l/16) ... kG (l/16) + kG - 1 of X's row l % 16 and of union column
-// 16 T + l % 16's Y row); MFMA step t multiplies element kG q + t of both, so
-// the kG steps of a tile cover all of d.  A panel whose union is large against
+// entries.  The 64 lanes split d four ways: lane l holds, of X's row l % 16
+// and of union column 16 T + l % 16's Y row, elements 16 v + 4 (l / 16) ... + 3
+// for v = 0 ... kG / 4 - 1, so the four lanes of a row read 64 contiguous bytes
+// per instruction; MFMA step 4 v + s multiplies element 16 v + 4 (l / 16) + s of
+// both, and the kG steps of a tile cover all of d.  A panel whose union is large against
 // its entry count (tile slots above kUnReuse per entry, or more than
 // kUnMaxCols columns) would spend more on products no entry needs than a
 // per-entry gather costs; its waves run the multi-row walk above on the
@@ -215,9 +216,12 @@ __global__ __launch_bounds__(kUnThreads) void sddmm_union_kernel(SddmmParams p)
     typedef float f4 __attribute__((ext_vector_type(4)));
     using V = GVec<float, 4>;
     constexpr int kS = kG;   // MFMA steps per tile: elements of d per lane
-    __shared__ unsigned short s_emap[kUnRows * kUnMaxCols];  // 1 + entry - e0, 0 = none
+    constexpr int kCache = 8;  // column indices a thread keeps between the two passes
+    // (row, slot) -> 1 + entry - e0, 0 = none; rows padded by two slots so the
+    // four rows one read instruction touches fall in different banks
+    constexpr int kEmapStride = kUnMaxCols + 2;
+    __shared__ __align__(16) unsigned short s_emap[kUnRows * kEmapStride];
     __shared__ int s_ucol[kUnMaxCols];
-    __shared__ int s_ro[kUnRows + 1];
     __shared__ int s_wsum[kUnWaves];
     extern __shared__ unsigned s_dyn[];
     const int nw = (p.k + 31) >> 5;
@@ -231,20 +235,34 @@ __global__ __launch_bounds__(kUnThreads) void sddmm_union_kernel(SddmmParams p)
     const int hg = (int)(w / panels);
     const int r0 = (int)(w - (long long)hg * panels) * kUnRows;
     const int nr = min(kUnRows, p.m - r0);
+    const int e0 = p.row_offsets[r0];
+    const int pn = p.row_offsets[r0 + nr] - e0;
+    if (pn == 0) return;  // the whole workgroup: the panel has no entries
     const int tid = threadIdx.x;
     // (uniform in the wave; the buffer resources below depend on it)
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
 
-    if (tid <= kUnRows) s_ro[tid] = p.row_offsets[r0 + min(tid, nr)];
-    for (int i = tid; i < nw; i += kUnThreads) s_bits[i] = 0u;
-    __syncthreads();
-    const int e0 = s_ro[0];
-    const int pn = s_ro[kUnRows] - e0;
-    if (pn == 0) return;  // every thread: the panel has no entries
-    // mark the panel's columns, 16 threads per row
+    // 16 threads per panel row; each keeps its first kCache column indices
     const int mr = tid / 16, mq = tid % 16;
-    for (int j = s_ro[mr] + mq; j < s_ro[mr + 1]; j += 16) {
+    const int rb = p.row_offsets[r0 + min(mr, nr)];
+    const int re = p.row_offsets[r0 + min(mr + 1, nr)];
+    unsigned cc[kCache];
+#pragma unroll
+    for (int t = 0; t < kCache; ++t) {
+        const int j = rb + mq + 16 * t;
+        cc[t] = j < re ? (unsigned)p.col_indices[j] : ~0u;
+    }
+    for (int i = tid; i < nw; i += kUnThreads) s_bits[i] = 0u;
+    for (int i = tid; i < kUnRows * kEmapStride / 2; i += kUnThreads)
+        reinterpret_cast<unsigned *>(s_emap)[i] = 0u;
+    __syncthreads();
+    // mark the panel's columns (indices past k, which a valid CSR never has,
+    // are left out)
+#pragma unroll
+    for (int t = 0; t < kCache; ++t)
+        if (cc[t] < (unsigned)p.k) atomicOr(&s_bits[cc[t] >> 5], 1u << (cc[t] & 31));
+    for (int j = rb + mq + 16 * kCache; j < re; j += 16) {
         const unsigned c = (unsigned)p.col_indices[j];
         if (c < (unsigned)p.k) atomicOr(&s_bits[c >> 5], 1u << (c & 31));
     }
@@ -277,7 +295,7 @@ __global__ __launch_bounds__(kUnThreads) void sddmm_union_kernel(SddmmParams p)
         }
         return;
     }
-    // the union's columns in rank order; the (row, slot) map cleared
+    // the union's columns in rank order
     for (int j = 0; j < wpt; ++j) {
         const int wi = w0 + j;
         if (wi < nw) {
@@ -289,16 +307,18 @@ __global__ __launch_bounds__(kUnThreads) void sddmm_union_kernel(SddmmParams p)
             }
         }
     }
-    const int width = ntiles * 16;
-    for (int i = tid; i < kUnRows * width; i += kUnThreads)
-        s_emap[(i / width) * kUnMaxCols + i % width] = 0;
     __syncthreads();
-    for (int j = s_ro[mr] + mq; j < s_ro[mr + 1]; j += 16) {
+    auto slot_of = [&](unsigned c) {
+        return s_rank[c >> 5] + __popc(s_bits[c >> 5] & ((1u << (c & 31)) - 1u));
+    };
+#pragma unroll
+    for (int t = 0; t < kCache; ++t)
+        if (cc[t] < (unsigned)p.k)
+            s_emap[mr * kEmapStride + slot_of(cc[t])] =
+                (unsigned short)(rb + mq + 16 * t - e0 + 1);
+    for (int j = rb + mq + 16 * kCache; j < re; j += 16) {
         const unsigned c = (unsigned)p.col_indices[j];
-        if (c < (unsigned)p.k) {
-            const int slot = s_rank[c >> 5] + __popc(s_bits[c >> 5] & ((1u << (c & 31)) - 1u));
-            s_emap[mr * kUnMaxCols + slot] = (unsigned short)(j - e0 + 1);
-        }
+        if (c < (unsigned)p.k) s_emap[mr * kEmapStride + slot_of(c)] = (unsigned short)(j - e0 + 1);
     }
     __syncthreads();
     if (z >= p.batch) return;
@@ -314,12 +334,14 @@ __global__ __launch_bounds__(kUnThreads) void sddmm_union_kernel(SddmmParams p)
     const __amdgpu_buffer_rsrc_t ro =
         __builtin_amdgcn_make_buffer_rsrc(oz, 0, (int)((unsigned)p.nnz * 4u), 0x00020000);
     const int jl = lane % 16;   // the lane's row of X, column of the tile
-    const int q = lane / 16;    // the lane's quarter of d
-    // byte offsets of the lane's kS / 4 vectors within a row (out of range past d)
+    const int q = lane / 16;    // which 16-byte piece of each 64-byte block of d
+    // Vector v of the lane holds elements 16 v + 4 q ... + 3 of its X row and of
+    // its Y row, so the four lanes of a row read 64 contiguous bytes; step
+    // 4 v + s of a tile multiplies element 16 v + 4 q + s.  Out of range past d.
     unsigned voff[kS / 4];
 #pragma unroll
     for (int v = 0; v < kS / 4; ++v) {
-        const int e = q * kS + 4 * v;
+        const int e = 16 * v + 4 * q;
         voff[v] = e < p.d ? (unsigned)e * 4u : kOutOfRange;
     }
     float xa[kS];
@@ -353,7 +375,7 @@ __global__ __launch_bounds__(kUnThreads) void sddmm_union_kernel(SddmmParams p)
         const int uc = min(u, kUnMaxCols - 1);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const unsigned idx = u < nu ? s_emap[(4 * q + r) * kUnMaxCols + uc] : 0u;
+            const unsigned idx = u < nu ? s_emap[(4 * q + r) * kEmapStride + uc] : 0u;
             const unsigned oo = idx ? (unsigned)(e0 + (int)idx - 1) * 4u : kOutOfRange;
             float scale = alpha;
             if (mvz) {
