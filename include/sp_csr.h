@@ -384,6 +384,12 @@ sp_status_t sp_spmm_ex(int m, int k, int n, int nnz, const int *row_indices, int
  *               one batch entry, n of at least one 128-column tile, enough
  *               panels to give every CU one, rows per panel times density at
  *               least 4);
+ *   "panel_union" batches (fp32, n = 64, 128 or 256, k <= 65,536): per
+ *               panel of 16 consecutive rows, the union of the rows' columns
+ *               is formed once for 4 batch entries and C[panel] computed as
+ *               matrix-core tiles over it; panels whose rows share few columns
+ *               (or whose union rows of B hold a value that is not finite) run
+ *               the wide kernel's accumulation, bit-identical to "wide";
  *   "narrow"    lanes over entries for B of at most 16 columns;
  *   "lds"       the streaming kernel, narrow B copied into LDS once per CU;
  *   "split"     few long rows cut into four parts per workgroup;
@@ -403,6 +409,11 @@ sp_status_t sp_spmm_kernel_name(int m, int k, int n, int nnz, const int *row_ind
 
 /* The name of the kernel sp_sddmm_general (and, for fp32 X and Y,
  * sp_sddmm_batched, sp_sddmm_ex) would run for these arguments:
+ *   "panel_union" batches in the "multirow" domain with k <= 65,536: per
+ *               panel of 16 consecutive rows, the union of the rows' columns
+ *               is formed once for 4 batch entries and the scores computed as
+ *               matrix-core tiles over it; panels whose rows share few columns
+ *               run the multi-row walk;
  *   "multirow"  several short rows per wave (fp32, 16-byte-aligned X and Y,
  *               d a multiple of 4 from 20 to 64, row slots not split);
  *   "rows"      one wave per row slot;

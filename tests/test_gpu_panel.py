@@ -24,6 +24,7 @@ from gpu_util import DevCsr, check_close, dev, host, note
 pytestmark = pytest.mark.gpu
 
 MANY_KC, FEW_KC = 128, 224    # B rows per chunk of the two shapes
+UNION_MAX_K = 65536           # rows of B up to which batches may take the panel-union kernel
 
 
 def swizzle(a):
@@ -41,11 +42,19 @@ def panel_and_wide(a, b_np, ri=None):
     b = dev(b_np)
     c = torch.full((a.m, n), float("nan"), device="cuda")
     assert sp.sp_spmm_kernel_name(a.m, a.k, n, a.nnz, a.d_vals, a.d_ci, b, c) == "panel"
+    # Batches of 64, 128 or 256 columns on at most 65,536 rows of B take the
+    # panel-union kernel; the reference batch gets B with zero rows appended
+    # past 65,536 (the structure is unchanged), which keeps it on the wide kernel.
+    kk, b_ref = a.k, b
+    if n in (64, 128, 256):
+        kk = UNION_MAX_K + 64
+        b_ref = dev(np.concatenate([b_np, np.zeros((kk - a.k, n), np.float32)]))
     c2 = torch.full((2, a.m, n), float("nan"), device="cuda")
-    other = sp.sp_spmm_kernel_name(a.m, a.k, n, a.nnz, a.d_vals, a.d_ci, b, c2, 2, 0, 0, a.m * n)
+    other = sp.sp_spmm_kernel_name(a.m, kk, n, a.nnz, a.d_vals, a.d_ci, b_ref, c2, 2, 0, 0,
+                                   a.m * n)
     assert other in ("wide", "split")
     sp.sp_spmm(a.m, a.k, n, a.nnz, ri, a.d_vals, a.d_ro, a.d_ci, b, c)
-    sp.sp_spmm_batched(a.m, a.k, n, a.nnz, ri, a.d_vals, a.d_ro, a.d_ci, b, c2, 2, 0, 0,
+    sp.sp_spmm_batched(a.m, kk, n, a.nnz, ri, a.d_vals, a.d_ro, a.d_ci, b_ref, c2, 2, 0, 0,
                        a.m * n)
     c2 = host(c2)
     assert np.array_equal(c2[0].view(np.int32), c2[1].view(np.int32))

@@ -8,6 +8,7 @@
 #include "sp_launch.h"
 #include "sp_types.h"
 #include "sddmm_rows.h"
+#include "panel_union.h"
 #include "sp_plan.h"
 
 namespace spk {
@@ -179,149 +180,52 @@ __global__ __launch_bounds__(kWave) void sddmm_multirow_kernel(SddmmParams p)
 }
 
 // Batched scores on masks whose neighbouring rows share most of their columns
-// (sparse attention's band): a workgroup of kUnWaves waves takes a panel of
-// kUnRows consecutive rows and kUnWaves batch entries, one per wave.  It first
-// forms the union of the panel's columns once for all of them: a bitmap of the
-// k columns in LDS, each set bit's rank (a prefix sum of the words' popcounts)
-// its slot in the union, the union's columns in slot order, and for every
-// (panel row, slot) the entry it holds, if any.  Each wave then computes the
-// dense 16 x U block X[panel] Y[union]^T of its batch entry in 16 x 16 tiles
-// with v_mfma_f32_16x16x4f32 -- every union column's Y row is loaded once per
+// (sparse attention's band).  A workgroup takes a panel of kRows consecutive
+// rows and kWaves batch entries and forms the panel's column union once
+// (panel_union.h).  Each wave then computes the dense 16 x U block
+// X[panel] Y[union]^T of its batch entry in 16 x 16 tiles with
+// v_mfma_f32_16x16x4f32 -- every union column's Y row is loaded once per
 // panel instead of once per entry -- and stores the tile values that are mask
 // entries.  The 64 lanes split d four ways: lane l holds, of X's row l % 16
 // and of union column 16 T + l % 16's Y row, elements 16 v + 4 (l / 16) ... + 3
 // for v = 0 ... kG / 4 - 1, so the four lanes of a row read 64 contiguous bytes
 // per instruction; MFMA step 4 v + s multiplies element 16 v + 4 (l / 16) + s of
-// both, and the kG steps of a tile cover all of d.  A panel whose union is large against
-// its entry count (tile slots above kUnReuse per entry, or more than
-// kUnMaxCols columns) would spend more on products no entry needs than a
-// per-entry gather costs; its waves run the multi-row walk above on the
-// panel's rows instead.  Y rows that a tile's padding columns or lanes past d
-// would read come from an out-of-range buffer offset (zeros), and only mask
-// entries are stored.  Sums differ in rounding from the per-entry kernels
-// (the MFMA's accumulation order), within the same bound.
-constexpr int kUnRows = 16;          // rows per panel: the MFMA tile's height
-constexpr int kUnWaves = 4;          // batch entries per workgroup, one per wave
-constexpr int kUnThreads = kUnWaves * kWave;
-constexpr int kUnMaxCols = 256;      // distinct columns per panel on the tile path
-constexpr int kUnMaxK = 65536;       // columns the LDS bitmap covers
-constexpr int kUnReuse = 6;          // tile slots per entry the tile path accepts
-
-// Dynamic LDS of the union kernel: the bitmap and its per-word ranks.
-size_t union_dynamic_lds(int k) { return 2 * sizeof(unsigned) * (size_t)((k + 31) / 32); }
+// both, and the kG steps of a tile cover all of d.  A panel whose union is too
+// wide for its entry count runs the multi-row walk above on its rows instead.
+// Y rows that a tile's padding columns or lanes past d would read come from an
+// out-of-range buffer offset (zeros), and only mask entries are stored.  Sums
+// differ in rounding from the per-entry kernels (the MFMA's accumulation
+// order), within the same bound.
+namespace pu = panel_union;
 
 template <int kG>
-__global__ __launch_bounds__(kUnThreads) void sddmm_union_kernel(SddmmParams p)
+__global__ __launch_bounds__(pu::kThreads) void sddmm_union_kernel(SddmmParams p)
 {
     typedef float f4 __attribute__((ext_vector_type(4)));
     using V = GVec<float, 4>;
     constexpr int kS = kG;   // MFMA steps per tile: elements of d per lane
-    constexpr int kCache = 8;  // column indices a thread keeps between the two passes
-    // (row, slot) -> 1 + entry - e0, 0 = none; rows padded by two slots so the
-    // four rows one read instruction touches fall in different banks
-    constexpr int kEmapStride = kUnMaxCols + 2;
-    __shared__ __align__(16) unsigned short s_emap[kUnRows * kEmapStride];
-    __shared__ int s_ucol[kUnMaxCols];
-    __shared__ int s_wsum[kUnWaves];
+    __shared__ pu::Shared s;
     extern __shared__ unsigned s_dyn[];
-    const int nw = (p.k + 31) >> 5;
-    unsigned *s_bits = s_dyn;
-    unsigned *s_rank = s_dyn + nw;
-
-    const int panels = (p.m + kUnRows - 1) / kUnRows;
-    const int groups = (p.batch + kUnWaves - 1) / kUnWaves;
-    const long long w = xcd_work_index(groups, panels);
-    if (w < 0) return;
-    const int hg = (int)(w / panels);
-    const int r0 = (int)(w - (long long)hg * panels) * kUnRows;
-    const int nr = min(kUnRows, p.m - r0);
-    const int e0 = p.row_offsets[r0];
-    const int pn = p.row_offsets[r0 + nr] - e0;
-    if (pn == 0) return;  // the whole workgroup: the panel has no entries
-    const int tid = threadIdx.x;
+    pu::Panel pp;
+    if (!pu::panel_of(p.m, p.batch, p.row_offsets, pp)) return;
+    if (pp.pn == 0) return;  // the whole workgroup: nothing to compute
+    const int nu = pu::build(p.row_offsets, p.col_indices, p.k, pp, s, s_dyn);
     // (uniform in the wave; the buffer resources below depend on it)
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int lane = tid % kWave;
-
-    // 16 threads per panel row; each keeps its first kCache column indices
-    const int mr = tid / 16, mq = tid % 16;
-    const int rb = p.row_offsets[r0 + min(mr, nr)];
-    const int re = p.row_offsets[r0 + min(mr + 1, nr)];
-    unsigned cc[kCache];
-#pragma unroll
-    for (int t = 0; t < kCache; ++t) {
-        const int j = rb + mq + 16 * t;
-        cc[t] = j < re ? (unsigned)p.col_indices[j] : ~0u;
-    }
-    for (int i = tid; i < nw; i += kUnThreads) s_bits[i] = 0u;
-    for (int i = tid; i < kUnRows * kEmapStride / 2; i += kUnThreads)
-        reinterpret_cast<unsigned *>(s_emap)[i] = 0u;
-    __syncthreads();
-    // mark the panel's columns (indices past k, which a valid CSR never has,
-    // are left out)
-#pragma unroll
-    for (int t = 0; t < kCache; ++t)
-        if (cc[t] < (unsigned)p.k) atomicOr(&s_bits[cc[t] >> 5], 1u << (cc[t] & 31));
-    for (int j = rb + mq + 16 * kCache; j < re; j += 16) {
-        const unsigned c = (unsigned)p.col_indices[j];
-        if (c < (unsigned)p.k) atomicOr(&s_bits[c >> 5], 1u << (c & 31));
-    }
-    __syncthreads();
-    // rank of each word's first bit: this thread's words, then the block's
-    const int wpt = (nw + kUnThreads - 1) / kUnThreads;
-    const int w0 = tid * wpt;
-    int cnt = 0;
-    for (int j = 0; j < wpt; ++j) cnt += w0 + j < nw ? __popc(s_bits[w0 + j]) : 0;
-    const int incl = wave_inclusive_sum(cnt);
-    if (lane == kWave - 1) s_wsum[wave] = incl;
-    __syncthreads();
-    int run = incl - cnt, nu = 0;
-#pragma unroll
-    for (int v = 0; v < kUnWaves; ++v) {
-        run += v < wave ? s_wsum[v] : 0;
-        nu += s_wsum[v];
-    }
-    const int ntiles = (nu + 15) / 16;
-    const bool tiles = nu <= kUnMaxCols && pn < 65535 && 256 * ntiles <= kUnReuse * pn;
-    const int z = hg * kUnWaves + wave;
-    if (!tiles) {
-        // the same decision in every thread: no barrier follows
-        if (z >= p.batch) return;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int z = pp.hg * pu::kWaves + wave;
+    if (z >= p.batch) return;
+    const int r0 = pp.r0, nr = pp.nr, e0 = pp.e0;
+    if (nu < 0) {
         constexpr int kR = kWave / kG;
 #pragma unroll 1
-        for (int u = 0; u < kUnRows / kR; ++u) {
+        for (int u = 0; u < pu::kRows / kR; ++u) {
             const int slot = u * kR + lane / kG;
             multirow_rows<kG>(p, z, slot < nr, slot < nr ? r0 + slot : r0);
         }
         return;
     }
-    // the union's columns in rank order
-    for (int j = 0; j < wpt; ++j) {
-        const int wi = w0 + j;
-        if (wi < nw) {
-            unsigned bits = s_bits[wi];
-            s_rank[wi] = run;
-            while (bits) {
-                s_ucol[run++] = wi * 32 + __builtin_ctz(bits);
-                bits &= bits - 1u;
-            }
-        }
-    }
-    __syncthreads();
-    auto slot_of = [&](unsigned c) {
-        return s_rank[c >> 5] + __popc(s_bits[c >> 5] & ((1u << (c & 31)) - 1u));
-    };
-#pragma unroll
-    for (int t = 0; t < kCache; ++t)
-        if (cc[t] < (unsigned)p.k)
-            s_emap[mr * kEmapStride + slot_of(cc[t])] =
-                (unsigned short)(rb + mq + 16 * t - e0 + 1);
-    for (int j = rb + mq + 16 * kCache; j < re; j += 16) {
-        const unsigned c = (unsigned)p.col_indices[j];
-        if (c < (unsigned)p.k) s_emap[mr * kEmapStride + slot_of(c)] = (unsigned short)(j - e0 + 1);
-    }
-    __syncthreads();
-    if (z >= p.batch) return;
+    const int ntiles = (nu + 15) / 16;
 
     const unsigned rowbytes = (unsigned)p.d * 4u;
     const float *xz = static_cast<const float *>(p.x) + z * p.stride_x;
@@ -335,9 +239,7 @@ __global__ __launch_bounds__(kUnThreads) void sddmm_union_kernel(SddmmParams p)
         __builtin_amdgcn_make_buffer_rsrc(oz, 0, (int)((unsigned)p.nnz * 4u), 0x00020000);
     const int jl = lane % 16;   // the lane's row of X, column of the tile
     const int q = lane / 16;    // which 16-byte piece of each 64-byte block of d
-    // Vector v of the lane holds elements 16 v + 4 q ... + 3 of its X row and of
-    // its Y row, so the four lanes of a row read 64 contiguous bytes; step
-    // 4 v + s of a tile multiplies element 16 v + 4 q + s.  Out of range past d.
+    // byte offsets of the lane's vectors within a row (out of range past d)
     unsigned voff[kS / 4];
 #pragma unroll
     for (int v = 0; v < kS / 4; ++v) {
@@ -356,7 +258,7 @@ __global__ __launch_bounds__(kUnThreads) void sddmm_union_kernel(SddmmParams p)
     auto load_tile = [&](int T, float (&yb)[kS]) {
         const int u = 16 * T + jl;
         const unsigned base =
-            u < nu ? (unsigned)s_ucol[min(u, kUnMaxCols - 1)] * rowbytes : kOutOfRange;
+            u < nu ? (unsigned)s.ucol[min(u, pu::kMaxCols - 1)] * rowbytes : kOutOfRange;
 #pragma unroll
         for (int v = 0; v < kS / 4; ++v) {
             const V::T t = V::buf_load(ry, base + voff[v] | (base & kOutOfRange));
@@ -372,10 +274,10 @@ __global__ __launch_bounds__(kUnThreads) void sddmm_union_kernel(SddmmParams p)
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[t], yb[t], acc, 0, 0, 0);
         // lane l holds rows 4 (l / 16) .. + 3 of tile column l % 16
         const int u = 16 * T + jl;
-        const int uc = min(u, kUnMaxCols - 1);
+        const int uc = min(u, pu::kMaxCols - 1);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const unsigned idx = u < nu ? s_emap[(4 * q + r) * kEmapStride + uc] : 0u;
+            const unsigned idx = u < nu ? s.emap[(4 * q + r) * pu::kEmapStride + uc] : 0u;
             const unsigned oo = idx ? (unsigned)(e0 + (int)idx - 1) * 4u : kOutOfRange;
             float scale = alpha;
             if (mvz) {
@@ -1263,14 +1165,12 @@ hipError_t launch_multirow(int g, const SddmmParams &p, hipStream_t s)
 
 hipError_t launch_union(int g, const SddmmParams &p, hipStream_t s)
 {
-    const long long panels = ((long long)p.m + kUnRows - 1) / kUnRows;
-    const long long groups = ((long long)p.batch + kUnWaves - 1) / kUnWaves;
-    const dim3 grid((unsigned)xcd_grid(groups, panels));
-    const size_t lds = union_dynamic_lds(p.k);
+    const dim3 grid((unsigned)pu::grid(p.m, p.batch));
+    const size_t lds = pu::dynamic_lds(p.k);
     if (g == 8)
-        hipLaunchKernelGGL(sddmm_union_kernel<8>, grid, dim3(kUnThreads), lds, s, p);
+        hipLaunchKernelGGL(sddmm_union_kernel<8>, grid, dim3(pu::kThreads), lds, s, p);
     else
-        hipLaunchKernelGGL(sddmm_union_kernel<16>, grid, dim3(kUnThreads), lds, s, p);
+        hipLaunchKernelGGL(sddmm_union_kernel<16>, grid, dim3(pu::kThreads), lds, s, p);
     return hipGetLastError();
 }
 
@@ -1549,12 +1449,11 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
                      (g == 8 || g == 16) && buf && (long long)a.nnz * 4 < (1LL << 31) &&
                      (long long)a.m * a.d * 4 < (1LL << 31) &&
                      xcd_grid(a.batch, ((long long)a.m + rpw - 1) / rpw) <= 0x7fffffffLL;
-    // Batched problems on up to kUnMaxK columns: the panel-union kernel, which
+    // Batched problems on up to 65,536 columns: the panel-union kernel, which
     // falls back to the multi-row walk panel by panel where columns are not
     // shared.  One batch entry would leave three of its four waves idle.
-    plan->panel_union = plan->multirow && a.batch >= 2 && a.k <= kUnMaxK &&
-                        xcd_grid((a.batch + kUnWaves - 1) / kUnWaves,
-                                 ((long long)a.m + kUnRows - 1) / kUnRows) <= 0x7fffffffLL;
+    plan->panel_union = plan->multirow && a.batch >= 2 && a.k <= pu::kMaxK &&
+                        pu::grid(a.m, a.batch) <= 0x7fffffffLL;
     return hipSuccess;
 }
 

@@ -10,7 +10,7 @@
 namespace spk {
 
 struct SpmmPlan {
-    enum Kind { kWide, kNarrow, kLds, kBalanced, kSplit, kPanel } kind;
+    enum Kind { kWide, kNarrow, kLds, kBalanced, kSplit, kPanel, kUnion } kind;
     spmm_detail::SpmmParams p;
     spmm_detail::PanelParams q;  // panel kernel
     int panel = 0;               // panel kernel: 0 many tiles (64-row panels), 1 few (32)

@@ -11,6 +11,7 @@
 #include "sp_plan.h"
 #include "spmm_panel.h"
 #include "spmm_wide.h"
+#include "panel_union.h"
 
 namespace spk {
 
@@ -282,6 +283,154 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void spmm_split_kernel(SpmmPar
 // each column vector are added across lanes (DPP rotations inside 16-lane
 // rows, then lane swaps between rows and between wave halves).
 // Deterministic; a different (tree) order from the wide kernel.
+// Batched fp32 SpMM over a structure whose neighbouring rows share most of
+// their columns (sparse attention's P V: 32 heads, one mask).  A workgroup
+// takes a panel of 16 consecutive rows and 4 batch entries and forms the
+// panel's column union once (panel_union.h); each wave then computes its batch
+// entry's C[panel] = A[panel, union] B[union] with v_mfma_f32_16x16x4f32, every
+// union row of B loaded once per panel instead of once per entry.  Per
+// 64-column block of C and per step of 4 union slots, lane l supplies
+// A[row l % 16][slot 4 st + l / 16] (the entry map gives the entry, a buffer
+// load its value; 0 where the row has no entry) and B[union row 4 st + l / 16]
+// [4 (l % 16) ... + 3]; the four MFMAs of a step take one of those columns
+// each, so lane l's accumulators hold C[4 (l / 16) + r][4 (l % 16) + c] and
+// leave as one 16-byte store per row.  A tile multiplies the zeros of absent
+// entries by B rows: a B value that is not finite would make 0 x Inf = NaN
+// where the per-entry result is finite, so a wave that loads one redoes its
+// panel on the per-entry path.  Panels whose union is too wide for their entry
+// count take that path too: the wide kernel's accumulation (wide_accumulate)
+// on the panel's rows, bit-identical to the wide kernel.  Tile sums round in
+// the MFMA's order, within the same bound.
+namespace pu = panel_union;
+
+template <int kLpr, bool kVecCsr>
+__global__ __launch_bounds__(pu::kThreads) void spmm_union_kernel(SpmmParams p)
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    using V4 = GVec<float, 4>;
+    constexpr int kBlocks = kLpr / 16;  // 64-column blocks of C: n = 64 kBlocks
+    constexpr int kRpw = kWave / kLpr;  // rows per wave on the per-entry path
+    constexpr int kChunk = kEpl * kLpr;
+    constexpr int kPitch = kChunk + kU + 4;
+    __shared__ pu::Shared s;
+    __shared__ __align__(16) int s_off[pu::kWaves * kRpw * kPitch];
+    __shared__ __align__(16) float s_val[pu::kWaves * kRpw * kPitch];
+    extern __shared__ unsigned s_dyn[];
+    pu::Panel pp;
+    if (!pu::panel_of(p.m, p.batch, p.row_offsets, pp)) return;
+    // an empty panel stores zeros through the tile path (no tiles)
+    const int nu = pp.pn > 0 ? pu::build(p.row_offsets, p.col_indices, p.k, pp, s, s_dyn) : 0;
+    // (uniform in the wave; the buffer resources below depend on it)
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int z = pp.hg * pu::kWaves + wave;
+    if (z >= p.batch) return;
+    const float *vals = static_cast<const float *>(p.values) + z * p.stride_values;
+    const float *bz = static_cast<const float *>(p.b) + z * p.stride_b;
+    float *cz = p.c + z * p.stride_c;
+
+    auto per_entry = [&]() {
+        const int grp = lane / kLpr, gl = lane % kLpr;
+        int *g_off = s_off + (wave * kRpw + grp) * kPitch;
+        float *g_val = s_val + (wave * kRpw + grp) * kPitch;
+#pragma unroll 1
+        for (int u = 0; u < pu::kRows / kRpw; ++u) {
+            const int slot = u * kRpw + grp;
+            const bool has = slot < pp.nr;
+            const int row = pp.r0 + (has ? slot : 0);
+            const int p0 = has ? p.row_offsets[row] : 0;
+            const int p1 = has ? p.row_offsets[row + 1] : 0;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            wide_accumulate<float, kLpr, 4, kVecCsr, true, true>(p, vals, bz, p0, p1, gl, 4 * gl,
+                                                                 true, g_off, g_val, acc);
+            if (has) V4::store(cz + (size_t)row * (size_t)p.n + 4 * gl, acc);
+        }
+    };
+    if (nu < 0) {
+        per_entry();
+        return;
+    }
+
+    const int ntiles = (nu + 15) / 16;
+    const unsigned rowbytes = (unsigned)p.n * 4u;
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(vals), 0, (int)p.csr_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(bz), 0, (int)p.b_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc(cz, 0, (int)p.c_bytes, 0x00020000);
+    const int jl = lane % 16;  // the lane's row of A, column group of B and C
+    const int q = lane / 16;   // the lane's union slot within a step
+    struct Tile {
+        float a[4];
+        V4::T b[4];
+    };
+    bool finite = true;
+#pragma unroll 1
+    for (int cb = 0; cb < kBlocks; ++cb) {
+        const unsigned col_bytes = (unsigned)(64 * cb + 4 * jl) * 4u;
+        auto load = [&](int T, Tile &t) {
+            // the step's map entries and union columns first (clamped slots,
+            // so every read is in bounds; slots past the union are not used)
+            unsigned idx[4], col[4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int uc = min(16 * T + 4 * st + q, pu::kMaxCols - 1);
+                idx[st] = s.emap[jl * pu::kEmapStride + uc];
+                col[st] = (unsigned)s.ucol[uc];
+            }
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const bool ok = 16 * T + 4 * st + q < nu;
+                const unsigned vo =
+                    ok && idx[st] ? (unsigned)(pp.e0 + (int)idx[st] - 1) * 4u : kOutOfRange;
+                t.a[st] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, (int)vo, 0, 0));
+                const unsigned base = ok ? col[st] * rowbytes : kOutOfRange;
+                t.b[st] = V4::buf_load(rb, base + col_bytes | (base & kOutOfRange));
+            }
+        };
+        f4 acc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = f4{0.f, 0.f, 0.f, 0.f};
+        auto mma = [&](const Tile &t) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                float bv[4];
+                memcpy(bv, &t.b[st], sizeof(bv));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    finite = finite && __builtin_isfinite(bv[c]);
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.a[st], bv[c], acc[c], 0, 0, 0);
+                }
+            }
+        };
+        Tile ta, tb;
+        load(0, ta);
+        // one exit, at the end (as in the SDDMM tile loop)
+        for (int T = 0; T < ntiles; T += 2) {
+            load(T + 1, tb);
+            keep_issued_above();
+            mma(ta);
+            load(T + 2, ta);
+            keep_issued_above();
+            mma(tb);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 4 * q + r;
+            const unsigned off =
+                row < pp.nr ? (unsigned)(pp.r0 + row) * rowbytes + col_bytes : kOutOfRange;
+            const u4 ov = {__float_as_uint(acc[0][r]), __float_as_uint(acc[1][r]),
+                           __float_as_uint(acc[2][r]), __float_as_uint(acc[3][r])};
+            __builtin_amdgcn_raw_buffer_store_b128(ov, rc, (int)off, 0, 0);
+        }
+    }
+    // a non-finite B value in this wave's union rows: the per-entry sums
+    // replace what the tiles stored (same wave, so the stores stay in order)
+    if (__builtin_amdgcn_ballot_w64(!finite) != 0) per_entry();
+}
+
 template <int kE, int kVec>
 __global__ __launch_bounds__(kWave) void spmm_narrow_kernel(SpmmParams p)
 {
@@ -739,6 +888,23 @@ hipError_t launch_split(int lpr, const SpmmParams &p, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int kLpr, bool kVecCsr>
+hipError_t launch_union_t(const SpmmParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL((spmm_union_kernel<kLpr, kVecCsr>), dim3((unsigned)pu::grid(p.m, p.batch)),
+                       dim3(pu::kThreads), pu::dynamic_lds(p.k), s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_union(int lpr, bool vec_csr, const SpmmParams &p, hipStream_t s)
+{
+    switch (lpr) {
+    case 16: return vec_csr ? launch_union_t<16, true>(p, s) : launch_union_t<16, false>(p, s);
+    case 32: return vec_csr ? launch_union_t<32, true>(p, s) : launch_union_t<32, false>(p, s);
+    default: return vec_csr ? launch_union_t<64, true>(p, s) : launch_union_t<64, false>(p, s);
+    }
+}
+
 template <typename E, int kVec>
 hipError_t launch_balanced(const SpmmParams &p, bool vec_csr, bool buf, hipStream_t s)
 {
@@ -887,6 +1053,17 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
             }
         }
     }
+    // Batched fp32 problems of 64, 128 or 256 columns on up to 65,536 rows of
+    // B: the panel-union kernel, which falls back to the wide kernel's
+    // accumulation panel by panel where rows share few columns.
+    if (plan->kind == SpmmPlan::kWide && f32 && vec && buf && a.batch >= 2 &&
+        a.k <= pu::kMaxK && (a.n == 64 || a.n == 128 || a.n == 256) &&
+        (long long)a.m * a.n * 4 < (1LL << 31) && (long long)a.nnz * 4 < (1LL << 31) &&
+        pu::grid(a.m, a.batch) <= 0x7fffffffLL) {
+        plan->kind = SpmmPlan::kUnion;
+        p.c_bytes = (unsigned)((long long)a.m * a.n * 4);
+        p.csr_bytes = (unsigned)((long long)a.nnz * 4);
+    }
     if (narrow) plan->kind = SpmmPlan::kNarrow;
     if (lds_ok) {
         // B in LDS when it fits and every CU has at least as many entries to
@@ -928,6 +1105,8 @@ hipError_t run_spmm(const SpmmPlan &plan, hipStream_t stream)
 {
     const SpmmParams &p = plan.p;
     switch (plan.kind) {
+    case SpmmPlan::kUnion:
+        return launch_union(plan.lpr, plan.vec_csr, p, stream);
     case SpmmPlan::kPanel:
         return plan.panel == 0 ? launch_panel_t<PanelMany>(p, plan.q, stream)
                                : launch_panel_t<PanelFew>(p, plan.q, stream);
@@ -996,6 +1175,7 @@ const char *spmm_kernel_name(const SpmmArgs &a)
     case SpmmPlan::kBalanced: return "balanced";
     case SpmmPlan::kSplit: return "split";
     case SpmmPlan::kPanel: return "panel";
+    case SpmmPlan::kUnion: return "panel_union";
     }
     return "unknown";
 }
