@@ -567,6 +567,13 @@ sp_status_t sp_sddmm_softmax(int m, int k, int d, int nnz, const int *row_indice
  * for 16-bit types; 16-byte aligned operands with strides that keep them so;
  * K and V under 2 GiB per batch entry.  Anything else returns
  * SP_ERROR_NOT_SUPPORTED (the three separate entry points handle it).
+ * Batches (batch >= 2) of fp32 heads with d = 32 or 64 on at most 65,536 key
+ * rows take a kernel that forms each 16-row panel's key union once for 4
+ * batch entries and computes scores and the weighted sum of V as matrix-core
+ * tiles over it (the softmax rescaled once per 16-key tile); panels whose rows
+ * share few keys, and panels whose union rows of V hold a value that is not
+ * finite, use the per-row walk, as do all other calls.  The results do not
+ * depend on row_indices.
  * Deterministic run to run; equal up to rounding to sp_sddmm_softmax (or
  * sp_sddmm + sp_csr_row_softmax) followed by sp_spmm. */
 sp_status_t sp_sparse_attention(int m, int k, int d, int nnz, const int *row_indices,

@@ -65,3 +65,35 @@ class DevCsr:
 def csr_of_row_lists(rl) -> DevCsr:
     return DevCsr(rl.m, rl.k, oracle.csr_offsets_from_lengths(rl.lengths), rl.cols,
                   rl.values)
+
+
+def check_attention(o_gpu, m, k, ro, ci, q, kk, v, alpha, what, rescalings=None):
+    """O against the oracle's double pipeline: P's relative error (scores,
+    fp32 softmax, the running-maximum rescalings, a few ulps each: one per
+    window of 64 entries, or `rescalings` per row when given) times
+    sum_j P_j |V_j|, plus the weighted sum's own 1e-5."""
+    s, s_abs = oracle.sddmm(m, k, q.shape[1], ro, ci, q, kk)
+    s, e_s = alpha * s, abs(alpha) * 1e-5 * s_abs
+    p_ref = oracle.softmax_rows(ro, s.astype(np.float32))
+    lengths = np.diff(ro)
+    rows = np.repeat(np.arange(m), lengths)
+    e_row = np.zeros(m)
+    np.maximum.at(e_row, rows, e_s)
+    smax = np.full(m, -np.inf)
+    np.maximum.at(smax, rows, s)
+    x_row = np.zeros(m)
+    np.maximum.at(x_row, rows, np.abs(s - smax[rows]))
+    a_row = np.zeros(m)
+    np.maximum.at(a_row, rows, np.abs(s))
+    windows = (lengths + 63) // 64 if rescalings is None else rescalings
+    rel = (2.0 * e_row + 2.0 * a_row * 2.0 ** -24 + (x_row + 8.0) * 2.0 ** -23
+           + 8.0 * windows * 2.0 ** -23 + 1e-5)
+    o_ref, _ = oracle.spmm(m, k, q.shape[1], ro, ci, p_ref, v)
+    pv, _ = oracle.spmm(m, k, q.shape[1], ro, ci, p_ref, np.abs(v))
+    err = np.abs(o_gpu.astype(np.float64) - o_ref)
+    bound = rel[:, None] * pv * 1.01 + 2.0 ** -126
+    assert np.all(np.isfinite(o_gpu)), what
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} out of bound; worst "
+                           f"{np.max(err / np.maximum(bound, 1e-300)):.3g}")
+    assert np.all(o_gpu[lengths == 0] == 0.0), f"{what}: empty rows not zero"

@@ -25,6 +25,7 @@
 #include "sp_device.h"
 #include "sp_launch.h"
 #include "sp_types.h"
+#include "panel_union.h"
 
 namespace spk {
 
@@ -59,51 +60,50 @@ struct AttnParams {
     const void *q, *k, *v;
     float alpha;
     unsigned kv_bytes;  // bytes of one K (= one V) operand
+    int k_rows;         // rows of K and V
     float *out;
     long long stride_q, stride_k, stride_v, stride_out;
 };
 
-template <typename E, int kDv>
-__global__ __launch_bounds__(kAttnWaves * kWave) void attention_kernel(AttnParams p)
-{
-    constexpr int kVec = 16 / Elem<E>::kBytes;   // elements per 16-byte vector
-    using V = GVec<E, kVec>;
-    using VecT = typename V::T;
-    constexpr unsigned kEb = Elem<E>::kBytes;
-    // score phase: kG lanes per entry, kNv vectors each, kNg entries per step
-    constexpr int kG = kDv <= 8 ? 8 : 16;
-    constexpr int kNv = kDv / kG;
-    constexpr int kNg = kWave / kG;
 #ifndef SP_ATTN_SCORE_LOADS
 #define SP_ATTN_SCORE_LOADS 2
 #endif
-    constexpr int kU = SP_ATTN_SCORE_LOADS / kNv > 0 ? SP_ATTN_SCORE_LOADS / kNv : 1;  // steps per batch
-    constexpr int kBatches = (kG + kU - 1) / kU;
+// The shape of one row's walk for element type E and kDv 16-byte vectors per
+// row, and the sizes of its per-wave LDS staging.
+template <typename E, int kDv> struct AttnShape {
+    static constexpr int kVec = 16 / Elem<E>::kBytes;   // elements per 16-byte vector
+    static constexpr unsigned kEb = Elem<E>::kBytes;
+    // score phase: kG lanes per entry, kNv vectors each, kNg entries per step
+    static constexpr int kG = kDv <= 8 ? 8 : 16;
+    static constexpr int kNv = kDv / kG;
+    static constexpr int kNg = kWave / kG;
+    static constexpr int kU = SP_ATTN_SCORE_LOADS / kNv > 0 ? SP_ATTN_SCORE_LOADS / kNv : 1;
+    static constexpr int kBatches = (kG + kU - 1) / kU;
     // P.V phase: kDv lanes per entry (one vector each), kSl entries per step
-    constexpr int kSl = kWave / kDv;
-    constexpr int kUv = kDv <= 16 ? 2 : kDv / 8; // P.V steps per batch (at most 8 batches)
-    constexpr int kVB = (kDv + kUv - 1) / kUv;   // P.V batches of a full window
+    static constexpr int kSl = kWave / kDv;
+    static constexpr int kUv = kDv <= 16 ? 2 : kDv / 8;  // P.V steps per batch (at most 8 batches)
+    static constexpr int kVB = (kDv + kUv - 1) / kUv;    // P.V batches of a full window
     static_assert(kNv * kG == kDv, "score lanes cover the row");
     // windows plus the padding read by the prefetch of up to two batches
-    constexpr int kVPad = 3 * kUv * kSl;
-    __shared__ unsigned s_koff_all[kAttnWaves][kWave + 2 * kU * kNg];
-    __shared__ unsigned s_voff_all[kAttnWaves][kWave + kVPad];
-    __shared__ float s_e_all[kAttnWaves][kWave + kVPad];
+    static constexpr int kVPad = 3 * kUv * kSl;
+    static constexpr int kKoff = kWave + 2 * kU * kNg;   // words of the K-offset staging
+    static constexpr int kVoff = kWave + kVPad;          // words of the V-offset / weight staging
+};
 
-    // workgroup: kAttnWaves consecutive slots of one batch entry
-    const long long groups = ((long long)p.m + kAttnWaves - 1) / kAttnWaves;
-    const long long w = xcd_work_index(p.batch, groups);
-    if (w < 0) return;
-    const long long z = w / groups;
-    const int wave = threadIdx.x / kWave;
-    const long long slot_ll = (w - z * groups) * kAttnWaves + wave;
-    if (slot_ll >= p.m) return;  // no workgroup barrier follows
-    const int slot = (int)slot_ll;
-    const int lane = threadIdx.x - wave * kWave;
-    unsigned *s_koff = s_koff_all[wave];
-    unsigned *s_voff = s_voff_all[wave];
-    float *s_e = s_e_all[wave];
-    const int row = p.row_indices ? p.row_indices[slot] : slot;
+// One wave's walk of one query row (batch entry z) through its own staging
+// regions s_koff, s_voff and s_e (AttnShape sizes); writes the output row.
+template <typename E, int kDv>
+__device__ __forceinline__ void attention_row(const AttnParams &p, long long z, int row,
+                                              int lane, unsigned *s_koff, unsigned *s_voff,
+                                              float *s_e)
+{
+    using S = AttnShape<E, kDv>;
+    constexpr int kVec = S::kVec;
+    using V = GVec<E, kVec>;
+    using VecT = typename V::T;
+    constexpr unsigned kEb = S::kEb;
+    constexpr int kG = S::kG, kNv = S::kNv, kNg = S::kNg, kU = S::kU, kBatches = S::kBatches;
+    constexpr int kSl = S::kSl, kUv = S::kUv, kVB = S::kVB, kVPad = S::kVPad;
     const int p0 = p.row_offsets[row];
     const int p1 = p.row_offsets[row + 1];
     const int d = p.d;
@@ -251,6 +251,233 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attention_kernel(AttnParam
 }
 
 template <typename E, int kDv>
+__global__ __launch_bounds__(kAttnWaves * kWave) void attention_kernel(AttnParams p)
+{
+    using S = AttnShape<E, kDv>;
+    __shared__ unsigned s_koff_all[kAttnWaves][S::kKoff];
+    __shared__ unsigned s_voff_all[kAttnWaves][S::kVoff];
+    __shared__ float s_e_all[kAttnWaves][S::kVoff];
+    // workgroup: kAttnWaves consecutive slots of one batch entry
+    const long long groups = ((long long)p.m + kAttnWaves - 1) / kAttnWaves;
+    const long long w = xcd_work_index(p.batch, groups);
+    if (w < 0) return;
+    const long long z = w / groups;
+    const int wave = threadIdx.x / kWave;
+    const long long slot_ll = (w - z * groups) * kAttnWaves + wave;
+    if (slot_ll >= p.m) return;  // no workgroup barrier follows
+    const int slot = (int)slot_ll;
+    const int lane = threadIdx.x - wave * kWave;
+    const int row = p.row_indices ? p.row_indices[slot] : slot;
+    attention_row<E, kDv>(p, z, row, lane, s_koff_all[wave], s_voff_all[wave], s_e_all[wave]);
+}
+
+// Batched fp32 attention (d = 32 or 64) over a mask whose neighbouring rows
+// share most of their keys (sparse attention's band).  A workgroup takes a
+// panel of 16 consecutive query rows and 4 batch entries and forms the panel's
+// key union once (panel_union.h); each wave then walks its batch entry's
+// union in 16-key tiles, the online softmax of the walk above on matrix cores:
+//   1. S = Q[panel] K[tile]^T with v_mfma_f32_16x16x4f32 (lane l holds, of
+//      Q's row l % 16 and of key 16 T + l % 16, elements 16 v + 4 (l / 16)
+//      ... + 3, as in the panel-union SDDMM), scaled by alpha; keys a row
+//      does not have become -Inf;
+//   2. per row (lanes of one 16-lane group hold the same four rows): the
+//      tile's maximum and the running maximum mx, the running sum l of
+//      exp(s - mx), and the rescaling of l and the output accumulators by
+//      exp(mx_old - mx_new) when mx grows;
+//   3. the weights exp(s - mx) go through a 16 x 16 LDS tile into the A
+//      operand's layout (row l % 16, key 4 st + l / 16), and
+//      O += P[panel, tile] V[tile] with four (d = 64) or two (d = 32) MFMAs
+//      per step of 4 keys, lane l's accumulators holding
+//      O[4 (l / 16) + r][kNc (l % 16) + c], as in the panel-union SpMM.
+// After the last tile O is divided by l (rows without entries stay zero) and
+// leaves as one vector store per row.  Panels whose union is too wide for
+// their entry count run attention_row on their rows; so does a wave that
+// loads a V value that is not finite (a tile multiplies the zero weights of
+// absent keys by V rows: 0 x Inf would be NaN where the row's result is
+// finite), its stores replacing the tile's.  Sums and maxima are taken in a
+// fixed order: deterministic, rounding in the MFMA's order.
+namespace pu = panel_union;
+
+template <int kD>
+__global__ __launch_bounds__(pu::kThreads) void attention_union_kernel(AttnParams p)
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    using V4 = GVec<float, 4>;
+    constexpr int kS = kD / 4;     // score MFMA steps per tile: elements of d per lane
+    constexpr int kNc = kD / 16;   // output columns per lane, one accumulator each
+    constexpr int kDv = kD / 4;    // 16-byte vectors per row (the per-row walk)
+    using Sh = AttnShape<float, kDv>;
+    constexpr int kPp = 17;        // pitch of the weight tile (odd: the transposed read is spread over banks)
+    __shared__ pu::Shared s;
+    __shared__ float s_p[pu::kWaves][16 * kPp];
+    __shared__ unsigned s_koff_all[pu::kWaves][Sh::kKoff];
+    __shared__ unsigned s_voff_all[pu::kWaves][Sh::kVoff];
+    __shared__ float s_e_all[pu::kWaves][Sh::kVoff];
+    extern __shared__ unsigned s_dyn[];
+    pu::Panel pp;
+    if (!pu::panel_of(p.m, p.batch, p.row_offsets, pp)) return;
+    // an empty panel stores zero rows through the tile path (no tiles)
+    const int nu = pp.pn > 0 ? pu::build(p.row_offsets, p.col_indices, p.k_rows, pp, s, s_dyn) : 0;
+    // (uniform in the wave; the buffer resources below depend on it)
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int z = pp.hg * pu::kWaves + wave;
+    if (z >= p.batch) return;
+    auto per_row = [&]() {
+#pragma unroll 1
+        for (int i = 0; i < pp.nr; ++i)
+            attention_row<float, kDv>(p, z, pp.r0 + i, lane, s_koff_all[wave], s_voff_all[wave],
+                                      s_e_all[wave]);
+    };
+    if (nu < 0) {
+        per_row();
+        return;
+    }
+
+    const int ntiles = (nu + 15) / 16;
+    const unsigned rowbytes = (unsigned)kD * 4u;
+    const unsigned qo_bytes = (unsigned)p.m * rowbytes;
+    float *oz = p.out + z * p.stride_out;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(static_cast<const float *>(p.q) + z * p.stride_q), 0, (int)qo_bytes,
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(static_cast<const float *>(p.k) + z * p.stride_k), 0,
+        (int)p.kv_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(static_cast<const float *>(p.v) + z * p.stride_v), 0,
+        (int)p.kv_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ro =
+        __builtin_amdgcn_make_buffer_rsrc(oz, 0, (int)qo_bytes, 0x00020000);
+    const int jl = lane % 16;  // the lane's Q row and key of a tile; its output column group
+    const int q = lane / 16;   // the lane's 16-byte piece of each 64-byte block of d; key of a step
+    float *tp = s_p[wave];
+
+    float xa[kS];
+    {
+        const unsigned base = jl < pp.nr ? (unsigned)(pp.r0 + jl) * rowbytes : kOutOfRange;
+#pragma unroll
+        for (int v = 0; v < kS / 4; ++v) {
+            const V4::T t = V4::buf_load(rq, base + (unsigned)(16 * v + 4 * q) * 4u);
+            memcpy(&xa[4 * v], &t, sizeof(t));
+        }
+    }
+    struct Tile {
+        float k[kS];        // key 16 T + jl: the lane's elements
+        float v[4][kNc];    // keys 16 T + 4 st + q: the lane's output columns
+    };
+    auto load = [&](int T, Tile &t) {
+        {
+            const int u = 16 * T + jl;
+            const unsigned col = (unsigned)s.ucol[min(u, pu::kMaxCols - 1)];
+            const unsigned base = u < nu ? col * rowbytes : kOutOfRange;
+#pragma unroll
+            for (int v = 0; v < kS / 4; ++v) {
+                const V4::T x = V4::buf_load(rk, base + (unsigned)(16 * v + 4 * q) * 4u);
+                memcpy(&t.k[4 * v], &x, sizeof(x));
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int u = 16 * T + 4 * st + q;
+            const unsigned col = (unsigned)s.ucol[min(u, pu::kMaxCols - 1)];
+            const unsigned off = (u < nu ? col * rowbytes : kOutOfRange) + (unsigned)(kNc * jl) * 4u;
+            if constexpr (kNc == 4) {
+                const V4::T x = V4::buf_load(rv, off);
+                memcpy(t.v[st], &x, sizeof(x));
+            } else {
+                const auto x = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)off, 0, 0);
+                t.v[st][0] = __uint_as_float(x[0]);
+                t.v[st][1] = __uint_as_float(x[1]);
+            }
+        }
+    };
+    f4 o[kNc];
+#pragma unroll
+    for (int c = 0; c < kNc; ++c) o[c] = f4{0.f, 0.f, 0.f, 0.f};
+    float mx[4], l[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        mx[r] = -INFINITY;
+        l[r] = 0.f;
+    }
+    bool finite = true;
+    auto process = [&](int T, const Tile &t) {
+        f4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kS; ++i)
+            sc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[i], t.k[i], sc, 0, 0, 0);
+        const int u = 16 * T + jl;
+        const int uc = min(u, pu::kMaxCols - 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool present = u < nu && s.emap[(4 * q + r) * pu::kEmapStride + uc] != 0;
+            const float sv = present ? p.alpha * sc[r] : -INFINITY;
+            const float mnew = fmaxf(mx[r], group_reduce<16>(sv, OpMax{}));
+            const float c = mnew == -INFINITY ? 1.f : expf(mx[r] - mnew);
+            const float e = present ? expf(sv - mnew) : 0.f;
+            l[r] = l[r] * c + group_sum<16>(e);
+            mx[r] = mnew;
+#pragma unroll
+            for (int cc = 0; cc < kNc; ++cc) o[cc][r] *= c;
+            tp[(4 * q + r) * kPp + jl] = e;
+        }
+        wave_lds_sync();
+        float a[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) a[st] = tp[jl * kPp + 4 * st + q];
+        wave_lds_sync();
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int cc = 0; cc < kNc; ++cc) {
+                finite = finite && __builtin_isfinite(t.v[st][cc]);
+                o[cc] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], t.v[st][cc], o[cc], 0, 0, 0);
+            }
+    };
+    Tile ta, tb;
+    load(0, ta);
+    // one exit, at the end (as in the panel-union SDDMM)
+    for (int T = 0; T < ntiles; T += 2) {
+        load(T + 1, tb);
+        keep_issued_above();
+        process(T, ta);
+        load(T + 2, ta);
+        keep_issued_above();
+        process(T + 1, tb);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 4 * q + r;
+        const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
+        const unsigned off =
+            row < pp.nr ? (unsigned)(pp.r0 + row) * rowbytes + (unsigned)(kNc * jl) * 4u
+                        : kOutOfRange;
+        if constexpr (kNc == 4) {
+            typedef unsigned u4 __attribute__((ext_vector_type(4)));
+            const u4 x = {__float_as_uint(o[0][r] * inv), __float_as_uint(o[1][r] * inv),
+                          __float_as_uint(o[2][r] * inv), __float_as_uint(o[3][r] * inv)};
+            __builtin_amdgcn_raw_buffer_store_b128(x, ro, (int)off, 0, 0);
+        } else {
+            typedef unsigned u2 __attribute__((ext_vector_type(2)));
+            const u2 x = {__float_as_uint(o[0][r] * inv), __float_as_uint(o[1][r] * inv)};
+            __builtin_amdgcn_raw_buffer_store_b64(x, ro, (int)off, 0, 0);
+        }
+    }
+    // a V value that is not finite among this wave's union rows: the per-row
+    // walk replaces what the tiles stored (same wave, so the stores stay in order)
+    if (__builtin_amdgcn_ballot_w64(!finite) != 0) per_row();
+}
+
+template <int kD>
+hipError_t launch_union_t(const AttnParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL((attention_union_kernel<kD>), dim3((unsigned)pu::grid(p.m, p.batch)),
+                       dim3(pu::kThreads), pu::dynamic_lds(p.k_rows), s, p);
+    return hipGetLastError();
+}
+
+template <typename E, int kDv>
 hipError_t launch_t(const AttnParams &p, hipStream_t s)
 {
     const long long groups = ((long long)p.m + kAttnWaves - 1) / kAttnWaves;
@@ -303,11 +530,18 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t stream)
     p.v = a.v;
     p.alpha = a.alpha;
     p.kv_bytes = (unsigned)((long long)a.k_rows * a.d * eb);
+    p.k_rows = a.k_rows;
     p.out = a.out;
     p.stride_q = a.stride_q;
     p.stride_k = a.stride_k;
     p.stride_v = a.stride_v;
     p.stride_out = a.stride_out;
+    // Batches of fp32 heads of 32 or 64 on up to 65,536 keys: the panel-union
+    // kernel, which runs the per-row walk on panels whose rows share few keys.
+    if (a.dtype == Dtype::f32 && (a.d == 32 || a.d == 64) && a.batch >= 2 &&
+        a.k_rows <= pu::kMaxK && (long long)a.m * a.d * 4 < (1LL << 31) &&
+        pu::grid(a.m, a.batch) <= 0x7fffffffLL)
+        return a.d == 32 ? launch_union_t<32>(p, stream) : launch_union_t<64>(p, stream);
     switch (a.dtype) {
     case Dtype::f16: return launch_e<_Float16>(dv, p, stream);
     case Dtype::bf16: return launch_e<bf16>(dv, p, stream);
