@@ -24,7 +24,7 @@ namespace spk {
 namespace panel_union {
 
 constexpr int kRows = 16;          // rows per panel: the MFMA tile's height
-constexpr int kWaves = 4;          // batch entries per workgroup, one per wave
+constexpr int kWaves = 4;          // batch entries per workgroup, one per wave (default)
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxCols = 256;      // distinct columns per panel on the tile path
 constexpr int kMaxK = 65536;       // columns the LDS bitmap covers
@@ -34,23 +34,24 @@ constexpr int kCache = 8;          // column indices a thread keeps between the 
 // instruction of the tile loops touches fall in different banks
 constexpr int kEmapStride = kMaxCols + 2;
 
-struct Shared {
+template <int kW = kWaves> struct SharedT {
     __align__(16) unsigned short emap[kRows * kEmapStride];
     int ucol[kMaxCols];
-    int wsum[kWaves];
+    int wsum[kW];
 };
+using Shared = SharedT<>;
 
 // Dynamic LDS: the bitmap and each word's rank.
 inline size_t dynamic_lds(int k) { return 2 * sizeof(unsigned) * (size_t)((k + 31) / 32); }
 
-// Workgroups of a launch over m rows and `batch` entries.
-inline long long grid(int m, int batch)
+// Workgroups of a launch over m rows and `batch` entries, kW per workgroup.
+template <int kW = kWaves> inline long long grid(int m, int batch)
 {
-    return xcd_grid(((long long)batch + kWaves - 1) / kWaves, ((long long)m + kRows - 1) / kRows);
+    return xcd_grid(((long long)batch + kW - 1) / kW, ((long long)m + kRows - 1) / kRows);
 }
 
 struct Panel {
-    int hg;  // group of kWaves batch entries
+    int hg;  // group of kW batch entries
     int r0;  // first row
     int nr;  // rows (kRows but for the last panel)
     int e0;  // first entry
@@ -58,10 +59,11 @@ struct Panel {
 };
 
 // This workgroup's panel; false for a padding slot of the launch.
+template <int kW = kWaves>
 __device__ __forceinline__ bool panel_of(int m, int batch, const int *row_offsets, Panel &pp)
 {
     const int panels = (m + kRows - 1) / kRows;
-    const int groups = (batch + kWaves - 1) / kWaves;
+    const int groups = (batch + kW - 1) / kW;
     const long long w = xcd_work_index(groups, panels);
     if (w < 0) return false;
     pp.hg = (int)(w / panels);
@@ -77,9 +79,12 @@ __device__ __forceinline__ bool panel_of(int m, int batch, const int *row_offset
 // panel that takes the per-entry path (no barrier follows that return, and
 // every thread takes it).  Column indices past k, which a valid CSR never
 // has, are left out.
+template <int kW = kWaves>
 __device__ __forceinline__ int build(const int *row_offsets, const int *col_indices, int k,
-                                     const Panel &pp, Shared &s, unsigned *s_dyn)
+                                     const Panel &pp, SharedT<kW> &s, unsigned *s_dyn)
 {
+    constexpr int kT = kW * kWave;       // threads of the workgroup
+    constexpr int kTpr = kT / kRows;     // threads per panel row
     // more entries than kRows rows of kMaxCols: some row alone is wider than
     // the tile path takes
     if (pp.pn > kRows * kMaxCols) return -1;
@@ -90,30 +95,30 @@ __device__ __forceinline__ int build(const int *row_offsets, const int *col_indi
     const int wave = tid / kWave;
     const int lane = tid % kWave;
 
-    // 16 threads per panel row; each keeps its first kCache column indices
-    const int mr = tid / 16, mq = tid % 16;
+    // kTpr threads per panel row; each keeps its first kCache column indices
+    const int mr = tid / kTpr, mq = tid % kTpr;
     const int rb = row_offsets[pp.r0 + min(mr, pp.nr)];
     const int re = row_offsets[pp.r0 + min(mr + 1, pp.nr)];
     unsigned cc[kCache];
 #pragma unroll
     for (int t = 0; t < kCache; ++t) {
-        const int j = rb + mq + 16 * t;
+        const int j = rb + mq + kTpr * t;
         cc[t] = j < re ? (unsigned)col_indices[j] : ~0u;
     }
-    for (int i = tid; i < nw; i += kThreads) s_bits[i] = 0u;
-    for (int i = tid; i < kRows * kEmapStride / 2; i += kThreads)
+    for (int i = tid; i < nw; i += kT) s_bits[i] = 0u;
+    for (int i = tid; i < kRows * kEmapStride / 2; i += kT)
         reinterpret_cast<unsigned *>(s.emap)[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < kCache; ++t)
         if (cc[t] < (unsigned)k) atomicOr(&s_bits[cc[t] >> 5], 1u << (cc[t] & 31));
-    for (int j = rb + mq + 16 * kCache; j < re; j += 16) {
+    for (int j = rb + mq + kTpr * kCache; j < re; j += kTpr) {
         const unsigned c = (unsigned)col_indices[j];
         if (c < (unsigned)k) atomicOr(&s_bits[c >> 5], 1u << (c & 31));
     }
     __syncthreads();
     // rank of each word's first bit: this thread's words, then the block's
-    const int wpt = (nw + kThreads - 1) / kThreads;
+    const int wpt = (nw + kT - 1) / kT;
     const int w0 = tid * wpt;
     int cnt = 0;
     for (int j = 0; j < wpt; ++j) cnt += w0 + j < nw ? __popc(s_bits[w0 + j]) : 0;
@@ -122,7 +127,7 @@ __device__ __forceinline__ int build(const int *row_offsets, const int *col_indi
     __syncthreads();
     int run = incl - cnt, nu = 0;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
+    for (int v = 0; v < kW; ++v) {
         run += v < wave ? s.wsum[v] : 0;
         nu += s.wsum[v];
     }
@@ -148,8 +153,8 @@ __device__ __forceinline__ int build(const int *row_offsets, const int *col_indi
     for (int t = 0; t < kCache; ++t)
         if (cc[t] < (unsigned)k)
             s.emap[mr * kEmapStride + slot_of(cc[t])] =
-                (unsigned short)(rb + mq + 16 * t - pp.e0 + 1);
-    for (int j = rb + mq + 16 * kCache; j < re; j += 16) {
+                (unsigned short)(rb + mq + kTpr * t - pp.e0 + 1);
+    for (int j = rb + mq + kTpr * kCache; j < re; j += kTpr) {
         const unsigned c = (unsigned)col_indices[j];
         if (c < (unsigned)k)
             s.emap[mr * kEmapStride + slot_of(c)] = (unsigned short)(j - pp.e0 + 1);

@@ -198,22 +198,25 @@ __global__ __launch_bounds__(kWave) void sddmm_multirow_kernel(SddmmParams p)
 // order), within the same bound.
 namespace pu = panel_union;
 
-template <int kG>
-__global__ __launch_bounds__(pu::kThreads) void sddmm_union_kernel(SddmmParams p)
+// Batch entries (waves) per workgroup of the union kernel.
+constexpr int kUnionWaves = 4;
+
+template <int kG, int kW>
+__global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
 {
     typedef float f4 __attribute__((ext_vector_type(4)));
     using V = GVec<float, 4>;
     constexpr int kS = kG;   // MFMA steps per tile: elements of d per lane
-    __shared__ pu::Shared s;
+    __shared__ pu::SharedT<kW> s;
     extern __shared__ unsigned s_dyn[];
     pu::Panel pp;
-    if (!pu::panel_of(p.m, p.batch, p.row_offsets, pp)) return;
+    if (!pu::panel_of<kW>(p.m, p.batch, p.row_offsets, pp)) return;
     if (pp.pn == 0) return;  // the whole workgroup: nothing to compute
-    const int nu = pu::build(p.row_offsets, p.col_indices, p.k, pp, s, s_dyn);
+    const int nu = pu::build<kW>(p.row_offsets, p.col_indices, p.k, pp, s, s_dyn);
     // (uniform in the wave; the buffer resources below depend on it)
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
-    const int z = pp.hg * pu::kWaves + wave;
+    const int z = pp.hg * kW + wave;
     if (z >= p.batch) return;
     const int r0 = pp.r0, nr = pp.nr, e0 = pp.e0;
     if (nu < 0) {
@@ -1165,12 +1168,13 @@ hipError_t launch_multirow(int g, const SddmmParams &p, hipStream_t s)
 
 hipError_t launch_union(int g, const SddmmParams &p, hipStream_t s)
 {
-    const dim3 grid((unsigned)pu::grid(p.m, p.batch));
+    constexpr int kW = kUnionWaves;
+    const dim3 grid((unsigned)pu::grid<kW>(p.m, p.batch));
     const size_t lds = pu::dynamic_lds(p.k);
     if (g == 8)
-        hipLaunchKernelGGL(sddmm_union_kernel<8>, grid, dim3(pu::kThreads), lds, s, p);
+        hipLaunchKernelGGL((sddmm_union_kernel<8, kW>), grid, dim3(kW * kWave), lds, s, p);
     else
-        hipLaunchKernelGGL(sddmm_union_kernel<16>, grid, dim3(pu::kThreads), lds, s, p);
+        hipLaunchKernelGGL((sddmm_union_kernel<16, kW>), grid, dim3(kW * kWave), lds, s, p);
     return hipGetLastError();
 }
 
@@ -1453,7 +1457,7 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
     // falls back to the multi-row walk panel by panel where columns are not
     // shared.  One batch entry would leave three of its four waves idle.
     plan->panel_union = plan->multirow && a.batch >= 2 && a.k <= pu::kMaxK &&
-                        pu::grid(a.m, a.batch) <= 0x7fffffffLL;
+                        pu::grid<kUnionWaves>(a.m, a.batch) <= 0x7fffffffLL;
     return hipSuccess;
 }
 
