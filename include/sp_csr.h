@@ -384,7 +384,8 @@ sp_status_t sp_spmm_ex(int m, int k, int n, int nnz, const int *row_indices, int
  *               one batch entry, n of at least one 128-column tile, enough
  *               panels to give every CU one, rows per panel times density at
  *               least 4);
- *   "panel_union" batches (fp32, n = 64, 128 or 256, k <= 65,536): per
+ *   "panel_union" batches (n = 64, 128 or 256, k <= 65,536; 16-bit values and
+ *               B widened to fp32 on load): per
  *               panel of 16 consecutive rows, the union of the rows' columns
  *               is formed once for 4 batch entries and C[panel] computed as
  *               matrix-core tiles over it; panels whose rows share few columns
@@ -567,8 +568,9 @@ sp_status_t sp_sddmm_softmax(int m, int k, int d, int nnz, const int *row_indice
  * for 16-bit types; 16-byte aligned operands with strides that keep them so;
  * K and V under 2 GiB per batch entry.  Anything else returns
  * SP_ERROR_NOT_SUPPORTED (the three separate entry points handle it).
- * Batches (batch >= 2) of fp32 heads with d = 32 or 64 on at most 65,536 key
- * rows take a kernel that forms each 16-row panel's key union once for 4
+ * Batches (batch >= 2) of fp32 heads with d = 32 or 64, or of 16-bit heads
+ * with d = 64 (widened to fp32), on at most 65,536 key rows take a kernel that
+ * forms each 16-row panel's key union once for 4
  * batch entries and computes scores and the weighted sum of V as matrix-core
  * tiles over it (the softmax rescaled once per 16-key tile); panels whose rows
  * share few keys, and panels whose union rows of V hold a value that is not

@@ -177,3 +177,39 @@ def test_deterministic_and_order_free():
     g1 = attend(a, qs, ks, vs, 0.125)
     g2 = attend(a, qs, ks, vs, 0.125, ri)
     assert np.array_equal(g1.view(np.uint32), g2.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_16bit_heads(kind):
+    """16-bit Q, K and V (d = 64), widened to fp32 on load: rows 0..159 banded
+    (tiles), rows 160..319 of 60 random keys (the per-row walk, bit-equal to a
+    one-head call), four heads; the oracle takes the decoded values."""
+    tdt, code = {"f16": (torch.float16, oracle.F16), "bf16": (torch.bfloat16, oracle.BF16)}[kind]
+    k, d = 2000, 64
+    rng = np.random.default_rng(11)
+    lists = band_lists(160, k, 32, 64)
+    lists += [sorted(rng.choice(k, 60, replace=False).tolist()) for _ in range(160)]
+    a = from_lists(320, k, lists)
+
+    def to16(x32):
+        t = torch.from_numpy(np.ascontiguousarray(x32)).to(tdt)
+        vals = oracle.decode16(code, t.view(torch.int16).numpy().view(np.uint16))
+        return t, vals.astype(np.float32).reshape(x32.shape)
+
+    q16, q = to16(np.stack([inputs.random_dense(160 + z, a.m, d) for z in range(4)]))
+    k16, kk = to16(np.stack([inputs.random_dense(170 + z, k, d) for z in range(4)]))
+    v16, v = to16(np.stack([inputs.random_dense(180 + z, k, d) for z in range(4)]))
+    out = torch.full((4, a.m, d), float("nan"), device="cuda")
+    note(f"panel-union attention {kind}")
+    sp.sp_sparse_attention(a.m, k, d, a.nnz, None, a.d_ro, a.d_ci, q16.cuda(), k16.cuda(),
+                           v16.cuda(), 0.125, out, 4, a.m * d, k * d, k * d, a.m * d)
+    got = host(out)
+    for z in range(4):
+        check_attention(got[z], a.m, k, a.ro, a.ci, q[z], kk[z], v[z], 0.125,
+                        f"{kind} head {z}", rescalings=TILES)
+        one = torch.full((a.m, d), float("nan"), device="cuda")
+        sp.sp_sparse_attention(a.m, k, d, a.nnz, None, a.d_ro, a.d_ci, q16[z].cuda(),
+                               k16[z].cuda(), v16[z].cuda(), 0.125, one)
+        ref = host(one)
+        assert np.array_equal(got[z][160:].view(np.uint32), ref[160:].view(np.uint32)), \
+            f"{kind} head {z}: per-row panels differ from the one-head call"

@@ -1,5 +1,5 @@
-"""GPU parity of the panel-union SpMM (batched fp32, n = 64, 128 or 256, at most
-65,536 rows of B).
+"""GPU parity of the panel-union SpMM (batched; fp32, or 16-bit values and B
+widened to fp32; n = 64, 128 or 256; at most 65,536 rows of B).
 
 A workgroup takes 16 consecutive rows and four batch entries, forms the union
 of the rows' columns once, and computes each entry's C[panel] = A[panel,
@@ -231,3 +231,42 @@ def test_deterministic():
     g1, _ = run(a, vals, bs, n)
     g2, _ = run(a, vals, bs, n)
     assert np.array_equal(g1.view(np.uint32), g2.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind,n", [("f16", 64), ("bf16", 64), ("bf16", 128)])
+def test_16bit(kind, n):
+    """16-bit values and B, widened to fp32 on load (C fp32): rows 0..159 banded
+    (tiles), rows 160..319 of 60 random columns (the wide kernel's
+    accumulation, bit-equal to the 16-bit wide kernel); the oracle takes the
+    decoded values."""
+    tdt, code = {"f16": (torch.float16, oracle.F16), "bf16": (torch.bfloat16, oracle.BF16)}[kind]
+    k = 3000
+    lists = band_lists(160, k, 32, 64) + random_lists(9, 160, k, 60)
+    a = from_lists(320, k, lists)
+
+    def to16(x32):
+        t = torch.from_numpy(np.ascontiguousarray(x32)).to(tdt)
+        vals = oracle.decode16(code, t.view(torch.int16).numpy().view(np.uint16))
+        return t.cuda(), vals.astype(np.float32).reshape(x32.shape)
+
+    v16, vals = to16(np.stack([inputs.random_dense(200 + z, a.nnz) for z in range(4)]))
+    b16, bs = to16(np.stack([inputs.random_dense(210 + z, k, n) for z in range(4)]))
+    c = torch.full((4, a.m, n), float("nan"), device="cuda")
+    name = sp.sp_spmm_kernel_name(a.m, k, n, a.nnz, v16, a.d_ci, b16, c, 4, a.nnz, k * n, a.m * n)
+    assert name == "panel_union"
+    note(f"panel-union spmm {kind} n={n}")
+    sp.sp_spmm_ex(a.m, k, n, a.nnz, None, v16, a.d_ro, a.d_ci, b16, c, 4, a.nnz, k * n, a.m * n)
+    got = host(c)
+    # the wide kernel's reference: B with zero rows appended past 65,536
+    bw = torch.zeros(4, WIDE_K, n, dtype=tdt, device="cuda")
+    bw[:, :k] = b16
+    cw = torch.full((4, a.m, n), float("nan"), device="cuda")
+    assert sp.sp_spmm_kernel_name(a.m, WIDE_K, n, a.nnz, v16, a.d_ci, bw, cw, 4, a.nnz,
+                                  WIDE_K * n, a.m * n) == "wide"
+    sp.sp_spmm_ex(a.m, WIDE_K, n, a.nnz, None, v16, a.d_ro, a.d_ci, bw, cw, 4, a.nnz,
+                  WIDE_K * n, a.m * n)
+    ref_w = host(cw)
+    for z in range(4):
+        check_oracle(a, got[z], vals[z], bs[z], f"{kind} n={n} entry {z}")
+        assert np.array_equal(got[z][160:].view(np.uint32), ref_w[z][160:].view(np.uint32)), \
+            f"{kind} entry {z}: fallback rows differ from the wide kernel"

@@ -298,15 +298,17 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attention_kernel(AttnParam
 // fixed order: deterministic, rounding in the MFMA's order.
 namespace pu = panel_union;
 
-template <int kD>
+template <typename E, int kD>
 __global__ __launch_bounds__(pu::kThreads) void attention_union_kernel(AttnParams p)
 {
     typedef float f4 __attribute__((ext_vector_type(4)));
-    using V4 = GVec<float, 4>;
+    constexpr int kVecE = 16 / (int)Elem<E>::kBytes;  // elements per 16-byte vector
+    constexpr unsigned kEb = Elem<E>::kBytes;
     constexpr int kS = kD / 4;     // score MFMA steps per tile: elements of d per lane
     constexpr int kNc = kD / 16;   // output columns per lane, one accumulator each
-    constexpr int kDv = kD / 4;    // 16-byte vectors per row (the per-row walk)
-    using Sh = AttnShape<float, kDv>;
+    constexpr int kDv = kD / kVecE;  // 16-byte vectors per row (the per-row walk)
+    static_assert(kS % kVecE == 0, "whole vectors per lane");
+    using Sh = AttnShape<E, kDv>;
     constexpr int kPp = 17;        // pitch of the weight tile (odd: the transposed read is spread over banks)
     __shared__ pu::Shared s;
     __shared__ float s_p[pu::kWaves][16 * kPp];
@@ -326,8 +328,8 @@ __global__ __launch_bounds__(pu::kThreads) void attention_union_kernel(AttnParam
     auto per_row = [&]() {
 #pragma unroll 1
         for (int i = 0; i < pp.nr; ++i)
-            attention_row<float, kDv>(p, z, pp.r0 + i, lane, s_koff_all[wave], s_voff_all[wave],
-                                      s_e_all[wave]);
+            attention_row<E, kDv>(p, z, pp.r0 + i, lane, s_koff_all[wave], s_voff_all[wave],
+                                  s_e_all[wave]);
     };
     if (nu < 0) {
         per_row();
@@ -335,32 +337,35 @@ __global__ __launch_bounds__(pu::kThreads) void attention_union_kernel(AttnParam
     }
 
     const int ntiles = (nu + 15) / 16;
-    const unsigned rowbytes = (unsigned)kD * 4u;
-    const unsigned qo_bytes = (unsigned)p.m * rowbytes;
+    const unsigned rowbytes = (unsigned)kD * kEb;      // a row of Q, K or V
+    const unsigned orowbytes = (unsigned)kD * 4u;      // a row of the fp32 output
     float *oz = p.out + z * p.stride_out;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(static_cast<const float *>(p.q) + z * p.stride_q), 0, (int)qo_bytes,
-        0x00020000);
+        const_cast<E *>(static_cast<const E *>(p.q) + z * p.stride_q), 0,
+        (int)((unsigned)p.m * rowbytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(static_cast<const float *>(p.k) + z * p.stride_k), 0,
-        (int)p.kv_bytes, 0x00020000);
+        const_cast<E *>(static_cast<const E *>(p.k) + z * p.stride_k), 0, (int)p.kv_bytes,
+        0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(static_cast<const float *>(p.v) + z * p.stride_v), 0,
-        (int)p.kv_bytes, 0x00020000);
+        const_cast<E *>(static_cast<const E *>(p.v) + z * p.stride_v), 0, (int)p.kv_bytes,
+        0x00020000);
     const __amdgpu_buffer_rsrc_t ro =
-        __builtin_amdgcn_make_buffer_rsrc(oz, 0, (int)qo_bytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(oz, 0, (int)((unsigned)p.m * orowbytes), 0x00020000);
     const int jl = lane % 16;  // the lane's Q row and key of a tile; its output column group
     const int q = lane / 16;   // the lane's 16-byte piece of each 64-byte block of d; key of a step
     float *tp = s_p[wave];
 
+    // The lane's kS elements of a Q or K row: vector v holds elements
+    // 4 kVecE v + kVecE q ... + kVecE - 1, so the four lanes of a row read 64
+    // contiguous bytes per instruction; step kVecE v + s multiplies element
+    // 4 kVecE v + kVecE q + s of both.
+    auto lane_elem_bytes = [&](int v) { return (unsigned)(4 * kVecE * v + kVecE * q) * kEb; };
     float xa[kS];
     {
         const unsigned base = jl < pp.nr ? (unsigned)(pp.r0 + jl) * rowbytes : kOutOfRange;
 #pragma unroll
-        for (int v = 0; v < kS / 4; ++v) {
-            const V4::T t = V4::buf_load(rq, base + (unsigned)(16 * v + 4 * q) * 4u);
-            memcpy(&xa[4 * v], &t, sizeof(t));
-        }
+        for (int v = 0; v < kS / kVecE; ++v)
+            load_widen<E, kVecE>(rq, base + lane_elem_bytes(v), &xa[kVecE * v]);
     }
     struct Tile {
         float k[kS];        // key 16 T + jl: the lane's elements
@@ -372,24 +377,15 @@ __global__ __launch_bounds__(pu::kThreads) void attention_union_kernel(AttnParam
             const unsigned col = (unsigned)s.ucol[min(u, pu::kMaxCols - 1)];
             const unsigned base = u < nu ? col * rowbytes : kOutOfRange;
 #pragma unroll
-            for (int v = 0; v < kS / 4; ++v) {
-                const V4::T x = V4::buf_load(rk, base + (unsigned)(16 * v + 4 * q) * 4u);
-                memcpy(&t.k[4 * v], &x, sizeof(x));
-            }
+            for (int v = 0; v < kS / kVecE; ++v)
+                load_widen<E, kVecE>(rk, base + lane_elem_bytes(v), &t.k[kVecE * v]);
         }
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const int u = 16 * T + 4 * st + q;
             const unsigned col = (unsigned)s.ucol[min(u, pu::kMaxCols - 1)];
-            const unsigned off = (u < nu ? col * rowbytes : kOutOfRange) + (unsigned)(kNc * jl) * 4u;
-            if constexpr (kNc == 4) {
-                const V4::T x = V4::buf_load(rv, off);
-                memcpy(t.v[st], &x, sizeof(x));
-            } else {
-                const auto x = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)off, 0, 0);
-                t.v[st][0] = __uint_as_float(x[0]);
-                t.v[st][1] = __uint_as_float(x[1]);
-            }
+            const unsigned off = (u < nu ? col * rowbytes : kOutOfRange) + (unsigned)(kNc * jl) * kEb;
+            load_widen<E, kNc>(rv, off, t.v[st]);
         }
     };
     f4 o[kNc];
@@ -451,7 +447,7 @@ __global__ __launch_bounds__(pu::kThreads) void attention_union_kernel(AttnParam
         const int row = 4 * q + r;
         const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
         const unsigned off =
-            row < pp.nr ? (unsigned)(pp.r0 + row) * rowbytes + (unsigned)(kNc * jl) * 4u
+            row < pp.nr ? (unsigned)(pp.r0 + row) * orowbytes + (unsigned)(kNc * jl) * 4u
                         : kOutOfRange;
         if constexpr (kNc == 4) {
             typedef unsigned u4 __attribute__((ext_vector_type(4)));
@@ -469,10 +465,10 @@ __global__ __launch_bounds__(pu::kThreads) void attention_union_kernel(AttnParam
     if (__builtin_amdgcn_ballot_w64(!finite) != 0) per_row();
 }
 
-template <int kD>
+template <typename E, int kD>
 hipError_t launch_union_t(const AttnParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL((attention_union_kernel<kD>), dim3((unsigned)pu::grid(p.m, p.batch)),
+    hipLaunchKernelGGL((attention_union_kernel<E, kD>), dim3((unsigned)pu::grid(p.m, p.batch)),
                        dim3(pu::kThreads), pu::dynamic_lds(p.k_rows), s, p);
     return hipGetLastError();
 }
@@ -536,12 +532,20 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t stream)
     p.stride_k = a.stride_k;
     p.stride_v = a.stride_v;
     p.stride_out = a.stride_out;
-    // Batches of fp32 heads of 32 or 64 on up to 65,536 keys: the panel-union
-    // kernel, which runs the per-row walk on panels whose rows share few keys.
-    if (a.dtype == Dtype::f32 && (a.d == 32 || a.d == 64) && a.batch >= 2 &&
+    // Batches of fp32 heads of 32 or 64, or 16-bit heads of 64, on up to
+    // 65,536 keys: the panel-union kernel, which runs the per-row walk on
+    // panels whose rows share few keys.
+    if ((a.d == 64 || (a.d == 32 && a.dtype == Dtype::f32)) && a.batch >= 2 &&
         a.k_rows <= pu::kMaxK && (long long)a.m * a.d * 4 < (1LL << 31) &&
-        pu::grid(a.m, a.batch) <= 0x7fffffffLL)
-        return a.d == 32 ? launch_union_t<32>(p, stream) : launch_union_t<64>(p, stream);
+        pu::grid(a.m, a.batch) <= 0x7fffffffLL) {
+        switch (a.dtype) {
+        case Dtype::f16: return launch_union_t<_Float16, 64>(p, stream);
+        case Dtype::bf16: return launch_union_t<bf16, 64>(p, stream);
+        default:
+            return a.d == 32 ? launch_union_t<float, 32>(p, stream)
+                             : launch_union_t<float, 64>(p, stream);
+        }
+    }
     switch (a.dtype) {
     case Dtype::f16: return launch_e<_Float16>(dv, p, stream);
     case Dtype::bf16: return launch_e<bf16>(dv, p, stream);

@@ -279,4 +279,33 @@ template <typename E> __device__ __forceinline__ void load4_f32(const E *p, floa
     f[3] = Elem<E>::hi(v.y);
 }
 
+// Loads kN consecutive elements of type E (kN * bytes <= 16) and widens them.
+// (through a buffer resource; out-of-range offsets read as zeros)
+template <typename E, int kN>
+__device__ __forceinline__ void load_widen(__amdgpu_buffer_rsrc_t r, unsigned off, float *f)
+{
+    constexpr int kBytes = kN * (int)Elem<E>::kBytes;
+    unsigned w[4];
+    if constexpr (kBytes == 16) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+        w[0] = x[0], w[1] = x[1], w[2] = x[2], w[3] = x[3];
+    } else if constexpr (kBytes == 8) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+        w[0] = x[0], w[1] = x[1];
+    } else {
+        static_assert(kBytes == 4, "4, 8 or 16 bytes");
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    }
+    if constexpr (__is_same(E, float)) {
+#pragma unroll
+        for (int i = 0; i < kN; ++i) f[i] = __uint_as_float(w[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kN / 2; ++i) {
+            f[2 * i] = Elem<E>::lo(w[i]);
+            f[2 * i + 1] = Elem<E>::hi(w[i]);
+        }
+    }
+}
+
 }  // namespace spk

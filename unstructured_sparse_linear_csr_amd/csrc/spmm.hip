@@ -303,13 +303,15 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void spmm_split_kernel(SpmmPar
 // the MFMA's order, within the same bound.
 namespace pu = panel_union;
 
-template <int kLpr, bool kVecCsr>
+template <typename E, int kLpr, bool kVecCsr>
 __global__ __launch_bounds__(pu::kThreads) void spmm_union_kernel(SpmmParams p)
 {
     typedef float f4 __attribute__((ext_vector_type(4)));
     typedef unsigned u4 __attribute__((ext_vector_type(4)));
-    using V4 = GVec<float, 4>;
-    constexpr int kBlocks = kLpr / 16;  // 64-column blocks of C: n = 64 kBlocks
+    constexpr int kVec = 16 / (int)Elem<E>::kBytes;  // elements per 16-byte vector
+    constexpr unsigned kEb = Elem<E>::kBytes;
+    using VE = GVec<E, kVec>;
+    constexpr int kBlocks = kLpr * kVec / 64;  // 64-column blocks of C: n = kLpr kVec
     constexpr int kRpw = kWave / kLpr;  // rows per wave on the per-entry path
     constexpr int kChunk = kEpl * kLpr;
     constexpr int kPitch = kChunk + kU + 4;
@@ -326,8 +328,8 @@ __global__ __launch_bounds__(pu::kThreads) void spmm_union_kernel(SpmmParams p)
     const int lane = threadIdx.x % kWave;
     const int z = pp.hg * pu::kWaves + wave;
     if (z >= p.batch) return;
-    const float *vals = static_cast<const float *>(p.values) + z * p.stride_values;
-    const float *bz = static_cast<const float *>(p.b) + z * p.stride_b;
+    const E *vals = static_cast<const E *>(p.values) + z * p.stride_values;
+    const E *bz = static_cast<const E *>(p.b) + z * p.stride_b;
     float *cz = p.c + z * p.stride_c;
 
     auto per_entry = [&]() {
@@ -341,10 +343,12 @@ __global__ __launch_bounds__(pu::kThreads) void spmm_union_kernel(SpmmParams p)
             const int row = pp.r0 + (has ? slot : 0);
             const int p0 = has ? p.row_offsets[row] : 0;
             const int p1 = has ? p.row_offsets[row + 1] : 0;
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
-            wide_accumulate<float, kLpr, 4, kVecCsr, true, true>(p, vals, bz, p0, p1, gl, 4 * gl,
-                                                                 true, g_off, g_val, acc);
-            if (has) V4::store(cz + (size_t)row * (size_t)p.n + 4 * gl, acc);
+            float acc[kVec];
+#pragma unroll
+            for (int t = 0; t < kVec; ++t) acc[t] = 0.f;
+            wide_accumulate<E, kLpr, kVec, kVecCsr, true, true>(p, vals, bz, p0, p1, gl,
+                                                                kVec * gl, true, g_off, g_val, acc);
+            if (has) VE::store(cz + (size_t)row * (size_t)p.n + kVec * gl, acc);
         }
     };
     if (nu < 0) {
@@ -353,41 +357,47 @@ __global__ __launch_bounds__(pu::kThreads) void spmm_union_kernel(SpmmParams p)
     }
 
     const int ntiles = (nu + 15) / 16;
-    const unsigned rowbytes = (unsigned)p.n * 4u;
+    const unsigned rowbytes = (unsigned)p.n * kEb;   // a row of B
+    const unsigned crowbytes = (unsigned)p.n * 4u;   // a row of the fp32 C
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(vals), 0, (int)p.csr_bytes, 0x00020000);
+        const_cast<E *>(vals), 0, (int)p.csr_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(bz), 0, (int)p.b_bytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<E *>(bz), 0, (int)p.b_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rc =
         __builtin_amdgcn_make_buffer_rsrc(cz, 0, (int)p.c_bytes, 0x00020000);
     const int jl = lane % 16;  // the lane's row of A, column group of B and C
     const int q = lane / 16;   // the lane's union slot within a step
     struct Tile {
         float a[4];
-        V4::T b[4];
+        float b[4][4];
     };
     bool finite = true;
 #pragma unroll 1
     for (int cb = 0; cb < kBlocks; ++cb) {
-        const unsigned col_bytes = (unsigned)(64 * cb + 4 * jl) * 4u;
+        const unsigned col = (unsigned)(64 * cb + 4 * jl);  // the lane's first column of C
         auto load = [&](int T, Tile &t) {
             // the step's map entries and union columns first (clamped slots,
             // so every read is in bounds; slots past the union are not used)
-            unsigned idx[4], col[4];
+            unsigned idx[4], ucol[4];
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const int uc = min(16 * T + 4 * st + q, pu::kMaxCols - 1);
                 idx[st] = s.emap[jl * pu::kEmapStride + uc];
-                col[st] = (unsigned)s.ucol[uc];
+                ucol[st] = (unsigned)s.ucol[uc];
             }
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const bool ok = 16 * T + 4 * st + q < nu;
                 const unsigned vo =
-                    ok && idx[st] ? (unsigned)(pp.e0 + (int)idx[st] - 1) * 4u : kOutOfRange;
-                t.a[st] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, (int)vo, 0, 0));
-                const unsigned base = ok ? col[st] * rowbytes : kOutOfRange;
-                t.b[st] = V4::buf_load(rb, base + col_bytes | (base & kOutOfRange));
+                    ok && idx[st] ? (unsigned)(pp.e0 + (int)idx[st] - 1) * kEb : kOutOfRange;
+                if constexpr (__is_same(E, float)) {
+                    t.a[st] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, (int)vo, 0, 0));
+                } else {
+                    const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(rv, (int)vo, 0, 0);
+                    t.a[st] = Elem<E>::lo(h);
+                }
+                const unsigned base = ok ? ucol[st] * rowbytes : kOutOfRange;
+                load_widen<E, 4>(rb, base + col * kEb | (base & kOutOfRange), t.b[st]);
             }
         };
         f4 acc[4];
@@ -396,12 +406,11 @@ __global__ __launch_bounds__(pu::kThreads) void spmm_union_kernel(SpmmParams p)
         auto mma = [&](const Tile &t) {
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                float bv[4];
-                memcpy(bv, &t.b[st], sizeof(bv));
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    finite = finite && __builtin_isfinite(bv[c]);
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.a[st], bv[c], acc[c], 0, 0, 0);
+                    finite = finite && __builtin_isfinite(t.b[st][c]);
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.a[st], t.b[st][c], acc[c], 0,
+                                                                  0, 0);
                 }
             }
         };
@@ -420,7 +429,7 @@ __global__ __launch_bounds__(pu::kThreads) void spmm_union_kernel(SpmmParams p)
         for (int r = 0; r < 4; ++r) {
             const int row = 4 * q + r;
             const unsigned off =
-                row < pp.nr ? (unsigned)(pp.r0 + row) * rowbytes + col_bytes : kOutOfRange;
+                row < pp.nr ? (unsigned)(pp.r0 + row) * crowbytes + col * 4u : kOutOfRange;
             const u4 ov = {__float_as_uint(acc[0][r]), __float_as_uint(acc[1][r]),
                            __float_as_uint(acc[2][r]), __float_as_uint(acc[3][r])};
             __builtin_amdgcn_raw_buffer_store_b128(ov, rc, (int)off, 0, 0);
@@ -888,20 +897,34 @@ hipError_t launch_split(int lpr, const SpmmParams &p, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int kLpr, bool kVecCsr>
+template <typename E, int kLpr, bool kVecCsr>
 hipError_t launch_union_t(const SpmmParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL((spmm_union_kernel<kLpr, kVecCsr>), dim3((unsigned)pu::grid(p.m, p.batch)),
-                       dim3(pu::kThreads), pu::dynamic_lds(p.k), s, p);
+    hipLaunchKernelGGL((spmm_union_kernel<E, kLpr, kVecCsr>),
+                       dim3((unsigned)pu::grid(p.m, p.batch)), dim3(pu::kThreads),
+                       pu::dynamic_lds(p.k), s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_union(int lpr, bool vec_csr, const SpmmParams &p, hipStream_t s)
+// lpr: the wide kernel's lanes per row for n (n = lpr * elements per vector)
+template <typename E, int kL0>
+hipError_t launch_union_e(int lpr, bool vec_csr, const SpmmParams &p, hipStream_t s)
 {
-    switch (lpr) {
-    case 16: return vec_csr ? launch_union_t<16, true>(p, s) : launch_union_t<16, false>(p, s);
-    case 32: return vec_csr ? launch_union_t<32, true>(p, s) : launch_union_t<32, false>(p, s);
-    default: return vec_csr ? launch_union_t<64, true>(p, s) : launch_union_t<64, false>(p, s);
+    if (lpr == kL0)
+        return vec_csr ? launch_union_t<E, kL0, true>(p, s) : launch_union_t<E, kL0, false>(p, s);
+    if (lpr == 2 * kL0)
+        return vec_csr ? launch_union_t<E, 2 * kL0, true>(p, s)
+                       : launch_union_t<E, 2 * kL0, false>(p, s);
+    return vec_csr ? launch_union_t<E, 4 * kL0, true>(p, s)
+                   : launch_union_t<E, 4 * kL0, false>(p, s);
+}
+
+hipError_t launch_union(Dtype dtype, int lpr, bool vec_csr, const SpmmParams &p, hipStream_t s)
+{
+    switch (dtype) {
+    case Dtype::f16: return launch_union_e<_Float16, 8>(lpr, vec_csr, p, s);
+    case Dtype::bf16: return launch_union_e<bf16, 8>(lpr, vec_csr, p, s);
+    default: return launch_union_e<float, 16>(lpr, vec_csr, p, s);
     }
 }
 
@@ -1053,16 +1076,15 @@ hipError_t plan_spmm(const SpmmArgs &a, SpmmPlan *plan)
             }
         }
     }
-    // Batched fp32 problems of 64, 128 or 256 columns on up to 65,536 rows of
-    // B: the panel-union kernel, which falls back to the wide kernel's
-    // accumulation panel by panel where rows share few columns.
-    if (plan->kind == SpmmPlan::kWide && f32 && vec && buf && a.batch >= 2 &&
-        a.k <= pu::kMaxK && (a.n == 64 || a.n == 128 || a.n == 256) &&
-        (long long)a.m * a.n * 4 < (1LL << 31) && (long long)a.nnz * 4 < (1LL << 31) &&
-        pu::grid(a.m, a.batch) <= 0x7fffffffLL) {
+    // Batched problems of 64, 128 or 256 columns on up to 65,536 rows of B: the
+    // panel-union kernel, which falls back to the wide kernel's accumulation
+    // panel by panel where rows share few columns.
+    if (plan->kind == SpmmPlan::kWide && vec && buf && a.batch >= 2 && a.k <= pu::kMaxK &&
+        (a.n == 64 || a.n == 128 || a.n == 256) && (long long)a.m * a.n * 4 < (1LL << 31) &&
+        (long long)a.nnz * eb < (1LL << 31) && pu::grid(a.m, a.batch) <= 0x7fffffffLL) {
         plan->kind = SpmmPlan::kUnion;
         p.c_bytes = (unsigned)((long long)a.m * a.n * 4);
-        p.csr_bytes = (unsigned)((long long)a.nnz * 4);
+        p.csr_bytes = (unsigned)((long long)a.nnz * eb);
     }
     if (narrow) plan->kind = SpmmPlan::kNarrow;
     if (lds_ok) {
@@ -1106,7 +1128,7 @@ hipError_t run_spmm(const SpmmPlan &plan, hipStream_t stream)
     const SpmmParams &p = plan.p;
     switch (plan.kind) {
     case SpmmPlan::kUnion:
-        return launch_union(plan.lpr, plan.vec_csr, p, stream);
+        return launch_union(plan.dtype, plan.lpr, plan.vec_csr, p, stream);
     case SpmmPlan::kPanel:
         return plan.panel == 0 ? launch_panel_t<PanelMany>(p, plan.q, stream)
                                : launch_panel_t<PanelFew>(p, plan.q, stream);
