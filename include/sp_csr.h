@@ -415,8 +415,10 @@ sp_status_t sp_spmm_kernel_name(int m, int k, int n, int nnz, const int *row_ind
  *               is formed once for 4 batch entries and the scores computed as
  *               matrix-core tiles over it; panels whose rows share few columns
  *               run the multi-row walk;
- *   "multirow"  several short rows per wave (fp32, 16-byte-aligned X and Y,
- *               d a multiple of 4 from 20 to 64, row slots not split);
+ *   "multirow"  several short rows per wave (16-byte-aligned X and Y, one
+ *               16-byte vector per lane with 8 or 16 lanes per entry: fp32 d a
+ *               multiple of 4 from 20 to 64, 16-bit d a multiple of 8 from 40
+ *               to 128; row slots not split);
  *   "rows"      one wave per row slot;
  *   "split"     one batch entry whose rows average 16 entries or more: a
  *               row's 64-entry windows spread over a workgroup of 4 waves;

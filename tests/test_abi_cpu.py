@@ -385,12 +385,15 @@ def test_sddmm_kernel_name(lib):
     assert call(100, 100, 20, 500) == OK and nm() == b"multirow"   # d = 20: groups of 8
     # one batch entry whose rows average 16 entries or more: split over waves
     assert call(64, 64, 64, 64 * 16) == OK and nm() == b"split"
-    # d = 16 (4 lanes per entry), d = 68 (two vectors per lane), misaligned X, bf16:
-    # one row per wave
+    # d = 16 (4 lanes per entry), d = 68 (two vectors per lane), misaligned X, bf16
+    # at d = 32 (4 lanes per entry): one row per wave
     assert call(100, 100, 16, 500) == OK and nm() == b"rows"
     assert call(100, 100, 68, 500) == OK and nm() == b"rows"
     assert call(100, 100, 64, 500, x=odd) == OK and nm() == b"rows"
-    assert call(100, 100, 64, 500, dtype=2) == OK and nm() == b"rows"
+    assert call(100, 100, 32, 500, dtype=2) == OK and nm() == b"rows"
+    # bf16 at d = 64 and 128 (8 and 16 lanes per entry): several rows per wave
+    assert call(100, 100, 64, 500, dtype=2) == OK and nm() == b"multirow"
+    assert call(100, 100, 128, 500, dtype=1) == OK and nm() == b"multirow"
     assert call(100, 100, 0, 500) == OK and nm() == b"fill"
     assert call(100, 100, 64, 500, layout=1) == OK and nm() in (b"dk_panel", b"dk_tile",
                                                                    b"columns")

@@ -157,8 +157,8 @@ def test_general_epilogue(beta):
 
 def test_not_taken_outside_its_shapes():
     """d = 16 (4 lanes per entry), d = 68 (two vectors per lane), one batch
-    entry of long rows (split over waves) and bf16 operands keep the other
-    kernels."""
+    entry of long rows (split over waves) and bf16 operands of d = 32 (4 lanes
+    per entry) keep the other kernels."""
     a = mixed_csr(5, 64, 300, [40])
     for d, nb in ((16, 2), (68, 2), (64, 1)):
         x = torch.zeros(nb, a.m, d, device="cuda")
@@ -170,7 +170,41 @@ def test_not_taken_outside_its_shapes():
     x = torch.zeros(s.m, 64, device="cuda")
     y = torch.zeros(s.k, 64, device="cuda")
     assert sp.sp_sddmm_kernel_name(s.m, s.k, 64, s.nnz, x, y) == "multirow"
-    xb = torch.zeros(2, a.m, 64, device="cuda", dtype=torch.bfloat16)
-    yb = torch.zeros(2, a.k, 64, device="cuda", dtype=torch.bfloat16)
-    assert sp.sp_sddmm_kernel_name(a.m, a.k, 64, a.nnz, xb, yb, 2, a.m * 64, a.k * 64,
+    xb = torch.zeros(2, a.m, 32, device="cuda", dtype=torch.bfloat16)
+    yb = torch.zeros(2, a.k, 32, device="cuda", dtype=torch.bfloat16)
+    assert sp.sp_sddmm_kernel_name(a.m, a.k, 32, a.nnz, xb, yb, 2, a.m * 32, a.k * 32,
                                    a.nnz) == "rows"
+
+
+def to16(x32, kind):
+    """(device tensor of the 16-bit rounding of x32, its exact fp32 values)."""
+    tdt, code = {"f16": (torch.float16, oracle.F16), "bf16": (torch.bfloat16, oracle.BF16)}[kind]
+    t = torch.from_numpy(np.ascontiguousarray(x32)).to(tdt)
+    vals = oracle.decode16(code, t.view(torch.int16).numpy().view(np.uint16))
+    return t.cuda(), vals.astype(np.float32).reshape(x32.shape)
+
+
+@pytest.mark.parametrize("kind,d", [("f16", 64), ("bf16", 64), ("bf16", 40), ("f16", 128)])
+def test_16bit(kind, d):
+    """16-bit X and Y (8 elements per 16-byte vector: 8 lanes per entry up to
+    d = 64, 16 up to 128), three batch entries: bit-equal to the one-row
+    kernel's sums (one batch entry of rows averaging 16+ entries takes the
+    split kernel) and within the bound of the oracle on the decoded values."""
+    a = mixed_csr(d + 7, 301, WIDE_K)
+    x16, x = to16(np.stack([inputs.random_dense(300 * d + z, a.m, d) for z in range(3)]), kind)
+    y16, y = to16(np.stack([inputs.random_dense(400 * d + z, a.k, d) for z in range(3)]), kind)
+    out = torch.full((3, a.nnz), float("nan"), device="cuda")
+    name = sp.sp_sddmm_kernel_name(a.m, a.k, d, a.nnz, x16, y16, 3, a.m * d, a.k * d, a.nnz)
+    assert name == "multirow"
+    note(f"multirow sddmm {kind} d={d}")
+    sp.sp_sddmm_ex(a.m, a.k, d, a.nnz, None, a.d_ro, a.d_ci, x16, y16, 0.5, out, 3, a.m * d,
+                   a.k * d, a.nnz)
+    got = host(out)
+    for z in range(3):
+        one = torch.full((a.nnz,), float("nan"), device="cuda")
+        assert sp.sp_sddmm_kernel_name(a.m, a.k, d, a.nnz, x16[z], y16[z]) == "split"
+        sp.sp_sddmm_ex(a.m, a.k, d, a.nnz, None, a.d_ro, a.d_ci, x16[z], y16[z], 0.5, one)
+        ref = host(one)
+        assert np.array_equal(got[z].view(np.uint32), ref.view(np.uint32)), f"{kind} entry {z}"
+        s, s_abs = oracle.sddmm(a.m, a.k, d, a.ro, a.ci, x[z], y[z])
+        check_close(got[z], 0.5 * s, 0.5 * s_abs, f"{kind} d={d} entry {z}")

@@ -243,3 +243,42 @@ def test_deterministic_and_order_free():
     g1, _ = run_batched(a, xs, ys, 1.0)
     g2, _ = run_batched(a, xs, ys, 1.0, swizzle(a))
     assert np.array_equal(g1.view(np.uint32), g2.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind,d", [("f16", 64), ("bf16", 64), ("bf16", 128)])
+def test_16bit(kind, d):
+    """16-bit X and Y widened to fp32 for the tiles: rows 0..159 banded (tiles),
+    rows 160..319 of 60 random columns (the multi-row walk, bit-equal to the
+    one-row kernel's sums), four batch entries; the oracle on the decoded
+    values."""
+    tdt, code = {"f16": (torch.float16, oracle.F16), "bf16": (torch.bfloat16, oracle.BF16)}[kind]
+
+    def to16(x32):
+        t = torch.from_numpy(np.ascontiguousarray(x32)).to(tdt)
+        vals = oracle.decode16(code, t.view(torch.int16).numpy().view(np.uint16))
+        return t.cuda(), vals.astype(np.float32).reshape(x32.shape)
+
+    k = 3000
+    band = band_csr(160, k, 32, 64)
+    lists = [band.ci[band.ro[i]:band.ro[i + 1]].tolist() for i in range(160)]
+    lists += random_lists(13, 160, k, 60)
+    a = from_lists(320, k, lists)
+    x16, x = to16(np.stack([inputs.random_dense(500 + z, a.m, d) for z in range(4)]))
+    y16, y = to16(np.stack([inputs.random_dense(510 + z, k, d) for z in range(4)]))
+    out = torch.full((4, a.nnz), float("nan"), device="cuda")
+    assert sp.sp_sddmm_kernel_name(a.m, k, d, a.nnz, x16, y16, 4, a.m * d, k * d,
+                                   a.nnz) == "panel_union"
+    note(f"panel-union sddmm {kind} d={d}")
+    sp.sp_sddmm_ex(a.m, k, d, a.nnz, None, a.d_ro, a.d_ci, x16, y16, 0.125, out, 4, a.m * d,
+                   k * d, a.nnz)
+    got = host(out)
+    tail = slice(int(a.ro[160]), a.nnz)
+    for z in range(4):
+        s, s_abs = oracle.sddmm(a.m, k, d, a.ro, a.ci, x[z], y[z])
+        check_close(got[z], 0.125 * s, 0.125 * s_abs, f"{kind} d={d} entry {z}")
+        one = torch.full((a.nnz,), float("nan"), device="cuda")
+        assert sp.sp_sddmm_kernel_name(a.m, k, d, a.nnz, x16[z], y16[z]) == "split"
+        sp.sp_sddmm_ex(a.m, k, d, a.nnz, None, a.d_ro, a.d_ci, x16[z], y16[z], 0.125, one)
+        ref = host(one)
+        assert np.array_equal(got[z][tail].view(np.uint32), ref[tail].view(np.uint32)), \
+            f"{kind} entry {z}: fallback panels differ from the one-row sums"

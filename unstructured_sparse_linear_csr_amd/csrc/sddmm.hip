@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kSplitParts * kWave) void sddmm_split_kernel(SddmmP
 // multirow_rows is the walk of one wave over its rows (batch entry z; the
 // group of lane l takes `row` if `has`, else nothing); the kernel maps row
 // slots to rows through the row order.
-template <int kG>
+template <typename E, int kG>
 __device__ __forceinline__ void multirow_rows(const SddmmParams &p, long long z, bool has,
                                               int row)
 {
@@ -61,30 +61,32 @@ __device__ __forceinline__ void multirow_rows(const SddmmParams &p, long long z,
     constexpr int kU = 4;            // steps per batch of gathers
     constexpr int kBpc = kC / kU;    // batches per chunk
     static_assert(kC % kU == 0, "whole batches per chunk");
-    using V = GVec<float, 4>;
+    constexpr int kVecE = 16 / (int)Elem<E>::kBytes;  // elements per 16-byte vector
+    using V = GVec<E, kVecE>;
+    using VT = typename V::T;
     const int lane = threadIdx.x % kWave;
     const int grp = lane / kG;
     const int gl = lane - grp * kG;
     const int p0 = p.row_offsets[row];
     const int len = has ? p.row_offsets[row + 1] - p0 : 0;
 
-    const unsigned rowbytes = (unsigned)p.d * 4u;
-    const float *xz = static_cast<const float *>(p.x) + z * p.stride_x;
-    const float *yz = static_cast<const float *>(p.y) + z * p.stride_y;
+    const unsigned rowbytes = (unsigned)p.d * Elem<E>::kBytes;
+    const E *xz = static_cast<const E *>(p.x) + z * p.stride_x;
+    const E *yz = static_cast<const E *>(p.y) + z * p.stride_y;
     float *oz = p.out + z * p.stride_out;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(xz), 0, (int)((unsigned)p.m * rowbytes), 0x00020000);
+        const_cast<E *>(xz), 0, (int)((unsigned)p.m * rowbytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t ry =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(yz), 0, (int)p.y_bytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<E *>(yz), 0, (int)p.y_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int *>(p.col_indices), 0, (int)((unsigned)p.nnz * 4u), 0x00020000);
     const __amdgpu_buffer_rsrc_t ro =
         __builtin_amdgcn_make_buffer_rsrc(oz, 0, (int)((unsigned)p.nnz * 4u), 0x00020000);
 
-    // lanes past d (d < 4 kG) gather nothing: their offsets get the top bit
-    const bool lane_ok = 4 * gl < p.d;
+    // lanes past d (d < kVecE kG) gather nothing: their offsets get the top bit
+    const bool lane_ok = kVecE * gl < p.d;
     const unsigned lane_mask = lane_ok ? 0u : kOutOfRange;
-    const V::T xr = V::buf_load(rx, has && lane_ok ? (unsigned)row * rowbytes + 16u * gl
+    const VT xr = V::buf_load(rx, has && lane_ok ? (unsigned)row * rowbytes + 16u * gl
                                                    : kOutOfRange);
 
     // chunk c's Y-row offset of this lane's entry (out of range past the row)
@@ -104,7 +106,7 @@ __device__ __forceinline__ void multirow_rows(const SddmmParams &p, long long z,
     unsigned off_c = chunk_offsets(0);  // the current chunk's offsets
     unsigned off_n = chunk_offsets(1);  // the next chunk's
     const int src0 = 4 * grp * kG;      // ds_bpermute byte address of lane 0 of the group
-    auto issue = [&](int b, V::T (&yy)[kU]) {
+    auto issue = [&](int b, VT (&yy)[kU]) {
         // batch b: steps (b % kBpc) kU ... of chunk b / kBpc, whose offsets are
         // off_c, or off_n for the first batch of the next chunk
         const unsigned src = (b % kBpc == 0 && b > 0) ? off_n : off_c;
@@ -117,7 +119,7 @@ __device__ __forceinline__ void multirow_rows(const SddmmParams &p, long long z,
         }
     };
     float res = 0.f;
-    auto consume = [&](int b, const V::T (&yy)[kU]) {
+    auto consume = [&](int b, const VT (&yy)[kU]) {
         const int t0 = (b % kBpc) * kU;
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
@@ -145,7 +147,7 @@ __device__ __forceinline__ void multirow_rows(const SddmmParams &p, long long z,
         }
     };
 
-    V::T ya[kU], yb[kU];
+    VT ya[kU], yb[kU];
     issue(0, ya);
     // one exit, at the end (a second exit would leave pending loads on an
     // edge into the loop header, and the compiler would then wait for every
@@ -160,7 +162,7 @@ __device__ __forceinline__ void multirow_rows(const SddmmParams &p, long long z,
     }
 }
 
-template <int kG>
+template <typename E, int kG>
 __global__ __launch_bounds__(kWave) void sddmm_multirow_kernel(SddmmParams p)
 {
     constexpr int kR = kWave / kG;   // rows per wave
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(kWave) void sddmm_multirow_kernel(SddmmParams p)
     const int sl = has ? slot : 0;
     const int *rsrc = p.row_indices ? p.row_indices : p.row_offsets;
     const int rv = rsrc[sl];
-    multirow_rows<kG>(p, z, has, p.row_indices ? rv : sl);
+    multirow_rows<E, kG>(p, z, has, p.row_indices ? rv : sl);
 }
 
 // Batched scores on masks whose neighbouring rows share most of their columns
@@ -201,12 +203,13 @@ namespace pu = panel_union;
 // Batch entries (waves) per workgroup of the union kernel.
 constexpr int kUnionWaves = 4;
 
-template <int kG, int kW>
+template <typename E, int kG, int kW>
 __global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
 {
     typedef float f4 __attribute__((ext_vector_type(4)));
-    using V = GVec<float, 4>;
-    constexpr int kS = kG;   // MFMA steps per tile: elements of d per lane
+    constexpr int kVecE = 16 / (int)Elem<E>::kBytes;  // elements per 16-byte vector
+    constexpr unsigned kEb = Elem<E>::kBytes;
+    constexpr int kS = kG * kVecE / 4;  // MFMA steps per tile: elements of d per lane
     __shared__ pu::SharedT<kW> s;
     extern __shared__ unsigned s_dyn[];
     pu::Panel pp;
@@ -224,49 +227,46 @@ __global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
 #pragma unroll 1
         for (int u = 0; u < pu::kRows / kR; ++u) {
             const int slot = u * kR + lane / kG;
-            multirow_rows<kG>(p, z, slot < nr, slot < nr ? r0 + slot : r0);
+            multirow_rows<E, kG>(p, z, slot < nr, slot < nr ? r0 + slot : r0);
         }
         return;
     }
     const int ntiles = (nu + 15) / 16;
 
-    const unsigned rowbytes = (unsigned)p.d * 4u;
-    const float *xz = static_cast<const float *>(p.x) + z * p.stride_x;
-    const float *yz = static_cast<const float *>(p.y) + z * p.stride_y;
+    const unsigned rowbytes = (unsigned)p.d * kEb;
+    const E *xz = static_cast<const E *>(p.x) + z * p.stride_x;
+    const E *yz = static_cast<const E *>(p.y) + z * p.stride_y;
     float *oz = p.out + z * p.stride_out;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(xz), 0, (int)((unsigned)p.m * rowbytes), 0x00020000);
+        const_cast<E *>(xz), 0, (int)((unsigned)p.m * rowbytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t ry =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(yz), 0, (int)p.y_bytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<E *>(yz), 0, (int)p.y_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t ro =
         __builtin_amdgcn_make_buffer_rsrc(oz, 0, (int)((unsigned)p.nnz * 4u), 0x00020000);
     const int jl = lane % 16;   // the lane's row of X, column of the tile
-    const int q = lane / 16;    // which 16-byte piece of each 64-byte block of d
-    // byte offsets of the lane's vectors within a row (out of range past d)
-    unsigned voff[kS / 4];
+    const int q = lane / 16;    // which 16-byte piece of each 64-byte block of a row
+    // byte offsets of the lane's vectors within a row (out of range past d):
+    // vector v holds elements 4 kVecE v + kVecE q ... + kVecE - 1
+    unsigned voff[kS / kVecE];
 #pragma unroll
-    for (int v = 0; v < kS / 4; ++v) {
-        const int e = 16 * v + 4 * q;
-        voff[v] = e < p.d ? (unsigned)e * 4u : kOutOfRange;
+    for (int v = 0; v < kS / kVecE; ++v) {
+        const int e = 4 * kVecE * v + kVecE * q;
+        voff[v] = e < p.d ? (unsigned)e * kEb : kOutOfRange;
     }
     float xa[kS];
     {
         const unsigned base = jl < nr ? (unsigned)(r0 + jl) * rowbytes : kOutOfRange;
 #pragma unroll
-        for (int v = 0; v < kS / 4; ++v) {
-            const V::T t = V::buf_load(rx, base + voff[v] | (base & kOutOfRange));
-            memcpy(&xa[4 * v], &t, sizeof(t));
-        }
+        for (int v = 0; v < kS / kVecE; ++v)
+            load_widen<E, kVecE>(rx, base + voff[v] | (base & kOutOfRange), &xa[kVecE * v]);
     }
     auto load_tile = [&](int T, float (&yb)[kS]) {
         const int u = 16 * T + jl;
         const unsigned base =
             u < nu ? (unsigned)s.ucol[min(u, pu::kMaxCols - 1)] * rowbytes : kOutOfRange;
 #pragma unroll
-        for (int v = 0; v < kS / 4; ++v) {
-            const V::T t = V::buf_load(ry, base + voff[v] | (base & kOutOfRange));
-            memcpy(&yb[4 * v], &t, sizeof(t));
-        }
+        for (int v = 0; v < kS / kVecE; ++v)
+            load_widen<E, kVecE>(ry, base + voff[v] | (base & kOutOfRange), &yb[kVecE * v]);
     };
     const float alpha = p.alpha, beta = p.beta;
     const float *mvz = p.mask_values ? p.mask_values + z * p.stride_values : nullptr;
@@ -1155,27 +1155,47 @@ hipError_t launch_t(const SddmmParams &p, bool split, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_multirow(int g, const SddmmParams &p, hipStream_t s)
+template <typename E>
+hipError_t launch_multirow_e(int g, const SddmmParams &p, hipStream_t s)
 {
     const long long units = ((long long)p.m + kWave / g - 1) / (kWave / g);
     const dim3 grid((unsigned)xcd_grid(p.batch, units));
     if (g == 8)
-        hipLaunchKernelGGL(sddmm_multirow_kernel<8>, grid, dim3(kWave), 0, s, p);
+        hipLaunchKernelGGL((sddmm_multirow_kernel<E, 8>), grid, dim3(kWave), 0, s, p);
     else
-        hipLaunchKernelGGL(sddmm_multirow_kernel<16>, grid, dim3(kWave), 0, s, p);
+        hipLaunchKernelGGL((sddmm_multirow_kernel<E, 16>), grid, dim3(kWave), 0, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_union(int g, const SddmmParams &p, hipStream_t s)
+hipError_t launch_multirow(Dtype dtype, int g, const SddmmParams &p, hipStream_t s)
+{
+    switch (dtype) {
+    case Dtype::f16: return launch_multirow_e<_Float16>(g, p, s);
+    case Dtype::bf16: return launch_multirow_e<bf16>(g, p, s);
+    default: return launch_multirow_e<float>(g, p, s);
+    }
+}
+
+template <typename E>
+hipError_t launch_union_e(int g, const SddmmParams &p, hipStream_t s)
 {
     constexpr int kW = kUnionWaves;
     const dim3 grid((unsigned)pu::grid<kW>(p.m, p.batch));
     const size_t lds = pu::dynamic_lds(p.k);
     if (g == 8)
-        hipLaunchKernelGGL((sddmm_union_kernel<8, kW>), grid, dim3(kW * kWave), lds, s, p);
+        hipLaunchKernelGGL((sddmm_union_kernel<E, 8, kW>), grid, dim3(kW * kWave), lds, s, p);
     else
-        hipLaunchKernelGGL((sddmm_union_kernel<16, kW>), grid, dim3(kW * kWave), lds, s, p);
+        hipLaunchKernelGGL((sddmm_union_kernel<E, 16, kW>), grid, dim3(kW * kWave), lds, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_union(Dtype dtype, int g, const SddmmParams &p, hipStream_t s)
+{
+    switch (dtype) {
+    case Dtype::f16: return launch_union_e<_Float16>(g, p, s);
+    case Dtype::bf16: return launch_union_e<bf16>(g, p, s);
+    default: return launch_union_e<float>(g, p, s);
+    }
 }
 
 template <typename E, int kG, int kVec, bool kSm>
@@ -1444,14 +1464,14 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
     plan->vec = vec;
     plan->g = g;
     plan->nv = nv;
-    // Rows of at most 64 fp32 (one vector per lane, 8 or 16 lanes per entry)
-    // not split over waves: several rows per wave (sddmm_multirow_kernel).
-    // Its buffer resources need X, Y and the outputs of one batch entry under
-    // 2 GiB.
+    // Rows of one 16-byte vector per lane with 8 or 16 lanes per entry (fp32 d
+    // from 20 to 64; 16-bit d from 40 to 128) not split over waves: several
+    // rows per wave (sddmm_multirow_kernel).  Its buffer resources need X, Y
+    // and the outputs of one batch entry under 2 GiB.
     const int rpw = kWave / g;
-    plan->multirow = a.dtype == Dtype::f32 && vec && !a.softmax && !plan->split && nv == 1 &&
-                     (g == 8 || g == 16) && buf && (long long)a.nnz * 4 < (1LL << 31) &&
-                     (long long)a.m * a.d * 4 < (1LL << 31) &&
+    plan->multirow = vec && !a.softmax && !plan->split && nv == 1 && (g == 8 || g == 16) &&
+                     buf && (long long)a.nnz * 4 < (1LL << 31) &&
+                     (long long)a.m * a.d * eb < (1LL << 31) &&
                      xcd_grid(a.batch, ((long long)a.m + rpw - 1) / rpw) <= 0x7fffffffLL;
     // Batched problems on up to 65,536 columns: the panel-union kernel, which
     // falls back to the multi-row walk panel by panel where columns are not
@@ -1503,8 +1523,8 @@ hipError_t run_sddmm(const SddmmPlan &plan, hipStream_t stream)
     default:
         break;
     }
-    if (plan.panel_union) return launch_union(plan.g, p, stream);
-    if (plan.multirow) return launch_multirow(plan.g, p, stream);
+    if (plan.panel_union) return launch_union(plan.dtype, plan.g, p, stream);
+    if (plan.multirow) return launch_multirow(plan.dtype, plan.g, p, stream);
     const bool sm = plan.softmax, sp = plan.split;
     switch (plan.dtype) {
     case Dtype::f16:
