@@ -74,6 +74,37 @@ __device__ __forceinline__ bool panel_of(int m, int batch, const int *row_offset
     return true;
 }
 
+// Sets column c's bit (c < k) with one atomic per run of lanes that set bits
+// of the same word.  A panel row's entries sit on consecutive lanes of a
+// 16-lane DPP row in column order, so equal words form runs; the bits of a run
+// are ORed into its first lane (the row mirrored, a shift-right scan, mirrored
+// back), which alone issues the ds_or: the row's lanes no longer all hit the
+// same LDS word.  Every lane of the wave must be active.
+__device__ __forceinline__ void mark_column(unsigned c, unsigned k, unsigned *s_bits)
+{
+    const bool ok = c < k;
+    const unsigned wd = ok ? (c >> 5) + 1u : 0u;   // word + 1 (0: nothing to set)
+    unsigned bits = ok ? 1u << (c & 31) : 0u;
+    // mirrored: lane i holds lane 15 - i's word and bits
+    const unsigned mw = dpp_read<kDppRowMirror>(wd);
+    unsigned mb = dpp_read<kDppRowMirror>(bits);
+    // (row_shr reads lane i - s, and 0 at the row's start: no word matches 0)
+    {
+        const unsigned w1 = dpp_read<kDppRowShr1>(mw), b1 = dpp_read<kDppRowShr1>(mb);
+        mb |= w1 == mw ? b1 : 0u;
+        const unsigned w2 = dpp_read<kDppRowShr2>(mw), b2 = dpp_read<kDppRowShr2>(mb);
+        mb |= w2 == mw ? b2 : 0u;
+        const unsigned w4 = dpp_read<kDppRowShr4>(mw), b4 = dpp_read<kDppRowShr4>(mb);
+        mb |= w4 == mw ? b4 : 0u;
+        const unsigned w8 = dpp_read<kDppRowShr8>(mw), b8 = dpp_read<kDppRowShr8>(mb);
+        mb |= w8 == mw ? b8 : 0u;
+    }
+    // back: lane i holds the OR of its run from lane i on
+    bits = dpp_read<kDppRowMirror>(mb);
+    const bool first = dpp_read<kDppRowShr1>(wd) != wd;
+    if (ok && first) atomicOr(&s_bits[wd - 1u], bits);
+}
+
 // Forms the panel's union (pp.pn > 0; every thread of the workgroup calls
 // it).  Returns the union's size with s.ucol and s.emap filled, or -1 for a
 // panel that takes the per-entry path (no barrier follows that return, and
@@ -110,8 +141,7 @@ __device__ __forceinline__ int build(const int *row_offsets, const int *col_indi
         reinterpret_cast<unsigned *>(s.emap)[i] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < kCache; ++t)
-        if (cc[t] < (unsigned)k) atomicOr(&s_bits[cc[t] >> 5], 1u << (cc[t] & 31));
+    for (int t = 0; t < kCache; ++t) mark_column(cc[t], (unsigned)k, s_bits);
     for (int j = rb + mq + kTpr * kCache; j < re; j += kTpr) {
         const unsigned c = (unsigned)col_indices[j];
         if (c < (unsigned)k) atomicOr(&s_bits[c >> 5], 1u << (c & 31));
