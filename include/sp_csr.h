@@ -414,7 +414,8 @@ sp_status_t sp_spmm_kernel_name(int m, int k, int n, int nnz, const int *row_ind
  *               panel of 16 consecutive rows, the union of the rows' columns
  *               is formed once for 4 batch entries and the scores computed as
  *               matrix-core tiles over it; panels whose rows share few columns
- *               run the multi-row walk;
+ *               run the multi-row walk (sp_sddmm_softmax, whose batches of
+ *               the same shape take this kernel too: the row softmax body);
  *   "multirow"  several short rows per wave (16-byte-aligned X and Y, one
  *               16-byte vector per lane with 8 or 16 lanes per entry: fp32 d a
  *               multiple of 4 from 20 to 64, 16-bit d a multiple of 8 from 40

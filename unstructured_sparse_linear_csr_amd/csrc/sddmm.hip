@@ -203,7 +203,12 @@ namespace pu = panel_union;
 // Batch entries (waves) per workgroup of the union kernel.
 constexpr int kUnionWaves = 4;
 
-template <typename E, int kG, int kW>
+// kSm: the row softmax of the scaled scores (sp_sddmm_softmax) in three walks
+// over the tiles -- each row's exact maximum, the sum of exp(s - max), then
+// the normalised writes -- recomputing the tiles each time, so the values are
+// formed as the row kernel forms them (no running-maximum rescaling); panels
+// that fall back run the row kernel's softmax body on their rows.
+template <typename E, int kG, int kW, bool kSm>
 __global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
 {
     typedef float f4 __attribute__((ext_vector_type(4)));
@@ -223,11 +228,20 @@ __global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
     if (z >= p.batch) return;
     const int r0 = pp.r0, nr = pp.nr, e0 = pp.e0;
     if (nu < 0) {
-        constexpr int kR = kWave / kG;
+        if constexpr (kSm) {
+            // one row at a time on this wave, through its own staging region
+            SddmmParams pr = p;
+            pr.row_indices = nullptr;
 #pragma unroll 1
-        for (int u = 0; u < pu::kRows / kR; ++u) {
-            const int slot = u * kR + lane / kG;
-            multirow_rows<E, kG>(p, z, slot < nr, slot < nr ? r0 + slot : r0);
+            for (int i = 0; i < nr; ++i)
+                sddmm_rows_body<E, kG, 1, kVecE, true, 1, kW>(pr, z * p.m + r0 + i);
+        } else {
+            constexpr int kR = kWave / kG;
+#pragma unroll 1
+            for (int u = 0; u < pu::kRows / kR; ++u) {
+                const int slot = u * kR + lane / kG;
+                multirow_rows<E, kG>(p, z, slot < nr, slot < nr ? r0 + slot : r0);
+            }
         }
         return;
     }
@@ -270,12 +284,15 @@ __global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
     };
     const float alpha = p.alpha, beta = p.beta;
     const float *mvz = p.mask_values ? p.mask_values + z * p.stride_values : nullptr;
-    auto tile_out = [&](int T, const float (&yb)[kS]) {
+    auto tile_acc = [&](const float (&yb)[kS]) {
         f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < kS; ++t)
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[t], yb[t], acc, 0, 0, 0);
-        // lane l holds rows 4 (l / 16) .. + 3 of tile column l % 16
+        return acc;  // lane l: rows 4 (l / 16) .. + 3 of tile column l % 16
+    };
+    auto tile_out = [&](int T, const float (&yb)[kS]) {
+        const f4 acc = tile_acc(yb);
         const int u = 16 * T + jl;
         const int uc = min(u, pu::kMaxCols - 1);
 #pragma unroll
@@ -295,16 +312,69 @@ __global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res), ro, (int)oo, 0, 0);
         }
     };
-    float ya[kS], yb[kS];
-    load_tile(0, ya);
-    // one exit, at the end (as in the multi-row walk)
-    for (int T = 0; T < ntiles; T += 2) {
-        load_tile(T + 1, yb);
-        keep_issued_above();
-        tile_out(T, ya);
-        load_tile(T + 2, ya);
-        keep_issued_above();
-        tile_out(T + 1, yb);
+    auto walk = [&](auto visit) {
+        float ya[kS], yb[kS];
+        load_tile(0, ya);
+        // one exit, at the end (as in the multi-row walk)
+        for (int T = 0; T < ntiles; T += 2) {
+            load_tile(T + 1, yb);
+            keep_issued_above();
+            visit(T, ya);
+            load_tile(T + 2, ya);
+            keep_issued_above();
+            visit(T + 1, yb);
+        }
+    };
+    if constexpr (!kSm) {
+        walk(tile_out);
+    } else {
+        // per row (the lanes of a 16-lane group hold the same four rows)
+        float rmax[4], rsum[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            rmax[r] = -INFINITY;
+            rsum[r] = 0.f;
+        }
+        // the scaled scores of tile T, -Inf where the row has no entry
+        auto scaled = [&](int T, const float (&yb)[kS], unsigned (&idx)[4], float (&sv)[4]) {
+            const f4 acc = tile_acc(yb);
+            const int u = 16 * T + jl;
+            const int uc = min(u, pu::kMaxCols - 1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                idx[r] = u < nu ? s.emap[(4 * q + r) * pu::kEmapStride + uc] : 0u;
+                sv[r] = idx[r] ? alpha * acc[r] : -INFINITY;
+            }
+        };
+        walk([&](int T, const float (&yb)[kS]) {
+            unsigned idx[4];
+            float sv[4];
+            scaled(T, yb, idx, sv);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rmax[r] = fmaxf(rmax[r], group_reduce<16>(sv[r], OpMax{}));
+        });
+        walk([&](int T, const float (&yb)[kS]) {
+            unsigned idx[4];
+            float sv[4];
+            scaled(T, yb, idx, sv);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                rsum[r] += group_sum<16>(idx[r] ? expf(sv[r] - rmax[r]) : 0.f);
+        });
+        float rinv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rinv[r] = 1.f / rsum[r];
+        walk([&](int T, const float (&yb)[kS]) {
+            unsigned idx[4];
+            float sv[4];
+            scaled(T, yb, idx, sv);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const unsigned oo = idx[r] ? (unsigned)(e0 + (int)idx[r] - 1) * 4u : kOutOfRange;
+                const float e = idx[r] ? expf(sv[r] - rmax[r]) * rinv[r] : 0.f;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), ro, (int)oo, 0, 0);
+            }
+        });
     }
 }
 
@@ -1176,25 +1246,31 @@ hipError_t launch_multirow(Dtype dtype, int g, const SddmmParams &p, hipStream_t
     }
 }
 
-template <typename E>
+template <typename E, bool kSm>
 hipError_t launch_union_e(int g, const SddmmParams &p, hipStream_t s)
 {
     constexpr int kW = kUnionWaves;
     const dim3 grid((unsigned)pu::grid<kW>(p.m, p.batch));
     const size_t lds = pu::dynamic_lds(p.k);
     if (g == 8)
-        hipLaunchKernelGGL((sddmm_union_kernel<E, 8, kW>), grid, dim3(kW * kWave), lds, s, p);
+        hipLaunchKernelGGL((sddmm_union_kernel<E, 8, kW, kSm>), grid, dim3(kW * kWave), lds, s, p);
     else
-        hipLaunchKernelGGL((sddmm_union_kernel<E, 16, kW>), grid, dim3(kW * kWave), lds, s, p);
+        hipLaunchKernelGGL((sddmm_union_kernel<E, 16, kW, kSm>), grid, dim3(kW * kWave), lds, s,
+                           p);
     return hipGetLastError();
 }
 
-hipError_t launch_union(Dtype dtype, int g, const SddmmParams &p, hipStream_t s)
+hipError_t launch_union(Dtype dtype, int g, bool softmax, const SddmmParams &p, hipStream_t s)
 {
     switch (dtype) {
-    case Dtype::f16: return launch_union_e<_Float16>(g, p, s);
-    case Dtype::bf16: return launch_union_e<bf16>(g, p, s);
-    default: return launch_union_e<float>(g, p, s);
+    case Dtype::f16:
+        return softmax ? launch_union_e<_Float16, true>(g, p, s)
+                       : launch_union_e<_Float16, false>(g, p, s);
+    case Dtype::bf16:
+        return softmax ? launch_union_e<bf16, true>(g, p, s) : launch_union_e<bf16, false>(g, p, s);
+    default:
+        return softmax ? launch_union_e<float, true>(g, p, s)
+                       : launch_union_e<float, false>(g, p, s);
     }
 }
 
@@ -1469,14 +1545,17 @@ hipError_t plan_sddmm(const SddmmArgs &a, SddmmPlan *plan)
     // rows per wave (sddmm_multirow_kernel).  Its buffer resources need X, Y
     // and the outputs of one batch entry under 2 GiB.
     const int rpw = kWave / g;
-    plan->multirow = vec && !a.softmax && !plan->split && nv == 1 && (g == 8 || g == 16) &&
-                     buf && (long long)a.nnz * 4 < (1LL << 31) &&
-                     (long long)a.m * a.d * eb < (1LL << 31) &&
+    const bool multirow_shape =
+        vec && !plan->split && nv == 1 && (g == 8 || g == 16) && buf &&
+        (long long)a.nnz * 4 < (1LL << 31) && (long long)a.m * a.d * eb < (1LL << 31);
+    plan->multirow = multirow_shape && !a.softmax &&
                      xcd_grid(a.batch, ((long long)a.m + rpw - 1) / rpw) <= 0x7fffffffLL;
-    // Batched problems on up to 65,536 columns: the panel-union kernel, which
-    // falls back to the multi-row walk panel by panel where columns are not
-    // shared.  One batch entry would leave three of its four waves idle.
-    plan->panel_union = plan->multirow && a.batch >= 2 && a.k <= pu::kMaxK &&
+    // Batched problems of that shape on up to 65,536 columns, scores alone or
+    // with their row softmax: the panel-union kernel, which falls back panel by
+    // panel (to the multi-row walk, or to the row kernel's softmax body) where
+    // columns are not shared.  One batch entry would leave three of its four
+    // waves idle.
+    plan->panel_union = multirow_shape && a.batch >= 2 && a.k <= pu::kMaxK &&
                         pu::grid<kUnionWaves>(a.m, a.batch) <= 0x7fffffffLL;
     return hipSuccess;
 }
@@ -1523,7 +1602,7 @@ hipError_t run_sddmm(const SddmmPlan &plan, hipStream_t stream)
     default:
         break;
     }
-    if (plan.panel_union) return launch_union(plan.dtype, plan.g, p, stream);
+    if (plan.panel_union) return launch_union(plan.dtype, plan.g, plan.softmax, p, stream);
     if (plan.multirow) return launch_multirow(plan.dtype, plan.g, p, stream);
     const bool sm = plan.softmax, sp = plan.split;
     switch (plan.dtype) {

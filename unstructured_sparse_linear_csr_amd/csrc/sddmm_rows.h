@@ -106,9 +106,15 @@ __device__ __forceinline__ void rows_sync()
     }
 }
 
-template <typename E, int kG, int kNv, int kVec, bool kSoftmax = false, int kParts = 1>
+// kWaves: the waves of the workgroup, each with its own staging region and a
+// wave-local sync (kParts of them split a row's windows; with kParts = 1 and
+// kWaves > 1 each wave walks rows of its own, as the panel-union kernel's
+// per-row fallback does).
+template <typename E, int kG, int kNv, int kVec, bool kSoftmax = false, int kParts = 1,
+          int kWaves = kParts>
 __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long w)
 {
+    static_assert(kParts == 1 || kParts == kWaves, "split rows use every wave");
     static_assert(!(kSoftmax && kParts > 1), "the row softmax needs the whole row in one wave");
     using V = GVec<E, kVec>;
     using VecT = typename V::T;
@@ -120,7 +126,7 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
     // The window's 64 entries, then padding for the prefetch of up to two
     // batches past the last step.
     constexpr int kSlots = kWave + 2 * kU * kNg;
-    __shared__ unsigned s_off_all[kParts][kSlots];
+    __shared__ unsigned s_off_all[kWaves][kSlots];
 
     constexpr int kHeldWindows = 4;
     float held[kHeldWindows];
@@ -131,8 +137,9 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
     const long long z = w / p.m;
     const int slot = (int)(w - z * p.m);
     const int part = kParts == 1 ? 0 : (int)threadIdx.x / kWave;  // this wave's windows
-    const int lane = kParts == 1 ? (int)threadIdx.x : (int)threadIdx.x % kWave;
-    unsigned *s_off = s_off_all[part];
+    const int region = kWaves == 1 ? 0 : (int)threadIdx.x / kWave;  // its staging
+    const int lane = kWaves == 1 ? (int)threadIdx.x : (int)threadIdx.x % kWave;
+    unsigned *s_off = s_off_all[region];
     const int g = lane / kG;
     const int gl = lane - g * kG;
     const int row = p.row_indices ? p.row_indices[slot] : slot;
@@ -162,13 +169,13 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
     };
 
     if constexpr (kNv == 0) {
-        __shared__ int s_col_all[kParts][kWave];
-        int *s_col = s_col_all[part];
+        __shared__ int s_col_all[kWaves][kWave];
+        int *s_col = s_col_all[region];
         for (int wi = part; wi < nwin; wi += kParts) {
             const int base = p0 + wi * kWave;
             const int cnt = min(kWave, p1 - base);
             s_col[lane] = lane < cnt ? p.col_indices[base + lane] : 0;
-            rows_sync<kParts>();
+            rows_sync<kWaves>();
             const int steps = (cnt + kNg - 1) / kNg;
             float res = 0.f;
             for (int s = 0; s < steps; ++s) {
@@ -185,7 +192,7 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
             }
             const int jo = gl * kNg + g;
             if (jo < cnt) emit(base + jo, res);
-            rows_sync<kParts>();
+            rows_sync<kWaves>();
             ++window;
         }
     } else {
@@ -226,7 +233,7 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
             s_off[lane] = lane < cnt
                               ? (unsigned)p.col_indices[base + lane] * (unsigned)p.d * kEb
                               : kOutOfRange;
-            rows_sync<kParts>();
+            rows_sync<kWaves>();
             const int steps = (cnt + kNg - 1) / kNg;
             float res = 0.f;
             // A window has at most kG steps, so its batches are unrolled into
@@ -247,7 +254,7 @@ __device__ __forceinline__ void sddmm_rows_body(const SddmmParams &p, long long 
             }
             const int jo = gl * kNg + g;  // the entry whose sum this lane kept
             if (jo < cnt) emit(base + jo, res);
-            rows_sync<kParts>();
+            rows_sync<kWaves>();
             ++window;
         }
     }
