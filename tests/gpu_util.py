@@ -97,3 +97,31 @@ def check_attention(o_gpu, m, k, ro, ci, q, kk, v, alpha, what, rescalings=None)
     assert not bad.any(), (f"{what}: {int(bad.sum())} out of bound; worst "
                            f"{np.max(err / np.maximum(bound, 1e-300)):.3g}")
     assert np.all(o_gpu[lengths == 0] == 0.0), f"{what}: empty rows not zero"
+
+
+def check_scores_softmax(got, m, k, ro, ci, x, y, alpha, what):
+    s, s_abs = oracle.sddmm(m, k, x.shape[1], ro, ci, x, y)
+    s, e_s = alpha * s, abs(alpha) * 1e-5 * s_abs
+    p_ref = oracle.softmax_rows(ro, s.astype(np.float32))
+    rows = np.repeat(np.arange(m), np.diff(ro))
+    e_row = np.zeros(m)
+    np.maximum.at(e_row, rows, e_s)
+    smax = np.full(m, -np.inf)
+    np.maximum.at(smax, rows, s)
+    x_row = np.zeros(m)
+    np.maximum.at(x_row, rows, np.abs(s - smax[rows]))
+    a_row = np.zeros(m)
+    np.maximum.at(a_row, rows, np.abs(s))
+    rel = 2.0 * e_row + 2.0 * a_row * 2.0 ** -24 + (x_row + 8.0) * 2.0 ** -23
+    bound = p_ref * rel[rows] * 1.01 + 2.0 ** -126
+    g = got.astype(np.float64)
+    assert np.all(np.isfinite(g)), what
+    err = np.abs(g - p_ref)
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} entries out of bound; worst "
+                           f"{np.max(err / np.maximum(bound, 1e-300)):.3g}")
+    # each nonempty row sums to 1 within the rounding of its entries
+    sums = np.zeros(m)
+    np.add.at(sums, rows, g)
+    nonempty = np.diff(ro) > 0
+    assert np.all(np.abs(sums[nonempty] - 1.0) <= 1e-5 + np.diff(ro)[nonempty] * 2.0 ** -22)

@@ -282,3 +282,32 @@ def test_16bit(kind, d):
         ref = host(one)
         assert np.array_equal(got[z][tail].view(np.uint32), ref[tail].view(np.uint32)), \
             f"{kind} entry {z}: fallback panels differ from the one-row sums"
+
+
+def test_softmax_deep_unions_and_fallback():
+    """sp_sddmm_softmax through the union kernel: rows 0..159 of a 200-key band
+    (unions of about 215 keys: 14 tiles, the deepest sums), rows 160..319 of 60
+    random keys (the row kernel's softmax body, bit-equal to a one-head call),
+    three heads; the bound of the row softmax against the oracle."""
+    from gpu_util import check_scores_softmax
+    k, d = 3000, 64
+    lists = [list(range(i, i + 200)) for i in range(160)]   # 200 keys each, shifting by one
+    lists += random_lists(17, 160, k, 60)
+    a = from_lists(320, k, lists)
+    xs = np.stack([inputs.random_dense(600 + z, a.m, d) for z in range(3)])
+    ys = np.stack([inputs.random_dense(610 + z, k, d) for z in range(3)])
+    x, y = dev(xs), dev(ys)
+    out = torch.full((3, a.nnz), float("nan"), device="cuda")
+    note("panel-union sddmm softmax")
+    sp.sp_sddmm_softmax(a.m, k, d, a.nnz, None, a.d_ro, a.d_ci, x, y, 0.125, out, 3, a.m * d,
+                        k * d, a.nnz)
+    got = host(out)
+    tail = slice(int(a.ro[160]), a.nnz)
+    for z in range(3):
+        check_scores_softmax(got[z], a.m, k, a.ro, a.ci, xs[z], ys[z], 0.125, f"head {z}")
+        one = torch.full((a.nnz,), float("nan"), device="cuda")
+        sp.sp_sddmm_softmax(a.m, k, d, a.nnz, None, a.d_ro, a.d_ci, dev(xs[z]), dev(ys[z]),
+                            0.125, one)
+        ref = host(one)
+        assert np.array_equal(got[z][tail].view(np.uint32), ref[tail].view(np.uint32)), \
+            f"head {z}: fallback rows differ from the row kernel's softmax"
