@@ -148,3 +148,69 @@ def test_graph_of_every_launch_kind():
         for name, t in outs.items():
             assert np.array_equal(host(t).view(np.int32), want[name].view(np.int32)), (rep, name)
         assert np.array_equal(host(t_ro), want["t_ro"]) and np.array_equal(host(t_ci), want["t_ci"])
+
+
+def test_graph_of_panel_union_launches():
+    """The panel-union kernels (batched scores, scores + softmax, P V and
+    one-pass attention on a band mask, 4 heads) and the multi-row SDDMM (one
+    batch entry of short rows), captured and replayed like the rest."""
+    m, d, heads = 512, 64, 4
+    lists = []
+    for i in range(m):
+        cols = set(range(max(0, i - 47), i + 1)) | set(range(0, max(0, i - 47), 64))
+        lists.append(sorted(cols))
+    lengths = np.array([len(c) for c in lists], np.int32)
+    ro_np = oracle.csr_offsets_from_lengths(lengths)
+    ci_np = np.concatenate([np.asarray(c, np.int32) for c in lists])
+    nnz = int(ro_np[-1])
+    ro, ci = dev(ro_np), dev(ci_np)
+    q = dev(inputs.random_dense(960, heads, m, d))
+    kk = dev(inputs.random_dense(961, heads, m, d))
+    v = dev(inputs.random_dense(962, heads, m, d))
+    pv = dev(np.abs(inputs.random_dense(963, heads, nnz)) / 48.0)
+    short = inputs.random_row_lists(964, 300, 400, np.full(300, 5, np.int32))
+    s_ro, s_ci = dev(oracle.csr_offsets_from_lengths(short.lengths)), dev(short.cols)
+    sx, sy = dev(inputs.random_dense(965, 300, d)), dev(inputs.random_dense(966, 400, d))
+    outs = {name: torch.empty(shape, device="cuda") for name, shape in {
+        "s": (heads, nnz), "p": (heads, nnz), "o": (heads, m, d), "att": (heads, m, d),
+        "short": (short.nnz,)}.items()}
+    st = m * d
+    assert sp.sp_sddmm_kernel_name(m, m, d, nnz, q, kk, heads, st, st, nnz) == "panel_union"
+    assert sp.sp_spmm_kernel_name(m, m, d, nnz, pv, ci, v, outs["o"], heads, nnz, st,
+                                  st) == "panel_union"
+    assert sp.sp_sddmm_kernel_name(300, 400, d, short.nnz, sx, sy) == "multirow"
+
+    def work():
+        sp.sp_sddmm_batched(m, m, d, nnz, None, ro, ci, q, kk, 0.125, outs["s"], heads, st, st,
+                            nnz)
+        sp.sp_sddmm_softmax(m, m, d, nnz, None, ro, ci, q, kk, 0.125, outs["p"], heads, st, st,
+                            nnz)
+        sp.sp_spmm_batched(m, m, d, nnz, None, pv, ro, ci, v, outs["o"], heads, nnz, st, st)
+        sp.sp_sparse_attention(m, m, d, nnz, None, ro, ci, q, kk, v, 0.125, outs["att"], heads,
+                               st, st, st, st)
+        sp.sp_sddmm(300, 400, d, short.nnz, None, s_ro, s_ci, sx, sy, outs["short"])
+
+    note("graph of panel-union launches: eager reference")
+    work()
+    torch.cuda.synchronize()
+    want = {name: host(t).copy() for name, t in outs.items()}
+    s_ref, s_abs = oracle.sddmm(m, m, d, ro_np, ci_np, host(q)[0], host(kk)[0])
+    check_close(want["s"][0], 0.125 * s_ref, 0.125 * s_abs, "union scores in the graph test")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(3):
+        note(f"panel-union graph replay {rep}")
+        for t in outs.values():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t in outs.items():
+            assert np.array_equal(host(t).view(np.int32), want[name].view(np.int32)), (rep, name)
