@@ -20,6 +20,11 @@
 // Head dimensions: Q, K and V rows have the same length d, a multiple of one
 // 16-byte vector, with d / (elements per vector) in {8, 16, 32, 64} (fp32: d =
 // 32, 64, 128, 256; fp16 and bf16: 64, 128, 256, 512).
+//
+// Batches whose heads are small enough (fp32 d = 32 or 64, 16-bit d = 64) take
+// attention_union_kernel below instead: panels of 16 query rows walked in
+// 16-key tiles of their key union on matrix cores, with the per-row walk
+// above (attention_row) for panels that share few keys.
 #include <algorithm>
 
 #include "sp_device.h"

@@ -1,7 +1,9 @@
 // CSR SDDMM for gfx950 ("Sparse GPU Kernels for Deep Learning", summary card,
 // "Summary" and "Interesting ideas" I3).  The body for Y stored k x d, and the
-// design notes for it, are in sddmm_rows.h; this file holds the kernel for Y
-// stored d x k (the general form I3 leaves out) and the variant selection.
+// design notes for it, are in sddmm_rows.h; this file holds the kernels that
+// walk several short rows per wave and that compute batched panels as matrix-
+// core tiles over their column union (panel_union.h), the kernels for Y stored
+// d x k (the general form I3 leaves out), and the variant selection.
 #include <algorithm>
 
 #include "sp_device.h"

@@ -1,7 +1,9 @@
 // CSR SpMM for gfx950: C = A * B with A sparse (CSR) and B, C dense row-major
 // ("Sparse GPU Kernels for Deep Learning", summary card, "Summary").  The wide
 // kernel's body, and the design notes for it, are in spmm_wide.h; this file
-// holds the narrow-B kernels and the variant selection.
+// holds the narrow-B, streaming, balanced, row-split and panel-union (batched
+// panels as matrix-core tiles over their column union, panel_union.h) kernels
+// and the variant selection.
 #include <algorithm>
 #include <type_traits>
 
