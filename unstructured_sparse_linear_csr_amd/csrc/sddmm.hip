@@ -205,11 +205,12 @@ namespace pu = panel_union;
 // Batch entries (waves) per workgroup of the union kernel.
 constexpr int kUnionWaves = 4;
 
-// kSm: the row softmax of the scaled scores (sp_sddmm_softmax) in three walks
-// over the tiles -- each row's exact maximum, the sum of exp(s - max), then
-// the normalised writes -- recomputing the tiles each time, so the values are
-// formed as the row kernel forms them (no running-maximum rescaling); panels
-// that fall back run the row kernel's softmax body on their rows.
+// kSm: the row softmax of the scaled scores (sp_sddmm_softmax): one walk over
+// the tiles keeps their scores in registers, then each row's exact maximum,
+// the sum of exp(s - max) and the normalised writes are taken from them, so
+// the values are formed as the row kernel forms them (no running-maximum
+// rescaling); panels that fall back run the row kernel's softmax body on
+// their rows.
 template <typename E, int kG, int kW, bool kSm>
 __global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
 {
@@ -326,6 +327,14 @@ __global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
     if constexpr (!kSm) {
         walk(tile_out);
     } else {
+        // one walk: every tile's scaled scores stay in registers (at most
+        // kMaxCols / 16 tiles of 4 values a lane), so Y is read once; then
+        // the sums and the normalised writes.  The values and their order of
+        // summation are those of three walks that recompute the tiles.
+        static_assert(pu::kMaxCols == 16 * 16, "score registers cover 16 tiles");
+        constexpr int kTiles = pu::kMaxCols / 16;
+        float sv[kTiles][4];
+        unsigned long long has = 0ull;  // bit 4 T + r: the lane's entry of tile T, row r
         // per row (the lanes of a 16-lane group hold the same four rows)
         float rmax[4], rsum[4];
 #pragma unroll
@@ -333,46 +342,50 @@ __global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
             rmax[r] = -INFINITY;
             rsum[r] = 0.f;
         }
-        // the scaled scores of tile T, -Inf where the row has no entry
-        auto scaled = [&](int T, const float (&yb)[kS], unsigned (&idx)[4], float (&sv)[4]) {
-            const f4 acc = tile_acc(yb);
-            const int u = 16 * T + jl;
-            const int uc = min(u, pu::kMaxCols - 1);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                idx[r] = u < nu ? s.emap[(4 * q + r) * pu::kEmapStride + uc] : 0u;
-                sv[r] = idx[r] ? alpha * acc[r] : -INFINITY;
+        for (int T = 0; T < kTiles; ++T) {
+            if (T < ntiles) {
+                float yt[kS];
+                load_tile(T, yt);
+                const f4 acc = tile_acc(yt);
+                const int u = 16 * T + jl;
+                const int uc = min(u, pu::kMaxCols - 1);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const unsigned idx = u < nu ? s.emap[(4 * q + r) * pu::kEmapStride + uc] : 0u;
+                    has |= idx ? 1ull << (4 * T + r) : 0ull;
+                    sv[T][r] = idx ? alpha * acc[r] : -INFINITY;
+                    rmax[r] = fmaxf(rmax[r], group_reduce<16>(sv[T][r], OpMax{}));
+                }
             }
-        };
-        walk([&](int T, const float (&yb)[kS]) {
-            unsigned idx[4];
-            float sv[4];
-            scaled(T, yb, idx, sv);
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) rmax[r] = fmaxf(rmax[r], group_reduce<16>(sv[r], OpMax{}));
-        });
-        walk([&](int T, const float (&yb)[kS]) {
-            unsigned idx[4];
-            float sv[4];
-            scaled(T, yb, idx, sv);
+        for (int T = 0; T < kTiles; ++T) {
+            if (T < ntiles) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                rsum[r] += group_sum<16>(idx[r] ? expf(sv[r] - rmax[r]) : 0.f);
-        });
+                for (int r = 0; r < 4; ++r) {
+                    const bool e = (has >> (4 * T + r)) & 1ull;
+                    rsum[r] += group_sum<16>(e ? expf(sv[T][r] - rmax[r]) : 0.f);
+                }
+            }
+        }
         float rinv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) rinv[r] = 1.f / rsum[r];
-        walk([&](int T, const float (&yb)[kS]) {
-            unsigned idx[4];
-            float sv[4];
-            scaled(T, yb, idx, sv);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const unsigned oo = idx[r] ? (unsigned)(e0 + (int)idx[r] - 1) * 4u : kOutOfRange;
-                const float e = idx[r] ? expf(sv[r] - rmax[r]) * rinv[r] : 0.f;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), ro, (int)oo, 0, 0);
+        for (int T = 0; T < kTiles; ++T) {
+            if (T < ntiles) {
+                const int u = 16 * T + jl;
+                const int uc = min(u, pu::kMaxCols - 1);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const unsigned idx = u < nu ? s.emap[(4 * q + r) * pu::kEmapStride + uc] : 0u;
+                    const unsigned oo = idx ? (unsigned)(e0 + (int)idx - 1) * 4u : kOutOfRange;
+                    const float e = idx ? expf(sv[T][r] - rmax[r]) * rinv[r] : 0.f;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), ro, (int)oo, 0, 0);
+                }
             }
-        });
+        }
     }
 }
 
