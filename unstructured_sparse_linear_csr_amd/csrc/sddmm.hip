@@ -355,17 +355,22 @@ __global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
                     const unsigned idx = u < nu ? s.emap[(4 * q + r) * pu::kEmapStride + uc] : 0u;
                     has |= idx ? 1ull << (4 * T + r) : 0ull;
                     sv[T][r] = idx ? alpha * acc[r] : -INFINITY;
-                    rmax[r] = fmaxf(rmax[r], group_reduce<16>(sv[T][r], OpMax{}));
+                    rmax[r] = fmaxf(rmax[r], sv[T][r]);  // the lane's maximum so far
                 }
             }
         }
+        // the row's maximum (exact in any order)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rmax[r] = group_reduce<16>(rmax[r], OpMax{});
+        // sv becomes exp(s - max) (0 where no entry)
 #pragma unroll
         for (int T = 0; T < kTiles; ++T) {
             if (T < ntiles) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const bool e = (has >> (4 * T + r)) & 1ull;
-                    rsum[r] += group_sum<16>(e ? expf(sv[T][r] - rmax[r]) : 0.f);
+                    sv[T][r] = e ? expf(sv[T][r] - rmax[r]) : 0.f;
+                    rsum[r] += group_sum<16>(sv[T][r]);
                 }
             }
         }
@@ -381,7 +386,7 @@ __global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
                 for (int r = 0; r < 4; ++r) {
                     const unsigned idx = u < nu ? s.emap[(4 * q + r) * pu::kEmapStride + uc] : 0u;
                     const unsigned oo = idx ? (unsigned)(e0 + (int)idx - 1) * 4u : kOutOfRange;
-                    const float e = idx ? expf(sv[T][r] - rmax[r]) * rinv[r] : 0.f;
+                    const float e = sv[T][r] * rinv[r];
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), ro, (int)oo, 0, 0);
                 }
             }
