@@ -329,8 +329,8 @@ __global__ __launch_bounds__(kW * kWave) void sddmm_union_kernel(SddmmParams p)
     } else {
         // one walk: every tile's scaled scores stay in registers (at most
         // kMaxCols / 16 tiles of 4 values a lane), so Y is read once; then
-        // the sums and the normalised writes.  The values and their order of
-        // summation are those of three walks that recompute the tiles.
+        // each row's maximum, the exps and their sum (per tile over the row's
+        // 16-lane group, then tile by tile), and the normalised writes.
         static_assert(pu::kMaxCols == 16 * 16, "score registers cover 16 tiles");
         constexpr int kTiles = pu::kMaxCols / 16;
         float sv[kTiles][4];
