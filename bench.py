@@ -388,6 +388,11 @@ def config_records(torch, sp, inputs, dev, flush) -> list:
     # the softmax moves 8 bytes per entry (read, write) and does no FMA work
     recs.append(kernel_record(torch, "sparse_attention", "row_softmax_x32", w["name"], smfn,
                               0.0, bh * 8.0 * nnz + 8 * seq, flush, 20, tag))
+    # scores and their row softmax in one launch: the SDDMM's traffic
+    fsfn = lambda: sp.sp_sddmm_softmax(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125, s_out,
+                                       bh, seq * hd, seq * hd, nnz)
+    recs.append(kernel_record(torch, "sparse_attention", "sddmm_softmax_x32", w["name"], fsfn,
+                              2.0 * bh * nnz * hd, bh * sb, flush, 20, tag))
     recs.append(kernel_record(torch, "sparse_attention", "spmm_x32", w["name"], pfn,
                               2.0 * bh * nnz * hd, bh * pb, flush, 20, tag))
     recs.append(kernel_record(torch, "sparse_attention", "attention_one_pass_x32", w["name"], afn,
@@ -577,7 +582,9 @@ def profile_workload_fns(torch, sp, inputs, dev, wanted):
                                            nnz, seq * hd, seq * hd),
                 lambda: sp.sp_sparse_attention(seq, seq, hd, nnz, ri, ro, cols, q, kk, v,
                                                0.125, o, bh, seq * hd, seq * hd, seq * hd,
-                                               seq * hd)]
+                                               seq * hd),
+                lambda: sp.sp_sddmm_softmax(seq, seq, hd, nnz, ri, ro, cols, q, kk, 0.125,
+                                            s_out, bh, seq * hd, seq * hd, nnz)]
     return fns + imbalance_fns()
 
 
@@ -798,7 +805,6 @@ def run_suite(torch, sp, inputs, dev, path: str) -> None:
     for kind, fn, flops, byts in (
             ("sddmm_general_dk_x32", tfn, 2.0 * bh * nnz * hd, bh * sb),
             ("sddmm_general_dk_workspace_x32", twfn, 2.0 * bh * nnz * hd, bh * sb),
-            ("sddmm_softmax_x32", fsfn, 2.0 * bh * nnz * hd, bh * sb),
             ("attention_all_device_x32", attention, 4.0 * bh * nnz * hd,
              bh * (sb + 8 * nnz + pb)),
             ("attention_all_device_fused_scores_x32", attention_fused, 4.0 * bh * nnz * hd,
