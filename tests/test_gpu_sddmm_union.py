@@ -311,3 +311,33 @@ def test_softmax_deep_unions_and_fallback():
         ref = host(one)
         assert np.array_equal(got[z][tail].view(np.uint32), ref[tail].view(np.uint32)), \
             f"head {z}: fallback rows differ from the row kernel's softmax"
+
+
+@pytest.mark.parametrize("ncols", [1, 17, 255, 256, 257])
+def test_softmax_union_width(ncols):
+    """sp_sddmm_softmax on 16 rows sharing ncols columns, two heads: 2 to 16
+    tiles of kept scores (256 columns fill every tile slot); one column (too
+    few entries for a tile) and more than 256 take the row kernel's softmax
+    body, bit-equal to a one-head call.  Against the oracle within the row
+    softmax's bound."""
+    from gpu_util import check_scores_softmax
+    k, d = 3000, 64
+    cols = sorted(np.random.default_rng(70 + ncols).choice(k, ncols, replace=False).tolist())
+    a = from_lists(16, k, [cols] * 16)
+    xs = np.stack([inputs.random_dense(700 + z, a.m, d) for z in range(2)])
+    ys = np.stack([inputs.random_dense(710 + z, k, d) for z in range(2)])
+    out = torch.full((2, a.nnz), float("nan"), device="cuda")
+    note(f"panel-union sddmm softmax union width {ncols}")
+    sp.sp_sddmm_softmax(a.m, k, d, a.nnz, None, a.d_ro, a.d_ci, dev(xs), dev(ys), 0.125, out, 2,
+                        a.m * d, k * d, a.nnz)
+    got = host(out)
+    for z in range(2):
+        check_scores_softmax(got[z], a.m, k, a.ro, a.ci, xs[z], ys[z], 0.125,
+                             f"width {ncols} head {z}")
+        if ncols == 1:
+            assert np.all(got[z] == 1.0)
+        if ncols == 1 or ncols > 256:
+            one = torch.full((a.nnz,), float("nan"), device="cuda")
+            sp.sp_sddmm_softmax(a.m, k, d, a.nnz, None, a.d_ro, a.d_ci, dev(xs[z]), dev(ys[z]),
+                                0.125, one)
+            assert np.array_equal(got[z].view(np.uint32), host(one).view(np.uint32))
